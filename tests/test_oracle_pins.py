@@ -1,0 +1,305 @@
+"""Pins of the fp64 oracle against things other than itself (CPU only).
+
+Each test fixes the oracle to a value or property the pages or the mathematics
+determine: a hand-worked example, closed forms of special cases (linear
+attention, pure decay, projection / delta-rule recall), exact rational
+arithmetic, a dense matrix brute force, the chunked-parallel form, split-T state
+carry, linearity and value-column separability, and the zero / empty cases.
+A dropped term, a wrong sign, a transposed state or an off-by-one in time
+fails at least one of them.
+"""
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import independent_routes as routes
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def _one_head(oracle_mod, r, w, k, v, a, b, S0, per_position=False):
+    """Run the oracle on one head given [T,N] fp64 arrays."""
+    ex = lambda x: np.asarray(x, np.float64)[None, :, None, :]
+    s_in = None if S0 is None else np.asarray(S0, np.float64)[None, None]
+    res = oracle_mod.forward(ex(r), ex(w), ex(k), ex(v), ex(a), ex(b), s_in,
+                             per_position=per_position, f64_inputs=True)
+    if per_position:
+        o, s, sp = res
+        return o[0, :, 0, :], s[0, 0], sp[0, :, 0]
+    o, s = res
+    return o[0, :, 0, :], s[0, 0]
+
+
+def _rand_head(rng, T, N, w_lo=0.55, w_hi=1.0, s_std=0.3):
+    r, k, v = (rng.standard_normal((T, N)) for _ in range(3))
+    kk = k / np.linalg.norm(k, axis=1, keepdims=True)
+    gate = 1 / (1 + np.exp(-rng.standard_normal((T, N))))
+    a = -kk
+    b = kk * gate
+    w = rng.uniform(w_lo, w_hi, (T, N))
+    S0 = rng.standard_normal((N, N)) * s_std
+    return r, w, k, v, a, b, S0
+
+
+def _rel(x, ref):
+    n = np.linalg.norm(ref)
+    return np.linalg.norm(x - ref) / (n if n > 0 else 1.0)
+
+
+# --- hand-worked example -----------------------------------------------------
+
+def _read_golden(name):
+    vals = {}
+    with open(os.path.join(HERE, "golden", name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            key, *nums = line.split()
+            vals[key] = np.array([float(Fraction(x)) for x in nums])
+    return vals
+
+
+def test_golden_handworked_n2_t2(oracle_mod):
+    g = _read_golden("wkv7_n2_t2_handworked.txt")
+    T, N = 2, 2
+    sh = lambda x: x.reshape(T, N)
+    o, s = _one_head(oracle_mod, sh(g["r"]), sh(g["w"]), sh(g["k"]), sh(g["v"]), sh(g["a"]),
+                     sh(g["b"]), g["state_in"].reshape(N, N))
+    assert np.array_equal(o, sh(g["expect_o"]))
+    assert np.array_equal(s, g["expect_state_out"].reshape(N, N))
+
+
+# --- I7: exact rational arithmetic on dyadic inputs ---------------------------
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_exact_rational_dyadic(oracle_mod, seed):
+    rng = np.random.default_rng(100 + seed)
+    T, N = 3, 3
+    dy = lambda *shape: rng.integers(-8, 9, shape) / 8.0      # multiples of 1/8: exact in fp64
+    r, k, v, a, b = dy(T, N), dy(T, N), dy(T, N), dy(T, N), dy(T, N)
+    w = rng.integers(1, 9, (T, N)) / 8.0
+    S0 = dy(N, N)
+    o, s = _one_head(oracle_mod, r, w, k, v, a, b, S0)
+    F = lambda x: [[Fraction(float(e)) for e in row] for row in x]
+    eo, es = routes.exact_rational(F(r), F(w), F(k), F(v), F(a), F(b), F(S0))
+    # every intermediate is a short dyadic rational, so fp64 is exact here
+    assert np.array_equal(o, np.array([[float(e) for e in row] for row in eo]))
+    assert np.array_equal(s, np.array([[float(e) for e in row] for row in es]))
+
+
+# --- orientation: S = [K, V], write k (x) v, readout r^T S -----------------------
+
+def test_orientation_unit_vectors(oracle_mod):
+    N, T = 8, 1
+    for (i, j) in [(0, 5), (6, 1), (3, 3)]:
+        z = np.zeros((T, N))
+        k = z.copy(); k[0, i] = 1.0
+        v = z.copy(); v[0, j] = 1.0
+        r = np.arange(1, N + 1, dtype=np.float64)[None]
+        o, s = _one_head(oracle_mod, r, np.ones((T, N)), k, v, z, z, None)
+        expect = np.zeros((N, N)); expect[i, j] = 1.0
+        assert np.array_equal(s, expect)               # row = key channel, column = value channel
+        eo = np.zeros(N); eo[j] = r[0, i]
+        assert np.array_equal(o[0], eo)                # o = S^T r
+
+
+# --- I1: linear attention ---------------------------------------------------------
+
+def test_linear_attention_closed_form(oracle_mod):
+    rng = np.random.default_rng(1)
+    T, N = 37, 64
+    r, k, v = (rng.standard_normal((T, N)) for _ in range(3))
+    S0 = rng.standard_normal((N, N))
+    z = np.zeros((T, N))
+    o, s = _one_head(oracle_mod, r, np.ones((T, N)), k, v, z, z, S0)
+    eo, es = routes.linear_attention(r, k, v, S0)
+    assert _rel(o, eo) < 1e-13 and _rel(s, es) < 1e-13
+
+
+# --- I2: pure decay -----------------------------------------------------------
+
+def test_pure_decay_closed_form(oracle_mod):
+    rng = np.random.default_rng(2)
+    T, N = 20, 64
+    r, k, v = (rng.standard_normal((T, N)) for _ in range(3))
+    w = rng.uniform(0.3, 1.0, (T, N))
+    S0 = rng.standard_normal((N, N))
+    z = np.zeros((T, N))
+    o, s = _one_head(oracle_mod, r, w, k, v, z, z, S0)
+    eo, es = routes.pure_decay(r, w, k, v, S0)
+    assert _rel(o, eo) < 1e-13 and _rel(s, es) < 1e-13
+
+
+def test_pure_decay_constant_w_power(oracle_mod):
+    rng = np.random.default_rng(3)
+    T, N = 50, 16
+    wrow = rng.uniform(0.5, 1.0, N)
+    w = np.tile(wrow, (T, 1))
+    S0 = rng.standard_normal((N, N))
+    z = np.zeros((T, N))
+    _, s = _one_head(oracle_mod, z, w, z, z, z, z, S0)
+    expect = (wrow ** T)[:, None] * S0           # decay acts on rows (key channels)
+    assert _rel(s, expect) < 1e-13
+
+
+# --- I3: projection (w = 1, gate = 1, unit kk) ------------------------------------
+
+def _unit(rng, N):
+    x = rng.standard_normal(N)
+    return x / np.linalg.norm(x)
+
+
+def test_projection_idempotent(oracle_mod):
+    rng = np.random.default_rng(4)
+    N = 64
+    kk = _unit(rng, N)
+    S0 = rng.standard_normal((N, N))
+    one = np.ones((1, N)); z = np.zeros((1, N))
+    _, s1 = _one_head(oracle_mod, z, one, z, z, -kk[None], kk[None], S0)
+    z2 = np.zeros((2, N))
+    _, s2 = _one_head(oracle_mod, z2, np.ones((2, N)), z2, z2, np.tile(-kk, (2, 1)),
+                      np.tile(kk, (2, 1)), S0)
+    P = np.eye(N) - np.outer(kk, kk)
+    assert _rel(s1, P @ S0) < 1e-13
+    assert _rel(s2, s1) < 1e-13                  # P^2 = P
+
+
+def test_delta_rule_recall(oracle_mod):
+    # S' = (I - kk kk^T) S + kk v^T  =>  kk^T S' = v^T, so reading with r = kk returns v.
+    rng = np.random.default_rng(5)
+    N = 64
+    kk = _unit(rng, N)
+    v = rng.standard_normal(N)
+    S0 = rng.standard_normal((N, N))
+    o, _ = _one_head(oracle_mod, kk[None], np.ones((1, N)), kk[None], v[None], -kk[None], kk[None], S0)
+    assert np.max(np.abs(o[0] - v)) < 1e-12
+
+
+@pytest.mark.parametrize("g", [0.0, 0.3, 0.7, 1.0])
+def test_projection_contracts(oracle_mod, g):
+    rng = np.random.default_rng(6)
+    N = 64
+    kk = _unit(rng, N)
+    S0 = rng.standard_normal((N, N))
+    z = np.zeros((1, N))
+    _, s = _one_head(oracle_mod, z, np.ones((1, N)), z, z, -kk[None], g * kk[None], S0)
+    assert np.linalg.norm(s) <= np.linalg.norm(S0) * (1 + 1e-14)
+    assert _rel(s, (np.eye(N) - g * np.outer(kk, kk)) @ S0) < 1e-13
+
+
+# --- I6: dense brute force -----------------------------------------------------
+
+@pytest.mark.parametrize("N,T", [(2, 8), (4, 7), (64, 8)])
+def test_dense_bruteforce(oracle_mod, N, T):
+    rng = np.random.default_rng(7 + N)
+    r, w, k, v, a, b, S0 = _rand_head(rng, T, N, w_lo=0.0, w_hi=1.0)
+    # independent a and b (not tied to kk) so the rank-1 term is general
+    a = rng.standard_normal((T, N)) * 0.3
+    b = rng.standard_normal((T, N)) * 0.3
+    o, s, sp = _one_head(oracle_mod, r, w, k, v, a, b, S0, per_position=True)
+    eo, es, estates = routes.dense_bruteforce(r, w, k, v, a, b, S0)
+    assert _rel(o, eo) < 1e-13 and _rel(s, es) < 1e-13 and _rel(sp, estates) < 1e-13
+
+
+# --- I5: step form == chunked-parallel form -----------------------------------------
+
+@pytest.mark.parametrize("C", [1, 3, 16, 64, 100])
+def test_chunk_form_equals_loop(oracle_mod, C):
+    rng = np.random.default_rng(8)
+    T, N = 100, 64
+    r, w, k, v, a, b, S0 = _rand_head(rng, T, N)
+    o, s = _one_head(oracle_mod, r, w, k, v, a, b, S0)
+    eo, es = routes.chunk_form(r, w, k, v, a, b, S0, C)
+    assert _rel(o, eo) < 1e-12 and _rel(s, es) < 1e-12
+
+
+# --- I4: split-T state carry is bit-exact ----------------------------------------
+
+@pytest.mark.parametrize("split", [0, 1, 17, 33, 34])
+def test_split_T_bit_exact(oracle_mod, split):
+    rng = np.random.default_rng(9)
+    B, T, H, N = 2, 34, 3, 64
+    ins = [rng.standard_normal((B, T, H, N)).astype(np.float32) for _ in range(6)]
+    ins[1] = rng.uniform(0.55, 1.0, (B, T, H, N)).astype(np.float32)
+    S0 = rng.standard_normal((B, H, N, N)) * 0.1
+    o, s = oracle_mod.forward(*ins, S0)
+    o1, s1 = oracle_mod.forward(*[x[:, :split] for x in ins], S0)
+    o2, s2 = oracle_mod.forward(*[x[:, split:] for x in ins], s1)
+    assert np.array_equal(np.concatenate([o1, o2], axis=1), o)
+    assert np.array_equal(s2, s)
+
+
+def test_per_position_states_match_prefixes(oracle_mod):
+    rng = np.random.default_rng(10)
+    B, T, H, N = 2, 5, 3, 64
+    ins = [rng.standard_normal((B, T, H, N)).astype(np.float32) for _ in range(6)]
+    S0 = rng.standard_normal((B, H, N, N)) * 0.1
+    o, s, sp = oracle_mod.forward(*ins, S0, per_position=True)
+    assert np.array_equal(sp[:, T - 1], s)
+    for t in range(T):
+        _, st = oracle_mod.forward(*[x[:, :t + 1] for x in ins], S0)
+        assert np.array_equal(sp[:, t], st)
+
+
+# --- I8: linearity in (v, S0) and value-column separability ---------------------------
+
+def test_linearity_in_v_and_state(oracle_mod):
+    rng = np.random.default_rng(11)
+    T, N = 12, 64
+    r, w, k, v1, a, b, S1 = _rand_head(rng, T, N)
+    v2 = rng.standard_normal((T, N))
+    S2 = rng.standard_normal((N, N))
+    al, be = 0.75, -1.5
+    o1, s1 = _one_head(oracle_mod, r, w, k, v1, a, b, S1)
+    o2, s2 = _one_head(oracle_mod, r, w, k, v2, a, b, S2)
+    o3, s3 = _one_head(oracle_mod, r, w, k, al * v1 + be * v2, a, b, al * S1 + be * S2)
+    assert _rel(o3, al * o1 + be * o2) < 1e-12 and _rel(s3, al * s1 + be * s2) < 1e-12
+
+
+def test_value_column_permutation(oracle_mod):
+    rng = np.random.default_rng(12)
+    T, N = 12, 64
+    r, w, k, v, a, b, S0 = _rand_head(rng, T, N)
+    p = rng.permutation(N)
+    o, s = _one_head(oracle_mod, r, w, k, v, a, b, S0)
+    op, sp = _one_head(oracle_mod, r, w, k, v[:, p], a, b, S0[:, p])
+    assert np.array_equal(op, o[:, p]) and np.array_equal(sp, s[:, p])
+
+
+# --- I9: zeros, empty, and sensitivity to every input -----------------------------------
+
+def test_zero_values_and_state_give_zero(oracle_mod):
+    rng = np.random.default_rng(13)
+    T, N = 9, 64
+    r, w, k, _, a, b, _ = _rand_head(rng, T, N)
+    o, s = _one_head(oracle_mod, r, w, k, np.zeros((T, N)), a, b, np.zeros((N, N)))
+    assert not np.any(o) and not np.any(s)
+
+
+def test_empty_sequence_passes_state_through(oracle_mod):
+    rng = np.random.default_rng(14)
+    B, H, N = 2, 3, 64
+    e = np.zeros((B, 0, H, N), np.float32)
+    S0 = rng.standard_normal((B, H, N, N))
+    o, s = oracle_mod.forward(e, e, e, e, e, e, S0)
+    assert o.shape == (B, 0, H, N) and np.array_equal(s, S0)
+    _, s0 = oracle_mod.forward(e, e, e, e, e, e, None)
+    assert not np.any(s0)
+
+
+@pytest.mark.parametrize("which", ["r", "w", "k", "v", "a", "b", "S0"])
+def test_every_input_matters(oracle_mod, which):
+    rng = np.random.default_rng(15)
+    T, N = 4, 64
+    r, w, k, v, a, b, S0 = _rand_head(rng, T, N)
+    args = dict(r=r, w=w, k=k, v=v, a=a, b=b, S0=S0)
+    o, s = _one_head(oracle_mod, **args)
+    x = args[which].copy()
+    x.flat[rng.integers(x.size)] += 0.5
+    args[which] = x
+    o2, s2 = _one_head(oracle_mod, **args)
+    changed = not np.array_equal(o, o2) or not np.array_equal(s, s2)
+    assert changed
