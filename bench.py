@@ -1,0 +1,300 @@
+#!/usr/bin/env python3
+"""Benchmark of libwkv7 on one MI355X: decode-step us/layer and prefill Mtok/s.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1|2|3|4] [--no-cpu-baseline]
+
+Prints ONE JSON line.  The headline workload (default) is the 2.9B-shaped
+decode step (B=32, T=1, H=40, N=64, bf16 inputs, fp32 state), one layer per
+call over 32 distinct layer buffer sets, state updated in place: a timed
+"step" is one sweep over the 32 layers, replayed from a captured HIP graph.
+``value`` is microseconds per layer.  The same line carries the roofline of
+the dominant kernel (live HIP-event timing; HBM traffic from committed
+rocprofv3 counter summaries when they were taken on the current kernel
+source), the fp64 CPU oracle timed on a bounded sample of the same workload,
+and (default run) the prefill and verify workloads measured the same way.
+
+Workloads (all synthetic, seeded; see synth/):
+  1 decode-2.9B       B=32 T=1    H=40  step kernel, 32 layers, in place
+  2 prefill-0.1B      B=8  T=4096 H=12  chunked kernel, one call
+  3 prefill-7.2B      B=4  T=8192 H=64  chunked kernel, one call, state carried in
+  4 mtp-verify-13.3B  B=16 T=5    H=64  step kernel + per-position states, 61 layers
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix, published
+N = 64
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "rwkv_linear_attention_amd", "csrc")
+
+
+def algorithmic_bytes(wl, kind: str) -> int:
+    """Bytes the method must move per call: inputs once, o once (fp32), state read and written once,
+    plus per-position states for the verify step."""
+    e_in = 2 if wl.dtype == "bf16" else 4
+    tokheads = wl.B * wl.T * wl.H
+    b = tokheads * (6 * N * e_in + 4 * N)
+    b += 2 * wl.B * wl.H * N * N * 4 if (wl.state_std > 0 or kind == "step") else wl.B * wl.H * N * N * 4
+    if kind == "verify":
+        b += tokheads * N * N * 4
+    return b
+
+
+def recurrent_flops(wl) -> int:
+    return wl.B * wl.T * wl.H * 9 * N * N
+
+
+def kernel_source_hash(kind: str) -> str:
+    name = {"step": "wkv7_step.hip", "verify": "wkv7_step.hip", "chunk": "wkv7_chunk.hip"}[kind]
+    h = hashlib.sha256()
+    for f in (name, "wkv7_device.h"):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kind: str, workload: int):
+    """HBM bytes per launch from profiles/hbm_traffic.txt, or None when absent or stale.
+
+    Lines: <kernel-kind> <workload> <source-hash> <fetch_bytes> <write_bytes>
+    (bytes already scaled by the copy-kernel calibration factor).
+    """
+    path = os.path.join(PROFILES, "hbm_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    cur = kernel_source_hash(kind)
+    with open(path) as f:
+        for line in f:
+            parts = line.split()
+            if len(parts) == 5 and not line.startswith("#") and parts[0] == kind and parts[1] == str(workload):
+                if parts[2] != cur:
+                    return None
+                return int(float(parts[3]) + float(parts[4]))
+    return None
+
+
+def roofline(bytes_per_launch: int, sec_per_launch: float, kind: str, workload: int):
+    ach = bytes_per_launch / sec_per_launch / 1e9
+    return {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": read_traffic(kind, workload)}
+
+
+# ----------------------------------------------------------------------------- GPU timing
+
+def make_layers(K, synth, idx: int, nlayers: int):
+    """nlayers distinct buffer sets of workload idx on the GPU (inputs, state, outputs)."""
+    import torch
+    wl = synth.WORKLOADS[idx]
+    sets = []
+    for l in range(nlayers):
+        inp = synth.workload_inputs(idx, seed_offset=1000 * l)
+        d = {n: inp[n].cuda() for n in ("r", "w", "k", "v", "a", "b")}
+        d["state"] = inp["state_in"].cuda()
+        d["o"] = torch.empty((wl.B, wl.T, wl.H, N), dtype=torch.float32, device="cuda")
+        d["pos"] = torch.empty((wl.B, wl.T, wl.H, N, N), dtype=torch.float32, device="cuda") if idx == 4 else None
+        sets.append(d)
+    return sets
+
+
+def sweep(K, sets):
+    for d in sets:
+        K.wkv7_step(d["r"], d["w"], d["k"], d["v"], d["a"], d["b"], d["state"], o=d["o"], state_out=d["state"],
+                    state_pos=d["pos"])
+
+
+def time_step_workload(K, synth, idx: int, steps: int, warmup: int):
+    """Graph-captured sweeps over the layer sets; returns dict of timings."""
+    import torch
+    wl = synth.WORKLOADS[idx]
+    sets = make_layers(K, synth, idx, wl.layers)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        sweep(K, sets)                      # eager warm-up (loads the code objects)
+        # graph replay must reproduce the eager result bit for bit
+        saved = [d["state"].clone() for d in sets]
+        sweep(K, sets)
+        eager = [d["state"].clone() for d in sets] + [d["o"].clone() for d in sets]
+        for d, s in zip(sets, saved):
+            d["state"].copy_(s)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            sweep(K, sets)
+        for d, s in zip(sets, saved):
+            d["state"].copy_(s)
+        g.replay()
+        torch.cuda.synchronize()
+        replay = [d["state"] for d in sets] + [d["o"] for d in sets]
+        if not all(torch.equal(a, b) for a, b in zip(eager, replay)):
+            raise RuntimeError("graph replay differs from the eager sweep")
+        for _ in range(warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            g.replay()
+        e1.record(stream)
+        e1.synchronize()
+    ms = e0.elapsed_time(e1)
+    per_layer_s = ms / 1e3 / (steps * wl.layers)
+    return {"ms_per_step": ms / steps, "us_per_layer": per_layer_s * 1e6, "sec_per_launch": per_layer_s,
+            "layers": wl.layers}
+
+
+def time_prefill_workload(K, synth, idx: int, steps: int, warmup: int):
+    import torch
+    wl = synth.WORKLOADS[idx]
+    d = synth.workload_inputs(idx, device="cuda")
+    o = torch.empty((wl.B, wl.T, wl.H, N), dtype=torch.float32, device="cuda")
+    s_out = torch.empty((wl.B, wl.H, N, N), dtype=torch.float32, device="cuda")
+    args = [d[n] for n in ("r", "w", "k", "v", "a", "b")]
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        for _ in range(max(1, warmup)):
+            K.wkv7_forward(*args, d["state_in"], o=o, state_out=s_out)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            K.wkv7_forward(*args, d["state_in"], o=o, state_out=s_out)
+        e1.record(stream)
+        e1.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    return {"ms_per_step": ms, "sec_per_launch": ms / 1e3, "mtok_s": wl.B * wl.T / (ms / 1e3) / 1e6}
+
+
+# ----------------------------------------------------------------------------- CPU baseline
+
+def cpu_baseline(synth, idx: int, budget_s: float = 12.0):
+    """The fp64 oracle, as it stands, on a bounded sample of the headline workload."""
+    import oracle
+    wl = synth.WORKLOADS[idx]
+    threads = min(16, len(os.sched_getaffinity(0)))
+    inp = synth.workload_inputs(idx)
+    args = [inp[n] for n in ("r", "w", "k", "v", "a", "b")]
+    oracle.forward(*args, inp["state_in"], nthreads=threads)  # load + warm
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.forward(*args, inp["state_in"], nthreads=threads, per_position=(idx == 4))
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    per_layer_us = el / reps * 1e6
+    return {"value": round(per_layer_us, 1), "unit": "us/layer", "cores": threads, "kind": "oracle",
+            "sample": f"{reps} calls of one full layer of workload {idx} ({wl.B}x{wl.T}x{wl.H} token-heads), "
+                      f"{el:.1f} s wall"}
+
+
+def cpu_baseline_prefill(synth, idx: int, budget_s: float = 8.0):
+    import oracle
+    wl = synth.WORKLOADS[idx]
+    threads = min(16, len(os.sched_getaffinity(0)))
+    Ts = 256
+    inp = synth.make_inputs(wl.B, Ts, wl.H, N, seed=wl.seed, dtype=wl.dtype, sigma_w=wl.sigma_w,
+                            state_std=wl.state_std)
+    args = [inp[n] for n in ("r", "w", "k", "v", "a", "b")]
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.forward(*args, inp["state_in"], nthreads=threads)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    return {"value": round(wl.B * Ts * reps / el / 1e6, 4), "unit": "Mtok/s", "cores": threads, "kind": "oracle",
+            "sample": f"{reps} calls over the first {Ts} tokens of workload {idx}, {el:.1f} s wall"}
+
+
+# ----------------------------------------------------------------------------- main
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=1, choices=[1, 2, 3, 4])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", action="store_true", help="measure the chosen workload only")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: the WKV-7 kernels here are measured on one MI355X "
+              f"(--gpus {args.gpus} is not supported; heads shard across GPUs with no exchange).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import rwkv_linear_attention_amd as K
+    K.lib()
+    if not torch.cuda.is_available():
+        raise SystemExit("no GPU visible")
+
+    def measure(idx):
+        wl = synth.WORKLOADS[idx]
+        if idx in (1, 4):
+            kind = "step" if idx == 1 else "verify"
+            t = time_step_workload(K, synth, idx, args.steps, args.warmup)
+            rl = roofline(algorithmic_bytes(wl, kind), t["sec_per_launch"], kind, idx)
+            return t, rl
+        t = time_prefill_workload(K, synth, idx, max(3, args.steps // 4), max(1, args.warmup // 2))
+        rl = roofline(algorithmic_bytes(wl, "chunk"), t["sec_per_launch"], "chunk", idx)
+        return t, rl
+
+    idx = args.workload
+    wl = synth.WORKLOADS[idx]
+    t, rl = measure(idx)
+    if idx in (1, 4):
+        metric_value, unit, hib = t["us_per_layer"], "us/layer", False
+    else:
+        metric_value, unit, hib = t["mtok_s"], "Mtok/s", True
+
+    line = {
+        "metric": "WKV-7 prefill Mtok/s & decode-step µs per layer; % of HBM/MFMA roofline",
+        "value": round(metric_value, 3),
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": args.steps if idx in (1, 4) else max(3, args.steps // 4),
+        "warmup": args.warmup,
+        "ms_per_step": round(t["ms_per_step"], 4),
+        "higher_is_better": hib,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "T": wl.T, "H": wl.H, "N": N, "inputs": wl.dtype,
+                   "state": "fp32", "layers_per_step": wl.layers, "parallelism": "single-gpu"},
+        "roofline": rl,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = (cpu_baseline(synth, idx) if idx in (1, 4) else cpu_baseline_prefill(synth, idx))
+    if not args.only:
+        others = {}
+        for j in (1, 2, 3, 4):
+            if j == idx:
+                continue
+            tj, rj = measure(j)
+            wj = synth.WORKLOADS[j]
+            entry = {"workload": wj.name, "ms_per_call": round(tj["sec_per_launch"] * 1e3, 4), "roofline": rj}
+            if j in (1, 4):
+                entry["us_per_layer"] = round(tj["us_per_layer"], 3)
+            else:
+                entry["mtok_s"] = round(tj["mtok_s"], 2)
+                entry["alg_flops_frac_bf16"] = round(recurrent_flops(wj) / tj["sec_per_launch"] / 1e12
+                                                     / PEAK_BF16_TFLOPS, 5)
+            others[str(j)] = entry
+        line["other_workloads"] = others
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

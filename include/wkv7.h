@@ -1,0 +1,140 @@
+/*
+ * wkv7.h -- libwkv7: the WKV-7 recurrence (RWKV-7 "generalized delta rule")
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * THE OPERATION.  Per batch row b and head h the library carries an N x N fp32
+ * state S (N = 64).  Row i of S is a key channel, column j a value channel
+ * (S = [K,V], as in the Core AI RWKV-7 note, section 1, and the head_size x
+ * head_size state of the RWKV-X Architecture page, section "WKV-7 Kernel
+ * (Generalized Delta Rule)").  For each token t:
+ *
+ *     sa[j]   = sum_i a_t[i] * S[i][j]                 (state before the step)
+ *     S[i][j] = w_t[i]*S[i][j] + b_t[i]*sa[j] + k_t[i]*v_t[j]
+ *     o_t[j]  = sum_i r_t[i] * S[i][j]                 (state after the step)
+ *
+ * i.e. S_t = diag(w_t) S_{t-1} + b_t (a_t^T S_{t-1}) + k_t v_t^T, o_t = S_t^T r_t.
+ * RWKV-7 feeds a = -kk and b = kk*a_gate (the Core AI note writes the rank-1
+ * term as -(kk*a)(kk^T S)); the library takes a and b as two general vectors.
+ * w is the decay MULTIPLIER (RWKV-7 keeps it in (0.545, 1)), not its log.
+ *
+ * The SwiftRWKV Inference guide describes the two passes this library
+ * provides: a parallel pass over a whole prompt (wkv7_forward, prefill) and a
+ * recurrent pass one token at a time (wkv7_step, decode).  They compute the
+ * same function and differ only in summation order.  wkv7_step also serves the
+ * verify pass of speculative decoding (RWKV7-MTP-Exp model card, section
+ * "Inference": the base model runs [t, d1..dK] in one forward and its recurrent
+ * state is rolled back to the accepted prefix), for which it can emit the
+ * state after every position.
+ *
+ * LAYOUTS (all row-major, contiguous, no padding):
+ *   r, w, k, v, a, b, o : [B, T, H, N]      element (b,t,h,n) at ((b*T+t)*H+h)*N+n
+ *   state_in, state_out : [B, H, N, N] fp32 element (b,h,i,j) at ((b*H+h)*N+i)*N+j
+ *   state_pos           : [B, T, H, N, N] fp32, [b,t,h] = S after token t
+ *
+ * MEMORY.  Every pointer is a DEVICE pointer on the current HIP device,
+ * 16-byte aligned.  The caller owns every buffer; the library never
+ * allocates, frees or synchronises, and keeps no global mutable state.
+ *
+ * ASYNCHRONY.  Calls enqueue on `stream` (a hipStream_t; NULL = the default
+ * stream) and return.  Argument errors are detected before any HIP call and
+ * reported synchronously; nothing is enqueued then.  WKV7_ERR_HIP reports a
+ * failed launch; faults inside a kernel surface at the caller's next
+ * synchronisation.
+ *
+ * ALIASING.  state_out may equal state_in exactly (update in place).  Any
+ * other overlap between an output (o, state_out, state_pos) and any other
+ * buffer of the call is refused with WKV7_ERR_ALIAS.
+ *
+ * NUMERICS.  The state and every accumulation are fp32.  bf16 inputs are
+ * widened exactly.  NaN / Inf propagate as the arithmetic dictates.  Results
+ * match an fp64 evaluation of the definition to a relative L2 error of about
+ * 1e-6 (fp32 inputs) and well under 2e-3 (bf16 inputs, fp32 state).
+ */
+#ifndef WKV7_H
+#define WKV7_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define WKV7_ABI_VERSION 1
+
+/* Element types of r, w, k, v, a, b (in_dtype) and of o (o_dtype). */
+enum wkv7_dtype {
+    WKV7_F32 = 0,  /* IEEE binary32 */
+    WKV7_BF16 = 1  /* bfloat16; o is rounded to nearest even when requested */
+};
+
+/* Return codes.  Every entry point returns one of these. */
+enum wkv7_status {
+    WKV7_OK = 0,
+    WKV7_ERR_NULL = -1,        /* a required pointer is NULL                          */
+    WKV7_ERR_SHAPE = -2,       /* B, H < 1, T < 0, or a size overflows int64          */
+    WKV7_ERR_UNSUPPORTED = -3, /* N != 64, or an unknown dtype                         */
+    WKV7_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned                     */
+    WKV7_ERR_ALIAS = -5,       /* an output overlaps another buffer (see ALIASING)     */
+    WKV7_ERR_HIP = -6          /* the HIP runtime refused a launch or a query          */
+};
+
+/*
+ * wkv7_forward -- the parallel (prefill) pass over T tokens.
+ *
+ *   r, w, k, v, a, b : [B,T,H,N] inputs of type in_dtype (WKV7_F32 | WKV7_BF16).
+ *   state_in         : [B,H,N,N] fp32 state entering token 0; NULL = all zeros.
+ *   o                : [B,T,H,N] outputs of type o_dtype (WKV7_F32 | WKV7_BF16).
+ *   state_out        : [B,H,N,N] fp32 state after token T-1 (may == state_in).
+ *   B, T, H, N       : batch, tokens, heads, head size (N must be 64).
+ *   stream           : hipStream_t to enqueue on, or NULL.
+ *
+ * Long sequences run a chunked-parallel kernel (chunks of 16 tokens, a
+ * triangular solve for the rank-1 terms inside a chunk, matrix-core products,
+ * and the state carried from chunk to chunk in order); short ones run the
+ * step kernel.  T = 0 copies state_in to state_out (zeros if state_in is NULL)
+ * and leaves o untouched.  Decays below 2^-15 are raised to 2^-15 by the
+ * chunked kernel (an absolute change of at most 3.1e-5 in that step's
+ * multiplier); RWKV-7's decays never come near that bound.
+ */
+int wkv7_forward(const void *r, const void *w, const void *k, const void *v,
+                 const void *a, const void *b, int in_dtype,
+                 const float *state_in, void *o, int o_dtype, float *state_out,
+                 int B, int T, int H, int N, void *stream);
+
+/*
+ * wkv7_step -- the recurrent (decode / speculative-verify) pass, token by token.
+ *
+ * Arguments as for wkv7_forward, plus
+ *   state_pos : [B,T,H,N,N] fp32, or NULL.  When given, state_pos[b,t,h] is the
+ *               state after token t, so a caller can keep the state after any
+ *               accepted prefix of a speculative step (state_pos[:,T-1] equals
+ *               state_out).
+ * Meant for small T (1 for decode, K+1 for a verify step), but correct for
+ * any T >= 0.  Exact for every decay in [0, 1].
+ */
+int wkv7_step(const void *r, const void *w, const void *k, const void *v,
+              const void *a, const void *b, int in_dtype,
+              const float *state_in, void *o, int o_dtype, float *state_out,
+              float *state_pos, int B, int T, int H, int N, void *stream);
+
+/*
+ * wkv7_state_reset -- zero the recurrent state (the RWKV-X Architecture page,
+ * section "Dual State": a reset zeros the recurrent state).
+ *
+ *   state    : [B,H,N,N] fp32.
+ *   row_mask : [B] bytes on the device, or NULL.  NULL zeros every batch row;
+ *              otherwise row b is zeroed iff row_mask[b] != 0 and the other rows
+ *              are left untouched.  (The mask itself needs no alignment.)
+ */
+int wkv7_state_reset(float *state, int B, int H, int N, const unsigned char *row_mask,
+                     void *stream);
+
+/* A static, human-readable name for a status code (never NULL). */
+const char *wkv7_status_string(int status);
+
+/* WKV7_ABI_VERSION of the built library. */
+int wkv7_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WKV7_H */

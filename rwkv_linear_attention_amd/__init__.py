@@ -1,0 +1,182 @@
+"""libwkv7 for MI355X: the WKV-7 recurrence (RWKV-7 generalized delta rule) on gfx950.
+
+A thin ctypes binding over the C ABI of ``libwkv7.so`` (declared in
+``include/wkv7.h``).  This module only marshals arguments: it checks device,
+dtype, shape and contiguity of torch tensors, passes their device pointers and
+the current HIP stream, and raises on a nonzero status.  Every step of the
+computation runs in the HIP kernels of the library; there is no CPU or
+PyTorch fallback, and the calls fail loudly when the library is not built.
+
+Functions (names as in the C ABI):
+
+* ``wkv7_forward(r, w, k, v, a, b, state_in=None, o_dtype=torch.float32)``
+  -> ``(o, state_out)``: the parallel (prefill) pass.
+* ``wkv7_step(r, w, k, v, a, b, state_in=None, per_position=False, ...)``
+  -> ``(o, state_out[, state_pos])``: the recurrent (decode / verify) pass.
+* ``wkv7_state_reset(state, row_mask=None)``: zero the state (all rows or masked ones).
+
+Tensors: r, w, k, v, a, b are [B, T, H, 64] bf16 or fp32 on the GPU; the
+state is [B, H, 64, 64] fp32 with row i a key channel and column j a value
+channel.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libwkv7.so")
+
+WKV7_F32, WKV7_BF16 = 0, 1
+HEAD_SIZE = 64
+_lib = None
+
+
+class Wkv7Error(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+def build() -> str:
+    """Compile libwkv7.so in-tree for gfx950 (always recompiles)."""
+    from . import _build
+    global _lib
+    _lib = None
+    return _build.build()
+
+
+def lib():
+    """The loaded C library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it first "
+                               "(python -c 'import __graft_entry__ as g; g.build()')")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, ci = ctypes.c_void_p, ctypes.c_int
+        L.wkv7_forward.argtypes = [vp] * 6 + [ci, vp, vp, ci, vp, ci, ci, ci, ci, vp]
+        L.wkv7_forward.restype = ci
+        L.wkv7_step.argtypes = [vp] * 6 + [ci, vp, vp, ci, vp, vp, ci, ci, ci, ci, vp]
+        L.wkv7_step.restype = ci
+        L.wkv7_state_reset.argtypes = [vp, ci, ci, ci, vp, vp]
+        L.wkv7_state_reset.restype = ci
+        L.wkv7_status_string.argtypes = [ci]
+        L.wkv7_status_string.restype = ctypes.c_char_p
+        L.wkv7_abi_version.argtypes = []
+        L.wkv7_abi_version.restype = ci
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().wkv7_status_string(int(status)).decode()
+
+
+def _check(status: int):
+    if status != 0:
+        raise Wkv7Error(status, status_string(status))
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return WKV7_BF16
+    if t.dtype == torch.float32:
+        return WKV7_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bf16 or fp32 only)")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check_inputs(r, w, k, v, a, b):
+    ins = (r, w, k, v, a, b)
+    if r.dim() != 4:
+        raise ValueError(f"inputs must be [B, T, H, N], got {tuple(r.shape)}")
+    for x in ins:
+        if not x.is_cuda:
+            raise ValueError("inputs must be on the GPU")
+        if x.shape != r.shape or x.dtype != r.dtype or x.device != r.device:
+            raise ValueError("r, w, k, v, a, b must share shape, dtype and device")
+        if not x.is_contiguous():
+            raise ValueError("inputs must be contiguous")
+    return r.shape
+
+
+def _state_arg(state, B, H, N, device, name):
+    if state is None:
+        return None
+    if (state.dtype != torch.float32 or tuple(state.shape) != (B, H, N, N) or not state.is_contiguous()
+            or state.device != device):
+        raise ValueError(f"{name} must be a contiguous fp32 [{B}, {H}, {N}, {N}] tensor on {device}")
+    return state
+
+
+def wkv7_forward(r, w, k, v, a, b, state_in=None, *, o_dtype=torch.float32, o=None, state_out=None):
+    """Parallel pass over the whole sequence.  Returns (o, state_out).
+
+    state_out may be passed as state_in itself to update the state in place.
+    """
+    B, T, H, N = _check_inputs(r, w, k, v, a, b)
+    dev = r.device
+    state_in = _state_arg(state_in, B, H, N, dev, "state_in")
+    if state_out is None:
+        state_out = torch.empty((B, H, N, N), dtype=torch.float32, device=dev)
+    _state_arg(state_out, B, H, N, dev, "state_out")
+    if o is None:
+        o = torch.empty((B, T, H, N), dtype=o_dtype, device=dev)
+    if o.shape != r.shape or not o.is_contiguous() or o.device != dev:
+        raise ValueError("o must be a contiguous [B, T, H, N] tensor on the inputs' device")
+    _check(lib().wkv7_forward(*[_ptr(x) for x in (r, w, k, v, a, b)], _dt(r), _ptr(state_in), _ptr(o),
+                              _dt(o), _ptr(state_out), B, T, H, N, _stream(dev)))
+    return o, state_out
+
+
+def wkv7_step(r, w, k, v, a, b, state_in=None, *, per_position=False, o_dtype=torch.float32, o=None,
+              state_out=None, state_pos=None):
+    """Recurrent pass, token by token.  Returns (o, state_out) or (o, state_out, state_pos).
+
+    With per_position=True, state_pos[:, t] is the state after token t.
+    """
+    B, T, H, N = _check_inputs(r, w, k, v, a, b)
+    dev = r.device
+    state_in = _state_arg(state_in, B, H, N, dev, "state_in")
+    if state_out is None:
+        state_out = torch.empty((B, H, N, N), dtype=torch.float32, device=dev)
+    _state_arg(state_out, B, H, N, dev, "state_out")
+    if o is None:
+        o = torch.empty((B, T, H, N), dtype=o_dtype, device=dev)
+    if per_position and state_pos is None:
+        state_pos = torch.empty((B, T, H, N, N), dtype=torch.float32, device=dev)
+    if state_pos is not None and (tuple(state_pos.shape) != (B, T, H, N, N) or state_pos.dtype != torch.float32
+                                  or not state_pos.is_contiguous()):
+        raise ValueError("state_pos must be a contiguous fp32 [B, T, H, N, N] tensor")
+    _check(lib().wkv7_step(*[_ptr(x) for x in (r, w, k, v, a, b)], _dt(r), _ptr(state_in), _ptr(o), _dt(o),
+                           _ptr(state_out), _ptr(state_pos), B, T, H, N, _stream(dev)))
+    if state_pos is not None:
+        return o, state_out, state_pos
+    return o, state_out
+
+
+def wkv7_state_reset(state, row_mask=None):
+    """Zero state [B, H, 64, 64] in place; with row_mask ([B] bool/uint8) only the flagged rows."""
+    if state.dim() != 4 or not state.is_cuda or state.dtype != torch.float32 or not state.is_contiguous():
+        raise ValueError("state must be a contiguous fp32 [B, H, N, N] GPU tensor")
+    B, H, N, _ = state.shape
+    if row_mask is not None:
+        row_mask = row_mask.to(device=state.device, dtype=torch.uint8).contiguous()
+        if row_mask.shape != (B,):
+            raise ValueError(f"row_mask must have shape [{B}]")
+    _check(lib().wkv7_state_reset(_ptr(state), B, H, N, _ptr(row_mask), _stream(state.device)))
+    return state
+
+
+def abi_version() -> int:
+    return int(lib().wkv7_abi_version())

@@ -1,0 +1,195 @@
+// wkv7_api.hip -- the C ABI of libwkv7 (declared in include/wkv7.h).
+//
+// Every argument is validated here, before any HIP call, so each error path
+// can be exercised without a GPU.  The entry points only enqueue work on the
+// caller's stream: no allocation, no synchronisation, no global state.
+#include <stdint.h>
+
+#include "../../include/wkv7.h"
+#include "wkv7_launch.h"
+
+namespace {
+
+using wkv7::SeqArgs;
+
+constexpr int64_t kN = 64;
+// Sequences shorter than this go to the step kernel in wkv7_forward.
+constexpr int kChunkMinT = 9;
+
+struct Range {
+    uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range range_of(const void *p, int64_t bytes)
+{
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    return Range{lo, lo + static_cast<uintptr_t>(bytes)};
+}
+
+bool overlap(const Range &x, const Range &y)
+{
+    return x.lo < y.hi && y.lo < x.hi && x.hi > x.lo && y.hi > y.lo;
+}
+
+bool misaligned(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+// B*T*H*N*N must fit in int64 (and every partial product with it).
+bool shape_ok(int B, int T, int H, int64_t *tokens_out)
+{
+    if (B < 1 || H < 1 || T < 0)
+        return false;
+    const int64_t lim = INT64_MAX / (kN * kN * 8);
+    const int64_t bh = static_cast<int64_t>(B) * H;
+    if (T > 0 && bh > lim / T)
+        return false;
+    *tokens_out = bh * T;
+    return true;
+}
+
+int check_seq(const void *r, const void *w, const void *k, const void *v, const void *a, const void *b,
+              int in_dtype, const float *state_in, void *o, int o_dtype, float *state_out, float *state_pos,
+              int B, int T, int H, int N)
+{
+    int64_t tok = 0;
+    if (N != kN)
+        return WKV7_ERR_UNSUPPORTED;
+    if ((in_dtype != WKV7_F32 && in_dtype != WKV7_BF16) || (o_dtype != WKV7_F32 && o_dtype != WKV7_BF16))
+        return WKV7_ERR_UNSUPPORTED;
+    if (!shape_ok(B, T, H, &tok))
+        return WKV7_ERR_SHAPE;
+    if (!state_out)
+        return WKV7_ERR_NULL;
+    if (T > 0 && (!r || !w || !k || !v || !a || !b || !o))
+        return WKV7_ERR_NULL;
+    const void *ptrs[] = {r, w, k, v, a, b, o, state_in, state_out, state_pos};
+    for (const void *ptr : ptrs)
+        if (ptr && misaligned(ptr))
+            return WKV7_ERR_ALIGN;
+
+    const int64_t ein = in_dtype == WKV7_BF16 ? 2 : 4, eo = o_dtype == WKV7_BF16 ? 2 : 4;
+    const int64_t seq_elems = tok * kN, st_bytes = static_cast<int64_t>(B) * H * kN * kN * 4;
+    Range ro{0, 0}, rpos{0, 0}, rin{0, 0};
+    const Range rst = range_of(state_out, st_bytes);
+    if (state_in)
+        rin = range_of(state_in, st_bytes);
+    if (T > 0)
+        ro = range_of(o, seq_elems * eo);
+    if (state_pos && T > 0)
+        rpos = range_of(state_pos, seq_elems * kN * 4);
+
+    // state_out may be state_in exactly; any other overlap is refused.
+    if (state_in && state_in != state_out && overlap(rst, rin))
+        return WKV7_ERR_ALIAS;
+    Range ins[7] = {rin, {0, 0}, {0, 0}, {0, 0}, {0, 0}, {0, 0}, {0, 0}};
+    if (T > 0) {
+        const void *vin[6] = {r, w, k, v, a, b};
+        for (int i = 0; i < 6; ++i)
+            ins[i + 1] = range_of(vin[i], seq_elems * ein);
+    }
+    const Range outs[3] = {ro, rst, rpos};
+    for (int x = 0; x < 3; ++x) {
+        for (int y = 0; y < 7; ++y) {
+            if (x == 1 && y == 0)
+                continue;  // state_out vs state_in handled above
+            if (overlap(outs[x], ins[y]))
+                return WKV7_ERR_ALIAS;
+        }
+        for (int y = x + 1; y < 3; ++y)
+            if (overlap(outs[x], outs[y]))
+                return WKV7_ERR_ALIAS;
+    }
+    return WKV7_OK;
+}
+
+SeqArgs make_args(const void *r, const void *w, const void *k, const void *v, const void *a, const void *b,
+                  int in_dtype, const float *state_in, void *o, int o_dtype, float *state_out,
+                  float *state_pos, int B, int T, int H)
+{
+    SeqArgs s;
+    s.r = r; s.w = w; s.k = k; s.v = v; s.a = a; s.b = b;
+    s.state_in = state_in; s.o = o; s.state_out = state_out; s.state_pos = state_pos;
+    s.B = B; s.T = T; s.H = H;
+    s.in_bf16 = in_dtype == WKV7_BF16;
+    s.o_bf16 = o_dtype == WKV7_BF16;
+    return s;
+}
+
+int empty_sequence(const float *state_in, float *state_out, int B, int H, hipStream_t stream)
+{
+    if (state_in == state_out)
+        return WKV7_OK;
+    const long long n = static_cast<long long>(B) * H * kN * kN;
+    return wkv7::launch_state_copy(state_in, state_out, n, stream) == hipSuccess ? WKV7_OK : WKV7_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int wkv7_forward(const void *r, const void *w, const void *k, const void *v, const void *a, const void *b,
+                 int in_dtype, const float *state_in, void *o, int o_dtype, float *state_out, int B, int T,
+                 int H, int N, void *stream)
+{
+    int st = check_seq(r, w, k, v, a, b, in_dtype, state_in, o, o_dtype, state_out, nullptr, B, T, H, N);
+    if (st != WKV7_OK)
+        return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (T == 0)
+        return empty_sequence(state_in, state_out, B, H, s);
+    const SeqArgs args = make_args(r, w, k, v, a, b, in_dtype, state_in, o, o_dtype, state_out, nullptr, B, T, H);
+    const hipError_t e = T < kChunkMinT ? wkv7::launch_step(args, s) : wkv7::launch_chunk(args, s);
+    return e == hipSuccess ? WKV7_OK : WKV7_ERR_HIP;
+}
+
+int wkv7_step(const void *r, const void *w, const void *k, const void *v, const void *a, const void *b,
+              int in_dtype, const float *state_in, void *o, int o_dtype, float *state_out, float *state_pos,
+              int B, int T, int H, int N, void *stream)
+{
+    int st = check_seq(r, w, k, v, a, b, in_dtype, state_in, o, o_dtype, state_out, state_pos, B, T, H, N);
+    if (st != WKV7_OK)
+        return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (T == 0)
+        return empty_sequence(state_in, state_out, B, H, s);
+    const SeqArgs args = make_args(r, w, k, v, a, b, in_dtype, state_in, o, o_dtype, state_out, state_pos, B, T, H);
+    return wkv7::launch_step(args, s) == hipSuccess ? WKV7_OK : WKV7_ERR_HIP;
+}
+
+int wkv7_state_reset(float *state, int B, int H, int N, const unsigned char *row_mask, void *stream)
+{
+    int64_t tok = 0;
+    if (N != kN)
+        return WKV7_ERR_UNSUPPORTED;
+    if (!shape_ok(B, 1, H, &tok))
+        return WKV7_ERR_SHAPE;
+    if (!state)
+        return WKV7_ERR_NULL;
+    if (misaligned(state))
+        return WKV7_ERR_ALIGN;
+    if (row_mask) {
+        const Range rs = range_of(state, static_cast<int64_t>(B) * H * kN * kN * 4);
+        if (overlap(rs, range_of(row_mask, B)))
+            return WKV7_ERR_ALIAS;
+    }
+    return wkv7::launch_state_reset(state, B, H, row_mask, static_cast<hipStream_t>(stream)) == hipSuccess
+               ? WKV7_OK
+               : WKV7_ERR_HIP;
+}
+
+const char *wkv7_status_string(int status)
+{
+    switch (status) {
+    case WKV7_OK: return "WKV7_OK: success";
+    case WKV7_ERR_NULL: return "WKV7_ERR_NULL: a required pointer is NULL";
+    case WKV7_ERR_SHAPE: return "WKV7_ERR_SHAPE: B and H must be >= 1, T >= 0, and sizes must fit in int64";
+    case WKV7_ERR_UNSUPPORTED: return "WKV7_ERR_UNSUPPORTED: N must be 64 and dtypes WKV7_F32 or WKV7_BF16";
+    case WKV7_ERR_ALIGN: return "WKV7_ERR_ALIGN: every buffer must be 16-byte aligned";
+    case WKV7_ERR_ALIAS: return "WKV7_ERR_ALIAS: an output overlaps another buffer (only state_out == state_in is allowed)";
+    case WKV7_ERR_HIP: return "WKV7_ERR_HIP: the HIP runtime refused a launch";
+    default: return "unknown wkv7 status";
+    }
+}
+
+int wkv7_abi_version(void) { return WKV7_ABI_VERSION; }
+
+}  // extern "C"

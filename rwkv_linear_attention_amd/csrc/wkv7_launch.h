@@ -1,0 +1,25 @@
+// wkv7_launch.h -- internal launch entry points of the libwkv7 kernels.
+// Arguments are validated by the C-ABI layer (wkv7_api.hip) before these run.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace wkv7 {
+
+struct SeqArgs {
+    const void *r, *w, *k, *v, *a, *b;  // [B,T,H,64], in_dtype
+    const float *state_in;              // [B,H,64,64] or nullptr (zeros)
+    void *o;                            // [B,T,H,64], o_dtype
+    float *state_out;                   // [B,H,64,64]
+    float *state_pos;                   // [B,T,H,64,64] or nullptr
+    int B, T, H;
+    int in_bf16, o_bf16;                // dtype flags
+};
+
+hipError_t launch_step(const SeqArgs &a, hipStream_t stream);
+hipError_t launch_chunk(const SeqArgs &a, hipStream_t stream);
+hipError_t launch_state_copy(const float *src, float *dst, long long n_floats, hipStream_t stream);
+hipError_t launch_state_reset(float *state, int B, int H, const unsigned char *row_mask,
+                              hipStream_t stream);
+
+}  // namespace wkv7

@@ -60,22 +60,26 @@ WORKLOADS = {
 
 
 def make_inputs(B: int, T: int, H: int, N: int = 64, *, seed: int = 0, dtype: str = "bf16",
-                sigma_w: float = 1.0, state_std: float = 0.1) -> dict:
-    """Draw one input set on the CPU.  Returns a dict of CPU tensors.
+                sigma_w: float = 1.0, state_std: float = 0.1, device: str = "cpu") -> dict:
+    """Draw one input set.  Returns a dict of tensors on ``device``.
 
     Keys r, w, k, v, a, b ([B,T,H,N], bf16 or fp32) and state_in ([B,H,N,N]
-    fp32, or None when state_std == 0).
+    fp32, or None when state_std == 0).  The same seed gives the same numbers
+    on every CPU run; a GPU generator (device="cuda", used only for inputs that
+    are timed and never compared) follows the same recipe with its own stream
+    of random numbers.
     """
-    g = torch.Generator(device="cpu").manual_seed(int(seed))
+    g = torch.Generator(device=device).manual_seed(int(seed))
     shape = (B, T, H, N)
-    r = torch.randn(shape, generator=g)
-    k = torch.randn(shape, generator=g)
-    v = torch.randn(shape, generator=g)
-    gate_x = torch.randn(shape, generator=g)
-    w_x = torch.randn(shape, generator=g) * sigma_w
+    rn = lambda shp: torch.randn(shp, generator=g, device=device)
+    r = rn(shape)
+    k = rn(shape)
+    v = rn(shape)
+    gate_x = rn(shape)
+    w_x = rn(shape) * sigma_w
     state_in = None
     if state_std > 0:
-        state_in = torch.randn((B, H, N, N), generator=g) * state_std
+        state_in = rn((B, H, N, N)) * state_std
     kk = k / k.norm(dim=-1, keepdim=True).clamp_min(1e-12)
     a = -kk
     b = kk * torch.sigmoid(gate_x)
@@ -90,11 +94,11 @@ def make_inputs(B: int, T: int, H: int, N: int = 64, *, seed: int = 0, dtype: st
     return out
 
 
-def workload_inputs(idx: int, *, T: int | None = None, seed_offset: int = 0) -> dict:
-    """Inputs of workload ``idx`` (optionally with another T or a shifted seed)."""
+def workload_inputs(idx: int, *, T: int | None = None, seed_offset: int = 0, device: str = "cpu") -> dict:
+    """Inputs of workload ``idx`` (optionally with another T, a shifted seed, or on the GPU)."""
     wl = WORKLOADS[idx]
     return make_inputs(wl.B, wl.T if T is None else T, wl.H, wl.N, seed=wl.seed + seed_offset,
-                       dtype=wl.dtype, sigma_w=wl.sigma_w, state_std=wl.state_std)
+                       dtype=wl.dtype, sigma_w=wl.sigma_w, state_std=wl.state_std, device=device)
 
 
 def content_hash(inputs: dict) -> str:

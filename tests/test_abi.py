@@ -1,0 +1,139 @@
+"""The C ABI of libwkv7 on the CPU: the library loads, exports every function the
+header declares, and refuses bad arguments before any HIP call (so no GPU is
+needed for these)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "wkv7.h")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_ALIGN, ERR_ALIAS, ERR_HIP = 0, -1, -2, -3, -4, -5, -6
+F32, BF16 = 0, 1
+
+
+@pytest.fixture(scope="module")
+def L():
+    import rwkv_linear_attention_amd as m
+    if not os.path.exists(m.LIB_PATH):
+        m.build()
+    return m.lib()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(wkv7_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    assert names == sorted(["wkv7_forward", "wkv7_step", "wkv7_state_reset", "wkv7_status_string",
+                            "wkv7_abi_version"])
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_abi_version(L):
+    src = open(HEADER).read()
+    ver = int(re.search(r"#define WKV7_ABI_VERSION (\d+)", src).group(1))
+    assert L.wkv7_abi_version() == ver
+
+
+def test_status_strings(L):
+    for st in (OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_ALIGN, ERR_ALIAS, ERR_HIP, 12345):
+        s = L.wkv7_status_string(st)
+        assert isinstance(s, bytes) and len(s) > 0
+
+
+# Fake device addresses: far apart, 16-byte aligned.  Validation must reject
+# every case below before touching them.
+BASE = 1 << 40
+SPAN = 1 << 34
+
+
+def fake(i, off=0):
+    return ctypes.c_void_p(BASE + i * SPAN + off)
+
+
+def fwd(L, B=2, T=8, H=3, N=64, in_dt=BF16, o_dt=F32, ptrs=None, sin="fake", sout=None):
+    p = [fake(i) for i in range(6)] if ptrs is None else ptrs
+    s_in = fake(7) if sin == "fake" else sin
+    s_out = fake(8) if sout is None else sout
+    return L.wkv7_forward(*p, in_dt, s_in, fake(6), o_dt, s_out, B, T, H, N, None)
+
+
+def step(L, B=2, T=5, H=3, N=64, pos="fake", **kw):
+    p = [fake(i) for i in range(6)]
+    sp = fake(9) if pos == "fake" else pos
+    return L.wkv7_step(*p, BF16, fake(7), fake(6), F32, fake(8), sp, B, T, H, N, None)
+
+
+@pytest.mark.parametrize("N", [0, 16, 32, 63, 65, 128])
+def test_head_size_must_be_64(L, N):
+    assert fwd(L, N=N) == ERR_UNSUPPORTED
+    assert step(L, N=N) == ERR_UNSUPPORTED
+    assert L.wkv7_state_reset(fake(8), 2, 3, N, None, None) == ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("in_dt,o_dt", [(2, F32), (-1, F32), (BF16, 7)])
+def test_unknown_dtypes(L, in_dt, o_dt):
+    assert fwd(L, in_dt=in_dt, o_dt=o_dt) == ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("B,T,H", [(0, 8, 3), (2, -1, 3), (2, 8, 0), (-3, 8, 3), (1 << 30, 1 << 30, 64)])
+def test_bad_shapes(L, B, T, H):
+    assert fwd(L, B=B, T=T, H=H) == ERR_SHAPE
+    assert step(L, B=B, T=T, H=H) == ERR_SHAPE
+
+
+@pytest.mark.parametrize("which", range(6))
+def test_null_inputs(L, which):
+    p = [fake(i) for i in range(6)]
+    p[which] = None
+    assert fwd(L, ptrs=p) == ERR_NULL
+
+
+def test_null_outputs(L):
+    p = [fake(i) for i in range(6)]
+    assert L.wkv7_forward(*p, BF16, fake(7), None, F32, fake(8), 2, 8, 3, 64, None) == ERR_NULL
+    assert L.wkv7_forward(*p, BF16, fake(7), fake(6), F32, None, 2, 8, 3, 64, None) == ERR_NULL
+    assert L.wkv7_state_reset(None, 2, 3, 64, None, None) == ERR_NULL
+
+
+@pytest.mark.parametrize("which", range(6))
+def test_misaligned(L, which):
+    p = [fake(i) for i in range(6)]
+    p[which] = fake(which, 2)
+    assert fwd(L, ptrs=p) == ERR_ALIGN
+    assert fwd(L, sout=fake(8, 4)) == ERR_ALIGN
+    assert L.wkv7_state_reset(fake(8, 8), 2, 3, 64, None, None) == ERR_ALIGN
+
+
+def test_aliasing_rules(L):
+    p = [fake(i) for i in range(6)]
+    # o overlapping an input
+    assert L.wkv7_forward(*p, BF16, fake(7), fake(0, 64), F32, fake(8), 2, 8, 3, 64, None) == ERR_ALIAS
+    # state_out overlapping state_in without being equal to it
+    assert L.wkv7_forward(*p, BF16, fake(7), fake(6), F32, fake(7, 256), 2, 8, 3, 64, None) == ERR_ALIAS
+    # state_out overlapping o
+    assert L.wkv7_forward(*p, BF16, fake(7), fake(6), F32, fake(6, 16), 2, 8, 3, 64, None) == ERR_ALIAS
+    # state_pos overlapping state_out
+    assert L.wkv7_step(*p, BF16, fake(7), fake(6), F32, fake(8), fake(8, 1024), 2, 5, 3, 64, None) == ERR_ALIAS
+    # state_pos overlapping an input
+    assert L.wkv7_step(*p, BF16, fake(7), fake(6), F32, fake(8), fake(3, 32), 2, 5, 3, 64, None) == ERR_ALIAS
+    # row mask inside the state
+    assert L.wkv7_state_reset(fake(8), 2, 3, 64, fake(8, 100), None) == ERR_ALIAS
+
+
+def test_errors_come_before_any_launch(L):
+    # A NULL required pointer with an otherwise impossible shape still reports one
+    # of the argument errors, never a HIP error: nothing reached the runtime.
+    p = [None] * 6
+    st = L.wkv7_forward(*p, BF16, None, None, F32, None, 1, 4, 1, 64, None)
+    assert st == ERR_NULL
