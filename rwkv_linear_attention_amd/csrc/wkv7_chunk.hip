@@ -60,7 +60,7 @@ constexpr float W_MIN = 0x1p-15f;  // lower bound applied to decay multipliers i
 constexpr int NPROD = 4;           // producer waves
 constexpr int LDA = kN + 8;        // row pitch (bf16) of [16][64] operand planes
 constexpr int LDT = CH + 8;        // row pitch (bf16) of [64][16] transposed planes
-constexpr int LDM = CH + 1;        // row pitch (fp32) of [16][16] matrices
+constexpr int LDM = CH + 4;        // row pitch (fp32) of [16][16] matrices (16-byte rows)
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
@@ -139,24 +139,51 @@ __device__ __forceinline__ void split4(const float (&v)[4], s16x4 (&out)[NP])
 
 __device__ __forceinline__ s16x4 lds4(const uint16_t *p) { return *reinterpret_cast<const s16x4 *>(p); }
 
-// One chunk's data in LDS.  Operand planes hold bf16 bit patterns.
+template <int NP, bool ON>
+struct RowMajorBK {
+    uint16_t Bp[NP][CH][LDA];
+    uint16_t Kp[NP][CH][LDA];
+};
+template <int NP>
+struct RowMajorBK<NP, false> {};
+
+// One chunk's data in LDS.  Operand planes hold bf16 bit patterns.  With
+// bf16 inputs (NP == 2) B' and K' are also kept row-major, so the matrix
+// stage reads its operands with 16-byte loads; the fp32-input build (NP == 3)
+// has no room for them and gathers from the transposed copies instead.
 template <int NP, int NPV, int NC>
-struct Slot {
+struct alignas(16) Slot {
     uint16_t Ap[NP][CH][LDA];    // A'[tau][i]
     uint16_t Rp[NP][CH][LDA];    // R'[tau][i]
+    RowMajorBK<NP, NP == 2> bk;  // B'[s][i], K'[s][i]  (NP == 2 only)
     uint16_t BpT[NP][kN][LDT];   // B'[s][i] stored as [i][s]
     uint16_t KpT[NP][kN][LDT];   // K'[s][i] stored as [i][s]
     uint16_t Vt[NPV][NC][LDT];   // v[s][j] stored as [j][s]
     float M[3][CH][LDM];         // M_ak, M_rb, M_rk (masked)
     float Tm[CH][LDM];           // (I - M_ab)^{-1}
-    float p7[kN];                // P_7 per key channel
-    float d15[kN];               // P_15 / P_7 per key channel
+    alignas(16) float p7[kN];    // P_7 per key channel
+    alignas(16) float d15[kN];   // P_15 / P_7 per key channel
 };
+
+// Raw bf16 input rows of one chunk, staged by the producers: [stream][tau][i]
+// with streams w, a, r, k, b, v (v holds all 64 columns of the head).
+struct alignas(16) RawSlot {
+    uint16_t x[6][CH][kN];
+};
+
+template <bool ON>
+struct RawRing {
+    RawSlot raw[2];
+};
+template <>
+struct RawRing<false> {};
 
 template <int NP, int NPV, int NC>
 struct Smem {
     Slot<NP, NPV, NC> slot[3];
+    RawRing<NP == 2> rr;         // staged raw rows (bf16 inputs only)
     float Mab[CH][LDM];          // scratch of the wave that solves for T
+    float Xs[8][9];              // scratch of the blocked triangular inverse
 };
 
 // Decay factors of one key channel over a chunk: d[tau+1] = P_tau / P_7 and
@@ -222,6 +249,7 @@ __global__ __launch_bounds__((kN / J / 16 + NPROD) * 64) void wkv7_chunk_kernel(
     const size_t head0 = (static_cast<size_t>(bb) * T * H + hh) * kN;   // (b, t=0, h, 0)
     const size_t sbase = static_cast<size_t>(bh) * (kN * kN);
     const int nchunks = (T + CH - 1) / CH;
+    constexpr bool STAGED = !F32IN;  // bf16 rows go through the LDS staging ring
 
     if (wv < NSW) {
         // ------------------------------------------------------------ consumer
@@ -236,26 +264,40 @@ __global__ __launch_bounds__((kN / J / 16 + NPROD) * 64) void wkv7_chunk_kernel(
             for (int e = 0; e < 4; ++e)
                 Sx[pt][e] = HAS_STATE_IN ? p.state_in[sbase + (16 * pt + 4 * q + e) * kN + jw + m] : 0.0f;
 
+        if constexpr (STAGED)
+            __syncthreads();  // matches the producers' prologue
         for (int i = -2; i < nchunks; ++i) {
             if (i >= 0) {
                 const SlotT &sl = sm.slot[i % 3];
                 const int t0 = i * CH;
+                // P_7 and d_15 of this lane's 16 key rows 16 pt + 4 q + e
+                f32x4 p7v[4], d15v[4];
+#pragma unroll
+                for (int pt = 0; pt < 4; ++pt) {
+                    p7v[pt] = *reinterpret_cast<const f32x4 *>(&sl.p7[16 * pt + 4 * q]);
+                    d15v[pt] = *reinterpret_cast<const f32x4 *>(&sl.d15[16 * pt + 4 * q]);
+                }
                 // S^ = diag(P_7) S, as matrix-core B operands over the key index:
                 // key slot (q, e) of k-step s is key row 16 (2 s + e/4) + 4 q + e%4,
                 // which this lane holds in Sx[2 s + e/4][e % 4].
+                float Sh[4][4];
+#pragma unroll
+                for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        Sh[pt][e] = Sx[pt][e] * p7v[pt][e];
                 s16x8 Bs[2][NP];
 #pragma unroll
                 for (int s = 0; s < 2; ++s) {
                     float v8[8];
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const int pt = 2 * s + e / 4;
-                        v8[e] = Sx[pt][e & 3] * sl.p7[16 * pt + 4 * q + (e & 3)];
-                    }
+                    for (int e = 0; e < 8; ++e)
+                        v8[e] = Sh[2 * s + e / 4][e & 3];
                     split8<NP>(v8, Bs[s]);
                 }
-                // A'-rows and R'-rows as A operands with the same key slots
-                f32x4 y = {0.f, 0.f, 0.f, 0.f}, o = {0.f, 0.f, 0.f, 0.f};
+                // A'-rows and R'-rows as A operands with the same key slots;
+                // independent accumulators per k-step keep the chains short.
+                f32x4 y2[2], o2[2];
 #pragma unroll
                 for (int s = 0; s < 2; ++s) {
                     s16x8 Af[NP], Rf[NP];
@@ -268,31 +310,34 @@ __global__ __launch_bounds__((kN / J / 16 + NPROD) * 64) void wkv7_chunk_kernel(
                         Af[pl] = s16x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
                         Rf[pl] = s16x8{r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
                     }
-                    mma32<NP, NP>(y, Af, Bs[s]);
-                    mma32<NP, NP>(o, Rf, Bs[s]);
+                    y2[s] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    o2[s] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    mma32<NP, NP>(y2[s], Af, Bs[s]);
+                    mma32<NP, NP>(o2[s], Rf, Bs[s]);
                 }
                 // V rows as a B operand over the token index (slot (q, e) = token 4 q + e)
                 s16x4 Vf[NPV];
 #pragma unroll
                 for (int pl = 0; pl < NPV; ++pl)
                     Vf[pl] = lds4(&sl.Vt[pl][jl][4 * q]);
-                // y += M_ak V
+                // M_ak V
+                f32x4 ym = {0.f, 0.f, 0.f, 0.f};
                 {
-                    float a4[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        a4[e] = sl.M[0][m][4 * q + e];
+                    const f32x4 mv = *reinterpret_cast<const f32x4 *>(&sl.M[0][m][4 * q]);
+                    const float a4[4] = {mv[0], mv[1], mv[2], mv[3]};
                     s16x4 Mf[NP];
                     split4<NP>(a4, Mf);
-                    mma16<NP, NPV>(y, Mf, Vf);
+                    mma16<NP, NPV>(ym, Mf, Vf);
                 }
-                // Z = T Y  (Y held in accumulator layout: Y[4 q + e][col m] = y[e])
+                // Z = T Y  (Y = A' S^ + M_ak V in accumulator layout: Y[4 q + e][col m])
                 f32x4 z = {0.f, 0.f, 0.f, 0.f};
                 {
-                    float t4[4], y4[4] = {y[0], y[1], y[2], y[3]};
+                    const f32x4 tv = *reinterpret_cast<const f32x4 *>(&sl.Tm[m][4 * q]);
+                    const float t4[4] = {tv[0], tv[1], tv[2], tv[3]};
+                    float y4[4];
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        t4[e] = sl.Tm[m][4 * q + e];
+                        y4[e] = (y2[0][e] + y2[1][e]) + ym[e];
                     s16x4 Tf[NP], Yf[NP];
                     split4<NP>(t4, Tf);
                     split4<NP>(y4, Yf);
@@ -302,7 +347,7 @@ __global__ __launch_bounds__((kN / J / 16 + NPROD) * 64) void wkv7_chunk_kernel(
                 // (this lane's z[e]), (q, e>=4) is V row 4q+e-4.
                 s16x8 ZV[NP];
                 {
-                    float z4[4] = {z[0], z[1], z[2], z[3]};
+                    const float z4[4] = {z[0], z[1], z[2], z[3]};
                     s16x4 Zf[NP];
                     split4<NP>(z4, Zf);
 #pragma unroll
@@ -311,23 +356,22 @@ __global__ __launch_bounds__((kN / J / 16 + NPROD) * 64) void wkv7_chunk_kernel(
                         ZV[pl] = s16x8{Zf[pl][0], Zf[pl][1], Zf[pl][2], Zf[pl][3], vv[0], vv[1], vv[2], vv[3]};
                     }
                 }
-                // o += [M_rb | M_rk] [Z ; V]
+                // o = R' S^ + [M_rb | M_rk] [Z ; V]
+                f32x4 o3 = {0.f, 0.f, 0.f, 0.f};
                 {
-                    float a8[8];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        a8[e] = sl.M[1][m][4 * q + e];
-                        a8[e + 4] = sl.M[2][m][4 * q + e];
-                    }
+                    const f32x4 mrb = *reinterpret_cast<const f32x4 *>(&sl.M[1][m][4 * q]);
+                    const f32x4 mrk = *reinterpret_cast<const f32x4 *>(&sl.M[2][m][4 * q]);
+                    const float a8[8] = {mrb[0], mrb[1], mrb[2], mrb[3], mrk[0], mrk[1], mrk[2], mrk[3]};
                     s16x8 Mf[NP];
                     split8<NP>(a8, Mf);
-                    mma32<NP, NP>(o, Mf, ZV);
+                    mma32<NP, NP>(o3, Mf, ZV);
                 }
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int tau = 4 * q + e;
                     if (t0 + tau < T)
-                        store_elem(go, head0 + static_cast<size_t>(t0 + tau) * rowstride + jw + m, o[e]);
+                        store_elem(go, head0 + static_cast<size_t>(t0 + tau) * rowstride + jw + m,
+                                   (o2[0][e] + o2[1][e]) + o3[e]);
                 }
                 // S = diag(d_15) (S^ + [B'^T | K'^T] [Z ; V]), one 16-row tile at a time
 #pragma unroll
@@ -339,14 +383,11 @@ __global__ __launch_bounds__((kN / J / 16 + NPROD) * 64) void wkv7_chunk_kernel(
                         const s16x4 k4 = lds4(&sl.KpT[pl][16 * pt + m][4 * q]);
                         Uf[pl] = s16x8{b4[0], b4[1], b4[2], b4[3], k4[0], k4[1], k4[2], k4[3]};
                     }
-                    f32x4 acc;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        acc[e] = Sx[pt][e] * sl.p7[16 * pt + 4 * q + e];
+                    f32x4 acc = {Sh[pt][0], Sh[pt][1], Sh[pt][2], Sh[pt][3]};
                     mma32<NP, NP>(acc, Uf, ZV);
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        Sx[pt][e] = acc[e] * sl.d15[16 * pt + 4 * q + e];
+                        Sx[pt][e] = acc[e] * d15v[pt][e];
                 }
             }
             __syncthreads();
@@ -360,48 +401,118 @@ __global__ __launch_bounds__((kN / J / 16 + NPROD) * 64) void wkv7_chunk_kernel(
     }
 
     // ---------------------------------------------------------------- producers
-    const int pw = wv - NSW;  // 0: M_ab and T; 1: A' K' and M_ak; 2: R' and M_rb; 3: B' v and M_rk
+    // Wave 0 builds M_ab and inverts I - M_ab; waves 1..3 build the operands
+    // (wave 1: A' and K'; wave 2: R'; wave 3: B', v and the decay factors) and
+    // the matrices M_ak (1), M_rb (2), M_rk (3).
+    const int pw = wv - NSW;
+    // ---- input path
+    // STAGED: producer pw in 1..3 owns two of the six input streams (w a | r k | b v)
+    // and moves them, as 16-byte pieces of whole 128-byte rows, from HBM to the
+    // staging ring: the loads of chunk c are issued in iteration c-5, written
+    // to ring slot c%2 in iteration c-3 and read in iteration c-2.
+    // Otherwise (fp32 inputs): per-lane loads straight into registers.
+    const uint16_t *gs0 = nullptr, *gs1 = nullptr;
+    int sidx0 = 0, sidx1 = 0;
+    if (pw == 1) { gs0 = static_cast<const uint16_t *>(p.w); sidx0 = 0; gs1 = static_cast<const uint16_t *>(p.a); sidx1 = 1; }
+    if (pw == 2) { gs0 = static_cast<const uint16_t *>(p.r); sidx0 = 2; gs1 = static_cast<const uint16_t *>(p.k); sidx1 = 3; }
+    if (pw == 3) { gs0 = static_cast<const uint16_t *>(p.b); sidx0 = 4; gs1 = static_cast<const uint16_t *>(p.v); sidx1 = 5; }
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    struct Stage {
+        u32x4 v[2][2];  // [stream][half]: rows 8*half + lane/8, bytes 16*(lane%8) .. +16
+    };
+    Stage sa, sb;
+    auto stage_load = [&](Stage &S, int c) {
+        if constexpr (STAGED) {
+            if (pw == 0 || c >= nchunks)
+                return;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int t = min(c * CH + 8 * h + (lane >> 3), T - 1);
+                const size_t off = head0 + static_cast<size_t>(t) * rowstride + 8 * (lane & 7);
+                S.v[0][h] = *reinterpret_cast<const u32x4 *>(gs0 + off);
+                S.v[1][h] = *reinterpret_cast<const u32x4 *>(gs1 + off);
+            }
+        }
+    };
+    auto stage_store = [&](const Stage &S, int c) {
+        if constexpr (STAGED) {
+            if (pw == 0 || c >= nchunks)
+                return;
+            RawSlot &rs = sm.rr.raw[c & 1];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int tau = 8 * h + (lane >> 3);
+                *reinterpret_cast<u32x4 *>(&rs.x[sidx0][tau][8 * (lane & 7)]) = S.v[0][h];
+                *reinterpret_cast<u32x4 *>(&rs.x[sidx1][tau][8 * (lane & 7)]) = S.v[1][h];
+            }
+        }
+    };
+    // fp32 inputs: registers of one chunk (lane = key channel, or value column for v)
     const Tin *__restrict__ gw = static_cast<const Tin *>(p.w);
     const Tin *__restrict__ gx0 = static_cast<const Tin *>(pw == 1 ? p.a : pw == 2 ? p.r : p.b);
     const Tin *__restrict__ gx1 = static_cast<const Tin *>(pw == 1 ? p.k : p.v);
-    const bool has_x1 = pw == 1 || pw == 3;   // second stream: k for wave 1, v for wave 3
-    // Prefetched raw inputs of one chunk (lane = key channel, or value column for v).
     struct Raw {
         Tin w[CH], x0[CH], x1[CH];
     };
     Raw ra, rb;
-    auto fetch = [&](Raw &R, int c) {
-        if (pw == 0 || c >= nchunks)
-            return;
-        const int t0 = c * CH;
+    auto reg_load = [&](Raw &R, int c) {
+        if constexpr (!STAGED) {
+            if (pw == 0 || c >= nchunks)
+                return;
 #pragma unroll
-        for (int tau = 0; tau < CH; ++tau) {
-            const int t = min(t0 + tau, T - 1);
-            const size_t row = head0 + static_cast<size_t>(t) * rowstride;
-            R.w[tau] = gw[row + lane];
-            R.x0[tau] = gx0[row + lane];
-            if (has_x1)
-                R.x1[tau] = gx1[row + (pw == 3 ? (j0 + (lane < NC ? lane : 0)) : lane)];
+            for (int tau = 0; tau < CH; ++tau) {
+                const int t = min(c * CH + tau, T - 1);
+                const size_t row = head0 + static_cast<size_t>(t) * rowstride;
+                R.w[tau] = gw[row + lane];
+                R.x0[tau] = gx0[row + lane];
+                R.x1[tau] = gx1[row + (pw == 3 ? j0 + (lane < NC ? lane : 0) : lane)];
+            }
         }
     };
-    // Operand stage: decay-scaled operands of chunk c into its slot.
+
+    // ---- operand stage: decay-scaled operands of chunk c into its slot
     auto operands = [&](const Raw &R, int c) {
         if (pw == 0 || c >= nchunks)
             return;
         SlotT &sl = sm.slot[c % 3];
         const int t0 = c * CH, i = lane;
         float w[CH], x0[CH], x1[CH];
+        if constexpr (STAGED) {
+            const RawSlot &rs = sm.rr.raw[c & 1];
+            // this wave's streams: wave 1 (a, k), wave 2 (r, -), wave 3 (b, v)
+            const int s0 = pw == 1 ? 1 : pw == 2 ? 2 : 4;
+            const int s1 = pw == 1 ? 3 : 5;
+            const int col1 = pw == 3 ? j0 + (lane < NC ? lane : 0) : lane;
+            // Read every row (rows past the end hold valid, clamped data), then
+            // mask with uniform bit masks, so the reads are not split by branches.
+            uint32_t rw[CH], r0[CH], r1[CH];
 #pragma unroll
-        for (int tau = 0; tau < CH; ++tau) {
-            const bool ok = t0 + tau < T;
-            w[tau] = ok ? fmaxf(load_elem(R.w, tau), W_MIN) : 1.0f;
-            x0[tau] = ok ? load_elem(R.x0, tau) : 0.0f;
-            x1[tau] = (ok && has_x1) ? load_elem(R.x1, tau) : 0.0f;
+            for (int tau = 0; tau < CH; ++tau) {
+                rw[tau] = rs.x[0][tau][i];
+                r0[tau] = rs.x[s0][tau][i];
+                r1[tau] = rs.x[s1][tau][col1];
+            }
+#pragma unroll
+            for (int tau = 0; tau < CH; ++tau) {
+                const uint32_t keep = t0 + tau < T ? 0xffffu : 0u;          // uniform
+                const uint32_t keep1 = pw != 2 ? keep : 0u;
+                w[tau] = fmaxf(bf16_val(static_cast<uint16_t>((rw[tau] & keep) | (0x3f80u & ~keep))), W_MIN);
+                x0[tau] = bf16_val(static_cast<uint16_t>(r0[tau] & keep));
+                x1[tau] = bf16_val(static_cast<uint16_t>(r1[tau] & keep1));
+            }
+        } else {
+#pragma unroll
+            for (int tau = 0; tau < CH; ++tau) {
+                const bool ok = t0 + tau < T;
+                w[tau] = ok ? fmaxf(load_elem(R.w, tau), W_MIN) : 1.0f;
+                x0[tau] = ok ? load_elem(R.x0, tau) : 0.0f;
+                x1[tau] = (ok && pw != 2) ? load_elem(R.x1, tau) : 0.0f;
+            }
         }
         float d[CH + 1], id[CH + 1];
         decay_factors(w, d, id);
         if (pw == 1 || pw == 2) {
-            // A' (wave 1) or R' (wave 2), rows over tau, one bf16 write per plane and row
+            // A' (wave 1) or R' (wave 2): row-major, one bf16 per plane and row
             uint16_t(*dst)[CH][LDA] = pw == 1 ? sl.Ap : sl.Rp;
 #pragma unroll
             for (int tau = 0; tau < CH; ++tau) {
@@ -412,9 +523,10 @@ __global__ __launch_bounds__((kN / J / 16 + NPROD) * 64) void wkv7_chunk_kernel(
                     dst[pl][tau][i] = pc[pl];
             }
         }
-        // K' (wave 1, from x1) or B' (wave 3, from x0): transposed rows, 16 bf16 per plane
         if (pw == 1 || pw == 3) {
-            uint16_t(*dst)[kN][LDT] = pw == 1 ? sl.KpT : sl.BpT;
+            // K' (wave 1, from x1) or B' (wave 3, from x0): transposed rows of 16
+            // bf16 per plane, and (bf16 inputs) the row-major copy as well
+            uint16_t(*dstT)[kN][LDT] = pw == 1 ? sl.KpT : sl.BpT;
             const float *src = pw == 1 ? x1 : x0;
             s16x8 lo[NP], hi[NP];
 #pragma unroll
@@ -427,12 +539,14 @@ __global__ __launch_bounds__((kN / J / 16 + NPROD) * 64) void wkv7_chunk_kernel(
                         lo[pl][s] = static_cast<short>(pc[pl]);
                     else
                         hi[pl][s - 8] = static_cast<short>(pc[pl]);
+                    if constexpr (NP == 2)
+                        (pw == 1 ? sl.bk.Kp : sl.bk.Bp)[pl][s][i] = pc[pl];
                 }
             }
 #pragma unroll
             for (int pl = 0; pl < NP; ++pl) {
-                *reinterpret_cast<s16x8 *>(&dst[pl][i][0]) = lo[pl];
-                *reinterpret_cast<s16x8 *>(&dst[pl][i][8]) = hi[pl];
+                *reinterpret_cast<s16x8 *>(&dstT[pl][i][0]) = lo[pl];
+                *reinterpret_cast<s16x8 *>(&dstT[pl][i][8]) = hi[pl];
             }
         }
         if (pw == 3) {
@@ -458,14 +572,15 @@ __global__ __launch_bounds__((kN / J / 16 + NPROD) * 64) void wkv7_chunk_kernel(
             }
         }
     };
-    // Matrix stage: one 16x16 tile M = tril(X' Y'^T) of chunk c per wave over
-    // the 64 key channels; wave 0 also inverts I - M_ab by forward substitution.
+
+    // ---- matrix stage: one 16x16 tile M = tril(X' Y'^T) of chunk c per wave
+    // over the 64 key channels; wave 0 then inverts I - M_ab.
     auto matrices = [&](int c) {
         if (c < 0 || c >= nchunks)
             return;
         SlotT &sl = sm.slot[c % 3];
         const uint16_t(*X)[CH][LDA] = (pw == 0 || pw == 1) ? sl.Ap : sl.Rp;
-        const uint16_t(*Y)[kN][LDT] = (pw == 0 || pw == 2) ? sl.BpT : sl.KpT;
+        const bool yb = pw == 0 || pw == 2;  // Y' = B' (else K')
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
@@ -473,9 +588,14 @@ __global__ __launch_bounds__((kN / J / 16 + NPROD) * 64) void wkv7_chunk_kernel(
 #pragma unroll
             for (int pl = 0; pl < NP; ++pl) {
                 Af[pl] = *reinterpret_cast<const s16x8 *>(&X[pl][m][32 * s + 8 * q]);
+                if constexpr (NP == 2) {
+                    Bf[pl] = *reinterpret_cast<const s16x8 *>(&(yb ? sl.bk.Bp : sl.bk.Kp)[pl][m][32 * s + 8 * q]);
+                } else {
+                    const uint16_t(*Y)[kN][LDT] = yb ? sl.BpT : sl.KpT;
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    Bf[pl][e] = static_cast<short>(Y[pl][32 * s + 8 * q + e][m]);
+                    for (int e = 0; e < 8; ++e)
+                        Bf[pl][e] = static_cast<short>(Y[pl][32 * s + 8 * q + e][m]);
+                }
             }
             mma32<NP, NP>(acc, Af, Bf);
         }
@@ -487,40 +607,82 @@ __global__ __launch_bounds__((kN / J / 16 + NPROD) * 64) void wkv7_chunk_kernel(
             dst[tau][m] = (m < tau || (!strict && m == tau)) ? acc[e] : 0.0f;
         }
         if (pw == 0) {
-            __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's M_ab writes are done
+            // (I - M_ab)^{-1} in 8x8 blocks: T11 = (I - M11)^{-1}, T22 = (I - M22)^{-1}
+            // by forward substitution (lanes 0..7 and 8..15, one column each), then
+            // T21 = T22 (M21 T11) with one entry per lane.  This wave's own LDS
+            // writes are complete before it reads them back.
+            __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
             __builtin_amdgcn_wave_barrier();
             if (lane < CH) {
-                // column `lane` of (I - M_ab)^{-1}
-                float x[CH];
+                const int off = lane < 8 ? 0 : 8, col = lane - off;
+                float x[8];
 #pragma unroll
-                for (int tau = 0; tau < CH; ++tau)
-                    x[tau] = tau == lane ? 1.0f : 0.0f;
+                for (int t = 0; t < 8; ++t)
+                    x[t] = t == col ? 1.0f : 0.0f;
 #pragma unroll
-                for (int s = 0; s < CH; ++s)
+                for (int s2 = 0; s2 < 8; ++s2)
 #pragma unroll
-                    for (int tau = s + 1; tau < CH; ++tau)
-                        x[tau] = fmaf(sm.Mab[tau][s], x[s], x[tau]);
+                    for (int t = s2 + 1; t < 8; ++t)
+                        x[t] = fmaf(sm.Mab[off + t][off + s2], x[s2], x[t]);
 #pragma unroll
-                for (int tau = 0; tau < CH; ++tau)
-                    sl.Tm[tau][lane] = x[tau];
+                for (int t = 0; t < 8; ++t) {
+                    sl.Tm[off + t][off + col] = x[t];
+                    if (off == 0)
+                        sl.Tm[t][8 + col] = 0.0f;  // upper-right block
+                }
             }
+            __builtin_amdgcn_s_waitcnt(0xc07f);
+            __builtin_amdgcn_wave_barrier();
+            const int r8 = lane >> 3, c8 = lane & 7;
+            float xv = 0.0f;
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                xv = fmaf(sm.Mab[8 + r8][k], sl.Tm[k][c8], xv);
+            sm.Xs[r8][c8] = xv;
+            __builtin_amdgcn_s_waitcnt(0xc07f);
+            __builtin_amdgcn_wave_barrier();
+            float tv = 0.0f;
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                tv = fmaf(sl.Tm[8 + r8][8 + k], sm.Xs[k][c8], tv);
+            sl.Tm[8 + r8][c8] = tv;
         }
     };
 
     // Pipeline: iteration i consumes chunk i (consumer waves), builds the
-    // matrices of chunk i+1 and the operands of chunk i+2, and prefetches the
-    // inputs of chunk i+4.  Two register sets alternate between even and odd i.
-    fetch(ra, 0);
-    fetch(rb, 1);
+    // matrices of chunk i+1 and the operands of chunk i+2 (reading ring slot
+    // (i+2)%2), writes the staged rows of chunk i+3 into the other ring slot
+    // and issues the loads of chunk i+5 (fp32 inputs: loads of chunk i+4).
+    // Register sets alternate between even and odd iterations.
+    if constexpr (STAGED) {
+        stage_load(sa, 0);
+        stage_load(sb, 1);
+        stage_store(sa, 0);
+        stage_load(sa, 2);
+        __syncthreads();  // ring slot 0 holds chunk 0 (matched by the consumers)
+    } else {
+        reg_load(ra, 0);
+        reg_load(rb, 1);
+    }
     for (int i = -2; i < nchunks; i += 2) {
         matrices(i + 1);
         operands(ra, i + 2);
-        fetch(ra, i + 4);
+        if constexpr (STAGED) {
+            stage_store(sb, i + 3);
+            stage_load(sb, i + 5);
+        } else {
+            reg_load(ra, i + 4);
+        }
         __syncthreads();
         if (i + 1 < nchunks) {
             matrices(i + 2);
             operands(rb, i + 3);
-            fetch(rb, i + 5);
+            if constexpr (STAGED) {
+                stage_store(sa, i + 4);
+                stage_load(sa, i + 6);
+            } else {
+                reg_load(rb, i + 5);
+            }
             __syncthreads();
         }
     }
