@@ -173,6 +173,40 @@ def time_prefill_workload(K, synth, idx: int, steps: int, warmup: int):
     return {"ms_per_step": ms, "sec_per_launch": ms / 1e3, "mtok_s": wl.B * wl.T / (ms / 1e3) / 1e6}
 
 
+def copy_ceiling(idx: int, steps: int, warmup: int):
+    """A plain device copy moving the same bytes as one call of workload idx (state in ->
+    state out, per-position states included), over the same number of distinct buffer sets,
+    graph-replayed like the step workloads: the HBM rate a streaming read+write reaches here."""
+    import torch
+    import synth
+    wl = synth.WORKLOADS[idx]
+    kind = "verify" if idx == 4 else "step" if idx == 1 else "chunk"
+    nbytes = algorithmic_bytes(wl, kind)
+    n = nbytes // 8  # floats per side: half the bytes read, half written
+    layers = max(1, wl.layers)
+    src = [torch.randn(n, device="cuda") for _ in range(layers)]
+    dst = [torch.empty(n, device="cuda") for _ in range(layers)]
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        for s_, d_ in zip(src, dst):
+            d_.copy_(s_)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for s_, d_ in zip(src, dst):
+                d_.copy_(s_)
+        for _ in range(warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            g.replay()
+        e1.record(stream)
+        e1.synchronize()
+    sec = e0.elapsed_time(e1) / 1e3 / (steps * layers)
+    return {"bytes_per_copy": 8 * n, "us_per_copy": round(sec * 1e6, 3), "GB/s": round(8 * n / sec / 1e9, 1)}
+
+
 # ----------------------------------------------------------------------------- CPU baseline
 
 def cpu_baseline(synth, idx: int, budget_s: float = 12.0):
@@ -225,6 +259,8 @@ def main():
     ap.add_argument("--workload", type=int, default=1, choices=[1, 2, 3, 4])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", action="store_true", help="measure the chosen workload only")
+    ap.add_argument("--copy-ceiling", action="store_true",
+                    help="time a plain device copy of the workload's bytes instead (HBM ceiling / counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the WKV-7 kernels here are measured on one MI355X "
@@ -234,10 +270,14 @@ def main():
 
     import torch
     import synth
-    import rwkv_linear_attention_amd as K
-    K.lib()
     if not torch.cuda.is_available():
         raise SystemExit("no GPU visible")
+    if args.copy_ceiling:
+        print(json.dumps({"copy_ceiling": copy_ceiling(args.workload, args.steps, args.warmup),
+                          "workload": synth.WORKLOADS[args.workload].name}), flush=True)
+        return
+    import rwkv_linear_attention_amd as K
+    K.lib()
 
     def measure(idx):
         wl = synth.WORKLOADS[idx]

@@ -9,89 +9,137 @@
 // RWKV7-MTP-Exp model card, section "Inference" (state rolled back to the
 // accepted prefix).
 //
-// Mapping to gfx950: one 64-lane wavefront per head; lane j owns VALUE column
-// j of the 64x64 fp32 state, i.e. 64 VGPRs holding S[0..63][j].  Because every
-// value column evolves independently given the shared key-side vectors, both
-// reductions over the key index (a^T S and r^T S) are in-lane dot products and
-// need no cross-lane traffic; the key-side scalars a[i], w[i], b[i], k[i], r[i]
-// are broadcast from the lane that loaded them.  A state row S[i][0..63] is
-// 256 contiguous bytes, so each of the 64 state loads and stores of a wave is
-// one fully coalesced 256-byte access.
+// Mapping to gfx950: one workgroup of NW wavefronts per head.  Lane j owns
+// VALUE column j of the 64x64 fp32 state; wave g holds the 64/NW key rows
+// i = g*RW .. g*RW + RW-1 of that column in registers.  Every value column
+// evolves independently given the shared key-side vectors, so the update is
+// lane-local; the reductions over the key index (a^T S and r^T S) are
+// in-lane partial sums over a wave's rows, combined across the NW waves
+// through LDS in a fixed order.  The key-side scalars a, w, b, k, r of a
+// wave's rows are uniform across its lanes and come in through scalar loads.
+// A state row S[i][0..63] is 256 contiguous bytes, so every state load and
+// store of a wave is one fully coalesced 256-byte access; the state streams
+// through once per call, so its loads and stores are marked nontemporal.  Splitting a head's
+// rows over several short waves lets the loads, arithmetic and stores of
+// different waves overlap, which is what a bandwidth-bound step needs.
 #include "wkv7_device.h"
 #include "wkv7_launch.h"
 
 namespace wkv7 {
 namespace {
 
-template <typename Tin, typename Tout, bool HAS_STATE_IN, bool WRITE_POS>
-__global__ __launch_bounds__(64) void wkv7_step_kernel(SeqArgs p)
-{
-    const int j = threadIdx.x;                 // value column owned by this lane
-    const int bh = blockIdx.x;                 // (batch, head) pair
-    const int H = p.H, T = p.T;
-    const int bb = bh / H, hh = bh - bb * H;
-    const Tin *__restrict__ r = static_cast<const Tin *>(p.r);
-    const Tin *__restrict__ w = static_cast<const Tin *>(p.w);
-    const Tin *__restrict__ k = static_cast<const Tin *>(p.k);
-    const Tin *__restrict__ v = static_cast<const Tin *>(p.v);
-    const Tin *__restrict__ a = static_cast<const Tin *>(p.a);
-    const Tin *__restrict__ b = static_cast<const Tin *>(p.b);
-    Tout *__restrict__ o = static_cast<Tout *>(p.o);
+constexpr int NW = 4;          // waves per head
+constexpr int RW = kN / NW;    // key rows per wave
 
-    const size_t sbase = static_cast<size_t>(bh) * (kN * kN) + j;
-    float S[kN];
+// RW consecutive elements of a key-side vector, widened to fp32, from a
+// wave-uniform address (scalar loads).
+__device__ __forceinline__ void load_rows(const uint16_t *__restrict__ p, float (&x)[RW])
+{
+    const uint32_t *p32 = reinterpret_cast<const uint32_t *>(p);
 #pragma unroll
-    for (int i = 0; i < kN; ++i)
-        S[i] = HAS_STATE_IN ? p.state_in[sbase + i * kN] : 0.0f;
+    for (int u = 0; u < RW / 2; ++u) {
+        const uint32_t bits = p32[u];
+        x[2 * u] = __uint_as_float(bits << 16);
+        x[2 * u + 1] = __uint_as_float(bits & 0xffff0000u);
+    }
+}
+__device__ __forceinline__ void load_rows(const float *__restrict__ p, float (&x)[RW])
+{
+#pragma unroll
+    for (int u = 0; u < RW; ++u)
+        x[u] = p[u];
+}
+
+template <typename Tin, typename Tout, bool HAS_STATE_IN, bool WRITE_POS>
+__global__ __launch_bounds__(NW * 64) void wkv7_step_kernel(
+    const Tin *__restrict__ r, const Tin *__restrict__ w, const Tin *__restrict__ k, const Tin *__restrict__ v,
+    const Tin *__restrict__ a, const Tin *__restrict__ b, const float *state_in, Tout *__restrict__ o,
+    float *state_out, float *__restrict__ state_pos, int T, int H)
+{
+    const int j = threadIdx.x & 63;                                   // value column of this lane
+    const int g = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // row block of this wave
+    const int i0 = g * RW;
+    const int bh = blockIdx.x;                                        // (batch, head) pair
+    const int bb = bh / H, hh = bh - bb * H;
+    __shared__ float part_a[2][NW][kN];  // a^T S partial sums, alternating between tokens
+    __shared__ float part_r[NW][kN];     // r^T S partial sums
+
+    const size_t sbase = static_cast<size_t>(bh) * (kN * kN) + static_cast<size_t>(i0) * kN + j;
+    float S[RW];
+#pragma unroll
+    for (int u = 0; u < RW; ++u)
+        S[u] = HAS_STATE_IN ? __builtin_nontemporal_load(state_in + sbase + u * kN) : 0.0f;
 
     for (int t = 0; t < T; ++t) {
-        const size_t base = ((static_cast<size_t>(bb) * T + t) * H + hh) * kN + j;
-        // lane j holds element j of every key-side vector and of v
-        const float a_j = load_elem(a, base), w_j = load_elem(w, base);
-        const float b_j = load_elem(b, base), k_j = load_elem(k, base);
-        const float r_j = load_elem(r, base), v_j = load_elem(v, base);
+        const size_t base = ((static_cast<size_t>(bb) * T + t) * H + hh) * kN;  // uniform
+        float ar[RW], wr[RW], br[RW], kr[RW], rr[RW];
+        load_rows(a + base + i0, ar);
+        load_rows(w + base + i0, wr);
+        load_rows(b + base + i0, br);
+        load_rows(k + base + i0, kr);
+        load_rows(r + base + i0, rr);
+        const float vj = load_elem(v, base + j);
 
-        // sa = a^T S (state before the step), in-lane over the key index
+        // sa[j] = a^T S over the state before this token: partial over this wave's rows
         float sa = 0.0f;
 #pragma unroll
-        for (int i = 0; i < kN; ++i)
-            sa = fmaf(lane_bcast(a_j, i), S[i], sa);
-        // S[i][j] = w[i] S[i][j] + b[i] sa[j] + k[i] v[j]
+        for (int u = 0; u < RW; ++u)
+            sa = fmaf(ar[u], S[u], sa);
+        part_a[t & 1][g][j] = sa;
+        __syncthreads();
+        sa = part_a[t & 1][0][j];
 #pragma unroll
-        for (int i = 0; i < kN; ++i)
-            S[i] = fmaf(lane_bcast(w_j, i), S[i], fmaf(lane_bcast(b_j, i), sa, lane_bcast(k_j, i) * v_j));
-        // o[j] = r^T S (after the write)
-        float acc = 0.0f;
+        for (int gg = 1; gg < NW; ++gg)
+            sa += part_a[t & 1][gg][j];
+        // S[i][j] = w[i] S[i][j] + b[i] sa[j] + k[i] v[j], then o[j] = r^T S
+        float op = 0.0f;
 #pragma unroll
-        for (int i = 0; i < kN; ++i)
-            acc = fmaf(lane_bcast(r_j, i), S[i], acc);
-        store_elem(o, base, acc);
-
+        for (int u = 0; u < RW; ++u) {
+            S[u] = fmaf(wr[u], S[u], fmaf(br[u], sa, kr[u] * vj));
+            op = fmaf(rr[u], S[u], op);
+        }
         if (WRITE_POS) {
-            float *dst = p.state_pos + ((static_cast<size_t>(bb) * T + t) * H + hh) * (kN * kN) + j;
+            float *dst = state_pos + ((static_cast<size_t>(bb) * T + t) * H + hh) * (kN * kN) + i0 * kN + j;
 #pragma unroll
-            for (int i = 0; i < kN; ++i)
-                dst[i * kN] = S[i];
+            for (int u = 0; u < RW; ++u)
+                __builtin_nontemporal_store(S[u], dst + u * kN);
+        }
+        part_r[g][j] = op;
+        __syncthreads();
+        if (g == 0) {
+            float acc = part_r[0][j];
+#pragma unroll
+            for (int gg = 1; gg < NW; ++gg)
+                acc += part_r[gg][j];
+            store_elem(o, base + j, acc);
         }
     }
 #pragma unroll
-    for (int i = 0; i < kN; ++i)
-        p.state_out[sbase + i * kN] = S[i];
+    for (int u = 0; u < RW; ++u)
+        __builtin_nontemporal_store(S[u], state_out + sbase + u * kN);
 }
 
 template <typename Tin, typename Tout>
 hipError_t launch_typed(const SeqArgs &p, hipStream_t stream)
 {
-    const dim3 grid(static_cast<unsigned>(p.B) * static_cast<unsigned>(p.H)), block(64);
+    const dim3 grid(static_cast<unsigned>(p.B) * static_cast<unsigned>(p.H)), block(NW * 64);
+    const Tin *r = static_cast<const Tin *>(p.r), *w = static_cast<const Tin *>(p.w);
+    const Tin *k = static_cast<const Tin *>(p.k), *v = static_cast<const Tin *>(p.v);
+    const Tin *a = static_cast<const Tin *>(p.a), *b = static_cast<const Tin *>(p.b);
+    Tout *o = static_cast<Tout *>(p.o);
     const bool sin = p.state_in != nullptr, pos = p.state_pos != nullptr;
+#define WKV7_STEP_LAUNCH(SIN, POS)                                                                        \
+    hipLaunchKernelGGL((wkv7_step_kernel<Tin, Tout, SIN, POS>), grid, block, 0, stream, r, w, k, v, a, b, \
+                       p.state_in, o, p.state_out, p.state_pos, p.T, p.H)
     if (sin && pos)
-        hipLaunchKernelGGL((wkv7_step_kernel<Tin, Tout, true, true>), grid, block, 0, stream, p);
+        WKV7_STEP_LAUNCH(true, true);
     else if (sin)
-        hipLaunchKernelGGL((wkv7_step_kernel<Tin, Tout, true, false>), grid, block, 0, stream, p);
+        WKV7_STEP_LAUNCH(true, false);
     else if (pos)
-        hipLaunchKernelGGL((wkv7_step_kernel<Tin, Tout, false, true>), grid, block, 0, stream, p);
+        WKV7_STEP_LAUNCH(false, true);
     else
-        hipLaunchKernelGGL((wkv7_step_kernel<Tin, Tout, false, false>), grid, block, 0, stream, p);
+        WKV7_STEP_LAUNCH(false, false);
+#undef WKV7_STEP_LAUNCH
     return hipGetLastError();
 }
 
