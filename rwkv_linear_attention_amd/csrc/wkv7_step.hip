@@ -16,7 +16,7 @@
 // lane-local; the reductions over the key index (a^T S and r^T S) are
 // in-lane partial sums over a wave's rows, combined across the NW waves
 // through LDS in a fixed order.  The key-side scalars a, w, b, k, r of a
-// wave's rows are uniform across its lanes and come in through scalar loads.
+// wave's rows are uniform across its lanes.
 // A state row S[i][0..63] is 256 contiguous bytes, so every state load and
 // store of a wave is one fully coalesced 256-byte access; the state streams
 // through once per call, so its loads and stores are marked nontemporal.  Splitting a head's
@@ -30,6 +30,7 @@ namespace {
 
 constexpr int NW = 4;          // waves per head
 constexpr int RW = kN / NW;    // key rows per wave
+constexpr int TB = 8;          // tokens per staged block
 
 // RW consecutive elements of a key-side vector, widened to fp32, from a
 // wave-uniform address (scalar loads).
@@ -50,7 +51,13 @@ __device__ __forceinline__ void load_rows(const float *__restrict__ p, float (&x
         x[u] = p[u];
 }
 
-template <typename Tin, typename Tout, bool HAS_STATE_IN, bool WRITE_POS>
+// The key-side inputs of a step reach the waves in one of two ways, chosen by
+// the launcher: a single token (decode) is read with scalar loads issued
+// together with the state loads; longer runs (speculative verify, replays)
+// stage blocks of TB tokens, widened to fp32, in LDS with one cooperative
+// load, so no global latency sits inside the token loop.  The arithmetic is
+// the same code either way.
+template <typename Tin, typename Tout, bool HAS_STATE_IN, bool WRITE_POS, bool STAGED>
 __global__ __launch_bounds__(NW * 64) void wkv7_step_kernel(
     const Tin *__restrict__ r, const Tin *__restrict__ w, const Tin *__restrict__ k, const Tin *__restrict__ v,
     const Tin *__restrict__ a, const Tin *__restrict__ b, const float *state_in, Tout *__restrict__ o,
@@ -63,6 +70,23 @@ __global__ __launch_bounds__(NW * 64) void wkv7_step_kernel(
     const int bb = bh / H, hh = bh - bb * H;
     __shared__ float part_a[2][NW][kN];  // a^T S partial sums, alternating between tokens
     __shared__ float part_r[NW][kN];     // r^T S partial sums
+    __shared__ alignas(16) float xin[STAGED ? TB : 1][6][kN];  // staged a, w, b, k, r, v
+
+    const Tin *const vecs[6] = {a, w, b, k, r, v};
+    constexpr int PER = STAGED ? (TB * 6 * kN) / (NW * 64) : 1;  // staged elements per thread
+    float stage[PER];
+    auto stage_load = [&](int t0, int nt) {
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+            const int e = u * NW * 64 + threadIdx.x;
+            // rows past the end re-read the last token (unconditional loads keep the
+            // waits for them out of the issue sequence); they are never stored
+            const int tt = min(e / (6 * kN), nt - 1), rem = e % (6 * kN), vec = rem / kN, n = rem % kN;
+            stage[u] = load_elem(vecs[vec], ((static_cast<size_t>(bb) * T + t0 + tt) * H + hh) * kN + n);
+        }
+    };
+    if constexpr (STAGED)
+        stage_load(0, min(TB, T));  // issued before the state loads: waiting for it skips them
 
     const size_t sbase = static_cast<size_t>(bh) * (kN * kN) + static_cast<size_t>(i0) * kN + j;
     float S[RW];
@@ -70,48 +94,85 @@ __global__ __launch_bounds__(NW * 64) void wkv7_step_kernel(
     for (int u = 0; u < RW; ++u)
         S[u] = HAS_STATE_IN ? __builtin_nontemporal_load(state_in + sbase + u * kN) : 0.0f;
 
-    for (int t = 0; t < T; ++t) {
-        const size_t base = ((static_cast<size_t>(bb) * T + t) * H + hh) * kN;  // uniform
-        float ar[RW], wr[RW], br[RW], kr[RW], rr[RW];
-        load_rows(a + base + i0, ar);
-        load_rows(w + base + i0, wr);
-        load_rows(b + base + i0, br);
-        load_rows(k + base + i0, kr);
-        load_rows(r + base + i0, rr);
-        const float vj = load_elem(v, base + j);
+    constexpr int BLK = STAGED ? TB : 1;
+    for (int t0 = 0; t0 < T; t0 += BLK) {
+        const int nt = min(BLK, T - t0);
+        if constexpr (STAGED) {
+            if (t0 > 0) {
+                __syncthreads();  // the previous block's inputs are no longer read
+                stage_load(t0, nt);
+            }
+#pragma unroll
+            for (int u = 0; u < PER; ++u) {
+                const int e = u * NW * 64 + threadIdx.x;
+                if (e < nt * 6 * kN)
+                    (&xin[0][0][0])[e] = stage[u];
+            }
+            __syncthreads();
+        }
+        for (int tt = 0; tt < nt; ++tt) {
+            const int t = t0 + tt;
+            const size_t base = ((static_cast<size_t>(bb) * T + t) * H + hh) * kN;  // uniform
+            // this wave's rows of a, w, b, k, r (uniform across lanes) and v[j]
+            float ar[RW], wr[RW], br[RW], kr[RW], rr[RW], vj;
+            if constexpr (STAGED) {
+                vj = xin[tt][5][j];
+            } else {
+                load_rows(a + base + i0, ar);
+                load_rows(w + base + i0, wr);
+                load_rows(b + base + i0, br);
+                load_rows(k + base + i0, kr);
+                load_rows(r + base + i0, rr);
+                vj = load_elem(v, base + j);
+            }
+            auto rows4 = [&](int vec, const float (&reg)[RW], int u) -> f32x4 {
+                if constexpr (STAGED)
+                    return *reinterpret_cast<const f32x4 *>(&xin[tt][vec][i0 + u]);
+                else
+                    return f32x4{reg[u], reg[u + 1], reg[u + 2], reg[u + 3]};
+            };
 
-        // sa[j] = a^T S over the state before this token: partial over this wave's rows
-        float sa = 0.0f;
+            // sa[j] = a^T S over the state before this token: partial over this wave's rows
+            float sa = 0.0f;
 #pragma unroll
-        for (int u = 0; u < RW; ++u)
-            sa = fmaf(ar[u], S[u], sa);
-        part_a[t & 1][g][j] = sa;
-        __syncthreads();
-        sa = part_a[t & 1][0][j];
+            for (int u = 0; u < RW; u += 4) {
+                const f32x4 a4 = rows4(0, ar, u);
 #pragma unroll
-        for (int gg = 1; gg < NW; ++gg)
-            sa += part_a[t & 1][gg][j];
-        // S[i][j] = w[i] S[i][j] + b[i] sa[j] + k[i] v[j], then o[j] = r^T S
-        float op = 0.0f;
-#pragma unroll
-        for (int u = 0; u < RW; ++u) {
-            S[u] = fmaf(wr[u], S[u], fmaf(br[u], sa, kr[u] * vj));
-            op = fmaf(rr[u], S[u], op);
-        }
-        if (WRITE_POS) {
-            float *dst = state_pos + ((static_cast<size_t>(bb) * T + t) * H + hh) * (kN * kN) + i0 * kN + j;
-#pragma unroll
-            for (int u = 0; u < RW; ++u)
-                __builtin_nontemporal_store(S[u], dst + u * kN);
-        }
-        part_r[g][j] = op;
-        __syncthreads();
-        if (g == 0) {
-            float acc = part_r[0][j];
+                for (int e = 0; e < 4; ++e)
+                    sa = fmaf(a4[e], S[u + e], sa);
+            }
+            part_a[t & 1][g][j] = sa;
+            __syncthreads();
+            sa = part_a[t & 1][0][j];
 #pragma unroll
             for (int gg = 1; gg < NW; ++gg)
-                acc += part_r[gg][j];
-            store_elem(o, base + j, acc);
+                sa += part_a[t & 1][gg][j];
+            // S[i][j] = w[i] S[i][j] + b[i] sa[j] + k[i] v[j], then o[j] = r^T S
+            float op = 0.0f;
+#pragma unroll
+            for (int u = 0; u < RW; u += 4) {
+                const f32x4 w4 = rows4(1, wr, u), b4 = rows4(2, br, u), k4 = rows4(3, kr, u), r4 = rows4(4, rr, u);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    S[u + e] = fmaf(w4[e], S[u + e], fmaf(b4[e], sa, k4[e] * vj));
+                    op = fmaf(r4[e], S[u + e], op);
+                }
+            }
+            if (WRITE_POS) {
+                float *dst = state_pos + ((static_cast<size_t>(bb) * T + t) * H + hh) * (kN * kN) + i0 * kN + j;
+#pragma unroll
+                for (int u = 0; u < RW; ++u)
+                    __builtin_nontemporal_store(S[u], dst + u * kN);
+            }
+            part_r[g][j] = op;
+            __syncthreads();
+            if (g == 0) {
+                float acc = part_r[0][j];
+#pragma unroll
+                for (int gg = 1; gg < NW; ++gg)
+                    acc += part_r[gg][j];
+                store_elem(o, base + j, acc);
+            }
         }
     }
 #pragma unroll
@@ -119,8 +180,8 @@ __global__ __launch_bounds__(NW * 64) void wkv7_step_kernel(
         __builtin_nontemporal_store(S[u], state_out + sbase + u * kN);
 }
 
-template <typename Tin, typename Tout>
-hipError_t launch_typed(const SeqArgs &p, hipStream_t stream)
+template <typename Tin, typename Tout, bool STAGED>
+hipError_t launch_mode(const SeqArgs &p, hipStream_t stream)
 {
     const dim3 grid(static_cast<unsigned>(p.B) * static_cast<unsigned>(p.H)), block(NW * 64);
     const Tin *r = static_cast<const Tin *>(p.r), *w = static_cast<const Tin *>(p.w);
@@ -128,8 +189,8 @@ hipError_t launch_typed(const SeqArgs &p, hipStream_t stream)
     const Tin *a = static_cast<const Tin *>(p.a), *b = static_cast<const Tin *>(p.b);
     Tout *o = static_cast<Tout *>(p.o);
     const bool sin = p.state_in != nullptr, pos = p.state_pos != nullptr;
-#define WKV7_STEP_LAUNCH(SIN, POS)                                                                        \
-    hipLaunchKernelGGL((wkv7_step_kernel<Tin, Tout, SIN, POS>), grid, block, 0, stream, r, w, k, v, a, b, \
+#define WKV7_STEP_LAUNCH(SIN, POS)                                                                                \
+    hipLaunchKernelGGL((wkv7_step_kernel<Tin, Tout, SIN, POS, STAGED>), grid, block, 0, stream, r, w, k, v, a, b, \
                        p.state_in, o, p.state_out, p.state_pos, p.T, p.H)
     if (sin && pos)
         WKV7_STEP_LAUNCH(true, true);
@@ -141,6 +202,12 @@ hipError_t launch_typed(const SeqArgs &p, hipStream_t stream)
         WKV7_STEP_LAUNCH(false, false);
 #undef WKV7_STEP_LAUNCH
     return hipGetLastError();
+}
+
+template <typename Tin, typename Tout>
+hipError_t launch_typed(const SeqArgs &p, hipStream_t stream)
+{
+    return p.T > 1 ? launch_mode<Tin, Tout, true>(p, stream) : launch_mode<Tin, Tout, false>(p, stream);
 }
 
 // Copy (or zero, when src is null) n_floats of state; n_floats is a multiple of 4.
