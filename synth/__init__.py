@@ -17,7 +17,8 @@ CPU with one ``torch.Generator`` seeded per workload):
   own; the state always stays fp32.
 
 The decay form and the a = -kk, b = kk*a_gate pair are the RWKV-7 inputs of
-the Core AI note, section 1 ("S = diag(exp w) S - (kk*a)(kk^T S)").  Shapes
+the Core AI note, section 1, whose rank-1 term removes the gated projection of
+the state onto the normalised key.  Shapes
 follow the model sizes the pages quote: 0.1B (D=768, 12 heads) in the
 SwiftRWKV Inference guide; 2.9B (32 layers / 2560), 7.2B (32 / 4096) and
 13.3B (61 / 4096) in the RWKV7-MTP-Exp model card; batch 32 (and 16 for
