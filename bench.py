@@ -75,8 +75,8 @@ def read_traffic(kind: str, workload: int):
     cur = kernel_source_hash(kind)
     with open(path) as f:
         for line in f:
-            parts = line.split()
-            if len(parts) == 5 and not line.startswith("#") and parts[0] == kind and parts[1] == str(workload):
+            parts = line.split("#", 1)[0].split()
+            if len(parts) == 5 and parts[0] == kind and parts[1] == str(workload):
                 if parts[2] != cur:
                     return None
                 return int(float(parts[3]) + float(parts[4]))
