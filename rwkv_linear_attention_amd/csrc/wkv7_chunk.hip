@@ -33,16 +33,23 @@
 // MAPPING (gfx950).  One workgroup per (batch, head, block of NC value
 // columns); value columns evolve independently, so a head splits into
 // J = 64/NC blocks with no communication.  The workgroup is a software
-// pipeline with one barrier per chunk:
+// pipeline with one barrier per chunk; in iteration i
 //  * consumer waves (NC/16 of them) each keep a 64x16 slice of the fp32 state
 //    in registers, in the accumulator layout of a 16x16 matrix-core tile, for
-//    the whole sequence, and run only the state-dependent products of chunk c;
-//  * eight producer waves work ahead: four build the intra-chunk matrices of
-//    chunk c+1 (M_ab with the triangular inverse T, M_ak, M_rb, M_rk), four
-//    build the decay-scaled operands of chunk c+2 (A', R', B', K' and v), and
-//    three of them also move the raw input rows of chunk c+3 into a staging
-//    ring in LDS, from 16-byte loads issued two iterations earlier.
-// Chunk data lives in a ring of three LDS slots.  All products run on
+//    the whole sequence, and run only the state-dependent products of chunk i;
+//  * three matrix waves build M_ab, M_ak, M_rb and M_rk of chunk i+1; the
+//    M_ab wave inverts I - M_ab by repeated squaring on the matrix cores,
+//    T = (I + M)(I + M^2)(I + M^4)(I + M^8) (M is strictly lower triangular,
+//    so M^16 = 0), carrying each matrix and its transpose in registers;
+//  * four scale waves form the decay-scaled operands A', R', B', K' (and the
+//    v rows) of chunk i+2, elementwise, from a table of decay factors;
+//  * one decay wave turns the w rows of chunk i+3 into that table.
+// The decay and scale waves load their own input rows from HBM, in their own
+// lane layouts, two iterations ahead; rows past the end of the sequence count
+// as w = 1 and zero vectors.
+// Every operand that a product needs transposed is read with the gfx950 LDS
+// transpose load (ds_read_b64_tr_b16) from row-major storage, so no stage
+// writes a second, transposed copy.  All products run on
 // v_mfma_f32_16x16x{32,16}_bf16 with fp32 accumulation; fp32 operands are
 // split into bf16 pieces (x = x0 + x1 [+ x2], stored pre-split in LDS by the
 // wave that makes them) and the piece products summed, which keeps
@@ -59,30 +66,48 @@ constexpr int CH = 16;             // chunk length
 constexpr int REF = 7;             // decays are measured relative to the state after this position
 constexpr float W_MIN = 0x1p-15f;  // lower bound applied to decay multipliers in this kernel
 constexpr int NPROD = 8;           // producer waves
-constexpr int LDA = kN + 8;        // row pitch (bf16) of [16][64] operand planes
-constexpr int LDT = CH + 8;        // row pitch (bf16) of [64][16] transposed planes and [16][16] planes
-constexpr int LDU = 32 + 8;        // row pitch (bf16) of interleaved [rows][32] planes
-constexpr int LDM = CH + 4;        // row pitch (fp32) of [16][16] scratch matrices (16-byte rows)
-constexpr uint32_t W_MIN_BITS = 0x38000000u;  // 2^-15 as fp32 bits
+constexpr int LDA = kN + 8;        // row pitch (bf16) of [16][64] planes
+constexpr int LDT = CH + 8;        // row pitch (bf16) of [16][16] planes
+constexpr int NDROW = 2 * CH + 1;  // decay table rows: d_0 .. d_16, then id_1 .. id_16
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ uint16_t bf16_bits(float x)
-{
-    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));  // round to nearest even
-}
-__device__ __forceinline__ float bf16_val(uint32_t h) { return __uint_as_float(h << 16); }
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
 
-// x = sum of NP bf16 pieces (to ~2^(-8 NP) relative).
-template <int NP>
-__device__ __forceinline__ void split(float x, uint16_t (&o)[NP])
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 values to a packed pair of bf16 (round to nearest even), element 0 low.
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b)
 {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+
+// Split 2 NW fp32 values into NP planes of packed bf16 pairs: x = x0 + x1 [+ x2]
+// (to ~2^(-8 NP) relative); each piece is the rounded remainder of the ones before.
+template <int NP, int NW>
+__device__ __forceinline__ void split_pk(const float (&v)[2 * NW], uint32_t (&o)[NP][NW])
+{
+    float r[2 * NW];
+#pragma unroll
+    for (int e = 0; e < 2 * NW; ++e)
+        r[e] = v[e];
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
-        o[p] = bf16_bits(x);
-        x -= bf16_val(o[p]);
+#pragma unroll
+        for (int w = 0; w < NW; ++w)
+            o[p][w] = pk_bf16(r[2 * w], r[2 * w + 1]);
+        if (p + 1 < NP) {
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                r[2 * w] -= bf16_lo(o[p][w]);
+                r[2 * w + 1] -= bf16_hi(o[p][w]);
+            }
+        }
     }
 }
 
@@ -119,30 +144,39 @@ __device__ __forceinline__ void mma16(f32x4 &acc, const s16x4 (&A)[NPA], const s
 template <int NP>
 __device__ __forceinline__ void split8(const float (&v)[8], s16x8 (&out)[NP])
 {
+    uint32_t o[NP][4];
+    split_pk<NP, 4>(v, o);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        uint16_t pc[NP];
-        split<NP>(v[e], pc);
-#pragma unroll
-        for (int p = 0; p < NP; ++p)
-            out[p][e] = static_cast<short>(pc[p]);
-    }
+    for (int p = 0; p < NP; ++p)
+        out[p] = __builtin_bit_cast(s16x8, u32x4{o[p][0], o[p][1], o[p][2], o[p][3]});
 }
 template <int NP>
-__device__ __forceinline__ void split4(const float (&v)[4], s16x4 (&out)[NP])
+__device__ __forceinline__ void split4(const f32x4 v, s16x4 (&out)[NP])
 {
+    const float a[4] = {v[0], v[1], v[2], v[3]};
+    uint32_t o[NP][2];
+    split_pk<NP, 2>(a, o);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        uint16_t pc[NP];
-        split<NP>(v[e], pc);
-#pragma unroll
-        for (int p = 0; p < NP; ++p)
-            out[p][e] = static_cast<short>(pc[p]);
-    }
+    for (int p = 0; p < NP; ++p)
+        out[p] = __builtin_bit_cast(s16x4, u32x2{o[p][0], o[p][1]});
 }
 
-__device__ __forceinline__ s16x4 lds4(const uint16_t *p) { return *reinterpret_cast<const s16x4 *>(p); }
 __device__ __forceinline__ s16x8 lds8(const uint16_t *p) { return *reinterpret_cast<const s16x8 *>(p); }
+
+// LDS transpose load of a 16x16 bf16 tile stored row-major as X[k][n]: lane
+// 16 q + i passes the address of X[4 q + i/4][4 (i%4)] (four consecutive n),
+// and lane (n = l%16, q = l/16) receives X[4 q + e][n], e = 0..3 -- the
+// fragment a 16x16x16 matrix-core operand takes over k.  The four n-groups of
+// a row may sit anywhere: each lane names its own.
+__device__ __forceinline__ s16x4 tr4(const uint16_t *p)
+{
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4 *)(p));
+}
+__device__ __forceinline__ s16x8 cat(const s16x4 a, const s16x4 b)
+{
+    return s16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
 
 // Column of key channel i in the row-major operand planes.  A matrix-core
 // lane (q, .) of k-step s consumes key rows 16 (2 s + e/4) + 4 q + e%4,
@@ -153,56 +187,38 @@ __device__ __forceinline__ int key_slot(int i)
 {
     return 32 * (i >> 5) + 8 * ((i >> 2) & 3) + 4 * ((i >> 4) & 1) + (i & 3);
 }
-__device__ __forceinline__ s16x8 cat(const s16x4 a, const s16x4 b)
-{
-    return s16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-}
+// Place of key slot s in a row of the decay table: slots 8 g + 4 h + c go to
+// 32 h + 4 g + c, so that eight lanes reading the first (or second) halves of
+// their eight slots read 128 contiguous bytes.
+__device__ __forceinline__ int dpos(int s) { return 32 * ((s >> 2) & 1) + 4 * (s >> 3) + (s & 3); }
 
-template <int NP, bool ON>
-struct RowMajorBK {
-    uint16_t Bp[NP][CH][LDA];
-    uint16_t Kp[NP][CH][LDA];
-};
-template <int NP>
-struct RowMajorBK<NP, false> {};
-
-// One chunk's data in LDS.  Planes hold bf16 bit patterns.  With bf16
-// inputs (NP == 2) B' and K' are also kept row-major, so the matrix stage
-// reads its operands with 16-byte loads; the fp32-input build (NP == 3) has
-// no room for them and gathers from the transposed copies instead.
-template <int NP, int NPV, int NC>
+// One chunk's operands and matrices in LDS (bf16 bit patterns; NP planes).
+// The 16x16 matrices are stored transposed, [s][tau], as their producers hold
+// them; consumers read them back with transpose loads.
+// Planes are selected by index (never by choosing between pointers), the
+// operands as X[OP_A], X[OP_R], X[OP_B], X[OP_K] and the matrices as
+// Mt[MT_T], Mt[MT_AK], Mt[MT_RB], Mt[MT_RK].
+enum { OP_A = 0, OP_R = 1, OP_B = 2, OP_K = 3 };
+enum { MT_T = 0, MT_AK = 1, MT_RB = 2, MT_RK = 3 };
+template <int NP, int NPV>
 struct alignas(16) Slot {
-    uint16_t Ap[NP][CH][LDA];    // A'[tau][key_slot(i)]
-    uint16_t Rp[NP][CH][LDA];    // R'[tau][key_slot(i)]
-    RowMajorBK<NP, NP == 2> bk;  // B'[s][key_slot(i)], K'[s][key_slot(i)]  (NP == 2 only)
-    uint16_t Ut[NP][kN][LDU];    // [i][8 g + e]: B'[4 g + e][i] for e < 4, K'[4 g + e - 4][i] for e >= 4
-    uint16_t Vt[NPV][NC][LDT];   // v[s][j] stored as [j][s]
-    uint16_t Mak[NP][CH][LDT];   // M_ak (masked)
-    uint16_t Mrr[NP][CH][LDU];   // [tau][8 g + e]: M_rb[tau][4 g + e] for e < 4, M_rk[tau][4 g + e - 4] for e >= 4
-    uint16_t Tp[NP][CH][LDT];    // T = (I - M_ab)^{-1}
-    alignas(16) float p7[kN];    // P_7 per key channel
-    alignas(16) float f[kN];     // d_15 of this chunk times P_7 of the next one (d_15 alone for the last)
+    uint16_t X[4][NP][CH][LDA];   // A'[tau], R'[tau], B'[s], K'[s] over key_slot(i)
+    uint16_t Vr[NPV][CH][LDA];    // v[s][j], all 64 value columns
+    uint16_t Mt[4][NP][CH][LDT];  // T, M_ak, M_rb, M_rk: element [tau][s] stored at [s][tau]
+    alignas(16) float f[kN];      // d_15 of this chunk times P_7 of the next one (d_15 alone for the last)
 };
 
-// Raw bf16 input rows of one chunk, staged by the producers: [stream][tau][i]
-// with streams w, a, r, k, b, v (v holds all 64 columns of the head).
-struct alignas(16) RawSlot {
-    uint16_t x[6][CH][kN];
+// Decay factors of one chunk per key channel, rows d_0 .. d_16 and id_1 .. id_16
+// (d_{tau+1} = P_tau / P_7, id_{tau+1} = P_7 / P_tau), columns at dpos(key_slot(i)).
+struct alignas(16) DSlot {
+    float v[NDROW][kN];
 };
-template <bool ON>
-struct RawRing {
-    RawSlot raw[2];
-};
-template <>
-struct RawRing<false> {};
 
-template <int NP, int NPV, int NC>
+template <int NP, int NPV>
 struct Smem {
-    Slot<NP, NPV, NC> slot[3];
-    RawRing<NP == 2> rr;         // staged raw rows (bf16 inputs only)
-    float Mab[CH][LDM];          // scratch of the wave that builds T
-    float Tf[CH][LDM];           // T in fp32 while it is built
-    float Xs[8][LDM];
+    Slot<NP, NPV> slot[3];
+    DSlot dt[2];
+    alignas(16) float p7[kN];  // P_7 of the first chunk
 };
 
 // Decay factors of one key channel over a chunk: d[tau+1] = P_tau / P_7 and
@@ -235,14 +251,6 @@ __device__ __forceinline__ void decay_factors(const float (&w)[CH], float (&d)[C
     }
 }
 
-// Wait for this wave's outstanding LDS accesses (its writes become visible to
-// its own later reads from other lanes).
-__device__ __forceinline__ void lds_fence_wave()
-{
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
-    __builtin_amdgcn_wave_barrier();
-}
-
 template <typename Tin, typename Tout, int J, bool HAS_STATE_IN>
 __global__ __launch_bounds__((kN / J / 16 + NPROD) * 64) void wkv7_chunk_kernel(SeqArgs p, int per_xcd,
                                                                                    int nblocks)
@@ -252,9 +260,8 @@ __global__ __launch_bounds__((kN / J / 16 + NPROD) * 64) void wkv7_chunk_kernel(
     constexpr bool F32IN = std::is_same<Tin, float>::value;
     constexpr int NP = F32IN ? 3 : 2;     // bf16 pieces of derived fp32 operands
     constexpr int NPV = F32IN ? 3 : 1;    // pieces of v (one is exact for bf16 inputs)
-    constexpr bool STAGED = !F32IN;       // bf16 rows go through the LDS staging ring
-    using SlotT = Slot<NP, NPV, NC>;
-    __shared__ Smem<NP, NPV, NC> sm;
+    using SlotT = Slot<NP, NPV>;
+    __shared__ Smem<NP, NPV> sm;
 
     // Workgroup -> (batch*head, column block).  Workgroups are dealt to the
     // XCDs round-robin; the J column blocks of one head stay on one XCD so the
@@ -273,11 +280,13 @@ __global__ __launch_bounds__((kN / J / 16 + NPROD) * 64) void wkv7_chunk_kernel(
     const size_t head0 = (static_cast<size_t>(bb) * T * H + hh) * kN;   // (b, t=0, h, 0)
     const size_t sbase = static_cast<size_t>(bh) * (kN * kN);
     const int nchunks = (T + CH - 1) / CH;
+    // Pipeline depth: iteration i consumes chunk i, builds the matrices of
+    // chunk i+1, the operands of chunk i+2 and the decay table of chunk i+3.
+    constexpr int I0 = -4;
 
     if (wv < NSW) {
         // ------------------------------------------------------------ consumer
         const int jw = j0 + 16 * wv;      // this wave's first state column
-        const int jl = 16 * wv + m;       // this lane's column inside the workgroup block
         Tout *__restrict__ go = static_cast<Tout *>(p.o);
         // Sx[pt][e] holds row 16 pt + 4 q + e, column jw + m of the state: the input
         // state before the first chunk, S^ of the coming chunk between chunks, and
@@ -288,10 +297,10 @@ __global__ __launch_bounds__((kN / J / 16 + NPROD) * 64) void wkv7_chunk_kernel(
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 Sx[pt][e] = HAS_STATE_IN ? p.state_in[sbase + (16 * pt + 4 * q + e) * kN + jw + m] : 0.0f;
+        // transpose-load address pieces of this lane: row 4 q + m/4, column group m%4
+        const int trow = 4 * q + (m >> 2), tcol = 4 * (m & 3);
 
-        if constexpr (STAGED)
-            __syncthreads();  // matches the producers' prologue
-        for (int i = -2; i < nchunks; ++i) {
+        for (int i = I0; i < nchunks; ++i) {
             if (i >= 0) {
                 const SlotT &sl = sm.slot[i % 3];
                 const int t0 = i * CH;
@@ -300,7 +309,7 @@ __global__ __launch_bounds__((kN / J / 16 + NPROD) * 64) void wkv7_chunk_kernel(
                     // leaves S^ of the next one (its row factor folds both scalings).
 #pragma unroll
                     for (int pt = 0; pt < 4; ++pt) {
-                        const f32x4 p7v = *reinterpret_cast<const f32x4 *>(&sl.p7[16 * pt + 4 * q]);
+                        const f32x4 p7v = *reinterpret_cast<const f32x4 *>(&sm.p7[16 * pt + 4 * q]);
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
                             Sx[pt][e] *= p7v[e];
@@ -326,8 +335,8 @@ __global__ __launch_bounds__((kN / J / 16 + NPROD) * 64) void wkv7_chunk_kernel(
                     s16x8 Af[NP], Rf[NP];
 #pragma unroll
                     for (int pl = 0; pl < NP; ++pl) {
-                        Af[pl] = lds8(&sl.Ap[pl][m][32 * s + 8 * q]);
-                        Rf[pl] = lds8(&sl.Rp[pl][m][32 * s + 8 * q]);
+                        Af[pl] = lds8(&sl.X[OP_A][pl][m][32 * s + 8 * q]);
+                        Rf[pl] = lds8(&sl.X[OP_R][pl][m][32 * s + 8 * q]);
                     }
                     y2[s] = f32x4{0.f, 0.f, 0.f, 0.f};
                     o2[s] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -338,27 +347,27 @@ __global__ __launch_bounds__((kN / J / 16 + NPROD) * 64) void wkv7_chunk_kernel(
                 s16x4 Vf[NPV];
 #pragma unroll
                 for (int pl = 0; pl < NPV; ++pl)
-                    Vf[pl] = lds4(&sl.Vt[pl][jl][4 * q]);
+                    Vf[pl] = tr4(&sl.Vr[pl][trow][jw + tcol]);
                 // M_ak V
                 f32x4 ym = {0.f, 0.f, 0.f, 0.f};
                 {
                     s16x4 Mf[NP];
 #pragma unroll
                     for (int pl = 0; pl < NP; ++pl)
-                        Mf[pl] = lds4(&sl.Mak[pl][m][4 * q]);
+                        Mf[pl] = tr4(&sl.Mt[MT_AK][pl][trow][tcol]);
                     mma16<NP, NPV>(ym, Mf, Vf);
                 }
                 // Z = T Y  (Y = A' S^ + M_ak V in accumulator layout: Y[4 q + e][col m])
                 f32x4 z = {0.f, 0.f, 0.f, 0.f};
                 {
-                    float y4[4];
+                    f32x4 y4;
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
                         y4[e] = (y2[0][e] + y2[1][e]) + ym[e];
                     s16x4 Tf[NP], Yf[NP];
 #pragma unroll
                     for (int pl = 0; pl < NP; ++pl)
-                        Tf[pl] = lds4(&sl.Tp[pl][m][4 * q]);
+                        Tf[pl] = tr4(&sl.Mt[MT_T][pl][trow][tcol]);
                     split4<NP>(y4, Yf);
                     mma16<NP, NP>(z, Tf, Yf);
                 }
@@ -366,9 +375,8 @@ __global__ __launch_bounds__((kN / J / 16 + NPROD) * 64) void wkv7_chunk_kernel(
                 // (this lane's z[e]), (q, e>=4) is V row 4q+e-4.
                 s16x8 ZV[NP];
                 {
-                    const float z4[4] = {z[0], z[1], z[2], z[3]};
                     s16x4 Zf[NP];
-                    split4<NP>(z4, Zf);
+                    split4<NP>(z, Zf);
 #pragma unroll
                     for (int pl = 0; pl < NP; ++pl)
                         ZV[pl] = cat(Zf[pl], pl < NPV ? Vf[pl < NPV ? pl : 0] : s16x4{0, 0, 0, 0});
@@ -379,7 +387,7 @@ __global__ __launch_bounds__((kN / J / 16 + NPROD) * 64) void wkv7_chunk_kernel(
                     s16x8 Mf[NP];
 #pragma unroll
                     for (int pl = 0; pl < NP; ++pl)
-                        Mf[pl] = lds8(&sl.Mrr[pl][m][8 * q]);
+                        Mf[pl] = cat(tr4(&sl.Mt[MT_RB][pl][trow][tcol]), tr4(&sl.Mt[MT_RK][pl][trow][tcol]));
                     mma32<NP, NP>(o3, Mf, ZV);
                 }
 #pragma unroll
@@ -389,13 +397,16 @@ __global__ __launch_bounds__((kN / J / 16 + NPROD) * 64) void wkv7_chunk_kernel(
                         store_elem(go, head0 + static_cast<size_t>(t0 + tau) * rowstride + jw + m,
                                    (o2[0][e] + o2[1][e]) + o3[e]);
                 }
-                // S^ <- diag(f) (S^ + [B'^T | K'^T] [Z ; V]), one 16-row tile at a time
+                // S^ <- diag(f) (S^ + [B'^T | K'^T] [Z ; V]), one 16-row tile at a time;
+                // the [B'^T | K'^T] fragment of key rows 16 pt .. 16 pt + 15 comes from the
+                // row-major B' and K' planes by transpose loads.
 #pragma unroll
                 for (int pt = 0; pt < 4; ++pt) {
+                    const int ukey = key_slot(16 * pt + tcol);
                     s16x8 Uf[NP];
 #pragma unroll
                     for (int pl = 0; pl < NP; ++pl)
-                        Uf[pl] = lds8(&sl.Ut[pl][16 * pt + m][8 * q]);
+                        Uf[pl] = cat(tr4(&sl.X[OP_B][pl][trow][ukey]), tr4(&sl.X[OP_K][pl][trow][ukey]));
                     f32x4 acc = {Sx[pt][0], Sx[pt][1], Sx[pt][2], Sx[pt][3]};
                     mma32<NP, NP>(acc, Uf, ZV);
                     const f32x4 fv = *reinterpret_cast<const f32x4 *>(&sl.f[16 * pt + 4 * q]);
@@ -415,323 +426,320 @@ __global__ __launch_bounds__((kN / J / 16 + NPROD) * 64) void wkv7_chunk_kernel(
     }
 
     // ---------------------------------------------------------------- producers
-    //   pw 0: M_ab and T                pw 4: A'  (from w, a)
-    //   pw 1: M_ak, stages w a          pw 5: R'  (from w, r)
-    //   pw 2: M_rb, stages r k          pw 6: B'  (from w, b), P_7 and d_15
-    //   pw 3: M_rk, stages b v          pw 7: K'  (from w, k) and v
-    const int pw = wv - NSW;
-    const bool stager = pw >= 1 && pw <= 3;
-    const bool maker = pw >= 4;
+    // Roles.  Waves go to the SIMDs round-robin (wave w on SIMD w % 4), so the
+    // role table spreads the heavy producers (T, decay, K' with v) over
+    // different SIMDs for every J.
+    //   R_T : M_ab and T            R_D : decay table (from w)
+    //   R_MA: M_ak                  R_SA, R_SR, R_SB, R_SK: A', R', B', K' (R_SK also v)
+    //   R_MR: M_rb, M_rk
+    enum { R_T = 0, R_MA = 1, R_MR = 2, R_D = 3, R_SA = 4, R_SR = 5, R_SB = 6, R_SK = 7 };
+    const int role = (0x61542730 >> (4 * (wv - NSW))) & 15;  // T D SK MR SA SR MA SB
+    const int t_end = T;
 
-    // ---- input path
-    // STAGED: waves 1..3 each own two of the six input streams and move them,
-    // as 16-byte pieces of whole 128-byte rows, from HBM to the staging ring:
-    // the loads of chunk c are issued in iteration c-5, written to ring slot
-    // c%2 in iteration c-3 and read by the operand makers in iteration c-2.
-    // Otherwise (fp32 inputs) the operand makers load straight into registers.
-    const uint16_t *gs0 = static_cast<const uint16_t *>(pw == 1 ? p.w : pw == 2 ? p.r : p.b);
-    const uint16_t *gs1 = static_cast<const uint16_t *>(pw == 1 ? p.a : pw == 2 ? p.k : p.v);
-    const int sidx0 = pw == 1 ? 0 : pw == 2 ? 2 : 4;
-    const int sidx1 = sidx0 + 1;
-    struct Stage {
-        u32x4 v[2][2];  // [stream][half]: row 8*half + lane/8, elements 8*(lane%8) .. +8
-    };
-    Stage sa, sb;
-    auto stage_load = [&](Stage &S, int c) {
-        if constexpr (STAGED) {
-            if (!stager || c >= nchunks)
-                return;
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int t = min(c * CH + 8 * h + (lane >> 3), T - 1);
-                const size_t off = head0 + static_cast<size_t>(t) * rowstride + 8 * (lane & 7);
-                S.v[0][h] = *reinterpret_cast<const u32x4 *>(gs0 + off);
-                S.v[1][h] = *reinterpret_cast<const u32x4 *>(gs1 + off);
-            }
-        }
-    };
-    auto stage_store = [&](const Stage &S, int c) {
-        if constexpr (STAGED) {
-            if (!stager || c >= nchunks)
-                return;
-            RawSlot &rs = sm.rr.raw[c & 1];
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int tau = 8 * h + (lane >> 3);
-                *reinterpret_cast<u32x4 *>(&rs.x[sidx0][tau][8 * (lane & 7)]) = S.v[0][h];
-                *reinterpret_cast<u32x4 *>(&rs.x[sidx1][tau][8 * (lane & 7)]) = S.v[1][h];
-            }
-        }
-    };
-    // operand makers: the stream each one scales, and (wave 7) v
-    const int xs = pw == 4 ? 1 : pw == 5 ? 2 : pw == 6 ? 4 : 3;   // a, r, b, k
-    const int vcol = j0 + (lane < NC ? lane : 0);
+    // ---- input path: the decay and scale waves load their own rows, in their
+    // own lane layouts, two iterations ahead of use, into alternating register
+    // sets (rows past the end are clamped here and masked where they are used).
+    const int op = role - R_SA;                       // scale waves: OP_A, OP_R, OP_B, OP_K
     const Tin *__restrict__ gw = static_cast<const Tin *>(p.w);
-    const Tin *__restrict__ gx =
-        static_cast<const Tin *>(pw == 4 ? p.a : pw == 5 ? p.r : pw == 6 ? p.b : p.k);
+    const Tin *__restrict__ gx = static_cast<const Tin *>((op & 2) ? ((op & 1) ? p.k : p.b) : ((op & 1) ? p.r : p.a));
     const Tin *__restrict__ gv = static_cast<const Tin *>(p.v);
+    const int g8 = lane & 7;                          // scale waves: slot group of this lane
+    const int k0 = 32 * (g8 >> 2) + 4 * (g8 & 3);     // its keys: k0 .. k0+3 and k0+16 .. k0+19
+    // One register set holds, as 32-bit words, either the decay wave's w[tau]
+    // (16 words) or a scale wave's rows: key runs x[pass][run] (words XW(pass,
+    // run) ..) and, for R_SK, the v row of each pass (words VW(pass) ..).
+    constexpr int EW = F32IN ? 1 : 2;                 // input elements per word
+    constexpr int XRW = 4 / EW;                       // words of a four-key run
+    constexpr int VRW = 8 / EW;                       // words of an eight-column v row piece
+    constexpr int NU = 4 * XRW + 2 * VRW > CH ? 4 * XRW + 2 * VRW : CH;
     struct Raw {
-        Tin w[CH], x[CH], v[CH];
+        uint32_t u[NU];
     };
-    Raw ra, rb;
-    auto reg_load = [&](Raw &R, int c) {
-        if constexpr (!STAGED) {
-            if (!maker || c >= nchunks)
-                return;
+    auto XW = [](int pz, int h) { return (2 * pz + h) * XRW; };
+    auto VW = [](int pz) { return 4 * XRW + pz * VRW; };
+    // Loads are unconditional (a chunk past the end re-reads the last one, which
+    // is never used): a load under a branch makes the compiler wait for it at
+    // the join, right after issuing it.
+    auto load_w = [&](Raw &R, int c) {
+        c = min(c, nchunks - 1);
 #pragma unroll
-            for (int tau = 0; tau < CH; ++tau) {
-                const int t = min(c * CH + tau, T - 1);
-                const size_t row = head0 + static_cast<size_t>(t) * rowstride;
-                R.w[tau] = gw[row + lane];
-                R.x[tau] = gx[row + lane];
-                if (pw == 7)
-                    R.v[tau] = gv[row + vcol];
+        for (int tau = 0; tau < CH; ++tau) {
+            const int t = min(c * CH + tau, t_end - 1);
+            const Tin x = gw[head0 + static_cast<size_t>(t) * rowstride + lane];
+            if constexpr (F32IN)
+                R.u[tau] = __float_as_uint(x);
+            else
+                R.u[tau] = x;
+        }
+    };
+    auto load_x = [&](Raw &R, int c, auto with_v) {
+        c = min(c, nchunks - 1);
+#pragma unroll
+        for (int pz = 0; pz < 2; ++pz) {
+            const int t = min(c * CH + 8 * pz + (lane >> 3), t_end - 1);
+            const size_t row = head0 + static_cast<size_t>(t) * rowstride;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const uint32_t *src = reinterpret_cast<const uint32_t *>(gx + row + k0 + 16 * h);
+                if constexpr (F32IN) {
+                    const u32x4 x4 = *reinterpret_cast<const u32x4 *>(src);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        R.u[XW(pz, h) + e] = x4[e];
+                } else {
+                    const u32x2 x2 = *reinterpret_cast<const u32x2 *>(src);
+                    R.u[XW(pz, h)] = x2[0];
+                    R.u[XW(pz, h) + 1] = x2[1];
+                }
+            }
+            if constexpr (decltype(with_v)::value) {
+                const uint32_t *src = reinterpret_cast<const uint32_t *>(gv + row + 8 * g8);
+#pragma unroll
+                for (int h = 0; h < VRW / 4; ++h) {
+                    const u32x4 v4 = *reinterpret_cast<const u32x4 *>(src + 4 * h);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        R.u[VW(pz) + 4 * h + e] = v4[e];
+                }
             }
         }
     };
 
-    // ---- operand stage (waves 4..7): decay-scaled operands of chunk c into its slot
-    const int ks = key_slot(lane);
-    float prev_d15 = 0.0f;  // wave 6: d_15 of the chunk before (its row factor is finished here)
-    auto operands = [&](const Raw &R, int c) {
-        if (!maker || c >= nchunks)
+    // ---- decay wave: the factor table of chunk c, P_7 of chunk 0, and the row
+    // factor f of chunk c-1 (d_15 of c-1 times P_7 of c; d_15 alone once c is
+    // past the end).
+    float prev_d15 = 1.0f;
+    auto decay = [&](const Raw &R, int c) {
+        if (c < 0 || c > nchunks)
             return;
-        SlotT &sl = sm.slot[c % 3];
-        const int t0 = c * CH, i = lane;
-        float w[CH], x[CH], v[CH];
-        if constexpr (STAGED) {
-            const RawSlot &rs = sm.rr.raw[c & 1];
-            // Read every row (rows past the end hold valid, clamped data) before
-            // any use, so the reads are not split by branches.
-            uint32_t rw[CH], rx[CH], rv[CH];
-#pragma unroll
-            for (int tau = 0; tau < CH; ++tau) {
-                rw[tau] = rs.x[0][tau][i];
-                rx[tau] = rs.x[xs][tau][i];
-                rv[tau] = rs.x[5][tau][vcol];
-            }
-            if (t0 + CH <= T) {
-#pragma unroll
-                for (int tau = 0; tau < CH; ++tau) {
-                    w[tau] = __uint_as_float(max(rw[tau] << 16, W_MIN_BITS));
-                    x[tau] = bf16_val(rx[tau]);
-                    v[tau] = bf16_val(rv[tau]);
-                }
-            } else {
-                // last, partial chunk: positions past the end act as w = 1 and zero vectors
-#pragma unroll
-                for (int tau = 0; tau < CH; ++tau) {
-                    const uint32_t keep = t0 + tau < T ? 0xffffu : 0u;  // uniform
-                    w[tau] = __uint_as_float(max(((rw[tau] & keep) | (0x3f80u & ~keep)) << 16, W_MIN_BITS));
-                    x[tau] = bf16_val(rx[tau] & keep);
-                    v[tau] = bf16_val(rv[tau] & keep);
-                }
-            }
-        } else {
-#pragma unroll
-            for (int tau = 0; tau < CH; ++tau) {
-                const bool ok = t0 + tau < T;
-                w[tau] = ok ? fmaxf(load_elem(R.w, tau), W_MIN) : 1.0f;
-                x[tau] = ok ? load_elem(R.x, tau) : 0.0f;
-                v[tau] = (ok && pw == 7) ? load_elem(R.v, tau) : 0.0f;
-            }
+        const int i = lane;
+        if (c == nchunks) {
+            sm.slot[(c - 1) % 3].f[i] = prev_d15;
+            return;
         }
+        float w[CH];
+#pragma unroll
+        for (int tau = 0; tau < CH; ++tau)
+            w[tau] = c * CH + tau < t_end ? fmaxf(F32IN ? __uint_as_float(R.u[tau]) : bf16_lo(R.u[tau]), W_MIN)
+                                          : 1.0f;  // past the end: 1
         float d[CH + 1], id[CH + 1];
         decay_factors(w, d, id);
-        if (pw == 4 || pw == 5) {
-            // A' (wave 4) or R' (wave 5): row-major, key columns in key_slot order
-            uint16_t(*dst)[CH][LDA] = pw == 4 ? sl.Ap : sl.Rp;
+        DSlot &D = sm.dt[c & 1];
+        const int ps = dpos(key_slot(i));
 #pragma unroll
-            for (int tau = 0; tau < CH; ++tau) {
-                uint16_t pc[NP];
-                split<NP>(x[tau] * (pw == 4 ? d[tau] : d[tau + 1]), pc);
+        for (int r = 0; r <= CH; ++r)
+            D.v[r][ps] = d[r];
 #pragma unroll
-                for (int pl = 0; pl < NP; ++pl)
-                    dst[pl][tau][ks] = pc[pl];
-            }
+        for (int r = 1; r <= CH; ++r)
+            D.v[CH + r][ps] = id[r];
+        if (c == 0)
+            sm.p7[i] = id[0];
+        else
+            sm.slot[(c - 1) % 3].f[i] = prev_d15 * id[0];
+        prev_d15 = d[CH];
+    };
+
+    // ---- scale waves: X' = x * factor, elementwise, lane = (token, slot group):
+    // token 8 pass + lane/8, key slots 8 g8 .. 8 g8 + 7.
+    auto scale = [&](const Raw &R, int c, auto with_v) {
+        if (c < 0 || c >= nchunks)
             return;
-        }
-        // B' (wave 6) or K' (wave 7): the interleaved transposed planes (four runs
-        // of four tokens per key row) and, with bf16 inputs, the row-major copy
-        const int half = pw == 6 ? 0 : 4;
-        s16x4 g4[NP][4];
+        SlotT &sl = sm.slot[c % 3];
+        const DSlot &D = sm.dt[c & 1];
+        const int roff = op == 0 ? 0 : op == 1 ? 1 : CH + 1;  // table row of token tau
+        const bool partial = c * CH + CH > t_end;  // uniform; rows past the end read as 0
 #pragma unroll
-        for (int s2 = 0; s2 < CH; ++s2) {
-            uint16_t pc[NP];
-            split<NP>(x[s2] * id[s2 + 1], pc);
+        for (int pz = 0; pz < 2; ++pz) {
+            const int tau = 8 * pz + (lane >> 3);
+            float x[8];
 #pragma unroll
-            for (int pl = 0; pl < NP; ++pl) {
-                g4[pl][s2 >> 2][s2 & 3] = static_cast<short>(pc[pl]);
-                if constexpr (NP == 2)
-                    (pw == 6 ? sl.bk.Bp : sl.bk.Kp)[pl][s2][ks] = pc[pl];
-            }
-        }
+            for (int h = 0; h < 2; ++h) {
+                if constexpr (F32IN) {
 #pragma unroll
-        for (int pl = 0; pl < NP; ++pl)
-#pragma unroll
-            for (int g = 0; g < 4; ++g)
-                *reinterpret_cast<s16x4 *>(&sl.Ut[pl][i][8 * g + half]) = g4[pl][g];
-        if (pw == 6) {
-            // P_7 of this chunk; row factor d_15 * P_7(next) of the previous chunk,
-            // and of this one when it is the last
-            sl.p7[i] = id[0];
-            if (c > 0)
-                sm.slot[(c + 2) % 3].f[i] = prev_d15 * id[0];
-            prev_d15 = d[CH];
-            if (c == nchunks - 1)
-                sl.f[i] = d[CH];
-        } else if (lane < NC) {
-            // v column j0 + lane over the chunk, transposed
-#pragma unroll
-            for (int pl = 0; pl < NPV; ++pl) {
-                s16x8 vlo, vhi;
-#pragma unroll
-                for (int s2 = 0; s2 < CH; ++s2) {
-                    uint16_t pc[NPV];
-                    split<NPV>(v[s2], pc);
-                    if (s2 < 8)
-                        vlo[s2] = static_cast<short>(pc[pl]);
-                    else
-                        vhi[s2 - 8] = static_cast<short>(pc[pl]);
+                    for (int e = 0; e < 4; ++e)
+                        x[4 * h + e] = __uint_as_float(R.u[XW(pz, h) + e]);
+                } else {
+                    x[4 * h + 0] = bf16_lo(R.u[XW(pz, h)]);
+                    x[4 * h + 1] = bf16_hi(R.u[XW(pz, h)]);
+                    x[4 * h + 2] = bf16_lo(R.u[XW(pz, h) + 1]);
+                    x[4 * h + 3] = bf16_hi(R.u[XW(pz, h) + 1]);
                 }
-                *reinterpret_cast<s16x8 *>(&sl.Vt[pl][lane][0]) = vlo;
-                *reinterpret_cast<s16x8 *>(&sl.Vt[pl][lane][8]) = vhi;
+            }
+            if (partial && c * CH + tau >= t_end) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    x[e] = 0.0f;
+            }
+            const f32x4 d0 = *reinterpret_cast<const f32x4 *>(&D.v[roff + tau][4 * g8]);
+            const f32x4 d1 = *reinterpret_cast<const f32x4 *>(&D.v[roff + tau][32 + 4 * g8]);
+            float y[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                y[e] = x[e] * d0[e];
+                y[4 + e] = x[4 + e] * d1[e];
+            }
+            s16x8 pc[NP];
+            split8<NP>(y, pc);
+#pragma unroll
+            for (int pl = 0; pl < NP; ++pl)
+                *reinterpret_cast<s16x8 *>(&sl.X[op][pl][tau][8 * g8]) = pc[pl];
+        }
+        if constexpr (decltype(with_v)::value) {
+            // v rows of the chunk (all 64 columns), row-major: lane -> row 8 pass + lane/8,
+            // columns 8 g8 .. 8 g8 + 7
+#pragma unroll
+            for (int pz = 0; pz < 2; ++pz) {
+                const int s = 8 * pz + (lane >> 3);
+                const bool live = !partial || c * CH + s < t_end;
+                if constexpr (F32IN) {
+                    float v8[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        v8[e] = live ? __uint_as_float(R.u[VW(pz) + e]) : 0.0f;
+                    s16x8 pc[NPV];
+                    split8<NPV>(v8, pc);
+#pragma unroll
+                    for (int pl = 0; pl < NPV; ++pl)
+                        *reinterpret_cast<s16x8 *>(&sl.Vr[pl][s][8 * g8]) = pc[pl];
+                } else {
+                    const u32x4 v4 = {R.u[VW(pz)], R.u[VW(pz) + 1], R.u[VW(pz) + 2], R.u[VW(pz) + 3]};
+                    *reinterpret_cast<u32x4 *>(&sl.Vr[0][s][8 * g8]) = live ? v4 : u32x4{0u, 0u, 0u, 0u};
+                }
             }
         }
     };
 
-    // ---- matrix stage (waves 0..3): one 16x16 tile M = tril(X' Y'^T) of chunk c
-    // per wave over the 64 key channels; wave 0 then inverts I - M_ab.
+    // ---- matrix waves: 16x16 tiles M = tril(X' Y'^T) of chunk c over the 64 key
+    // channels, stored transposed; R_T also inverts I - M_ab.
     auto matrices = [&](int c) {
-        if (maker || c < 0 || c >= nchunks)
+        if (c < 0 || c >= nchunks)
             return;
         SlotT &sl = sm.slot[c % 3];
-        const uint16_t(*X)[CH][LDA] = pw <= 1 ? sl.Ap : sl.Rp;
-        const bool yb = pw == 0 || pw == 2;  // Y' = B' (else K')
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        const int xo = role == R_MR ? OP_R : OP_A;
+        const int yo = role == R_MA ? OP_K : OP_B;       // R_T: (A',B'); R_MA: (A',K'); R_MR: (R',B') and (R',K')
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             s16x8 Af[NP], Bf[NP];
 #pragma unroll
             for (int pl = 0; pl < NP; ++pl) {
-                Af[pl] = *reinterpret_cast<const s16x8 *>(&X[pl][m][32 * s + 8 * q]);
-                if constexpr (NP == 2) {
-                    Bf[pl] = *reinterpret_cast<const s16x8 *>(&(yb ? sl.bk.Bp : sl.bk.Kp)[pl][m][32 * s + 8 * q]);
-                } else {
-                    // key slot (q, e) of k-step s is key 16 (2 s + e/4) + 4 q + e%4
-                    const int col = 8 * (m >> 2) + (yb ? 0 : 4) + (m & 3);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        Bf[pl][e] = static_cast<short>(sl.Ut[pl][16 * (2 * s + e / 4) + 4 * q + (e & 3)][col]);
-                }
+                Af[pl] = lds8(&sl.X[xo][pl][m][32 * s + 8 * q]);
+                Bf[pl] = lds8(&sl.X[yo][pl][m][32 * s + 8 * q]);
             }
-            mma32<NP, NP>(acc, Af, Bf);
+            mma32<NP, NP>(acc, Af, Bf);           // lane (m, q): M[4 q + e][m]
+            if (role == R_T) {
+                mma32<NP, NP>(acc2, Bf, Af);      // lane (m, q): M[m][4 q + e]
+            } else if (role == R_MR) {
+                s16x8 Kf[NP];
+#pragma unroll
+                for (int pl = 0; pl < NP; ++pl)
+                    Kf[pl] = lds8(&sl.X[OP_K][pl][m][32 * s + 8 * q]);
+                mma32<NP, NP>(acc2, Af, Kf);      // M_rk
+            }
         }
-        const bool strict = pw < 2;  // a rows exclude the diagonal, r rows include it
-        if (pw > 0) {
+        if (role != R_T) {
+            // a rows exclude the diagonal, r rows include it
+            f32x4 mv, mv2;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int tau = 4 * q + e;
-                uint16_t pc[NP];
-                split<NP>((m < tau || (!strict && m == tau)) ? acc[e] : 0.0f, pc);
+                const bool keep = m < tau || (role == R_MR && m == tau);
+                mv[e] = keep ? acc[e] : 0.0f;
+                mv2[e] = keep ? acc2[e] : 0.0f;
+            }
+            s16x4 pc[NP];
+            split4<NP>(mv, pc);
+            const int mt = role == R_MA ? MT_AK : MT_RB;
 #pragma unroll
-                for (int pl = 0; pl < NP; ++pl) {
-                    if (pw == 1)
-                        sl.Mak[pl][tau][m] = pc[pl];
-                    else
-                        sl.Mrr[pl][tau][8 * (m >> 2) + (pw == 2 ? 0 : 4) + (m & 3)] = pc[pl];
-                }
+            for (int pl = 0; pl < NP; ++pl)
+                *reinterpret_cast<s16x4 *>(&sl.Mt[mt][pl][m][4 * q]) = pc[pl];
+            if (role == R_MR) {
+                split4<NP>(mv2, pc);
+#pragma unroll
+                for (int pl = 0; pl < NP; ++pl)
+                    *reinterpret_cast<s16x4 *>(&sl.Mt[MT_RK][pl][m][4 * q]) = pc[pl];
             }
             return;
         }
+        // T = (I - M)^{-1} = (I + M)(I + M^2)(I + M^4)(I + M^8) for strictly lower M.
+        // A matrix X enters a product as the A operand through the accumulator of
+        // X^T and as the B operand through its own accumulator, so every product
+        // is formed together with the transpose the next one needs.
+        f32x4 P, Pt, Q, Qt;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int tau = 4 * q + e;
-            sm.Mab[tau][m] = m < tau ? acc[e] : 0.0f;
+            P[e] = m < tau ? acc[e] : 0.0f;     // M[tau][m]
+            Pt[e] = tau < m ? acc2[e] : 0.0f;   // M^T[tau][m] = M[m][tau]
+            Q[e] = P[e] + (m == tau ? 1.0f : 0.0f);
+            Qt[e] = Pt[e] + (m == tau ? 1.0f : 0.0f);
         }
-        // (I - M_ab)^{-1} in 8x8 blocks: T11 = (I - M11)^{-1} and T22 = (I - M22)^{-1}
-        // by forward substitution (lanes 0..7 and 8..15, one column each), then
-        // T21 = T22 (M21 T11) with one entry per lane; finally split into planes.
-        lds_fence_wave();
-        if (lane < CH) {
-            const int off = lane < 8 ? 0 : 8, col = lane - off;
-            float x[8];
 #pragma unroll
-            for (int t = 0; t < 8; ++t)
-                x[t] = t == col ? 1.0f : 0.0f;
-#pragma unroll
-            for (int s2 = 0; s2 < 8; ++s2)
-#pragma unroll
-                for (int t = s2 + 1; t < 8; ++t)
-                    x[t] = fmaf(sm.Mab[off + t][off + s2], x[s2], x[t]);
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                sm.Tf[off + t][off + col] = x[t];
-                if (off == 0)
-                    sm.Tf[t][8 + col] = 0.0f;  // upper-right block
-            }
+        for (int lvl = 0; lvl < 3; ++lvl) {
+            s16x4 Ps[NP], Pts[NP];
+            split4<NP>(P, Ps);
+            split4<NP>(Pt, Pts);
+            f32x4 Pn = {0.f, 0.f, 0.f, 0.f}, Ptn = {0.f, 0.f, 0.f, 0.f};
+            mma16<NP, NP>(Pn, Pts, Ps);          // P P
+            if (lvl < 2)
+                mma16<NP, NP>(Ptn, Ps, Pts);     // (P P)^T = P^T P^T
+            s16x4 Qts[NP], Pns[NP];
+            split4<NP>(Qt, Qts);
+            split4<NP>(Pn, Pns);
+            f32x4 Qn = Q, Qtn = Qt;
+            mma16<NP, NP>(Qn, Qts, Pns);         // Q + Q Pn
+            if (lvl < 2)
+                mma16<NP, NP>(Qtn, Pns, Qts);    // Q^T + Pn^T Q^T
+            P = Pn;
+            Pt = Ptn;
+            Q = Qn;
+            Qt = Qtn;
         }
-        lds_fence_wave();
-        const int r8 = lane >> 3, c8 = lane & 7;
-        float xv = 0.0f;
-#pragma unroll
-        for (int k = 0; k < 8; ++k)
-            xv = fmaf(sm.Mab[8 + r8][k], sm.Tf[k][c8], xv);
-        sm.Xs[r8][c8] = xv;
-        lds_fence_wave();
-        float tv = 0.0f;
-#pragma unroll
-        for (int k = 0; k < 8; ++k)
-            tv = fmaf(sm.Tf[8 + r8][8 + k], sm.Xs[k][c8], tv);
-        sm.Tf[8 + r8][c8] = tv;
-        lds_fence_wave();
-        // planes: lane -> row lane/4, columns 4 (lane%4) .. +4
-        const int tr = lane >> 2, tc = 4 * (lane & 3);
-        const f32x4 tq = *reinterpret_cast<const f32x4 *>(&sm.Tf[tr][tc]);
-        const float t4[4] = {tq[0], tq[1], tq[2], tq[3]};
         s16x4 tp[NP];
-        split4<NP>(t4, tp);
+        split4<NP>(Q, tp);
 #pragma unroll
         for (int pl = 0; pl < NP; ++pl)
-            *reinterpret_cast<s16x4 *>(&sl.Tp[pl][tr][tc]) = tp[pl];
+            *reinterpret_cast<s16x4 *>(&sl.Mt[MT_T][pl][m][4 * q]) = tp[pl];
     };
 
-    // Pipeline: iteration i consumes chunk i (consumer waves), builds the
-    // matrices of chunk i+1 and the operands of chunk i+2 (reading ring slot
-    // (i+2)%2), writes the staged rows of chunk i+3 into the other ring slot
-    // and issues the loads of chunk i+5 (fp32 inputs: loads of chunk i+4).
-    // Register sets alternate between even and odd iterations.
-    if constexpr (STAGED) {
-        stage_load(sa, 0);
-        stage_load(sb, 1);
-        stage_store(sa, 0);
-        stage_load(sa, 2);
-        __syncthreads();  // ring slot 0 holds chunk 0 (matched by the consumers)
-    } else {
-        reg_load(ra, 0);
-        reg_load(rb, 1);
-    }
-    for (int i = -2; i < nchunks; i += 2) {
-        matrices(i + 1);
-        operands(ra, i + 2);
-        if constexpr (STAGED) {
-            stage_store(sb, i + 3);
-            stage_load(sb, i + 5);
-        } else {
-            reg_load(ra, i + 4);
-        }
-        __syncthreads();
-        if (i + 1 < nchunks) {
-            matrices(i + 2);
-            operands(rb, i + 3);
-            if constexpr (STAGED) {
-                stage_store(sa, i + 4);
-                stage_load(sa, i + 6);
-            } else {
-                reg_load(rb, i + 5);
-            }
+    // Pipeline: each role runs its own copy of the loop, one barrier per
+    // iteration, unrolled by two so that register sets alternate statically:
+    // the rows a wave works on in iteration i were loaded in iteration i-2,
+    // into set fa in even iterations and fb in odd ones.
+    using F = std::integral_constant<bool, false>;
+    using U = std::integral_constant<bool, true>;
+    auto run = [&](auto work) {
+        for (int i = I0; i < nchunks; i += 2) {
+            work(i, F{});
             __syncthreads();
+            if (i + 1 < nchunks) {
+                work(i + 1, U{});
+                __syncthreads();
+            }
         }
+    };
+    auto scale_role = [&](auto with_v) {
+        Raw fa, fb;
+        run([&](int i, auto odd_c) {
+            Raw &fr = decltype(odd_c)::value ? fb : fa;
+            scale(fr, i + 2, with_v);
+            load_x(fr, i + 4, with_v);
+        });
+    };
+    if (role <= R_MR) {
+        run([&](int i, auto) { matrices(i + 1); });
+    } else if (role == R_D) {
+        Raw fa, fb;
+        load_w(fb, 0);  // chunk 0 is used in iteration -3
+        run([&](int i, auto odd_c) {
+            Raw &fr = decltype(odd_c)::value ? fb : fa;
+            decay(fr, i + 3);
+            load_w(fr, i + 5);
+        });
+    } else if (role == R_SK) {
+        scale_role(U{});
+    } else {
+        scale_role(F{});
     }
 }
 
