@@ -214,9 +214,10 @@ struct alignas(16) DSlot {
     float v[NDROW][kN];
 };
 
-template <int NP, int NPV>
+template <typename Tin, int NP, int NPV, int NS>
 struct Smem {
-    Slot<NP, NPV> slot[3];
+    Slot<NP, NPV> slot[NS];
+    alignas(16) Tin wbuf[CH][kN];  // w rows of one chunk, transposed through here by the decay wave
     DSlot dt[2];
     alignas(16) float p7[kN];  // P_7 of the first chunk
 };
@@ -260,8 +261,13 @@ __global__ __launch_bounds__((kN / J / 16 + NPROD) * 64) void wkv7_chunk_kernel(
     constexpr bool F32IN = std::is_same<Tin, float>::value;
     constexpr int NP = F32IN ? 3 : 2;     // bf16 pieces of derived fp32 operands
     constexpr int NPV = F32IN ? 3 : 1;    // pieces of v (one is exact for bf16 inputs)
+    // bf16 inputs: a four-slot ring, with the decay-table and inverse waves
+    // each working on two chunks at once (see the pipeline below); fp32 inputs
+    // (three bf16 pieces, larger slots) keep a three-slot ring.
+    constexpr bool DEEP = !F32IN;
+    constexpr int NS = DEEP ? 4 : 3;
     using SlotT = Slot<NP, NPV>;
-    __shared__ Smem<NP, NPV> sm;
+    __shared__ Smem<Tin, NP, NPV, NS> sm;
 
     // Workgroup -> (batch*head, column block).  Workgroups are dealt to the
     // XCDs round-robin; the J column blocks of one head stay on one XCD so the
@@ -276,13 +282,20 @@ __global__ __launch_bounds__((kN / J / 16 + NPROD) * 64) void wkv7_chunk_kernel(
     const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, m = lane & 15;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int j0 = jb * NC;
-    const size_t rowstride = static_cast<size_t>(H) * kN;              // elements between tokens
     const size_t head0 = (static_cast<size_t>(bb) * T * H + hh) * kN;   // (b, t=0, h, 0)
     const size_t sbase = static_cast<size_t>(bh) * (kN * kN);
     const int nchunks = (T + CH - 1) / CH;
-    // Pipeline depth: iteration i consumes chunk i, builds the matrices of
-    // chunk i+1, the operands of chunk i+2 and the decay table of chunk i+3.
-    constexpr int I0 = -4;
+    // element offset of token t in this (batch, head)'s rows: one 32x32->64 multiply-add
+    const uint32_t rs32 = static_cast<uint32_t>(H) * kN;
+    auto row_of = [&](int t) { return head0 + static_cast<uint64_t>(static_cast<uint32_t>(t)) * rs32; };
+    // Pipeline depth: iteration i consumes chunk i and builds the matrices of
+    // chunk i+1; the operands of chunk i+OFF_S and the decay table of chunk
+    // i+OFF_D (DEEP: also M_ab of chunk i+2 and the decay factors of chunk i+5).
+    constexpr int OFF_S = DEEP ? 3 : 2;
+    constexpr int OFF_D = DEEP ? 4 : 3;
+    constexpr int OFF_D1 = DEEP ? OFF_D + 1 : OFF_D;  // where the decay factors are computed
+    constexpr int I0 = -OFF_D1;                        // first iteration: decay factors of chunk 0
+
 
     if (wv < NSW) {
         // ------------------------------------------------------------ consumer
@@ -299,10 +312,14 @@ __global__ __launch_bounds__((kN / J / 16 + NPROD) * 64) void wkv7_chunk_kernel(
                 Sx[pt][e] = HAS_STATE_IN ? p.state_in[sbase + (16 * pt + 4 * q + e) * kN + jw + m] : 0.0f;
         // transpose-load address pieces of this lane: row 4 q + m/4, column group m%4
         const int trow = 4 * q + (m >> 2), tcol = 4 * (m & 3);
+        uint32_t ooff[4];  // output offsets of this lane's rows 4 q + e, column m, from a chunk's base
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            ooff[e] = static_cast<uint32_t>(4 * q + e) * rs32 + m;
 
         for (int i = I0; i < nchunks; ++i) {
             if (i >= 0) {
-                const SlotT &sl = sm.slot[i % 3];
+                const SlotT &sl = sm.slot[i % NS];
                 const int t0 = i * CH;
                 if (i == 0) {
                     // S^ = diag(P_7) S_in for the first chunk; afterwards every chunk
@@ -390,12 +407,19 @@ __global__ __launch_bounds__((kN / J / 16 + NPROD) * 64) void wkv7_chunk_kernel(
                         Mf[pl] = cat(tr4(&sl.Mt[MT_RB][pl][trow][tcol]), tr4(&sl.Mt[MT_RK][pl][trow][tcol]));
                     mma32<NP, NP>(o3, Mf, ZV);
                 }
+                {
+                    // one uniform base per chunk, per-lane 32-bit offsets
+                    Tout *const ob = go + row_of(t0) + jw;
+                    if (t0 + CH <= T) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int tau = 4 * q + e;
-                    if (t0 + tau < T)
-                        store_elem(go, head0 + static_cast<size_t>(t0 + tau) * rowstride + jw + m,
-                                   (o2[0][e] + o2[1][e]) + o3[e]);
+                        for (int e = 0; e < 4; ++e)
+                            store_elem(ob, ooff[e], (o2[0][e] + o2[1][e]) + o3[e]);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (t0 + 4 * q + e < T)
+                                store_elem(ob, ooff[e], (o2[0][e] + o2[1][e]) + o3[e]);
+                    }
                 }
                 // S^ <- diag(f) (S^ + [B'^T | K'^T] [Z ; V]), one 16-row tile at a time;
                 // the [B'^T | K'^T] fragment of key rows 16 pt .. 16 pt + 15 comes from the
@@ -433,7 +457,9 @@ __global__ __launch_bounds__((kN / J / 16 + NPROD) * 64) void wkv7_chunk_kernel(
     //   R_MA: M_ak                  R_SA, R_SR, R_SB, R_SK: A', R', B', K' (R_SK also v)
     //   R_MR: M_rb, M_rk
     enum { R_T = 0, R_MA = 1, R_MR = 2, R_D = 3, R_SA = 4, R_SR = 5, R_SB = 6, R_SK = 7 };
-    const int role = (0x61542730 >> (4 * (wv - NSW))) & 15;  // T D SK MR SA SR MA SB
+    // producer k runs on SIMD (NSW + k) % 4; pairs per SIMD for J = 1:
+    // (T, M_ak) (K', decay) (A', R') (B', M_rb/M_rk)
+    const int role = (0x25316470 >> (4 * (wv - NSW))) & 15;  // T SK SA SB MA D SR MR
     const int t_end = T;
 
     // ---- input path: the decay and scale waves load their own rows, in their
@@ -460,24 +486,29 @@ __global__ __launch_bounds__((kN / J / 16 + NPROD) * 64) void wkv7_chunk_kernel(
     // Loads are unconditional (a chunk past the end re-reads the last one, which
     // is never used): a load under a branch makes the compiler wait for it at
     // the join, right after issuing it.
+    // decay wave: rows in the scale waves' layout (token 8 pass + lane/8, eight
+    // keys from 8 g8), transposed to one key per lane through LDS when used
     auto load_w = [&](Raw &R, int c) {
-        c = min(c, nchunks - 1);
-#pragma unroll
-        for (int tau = 0; tau < CH; ++tau) {
-            const int t = min(c * CH + tau, t_end - 1);
-            const Tin x = gw[head0 + static_cast<size_t>(t) * rowstride + lane];
-            if constexpr (F32IN)
-                R.u[tau] = __float_as_uint(x);
-            else
-                R.u[tau] = x;
-        }
-    };
-    auto load_x = [&](Raw &R, int c, auto with_v) {
-        c = min(c, nchunks - 1);
+        c = max(0, min(c, nchunks - 1));
 #pragma unroll
         for (int pz = 0; pz < 2; ++pz) {
             const int t = min(c * CH + 8 * pz + (lane >> 3), t_end - 1);
-            const size_t row = head0 + static_cast<size_t>(t) * rowstride;
+            const uint32_t *src = reinterpret_cast<const uint32_t *>(gw + row_of(t) + 8 * g8);
+#pragma unroll
+            for (int h = 0; h < VRW / 4; ++h) {
+                const u32x4 x4 = *reinterpret_cast<const u32x4 *>(src + 4 * h);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    R.u[pz * VRW + 4 * h + e] = x4[e];
+            }
+        }
+    };
+    auto load_x = [&](Raw &R, int c, auto with_v) {
+        c = max(0, min(c, nchunks - 1));
+#pragma unroll
+        for (int pz = 0; pz < 2; ++pz) {
+            const int t = min(c * CH + 8 * pz + (lane >> 3), t_end - 1);
+            const uint64_t row = row_of(t);
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const uint32_t *src = reinterpret_cast<const uint32_t *>(gx + row + k0 + 16 * h);
@@ -505,38 +536,62 @@ __global__ __launch_bounds__((kN / J / 16 + NPROD) * 64) void wkv7_chunk_kernel(
         }
     };
 
-    // ---- decay wave: the factor table of chunk c, P_7 of chunk 0, and the row
-    // factor f of chunk c-1 (d_15 of c-1 times P_7 of c; d_15 alone once c is
-    // past the end).
+    // ---- decay wave.  Part 1 turns the w rows of chunk c into its decay
+    // factors (kept in registers); part 2 writes them as the table of chunk c,
+    // with P_7 of chunk 0 and the row factor f of chunk c-1 (d_15 of c-1 times
+    // P_7 of c; d_15 alone once c is past the end).
     float prev_d15 = 1.0f;
-    auto decay = [&](const Raw &R, int c) {
+    float dk[CH + 1], idk[CH + 1];  // factors of the chunk between the two parts
+    auto decay1 = [&](const Raw &R, int c) {
+        if (c < 0 || c >= nchunks)
+            return;
+        const int i = lane;
+        // transpose through LDS: rows in, one key channel per lane out (this
+        // wave's own accesses, which LDS performs in order)
+#pragma unroll
+        for (int pz = 0; pz < 2; ++pz)
+#pragma unroll
+            for (int h = 0; h < VRW / 4; ++h)
+                *reinterpret_cast<u32x4 *>(&sm.wbuf[8 * pz + (lane >> 3)][8 * g8 + 4 * EW * h]) =
+                    u32x4{R.u[pz * VRW + 4 * h], R.u[pz * VRW + 4 * h + 1], R.u[pz * VRW + 4 * h + 2],
+                          R.u[pz * VRW + 4 * h + 3]};
+        float w[CH];
+#pragma unroll
+        for (int tau = 0; tau < CH; ++tau) {
+            // decays below 2^-15 are raised to it (integer order is float order here)
+            const uint32_t bits = F32IN ? __float_as_uint(load_elem(&sm.wbuf[0][0], tau * kN + i))
+                                        : static_cast<uint32_t>(reinterpret_cast<const uint16_t *>(&sm.wbuf[0][0])[tau * kN + i]) << 16;
+            w[tau] = __uint_as_float(max(bits, 0x38000000u));
+        }
+        if (c * CH + CH > t_end) {  // partial chunk (uniform): positions past the end decay by 1
+#pragma unroll
+            for (int tau = 0; tau < CH; ++tau)
+                if (c * CH + tau >= t_end)
+                    w[tau] = 1.0f;
+        }
+        decay_factors(w, dk, idk);
+    };
+    auto decay2 = [&](int c) {
         if (c < 0 || c > nchunks)
             return;
         const int i = lane;
         if (c == nchunks) {
-            sm.slot[(c - 1) % 3].f[i] = prev_d15;
+            sm.slot[(c - 1) % NS].f[i] = prev_d15;
             return;
         }
-        float w[CH];
-#pragma unroll
-        for (int tau = 0; tau < CH; ++tau)
-            w[tau] = c * CH + tau < t_end ? fmaxf(F32IN ? __uint_as_float(R.u[tau]) : bf16_lo(R.u[tau]), W_MIN)
-                                          : 1.0f;  // past the end: 1
-        float d[CH + 1], id[CH + 1];
-        decay_factors(w, d, id);
         DSlot &D = sm.dt[c & 1];
         const int ps = dpos(key_slot(i));
 #pragma unroll
         for (int r = 0; r <= CH; ++r)
-            D.v[r][ps] = d[r];
+            D.v[r][ps] = dk[r];
 #pragma unroll
         for (int r = 1; r <= CH; ++r)
-            D.v[CH + r][ps] = id[r];
+            D.v[CH + r][ps] = idk[r];
         if (c == 0)
-            sm.p7[i] = id[0];
+            sm.p7[i] = idk[0];
         else
-            sm.slot[(c - 1) % 3].f[i] = prev_d15 * id[0];
-        prev_d15 = d[CH];
+            sm.slot[(c - 1) % NS].f[i] = prev_d15 * idk[0];
+        prev_d15 = dk[CH];
     };
 
     // ---- scale waves: X' = x * factor, elementwise, lane = (token, slot group):
@@ -544,7 +599,7 @@ __global__ __launch_bounds__((kN / J / 16 + NPROD) * 64) void wkv7_chunk_kernel(
     auto scale = [&](const Raw &R, int c, auto with_v) {
         if (c < 0 || c >= nchunks)
             return;
-        SlotT &sl = sm.slot[c % 3];
+        SlotT &sl = sm.slot[c % NS];
         const DSlot &D = sm.dt[c & 1];
         const int roff = op == 0 ? 0 : op == 1 ? 1 : CH + 1;  // table row of token tau
         const bool partial = c * CH + CH > t_end;  // uniform; rows past the end read as 0
@@ -610,13 +665,17 @@ __global__ __launch_bounds__((kN / J / 16 + NPROD) * 64) void wkv7_chunk_kernel(
     };
 
     // ---- matrix waves: 16x16 tiles M = tril(X' Y'^T) of chunk c over the 64 key
-    // channels, stored transposed; R_T also inverts I - M_ab.
-    auto matrices = [&](int c) {
+    // channels, stored transposed.  Each role has its own straight-line code
+    // (mr is a compile-time flag): a branch between a matrix-core result and
+    // the instruction reading it has been seen to lose the wait states that
+    // read needs.
+    auto matrices = [&](int c, auto mr_c) {
+        constexpr bool MR = decltype(mr_c)::value;   // R_MR: (R',B') and (R',K'); else R_MA: (A',K')
         if (c < 0 || c >= nchunks)
             return;
-        SlotT &sl = sm.slot[c % 3];
-        const int xo = role == R_MR ? OP_R : OP_A;
-        const int yo = role == R_MA ? OP_K : OP_B;       // R_T: (A',B'); R_MA: (A',K'); R_MR: (R',B') and (R',K')
+        SlotT &sl = sm.slot[c % NS];
+        constexpr int yo = MR ? OP_B : OP_K;
+        constexpr int xo = MR ? OP_R : OP_A;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
@@ -627,9 +686,7 @@ __global__ __launch_bounds__((kN / J / 16 + NPROD) * 64) void wkv7_chunk_kernel(
                 Bf[pl] = lds8(&sl.X[yo][pl][m][32 * s + 8 * q]);
             }
             mma32<NP, NP>(acc, Af, Bf);           // lane (m, q): M[4 q + e][m]
-            if (role == R_T) {
-                mma32<NP, NP>(acc2, Bf, Af);      // lane (m, q): M[m][4 q + e]
-            } else if (role == R_MR) {
+            if constexpr (MR) {
                 s16x8 Kf[NP];
 #pragma unroll
                 for (int pl = 0; pl < NP; ++pl)
@@ -637,42 +694,69 @@ __global__ __launch_bounds__((kN / J / 16 + NPROD) * 64) void wkv7_chunk_kernel(
                 mma32<NP, NP>(acc2, Af, Kf);      // M_rk
             }
         }
-        if (role != R_T) {
-            // a rows exclude the diagonal, r rows include it
-            f32x4 mv, mv2;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int tau = 4 * q + e;
-                const bool keep = m < tau || (role == R_MR && m == tau);
-                mv[e] = keep ? acc[e] : 0.0f;
-                mv2[e] = keep ? acc2[e] : 0.0f;
-            }
-            s16x4 pc[NP];
-            split4<NP>(mv, pc);
-            const int mt = role == R_MA ? MT_AK : MT_RB;
-#pragma unroll
-            for (int pl = 0; pl < NP; ++pl)
-                *reinterpret_cast<s16x4 *>(&sl.Mt[mt][pl][m][4 * q]) = pc[pl];
-            if (role == R_MR) {
-                split4<NP>(mv2, pc);
-#pragma unroll
-                for (int pl = 0; pl < NP; ++pl)
-                    *reinterpret_cast<s16x4 *>(&sl.Mt[MT_RK][pl][m][4 * q]) = pc[pl];
-            }
-            return;
-        }
-        // T = (I - M)^{-1} = (I + M)(I + M^2)(I + M^4)(I + M^8) for strictly lower M.
-        // A matrix X enters a product as the A operand through the accumulator of
-        // X^T and as the B operand through its own accumulator, so every product
-        // is formed together with the transpose the next one needs.
-        f32x4 P, Pt, Q, Qt;
+        // a rows exclude the diagonal, r rows include it
+        f32x4 mv, mv2;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int tau = 4 * q + e;
-            P[e] = m < tau ? acc[e] : 0.0f;     // M[tau][m]
-            Pt[e] = tau < m ? acc2[e] : 0.0f;   // M^T[tau][m] = M[m][tau]
-            Q[e] = P[e] + (m == tau ? 1.0f : 0.0f);
-            Qt[e] = Pt[e] + (m == tau ? 1.0f : 0.0f);
+            const bool keep = m < tau || (MR && m == tau);
+            mv[e] = keep ? acc[e] : 0.0f;
+            mv2[e] = keep ? acc2[e] : 0.0f;
+        }
+        s16x4 pc[NP];
+        split4<NP>(mv, pc);
+        constexpr int mt = MR ? MT_RB : MT_AK;
+#pragma unroll
+        for (int pl = 0; pl < NP; ++pl)
+            *reinterpret_cast<s16x4 *>(&sl.Mt[mt][pl][m][4 * q]) = pc[pl];
+        if constexpr (MR) {
+            split4<NP>(mv2, pc);
+#pragma unroll
+            for (int pl = 0; pl < NP; ++pl)
+                *reinterpret_cast<s16x4 *>(&sl.Mt[MT_RK][pl][m][4 * q]) = pc[pl];
+        }
+    };
+
+    // ---- inverse wave.  Part A forms M = M_ab of chunk c and its transpose
+    // (kept in registers); part B inverts I - M,
+    //   T = (I - M)^{-1} = (I + M)(I + M^2)(I + M^4)(I + M^8)   (M strictly lower),
+    // and stores T.  A matrix X enters a product as the A operand through the
+    // accumulator of X^T and as the B operand through its own accumulator, so
+    // every product is formed together with the transpose the next one needs.
+    f32x4 tM, tMt;  // M and M^T of the chunk between the two parts
+    auto inv_a = [&](int c) {
+        if (c < 0 || c >= nchunks)
+            return;
+        const SlotT &sl = sm.slot[c % NS];
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acct = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            s16x8 Af[NP], Bf[NP];
+#pragma unroll
+            for (int pl = 0; pl < NP; ++pl) {
+                Af[pl] = lds8(&sl.X[OP_A][pl][m][32 * s + 8 * q]);
+                Bf[pl] = lds8(&sl.X[OP_B][pl][m][32 * s + 8 * q]);
+            }
+            mma32<NP, NP>(acc, Af, Bf);           // lane (m, q): M[4 q + e][m]
+            mma32<NP, NP>(acct, Bf, Af);          // lane (m, q): M[m][4 q + e]
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int tau = 4 * q + e;
+            tM[e] = m < tau ? acc[e] : 0.0f;      // M[tau][m]
+            tMt[e] = tau < m ? acct[e] : 0.0f;    // M^T[tau][m] = M[m][tau]
+        }
+    };
+    auto inv_b = [&](int c) {
+        if (c < 0 || c >= nchunks)
+            return;
+        SlotT &sl = sm.slot[c % NS];
+        f32x4 P = tM, Pt = tMt, Q, Qt;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float one = m == 4 * q + e ? 1.0f : 0.0f;
+            Q[e] = P[e] + one;
+            Qt[e] = Pt[e] + one;
         }
 #pragma unroll
         for (int lvl = 0; lvl < 3; ++lvl) {
@@ -703,38 +787,88 @@ __global__ __launch_bounds__((kN / J / 16 + NPROD) * 64) void wkv7_chunk_kernel(
     };
 
     // Pipeline: each role runs its own copy of the loop, one barrier per
-    // iteration, unrolled by two so that register sets alternate statically:
-    // the rows a wave works on in iteration i were loaded in iteration i-2,
-    // into set fa in even iterations and fb in odd ones.
+    // iteration.  The waves that load input rows unroll it by three and keep
+    // three register sets: the rows a wave works on in iteration i were loaded
+    // in iteration i-3 into set (i - I0) % 3.  Before the loop the three sets
+    // are loaded in the same order as in every later round, so the compiler's
+    // waits (which may also cover the set loaded one round before) only ever
+    // wait for rows two or more iterations old.
     using F = std::integral_constant<bool, false>;
     using U = std::integral_constant<bool, true>;
+    using K0 = std::integral_constant<int, 0>;
+    using K1 = std::integral_constant<int, 1>;
+    using K2 = std::integral_constant<int, 2>;
     auto run = [&](auto work) {
-        for (int i = I0; i < nchunks; i += 2) {
-            work(i, F{});
+        for (int i = I0; i < nchunks; ++i) {
+            work(i);
+            __syncthreads();
+        }
+    };
+    auto run3 = [&](auto work) {
+        // whole rounds in the loop (its back edge then has one predecessor, and
+        // the wait analysis stays exact), the last one or two iterations after it
+        int i = I0;
+        for (; i + 2 < nchunks; i += 3) {
+            work(i, K0{});
+            __syncthreads();
+            work(i + 1, K1{});
+            __syncthreads();
+            work(i + 2, K2{});
+            __syncthreads();
+        }
+        if (i < nchunks) {
+            work(i, K0{});
             __syncthreads();
             if (i + 1 < nchunks) {
-                work(i + 1, U{});
+                work(i + 1, K1{});
                 __syncthreads();
             }
         }
     };
     auto scale_role = [&](auto with_v) {
-        Raw fa, fb;
-        run([&](int i, auto odd_c) {
-            Raw &fr = decltype(odd_c)::value ? fb : fa;
-            scale(fr, i + 2, with_v);
-            load_x(fr, i + 4, with_v);
+        Raw f0, f1, f2;
+        load_x(f0, I0 + OFF_S, with_v);  // chunks below 0 are nothing (rows of chunk 0 are read instead)
+        load_x(f1, I0 + OFF_S + 1, with_v);
+        load_x(f2, I0 + OFF_S + 2, with_v);
+        run3([&](int i, auto k) {
+            constexpr int K = decltype(k)::value;
+            Raw &fr = K == 0 ? f0 : K == 1 ? f1 : f2;
+            scale(fr, i + OFF_S, with_v);
+            load_x(fr, i + OFF_S + 3, with_v);
         });
     };
-    if (role <= R_MR) {
-        run([&](int i, auto) { matrices(i + 1); });
+    if (role == R_T) {
+        if constexpr (DEEP) {
+            run([&](int i) {
+                inv_b(i + 1);   // T of chunk i+1 from M formed last iteration
+                inv_a(i + 2);   // M of chunk i+2 (independent: the two interleave)
+            });
+        } else {
+            run([&](int i) {
+                inv_a(i + 1);
+                inv_b(i + 1);
+            });
+        }
+    } else if (role == R_MA) {
+        run([&](int i) { matrices(i + 1, F{}); });
+    } else if (role == R_MR) {
+        run([&](int i) { matrices(i + 1, U{}); });
     } else if (role == R_D) {
-        Raw fa, fb;
-        load_w(fb, 0);  // chunk 0 is used in iteration -3
-        run([&](int i, auto odd_c) {
-            Raw &fr = decltype(odd_c)::value ? fb : fa;
-            decay(fr, i + 3);
-            load_w(fr, i + 5);
+        Raw f0, f1, f2;
+        load_w(f0, I0 + OFF_D1);
+        load_w(f1, I0 + OFF_D1 + 1);
+        load_w(f2, I0 + OFF_D1 + 2);
+        run3([&](int i, auto k) {
+            constexpr int K = decltype(k)::value;
+            Raw &fr = K == 0 ? f0 : K == 1 ? f1 : f2;
+            if constexpr (DEEP) {
+                decay2(i + OFF_D);       // table of chunk i+4 from factors computed last iteration
+                decay1(fr, i + OFF_D1);  // factors of chunk i+5
+            } else {
+                decay1(fr, i + OFF_D);
+                decay2(i + OFF_D);
+            }
+            load_w(fr, i + OFF_D1 + 3);
         });
     } else if (role == R_SK) {
         scale_role(U{});
