@@ -317,6 +317,25 @@ __global__ __launch_bounds__((kN / J / 16 + NPROD) * 64) void wkv7_chunk_kernel(
         for (int e = 0; e < 4; ++e)
             ooff[e] = static_cast<uint32_t>(4 * q + e) * rs32 + m;
 
+        // A', R' and v of the next chunk are read at the end of each iteration
+        // (they were final one or more iterations before) and stay in flight
+        // across the barrier: this wave writes no LDS, so its barrier needs no
+        // wait for its own LDS accesses.
+        s16x8 pA[2][NP], pR[2][NP];
+        s16x4 pV[NPV];
+        auto prefetch = [&](int c) {
+            const SlotT &sl = sm.slot[max(c, 0) % NS];
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+#pragma unroll
+                for (int pl = 0; pl < NP; ++pl) {
+                    pA[s][pl] = lds8(&sl.X[OP_A][pl][m][32 * s + 8 * q]);
+                    pR[s][pl] = lds8(&sl.X[OP_R][pl][m][32 * s + 8 * q]);
+                }
+#pragma unroll
+            for (int pl = 0; pl < NPV; ++pl)
+                pV[pl] = tr4(&sl.Vr[pl][trow][jw + tcol]);
+        };
         for (int i = I0; i < nchunks; ++i) {
             if (i >= 0) {
                 const SlotT &sl = sm.slot[i % NS];
@@ -349,22 +368,16 @@ __global__ __launch_bounds__((kN / J / 16 + NPROD) * 64) void wkv7_chunk_kernel(
                 f32x4 y2[2], o2[2];
 #pragma unroll
                 for (int s = 0; s < 2; ++s) {
-                    s16x8 Af[NP], Rf[NP];
-#pragma unroll
-                    for (int pl = 0; pl < NP; ++pl) {
-                        Af[pl] = lds8(&sl.X[OP_A][pl][m][32 * s + 8 * q]);
-                        Rf[pl] = lds8(&sl.X[OP_R][pl][m][32 * s + 8 * q]);
-                    }
                     y2[s] = f32x4{0.f, 0.f, 0.f, 0.f};
                     o2[s] = f32x4{0.f, 0.f, 0.f, 0.f};
-                    mma32<NP, NP>(y2[s], Af, Bs[s]);
-                    mma32<NP, NP>(o2[s], Rf, Bs[s]);
+                    mma32<NP, NP>(y2[s], pA[s], Bs[s]);
+                    mma32<NP, NP>(o2[s], pR[s], Bs[s]);
                 }
                 // V rows as a B operand over the token index (slot (q, e) = token 4 q + e)
                 s16x4 Vf[NPV];
 #pragma unroll
                 for (int pl = 0; pl < NPV; ++pl)
-                    Vf[pl] = tr4(&sl.Vr[pl][trow][jw + tcol]);
+                    Vf[pl] = pV[pl];
                 // M_ak V
                 f32x4 ym = {0.f, 0.f, 0.f, 0.f};
                 {
@@ -439,7 +452,8 @@ __global__ __launch_bounds__((kN / J / 16 + NPROD) * 64) void wkv7_chunk_kernel(
                         Sx[pt][e] = acc[e] * fv[e];
                 }
             }
-            __syncthreads();
+            prefetch(i + 1);
+            __builtin_amdgcn_s_barrier();
         }
 #pragma unroll
         for (int pt = 0; pt < 4; ++pt)
@@ -542,9 +556,7 @@ __global__ __launch_bounds__((kN / J / 16 + NPROD) * 64) void wkv7_chunk_kernel(
     // P_7 of c; d_15 alone once c is past the end).
     float prev_d15 = 1.0f;
     float dk[CH + 1], idk[CH + 1];  // factors of the chunk between the two parts
-    auto decay1 = [&](const Raw &R, int c) {
-        if (c < 0 || c >= nchunks)
-            return;
+    auto decay1_body = [&](const Raw &R, int c) {
         const int i = lane;
         // transpose through LDS: rows in, one key channel per lane out (this
         // wave's own accesses, which LDS performs in order)
@@ -571,14 +583,12 @@ __global__ __launch_bounds__((kN / J / 16 + NPROD) * 64) void wkv7_chunk_kernel(
         }
         decay_factors(w, dk, idk);
     };
-    auto decay2 = [&](int c) {
-        if (c < 0 || c > nchunks)
-            return;
+    auto decay1 = [&](const Raw &R, int c) {
+        if (c >= 0 && c < nchunks)
+            decay1_body(R, c);
+    };
+    auto decay2_body = [&](int c) {  // 0 <= c < nchunks
         const int i = lane;
-        if (c == nchunks) {
-            sm.slot[(c - 1) % NS].f[i] = prev_d15;
-            return;
-        }
         DSlot &D = sm.dt[c & 1];
         const int ps = dpos(key_slot(i));
 #pragma unroll
@@ -592,6 +602,12 @@ __global__ __launch_bounds__((kN / J / 16 + NPROD) * 64) void wkv7_chunk_kernel(
         else
             sm.slot[(c - 1) % NS].f[i] = prev_d15 * idk[0];
         prev_d15 = dk[CH];
+    };
+    auto decay2 = [&](int c) {
+        if (c == nchunks)
+            sm.slot[(c - 1) % NS].f[lane] = prev_d15;
+        else if (c >= 0 && c < nchunks)
+            decay2_body(c);
     };
 
     // ---- scale waves: X' = x * factor, elementwise, lane = (token, slot group):
@@ -724,9 +740,7 @@ __global__ __launch_bounds__((kN / J / 16 + NPROD) * 64) void wkv7_chunk_kernel(
     // accumulator of X^T and as the B operand through its own accumulator, so
     // every product is formed together with the transpose the next one needs.
     f32x4 tM, tMt;  // M and M^T of the chunk between the two parts
-    auto inv_a = [&](int c) {
-        if (c < 0 || c >= nchunks)
-            return;
+    auto inv_a_body = [&](int c) {
         const SlotT &sl = sm.slot[c % NS];
         f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acct = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -747,9 +761,11 @@ __global__ __launch_bounds__((kN / J / 16 + NPROD) * 64) void wkv7_chunk_kernel(
             tMt[e] = tau < m ? acct[e] : 0.0f;    // M^T[tau][m] = M[m][tau]
         }
     };
-    auto inv_b = [&](int c) {
-        if (c < 0 || c >= nchunks)
-            return;
+    auto inv_a = [&](int c) {
+        if (c >= 0 && c < nchunks)
+            inv_a_body(c);
+    };
+    auto inv_b_body = [&](int c) {
         SlotT &sl = sm.slot[c % NS];
         f32x4 P = tM, Pt = tMt, Q, Qt;
 #pragma unroll
@@ -784,6 +800,10 @@ __global__ __launch_bounds__((kN / J / 16 + NPROD) * 64) void wkv7_chunk_kernel(
 #pragma unroll
         for (int pl = 0; pl < NP; ++pl)
             *reinterpret_cast<s16x4 *>(&sl.Mt[MT_T][pl][m][4 * q]) = tp[pl];
+    };
+    auto inv_b = [&](int c) {
+        if (c >= 0 && c < nchunks)
+            inv_b_body(c);
     };
 
     // Pipeline: each role runs its own copy of the loop, one barrier per
@@ -840,8 +860,15 @@ __global__ __launch_bounds__((kN / J / 16 + NPROD) * 64) void wkv7_chunk_kernel(
     if (role == R_T) {
         if constexpr (DEEP) {
             run([&](int i) {
-                inv_b(i + 1);   // T of chunk i+1 from M formed last iteration
-                inv_a(i + 2);   // M of chunk i+2 (independent: the two interleave)
+                // T of chunk i+1 from M formed last iteration, and M of chunk i+2:
+                // independent, and in one block when both exist so they interleave
+                if (i + 1 >= 0 && i + 2 < nchunks) {
+                    inv_b_body(i + 1);
+                    inv_a_body(i + 2);
+                } else {
+                    inv_b(i + 1);
+                    inv_a(i + 2);
+                }
             });
         } else {
             run([&](int i) {
@@ -862,8 +889,15 @@ __global__ __launch_bounds__((kN / J / 16 + NPROD) * 64) void wkv7_chunk_kernel(
             constexpr int K = decltype(k)::value;
             Raw &fr = K == 0 ? f0 : K == 1 ? f1 : f2;
             if constexpr (DEEP) {
-                decay2(i + OFF_D);       // table of chunk i+4 from factors computed last iteration
-                decay1(fr, i + OFF_D1);  // factors of chunk i+5
+                // table of chunk i+4 from factors computed last iteration, and the
+                // factors of chunk i+5 (one block in the steady state)
+                if (i + OFF_D >= 0 && i + OFF_D1 < nchunks) {
+                    decay2_body(i + OFF_D);
+                    decay1_body(fr, i + OFF_D1);
+                } else {
+                    decay2(i + OFF_D);
+                    decay1(fr, i + OFF_D1);
+                }
             } else {
                 decay1(fr, i + OFF_D);
                 decay2(i + OFF_D);
