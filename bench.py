@@ -91,6 +91,20 @@ def roofline(bytes_per_launch: int, sec_per_launch: float, kind: str, workload: 
 
 # ----------------------------------------------------------------------------- GPU timing
 
+WARM_SECONDS = 0.3  # untimed warm-up: at least this long (clocks settle) and at least W steps
+
+
+def warm(fn, steps: int):
+    """Run fn() at least `steps` times and for at least WARM_SECONDS, then synchronize."""
+    import torch
+    t0, n = time.perf_counter(), 0
+    while n < steps or time.perf_counter() - t0 < WARM_SECONDS:
+        fn()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+
 def make_layers(K, synth, idx: int, nlayers: int):
     """nlayers distinct buffer sets of workload idx on the GPU (inputs, state, outputs)."""
     import torch
@@ -136,9 +150,7 @@ def time_step_workload(K, synth, idx: int, steps: int, warmup: int):
         replay = [d["state"] for d in sets] + [d["o"] for d in sets]
         if not all(torch.equal(a, b) for a, b in zip(eager, replay)):
             raise RuntimeError("graph replay differs from the eager sweep")
-        for _ in range(warmup):
-            g.replay()
-        torch.cuda.synchronize()
+        warm(g.replay, warmup)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for _ in range(steps):
@@ -160,9 +172,7 @@ def time_prefill_workload(K, synth, idx: int, steps: int, warmup: int):
     args = [d[n] for n in ("r", "w", "k", "v", "a", "b")]
     stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):
-        for _ in range(max(1, warmup)):
-            K.wkv7_forward(*args, d["state_in"], o=o, state_out=s_out)
-        torch.cuda.synchronize()
+        warm(lambda: K.wkv7_forward(*args, d["state_in"], o=o, state_out=s_out), warmup)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for _ in range(steps):
@@ -194,9 +204,7 @@ def copy_ceiling(idx: int, steps: int, warmup: int):
         with torch.cuda.graph(g, stream=stream):
             for s_, d_ in zip(src, dst):
                 d_.copy_(s_)
-        for _ in range(warmup):
-            g.replay()
-        torch.cuda.synchronize()
+        warm(g.replay, warmup)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for _ in range(steps):
@@ -286,7 +294,7 @@ def main():
             t = time_step_workload(K, synth, idx, args.steps, args.warmup)
             rl = roofline(algorithmic_bytes(wl, kind), t["sec_per_launch"], kind, idx)
             return t, rl
-        t = time_prefill_workload(K, synth, idx, max(3, args.steps // 4), max(1, args.warmup // 2))
+        t = time_prefill_workload(K, synth, idx, max(20, args.steps), args.warmup)
         rl = roofline(algorithmic_bytes(wl, "chunk"), t["sec_per_launch"], "chunk", idx)
         return t, rl
 
@@ -303,7 +311,7 @@ def main():
         "value": round(metric_value, 3),
         "unit": unit,
         "n_gpus": 1,
-        "steps": args.steps if idx in (1, 4) else max(3, args.steps // 4),
+        "steps": args.steps if idx in (1, 4) else max(20, args.steps),
         "warmup": args.warmup,
         "ms_per_step": round(t["ms_per_step"], 4),
         "higher_is_better": hib,
