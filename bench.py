@@ -267,9 +267,13 @@ def main():
     ap.add_argument("--workload", type=int, default=1, choices=[1, 2, 3, 4])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", action="store_true", help="measure the chosen workload only")
+    ap.add_argument("--warm-seconds", type=float, default=WARM_SECONDS,
+                    help="minimum untimed warm-up per measurement (0: just --warmup steps)")
     ap.add_argument("--copy-ceiling", action="store_true",
                     help="time a plain device copy of the workload's bytes instead (HBM ceiling / counter calibration)")
     args = ap.parse_args()
+    global WARM_SECONDS
+    WARM_SECONDS = args.warm_seconds
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the WKV-7 kernels here are measured on one MI355X "
               f"(--gpus {args.gpus} is not supported; heads shard across GPUs with no exchange).",
