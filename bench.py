@@ -260,6 +260,7 @@ def cpu_baseline_prefill(synth, idx: int, budget_s: float = 8.0):
 # ----------------------------------------------------------------------------- main
 
 def main():
+    global WARM_SECONDS
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
@@ -272,7 +273,6 @@ def main():
     ap.add_argument("--copy-ceiling", action="store_true",
                     help="time a plain device copy of the workload's bytes instead (HBM ceiling / counter calibration)")
     args = ap.parse_args()
-    global WARM_SECONDS
     WARM_SECONDS = args.warm_seconds
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the WKV-7 kernels here are measured on one MI355X "
