@@ -65,7 +65,9 @@ namespace {
 constexpr int CH = 16;             // chunk length
 constexpr int REF = 7;             // decays are measured relative to the state after this position
 constexpr float W_MIN = 0x1p-15f;  // lower bound applied to decay multipliers in this kernel
-constexpr int NPROD = 8;           // producer waves
+// producer waves: nine with bf16 inputs (two inverse waves), eight with fp32 inputs
+template <typename Tin>
+constexpr int nprod() { return std::is_same<Tin, float>::value ? 8 : 9; }
 constexpr int LDA = kN + 8;        // row pitch (bf16) of [16][64] planes
 constexpr int LDT = CH + 8;        // row pitch (bf16) of [16][16] planes
 constexpr int NDROW = 2 * CH + 1;  // decay table rows: d_0 .. d_16, then id_1 .. id_16
@@ -253,7 +255,7 @@ __device__ __forceinline__ void decay_factors(const float (&w)[CH], float (&d)[C
 }
 
 template <typename Tin, typename Tout, int J, bool HAS_STATE_IN>
-__global__ __launch_bounds__((kN / J / 16 + NPROD) * 64) void wkv7_chunk_kernel(SeqArgs p, int per_xcd,
+__global__ __launch_bounds__((kN / J / 16 + nprod<Tin>()) * 64) void wkv7_chunk_kernel(SeqArgs p, int per_xcd,
                                                                                    int nblocks)
 {
     constexpr int NC = kN / J;            // value columns of this workgroup
@@ -470,10 +472,13 @@ __global__ __launch_bounds__((kN / J / 16 + NPROD) * 64) void wkv7_chunk_kernel(
     //   R_T : M_ab and T            R_D : decay table (from w)
     //   R_MA: M_ak                  R_SA, R_SR, R_SB, R_SK: A', R', B', K' (R_SK also v)
     //   R_MR: M_rb, M_rk
-    enum { R_T = 0, R_MA = 1, R_MR = 2, R_D = 3, R_SA = 4, R_SR = 5, R_SB = 6, R_SK = 7 };
+    enum { R_T = 0, R_MA = 1, R_MR = 2, R_D = 3, R_SA = 4, R_SR = 5, R_SB = 6, R_SK = 7, R_T1 = 8 };
     // producer k runs on SIMD (NSW + k) % 4; pairs per SIMD for J = 1:
     // (T, M_ak) (K', decay) (A', R') (B', M_rb/M_rk)
-    const int role = (0x25316470 >> (4 * (wv - NSW))) & 15;  // T SK SA SB MA D SR MR
+    // bf16 inputs (nine producers, J = 1): (T, SB, MA) (T1, D) (SK, MR) (SA, SR);
+    // R_T and R_T1 take the even and the odd chunks
+    const int role = DEEP ? static_cast<int>((0x152364780ull >> (4 * (wv - NSW))) & 15)
+                          : (0x25316470 >> (4 * (wv - NSW))) & 15;  // T SK SA SB MA D SR MR
     const int t_end = T;
 
     // ---- input path: the decay and scale waves load their own rows, in their
@@ -824,6 +829,20 @@ __global__ __launch_bounds__((kN / J / 16 + NPROD) * 64) void wkv7_chunk_kernel(
             __syncthreads();
         }
     };
+    auto run2 = [&](auto work) {
+        // whole pairs in the loop, the last iteration after it; K0 is i = I0 + 2j
+        int i = I0;
+        for (; i + 1 < nchunks; i += 2) {
+            work(i, K0{});
+            __syncthreads();
+            work(i + 1, K1{});
+            __syncthreads();
+        }
+        if (i < nchunks) {
+            work(i, K0{});
+            __syncthreads();
+        }
+    };
     auto run3 = [&](auto work) {
         // whole rounds in the loop (its back edge then has one predecessor, and
         // the wait analysis stays exact), the last one or two iterations after it
@@ -857,19 +876,23 @@ __global__ __launch_bounds__((kN / J / 16 + NPROD) * 64) void wkv7_chunk_kernel(
             load_x(fr, i + OFF_S + 3, with_v);
         });
     };
-    if (role == R_T) {
+    // one inverse wave per chunk parity: chunk c's M in iteration c-2, its T in c-1
+    auto inv_role = [&](auto par_c) {
+        constexpr int PAR = decltype(par_c)::value;
+        run2([&](int i, auto k) {
+            constexpr int PI = ((I0 & 1) + decltype(k)::value) & 1;  // parity of i
+            if constexpr (((PI + 1) & 1) == PAR)
+                inv_b(i + 1);
+            else
+                inv_a(i + 2);
+        });
+    };
+    if (role == R_T || role == R_T1) {
         if constexpr (DEEP) {
-            run([&](int i) {
-                // T of chunk i+1 from M formed last iteration, and M of chunk i+2:
-                // independent, and in one block when both exist so they interleave
-                if (i + 1 >= 0 && i + 2 < nchunks) {
-                    inv_b_body(i + 1);
-                    inv_a_body(i + 2);
-                } else {
-                    inv_b(i + 1);
-                    inv_a(i + 2);
-                }
-            });
+            if (role == R_T)
+                inv_role(std::integral_constant<int, 0>{});
+            else
+                inv_role(std::integral_constant<int, 1>{});
         } else {
             run([&](int i) {
                 inv_a(i + 1);
@@ -917,7 +940,7 @@ hipError_t launch_j(const SeqArgs &p, hipStream_t stream)
     const int nblocks = p.B * p.H * J;
     int per_xcd = (nblocks + 7) / 8;
     per_xcd = (per_xcd + J - 1) / J * J;  // a head's column blocks never straddle two XCDs
-    const dim3 grid(8 * per_xcd), block((kN / J / 16 + NPROD) * 64);
+    const dim3 grid(8 * per_xcd), block((kN / J / 16 + nprod<Tin>()) * 64);
     if (p.state_in)
         hipLaunchKernelGGL((wkv7_chunk_kernel<Tin, Tout, J, true>), grid, block, 0, stream, p, per_xcd, nblocks);
     else
