@@ -65,9 +65,9 @@ namespace {
 constexpr int CH = 16;             // chunk length
 constexpr int REF = 7;             // decays are measured relative to the state after this position
 constexpr float W_MIN = 0x1p-15f;  // lower bound applied to decay multipliers in this kernel
-// producer waves: nine with bf16 inputs (two inverse waves), eight with fp32 inputs
+// producer waves: ten with bf16 inputs (two inverse and two decay waves), eight with fp32 inputs
 template <typename Tin>
-constexpr int nprod() { return std::is_same<Tin, float>::value ? 8 : 9; }
+constexpr int nprod() { return std::is_same<Tin, float>::value ? 8 : 10; }
 constexpr int LDA = kN + 8;        // row pitch (bf16) of [16][64] planes
 constexpr int LDT = CH + 8;        // row pitch (bf16) of [16][16] planes
 constexpr int NDROW = 2 * CH + 1;  // decay table rows: d_0 .. d_16, then id_1 .. id_16
@@ -222,6 +222,7 @@ struct Smem {
     alignas(16) Tin wbuf[CH][kN];  // w rows of one chunk, transposed through here by the decay wave
     DSlot dt[2];
     alignas(16) float p7[kN];  // P_7 of the first chunk
+    alignas(16) float d15[2][kN];  // d_15 of the last two chunks whose table was written
 };
 
 // Decay factors of one key channel over a chunk: d[tau+1] = P_tau / P_7 and
@@ -472,12 +473,12 @@ __global__ __launch_bounds__((kN / J / 16 + nprod<Tin>()) * 64) void wkv7_chunk_
     //   R_T : M_ab and T            R_D : decay table (from w)
     //   R_MA: M_ak                  R_SA, R_SR, R_SB, R_SK: A', R', B', K' (R_SK also v)
     //   R_MR: M_rb, M_rk
-    enum { R_T = 0, R_MA = 1, R_MR = 2, R_D = 3, R_SA = 4, R_SR = 5, R_SB = 6, R_SK = 7, R_T1 = 8 };
+    enum { R_T = 0, R_MA = 1, R_MR = 2, R_D = 3, R_SA = 4, R_SR = 5, R_SB = 6, R_SK = 7, R_T1 = 8, R_D1 = 9 };
     // producer k runs on SIMD (NSW + k) % 4; pairs per SIMD for J = 1:
     // (T, M_ak) (K', decay) (A', R') (B', M_rb/M_rk)
-    // bf16 inputs (nine producers, J = 1): (T, SB, MA) (T1, D) (SK, MR) (SA, SR);
-    // R_T and R_T1 take the even and the odd chunks
-    const int role = DEEP ? static_cast<int>((0x152364780ull >> (4 * (wv - NSW))) & 15)
+    // bf16 inputs (ten producers, J = 1): (T, D1, MA) (T1, D, MR) (SK, SA) (SB, SR);
+    // R_T / R_T1 and R_D / R_D1 take the even and the odd chunks
+    const int role = DEEP ? static_cast<int>((0x2154396780ull >> (4 * (wv - NSW))) & 15)
                           : (0x25316470 >> (4 * (wv - NSW))) & 15;  // T SK SA SB MA D SR MR
     const int t_end = T;
 
@@ -555,11 +556,11 @@ __global__ __launch_bounds__((kN / J / 16 + nprod<Tin>()) * 64) void wkv7_chunk_
         }
     };
 
-    // ---- decay wave.  Part 1 turns the w rows of chunk c into its decay
+    // ---- decay waves.  Part 1 turns the w rows of chunk c into its decay
     // factors (kept in registers); part 2 writes them as the table of chunk c,
-    // with P_7 of chunk 0 and the row factor f of chunk c-1 (d_15 of c-1 times
-    // P_7 of c; d_15 alone once c is past the end).
-    float prev_d15 = 1.0f;
+    // with P_7 of chunk 0 and the row factor f of chunk c-1 (d_15 of c-1, left
+    // in LDS by the part 2 of chunk c-1, times P_7 of c; d_15 alone once c is
+    // past the end).
     float dk[CH + 1], idk[CH + 1];  // factors of the chunk between the two parts
     auto decay1_body = [&](const Raw &R, int c) {
         const int i = lane;
@@ -605,12 +606,12 @@ __global__ __launch_bounds__((kN / J / 16 + nprod<Tin>()) * 64) void wkv7_chunk_
         if (c == 0)
             sm.p7[i] = idk[0];
         else
-            sm.slot[(c - 1) % NS].f[i] = prev_d15 * idk[0];
-        prev_d15 = dk[CH];
+            sm.slot[(c - 1) % NS].f[i] = sm.d15[(c - 1) & 1][i] * idk[0];
+        sm.d15[c & 1][i] = dk[CH];
     };
     auto decay2 = [&](int c) {
         if (c == nchunks)
-            sm.slot[(c - 1) % NS].f[lane] = prev_d15;
+            sm.slot[(c - 1) % NS].f[lane] = sm.d15[(c - 1) & 1][lane];
         else if (c >= 0 && c < nchunks)
             decay2_body(c);
     };
@@ -903,6 +904,28 @@ __global__ __launch_bounds__((kN / J / 16 + nprod<Tin>()) * 64) void wkv7_chunk_
         run([&](int i) { matrices(i + 1, F{}); });
     } else if (role == R_MR) {
         run([&](int i) { matrices(i + 1, U{}); });
+    } else if (DEEP && (role == R_D || role == R_D1)) {
+        // one decay wave per chunk parity: chunk c's factors in iteration c-5,
+        // its table in c-4; its rows are loaded right after the factors of the
+        // chunk two before (one register set, two iterations ahead)
+        auto decay_role = [&](auto par_c) {
+            constexpr int PAR = decltype(par_c)::value;
+            Raw fr;
+            load_w(fr, PAR);
+            run2([&](int i, auto k) {
+                constexpr int PI = ((I0 & 1) + decltype(k)::value) & 1;  // parity of i
+                if constexpr (((PI + OFF_D) & 1) == PAR) {
+                    decay2(i + OFF_D);
+                } else {
+                    decay1(fr, i + OFF_D1);
+                    load_w(fr, i + OFF_D1 + 2);
+                }
+            });
+        };
+        if (role == R_D)
+            decay_role(std::integral_constant<int, 0>{});
+        else
+            decay_role(std::integral_constant<int, 1>{});
     } else if (role == R_D) {
         Raw f0, f1, f2;
         load_w(f0, I0 + OFF_D1);
