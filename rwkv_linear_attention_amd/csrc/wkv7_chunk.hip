@@ -302,6 +302,10 @@ __global__ __launch_bounds__((kN / J / 16 + nprod<Tin>()) * 64) void wkv7_chunk_
 
     if (wv < NSW) {
         // ------------------------------------------------------------ consumer
+        // The consumers' chain of dependent products is the longest per chunk;
+        // the producer waves sharing their SIMDs have slack, so the consumers'
+        // instructions go first.
+        __builtin_amdgcn_s_setprio(2);
         const int jw = j0 + 16 * wv;      // this wave's first state column
         Tout *__restrict__ go = static_cast<Tout *>(p.o);
         // Sx[pt][e] holds row 16 pt + 4 q + e, column jw + m of the state: the input
