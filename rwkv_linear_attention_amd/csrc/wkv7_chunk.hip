@@ -324,21 +324,19 @@ __global__ __launch_bounds__((kN / J / 16 + nprod<Tin>()) * 64) void wkv7_chunk_
         for (int e = 0; e < 4; ++e)
             ooff[e] = static_cast<uint32_t>(4 * q + e) * rs32 + m;
 
-        // A', R' and v of the next chunk are read at the end of each iteration
+        // A' and v of the next chunk are read at the end of each iteration
         // (they were final one or more iterations before) and stay in flight
         // across the barrier: this wave writes no LDS, so its barrier needs no
         // wait for its own LDS accesses.
-        s16x8 pA[2][NP], pR[2][NP];
+        s16x8 pA[2][NP];
         s16x4 pV[NPV];
         auto prefetch = [&](int c) {
             const SlotT &sl = sm.slot[max(c, 0) % NS];
 #pragma unroll
             for (int s = 0; s < 2; ++s)
 #pragma unroll
-                for (int pl = 0; pl < NP; ++pl) {
+                for (int pl = 0; pl < NP; ++pl)
                     pA[s][pl] = lds8(&sl.X[OP_A][pl][m][32 * s + 8 * q]);
-                    pR[s][pl] = lds8(&sl.X[OP_R][pl][m][32 * s + 8 * q]);
-                }
 #pragma unroll
             for (int pl = 0; pl < NPV; ++pl)
                 pV[pl] = tr4(&sl.Vr[pl][trow][jw + tcol]);
@@ -377,8 +375,12 @@ __global__ __launch_bounds__((kN / J / 16 + nprod<Tin>()) * 64) void wkv7_chunk_
                 for (int s = 0; s < 2; ++s) {
                     y2[s] = f32x4{0.f, 0.f, 0.f, 0.f};
                     o2[s] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    s16x8 Rf[NP];
+#pragma unroll
+                    for (int pl = 0; pl < NP; ++pl)
+                        Rf[pl] = lds8(&sl.X[OP_R][pl][m][32 * s + 8 * q]);
                     mma32<NP, NP>(y2[s], pA[s], Bs[s]);
-                    mma32<NP, NP>(o2[s], pR[s], Bs[s]);
+                    mma32<NP, NP>(o2[s], Rf, Bs[s]);
                 }
                 // V rows as a B operand over the token index (slot (q, e) = token 4 q + e)
                 s16x4 Vf[NPV];
@@ -407,6 +409,16 @@ __global__ __launch_bounds__((kN / J / 16 + nprod<Tin>()) * 64) void wkv7_chunk_
                         Tf[pl] = tr4(&sl.Mt[MT_T][pl][trow][tcol]);
                     split4<NP>(y4, Yf);
                     mma16<NP, NP>(z, Tf, Yf);
+                }
+                // the state update's [B'^T | K'^T] fragments (key rows 16 pt ..), read
+                // now so they arrive while Z, o and the stores are formed
+                s16x8 Uf[4][NP];
+#pragma unroll
+                for (int pt = 0; pt < 4; ++pt) {
+                    const int ukey = key_slot(16 * pt + tcol);
+#pragma unroll
+                    for (int pl = 0; pl < NP; ++pl)
+                        Uf[pt][pl] = cat(tr4(&sl.X[OP_B][pl][trow][ukey]), tr4(&sl.X[OP_K][pl][trow][ukey]));
                 }
                 // [Z ; V] as one B operand over 32 token slots: (q, e<4) is Z row 4q+e
                 // (this lane's z[e]), (q, e>=4) is V row 4q+e-4.
@@ -446,13 +458,8 @@ __global__ __launch_bounds__((kN / J / 16 + nprod<Tin>()) * 64) void wkv7_chunk_
                 // row-major B' and K' planes by transpose loads.
 #pragma unroll
                 for (int pt = 0; pt < 4; ++pt) {
-                    const int ukey = key_slot(16 * pt + tcol);
-                    s16x8 Uf[NP];
-#pragma unroll
-                    for (int pl = 0; pl < NP; ++pl)
-                        Uf[pl] = cat(tr4(&sl.X[OP_B][pl][trow][ukey]), tr4(&sl.X[OP_K][pl][trow][ukey]));
                     f32x4 acc = {Sx[pt][0], Sx[pt][1], Sx[pt][2], Sx[pt][3]};
-                    mma32<NP, NP>(acc, Uf, ZV);
+                    mma32<NP, NP>(acc, Uf[pt], ZV);
                     const f32x4 fv = *reinterpret_cast<const f32x4 *>(&sl.f[16 * pt + 4 * q]);
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
