@@ -9,7 +9,9 @@
 // RWKV7-MTP-Exp model card, section "Inference" (state rolled back to the
 // accepted prefix).
 //
-// Mapping to gfx950: one workgroup of NW wavefronts per head.  Lane j owns
+// Mapping to gfx950: one workgroup of NW wavefronts per head (four for one
+// token, eight for longer runs, whose per-position state stores are then
+// spread over more waves).  Lane j owns
 // VALUE column j of the 64x64 fp32 state; wave g holds the 64/NW key rows
 // i = g*RW .. g*RW + RW-1 of that column in registers.  Every value column
 // evolves independently given the shared key-side vectors, so the update is
@@ -28,12 +30,11 @@
 namespace wkv7 {
 namespace {
 
-constexpr int NW = 4;          // waves per head
-constexpr int RW = kN / NW;    // key rows per wave
 constexpr int TB = 8;          // tokens per staged block
 
 // RW consecutive elements of a key-side vector, widened to fp32, from a
 // wave-uniform address (scalar loads).
+template <int RW>
 __device__ __forceinline__ void load_rows(const uint16_t *__restrict__ p, float (&x)[RW])
 {
     const uint32_t *p32 = reinterpret_cast<const uint32_t *>(p);
@@ -44,6 +45,7 @@ __device__ __forceinline__ void load_rows(const uint16_t *__restrict__ p, float 
         x[2 * u + 1] = __uint_as_float(bits & 0xffff0000u);
     }
 }
+template <int RW>
 __device__ __forceinline__ void load_rows(const float *__restrict__ p, float (&x)[RW])
 {
 #pragma unroll
@@ -57,12 +59,13 @@ __device__ __forceinline__ void load_rows(const float *__restrict__ p, float (&x
 // stage blocks of TB tokens, widened to fp32, in LDS with one cooperative
 // load, so no global latency sits inside the token loop.  The arithmetic is
 // the same code either way.
-template <typename Tin, typename Tout, bool HAS_STATE_IN, bool WRITE_POS, bool STAGED>
+template <typename Tin, typename Tout, bool HAS_STATE_IN, bool WRITE_POS, bool STAGED, int NW>
 __global__ __launch_bounds__(NW * 64) void wkv7_step_kernel(
     const Tin *__restrict__ r, const Tin *__restrict__ w, const Tin *__restrict__ k, const Tin *__restrict__ v,
     const Tin *__restrict__ a, const Tin *__restrict__ b, const float *state_in, Tout *__restrict__ o,
     float *state_out, float *__restrict__ state_pos, int T, int H)
 {
+    constexpr int RW = kN / NW;                                       // key rows per wave
     const int j = threadIdx.x & 63;                                   // value column of this lane
     const int g = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // row block of this wave
     const int i0 = g * RW;
@@ -180,7 +183,7 @@ __global__ __launch_bounds__(NW * 64) void wkv7_step_kernel(
         __builtin_nontemporal_store(S[u], state_out + sbase + u * kN);
 }
 
-template <typename Tin, typename Tout, bool STAGED>
+template <typename Tin, typename Tout, bool STAGED, int NW>
 hipError_t launch_mode(const SeqArgs &p, hipStream_t stream)
 {
     const dim3 grid(static_cast<unsigned>(p.B) * static_cast<unsigned>(p.H)), block(NW * 64);
@@ -190,7 +193,7 @@ hipError_t launch_mode(const SeqArgs &p, hipStream_t stream)
     Tout *o = static_cast<Tout *>(p.o);
     const bool sin = p.state_in != nullptr, pos = p.state_pos != nullptr;
 #define WKV7_STEP_LAUNCH(SIN, POS)                                                                                \
-    hipLaunchKernelGGL((wkv7_step_kernel<Tin, Tout, SIN, POS, STAGED>), grid, block, 0, stream, r, w, k, v, a, b, \
+    hipLaunchKernelGGL((wkv7_step_kernel<Tin, Tout, SIN, POS, STAGED, NW>), grid, block, 0, stream, r, w, k, v, a, b, \
                        p.state_in, o, p.state_out, p.state_pos, p.T, p.H)
     if (sin && pos)
         WKV7_STEP_LAUNCH(true, true);
@@ -207,7 +210,8 @@ hipError_t launch_mode(const SeqArgs &p, hipStream_t stream)
 template <typename Tin, typename Tout>
 hipError_t launch_typed(const SeqArgs &p, hipStream_t stream)
 {
-    return p.T > 1 ? launch_mode<Tin, Tout, true>(p, stream) : launch_mode<Tin, Tout, false>(p, stream);
+    // waves per head: four for a single token, eight for longer runs (measured best)
+    return p.T > 1 ? launch_mode<Tin, Tout, true, 8>(p, stream) : launch_mode<Tin, Tout, false, 4>(p, stream);
 }
 
 // Copy (or zero, when src is null) n_floats of state; n_floats is a multiple of 4.
