@@ -68,8 +68,10 @@ constexpr float W_MIN = 0x1p-15f;  // lower bound applied to decay multipliers i
 // producer waves: ten with bf16 inputs (two inverse and two decay waves), eight with fp32 inputs
 template <typename Tin>
 constexpr int nprod() { return std::is_same<Tin, float>::value ? 8 : 10; }
-constexpr int LDA = kN + 8;        // row pitch (bf16) of [16][64] planes
-constexpr int LDT = CH + 8;        // row pitch (bf16) of [16][16] planes
+// LDS layouts are chosen so that every access pattern below runs free of
+// bank conflicts on gfx950 (64 banks of 4 bytes): 160-byte rows for the
+// [16][64] planes, and XOR-swizzled, unpadded [16][16] tiles and decay rows.
+constexpr int LDA = kN + 16;       // row pitch (bf16) of [16][64] planes
 constexpr int NDROW = 2 * CH + 1;  // decay table rows: d_0 .. d_16, then id_1 .. id_16
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -189,14 +191,16 @@ __device__ __forceinline__ int key_slot(int i)
 {
     return 32 * (i >> 5) + 8 * ((i >> 2) & 3) + 4 * ((i >> 4) & 1) + (i & 3);
 }
-// Place of key slot s in a row of the decay table: slots 8 g + 4 h + c go to
-// 32 h + 4 g + c, so that eight lanes reading the first (or second) halves of
-// their eight slots read 128 contiguous bytes.
-__device__ __forceinline__ int dpos(int s) { return 32 * ((s >> 2) & 1) + 4 * (s >> 3) + (s & 3); }
+// Column of key channel i in row r of the decay table: key order, with the
+// two 16-key halves of each 32-key group exchanged on odd rows.
+__device__ __forceinline__ int dcol(int r, int i) { return i ^ (16 * (r & 1)); }
+// Place of the four elements [row][4 c .. 4 c + 3] of a 16x16 matrix tile:
+// the 8-byte unit c moves to c ^ (row / 4 % 4).
+__device__ __forceinline__ int mcol(int row, int c) { return 4 * (c ^ ((row >> 2) & 3)); }
 
 // One chunk's operands and matrices in LDS (bf16 bit patterns; NP planes).
 // The 16x16 matrices are stored transposed, [s][tau], as their producers hold
-// them; consumers read them back with transpose loads.
+// them, at mcol(); consumers read them back with transpose loads.
 // Planes are selected by index (never by choosing between pointers), the
 // operands as X[OP_A], X[OP_R], X[OP_B], X[OP_K] and the matrices as
 // Mt[MT_T], Mt[MT_AK], Mt[MT_RB], Mt[MT_RK].
@@ -206,12 +210,12 @@ template <int NP, int NPV>
 struct alignas(16) Slot {
     uint16_t X[4][NP][CH][LDA];   // A'[tau], R'[tau], B'[s], K'[s] over key_slot(i)
     uint16_t Vr[NPV][CH][LDA];    // v[s][j], all 64 value columns
-    uint16_t Mt[4][NP][CH][LDT];  // T, M_ak, M_rb, M_rk: element [tau][s] stored at [s][tau]
+    uint16_t Mt[4][NP][CH][CH];   // T, M_ak, M_rb, M_rk: element [tau][s] stored at [s][tau]
     alignas(16) float f[kN];      // d_15 of this chunk times P_7 of the next one (d_15 alone for the last)
 };
 
 // Decay factors of one chunk per key channel, rows d_0 .. d_16 and id_1 .. id_16
-// (d_{tau+1} = P_tau / P_7, id_{tau+1} = P_7 / P_tau), columns at dpos(key_slot(i)).
+// (d_{tau+1} = P_tau / P_7, id_{tau+1} = P_7 / P_tau), key i of row r at dcol(r, i).
 struct alignas(16) DSlot {
     float v[NDROW][kN];
 };
@@ -319,6 +323,7 @@ __global__ __launch_bounds__((kN / J / 16 + nprod<Tin>()) * 64) void wkv7_chunk_
                 Sx[pt][e] = HAS_STATE_IN ? p.state_in[sbase + (16 * pt + 4 * q + e) * kN + jw + m] : 0.0f;
         // transpose-load address pieces of this lane: row 4 q + m/4, column group m%4
         const int trow = 4 * q + (m >> 2), tcol = 4 * (m & 3);
+        const int mcol_t = mcol(trow, m & 3);  // the same unit in a swizzled matrix tile
         uint32_t ooff[4];  // output offsets of this lane's rows 4 q + e, column m, from a chunk's base
 #pragma unroll
         for (int e = 0; e < 4; ++e)
@@ -393,7 +398,7 @@ __global__ __launch_bounds__((kN / J / 16 + nprod<Tin>()) * 64) void wkv7_chunk_
                     s16x4 Mf[NP];
 #pragma unroll
                     for (int pl = 0; pl < NP; ++pl)
-                        Mf[pl] = tr4(&sl.Mt[MT_AK][pl][trow][tcol]);
+                        Mf[pl] = tr4(&sl.Mt[MT_AK][pl][trow][mcol_t]);
                     mma16<NP, NPV>(ym, Mf, Vf);
                 }
                 // Z = T Y  (Y = A' S^ + M_ak V in accumulator layout: Y[4 q + e][col m])
@@ -406,7 +411,7 @@ __global__ __launch_bounds__((kN / J / 16 + nprod<Tin>()) * 64) void wkv7_chunk_
                     s16x4 Tf[NP], Yf[NP];
 #pragma unroll
                     for (int pl = 0; pl < NP; ++pl)
-                        Tf[pl] = tr4(&sl.Mt[MT_T][pl][trow][tcol]);
+                        Tf[pl] = tr4(&sl.Mt[MT_T][pl][trow][mcol_t]);
                     split4<NP>(y4, Yf);
                     mma16<NP, NP>(z, Tf, Yf);
                 }
@@ -436,7 +441,7 @@ __global__ __launch_bounds__((kN / J / 16 + nprod<Tin>()) * 64) void wkv7_chunk_
                     s16x8 Mf[NP];
 #pragma unroll
                     for (int pl = 0; pl < NP; ++pl)
-                        Mf[pl] = cat(tr4(&sl.Mt[MT_RB][pl][trow][tcol]), tr4(&sl.Mt[MT_RK][pl][trow][tcol]));
+                        Mf[pl] = cat(tr4(&sl.Mt[MT_RB][pl][trow][mcol_t]), tr4(&sl.Mt[MT_RK][pl][trow][mcol_t]));
                     mma32<NP, NP>(o3, Mf, ZV);
                 }
                 {
@@ -607,13 +612,12 @@ __global__ __launch_bounds__((kN / J / 16 + nprod<Tin>()) * 64) void wkv7_chunk_
     auto decay2_body = [&](int c) {  // 0 <= c < nchunks
         const int i = lane;
         DSlot &D = sm.dt[c & 1];
-        const int ps = dpos(key_slot(i));
 #pragma unroll
         for (int r = 0; r <= CH; ++r)
-            D.v[r][ps] = dk[r];
+            D.v[r][dcol(r, i)] = dk[r];
 #pragma unroll
         for (int r = 1; r <= CH; ++r)
-            D.v[CH + r][ps] = idk[r];
+            D.v[CH + r][dcol(CH + r, i)] = idk[r];
         if (c == 0)
             sm.p7[i] = idk[0];
         else
@@ -658,8 +662,9 @@ __global__ __launch_bounds__((kN / J / 16 + nprod<Tin>()) * 64) void wkv7_chunk_
                 for (int e = 0; e < 8; ++e)
                     x[e] = 0.0f;
             }
-            const f32x4 d0 = *reinterpret_cast<const f32x4 *>(&D.v[roff + tau][4 * g8]);
-            const f32x4 d1 = *reinterpret_cast<const f32x4 *>(&D.v[roff + tau][32 + 4 * g8]);
+            const int drow = roff + tau;
+            const f32x4 d0 = *reinterpret_cast<const f32x4 *>(&D.v[drow][dcol(drow, k0)]);
+            const f32x4 d1 = *reinterpret_cast<const f32x4 *>(&D.v[drow][dcol(drow, k0 + 16)]);
             float y[8];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -741,12 +746,12 @@ __global__ __launch_bounds__((kN / J / 16 + nprod<Tin>()) * 64) void wkv7_chunk_
         constexpr int mt = MR ? MT_RB : MT_AK;
 #pragma unroll
         for (int pl = 0; pl < NP; ++pl)
-            *reinterpret_cast<s16x4 *>(&sl.Mt[mt][pl][m][4 * q]) = pc[pl];
+            *reinterpret_cast<s16x4 *>(&sl.Mt[mt][pl][m][mcol(m, q)]) = pc[pl];
         if constexpr (MR) {
             split4<NP>(mv2, pc);
 #pragma unroll
             for (int pl = 0; pl < NP; ++pl)
-                *reinterpret_cast<s16x4 *>(&sl.Mt[MT_RK][pl][m][4 * q]) = pc[pl];
+                *reinterpret_cast<s16x4 *>(&sl.Mt[MT_RK][pl][m][mcol(m, q)]) = pc[pl];
         }
     };
 
@@ -816,7 +821,7 @@ __global__ __launch_bounds__((kN / J / 16 + nprod<Tin>()) * 64) void wkv7_chunk_
         split4<NP>(Q, tp);
 #pragma unroll
         for (int pl = 0; pl < NP; ++pl)
-            *reinterpret_cast<s16x4 *>(&sl.Mt[MT_T][pl][m][4 * q]) = tp[pl];
+            *reinterpret_cast<s16x4 *>(&sl.Mt[MT_T][pl][m][mcol(m, q)]) = tp[pl];
     };
     auto inv_b = [&](int c) {
         if (c >= 0 && c < nchunks)
