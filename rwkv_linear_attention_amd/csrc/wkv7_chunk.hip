@@ -498,6 +498,9 @@ __global__ __launch_bounds__((kN / J / 16 + nprod<Tin>()) * 64) void wkv7_chunk_
                           : (0x25316470 >> (4 * (wv - NSW))) & 15;  // T SK SA SB MA D SR MR
     const int t_end = T;
 
+    using F = std::integral_constant<bool, false>;
+    using U = std::integral_constant<bool, true>;
+
     // ---- input path: the decay and scale waves load their own rows, in their
     // own lane layouts, two iterations ahead of use, into alternating register
     // sets (rows past the end are clamped here and masked where they are used).
@@ -633,13 +636,13 @@ __global__ __launch_bounds__((kN / J / 16 + nprod<Tin>()) * 64) void wkv7_chunk_
 
     // ---- scale waves: X' = x * factor, elementwise, lane = (token, slot group):
     // token 8 pass + lane/8, key slots 8 g8 .. 8 g8 + 7.
-    auto scale = [&](const Raw &R, int c, auto with_v) {
-        if (c < 0 || c >= nchunks)
-            return;
+    // The last, partial chunk has its own copy of the body (rows past the end
+    // read as 0), so full chunks carry no per-row selects.
+    auto scale_body = [&](const Raw &R, int c, auto with_v, auto partial_c) {
+        constexpr bool partial = decltype(partial_c)::value;
         SlotT &sl = sm.slot[c % NS];
         const DSlot &D = sm.dt[c & 1];
         const int roff = op == 0 ? 0 : op == 1 ? 1 : CH + 1;  // table row of token tau
-        const bool partial = c * CH + CH > t_end;  // uniform; rows past the end read as 0
 #pragma unroll
         for (int pz = 0; pz < 2; ++pz) {
             const int tau = 8 * pz + (lane >> 3);
@@ -700,6 +703,14 @@ __global__ __launch_bounds__((kN / J / 16 + nprod<Tin>()) * 64) void wkv7_chunk_
                 }
             }
         }
+    };
+    auto scale = [&](const Raw &R, int c, auto with_v) {
+        if (c < 0 || c >= nchunks)
+            return;
+        if (c * CH + CH > t_end)  // uniform
+            scale_body(R, c, with_v, U{});
+        else
+            scale_body(R, c, with_v, F{});
     };
 
     // ---- matrix waves: 16x16 tiles M = tril(X' Y'^T) of chunk c over the 64 key
@@ -835,8 +846,6 @@ __global__ __launch_bounds__((kN / J / 16 + nprod<Tin>()) * 64) void wkv7_chunk_
     // are loaded in the same order as in every later round, so the compiler's
     // waits (which may also cover the set loaded one round before) only ever
     // wait for rows two or more iterations old.
-    using F = std::integral_constant<bool, false>;
-    using U = std::integral_constant<bool, true>;
     using K0 = std::integral_constant<int, 0>;
     using K1 = std::integral_constant<int, 1>;
     using K2 = std::integral_constant<int, 2>;
