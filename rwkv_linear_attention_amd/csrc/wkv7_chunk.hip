@@ -324,10 +324,16 @@ __global__ __launch_bounds__((kN / J / 16 + nprod<Tin>()) * 64) void wkv7_chunk_
         // transpose-load address pieces of this lane: row 4 q + m/4, column group m%4
         const int trow = 4 * q + (m >> 2), tcol = 4 * (m & 3);
         const int mcol_t = mcol(trow, m & 3);  // the same unit in a swizzled matrix tile
-        uint32_t ooff[4];  // output offsets of this lane's rows 4 q + e, column m, from a chunk's base
+        // byte offsets of this lane's outputs (rows 4 q + e, column m) from a chunk's
+        // base: 32-bit offsets from a uniform base keep the stores' addresses in one register
+        uint32_t ooff[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-            ooff[e] = static_cast<uint32_t>(4 * q + e) * rs32 + m;
+            ooff[e] = (static_cast<uint32_t>(4 * q + e) * rs32 + m) * static_cast<uint32_t>(sizeof(Tout));
+        auto store_o = [](Tout *base, uint32_t off, float x) {
+            asm volatile("" : "+v"(off));  // keeps the offset 32-bit (not widened ahead of the loop)
+            store_elem(reinterpret_cast<Tout *>(reinterpret_cast<char *>(base) + off), 0, x);
+        };
 
         // A' and v of the next chunk are read at the end of each iteration
         // (they were final one or more iterations before) and stay in flight
@@ -350,6 +356,20 @@ __global__ __launch_bounds__((kN / J / 16 + nprod<Tin>()) * 64) void wkv7_chunk_
             if (i >= 0) {
                 const SlotT &sl = sm.slot[i % NS];
                 const int t0 = i * CH;
+                // this chunk's R' rows and the M_ak and T tiles, read first so that
+                // they arrive while S^ is split
+                s16x8 Rf[2][NP];
+                s16x4 Mak[NP], Tf[NP];
+#pragma unroll
+                for (int s = 0; s < 2; ++s)
+#pragma unroll
+                    for (int pl = 0; pl < NP; ++pl)
+                        Rf[s][pl] = lds8(&sl.X[OP_R][pl][m][32 * s + 8 * q]);
+#pragma unroll
+                for (int pl = 0; pl < NP; ++pl) {
+                    Mak[pl] = tr4(&sl.Mt[MT_AK][pl][trow][mcol_t]);
+                    Tf[pl] = tr4(&sl.Mt[MT_T][pl][trow][mcol_t]);
+                }
                 if (i == 0) {
                     // S^ = diag(P_7) S_in for the first chunk; afterwards every chunk
                     // leaves S^ of the next one (its row factor folds both scalings).
@@ -380,13 +400,11 @@ __global__ __launch_bounds__((kN / J / 16 + nprod<Tin>()) * 64) void wkv7_chunk_
                 for (int s = 0; s < 2; ++s) {
                     y2[s] = f32x4{0.f, 0.f, 0.f, 0.f};
                     o2[s] = f32x4{0.f, 0.f, 0.f, 0.f};
-                    s16x8 Rf[NP];
-#pragma unroll
-                    for (int pl = 0; pl < NP; ++pl)
-                        Rf[pl] = lds8(&sl.X[OP_R][pl][m][32 * s + 8 * q]);
                     mma32<NP, NP>(y2[s], pA[s], Bs[s]);
-                    mma32<NP, NP>(o2[s], Rf, Bs[s]);
                 }
+#pragma unroll
+                for (int s = 0; s < 2; ++s)
+                    mma32<NP, NP>(o2[s], Rf[s], Bs[s]);
                 // V rows as a B operand over the token index (slot (q, e) = token 4 q + e)
                 s16x4 Vf[NPV];
 #pragma unroll
@@ -394,13 +412,7 @@ __global__ __launch_bounds__((kN / J / 16 + nprod<Tin>()) * 64) void wkv7_chunk_
                     Vf[pl] = pV[pl];
                 // M_ak V
                 f32x4 ym = {0.f, 0.f, 0.f, 0.f};
-                {
-                    s16x4 Mf[NP];
-#pragma unroll
-                    for (int pl = 0; pl < NP; ++pl)
-                        Mf[pl] = tr4(&sl.Mt[MT_AK][pl][trow][mcol_t]);
-                    mma16<NP, NPV>(ym, Mf, Vf);
-                }
+                mma16<NP, NPV>(ym, Mak, Vf);
                 // Z = T Y  (Y = A' S^ + M_ak V in accumulator layout: Y[4 q + e][col m])
                 f32x4 z = {0.f, 0.f, 0.f, 0.f};
                 {
@@ -408,10 +420,7 @@ __global__ __launch_bounds__((kN / J / 16 + nprod<Tin>()) * 64) void wkv7_chunk_
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
                         y4[e] = (y2[0][e] + y2[1][e]) + ym[e];
-                    s16x4 Tf[NP], Yf[NP];
-#pragma unroll
-                    for (int pl = 0; pl < NP; ++pl)
-                        Tf[pl] = tr4(&sl.Mt[MT_T][pl][trow][mcol_t]);
+                    s16x4 Yf[NP];
                     split4<NP>(y4, Yf);
                     mma16<NP, NP>(z, Tf, Yf);
                 }
@@ -450,12 +459,12 @@ __global__ __launch_bounds__((kN / J / 16 + nprod<Tin>()) * 64) void wkv7_chunk_
                     if (t0 + CH <= T) {
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
-                            store_elem(ob, ooff[e], (o2[0][e] + o2[1][e]) + o3[e]);
+                            store_o(ob, ooff[e], (o2[0][e] + o2[1][e]) + o3[e]);
                     } else {
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
                             if (t0 + 4 * q + e < T)
-                                store_elem(ob, ooff[e], (o2[0][e] + o2[1][e]) + o3[e]);
+                                store_o(ob, ooff[e], (o2[0][e] + o2[1][e]) + o3[e]);
                     }
                 }
                 // S^ <- diag(f) (S^ + [B'^T | K'^T] [Z ; V]), one 16-row tile at a time;
