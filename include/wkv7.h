@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define WKV7_ABI_VERSION 1
+#define WKV7_ABI_VERSION 2
 
 /* Element types of r, w, k, v, a, b (in_dtype) and of o (o_dtype). */
 enum wkv7_dtype {
@@ -100,6 +100,26 @@ int wkv7_forward(const void *r, const void *w, const void *k, const void *v,
                  int B, int T, int H, int N, void *stream);
 
 /*
+ * wkv7_forward_varlen -- wkv7_forward over right-padded rows of their own lengths
+ * (batched prefill of prompts of different lengths).
+ *
+ * Arguments as for wkv7_forward, plus
+ *   lengths : [B] int32 on the device (4-byte aligned).  Row b runs its first
+ *             L_b = lengths[b] tokens, L_b clamped to [0, T]: o[b, t] for
+ *             t < L_b and state_out[b] (the state after those L_b tokens;
+ *             state_in[b], or zeros, when L_b = 0) are written, and o[b, t]
+ *             for t >= L_b is left untouched.  The inputs keep the [B,T,H,N]
+ *             layout with row stride T; the values past L_b are not read.
+ * A NULL lengths is refused (WKV7_ERR_NULL); lengths may not overlap o or
+ * state_out (WKV7_ERR_ALIAS).  The lengths are device values, so they are not
+ * checked here: values outside [0, T] are clamped by the kernels.
+ */
+int wkv7_forward_varlen(const void *r, const void *w, const void *k, const void *v,
+                        const void *a, const void *b, int in_dtype,
+                        const float *state_in, void *o, int o_dtype, float *state_out,
+                        const int *lengths, int B, int T, int H, int N, void *stream);
+
+/*
  * wkv7_step -- the recurrent (decode / speculative-verify) pass, token by token.
  *
  * Arguments as for wkv7_forward, plus
@@ -126,6 +146,25 @@ int wkv7_step(const void *r, const void *w, const void *k, const void *v,
  */
 int wkv7_state_reset(float *state, int B, int H, int N, const unsigned char *row_mask,
                      void *stream);
+
+/*
+ * wkv7_state_commit -- keep the state after each row's accepted prefix of a
+ * speculative verify step (RWKV7-MTP-Exp model card, section "Inference": the
+ * recurrent state is rolled back to the accepted prefix).
+ *
+ *   state_pos : [B,T,H,N,N] fp32, the per-position states of wkv7_step
+ *               (state_pos[b,t] = state after token t); may be NULL when T = 0.
+ *   accepted  : [B] int32 on the device (4-byte aligned): n_b tokens of row b
+ *               are accepted.
+ *   state_in  : [B,H,N,N] fp32, the state before the step, or NULL (zeros).
+ *   state_out : [B,H,N,N] fp32; may equal state_in exactly.
+ * Row b of state_out becomes state_pos[b, n_b - 1] for 1 <= n_b <= T and
+ * state_in[b] for n_b = 0; a row with n_b outside [0, T] is left untouched
+ * (device values are not checked here).  state_out may not overlap state_pos
+ * or accepted, and may overlap state_in only by being equal to it.
+ */
+int wkv7_state_commit(const float *state_pos, const int *accepted, const float *state_in,
+                      float *state_out, int B, int T, int H, int N, void *stream);
 
 /* A static, human-readable name for a status code (never NULL). */
 const char *wkv7_status_string(int status);

@@ -105,3 +105,54 @@ def forward(r, w, k, v, a, b, state_in=None, *, per_position=False, nthreads=0,
     if per_position:
         return o, s_out, s_pos
     return o, s_out
+
+
+def forward_varlen(r, w, k, v, a, b, state_in=None, lengths=None, **kw):
+    """Rows of their own lengths: row b runs only its first L_b tokens.
+
+    The batched prefill of the SwiftRWKV Inference guide (its batched
+    generation) pads prompts on the right and ends each row on its own last
+    real token.  Plain definition: L_b = lengths[b] clamped to [0, T]; row b is
+    ``forward`` over tokens [0, L_b) of that row from state_in[b] (zeros when
+    None).  Returns (o [B,T,H,N], state_out [B,H,N,N]), fp64, with o[b, t] = NaN
+    for t >= L_b (those outputs are not defined).
+    """
+    B, T, H, N = np.asarray(r.shape if hasattr(r, "shape") else np.shape(r))
+    L = np.clip(np.asarray(lengths, dtype=np.int64).reshape(-1), 0, T)
+    if L.shape != (B,):
+        raise ValueError(f"lengths must have {B} entries")
+    o = np.full((B, T, H, N), np.nan)
+    s_out = np.zeros((B, H, N, N))
+    for bb in range(B):
+        s0 = None if state_in is None else state_in[bb:bb + 1]
+        if L[bb] == 0:
+            if s0 is not None:
+                s_out[bb] = _as_input(s0, np.float64)[0]
+            continue
+        rows = [x[bb:bb + 1, :L[bb]] for x in (r, w, k, v, a, b)]
+        o_b, s_b = forward(*rows, s0, **kw)
+        o[bb, :L[bb]] = o_b[0]
+        s_out[bb] = s_b[0]
+    return o, s_out
+
+
+def state_commit(state_pos, accepted, state_in=None, state_out=None):
+    """The state after each row's accepted prefix of a speculative verify step.
+
+    The RWKV7-MTP-Exp model card ("Inference") rolls the recurrent state back
+    to the accepted prefix.  Plain definition, with n = accepted[b] and T the
+    step length: row b is state_pos[b, n - 1] for 1 <= n <= T, state_in[b]
+    (zeros when None) for n = 0, and state_out[b] unchanged (zeros when None)
+    for n outside [0, T].  Returns [B, H, N, N] fp64.
+    """
+    sp = _as_input(state_pos, np.float64)
+    B, T, H, N, _ = sp.shape
+    acc = np.asarray(accepted, dtype=np.int64).reshape(-1)
+    out = np.zeros((B, H, N, N)) if state_out is None else _as_input(state_out, np.float64).copy()
+    for bb in range(B):
+        n = int(acc[bb])
+        if 1 <= n <= T:
+            out[bb] = sp[bb, n - 1]
+        elif n == 0:
+            out[bb] = 0.0 if state_in is None else _as_input(state_in, np.float64)[bb]
+    return out

@@ -9,10 +9,13 @@ PyTorch fallback, and the calls fail loudly when the library is not built.
 
 Functions (names as in the C ABI):
 
-* ``wkv7_forward(r, w, k, v, a, b, state_in=None, o_dtype=torch.float32)``
-  -> ``(o, state_out)``: the parallel (prefill) pass.
+* ``wkv7_forward(r, w, k, v, a, b, state_in=None, o_dtype=torch.float32, lengths=None)``
+  -> ``(o, state_out)``: the parallel (prefill) pass; with ``lengths`` ([B] int32),
+  row b runs its first lengths[b] tokens (``wkv7_forward_varlen`` of the C ABI).
 * ``wkv7_step(r, w, k, v, a, b, state_in=None, per_position=False, ...)``
   -> ``(o, state_out[, state_pos])``: the recurrent (decode / verify) pass.
+* ``wkv7_state_commit(state_pos, accepted, state_in=None)`` -> ``state_out``: the state
+  after each row's accepted prefix of a speculative verify step.
 * ``wkv7_state_reset(state, row_mask=None)``: zero the state (all rows or masked ones).
 
 Tensors: r, w, k, v, a, b are [B, T, H, 64] bf16 or fp32 on the GPU; the
@@ -59,8 +62,12 @@ def lib():
         vp, ci = ctypes.c_void_p, ctypes.c_int
         L.wkv7_forward.argtypes = [vp] * 6 + [ci, vp, vp, ci, vp, ci, ci, ci, ci, vp]
         L.wkv7_forward.restype = ci
+        L.wkv7_forward_varlen.argtypes = [vp] * 6 + [ci, vp, vp, ci, vp, vp, ci, ci, ci, ci, vp]
+        L.wkv7_forward_varlen.restype = ci
         L.wkv7_step.argtypes = [vp] * 6 + [ci, vp, vp, ci, vp, vp, ci, ci, ci, ci, vp]
         L.wkv7_step.restype = ci
+        L.wkv7_state_commit.argtypes = [vp, vp, vp, vp, ci, ci, ci, ci, vp]
+        L.wkv7_state_commit.restype = ci
         L.wkv7_state_reset.argtypes = [vp, ci, ci, ci, vp, vp]
         L.wkv7_state_reset.restype = ci
         L.wkv7_status_string.argtypes = [ci]
@@ -119,10 +126,21 @@ def _state_arg(state, B, H, N, device, name):
     return state
 
 
-def wkv7_forward(r, w, k, v, a, b, state_in=None, *, o_dtype=torch.float32, o=None, state_out=None):
+def _int_rows(x, B, device, name):
+    """A [B] int32 device tensor (converted from any integer tensor or sequence)."""
+    x = torch.as_tensor(x, device=device).to(torch.int32).contiguous()
+    if x.shape != (B,):
+        raise ValueError(f"{name} must have shape [{B}]")
+    return x
+
+
+def wkv7_forward(r, w, k, v, a, b, state_in=None, *, o_dtype=torch.float32, o=None, state_out=None,
+                 lengths=None):
     """Parallel pass over the whole sequence.  Returns (o, state_out).
 
     state_out may be passed as state_in itself to update the state in place.
+    With lengths ([B] integers), row b runs its first lengths[b] tokens (clamped
+    to [0, T]); o[b, t] for t >= lengths[b] is left as it was.
     """
     B, T, H, N = _check_inputs(r, w, k, v, a, b)
     dev = r.device
@@ -134,8 +152,14 @@ def wkv7_forward(r, w, k, v, a, b, state_in=None, *, o_dtype=torch.float32, o=No
         o = torch.empty((B, T, H, N), dtype=o_dtype, device=dev)
     if o.shape != r.shape or not o.is_contiguous() or o.device != dev:
         raise ValueError("o must be a contiguous [B, T, H, N] tensor on the inputs' device")
-    _check(lib().wkv7_forward(*[_ptr(x) for x in (r, w, k, v, a, b)], _dt(r), _ptr(state_in), _ptr(o),
-                              _dt(o), _ptr(state_out), B, T, H, N, _stream(dev)))
+    if lengths is None:
+        _check(lib().wkv7_forward(*[_ptr(x) for x in (r, w, k, v, a, b)], _dt(r), _ptr(state_in), _ptr(o),
+                                  _dt(o), _ptr(state_out), B, T, H, N, _stream(dev)))
+    else:
+        lengths = _int_rows(lengths, B, dev, "lengths")
+        _check(lib().wkv7_forward_varlen(*[_ptr(x) for x in (r, w, k, v, a, b)], _dt(r), _ptr(state_in),
+                                         _ptr(o), _dt(o), _ptr(state_out), _ptr(lengths), B, T, H, N,
+                                         _stream(dev)))
     return o, state_out
 
 
@@ -163,6 +187,29 @@ def wkv7_step(r, w, k, v, a, b, state_in=None, *, per_position=False, o_dtype=to
     if state_pos is not None:
         return o, state_out, state_pos
     return o, state_out
+
+
+def wkv7_state_commit(state_pos, accepted, state_in=None, *, state_out=None):
+    """State after each row's accepted prefix of a verify step.  Returns state_out.
+
+    state_pos: [B, T, H, N, N] from wkv7_step(per_position=True); accepted: [B]
+    integers.  Row b becomes state_pos[b, accepted[b] - 1], or state_in[b] (zeros
+    when None) for accepted[b] == 0; rows with accepted[b] outside [0, T] keep
+    state_out (pass state_out=state_in to commit in place).
+    """
+    if state_pos.dim() != 5 or not state_pos.is_cuda or state_pos.dtype != torch.float32 \
+            or not state_pos.is_contiguous():
+        raise ValueError("state_pos must be a contiguous fp32 [B, T, H, N, N] GPU tensor")
+    B, T, H, N, _ = state_pos.shape
+    dev = state_pos.device
+    accepted = _int_rows(accepted, B, dev, "accepted")
+    state_in = _state_arg(state_in, B, H, N, dev, "state_in")
+    if state_out is None:
+        state_out = torch.empty((B, H, N, N), dtype=torch.float32, device=dev)
+    _state_arg(state_out, B, H, N, dev, "state_out")
+    _check(lib().wkv7_state_commit(_ptr(state_pos), _ptr(accepted), _ptr(state_in), _ptr(state_out),
+                                   B, T, H, N, _stream(dev)))
+    return state_out
 
 
 def wkv7_state_reset(state, row_mask=None):

@@ -108,6 +108,7 @@ SeqArgs make_args(const void *r, const void *w, const void *k, const void *v, co
     SeqArgs s;
     s.r = r; s.w = w; s.k = k; s.v = v; s.a = a; s.b = b;
     s.state_in = state_in; s.o = o; s.state_out = state_out; s.state_pos = state_pos;
+    s.lengths = nullptr;
     s.B = B; s.T = T; s.H = H;
     s.in_bf16 = in_dtype == WKV7_BF16;
     s.o_bf16 = o_dtype == WKV7_BF16;
@@ -137,6 +138,33 @@ int wkv7_forward(const void *r, const void *w, const void *k, const void *v, con
     if (T == 0)
         return empty_sequence(state_in, state_out, B, H, s);
     const SeqArgs args = make_args(r, w, k, v, a, b, in_dtype, state_in, o, o_dtype, state_out, nullptr, B, T, H);
+    const hipError_t e = T < kChunkMinT ? wkv7::launch_step(args, s) : wkv7::launch_chunk(args, s);
+    return e == hipSuccess ? WKV7_OK : WKV7_ERR_HIP;
+}
+
+int wkv7_forward_varlen(const void *r, const void *w, const void *k, const void *v, const void *a,
+                        const void *b, int in_dtype, const float *state_in, void *o, int o_dtype,
+                        float *state_out, const int *lengths, int B, int T, int H, int N, void *stream)
+{
+    int st = check_seq(r, w, k, v, a, b, in_dtype, state_in, o, o_dtype, state_out, nullptr, B, T, H, N);
+    if (st != WKV7_OK)
+        return st;
+    if (!lengths)
+        return WKV7_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(lengths) & 3u) != 0)
+        return WKV7_ERR_ALIGN;
+    // the lengths must not overlap an output
+    const Range rl = range_of(lengths, static_cast<int64_t>(B) * 4);
+    const int64_t eo = o_dtype == WKV7_BF16 ? 2 : 4;
+    const int64_t st_bytes = static_cast<int64_t>(B) * H * kN * kN * 4;
+    if (overlap(rl, range_of(state_out, st_bytes)) ||
+        (T > 0 && overlap(rl, range_of(o, static_cast<int64_t>(B) * T * H * kN * eo))))
+        return WKV7_ERR_ALIAS;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (T == 0)
+        return empty_sequence(state_in, state_out, B, H, s);
+    SeqArgs args = make_args(r, w, k, v, a, b, in_dtype, state_in, o, o_dtype, state_out, nullptr, B, T, H);
+    args.lengths = lengths;
     const hipError_t e = T < kChunkMinT ? wkv7::launch_step(args, s) : wkv7::launch_chunk(args, s);
     return e == hipSuccess ? WKV7_OK : WKV7_ERR_HIP;
 }
@@ -172,6 +200,38 @@ int wkv7_state_reset(float *state, int B, int H, int N, const unsigned char *row
             return WKV7_ERR_ALIAS;
     }
     return wkv7::launch_state_reset(state, B, H, row_mask, static_cast<hipStream_t>(stream)) == hipSuccess
+               ? WKV7_OK
+               : WKV7_ERR_HIP;
+}
+
+int wkv7_state_commit(const float *state_pos, const int *accepted, const float *state_in, float *state_out,
+                      int B, int T, int H, int N, void *stream)
+{
+    int64_t tok = 0;
+    if (N != kN)
+        return WKV7_ERR_UNSUPPORTED;
+    if (!shape_ok(B, T, H, &tok))
+        return WKV7_ERR_SHAPE;
+    if (!accepted || !state_out || (T > 0 && !state_pos))
+        return WKV7_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(accepted) & 3u) != 0)
+        return WKV7_ERR_ALIGN;
+    const void *ptrs[] = {state_pos, state_in, state_out};
+    for (const void *ptr : ptrs)
+        if (ptr && misaligned(ptr))
+            return WKV7_ERR_ALIGN;
+    const int64_t st_bytes = static_cast<int64_t>(B) * H * kN * kN * 4;
+    const Range rst = range_of(state_out, st_bytes);
+    const Range racc = range_of(accepted, static_cast<int64_t>(B) * 4);
+    Range rpos{0, 0}, rin{0, 0};
+    if (T > 0)
+        rpos = range_of(state_pos, tok * kN * kN * 4);
+    if (state_in)
+        rin = range_of(state_in, st_bytes);
+    if (overlap(rst, rpos) || overlap(rst, racc) || (state_in && state_in != state_out && overlap(rst, rin)))
+        return WKV7_ERR_ALIAS;
+    return wkv7::launch_state_commit(state_pos, accepted, state_in, state_out, B, T, H,
+                                     static_cast<hipStream_t>(stream)) == hipSuccess
                ? WKV7_OK
                : WKV7_ERR_HIP;
 }

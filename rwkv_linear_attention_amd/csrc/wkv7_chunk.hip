@@ -284,14 +284,27 @@ __global__ __launch_bounds__((kN / J / 16 + nprod<Tin>()) * 64) void wkv7_chunk_
     if (lid >= nblocks)
         return;
     const int bh = lid / J, jb = lid - bh * J;
-    const int H = p.H, T = p.T;
+    const int H = p.H, T = p.T;  // T: the row stride of the [B, T, H, N] tensors
     const int bb = bh / H, hh = bh - bb * H;
     const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, m = lane & 15;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int j0 = jb * NC;
     const size_t head0 = (static_cast<size_t>(bb) * T * H + hh) * kN;   // (b, t=0, h, 0)
     const size_t sbase = static_cast<size_t>(bh) * (kN * kN);
-    const int nchunks = (T + CH - 1) / CH;
+    // tokens of this row: all T, or its own length (clamped to [0, T])
+    const int L = p.lengths ? min(max(p.lengths[bb], 0), T) : T;
+    if (L == 0) {
+        // an empty row: the state passes through (zeros without state_in)
+        for (int e = 4 * tid; e < kN * (kN / J); e += 4 * static_cast<int>(blockDim.x)) {
+            const int i = e / (kN / J), jj = j0 + e % (kN / J);  // this workgroup's columns of row i
+            f32x4 x = {0.f, 0.f, 0.f, 0.f};
+            if (HAS_STATE_IN)
+                x = *reinterpret_cast<const f32x4 *>(&p.state_in[sbase + i * kN + jj]);
+            *reinterpret_cast<f32x4 *>(&p.state_out[sbase + i * kN + jj]) = x;
+        }
+        return;
+    }
+    const int nchunks = (L + CH - 1) / CH;
     // element offset of token t in this (batch, head)'s rows: one 32x32->64 multiply-add
     const uint32_t rs32 = static_cast<uint32_t>(H) * kN;
     auto row_of = [&](int t) { return head0 + static_cast<uint64_t>(static_cast<uint32_t>(t)) * rs32; };
@@ -456,14 +469,14 @@ __global__ __launch_bounds__((kN / J / 16 + nprod<Tin>()) * 64) void wkv7_chunk_
                 {
                     // one uniform base per chunk, per-lane 32-bit offsets
                     Tout *const ob = go + row_of(t0) + jw;
-                    if (t0 + CH <= T) {
+                    if (t0 + CH <= L) {
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
                             store_o(ob, ooff[e], (o2[0][e] + o2[1][e]) + o3[e]);
                     } else {
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
-                            if (t0 + 4 * q + e < T)
+                            if (t0 + 4 * q + e < L)
                                 store_o(ob, ooff[e], (o2[0][e] + o2[1][e]) + o3[e]);
                     }
                 }
@@ -505,7 +518,7 @@ __global__ __launch_bounds__((kN / J / 16 + nprod<Tin>()) * 64) void wkv7_chunk_
     // R_T / R_T1 and R_D / R_D1 take the even and the odd chunks
     const int role = DEEP ? static_cast<int>((0x2154396780ull >> (4 * (wv - NSW))) & 15)
                           : (0x25316470 >> (4 * (wv - NSW))) & 15;  // T SK SA SB MA D SR MR
-    const int t_end = T;
+    const int t_end = L;
 
     using F = std::integral_constant<bool, false>;
     using U = std::integral_constant<bool, true>;

@@ -12,6 +12,7 @@ struct SeqArgs {
     void *o;                            // [B,T,H,64], o_dtype
     float *state_out;                   // [B,H,64,64]
     float *state_pos;                   // [B,T,H,64,64] or nullptr
+    const int *lengths;                 // [B] tokens of each row (clamped to [0, T]), or nullptr: all T
     int B, T, H;
     int in_bf16, o_bf16;                // dtype flags
 };
@@ -21,5 +22,7 @@ hipError_t launch_chunk(const SeqArgs &a, hipStream_t stream);
 hipError_t launch_state_copy(const float *src, float *dst, long long n_floats, hipStream_t stream);
 hipError_t launch_state_reset(float *state, int B, int H, const unsigned char *row_mask,
                               hipStream_t stream);
+hipError_t launch_state_commit(const float *state_pos, const int *accepted, const float *state_in,
+                               float *state_out, int B, int T, int H, hipStream_t stream);
 
 }  // namespace wkv7

@@ -59,11 +59,13 @@ __device__ __forceinline__ void load_rows(const float *__restrict__ p, float (&x
 // stage blocks of TB tokens, widened to fp32, in LDS with one cooperative
 // load, so no global latency sits inside the token loop.  The arithmetic is
 // the same code either way.
-template <typename Tin, typename Tout, bool HAS_STATE_IN, bool WRITE_POS, bool STAGED, int NW>
+// With VARLEN, row b runs its first lengths[b] tokens only (clamped to [0, T]);
+// T stays the row stride of the [B, T, H, N] tensors.
+template <typename Tin, typename Tout, bool HAS_STATE_IN, bool WRITE_POS, bool STAGED, int NW, bool VARLEN>
 __global__ __launch_bounds__(NW * 64) void wkv7_step_kernel(
     const Tin *__restrict__ r, const Tin *__restrict__ w, const Tin *__restrict__ k, const Tin *__restrict__ v,
     const Tin *__restrict__ a, const Tin *__restrict__ b, const float *state_in, Tout *__restrict__ o,
-    float *state_out, float *__restrict__ state_pos, int T, int H)
+    float *state_out, float *__restrict__ state_pos, int T, int H, const int *__restrict__ lengths)
 {
     constexpr int RW = kN / NW;                                       // key rows per wave
     const int j = threadIdx.x & 63;                                   // value column of this lane
@@ -71,6 +73,7 @@ __global__ __launch_bounds__(NW * 64) void wkv7_step_kernel(
     const int i0 = g * RW;
     const int bh = blockIdx.x;                                        // (batch, head) pair
     const int bb = bh / H, hh = bh - bb * H;
+    const int L = VARLEN ? min(max(lengths[bb], 0), T) : T;  // tokens of this row
     __shared__ float part_a[2][NW][kN];  // a^T S partial sums, alternating between tokens
     __shared__ float part_r[NW][kN];     // r^T S partial sums
     __shared__ alignas(16) float xin[STAGED ? TB : 1][6][kN];  // staged a, w, b, k, r, v
@@ -89,7 +92,7 @@ __global__ __launch_bounds__(NW * 64) void wkv7_step_kernel(
         }
     };
     if constexpr (STAGED)
-        stage_load(0, min(TB, T));  // issued before the state loads: waiting for it skips them
+        stage_load(0, max(min(TB, L), 1));  // issued before the state loads: waiting for it skips them
 
     const size_t sbase = static_cast<size_t>(bh) * (kN * kN) + static_cast<size_t>(i0) * kN + j;
     float S[RW];
@@ -98,8 +101,8 @@ __global__ __launch_bounds__(NW * 64) void wkv7_step_kernel(
         S[u] = HAS_STATE_IN ? __builtin_nontemporal_load(state_in + sbase + u * kN) : 0.0f;
 
     constexpr int BLK = STAGED ? TB : 1;
-    for (int t0 = 0; t0 < T; t0 += BLK) {
-        const int nt = min(BLK, T - t0);
+    for (int t0 = 0; t0 < L; t0 += BLK) {
+        const int nt = min(BLK, L - t0);
         if constexpr (STAGED) {
             if (t0 > 0) {
                 __syncthreads();  // the previous block's inputs are no longer read
@@ -192,17 +195,21 @@ hipError_t launch_mode(const SeqArgs &p, hipStream_t stream)
     const Tin *a = static_cast<const Tin *>(p.a), *b = static_cast<const Tin *>(p.b);
     Tout *o = static_cast<Tout *>(p.o);
     const bool sin = p.state_in != nullptr, pos = p.state_pos != nullptr;
-#define WKV7_STEP_LAUNCH(SIN, POS)                                                                                \
-    hipLaunchKernelGGL((wkv7_step_kernel<Tin, Tout, SIN, POS, STAGED, NW>), grid, block, 0, stream, r, w, k, v, a, b, \
-                       p.state_in, o, p.state_out, p.state_pos, p.T, p.H)
-    if (sin && pos)
-        WKV7_STEP_LAUNCH(true, true);
+#define WKV7_STEP_LAUNCH(SIN, POS, VL)                                                                      \
+    hipLaunchKernelGGL((wkv7_step_kernel<Tin, Tout, SIN, POS, STAGED, NW, VL>), grid, block, 0, stream, r, w, k, v, \
+                       a, b, p.state_in, o, p.state_out, p.state_pos, p.T, p.H, p.lengths)
+    if (p.lengths && sin)  // rows of their own lengths (the forward pass, no per-position states)
+        WKV7_STEP_LAUNCH(true, false, true);
+    else if (p.lengths)
+        WKV7_STEP_LAUNCH(false, false, true);
+    else if (sin && pos)
+        WKV7_STEP_LAUNCH(true, true, false);
     else if (sin)
-        WKV7_STEP_LAUNCH(true, false);
+        WKV7_STEP_LAUNCH(true, false, false);
     else if (pos)
-        WKV7_STEP_LAUNCH(false, true);
+        WKV7_STEP_LAUNCH(false, true, false);
     else
-        WKV7_STEP_LAUNCH(false, false);
+        WKV7_STEP_LAUNCH(false, false, false);
 #undef WKV7_STEP_LAUNCH
     return hipGetLastError();
 }
@@ -232,6 +239,30 @@ __global__ __launch_bounds__(256) void state_reset_kernel(float4 *state, const u
     }
 }
 
+// Commit of a speculative step: per (batch row b, head), with n = accepted[b],
+// the state after the first n tokens (state_pos[b, n-1]; state_in[b] for n = 0,
+// zeros when state_in is null); rows with n outside [0, T] keep state_out.
+__global__ __launch_bounds__(256) void state_commit_kernel(const float4 *state_pos, const int *accepted,
+                                                           const float4 *state_in, float4 *state_out, int T,
+                                                           int H)
+{
+    constexpr int PER = kN * kN / 4;  // float4 per head
+    const int bh = blockIdx.x, bb = bh / H, hh = bh - bb * H;
+    const int n = accepted[bb];
+    if (n < 0 || n > T)
+        return;
+    float4 *dst = state_out + static_cast<size_t>(bh) * PER;
+    const float4 *src = nullptr;
+    if (n > 0)
+        src = state_pos + ((static_cast<size_t>(bb) * T + (n - 1)) * H + hh) * PER;
+    else if (state_in)
+        src = state_in + static_cast<size_t>(bh) * PER;
+    if (src == dst)
+        return;
+    for (int i = threadIdx.x; i < PER; i += 256)
+        dst[i] = src ? src[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
 unsigned grid_for(long long n4)
 {
     long long blocks = (n4 + 255) / 256;
@@ -252,6 +283,15 @@ hipError_t launch_state_copy(const float *src, float *dst, long long n_floats, h
     const long long n4 = n_floats / 4;
     hipLaunchKernelGGL(state_copy_kernel, dim3(grid_for(n4)), dim3(256), 0, stream,
                        reinterpret_cast<const float4 *>(src), reinterpret_cast<float4 *>(dst), n4);
+    return hipGetLastError();
+}
+
+hipError_t launch_state_commit(const float *state_pos, const int *accepted, const float *state_in,
+                               float *state_out, int B, int T, int H, hipStream_t stream)
+{
+    hipLaunchKernelGGL(state_commit_kernel, dim3(static_cast<unsigned>(B) * static_cast<unsigned>(H)), dim3(256), 0,
+                       stream, reinterpret_cast<const float4 *>(state_pos), accepted,
+                       reinterpret_cast<const float4 *>(state_in), reinterpret_cast<float4 *>(state_out), T, H);
     return hipGetLastError();
 }
 

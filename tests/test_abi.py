@@ -30,8 +30,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    assert names == sorted(["wkv7_forward", "wkv7_step", "wkv7_state_reset", "wkv7_status_string",
-                            "wkv7_abi_version"])
+    assert names == sorted(["wkv7_forward", "wkv7_forward_varlen", "wkv7_step", "wkv7_state_commit",
+                            "wkv7_state_reset", "wkv7_status_string", "wkv7_abi_version"])
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -137,3 +137,43 @@ def test_errors_come_before_any_launch(L):
     p = [None] * 6
     st = L.wkv7_forward(*p, BF16, None, None, F32, None, 1, 4, 1, 64, None)
     assert st == ERR_NULL
+
+
+def varlen(L, B=2, T=8, H=3, N=64, lengths="fake", o=None, sout=None):
+    p = [fake(i) for i in range(6)]
+    ln = fake(10) if lengths == "fake" else lengths
+    return L.wkv7_forward_varlen(*p, BF16, fake(7), fake(6) if o is None else o, F32,
+                                 fake(8) if sout is None else sout, ln, B, T, H, N, None)
+
+
+def commit(L, B=2, T=5, H=3, N=64, pos="fake", acc="fake", sin="fake", sout="fake"):
+    pick = lambda x, d: d if x == "fake" else x
+    return L.wkv7_state_commit(pick(pos, fake(9)), pick(acc, fake(10)), pick(sin, fake(7)),
+                               pick(sout, fake(8)), B, T, H, N, None)
+
+
+def test_varlen_validation(L):
+    # the checks of wkv7_forward apply unchanged
+    assert varlen(L, N=32) == ERR_UNSUPPORTED
+    assert varlen(L, B=0) == ERR_SHAPE
+    # the lengths array: required, 4-byte aligned, not inside an output
+    assert varlen(L, lengths=None) == ERR_NULL
+    assert varlen(L, lengths=fake(10, 2)) == ERR_ALIGN
+    assert varlen(L, lengths=fake(6, 8)) == ERR_ALIAS        # inside o
+    assert varlen(L, lengths=fake(8, 64)) == ERR_ALIAS       # inside state_out
+
+
+def test_commit_validation(L):
+    assert commit(L, N=128) == ERR_UNSUPPORTED
+    assert commit(L, B=0) == ERR_SHAPE
+    assert commit(L, T=-1) == ERR_SHAPE
+    assert commit(L, acc=None) == ERR_NULL
+    assert commit(L, sout=None) == ERR_NULL
+    assert commit(L, pos=None) == ERR_NULL                   # T > 0 needs the per-position states
+    assert commit(L, acc=fake(10, 2)) == ERR_ALIGN
+    assert commit(L, pos=fake(9, 8)) == ERR_ALIGN
+    assert commit(L, sout=fake(8, 4)) == ERR_ALIGN
+    assert commit(L, sin=fake(7, 8)) == ERR_ALIGN
+    assert commit(L, sout=fake(9, 4096)) == ERR_ALIAS        # state_out inside state_pos
+    assert commit(L, acc=fake(8, 16)) == ERR_ALIAS           # accepted inside state_out
+    assert commit(L, sin=fake(8, 256)) == ERR_ALIAS          # partial overlap with state_in

@@ -1,0 +1,87 @@
+"""GPU parity of the serving-path entry points against the fp64 oracle:
+right-padded rows of their own lengths (wkv7_forward_varlen) and the commit of
+a speculative verify step (wkv7_state_commit)."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from test_gpu_parity import K, TOL, check, to_dev  # noqa: F401  (K is a fixture)
+
+pytestmark = pytest.mark.gpu
+
+NAMES = ("r", "w", "k", "v", "a", "b")
+
+
+def _lengths(B, T):
+    base = [0, 1, T // 2 + 1, T, T + 7, 3, max(T - 1, 0), T // 3]
+    return [base[i % len(base)] for i in range(B)]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("B,T,H", [(3, 1, 2), (5, 6, 3), (5, 40, 3), (4, 40, 64), (3, 100, 50)])
+def test_forward_varlen(K, oracle_mod, dtype, B, T, H):
+    # T < 9 runs the step kernel, longer T the chunked one (J = 4, 1 and 2 column blocks)
+    inp = synth.make_inputs(B, T, H, 64, seed=5000 + 7 * T + H, dtype=dtype, state_std=0.1)
+    lengths = _lengths(B, T)
+    print(f"  varlen {dtype} B={B} T={T} H={H} lengths={lengths}", flush=True)
+    d = to_dev(inp)
+    sentinel = 1234.5
+    o = torch.full((B, T, H, 64), sentinel, device="cuda")
+    o, s = K.wkv7_forward(*[d[n] for n in NAMES], d["state_in"], o=o, lengths=lengths)
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle_mod.forward_varlen(*[inp[n] for n in NAMES], inp["state_in"], lengths)
+    L = np.clip(np.asarray(lengths), 0, T)
+    valid = np.arange(T)[None, :] < L[:, None]                       # [B, T]
+    og = o.double().cpu().numpy()
+    if valid.any():
+        check(og[valid], o_ref[valid], TOL[dtype], "o (valid tokens)")
+    assert (og[~valid] == sentinel).all(), "o past a row's length must be left untouched"
+    check(s, s_ref, TOL[dtype], "state_out")
+    for bb in np.nonzero(L == 0)[0]:
+        assert torch.equal(s[bb], d["state_in"][bb]), "an empty row passes its state through"
+
+
+def test_forward_varlen_full_lengths_equal_forward(K):
+    # lengths of T on every row: the same kernels, the same results, bit for bit
+    inp = synth.make_inputs(3, 50, 5, 64, seed=77, dtype="bf16", state_std=0.1)
+    d = to_dev(inp)
+    args = [d[n] for n in NAMES]
+    o1, s1 = K.wkv7_forward(*args, d["state_in"])
+    o2, s2 = K.wkv7_forward(*args, d["state_in"], lengths=[50, 50, 50])
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+
+
+def test_state_commit(K, oracle_mod):
+    B, T, H = 7, 5, 3
+    inp = synth.make_inputs(B, T, H, 64, seed=61, dtype="bf16", state_std=0.1)
+    d = to_dev(inp)
+    _, _, sp = K.wkv7_step(*[d[n] for n in NAMES], d["state_in"], per_position=True)
+    accepted = [0, 1, 2, 4, 5, 6, -1]
+    before = torch.full((B, H, 64, 64), 3.5, device="cuda")
+    got = K.wkv7_state_commit(sp, accepted, d["state_in"], state_out=before.clone())
+    torch.cuda.synchronize()
+    # a copy: bit-exact against the step's own per-position states
+    for bb, n in enumerate(accepted):
+        if 1 <= n <= T:
+            assert torch.equal(got[bb], sp[bb, n - 1])
+        elif n == 0:
+            assert torch.equal(got[bb], d["state_in"][bb])
+        else:
+            assert torch.equal(got[bb], before[bb])
+    # and against the oracle's commit of its own per-position states
+    _, _, sp_ref = oracle_mod.forward(*[inp[n] for n in NAMES], inp["state_in"], per_position=True)
+    ref = oracle_mod.state_commit(sp_ref, accepted, inp["state_in"], before.cpu())
+    check(got, ref, TOL["bf16"], "committed state")
+    # in place over the state the step started from
+    st = d["state_in"].clone()
+    K.wkv7_state_commit(sp, accepted, st, state_out=st)
+    torch.cuda.synchronize()
+    for bb, n in enumerate(accepted):
+        expect = sp[bb, n - 1] if 1 <= n <= T else d["state_in"][bb]
+        assert torch.equal(st[bb], expect)
+    # no state_in: an accepted count of 0 gives the zero state
+    z = K.wkv7_state_commit(sp, [0] * B)
+    torch.cuda.synchronize()
+    assert not torch.any(z)

@@ -303,3 +303,47 @@ def test_every_input_matters(oracle_mod, which):
     o2, s2 = _one_head(oracle_mod, **args)
     changed = not np.array_equal(o, o2) or not np.array_equal(s, s2)
     assert changed
+
+
+def test_varlen_rows_match_the_full_run(oracle_mod):
+    # Each row of the variable-length pass against a different route: one run
+    # over the whole padded sequence with per-position states.  By causality the
+    # first L_b outputs agree and the state after L_b tokens is state_pos[b, L_b-1];
+    # the same fp64 loop in the same order makes both bit-equal.
+    import synth
+    T = 23
+    inp = synth.make_inputs(6, T, 2, seed=41, dtype="f32")
+    lengths = [0, 1, 9, T, T + 5, -3]
+    args = [inp[n] for n in ("r", "w", "k", "v", "a", "b")]
+    o_full, _, s_pos = oracle_mod.forward(*args, inp["state_in"], per_position=True)
+    o, s = oracle_mod.forward_varlen(*args, inp["state_in"], lengths)
+    s_in = inp["state_in"].double().numpy()
+    for bb, L in enumerate(lengths):
+        L = min(max(L, 0), T)
+        assert np.array_equal(o[bb, :L], o_full[bb, :L])
+        assert np.isnan(o[bb, L:]).all()
+        expect = s_in[bb] if L == 0 else s_pos[bb, L - 1]
+        assert np.array_equal(s[bb], expect)
+
+
+def test_state_commit_matches_prefix_runs(oracle_mod):
+    # The commit against a different route: a separate run over the accepted
+    # prefix of each row (bit-equal: the same loop in the same order).
+    import synth
+    T = 6
+    inp = synth.make_inputs(7, T, 3, seed=43, dtype="f32")
+    args = [inp[n] for n in ("r", "w", "k", "v", "a", "b")]
+    _, _, s_pos = oracle_mod.forward(*args, inp["state_in"], per_position=True)
+    accepted = [0, 1, 2, 5, T, T + 1, -1]
+    before = np.full((7, 3, 64, 64), 7.25)
+    got = oracle_mod.state_commit(s_pos, accepted, inp["state_in"], before)
+    s_in = inp["state_in"].double().numpy()
+    for bb, n in enumerate(accepted):
+        if 1 <= n <= T:
+            rows = [x[bb:bb + 1, :n] for x in args]
+            _, s_ref = oracle_mod.forward(*rows, inp["state_in"][bb:bb + 1])
+            assert np.array_equal(got[bb], s_ref[0])
+        elif n == 0:
+            assert np.array_equal(got[bb], s_in[bb])
+        else:
+            assert np.array_equal(got[bb], before[bb])
