@@ -38,12 +38,12 @@ PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "rwkv_linear_attention_amd", "csrc")
 
 
-def algorithmic_bytes(wl, kind: str) -> int:
-    """Bytes the method must move per call: inputs once, o once (fp32), state read and written once,
-    plus per-position states for the verify step."""
+def algorithmic_bytes(wl, kind: str, o_bytes: int = 4) -> int:
+    """Bytes the method must move per call: inputs once, o once (fp32 unless o_bytes says
+    otherwise), state read and written once, plus per-position states for the verify step."""
     e_in = 2 if wl.dtype == "bf16" else 4
     tokheads = wl.B * wl.T * wl.H
-    b = tokheads * (6 * N * e_in + 4 * N)
+    b = tokheads * (6 * N * e_in + o_bytes * N)
     b += 2 * wl.B * wl.H * N * N * 4 if (wl.state_std > 0 or kind == "step") else wl.B * wl.H * N * N * 4
     if kind == "verify":
         b += tokheads * N * N * 4
@@ -163,11 +163,11 @@ def time_step_workload(K, synth, idx: int, steps: int, warmup: int):
             "layers": wl.layers}
 
 
-def time_prefill_workload(K, synth, idx: int, steps: int, warmup: int):
+def time_prefill_workload(K, synth, idx: int, steps: int, warmup: int, o_bf16: bool = False):
     import torch
     wl = synth.WORKLOADS[idx]
     d = synth.workload_inputs(idx, device="cuda")
-    o = torch.empty((wl.B, wl.T, wl.H, N), dtype=torch.float32, device="cuda")
+    o = torch.empty((wl.B, wl.T, wl.H, N), dtype=torch.bfloat16 if o_bf16 else torch.float32, device="cuda")
     s_out = torch.empty((wl.B, wl.H, N, N), dtype=torch.float32, device="cuda")
     args = [d[n] for n in ("r", "w", "k", "v", "a", "b")]
     stream = torch.cuda.Stream()
@@ -344,6 +344,14 @@ def main():
                 entry["alg_flops_frac_bf16"] = round(recurrent_flops(wj) / tj["sec_per_launch"] / 1e12
                                                      / PEAK_BF16_TFLOPS, 5)
             others[str(j)] = entry
+        # the prefill of workload 3 with a bf16 o (the ABI's o_dtype option): 896 instead of
+        # 1024 algorithmic bytes per token-head; its HBM counters are not taken (traffic null)
+        w3 = synth.WORKLOADS[3]
+        tb = time_prefill_workload(K, synth, 3, max(20, args.steps), args.warmup, o_bf16=True)
+        rb = roofline(algorithmic_bytes(w3, "chunk", o_bytes=2), tb["sec_per_launch"], "chunk", 3)
+        rb["traffic"] = None
+        others["3-bf16o"] = {"workload": w3.name + " (bf16 o)", "ms_per_call": round(tb["sec_per_launch"] * 1e3, 4),
+                             "roofline": rb, "mtok_s": round(tb["mtok_s"], 2)}
         line["other_workloads"] = others
     print(json.dumps(line), flush=True)
 

@@ -85,3 +85,21 @@ def test_state_commit(K, oracle_mod):
     z = K.wkv7_state_commit(sp, [0] * B)
     torch.cuda.synchronize()
     assert not torch.any(z)
+
+
+def test_bf16_output_accuracy_workload3(K, oracle_mod):
+    # The cost of a bf16 o (the o_dtype option) on the prefill workload, measured on
+    # sampled heads over the full sequence; it stays inside the bf16-input tolerance.
+    inp = synth.workload_inputs(3)
+    d = to_dev(inp)
+    o16, _ = K.wkv7_forward(*[d[n] for n in NAMES], d["state_in"], o_dtype=torch.bfloat16)
+    o32, _ = K.wkv7_forward(*[d[n] for n in NAMES], d["state_in"])
+    torch.cuda.synchronize()
+    o16, o32 = o16.float().cpu(), o32.cpu()
+    del d
+    for (bb, hh) in [(0, 5), (3, 60)]:
+        sub = {n: x[bb:bb + 1, :, hh:hh + 1].contiguous() for n, x in inp.items() if n != "state_in"}
+        sub["state_in"] = inp["state_in"][bb:bb + 1, hh:hh + 1].contiguous()
+        o_ref, _ = oracle_mod.forward(*[sub[n] for n in NAMES], sub["state_in"])
+        check(o32[bb:bb + 1, :, hh:hh + 1], o_ref, TOL["bf16"], f"workload 3 (b={bb}, h={hh}) o fp32")
+        check(o16[bb:bb + 1, :, hh:hh + 1], o_ref, TOL["bf16"], f"workload 3 (b={bb}, h={hh}) o bf16")
