@@ -408,25 +408,28 @@ __global__ __launch_bounds__((kN / J / 16 + nprod<Tin>()) * 64) void wkv7_chunk_
                 }
                 // A'-rows and R'-rows as A operands with the same key slots (stored
                 // contiguously, see key_slot); one accumulator per k-step.
-                f32x4 y2[2], o2[2];
+                // Y = A' S^ + M_ak V in accumulator layout (Y[4 q + e][col m]), one
+                // accumulator per k-step and one for M_ak V (a 16x16x16 product never
+                // accumulates onto a 16x16x32 one: the compiler inserts no wait states
+                // between the two shapes); R' S^ in one accumulator that the
+                // [M_rb | M_rk] product (the same shape) later continues
+                f32x4 y2[2], oacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int s = 0; s < 2; ++s) {
                     y2[s] = f32x4{0.f, 0.f, 0.f, 0.f};
-                    o2[s] = f32x4{0.f, 0.f, 0.f, 0.f};
                     mma32<NP, NP>(y2[s], pA[s], Bs[s]);
                 }
 #pragma unroll
                 for (int s = 0; s < 2; ++s)
-                    mma32<NP, NP>(o2[s], Rf[s], Bs[s]);
+                    mma32<NP, NP>(oacc, Rf[s], Bs[s]);
                 // V rows as a B operand over the token index (slot (q, e) = token 4 q + e)
                 s16x4 Vf[NPV];
 #pragma unroll
                 for (int pl = 0; pl < NPV; ++pl)
                     Vf[pl] = pV[pl];
-                // M_ak V
                 f32x4 ym = {0.f, 0.f, 0.f, 0.f};
                 mma16<NP, NPV>(ym, Mak, Vf);
-                // Z = T Y  (Y = A' S^ + M_ak V in accumulator layout: Y[4 q + e][col m])
+                // Z = T Y
                 f32x4 z = {0.f, 0.f, 0.f, 0.f};
                 {
                     f32x4 y4;
@@ -458,13 +461,12 @@ __global__ __launch_bounds__((kN / J / 16 + nprod<Tin>()) * 64) void wkv7_chunk_
                         ZV[pl] = cat(Zf[pl], pl < NPV ? Vf[pl < NPV ? pl : 0] : s16x4{0, 0, 0, 0});
                 }
                 // o = R' S^ + [M_rb | M_rk] [Z ; V]
-                f32x4 o3 = {0.f, 0.f, 0.f, 0.f};
                 {
                     s16x8 Mf[NP];
 #pragma unroll
                     for (int pl = 0; pl < NP; ++pl)
                         Mf[pl] = cat(tr4(&sl.Mt[MT_RB][pl][trow][mcol_t]), tr4(&sl.Mt[MT_RK][pl][trow][mcol_t]));
-                    mma32<NP, NP>(o3, Mf, ZV);
+                    mma32<NP, NP>(oacc, Mf, ZV);
                 }
                 {
                     // one uniform base per chunk, per-lane 32-bit offsets
@@ -472,12 +474,12 @@ __global__ __launch_bounds__((kN / J / 16 + nprod<Tin>()) * 64) void wkv7_chunk_
                     if (t0 + CH <= L) {
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
-                            store_o(ob, ooff[e], (o2[0][e] + o2[1][e]) + o3[e]);
+                            store_o(ob, ooff[e], oacc[e]);
                     } else {
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
                             if (t0 + 4 * q + e < L)
-                                store_o(ob, ooff[e], (o2[0][e] + o2[1][e]) + o3[e]);
+                                store_o(ob, ooff[e], oacc[e]);
                     }
                 }
                 // S^ <- diag(f) (S^ + [B'^T | K'^T] [Z ; V]), one 16-row tile at a time;
