@@ -408,17 +408,15 @@ __global__ __launch_bounds__((kN / J / 16 + nprod<Tin>()) * 64) void wkv7_chunk_
                 }
                 // A'-rows and R'-rows as A operands with the same key slots (stored
                 // contiguously, see key_slot); one accumulator per k-step.
-                // Y = A' S^ + M_ak V in accumulator layout (Y[4 q + e][col m]), one
-                // accumulator per k-step and one for M_ak V (a 16x16x16 product never
-                // accumulates onto a 16x16x32 one: the compiler inserts no wait states
-                // between the two shapes); R' S^ in one accumulator that the
+                // Y = A' S^ + M_ak V in accumulator layout (Y[4 q + e][col m]): A' S^ in
+                // one accumulator over both k-steps and M_ak V in another (a 16x16x16
+                // product never accumulates onto a 16x16x32 one: the compiler inserts no
+                // wait states between the two shapes); R' S^ in one accumulator that the
                 // [M_rb | M_rk] product (the same shape) later continues
-                f32x4 y2[2], oacc = {0.f, 0.f, 0.f, 0.f};
+                f32x4 ya = {0.f, 0.f, 0.f, 0.f}, oacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int s = 0; s < 2; ++s) {
-                    y2[s] = f32x4{0.f, 0.f, 0.f, 0.f};
-                    mma32<NP, NP>(y2[s], pA[s], Bs[s]);
-                }
+                for (int s = 0; s < 2; ++s)
+                    mma32<NP, NP>(ya, pA[s], Bs[s]);
 #pragma unroll
                 for (int s = 0; s < 2; ++s)
                     mma32<NP, NP>(oacc, Rf[s], Bs[s]);
@@ -435,7 +433,7 @@ __global__ __launch_bounds__((kN / J / 16 + nprod<Tin>()) * 64) void wkv7_chunk_
                     f32x4 y4;
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        y4[e] = (y2[0][e] + y2[1][e]) + ym[e];
+                        y4[e] = ya[e] + ym[e];
                     s16x4 Yf[NP];
                     split4<NP>(y4, Yf);
                     mma16<NP, NP>(z, Tf, Yf);
