@@ -105,8 +105,19 @@ def warm(fn, steps: int):
             torch.cuda.synchronize()
     torch.cuda.synchronize()
 
-def make_layers(K, synth, idx: int, nlayers: int):
-    """nlayers distinct buffer sets of workload idx on the GPU (inputs, state, outputs)."""
+def tail_params(H: int, seed: int):
+    """Per-head parameters of the time-mix tail (random, fp32 [H, N]) on the GPU."""
+    import torch
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    r_k = torch.randn((H, N), generator=g, device="cuda") * 0.1
+    ln_w = 1 + 0.1 * torch.randn((H, N), generator=g, device="cuda")
+    ln_b = 0.1 * torch.randn((H, N), generator=g, device="cuda")
+    return r_k, ln_w, ln_b
+
+
+def make_layers(K, synth, idx: int, nlayers: int, tail=False):
+    """nlayers distinct buffer sets of workload idx on the GPU (inputs, state, outputs; with tail,
+    also a gate and the tail's per-head parameters)."""
     import torch
     wl = synth.WORKLOADS[idx]
     sets = []
@@ -116,21 +127,36 @@ def make_layers(K, synth, idx: int, nlayers: int):
         d["state"] = inp["state_in"].cuda()
         d["o"] = torch.empty((wl.B, wl.T, wl.H, N), dtype=torch.float32, device="cuda")
         d["pos"] = torch.empty((wl.B, wl.T, wl.H, N, N), dtype=torch.float32, device="cuda") if idx == 4 else None
+        if tail:  # "fused" (the tail in the step's epilogue) or "separate" (a second launch)
+            gen = torch.Generator(device="cuda").manual_seed(77 + l)
+            d["g"] = torch.sigmoid(torch.randn(d["r"].shape, generator=gen, device="cuda")).to(d["r"].dtype)
+            d["tail"] = tail_params(wl.H, 78 + l)
+            d["mode"] = tail
+            if tail == "separate":
+                d["x"] = torch.empty_like(d["o"])
         sets.append(d)
     return sets
 
 
 def sweep(K, sets):
     for d in sets:
-        K.wkv7_step(d["r"], d["w"], d["k"], d["v"], d["a"], d["b"], d["state"], o=d["o"], state_out=d["state"],
-                    state_pos=d["pos"])
+        if d.get("mode") == "fused":
+            K.wkv7_step_tail(d["r"], d["w"], d["k"], d["v"], d["a"], d["b"], d["g"], *d["tail"], 64e-5,
+                             d["state"], x=d["o"], state_out=d["state"], state_pos=d["pos"])
+        elif d.get("mode") == "separate":
+            K.wkv7_step(d["r"], d["w"], d["k"], d["v"], d["a"], d["b"], d["state"], o=d["o"],
+                        state_out=d["state"], state_pos=d["pos"])
+            K.wkv7_tmix_tail(d["o"], d["r"], d["k"], d["v"], d["g"], *d["tail"], 64e-5, x=d["x"])
+        else:
+            K.wkv7_step(d["r"], d["w"], d["k"], d["v"], d["a"], d["b"], d["state"], o=d["o"],
+                        state_out=d["state"], state_pos=d["pos"])
 
 
-def time_step_workload(K, synth, idx: int, steps: int, warmup: int):
+def time_step_workload(K, synth, idx: int, steps: int, warmup: int, tail=False):
     """Graph-captured sweeps over the layer sets; returns dict of timings."""
     import torch
     wl = synth.WORKLOADS[idx]
-    sets = make_layers(K, synth, idx, wl.layers)
+    sets = make_layers(K, synth, idx, wl.layers, tail)
     stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):
         sweep(K, sets)                      # eager warm-up (loads the code objects)
@@ -181,6 +207,30 @@ def time_prefill_workload(K, synth, idx: int, steps: int, warmup: int, o_bf16: b
         e1.synchronize()
     ms = e0.elapsed_time(e1) / steps
     return {"ms_per_step": ms, "sec_per_launch": ms / 1e3, "mtok_s": wl.B * wl.T / (ms / 1e3) / 1e6}
+
+
+def time_tail_pass(K, synth, idx: int, steps: int, warmup: int):
+    """The time-mix tail as a pass of its own over the outputs of prefill workload idx."""
+    import torch
+    wl = synth.WORKLOADS[idx]
+    d = synth.workload_inputs(idx, device="cuda")
+    o, _ = K.wkv7_forward(*[d[n] for n in ("r", "w", "k", "v", "a", "b")], d["state_in"])
+    gen = torch.Generator(device="cuda").manual_seed(79)
+    g = torch.sigmoid(torch.randn(d["r"].shape, generator=gen, device="cuda")).to(d["r"].dtype)
+    prm = tail_params(wl.H, 80)
+    x = torch.empty_like(o)
+    stream = torch.cuda.Stream()
+    run = lambda: K.wkv7_tmix_tail(o, d["r"], d["k"], d["v"], g, *prm, 64e-5, x=x)
+    with torch.cuda.stream(stream):
+        warm(run, warmup)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            run()
+        e1.record(stream)
+        e1.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    return {"sec_per_launch": ms / 1e3}
 
 
 def copy_ceiling(idx: int, steps: int, warmup: int):
@@ -352,6 +402,23 @@ def main():
         rb["traffic"] = None
         others["3-bf16o"] = {"workload": w3.name + " (bf16 o)", "ms_per_call": round(tb["sec_per_launch"] * 1e3, 4),
                              "roofline": rb, "mtok_s": round(tb["mtok_s"], 2)}
+        # the time-mix tail: fused into the decode step (workload 1), and as a pass of its own
+        # over the prefill outputs of workload 3 (fp32 o and x, bf16 r, k, v, g); no HBM counters
+        w1 = synth.WORKLOADS[1]
+        tt = time_step_workload(K, synth, 1, args.steps, args.warmup, tail="fused")
+        ts = time_step_workload(K, synth, 1, args.steps, args.warmup, tail="separate")
+        b_tail = algorithmic_bytes(w1, "step") + w1.B * w1.T * w1.H * N * 2 + 3 * w1.H * N * 4
+        rt = roofline(b_tail, tt["sec_per_launch"], "step", 1)
+        rt["traffic"] = None
+        others["1-tail"] = {"workload": w1.name + " (fused time-mix tail)", "us_per_layer": round(tt["us_per_layer"], 3),
+                            "roofline": rt,
+                            "us_per_layer_step_then_tail_pass": round(ts["us_per_layer"], 3)}
+        tp = time_tail_pass(K, synth, 3, max(20, args.steps), args.warmup)
+        b_pass = w3.B * w3.T * w3.H * N * (4 + 4 * 2 + 4) + 3 * w3.H * N * 4
+        rp = roofline(b_pass, tp["sec_per_launch"], "chunk", 3)
+        rp["traffic"] = None
+        others["3-tail-pass"] = {"workload": w3.name + " (time-mix tail pass)",
+                                 "ms_per_call": round(tp["sec_per_launch"] * 1e3, 4), "roofline": rp}
         line["other_workloads"] = others
     print(json.dumps(line), flush=True)
 

@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define WKV7_ABI_VERSION 2
+#define WKV7_ABI_VERSION 3
 
 /* Element types of r, w, k, v, a, b (in_dtype) and of o (o_dtype). */
 enum wkv7_dtype {
@@ -146,6 +146,49 @@ int wkv7_step(const void *r, const void *w, const void *k, const void *v,
  */
 int wkv7_state_reset(float *state, int B, int H, int N, const unsigned char *row_mask,
                      void *stream);
+
+/*
+ * THE TIME-MIX TAIL.  The SwiftRWKV Inference guide (its decode-path list and
+ * the fused frozen pass) fuses the three steps that follow WKV in an RWKV-7
+ * block -- group norm, bonus and gate -- and names only those parts.  The
+ * reading taken here, per (b, t, h) over the N value channels j of o:
+ *     mu   = mean_j o[j],  var = mean_j (o[j] - mu)^2                (biased)
+ *     y[j] = (o[j] - mu) / sqrt(var + eps) * ln_w[h,j] + ln_b[h,j]
+ *     x[j] = (y[j] + (sum_i r[i] k[i] r_k[h,i]) * v[j]) * g[j]
+ * with r, k, v the WKV inputs of the same token, g the gate, and r_k, ln_w,
+ * ln_b [H,N] fp32 per-head parameters (16-byte aligned).  The arithmetic is
+ * fp32; eps is taken as given (eps <= 0 with a constant row gives Inf / NaN).
+ */
+
+/*
+ * wkv7_step_tail -- wkv7_step with the time-mix tail fused into its epilogue:
+ * each token's o never leaves the kernel, and x (type x_dtype, layout of o) is
+ * written instead.
+ *   gate : [B,T,H,N] of in_dtype;  r_k, ln_w, ln_b : [H,N] fp32;  eps : as above.
+ * Every other argument as for wkv7_step (x in the place of o).  gate, r_k,
+ * ln_w and ln_b may not overlap x, state_out or state_pos.
+ */
+int wkv7_step_tail(const void *r, const void *w, const void *k, const void *v,
+                   const void *a, const void *b, int in_dtype, const float *state_in,
+                   const void *gate, const float *r_k, const float *ln_w, const float *ln_b,
+                   float eps, void *x, int x_dtype, float *state_out, float *state_pos,
+                   int B, int T, int H, int N, void *stream);
+
+/*
+ * wkv7_tmix_tail -- the time-mix tail as a pass of its own, for the output of
+ * wkv7_forward / wkv7_forward_varlen (whose chunked kernel spreads one token's
+ * outputs over several waves).
+ *   o          : [B,T,H,N] of o_dtype (WKV7_F32 | WKV7_BF16).
+ *   r, k, v, g : [B,T,H,N] of in_dtype.
+ *   r_k, ln_w, ln_b : [H,N] fp32;  eps : as above.
+ *   x          : [B,T,H,N] of x_dtype; may be o itself when x_dtype == o_dtype,
+ *                otherwise it may not overlap any input.
+ * T = 0 does nothing.
+ */
+int wkv7_tmix_tail(const void *o, int o_dtype, const void *r, const void *k, const void *v,
+                   const void *g, int in_dtype, const float *r_k, const float *ln_w,
+                   const float *ln_b, float eps, void *x, int x_dtype,
+                   int B, int T, int H, int N, void *stream);
 
 /*
  * wkv7_state_commit -- keep the state after each row's accepted prefix of a

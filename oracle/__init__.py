@@ -156,3 +156,31 @@ def state_commit(state_pos, accepted, state_in=None, state_out=None):
         elif n == 0:
             out[bb] = 0.0 if state_in is None else _as_input(state_in, np.float64)[bb]
     return out
+
+
+def tmix_tail(o, r, k, v, g, r_k, ln_w, ln_b, eps):
+    """The time-mix tail after WKV: group norm, bonus and gate.
+
+    The SwiftRWKV Inference guide (its decode-path list and the fused frozen
+    pass) fuses these three steps after the WKV output and names only their
+    parts.  The reading taken, per (b, t, h), over the N value channels j:
+        mu   = mean_j o[j],  var = mean_j (o[j] - mu)^2          (biased)
+        y[j] = (o[j] - mu) / sqrt(var + eps) * ln_w[h, j] + ln_b[h, j]
+        x[j] = (y[j] + (sum_i r[i] k[i] r_k[h, i]) * v[j]) * g[j]
+    o, r, k, v, g: [B,T,H,N]; r_k, ln_w, ln_b: [H,N]; returns x [B,T,H,N] fp64.
+    """
+    f = lambda a: _as_input(a, np.float64)
+    o, r, k, v, g = (f(a) for a in (o, r, k, v, g))
+    r_k, ln_w, ln_b = (f(a) for a in (r_k, ln_w, ln_b))
+    B, T, H, N = o.shape
+    x = np.zeros((B, T, H, N))
+    for bb in range(B):
+        for t in range(T):
+            for h in range(H):
+                row = o[bb, t, h]
+                mu = row.sum() / N
+                var = ((row - mu) ** 2).sum() / N
+                y = (row - mu) / np.sqrt(var + eps) * ln_w[h] + ln_b[h]
+                bonus = (r[bb, t, h] * k[bb, t, h] * r_k[h]).sum()
+                x[bb, t, h] = (y + bonus * v[bb, t, h]) * g[bb, t, h]
+    return x

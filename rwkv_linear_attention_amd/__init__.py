@@ -14,6 +14,11 @@ Functions (names as in the C ABI):
   row b runs its first lengths[b] tokens (``wkv7_forward_varlen`` of the C ABI).
 * ``wkv7_step(r, w, k, v, a, b, state_in=None, per_position=False, ...)``
   -> ``(o, state_out[, state_pos])``: the recurrent (decode / verify) pass.
+* ``wkv7_step_tail(r, w, k, v, a, b, g, r_k, ln_w, ln_b, eps, state_in=None, ...)``
+  -> ``(x, state_out[, state_pos])``: the recurrent pass with the time-mix tail
+  (group norm, bonus, gate) fused into its epilogue.
+* ``wkv7_tmix_tail(o, r, k, v, g, r_k, ln_w, ln_b, eps, x_dtype=torch.float32)`` -> ``x``:
+  the same tail as a pass of its own, after the parallel pass.
 * ``wkv7_state_commit(state_pos, accepted, state_in=None)`` -> ``state_out``: the state
   after each row's accepted prefix of a speculative verify step.
 * ``wkv7_state_reset(state, row_mask=None)``: zero the state (all rows or masked ones).
@@ -68,6 +73,11 @@ def lib():
         L.wkv7_step.restype = ci
         L.wkv7_state_commit.argtypes = [vp, vp, vp, vp, ci, ci, ci, ci, vp]
         L.wkv7_state_commit.restype = ci
+        cf = ctypes.c_float
+        L.wkv7_step_tail.argtypes = [vp] * 6 + [ci, vp, vp, vp, vp, vp, cf, vp, ci, vp, vp, ci, ci, ci, ci, vp]
+        L.wkv7_step_tail.restype = ci
+        L.wkv7_tmix_tail.argtypes = [vp, ci, vp, vp, vp, vp, ci, vp, vp, vp, cf, vp, ci, ci, ci, ci, ci, vp]
+        L.wkv7_tmix_tail.restype = ci
         L.wkv7_state_reset.argtypes = [vp, ci, ci, ci, vp, vp]
         L.wkv7_state_reset.restype = ci
         L.wkv7_status_string.argtypes = [ci]
@@ -187,6 +197,56 @@ def wkv7_step(r, w, k, v, a, b, state_in=None, *, per_position=False, o_dtype=to
     if state_pos is not None:
         return o, state_out, state_pos
     return o, state_out
+
+
+def _head_params(H, N, device, **named):
+    out = []
+    for name, t in named.items():
+        if (t.dtype != torch.float32 or tuple(t.shape) != (H, N) or not t.is_contiguous() or t.device != device):
+            raise ValueError(f"{name} must be a contiguous fp32 [{H}, {N}] tensor on {device}")
+        out.append(t)
+    return out
+
+
+def wkv7_step_tail(r, w, k, v, a, b, g, r_k, ln_w, ln_b, eps, state_in=None, *, per_position=False,
+                   x_dtype=torch.float32, x=None, state_out=None, state_pos=None):
+    """wkv7_step with the time-mix tail fused: returns (x, state_out) or (x, state_out, state_pos).
+
+    g: gate [B, T, H, N] like r; r_k, ln_w, ln_b: fp32 [H, N]; eps: float.
+    """
+    B, T, H, N = _check_inputs(r, w, k, v, a, b)
+    dev = r.device
+    if g.shape != r.shape or g.dtype != r.dtype or not g.is_contiguous() or g.device != dev:
+        raise ValueError("g must match r in shape, dtype and device, and be contiguous")
+    r_k, ln_w, ln_b = _head_params(H, N, dev, r_k=r_k, ln_w=ln_w, ln_b=ln_b)
+    state_in = _state_arg(state_in, B, H, N, dev, "state_in")
+    if state_out is None:
+        state_out = torch.empty((B, H, N, N), dtype=torch.float32, device=dev)
+    _state_arg(state_out, B, H, N, dev, "state_out")
+    if x is None:
+        x = torch.empty((B, T, H, N), dtype=x_dtype, device=dev)
+    if per_position and state_pos is None:
+        state_pos = torch.empty((B, T, H, N, N), dtype=torch.float32, device=dev)
+    _check(lib().wkv7_step_tail(*[_ptr(t) for t in (r, w, k, v, a, b)], _dt(r), _ptr(state_in), _ptr(g),
+                                _ptr(r_k), _ptr(ln_w), _ptr(ln_b), float(eps), _ptr(x), _dt(x), _ptr(state_out),
+                                _ptr(state_pos), B, T, H, N, _stream(dev)))
+    if state_pos is not None:
+        return x, state_out, state_pos
+    return x, state_out
+
+
+def wkv7_tmix_tail(o, r, k, v, g, r_k, ln_w, ln_b, eps, *, x_dtype=torch.float32, x=None):
+    """The time-mix tail of o (from wkv7_forward): returns x [B, T, H, N].  x may be o itself."""
+    B, T, H, N = _check_inputs(r, r, k, v, g, g)
+    dev = r.device
+    if o.shape != r.shape or not o.is_contiguous() or o.device != dev:
+        raise ValueError("o must be a contiguous [B, T, H, N] tensor on the inputs' device")
+    r_k, ln_w, ln_b = _head_params(H, N, dev, r_k=r_k, ln_w=ln_w, ln_b=ln_b)
+    if x is None:
+        x = torch.empty((B, T, H, N), dtype=x_dtype, device=dev)
+    _check(lib().wkv7_tmix_tail(_ptr(o), _dt(o), _ptr(r), _ptr(k), _ptr(v), _ptr(g), _dt(r), _ptr(r_k),
+                                _ptr(ln_w), _ptr(ln_b), float(eps), _ptr(x), _dt(x), B, T, H, N, _stream(dev)))
+    return x
 
 
 def wkv7_state_commit(state_pos, accepted, state_in=None, *, state_out=None):

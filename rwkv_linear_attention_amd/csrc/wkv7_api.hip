@@ -109,10 +109,36 @@ SeqArgs make_args(const void *r, const void *w, const void *k, const void *v, co
     s.r = r; s.w = w; s.k = k; s.v = v; s.a = a; s.b = b;
     s.state_in = state_in; s.o = o; s.state_out = state_out; s.state_pos = state_pos;
     s.lengths = nullptr;
+    s.gate = nullptr;
+    s.r_k = s.ln_w = s.ln_b = nullptr;
+    s.eps = 0.f;
     s.B = B; s.T = T; s.H = H;
     s.in_bf16 = in_dtype == WKV7_BF16;
     s.o_bf16 = o_dtype == WKV7_BF16;
     return s;
+}
+
+// The tail's inputs: gate [B,T,H,N] of in_dtype and r_k, ln_w, ln_b [H,N] fp32 --
+// present, aligned, and outside every output range given.
+int check_tail_inputs(const void *gate, const float *r_k, const float *ln_w, const float *ln_b, int in_dtype,
+                      int B, int T, int H, const Range *outs, int nouts)
+{
+    if (T > 0 && (!gate || !r_k || !ln_w || !ln_b))
+        return WKV7_ERR_NULL;
+    if (T == 0)
+        return WKV7_OK;
+    const void *ptrs[] = {gate, r_k, ln_w, ln_b};
+    for (const void *ptr : ptrs)
+        if (misaligned(ptr))
+            return WKV7_ERR_ALIGN;
+    const int64_t ein = in_dtype == WKV7_BF16 ? 2 : 4;
+    const Range ins[4] = {range_of(gate, static_cast<int64_t>(B) * T * H * kN * ein), range_of(r_k, H * kN * 4),
+                          range_of(ln_w, H * kN * 4), range_of(ln_b, H * kN * 4)};
+    for (int x = 0; x < nouts; ++x)
+        for (const Range &y : ins)
+            if (overlap(outs[x], y))
+                return WKV7_ERR_ALIAS;
+    return WKV7_OK;
 }
 
 int empty_sequence(const float *state_in, float *state_out, int B, int H, hipStream_t stream)
@@ -202,6 +228,79 @@ int wkv7_state_reset(float *state, int B, int H, int N, const unsigned char *row
     return wkv7::launch_state_reset(state, B, H, row_mask, static_cast<hipStream_t>(stream)) == hipSuccess
                ? WKV7_OK
                : WKV7_ERR_HIP;
+}
+
+int wkv7_step_tail(const void *r, const void *w, const void *k, const void *v, const void *a, const void *b,
+                   int in_dtype, const float *state_in, const void *gate, const float *r_k, const float *ln_w,
+                   const float *ln_b, float eps, void *x, int x_dtype, float *state_out, float *state_pos, int B,
+                   int T, int H, int N, void *stream)
+{
+    int st = check_seq(r, w, k, v, a, b, in_dtype, state_in, x, x_dtype, state_out, state_pos, B, T, H, N);
+    if (st != WKV7_OK)
+        return st;
+    const int64_t tok = static_cast<int64_t>(B) * T * H;
+    const int64_t ex = x_dtype == WKV7_BF16 ? 2 : 4;
+    const Range outs[3] = {T > 0 ? range_of(x, tok * kN * ex) : Range{0, 0},
+                           range_of(state_out, static_cast<int64_t>(B) * H * kN * kN * 4),
+                           state_pos && T > 0 ? range_of(state_pos, tok * kN * kN * 4) : Range{0, 0}};
+    st = check_tail_inputs(gate, r_k, ln_w, ln_b, in_dtype, B, T, H, outs, 3);
+    if (st != WKV7_OK)
+        return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (T == 0)
+        return empty_sequence(state_in, state_out, B, H, s);
+    SeqArgs args = make_args(r, w, k, v, a, b, in_dtype, state_in, x, x_dtype, state_out, state_pos, B, T, H);
+    args.gate = gate;
+    args.r_k = r_k;
+    args.ln_w = ln_w;
+    args.ln_b = ln_b;
+    args.eps = eps;
+    return wkv7::launch_step(args, s) == hipSuccess ? WKV7_OK : WKV7_ERR_HIP;
+}
+
+int wkv7_tmix_tail(const void *o, int o_dtype, const void *r, const void *k, const void *v, const void *gate,
+                   int in_dtype, const float *r_k, const float *ln_w, const float *ln_b, float eps, void *x,
+                   int x_dtype, int B, int T, int H, int N, void *stream)
+{
+    int64_t tok = 0;
+    if (N != kN)
+        return WKV7_ERR_UNSUPPORTED;
+    const int dts[3] = {o_dtype, in_dtype, x_dtype};
+    for (int dt : dts)
+        if (dt != WKV7_F32 && dt != WKV7_BF16)
+            return WKV7_ERR_UNSUPPORTED;
+    if (!shape_ok(B, T, H, &tok))
+        return WKV7_ERR_SHAPE;
+    if (T > 0 && (!o || !r || !k || !v || !x))
+        return WKV7_ERR_NULL;
+    if (T == 0)
+        return check_tail_inputs(gate, r_k, ln_w, ln_b, in_dtype, B, T, H, nullptr, 0);
+    const void *ptrs[] = {o, r, k, v, x};
+    for (const void *ptr : ptrs)
+        if (misaligned(ptr))
+            return WKV7_ERR_ALIGN;
+    const int64_t n = tok * kN;
+    const int64_t eo = o_dtype == WKV7_BF16 ? 2 : 4, ein = in_dtype == WKV7_BF16 ? 2 : 4;
+    const int64_t ex = x_dtype == WKV7_BF16 ? 2 : 4;
+    const Range rx = range_of(x, n * ex);
+    // x may be o itself when both have one type (each lane reads its element before writing it)
+    if (overlap(rx, range_of(o, n * eo)) && !(x == o && x_dtype == o_dtype))
+        return WKV7_ERR_ALIAS;
+    const void *vin[3] = {r, k, v};
+    for (const void *ptr : vin)
+        if (overlap(rx, range_of(ptr, n * ein)))
+            return WKV7_ERR_ALIAS;
+    int st = check_tail_inputs(gate, r_k, ln_w, ln_b, in_dtype, B, T, H, &rx, 1);
+    if (st != WKV7_OK)
+        return st;
+    wkv7::TailArgs t;
+    t.o = o; t.r = r; t.k = k; t.v = v; t.gate = gate;
+    t.r_k = r_k; t.ln_w = ln_w; t.ln_b = ln_b; t.eps = eps;
+    t.x = x; t.rows = tok; t.H = H;
+    t.in_bf16 = in_dtype == WKV7_BF16;
+    t.o_bf16 = o_dtype == WKV7_BF16;
+    t.x_bf16 = x_dtype == WKV7_BF16;
+    return wkv7::launch_tail(t, static_cast<hipStream_t>(stream)) == hipSuccess ? WKV7_OK : WKV7_ERR_HIP;
 }
 
 int wkv7_state_commit(const float *state_pos, const int *accepted, const float *state_in, float *state_out,

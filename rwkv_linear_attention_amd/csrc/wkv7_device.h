@@ -37,4 +37,34 @@ __device__ __forceinline__ float lane_bcast(float x, int src)
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), src));
 }
 
+// Sum of x over the 64 lanes of a wave (every lane active), returned to every lane.
+__device__ __forceinline__ float wave_sum(float x)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+        x += __shfl_xor(x, off);
+    return x;
+}
+
+// The time-mix tail after WKV for one (b, t, h) row held one channel per lane
+// (the SwiftRWKV Inference guide fuses its three named parts: group norm,
+// bonus, gate): the row of o is normalised over its 64 channels (mean,
+// biased variance, eps), scaled and shifted per channel, the bonus
+// (sum over keys of r k r_k) times v is added, and the gate multiplies.
+// Lane j passes o[j], v[j], g[j], ln_w[j], ln_b[j] and also r[j], k[j], r_k[j]
+// for the bonus sum over the key index.
+// tail_norm takes the bonus sum already formed (it does not depend on o).
+__device__ __forceinline__ float tail_norm(float oj, float bonus, float vj, float gj, float wj, float bj, float eps)
+{
+    const float mu = wave_sum(oj) * (1.0f / kN);
+    const float d = oj - mu;
+    const float var = wave_sum(d * d) * (1.0f / kN);
+    return (d / sqrtf(var + eps) * wj + bj + bonus * vj) * gj;
+}
+__device__ __forceinline__ float tail_lane(float oj, float rj, float kj, float rkj, float vj, float gj, float wj,
+                                           float bj, float eps)
+{
+    return tail_norm(oj, wave_sum(rj * kj * rkj), vj, gj, wj, bj, eps);
+}
+
 }  // namespace wkv7

@@ -15,6 +15,20 @@ struct SeqArgs {
     const int *lengths;                 // [B] tokens of each row (clamped to [0, T]), or nullptr: all T
     int B, T, H;
     int in_bf16, o_bf16;                // dtype flags
+    // the fused time-mix tail (o then holds x): gate [B,T,H,64] in_dtype, r_k / ln_w / ln_b [H,64]
+    const void *gate;                   // nullptr: no tail
+    const float *r_k, *ln_w, *ln_b;
+    float eps;
+};
+
+struct TailArgs {
+    const void *o, *r, *k, *v, *gate;   // [B,T,H,64]; o of o_dtype, the rest of in_dtype
+    const float *r_k, *ln_w, *ln_b;     // [H,64]
+    float eps;
+    void *x;                            // [B,T,H,64] of x_dtype
+    long long rows;                     // B*T*H
+    int H;
+    int in_bf16, o_bf16, x_bf16;
 };
 
 hipError_t launch_step(const SeqArgs &a, hipStream_t stream);
@@ -22,6 +36,7 @@ hipError_t launch_chunk(const SeqArgs &a, hipStream_t stream);
 hipError_t launch_state_copy(const float *src, float *dst, long long n_floats, hipStream_t stream);
 hipError_t launch_state_reset(float *state, int B, int H, const unsigned char *row_mask,
                               hipStream_t stream);
+hipError_t launch_tail(const TailArgs &a, hipStream_t stream);
 hipError_t launch_state_commit(const float *state_pos, const int *accepted, const float *state_in,
                                float *state_out, int B, int T, int H, hipStream_t stream);
 

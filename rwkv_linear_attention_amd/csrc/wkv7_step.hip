@@ -60,12 +60,20 @@ __device__ __forceinline__ void load_rows(const float *__restrict__ p, float (&x
 // load, so no global latency sits inside the token loop.  The arithmetic is
 // the same code either way.
 // With VARLEN, row b runs its first lengths[b] tokens only (clamped to [0, T]);
-// T stays the row stride of the [B, T, H, N] tensors.
-template <typename Tin, typename Tout, bool HAS_STATE_IN, bool WRITE_POS, bool STAGED, int NW, bool VARLEN>
+// T stays the row stride of the [B, T, H, N] tensors.  With TAIL, the time-mix
+// tail (group norm, bonus, gate; see tail_lane) is applied to each token's o
+// in the wave that reduces it, and o receives x.
+struct TailIn {
+    const void *gate;
+    const float *r_k, *ln_w, *ln_b;
+    float eps;
+};
+template <typename Tin, typename Tout, bool HAS_STATE_IN, bool WRITE_POS, bool STAGED, int NW, bool VARLEN,
+          bool TAIL>
 __global__ __launch_bounds__(NW * 64) void wkv7_step_kernel(
     const Tin *__restrict__ r, const Tin *__restrict__ w, const Tin *__restrict__ k, const Tin *__restrict__ v,
     const Tin *__restrict__ a, const Tin *__restrict__ b, const float *state_in, Tout *__restrict__ o,
-    float *state_out, float *__restrict__ state_pos, int T, int H, const int *__restrict__ lengths)
+    float *state_out, float *__restrict__ state_pos, int T, int H, const int *__restrict__ lengths, TailIn tail)
 {
     constexpr int RW = kN / NW;                                       // key rows per wave
     const int j = threadIdx.x & 63;                                   // value column of this lane
@@ -94,6 +102,13 @@ __global__ __launch_bounds__(NW * 64) void wkv7_step_kernel(
     if constexpr (STAGED)
         stage_load(0, max(min(TB, L), 1));  // issued before the state loads: waiting for it skips them
 
+    // the tail's per-head parameters of this lane's channel
+    float t_w = 0.f, t_b = 0.f, t_rk = 0.f;
+    if constexpr (TAIL) {
+        t_w = tail.ln_w[hh * kN + j];
+        t_b = tail.ln_b[hh * kN + j];
+        t_rk = tail.r_k[hh * kN + j];
+    }
     const size_t sbase = static_cast<size_t>(bh) * (kN * kN) + static_cast<size_t>(i0) * kN + j;
     float S[RW];
 #pragma unroll
@@ -130,6 +145,23 @@ __global__ __launch_bounds__(NW * 64) void wkv7_step_kernel(
                 load_rows(k + base + i0, kr);
                 load_rows(r + base + i0, rr);
                 vj = load_elem(v, base + j);
+            }
+            // the tail's bonus sum and gate do not depend on the state: wave 0 forms them
+            // here, beside the other waves' partial sums
+            float t_bonus = 0.f, t_g = 0.f;
+            if constexpr (TAIL) {
+                if (g == 0) {
+                    float rj, kj;
+                    if constexpr (STAGED) {
+                        rj = xin[tt][4][j];
+                        kj = xin[tt][3][j];
+                    } else {
+                        rj = load_elem(r, base + j);
+                        kj = load_elem(k, base + j);
+                    }
+                    t_g = load_elem(static_cast<const Tin *>(tail.gate), base + j);
+                    t_bonus = wave_sum(rj * kj * t_rk);
+                }
             }
             auto rows4 = [&](int vec, const float (&reg)[RW], int u) -> f32x4 {
                 if constexpr (STAGED)
@@ -177,6 +209,8 @@ __global__ __launch_bounds__(NW * 64) void wkv7_step_kernel(
 #pragma unroll
                 for (int gg = 1; gg < NW; ++gg)
                     acc += part_r[gg][j];
+                if constexpr (TAIL)
+                    acc = tail_norm(acc, t_bonus, vj, t_g, t_w, t_b, tail.eps);
                 store_elem(o, base + j, acc);
             }
         }
@@ -195,10 +229,21 @@ hipError_t launch_mode(const SeqArgs &p, hipStream_t stream)
     const Tin *a = static_cast<const Tin *>(p.a), *b = static_cast<const Tin *>(p.b);
     Tout *o = static_cast<Tout *>(p.o);
     const bool sin = p.state_in != nullptr, pos = p.state_pos != nullptr;
-#define WKV7_STEP_LAUNCH(SIN, POS, VL)                                                                      \
-    hipLaunchKernelGGL((wkv7_step_kernel<Tin, Tout, SIN, POS, STAGED, NW, VL>), grid, block, 0, stream, r, w, k, v, \
-                       a, b, p.state_in, o, p.state_out, p.state_pos, p.T, p.H, p.lengths)
-    if (p.lengths && sin)  // rows of their own lengths (the forward pass, no per-position states)
+    const TailIn tail{p.gate, p.r_k, p.ln_w, p.ln_b, p.eps};
+#define WKV7_STEP_LAUNCH_T(SIN, POS, VL, TL)                                                                   \
+    hipLaunchKernelGGL((wkv7_step_kernel<Tin, Tout, SIN, POS, STAGED, NW, VL, TL>), grid, block, 0, stream, r, w, \
+                       k, v, a, b, p.state_in, o, p.state_out, p.state_pos, p.T, p.H, p.lengths, tail)
+#define WKV7_STEP_LAUNCH(SIN, POS, VL) WKV7_STEP_LAUNCH_T(SIN, POS, VL, false)
+    if (p.gate) {  // the fused tail (whole rows, per-position states optional)
+        if (sin && pos)
+            WKV7_STEP_LAUNCH_T(true, true, false, true);
+        else if (sin)
+            WKV7_STEP_LAUNCH_T(true, false, false, true);
+        else if (pos)
+            WKV7_STEP_LAUNCH_T(false, true, false, true);
+        else
+            WKV7_STEP_LAUNCH_T(false, false, false, true);
+    } else if (p.lengths && sin)  // rows of their own lengths (the forward pass, no per-position states)
         WKV7_STEP_LAUNCH(true, false, true);
     else if (p.lengths)
         WKV7_STEP_LAUNCH(false, false, true);
@@ -211,6 +256,7 @@ hipError_t launch_mode(const SeqArgs &p, hipStream_t stream)
     else
         WKV7_STEP_LAUNCH(false, false, false);
 #undef WKV7_STEP_LAUNCH
+#undef WKV7_STEP_LAUNCH_T
     return hipGetLastError();
 }
 

@@ -30,8 +30,9 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    assert names == sorted(["wkv7_forward", "wkv7_forward_varlen", "wkv7_step", "wkv7_state_commit",
-                            "wkv7_state_reset", "wkv7_status_string", "wkv7_abi_version"])
+    assert names == sorted(["wkv7_forward", "wkv7_forward_varlen", "wkv7_step", "wkv7_step_tail",
+                            "wkv7_tmix_tail", "wkv7_state_commit", "wkv7_state_reset", "wkv7_status_string",
+                            "wkv7_abi_version"])
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -177,3 +178,43 @@ def test_commit_validation(L):
     assert commit(L, sout=fake(9, 4096)) == ERR_ALIAS        # state_out inside state_pos
     assert commit(L, acc=fake(8, 16)) == ERR_ALIAS           # accepted inside state_out
     assert commit(L, sin=fake(8, 256)) == ERR_ALIAS          # partial overlap with state_in
+
+
+def step_tail(L, B=2, T=5, H=3, N=64, gate="fake", rk="fake", x="fake", pos="fake"):
+    p = [fake(i) for i in range(6)]
+    pick = lambda v, d: d if v == "fake" else v
+    return L.wkv7_step_tail(*p, BF16, fake(7), pick(gate, fake(11)), pick(rk, fake(12)), fake(13), fake(14),
+                            ctypes.c_float(1e-5), pick(x, fake(6)), F32, fake(8), pick(pos, fake(9)), B, T, H, N, None)
+
+
+def tmix(L, B=2, T=8, H=3, N=64, o="fake", x="fake", o_dt=F32, x_dt=F32, lnw="fake"):
+    pick = lambda v, d: d if v == "fake" else v
+    return L.wkv7_tmix_tail(pick(o, fake(6)), o_dt, fake(0), fake(2), fake(3), fake(11), BF16, fake(12),
+                            pick(lnw, fake(13)), fake(14), ctypes.c_float(1e-5), pick(x, fake(8)), x_dt,
+                            B, T, H, N, None)
+
+
+def test_step_tail_validation(L):
+    assert step_tail(L, N=32) == ERR_UNSUPPORTED
+    assert step_tail(L, B=0) == ERR_SHAPE
+    assert step_tail(L, gate=None) == ERR_NULL
+    assert step_tail(L, rk=None) == ERR_NULL
+    assert step_tail(L, gate=fake(11, 4)) == ERR_ALIGN
+    assert step_tail(L, rk=fake(6, 64)) == ERR_ALIAS          # r_k inside x
+    assert step_tail(L, gate=fake(9, 1024)) == ERR_ALIAS      # gate inside state_pos
+    assert step_tail(L, x=fake(0, 16)) == ERR_ALIAS           # x inside an input
+
+
+def test_tmix_tail_validation(L):
+    assert tmix(L, N=128) == ERR_UNSUPPORTED
+    assert tmix(L, o_dt=5) == ERR_UNSUPPORTED
+    assert tmix(L, x_dt=-1) == ERR_UNSUPPORTED
+    assert tmix(L, H=0) == ERR_SHAPE
+    assert tmix(L, o=None) == ERR_NULL
+    assert tmix(L, lnw=None) == ERR_NULL
+    assert tmix(L, x=fake(8, 8)) == ERR_ALIGN
+    assert tmix(L, x=fake(0, 32)) == ERR_ALIAS                # x inside r
+    assert tmix(L, x=fake(6, 64)) == ERR_ALIAS                # x partly over o
+    assert tmix(L, x=fake(6), x_dt=BF16) == ERR_ALIAS         # x == o with another type
+    assert tmix(L, lnw=fake(8, 16)) == ERR_ALIAS              # a parameter inside x
+    assert tmix(L, T=0, o=None, x=None) == OK                 # nothing to do

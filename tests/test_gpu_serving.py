@@ -103,3 +103,68 @@ def test_bf16_output_accuracy_workload3(K, oracle_mod):
         o_ref, _ = oracle_mod.forward(*[sub[n] for n in NAMES], sub["state_in"])
         check(o32[bb:bb + 1, :, hh:hh + 1], o_ref, TOL["bf16"], f"workload 3 (b={bb}, h={hh}) o fp32")
         check(o16[bb:bb + 1, :, hh:hh + 1], o_ref, TOL["bf16"], f"workload 3 (b={bb}, h={hh}) o bf16")
+
+
+def _tail_params(H, seed):
+    g = torch.Generator().manual_seed(seed)
+    r_k = (torch.randn((H, 64), generator=g) * 0.1).contiguous()
+    ln_w = (1 + 0.1 * torch.randn((H, 64), generator=g)).contiguous()
+    ln_b = (0.1 * torch.randn((H, 64), generator=g)).contiguous()
+    return r_k, ln_w, ln_b
+
+
+def _gate(shape, dtype, seed):
+    g = torch.Generator().manual_seed(seed)
+    x = torch.sigmoid(torch.randn(shape, generator=g))
+    return x.to(torch.bfloat16 if dtype == "bf16" else torch.float32).contiguous()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("x_dtype", [torch.float32, torch.bfloat16])
+def test_tmix_tail_vs_oracle(K, oracle_mod, dtype, x_dtype):
+    B, T, H = 2, 37, 5
+    inp = synth.make_inputs(B, T, H, 64, seed=91, dtype=dtype, state_std=0.1)
+    gate = _gate((B, T, H, 64), dtype, 92)
+    r_k, ln_w, ln_b = _tail_params(H, 93)
+    eps = 64e-5
+    o_ref, _ = oracle_mod.forward(*[inp[n] for n in NAMES], inp["state_in"])
+    o_dev = torch.from_numpy(o_ref).float().cuda()           # the tail's own input: a fixed fp32 o
+    d = to_dev(inp)
+    x = K.wkv7_tmix_tail(o_dev, d["r"], d["k"], d["v"], gate.cuda(), r_k.cuda(), ln_w.cuda(), ln_b.cuda(), eps,
+                         x_dtype=x_dtype)
+    torch.cuda.synchronize()
+    x_ref = oracle_mod.tmix_tail(o_dev.cpu(), inp["r"], inp["k"], inp["v"], gate, r_k, ln_w, ln_b, eps)
+    tol = 2e-3 if x_dtype == torch.bfloat16 else 1e-5
+    check(x, x_ref, tol, f"tail ({dtype} inputs, {x_dtype} x)")
+    # in place over o
+    o2 = o_dev.clone()
+    K.wkv7_tmix_tail(o2, d["r"], d["k"], d["v"], gate.cuda(), r_k.cuda(), ln_w.cuda(), ln_b.cuda(), eps, x=o2)
+    torch.cuda.synchronize()
+    x32 = K.wkv7_tmix_tail(o_dev, d["r"], d["k"], d["v"], gate.cuda(), r_k.cuda(), ln_w.cuda(), ln_b.cuda(), eps)
+    torch.cuda.synchronize()
+    assert torch.equal(o2, x32)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("T", [1, 5])
+def test_step_tail_vs_oracle(K, oracle_mod, dtype, T):
+    B, H = 4, 6
+    inp = synth.make_inputs(B, T, H, 64, seed=95 + T, dtype=dtype, state_std=0.1)
+    gate = _gate((B, T, H, 64), dtype, 96)
+    r_k, ln_w, ln_b = _tail_params(H, 97)
+    eps = 64e-5
+    d = to_dev(inp)
+    x, s, sp = K.wkv7_step_tail(*[d[n] for n in NAMES], gate.cuda(), r_k.cuda(), ln_w.cuda(), ln_b.cuda(), eps,
+                                d["state_in"], per_position=True)
+    torch.cuda.synchronize()
+    o_ref, s_ref, sp_ref = oracle_mod.forward(*[inp[n] for n in NAMES], inp["state_in"], per_position=True)
+    x_ref = oracle_mod.tmix_tail(o_ref, inp["r"], inp["k"], inp["v"], gate, r_k, ln_w, ln_b, eps)
+    check(x, x_ref, TOL[dtype], f"fused tail T={T} x")
+    check(s, s_ref, TOL[dtype], f"fused tail T={T} state")
+    check(sp, sp_ref, TOL[dtype], f"fused tail T={T} state_pos")
+    # the fused epilogue and the separate pass: the same arithmetic on the same o, summed in
+    # another order (64 lanes against 16 lanes of four channels)
+    o, _ = K.wkv7_step(*[d[n] for n in NAMES], d["state_in"])
+    x2 = K.wkv7_tmix_tail(o, d["r"], d["k"], d["v"], gate.cuda(), r_k.cuda(), ln_w.cuda(), ln_b.cuda(), eps)
+    torch.cuda.synchronize()
+    check(x, x2.double().cpu().numpy(), 1e-6, "fused against separate tail")

@@ -347,3 +347,51 @@ def test_state_commit_matches_prefix_runs(oracle_mod):
             assert np.array_equal(got[bb], s_in[bb])
         else:
             assert np.array_equal(got[bb], before[bb])
+
+
+def _tail_inputs(seed, B=2, T=3, H=2, N=64):
+    rng = np.random.default_rng(seed)
+    o, r, k, v = (rng.standard_normal((B, T, H, N)) for _ in range(4))
+    g = 1 / (1 + np.exp(-rng.standard_normal((B, T, H, N))))
+    r_k = rng.standard_normal((H, N)) * 0.1
+    ln_w = 1 + 0.1 * rng.standard_normal((H, N))
+    ln_b = 0.1 * rng.standard_normal((H, N))
+    return o, r, k, v, g, r_k, ln_w, ln_b
+
+
+def test_tail_group_norm_moments(oracle_mod):
+    # unit affine, no bonus, open gate: every (b,t,h) row has mean 0 and variance
+    # var/(var+eps) (closed form of the normalisation)
+    o, r, k, v, g, r_k, ln_w, ln_b = _tail_inputs(71)
+    eps = 0.3
+    x = oracle_mod.tmix_tail(o, r, k, v, np.ones_like(g), np.zeros_like(r_k), np.ones_like(ln_w),
+                             np.zeros_like(ln_b), eps)
+    var = o.var(axis=-1)
+    np.testing.assert_allclose(x.mean(axis=-1), 0.0, atol=1e-12)
+    np.testing.assert_allclose(x.var(axis=-1), var / (var + eps), rtol=1e-12)
+
+
+def test_tail_constant_row_leaves_bias_and_bonus(oracle_mod):
+    # a constant o row normalises to 0: x = (ln_b + bonus * v) * g, bonus by hand
+    o, r, k, v, g, r_k, ln_w, ln_b = _tail_inputs(72)
+    o[:] = 2.5
+    x = oracle_mod.tmix_tail(o, r, k, v, g, r_k, ln_w, ln_b, 1e-3)
+    for bb in range(o.shape[0]):
+        for t in range(o.shape[1]):
+            for h in range(o.shape[2]):
+                bonus = sum(r[bb, t, h, i] * k[bb, t, h, i] * r_k[h, i] for i in range(o.shape[3]))
+                expect = (ln_b[h] + bonus * v[bb, t, h]) * g[bb, t, h]
+                np.testing.assert_allclose(x[bb, t, h], expect, rtol=1e-12, atol=1e-14)
+
+
+def test_tail_gate_and_head_parameters(oracle_mod):
+    # the gate scales elementwise; each head uses its own r_k / ln_w / ln_b row
+    o, r, k, v, g, r_k, ln_w, ln_b = _tail_inputs(73)
+    x1 = oracle_mod.tmix_tail(o, r, k, v, np.ones_like(g), r_k, ln_w, ln_b, 1e-4)
+    xg = oracle_mod.tmix_tail(o, r, k, v, g, r_k, ln_w, ln_b, 1e-4)
+    np.testing.assert_allclose(xg, x1 * g, rtol=1e-13)
+    ln_b2 = ln_b.copy()
+    ln_b2[1] += 1.0
+    x2 = oracle_mod.tmix_tail(o, r, k, v, g, r_k, ln_w, ln_b2, 1e-4)
+    np.testing.assert_allclose(x2[:, :, 0], xg[:, :, 0], rtol=0, atol=0)
+    np.testing.assert_allclose(x2[:, :, 1], xg[:, :, 1] + g[:, :, 1], rtol=1e-12)
