@@ -55,7 +55,8 @@ def recurrent_flops(wl) -> int:
 
 
 def kernel_source_hash(kind: str) -> str:
-    name = {"step": "wkv7_step.hip", "verify": "wkv7_step.hip", "chunk": "wkv7_chunk.hip"}[kind]
+    name = {"step": "wkv7_step.hip", "verify": "wkv7_step.hip", "chunk": "wkv7_chunk.hip",
+            "step_tail": "wkv7_step.hip", "tail_pass": "wkv7_tail.hip"}[kind]
     h = hashlib.sha256()
     for f in (name, "wkv7_device.h"):
         with open(os.path.join(CSRC, f), "rb") as fh:
@@ -403,20 +404,18 @@ def main():
         others["3-bf16o"] = {"workload": w3.name + " (bf16 o)", "ms_per_call": round(tb["sec_per_launch"] * 1e3, 4),
                              "roofline": rb, "mtok_s": round(tb["mtok_s"], 2)}
         # the time-mix tail: fused into the decode step (workload 1), and as a pass of its own
-        # over the prefill outputs of workload 3 (fp32 o and x, bf16 r, k, v, g); no HBM counters
+        # over the prefill outputs of workload 3 (fp32 o and x, bf16 r, k, v, g)
         w1 = synth.WORKLOADS[1]
         tt = time_step_workload(K, synth, 1, args.steps, args.warmup, tail="fused")
         ts = time_step_workload(K, synth, 1, args.steps, args.warmup, tail="separate")
         b_tail = algorithmic_bytes(w1, "step") + w1.B * w1.T * w1.H * N * 2 + 3 * w1.H * N * 4
-        rt = roofline(b_tail, tt["sec_per_launch"], "step", 1)
-        rt["traffic"] = None
+        rt = roofline(b_tail, tt["sec_per_launch"], "step_tail", 1)
         others["1-tail"] = {"workload": w1.name + " (fused time-mix tail)", "us_per_layer": round(tt["us_per_layer"], 3),
                             "roofline": rt,
                             "us_per_layer_step_then_tail_pass": round(ts["us_per_layer"], 3)}
         tp = time_tail_pass(K, synth, 3, max(20, args.steps), args.warmup)
         b_pass = w3.B * w3.T * w3.H * N * (4 + 4 * 2 + 4) + 3 * w3.H * N * 4
-        rp = roofline(b_pass, tp["sec_per_launch"], "chunk", 3)
-        rp["traffic"] = None
+        rp = roofline(b_pass, tp["sec_per_launch"], "tail_pass", 3)
         others["3-tail-pass"] = {"workload": w3.name + " (time-mix tail pass)",
                                  "ms_per_call": round(tp["sec_per_launch"] * 1e3, 4), "roofline": rp}
         line["other_workloads"] = others
