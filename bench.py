@@ -128,7 +128,9 @@ def make_layers(K, synth, idx: int, nlayers: int, tail=False):
         d["state"] = inp["state_in"].cuda()
         d["o"] = torch.empty((wl.B, wl.T, wl.H, N), dtype=torch.float32, device="cuda")
         d["pos"] = torch.empty((wl.B, wl.T, wl.H, N, N), dtype=torch.float32, device="cuda") if idx == 4 else None
-        if tail:  # "fused" (the tail in the step's epilogue) or "separate" (a second launch)
+        if tail == "pos_only":  # the verify step with per-position states only (no separate state_out)
+            d["mode"] = tail
+        elif tail:  # "fused" (the tail in the step's epilogue) or "separate" (a second launch)
             gen = torch.Generator(device="cuda").manual_seed(77 + l)
             d["g"] = torch.sigmoid(torch.randn(d["r"].shape, generator=gen, device="cuda")).to(d["r"].dtype)
             d["tail"] = tail_params(wl.H, 78 + l)
@@ -141,7 +143,10 @@ def make_layers(K, synth, idx: int, nlayers: int, tail=False):
 
 def sweep(K, sets):
     for d in sets:
-        if d.get("mode") == "fused":
+        if d.get("mode") == "pos_only":
+            K.wkv7_step(d["r"], d["w"], d["k"], d["v"], d["a"], d["b"], d["state"], o=d["o"],
+                        state_pos=d["pos"], write_state_out=False)
+        elif d.get("mode") == "fused":
             K.wkv7_step_tail(d["r"], d["w"], d["k"], d["v"], d["a"], d["b"], d["g"], *d["tail"], 64e-5,
                              d["state"], x=d["o"], state_out=d["state"], state_pos=d["pos"])
         elif d.get("mode") == "separate":
@@ -413,6 +418,13 @@ def main():
         others["1-tail"] = {"workload": w1.name + " (fused time-mix tail)", "us_per_layer": round(tt["us_per_layer"], 3),
                             "roofline": rt,
                             "us_per_layer_step_then_tail_pass": round(ts["us_per_layer"], 3)}
+        # the verify step writing per-position states only (the final state is the last of them)
+        w4 = synth.WORKLOADS[4]
+        tv = time_step_workload(K, synth, 4, args.steps, args.warmup, tail="pos_only")
+        rv = roofline(algorithmic_bytes(w4, "verify") - w4.B * w4.H * N * N * 4, tv["sec_per_launch"], "verify", 4)
+        rv["traffic"] = None
+        others["4-pos-only"] = {"workload": w4.name + " (per-position states only)",
+                                "us_per_layer": round(tv["us_per_layer"], 3), "roofline": rv}
         tp = time_tail_pass(K, synth, 3, max(20, args.steps), args.warmup)
         b_pass = w3.B * w3.T * w3.H * N * (4 + 4 * 2 + 4) + 3 * w3.H * N * 4
         rp = roofline(b_pass, tp["sec_per_launch"], "tail_pass", 3)

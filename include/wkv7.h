@@ -126,7 +126,9 @@ int wkv7_forward_varlen(const void *r, const void *w, const void *k, const void 
  *   state_pos : [B,T,H,N,N] fp32, or NULL.  When given, state_pos[b,t,h] is the
  *               state after token t, so a caller can keep the state after any
  *               accepted prefix of a speculative step (state_pos[:,T-1] equals
- *               state_out).
+ *               state_out).  With state_pos given and T > 0, state_out may be
+ *               NULL: the final state is then only in state_pos (a verify step
+ *               followed by wkv7_state_commit needs no separate copy).
  * Meant for small T (1 for decode, K+1 for a verify step), but correct for
  * any T >= 0.  Exact for every decay in [0, 1].
  */

@@ -174,17 +174,22 @@ def wkv7_forward(r, w, k, v, a, b, state_in=None, *, o_dtype=torch.float32, o=No
 
 
 def wkv7_step(r, w, k, v, a, b, state_in=None, *, per_position=False, o_dtype=torch.float32, o=None,
-              state_out=None, state_pos=None):
+              state_out=None, state_pos=None, write_state_out=True):
     """Recurrent pass, token by token.  Returns (o, state_out) or (o, state_out, state_pos).
 
-    With per_position=True, state_pos[:, t] is the state after token t.
+    With per_position=True, state_pos[:, t] is the state after token t; then
+    write_state_out=False skips the separate final state (state_out is None).
     """
     B, T, H, N = _check_inputs(r, w, k, v, a, b)
     dev = r.device
     state_in = _state_arg(state_in, B, H, N, dev, "state_in")
-    if state_out is None:
+    if not write_state_out:
+        if not (per_position or state_pos is not None) or state_out is not None:
+            raise ValueError("write_state_out=False needs per-position states and no state_out")
+    elif state_out is None:
         state_out = torch.empty((B, H, N, N), dtype=torch.float32, device=dev)
-    _state_arg(state_out, B, H, N, dev, "state_out")
+    if state_out is not None:
+        _state_arg(state_out, B, H, N, dev, "state_out")
     if o is None:
         o = torch.empty((B, T, H, N), dtype=o_dtype, device=dev)
     if per_position and state_pos is None:

@@ -46,9 +46,11 @@ bool shape_ok(int B, int T, int H, int64_t *tokens_out)
     return true;
 }
 
+// state_out may be NULL only where the caller allows it (the recurrent pass with
+// per-position states and T > 0: the last of those is the final state).
 int check_seq(const void *r, const void *w, const void *k, const void *v, const void *a, const void *b,
               int in_dtype, const float *state_in, void *o, int o_dtype, float *state_out, float *state_pos,
-              int B, int T, int H, int N)
+              int B, int T, int H, int N, bool out_optional = false)
 {
     int64_t tok = 0;
     if (N != kN)
@@ -57,7 +59,7 @@ int check_seq(const void *r, const void *w, const void *k, const void *v, const 
         return WKV7_ERR_UNSUPPORTED;
     if (!shape_ok(B, T, H, &tok))
         return WKV7_ERR_SHAPE;
-    if (!state_out)
+    if (!state_out && !(out_optional && state_pos && T > 0))
         return WKV7_ERR_NULL;
     if (T > 0 && (!r || !w || !k || !v || !a || !b || !o))
         return WKV7_ERR_NULL;
@@ -68,8 +70,9 @@ int check_seq(const void *r, const void *w, const void *k, const void *v, const 
 
     const int64_t ein = in_dtype == WKV7_BF16 ? 2 : 4, eo = o_dtype == WKV7_BF16 ? 2 : 4;
     const int64_t seq_elems = tok * kN, st_bytes = static_cast<int64_t>(B) * H * kN * kN * 4;
-    Range ro{0, 0}, rpos{0, 0}, rin{0, 0};
-    const Range rst = range_of(state_out, st_bytes);
+    Range ro{0, 0}, rpos{0, 0}, rin{0, 0}, rst{0, 0};
+    if (state_out)
+        rst = range_of(state_out, st_bytes);
     if (state_in)
         rin = range_of(state_in, st_bytes);
     if (T > 0)
@@ -78,7 +81,7 @@ int check_seq(const void *r, const void *w, const void *k, const void *v, const 
         rpos = range_of(state_pos, seq_elems * kN * 4);
 
     // state_out may be state_in exactly; any other overlap is refused.
-    if (state_in && state_in != state_out && overlap(rst, rin))
+    if (state_in && state_out && state_in != state_out && overlap(rst, rin))
         return WKV7_ERR_ALIAS;
     Range ins[7] = {rin, {0, 0}, {0, 0}, {0, 0}, {0, 0}, {0, 0}, {0, 0}};
     if (T > 0) {
@@ -199,7 +202,7 @@ int wkv7_step(const void *r, const void *w, const void *k, const void *v, const 
               int in_dtype, const float *state_in, void *o, int o_dtype, float *state_out, float *state_pos,
               int B, int T, int H, int N, void *stream)
 {
-    int st = check_seq(r, w, k, v, a, b, in_dtype, state_in, o, o_dtype, state_out, state_pos, B, T, H, N);
+    int st = check_seq(r, w, k, v, a, b, in_dtype, state_in, o, o_dtype, state_out, state_pos, B, T, H, N, true);
     if (st != WKV7_OK)
         return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -235,13 +238,13 @@ int wkv7_step_tail(const void *r, const void *w, const void *k, const void *v, c
                    const float *ln_b, float eps, void *x, int x_dtype, float *state_out, float *state_pos, int B,
                    int T, int H, int N, void *stream)
 {
-    int st = check_seq(r, w, k, v, a, b, in_dtype, state_in, x, x_dtype, state_out, state_pos, B, T, H, N);
+    int st = check_seq(r, w, k, v, a, b, in_dtype, state_in, x, x_dtype, state_out, state_pos, B, T, H, N, true);
     if (st != WKV7_OK)
         return st;
     const int64_t tok = static_cast<int64_t>(B) * T * H;
     const int64_t ex = x_dtype == WKV7_BF16 ? 2 : 4;
     const Range outs[3] = {T > 0 ? range_of(x, tok * kN * ex) : Range{0, 0},
-                           range_of(state_out, static_cast<int64_t>(B) * H * kN * kN * 4),
+                           state_out ? range_of(state_out, static_cast<int64_t>(B) * H * kN * kN * 4) : Range{0, 0},
                            state_pos && T > 0 ? range_of(state_pos, tok * kN * kN * 4) : Range{0, 0}};
     st = check_tail_inputs(gate, r_k, ln_w, ln_b, in_dtype, B, T, H, outs, 3);
     if (st != WKV7_OK)

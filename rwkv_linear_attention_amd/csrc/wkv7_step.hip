@@ -215,9 +215,10 @@ __global__ __launch_bounds__(NW * 64) void wkv7_step_kernel(
             }
         }
     }
+    if (state_out)  // absent when the per-position states carry the final state
 #pragma unroll
-    for (int u = 0; u < RW; ++u)
-        __builtin_nontemporal_store(S[u], state_out + sbase + u * kN);
+        for (int u = 0; u < RW; ++u)
+            __builtin_nontemporal_store(S[u], state_out + sbase + u * kN);
 }
 
 template <typename Tin, typename Tout, bool STAGED, int NW>

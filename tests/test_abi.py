@@ -218,3 +218,11 @@ def test_tmix_tail_validation(L):
     assert tmix(L, x=fake(6), x_dt=BF16) == ERR_ALIAS         # x == o with another type
     assert tmix(L, lnw=fake(8, 16)) == ERR_ALIAS              # a parameter inside x
     assert tmix(L, T=0, o=None, x=None) == OK                 # nothing to do
+
+
+def test_state_out_needs_per_position_states(L):
+    # state_out may be NULL only for the recurrent pass with per-position states and T > 0
+    p = [fake(i) for i in range(6)]
+    assert L.wkv7_step(*p, BF16, fake(7), fake(6), F32, None, None, 2, 5, 3, 64, None) == ERR_NULL
+    assert L.wkv7_step(*p, BF16, fake(7), fake(6), F32, None, fake(9), 2, 0, 3, 64, None) == ERR_NULL
+    assert L.wkv7_forward(*p, BF16, fake(7), fake(6), F32, None, 2, 8, 3, 64, None) == ERR_NULL

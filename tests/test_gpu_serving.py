@@ -168,3 +168,20 @@ def test_step_tail_vs_oracle(K, oracle_mod, dtype, T):
     x2 = K.wkv7_tmix_tail(o, d["r"], d["k"], d["v"], gate.cuda(), r_k.cuda(), ln_w.cuda(), ln_b.cuda(), eps)
     torch.cuda.synchronize()
     check(x, x2.double().cpu().numpy(), 1e-6, "fused against separate tail")
+
+
+def test_verify_without_separate_state_out(K, oracle_mod):
+    # the verify step with per-position states only, then the commit: the same states
+    B, T, H = 4, 5, 8
+    inp = synth.make_inputs(B, T, H, 64, seed=99, dtype="bf16", state_std=0.1)
+    d = to_dev(inp)
+    args = [d[n] for n in NAMES]
+    o1, s1, sp1 = K.wkv7_step(*args, d["state_in"], per_position=True)
+    o2, none, sp2 = K.wkv7_step(*args, d["state_in"], per_position=True, write_state_out=False)
+    torch.cuda.synchronize()
+    assert none is None
+    assert torch.equal(o1, o2) and torch.equal(sp1, sp2)
+    assert torch.equal(sp2[:, T - 1], s1)
+    committed = K.wkv7_state_commit(sp2, [T] * B)
+    torch.cuda.synchronize()
+    assert torch.equal(committed, s1)
