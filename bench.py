@@ -271,6 +271,37 @@ def copy_ceiling(idx: int, steps: int, warmup: int):
     return {"bytes_per_copy": 8 * n, "us_per_copy": round(sec * 1e6, 3), "GB/s": round(8 * n / sec / 1e9, 1)}
 
 
+def fill_ceiling(idx: int, steps: int, warmup: int):
+    """A write-only fill of the bytes one call of workload idx writes (o, state_out and, for
+    the verify step, the per-position states), over the same number of distinct buffers,
+    graph-replayed: the HBM rate a streaming write reaches here."""
+    import torch
+    import synth
+    wl = synth.WORKLOADS[idx]
+    tokheads = wl.B * wl.T * wl.H
+    nbytes = tokheads * N * 4 + wl.B * wl.H * N * N * 4 + (tokheads * N * N * 4 if idx == 4 else 0)
+    n = nbytes // 4
+    layers = max(1, wl.layers)
+    bufs = [torch.empty(n, device="cuda") for _ in range(layers)]
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        for b_ in bufs:
+            b_.fill_(1.0)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for b_ in bufs:
+                b_.fill_(1.0)
+        warm(g.replay, warmup)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            g.replay()
+        e1.record(stream)
+        e1.synchronize()
+    sec = e0.elapsed_time(e1) / 1e3 / (steps * layers)
+    return {"bytes_per_fill": 4 * n, "us_per_fill": round(sec * 1e6, 3), "GB/s": round(4 * n / sec / 1e9, 1)}
+
+
 # ----------------------------------------------------------------------------- CPU baseline
 
 def cpu_baseline(synth, idx: int, budget_s: float = 12.0):
@@ -326,6 +357,8 @@ def main():
     ap.add_argument("--only", action="store_true", help="measure the chosen workload only")
     ap.add_argument("--warm-seconds", type=float, default=WARM_SECONDS,
                     help="minimum untimed warm-up per measurement (0: just --warmup steps)")
+    ap.add_argument("--fill-ceiling", action="store_true",
+                    help="time a write-only fill of the bytes the workload writes instead (write ceiling)")
     ap.add_argument("--copy-ceiling", action="store_true",
                     help="time a plain device copy of the workload's bytes instead (HBM ceiling / counter calibration)")
     args = ap.parse_args()
@@ -340,6 +373,10 @@ def main():
     import synth
     if not torch.cuda.is_available():
         raise SystemExit("no GPU visible")
+    if args.fill_ceiling:
+        print(json.dumps({"fill_ceiling": fill_ceiling(args.workload, args.steps, args.warmup),
+                          "workload": synth.WORKLOADS[args.workload].name}), flush=True)
+        return
     if args.copy_ceiling:
         print(json.dumps({"copy_ceiling": copy_ceiling(args.workload, args.steps, args.warmup),
                           "workload": synth.WORKLOADS[args.workload].name}), flush=True)
