@@ -46,7 +46,11 @@
  * buffer of the call is refused with WKV7_ERR_ALIAS.
  *
  * NUMERICS.  The state and every accumulation are fp32.  bf16 inputs are
- * widened exactly.  NaN / Inf propagate as the arithmetic dictates.  Results
+ * widened exactly.  NaN / Inf propagate as the arithmetic dictates: value
+ * channels stay independent (a NaN in v[b,t,h,j] reaches only column j of that
+ * head, from token t on), except that the chunked kernel of wkv7_forward forms
+ * the outputs of 16 tokens together, so there it can also reach the earlier
+ * tokens of the same 16-token chunk.  Results
  * match an fp64 evaluation of the definition to a relative L2 error of about
  * 1e-6 (fp32 inputs) and well under 2e-3 (bf16 inputs, fp32 state).
  */

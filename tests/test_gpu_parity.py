@@ -291,3 +291,24 @@ def test_workload3_prefill_sampled_heads(K, oracle_mod):
         o_ref, s_ref = oracle_run(oracle_mod, sub)
         check(o[bb:bb + 1, :, hh:hh + 1], o_ref, TOL["bf16"], f"workload 3 (b={bb}, h={hh}) o")
         check(s[bb:bb + 1, hh:hh + 1], s_ref, TOL["bf16"], f"workload 3 (b={bb}, h={hh}) state")
+
+
+@pytest.mark.parametrize("kernel", ["step", "forward"])
+def test_nan_in_a_value_channel_stays_in_its_column(K, kernel):
+    # Value channels evolve independently: a NaN in v[b, t, h, j] reaches o[b, t', h, j] for
+    # t' >= t and nothing else -- no other column, head or batch row.  The step kernel keeps
+    # every earlier token finite; the chunked kernel forms a chunk's outputs together (its
+    # masked products multiply 0 by the NaN), so there only the chunks before stay finite.
+    B, T, H, t_nan, j_nan = 2, 40, 3, 21, 5
+    inp = synth.make_inputs(B, T, H, 64, seed=123, dtype="bf16", state_std=0.1)
+    inp["v"][1, t_nan, 2, j_nan] = float("nan")
+    o, s = gpu_run(K, to_dev(inp), kernel)
+    o, s = o.cpu(), s.cpu()
+    bad = torch.isnan(o)
+    assert bad[1, t_nan:, 2, j_nan].all(), "the NaN must reach every later output of its column"
+    mask = torch.zeros_like(bad)
+    first = t_nan if kernel == "step" else (t_nan // 16) * 16
+    mask[1, first:, 2, j_nan] = True
+    assert not (bad & ~mask).any(), "the NaN leaked out of its column, head or time range"
+    assert torch.isnan(s[1, 2, :, j_nan]).all() and torch.isfinite(s[1, 2, :, :j_nan]).all()
+    assert torch.isfinite(s[0]).all() and torch.isfinite(s[1, :2]).all()
