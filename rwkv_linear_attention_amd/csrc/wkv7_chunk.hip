@@ -512,12 +512,17 @@ __global__ __launch_bounds__((kN / J / 16 + nprod<Tin>()) * 64) void wkv7_chunk_
     //   R_MA: M_ak                  R_SA, R_SR, R_SB, R_SK: A', R', B', K' (R_SK also v)
     //   R_MR: M_rb, M_rk
     enum { R_T = 0, R_MA = 1, R_MR = 2, R_D = 3, R_SA = 4, R_SR = 5, R_SB = 6, R_SK = 7, R_T1 = 8, R_D1 = 9 };
-    // producer k runs on SIMD (NSW + k) % 4; pairs per SIMD for J = 1:
-    // (T, M_ak) (K', decay) (A', R') (B', M_rb/M_rk)
-    // bf16 inputs (ten producers, J = 1): (T, D1, MA) (T1, D, MR) (SK, SA) (SB, SR);
-    // R_T / R_T1 and R_D / R_D1 take the even and the odd chunks
-    const int role = DEEP ? static_cast<int>((0x2154396780ull >> (4 * (wv - NSW))) & 15)
-                          : (0x25316470 >> (4 * (wv - NSW))) & 15;  // T SK SA SB MA D SR MR
+    // Producer k runs on SIMD (NSW + k) % 4, beside the consumer wave of that SIMD
+    // if there is one.  The consumers set the pace, so the matrix-core work of the
+    // producers (the inverse waves above all) is spread evenly over the consumers'
+    // SIMDs, and the scale waves' elementwise work fills in around it.
+    //   fp32 inputs (eight producers, J = 1): (T, MA) (SK, D) (SA, SR) (SB, MR)
+    //   bf16 inputs, J = 1: (MR, SB, D) (SK, MA, D1) (T, SA) (T1, SR)
+    //   bf16 inputs, J = 2 (consumers on SIMDs 0 and 1): (SK, SA) (SB, SR) on the
+    //   consumers' SIMDs, (T, D1, MA) (T1, D, MR) on the other two
+    // R_T / R_T1 and R_D / R_D1 take the even and the odd chunks.
+    constexpr unsigned long long ROLES = !DEEP ? 0x25316470ull : J == 1 ? 0x9354168072ull : 0x2154396780ull;
+    const int role = static_cast<int>((ROLES >> (4 * (wv - NSW))) & 15);
     const int t_end = L;
 
     using F = std::integral_constant<bool, false>;
