@@ -220,13 +220,15 @@ struct alignas(16) DSlot {
     float v[NDROW][kN];
 };
 
-template <typename Tin, int NP, int NPV, int NS>
+constexpr int MTP = 20;  // row pitch (floats) of the fp32 transpose tiles of M_ab
+template <typename Tin, int NP, int NPV, int NS, int NT>
 struct Smem {
     Slot<NP, NPV> slot[NS];
     alignas(16) Tin wbuf[CH][kN];  // w rows of one chunk, transposed through here by the decay wave
     DSlot dt[2];
     alignas(16) float p7[kN];  // P_7 of the first chunk
     alignas(16) float d15[2][kN];  // d_15 of the last two chunks whose table was written
+    alignas(16) float mt[NT][CH][MTP];  // M_ab of one chunk per inverse wave, row-major
 };
 
 // Decay factors of one key channel over a chunk: d[tau+1] = P_tau / P_7 and
@@ -274,7 +276,7 @@ __global__ __launch_bounds__((kN / J / 16 + nprod<Tin>()) * 64) void wkv7_chunk_
     constexpr bool DEEP = !F32IN;
     constexpr int NS = DEEP ? 4 : 3;
     using SlotT = Slot<NP, NPV>;
-    __shared__ Smem<Tin, NP, NPV, NS> sm;
+    __shared__ Smem<Tin, NP, NPV, NS, DEEP ? 2 : 1> sm;
 
     // Workgroup -> (batch*head, column block).  Workgroups are dealt to the
     // XCDs round-robin; the J column blocks of one head stay on one XCD so the
@@ -793,16 +795,18 @@ __global__ __launch_bounds__((kN / J / 16 + nprod<Tin>()) * 64) void wkv7_chunk_
         }
     };
 
-    // ---- inverse wave.  Part A forms M = M_ab of chunk c and its transpose
-    // (kept in registers); part B inverts I - M,
+    // ---- inverse wave.  Part A forms M = M_ab of chunk c (kept in registers)
+    // and writes it to this wave's LDS tile; part B reads back M^T, inverts I - M,
     //   T = (I - M)^{-1} = (I + M)(I + M^2)(I + M^4)(I + M^8)   (M strictly lower),
     // and stores T.  A matrix X enters a product as the A operand through the
     // accumulator of X^T and as the B operand through its own accumulator, so
-    // every product is formed together with the transpose the next one needs.
-    f32x4 tM, tMt;  // M and M^T of the chunk between the two parts
+    // every product in part B is formed together with the transpose the next
+    // one needs; the first transpose crosses the barrier between the parts in LDS.
+    f32x4 tM;  // M of the chunk between the two parts
+    float (*const mtile)[MTP] = sm.mt[role == R_T1 ? 1 : 0];
     auto inv_a_body = [&](int c) {
         const SlotT &sl = sm.slot[c % NS];
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acct = {0.f, 0.f, 0.f, 0.f};
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             s16x8 Af[NP], Bf[NP];
@@ -812,13 +816,12 @@ __global__ __launch_bounds__((kN / J / 16 + nprod<Tin>()) * 64) void wkv7_chunk_
                 Bf[pl] = lds8(&sl.X[OP_B][pl][m][32 * s + 8 * q]);
             }
             mma32<NP, NP>(acc, Af, Bf);           // lane (m, q): M[4 q + e][m]
-            mma32<NP, NP>(acct, Bf, Af);          // lane (m, q): M[m][4 q + e]
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int tau = 4 * q + e;
             tM[e] = m < tau ? acc[e] : 0.0f;      // M[tau][m]
-            tMt[e] = tau < m ? acct[e] : 0.0f;    // M^T[tau][m] = M[m][tau]
+            mtile[tau][m] = tM[e];
         }
     };
     auto inv_a = [&](int c) {
@@ -827,6 +830,8 @@ __global__ __launch_bounds__((kN / J / 16 + nprod<Tin>()) * 64) void wkv7_chunk_
     };
     auto inv_b_body = [&](int c) {
         SlotT &sl = sm.slot[c % NS];
+        // M^T[4 q + e][m] = M[m][4 q + e]: row m of the tile
+        const f32x4 tMt = *reinterpret_cast<const f32x4 *>(&mtile[m][4 * q]);
         f32x4 P = tM, Pt = tMt, Q, Qt;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
