@@ -415,20 +415,39 @@ __global__ __launch_bounds__((kN / J / 16 + nprod<Tin>()) * 64) void wkv7_chunk_
                 // product never accumulates onto a 16x16x32 one: the compiler inserts no
                 // wait states between the two shapes); R' S^ in one accumulator that the
                 // [M_rb | M_rk] product (the same shape) later continues
-                f32x4 ya = {0.f, 0.f, 0.f, 0.f}, oacc = {0.f, 0.f, 0.f, 0.f};
+                // V rows as a B operand over the token index (slot (q, e) = token 4 q + e)
+                s16x4 Vf[NPV];
+#pragma unroll
+                for (int pl = 0; pl < NPV; ++pl)
+                    Vf[pl] = pV[pl];
+                f32x4 ym = {0.f, 0.f, 0.f, 0.f}, ya = {0.f, 0.f, 0.f, 0.f}, oacc = {0.f, 0.f, 0.f, 0.f};
+                mma16<NP, NPV>(ym, Mak, Vf);
 #pragma unroll
                 for (int s = 0; s < 2; ++s)
                     mma32<NP, NP>(ya, pA[s], Bs[s]);
 #pragma unroll
                 for (int s = 0; s < 2; ++s)
                     mma32<NP, NP>(oacc, Rf[s], Bs[s]);
-                // V rows as a B operand over the token index (slot (q, e) = token 4 q + e)
-                s16x4 Vf[NPV];
+                // The LDS reads for the rest of the chunk are issued here, once the
+                // products above have taken A', R' and S^ out of their registers,
+                // so that they arrive while Z is formed (the fences keep the
+                // compiler from sinking them to their first use).
+                __builtin_amdgcn_sched_barrier(0);
+                // the state update's [B'^T | K'^T] fragments (key rows 16 pt ..)
+                s16x8 Uf[4][NP];
 #pragma unroll
-                for (int pl = 0; pl < NPV; ++pl)
-                    Vf[pl] = pV[pl];
-                f32x4 ym = {0.f, 0.f, 0.f, 0.f};
-                mma16<NP, NPV>(ym, Mak, Vf);
+                for (int pt = 0; pt < 4; ++pt) {
+                    const int ukey = key_slot(16 * pt + tcol);
+#pragma unroll
+                    for (int pl = 0; pl < NP; ++pl)
+                        Uf[pt][pl] = cat(tr4(&sl.X[OP_B][pl][trow][ukey]), tr4(&sl.X[OP_K][pl][trow][ukey]));
+                }
+                // [M_rb | M_rk] for the output
+                s16x8 Mf[NP];
+#pragma unroll
+                for (int pl = 0; pl < NP; ++pl)
+                    Mf[pl] = cat(tr4(&sl.Mt[MT_RB][pl][trow][mcol_t]), tr4(&sl.Mt[MT_RK][pl][trow][mcol_t]));
+                __builtin_amdgcn_sched_barrier(0);
                 // Z = T Y
                 f32x4 z = {0.f, 0.f, 0.f, 0.f};
                 {
@@ -439,16 +458,6 @@ __global__ __launch_bounds__((kN / J / 16 + nprod<Tin>()) * 64) void wkv7_chunk_
                     s16x4 Yf[NP];
                     split4<NP>(y4, Yf);
                     mma16<NP, NP>(z, Tf, Yf);
-                }
-                // the state update's [B'^T | K'^T] fragments (key rows 16 pt ..), read
-                // now so they arrive while Z, o and the stores are formed
-                s16x8 Uf[4][NP];
-#pragma unroll
-                for (int pt = 0; pt < 4; ++pt) {
-                    const int ukey = key_slot(16 * pt + tcol);
-#pragma unroll
-                    for (int pl = 0; pl < NP; ++pl)
-                        Uf[pt][pl] = cat(tr4(&sl.X[OP_B][pl][trow][ukey]), tr4(&sl.X[OP_K][pl][trow][ukey]));
                 }
                 // [Z ; V] as one B operand over 32 token slots: (q, e<4) is Z row 4q+e
                 // (this lane's z[e]), (q, e>=4) is V row 4q+e-4.
@@ -462,10 +471,6 @@ __global__ __launch_bounds__((kN / J / 16 + nprod<Tin>()) * 64) void wkv7_chunk_
                 }
                 // o = R' S^ + [M_rb | M_rk] [Z ; V]
                 {
-                    s16x8 Mf[NP];
-#pragma unroll
-                    for (int pl = 0; pl < NP; ++pl)
-                        Mf[pl] = cat(tr4(&sl.Mt[MT_RB][pl][trow][mcol_t]), tr4(&sl.Mt[MT_RK][pl][trow][mcol_t]));
                     mma32<NP, NP>(oacc, Mf, ZV);
                 }
                 {
