@@ -470,9 +470,21 @@ __global__ __launch_bounds__((kN / J / 16 + nprod<Tin>()) * 64) void wkv7_chunk_
                         ZV[pl] = cat(Zf[pl], pl < NPV ? Vf[pl < NPV ? pl : 0] : s16x4{0, 0, 0, 0});
                 }
                 // o = R' S^ + [M_rb | M_rk] [Z ; V]
-                {
-                    mma32<NP, NP>(oacc, Mf, ZV);
+                mma32<NP, NP>(oacc, Mf, ZV);
+                // S^ <- diag(f) (S^ + [B'^T | K'^T] [Z ; V]), one 16-row tile at a time;
+                // the [B'^T | K'^T] fragment of key rows 16 pt .. 16 pt + 15 comes from the
+                // row-major B' and K' planes by transpose loads.  The products go out
+                // before the output stores (a branch the compiler schedules nothing
+                // across), and the row factors are read behind them.
+                f32x4 acc[4], fv[4];
+#pragma unroll
+                for (int pt = 0; pt < 4; ++pt) {
+                    acc[pt] = f32x4{Sx[pt][0], Sx[pt][1], Sx[pt][2], Sx[pt][3]};
+                    mma32<NP, NP>(acc[pt], Uf[pt], ZV);
                 }
+#pragma unroll
+                for (int pt = 0; pt < 4; ++pt)
+                    fv[pt] = *reinterpret_cast<const f32x4 *>(&sl.f[16 * pt + 4 * q]);
                 {
                     // one uniform base per chunk, per-lane 32-bit offsets
                     Tout *const ob = go + row_of(t0) + jw;
@@ -487,18 +499,11 @@ __global__ __launch_bounds__((kN / J / 16 + nprod<Tin>()) * 64) void wkv7_chunk_
                                 store_o(ob, ooff[e], oacc[e]);
                     }
                 }
-                // S^ <- diag(f) (S^ + [B'^T | K'^T] [Z ; V]), one 16-row tile at a time;
-                // the [B'^T | K'^T] fragment of key rows 16 pt .. 16 pt + 15 comes from the
-                // row-major B' and K' planes by transpose loads.
 #pragma unroll
-                for (int pt = 0; pt < 4; ++pt) {
-                    f32x4 acc = {Sx[pt][0], Sx[pt][1], Sx[pt][2], Sx[pt][3]};
-                    mma32<NP, NP>(acc, Uf[pt], ZV);
-                    const f32x4 fv = *reinterpret_cast<const f32x4 *>(&sl.f[16 * pt + 4 * q]);
+                for (int pt = 0; pt < 4; ++pt)
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        Sx[pt][e] = acc[e] * fv[e];
-                }
+                        Sx[pt][e] = acc[pt][e] * fv[pt][e];
             }
             prefetch(i + 1);
             __builtin_amdgcn_s_barrier();
