@@ -400,14 +400,13 @@ __global__ __launch_bounds__((kN / J / 16 + nprod<Tin>()) * 64) void wkv7_chunk_
                 // k-step s is key row 16 (2 s + e/4) + 4 q + e%4, which this lane holds
                 // in Sx[2 s + e/4][e % 4].
                 s16x8 Bs[2][NP];
-#pragma unroll
-                for (int s = 0; s < 2; ++s) {
+                auto split_state = [&](int s) {
                     float v8[8];
 #pragma unroll
                     for (int e = 0; e < 8; ++e)
                         v8[e] = Sx[2 * s + e / 4][e & 3];
                     split8<NP>(v8, Bs[s]);
-                }
+                };
                 // A'-rows and R'-rows as A operands with the same key slots (stored
                 // contiguously, see key_slot); one accumulator per k-step.
                 // Y = A' S^ + M_ak V in accumulator layout (Y[4 q + e][col m]): A' S^ in
@@ -421,10 +420,21 @@ __global__ __launch_bounds__((kN / J / 16 + nprod<Tin>()) * 64) void wkv7_chunk_
                 for (int pl = 0; pl < NPV; ++pl)
                     Vf[pl] = pV[pl];
                 f32x4 ym = {0.f, 0.f, 0.f, 0.f}, ya = {0.f, 0.f, 0.f, 0.f}, oacc = {0.f, 0.f, 0.f, 0.f};
+                // The first k-step's products run while the second half of S^ is
+                // split: the scheduling groups interleave one product with a few
+                // elementwise instructions.
+                split_state(0);
+                __builtin_amdgcn_sched_barrier(0);
                 mma16<NP, NPV>(ym, Mak, Vf);
+                mma32<NP, NP>(ya, pA[0], Bs[0]);
+                split_state(1);
 #pragma unroll
-                for (int s = 0; s < 2; ++s)
-                    mma32<NP, NP>(ya, pA[s], Bs[s]);
+                for (int g = 0; g < 5; ++g) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one matrix-core product
+                    __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // then elementwise work
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                mma32<NP, NP>(ya, pA[1], Bs[1]);
 #pragma unroll
                 for (int s = 0; s < 2; ++s)
                     mma32<NP, NP>(oacc, Rf[s], Bs[s]);
