@@ -312,3 +312,47 @@ def test_nan_in_a_value_channel_stays_in_its_column(K, kernel):
     assert not (bad & ~mask).any(), "the NaN leaked out of its column, head or time range"
     assert torch.isnan(s[1, 2, :, j_nan]).all() and torch.isfinite(s[1, 2, :, :j_nan]).all()
     assert torch.isfinite(s[0]).all() and torch.isfinite(s[1, :2]).all()
+
+
+# --- element offsets beyond 32 bits ------------------------------------------------
+# Every (b, h) row of these inputs is one seeded head, with v scaled by a power of
+# two c[b, h] = 2^((b H + h) % 8 - 4).  With a zero input state the recurrence is
+# linear in v, and a power-of-two scale is exact in every floating-point step, so
+# each head's o and state must equal c[b, h] times those of head (0, 0) bit for
+# bit; an offset that wrapped at 32 bits would read a head of another scale.
+# Head (0, 0) itself is checked against the oracle.
+
+def _tiled_inputs(base, B, H):
+    T = base["r"].shape[1]
+    d = {}
+    for n in ("r", "w", "k", "v", "a", "b"):
+        x = torch.empty((B, T, H, 64), dtype=base[n].dtype, device="cuda")
+        x.copy_(base[n][0, :, 0, :].cuda()[None, :, None, :].expand(B, T, H, 64))
+        d[n] = x
+    idx = torch.arange(B * H, device="cuda").view(B, H)
+    c = torch.pow(2.0, (idx % 8 - 4).double()).float()
+    d["v"].mul_(c.view(B, 1, H, 1).to(d["v"].dtype))
+    d["state_in"] = None
+    return d, c
+
+
+@pytest.mark.parametrize("kernel,B,T,H", [("forward", 5, 65536, 256), ("step", 4100, 128, 128)])
+def test_offsets_beyond_32_bits(K, oracle_mod, kernel, B, T, H):
+    assert B * T * H * 64 > 2**32
+    base = synth.make_inputs(1, T, 1, seed=11, dtype="bf16", state_std=0.0)
+    d, c = _tiled_inputs(base, B, H)
+    o, s = gpu_run(K, d, kernel)
+    del d
+    c0 = c[0, 0].item()
+    o_ref, s_ref = oracle_run(oracle_mod, base)
+    check(o[0:1, :, 0:1].cpu() / c0, o_ref, TOL["bf16"], f"{kernel} B={B} T={T} H={H} head (0, 0) o")
+    check(s[0:1, 0:1].cpu() / c0, s_ref, TOL["bf16"], f"{kernel} B={B} T={T} H={H} head (0, 0) state")
+    o00, s00 = o[0, :, 0] / c0, s[0, 0] / c0
+    for bb, hh in [(B // 2, H // 3), (B - 2, 7), (B - 1, H - 1)]:
+        first = ((bb * T) * H + hh) * 64
+        cb = c[bb, hh].item()
+        assert torch.equal(o[bb, :, hh] / cb, o00), f"{kernel}: o of head ({bb}, {hh}) (offset {first}) differs"
+        assert torch.equal(s[bb, hh] / cb, s00), f"{kernel}: state of head ({bb}, {hh}) differs"
+        print(f"  head ({bb}, {hh}), first element offset {first}: o and state = {cb} x head (0, 0)", flush=True)
+    del o, s
+    torch.cuda.empty_cache()
