@@ -73,12 +73,27 @@ enum wkv7_dtype {
 enum wkv7_status {
     WKV7_OK = 0,
     WKV7_ERR_NULL = -1,        /* a required pointer is NULL                          */
-    WKV7_ERR_SHAPE = -2,       /* B, H < 1, T < 0, or a size overflows int64          */
+    WKV7_ERR_SHAPE = -2,       /* B, H < 1, T < 0, a size overflows int64, or a call
+                                  exceeds what one launch covers (WKV7_MAX_* below)   */
     WKV7_ERR_UNSUPPORTED = -3, /* N != 64, or an unknown dtype                         */
     WKV7_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned                     */
     WKV7_ERR_ALIAS = -5,       /* an output overlaps another buffer (see ALIASING)     */
     WKV7_ERR_HIP = -6          /* the HIP runtime refused a launch or a query          */
 };
+
+/*
+ * Size limits (WKV7_ERR_SHAPE beyond them).  Each head runs as one or a few
+ * workgroups of one launch, and a launch holds fewer than 2^32 threads:
+ *   B * H <= WKV7_MAX_HEADS_STEP   for wkv7_step, wkv7_step_tail, wkv7_state_commit,
+ *                                  and wkv7_forward[_varlen] with T < 9;
+ *   B * H <= WKV7_MAX_HEADS_CHUNK  for wkv7_forward[_varlen] with T >= 9;
+ *   B * T * H <= WKV7_MAX_ROWS_TAIL for wkv7_tmix_tail.
+ * Element offsets are 64-bit everywhere: tensors of more than 2^32 elements are
+ * supported within these limits.
+ */
+#define WKV7_MAX_HEADS_STEP 8000000
+#define WKV7_MAX_HEADS_CHUNK 4000000
+#define WKV7_MAX_ROWS_TAIL 200000000
 
 /*
  * wkv7_forward -- the parallel (prefill) pass over T tokens.

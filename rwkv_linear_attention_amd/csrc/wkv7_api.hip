@@ -34,12 +34,26 @@ bool overlap(const Range &x, const Range &y)
 bool misaligned(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
 
 // B*T*H*N*N must fit in int64 (and every partial product with it).
-bool shape_ok(int B, int T, int H, int64_t *tokens_out)
+// Largest B * H that one launch of a kernel covers.  A head is one workgroup of
+// the step kernel (up to 512 threads) or up to J workgroups of the chunked kernel
+// (up to 896 threads each, J = 1 beyond 128 heads), and a launch holds fewer than
+// 2^32 threads.
+constexpr int64_t kMaxHeadsStep = WKV7_MAX_HEADS_STEP;
+constexpr int64_t kMaxHeadsChunk = WKV7_MAX_HEADS_CHUNK;
+// Largest B * T * H of the time-mix tail pass (16 threads per row).
+constexpr int64_t kMaxRowsTail = WKV7_MAX_ROWS_TAIL;
+static_assert(kMaxHeadsStep * 512 < (1ll << 32) && kMaxHeadsChunk * 896 < (1ll << 32) &&
+                  kMaxRowsTail * 16 < (1ll << 32),
+              "a launch must hold fewer than 2^32 threads");
+
+bool shape_ok(int B, int T, int H, int64_t *tokens_out, int64_t max_heads = INT64_MAX)
 {
     if (B < 1 || H < 1 || T < 0)
         return false;
     const int64_t lim = INT64_MAX / (kN * kN * 8);
     const int64_t bh = static_cast<int64_t>(B) * H;
+    if (bh > max_heads)
+        return false;
     if (T > 0 && bh > lim / T)
         return false;
     *tokens_out = bh * T;
@@ -50,14 +64,16 @@ bool shape_ok(int B, int T, int H, int64_t *tokens_out)
 // per-position states and T > 0: the last of those is the final state).
 int check_seq(const void *r, const void *w, const void *k, const void *v, const void *a, const void *b,
               int in_dtype, const float *state_in, void *o, int o_dtype, float *state_out, float *state_pos,
-              int B, int T, int H, int N, bool out_optional = false)
+              int B, int T, int H, int N, bool out_optional = false, bool step_only = true)
 {
     int64_t tok = 0;
     if (N != kN)
         return WKV7_ERR_UNSUPPORTED;
     if ((in_dtype != WKV7_F32 && in_dtype != WKV7_BF16) || (o_dtype != WKV7_F32 && o_dtype != WKV7_BF16))
         return WKV7_ERR_UNSUPPORTED;
-    if (!shape_ok(B, T, H, &tok))
+    // the parallel pass routes T >= kChunkMinT to the chunked kernel
+    const int64_t max_heads = !step_only && T >= kChunkMinT ? kMaxHeadsChunk : kMaxHeadsStep;
+    if (!shape_ok(B, T, H, &tok, max_heads))
         return WKV7_ERR_SHAPE;
     if (!state_out && !(out_optional && state_pos && T > 0))
         return WKV7_ERR_NULL;
@@ -160,7 +176,8 @@ int wkv7_forward(const void *r, const void *w, const void *k, const void *v, con
                  int in_dtype, const float *state_in, void *o, int o_dtype, float *state_out, int B, int T,
                  int H, int N, void *stream)
 {
-    int st = check_seq(r, w, k, v, a, b, in_dtype, state_in, o, o_dtype, state_out, nullptr, B, T, H, N);
+    int st = check_seq(r, w, k, v, a, b, in_dtype, state_in, o, o_dtype, state_out, nullptr, B, T, H, N,
+                       false, false);
     if (st != WKV7_OK)
         return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -175,7 +192,8 @@ int wkv7_forward_varlen(const void *r, const void *w, const void *k, const void 
                         const void *b, int in_dtype, const float *state_in, void *o, int o_dtype,
                         float *state_out, const int *lengths, int B, int T, int H, int N, void *stream)
 {
-    int st = check_seq(r, w, k, v, a, b, in_dtype, state_in, o, o_dtype, state_out, nullptr, B, T, H, N);
+    int st = check_seq(r, w, k, v, a, b, in_dtype, state_in, o, o_dtype, state_out, nullptr, B, T, H, N,
+                       false, false);
     if (st != WKV7_OK)
         return st;
     if (!lengths)
@@ -272,7 +290,7 @@ int wkv7_tmix_tail(const void *o, int o_dtype, const void *r, const void *k, con
     for (int dt : dts)
         if (dt != WKV7_F32 && dt != WKV7_BF16)
             return WKV7_ERR_UNSUPPORTED;
-    if (!shape_ok(B, T, H, &tok))
+    if (!shape_ok(B, T, H, &tok) || tok > kMaxRowsTail)
         return WKV7_ERR_SHAPE;
     if (T > 0 && (!o || !r || !k || !v || !x))
         return WKV7_ERR_NULL;
@@ -312,7 +330,7 @@ int wkv7_state_commit(const float *state_pos, const int *accepted, const float *
     int64_t tok = 0;
     if (N != kN)
         return WKV7_ERR_UNSUPPORTED;
-    if (!shape_ok(B, T, H, &tok))
+    if (!shape_ok(B, T, H, &tok, kMaxHeadsStep))
         return WKV7_ERR_SHAPE;
     if (!accepted || !state_out || (T > 0 && !state_pos))
         return WKV7_ERR_NULL;

@@ -226,3 +226,23 @@ def test_state_out_needs_per_position_states(L):
     assert L.wkv7_step(*p, BF16, fake(7), fake(6), F32, None, None, 2, 5, 3, 64, None) == ERR_NULL
     assert L.wkv7_step(*p, BF16, fake(7), fake(6), F32, None, fake(9), 2, 0, 3, 64, None) == ERR_NULL
     assert L.wkv7_forward(*p, BF16, fake(7), fake(6), F32, None, 2, 8, 3, 64, None) == ERR_NULL
+
+
+def test_launch_size_limits(L):
+    # B * H beyond what one launch covers is refused on the host (the limits are
+    # the header's WKV7_MAX_* values); at the limit itself validation goes on
+    # (here to the overlap checks, which the fake addresses then fail).
+    max_step, max_chunk, max_rows = 8000000, 4000000, 200000000
+    assert fwd(L, B=max_chunk + 1, T=16, H=1) == ERR_SHAPE
+    assert fwd(L, B=2000, T=9, H=2001) == ERR_SHAPE
+    assert varlen(L, B=max_chunk + 1, T=16, H=1) == ERR_SHAPE
+    assert fwd(L, B=max_chunk, T=16, H=1) == ERR_ALIAS
+    # short sequences take the step kernel and its own limit
+    assert fwd(L, B=max_chunk + 1, T=8, H=1) == ERR_ALIAS
+    assert fwd(L, B=max_step + 1, T=8, H=1) == ERR_SHAPE
+    assert step(L, B=max_step + 1, T=5, H=1) == ERR_SHAPE
+    assert step(L, B=4000, T=5, H=2001) == ERR_SHAPE
+    assert step_tail(L, B=max_step + 1, T=1, H=1) == ERR_SHAPE
+    assert commit(L, B=max_step + 1, T=5, H=1) == ERR_SHAPE
+    assert tmix(L, B=1, T=max_rows + 1, H=1) == ERR_SHAPE
+    assert tmix(L, B=1, T=max_rows // 64 + 1, H=64) == ERR_SHAPE
