@@ -517,6 +517,10 @@ __global__ __launch_bounds__((kN / J / 16 + nprod<Tin>()) * 64) void wkv7_chunk_
             }
             prefetch(i + 1);
             __builtin_amdgcn_s_barrier();
+            // The barrier alone is not a memory operation to the compiler: this
+            // keeps it from moving or merging LDS reads across it (no instruction,
+            // and no wait for the reads in flight).
+            asm volatile("" ::: "memory");
         }
 #pragma unroll
         for (int pt = 0; pt < 4; ++pt)
