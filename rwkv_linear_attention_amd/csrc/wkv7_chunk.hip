@@ -33,20 +33,24 @@
 // MAPPING (gfx950).  One workgroup per (batch, head, block of NC value
 // columns); value columns evolve independently, so a head splits into
 // J = 64/NC blocks with no communication.  The workgroup is a software
-// pipeline with one barrier per chunk; in iteration i
+// pipeline with one barrier per chunk; in iteration i (fp32 inputs; the bf16
+// build runs one stage deeper, see the pipeline below)
 //  * consumer waves (NC/16 of them) each keep a 64x16 slice of the fp32 state
 //    in registers, in the accumulator layout of a 16x16 matrix-core tile, for
 //    the whole sequence, and run only the state-dependent products of chunk i;
-//  * three matrix waves build M_ab, M_ak, M_rb and M_rk of chunk i+1; the
-//    M_ab wave inverts I - M_ab by repeated squaring on the matrix cores,
+//  * the matrix waves build M_ab, M_ak, M_rb and M_rk of chunk i+1; the
+//    inverse wave inverts I - M_ab by repeated squaring on the matrix cores,
 //    T = (I + M)(I + M^2)(I + M^4)(I + M^8) (M is strictly lower triangular,
-//    so M^16 = 0), carrying each matrix and its transpose in registers;
+//    so M^16 = 0), carrying each matrix and its transpose in registers (the
+//    first transpose goes through LDS);
 //  * four scale waves form the decay-scaled operands A', R', B', K' (and the
 //    v rows) of chunk i+2, elementwise, from a table of decay factors;
-//  * one decay wave turns the w rows of chunk i+3 into that table.
+//  * a decay wave turns the w rows of chunk i+3 into that table.
+// With bf16 inputs two inverse waves and two decay waves take the even and the
+// odd chunks, each spreading one chunk's work over two iterations.
 // The decay and scale waves load their own input rows from HBM, in their own
-// lane layouts, two iterations ahead; rows past the end of the sequence count
-// as w = 1 and zero vectors.
+// lane layouts, two or more iterations ahead; rows past the end of the sequence
+// count as w = 1 and zero vectors.
 // Every operand that a product needs transposed is read with the gfx950 LDS
 // transpose load (ds_read_b64_tr_b16) from row-major storage, so no stage
 // writes a second, transposed copy.  All products run on
