@@ -88,6 +88,17 @@ def test_forward_column_blocks_and_tails(K, oracle_mod, B, H, T):
     check(s, s_ref, TOL["bf16"], f"forward B={B} H={H} T={T} state")
 
 
+@pytest.mark.parametrize("B,H", [(2, 50), (3, 50)])
+def test_forward_f32_inputs_column_blocks(K, oracle_mod, B, H):
+    # fp32 inputs build the chunked kernel with three bf16 pieces per operand and a
+    # shallower pipeline; B*H = 100 and 150 take 2 and 1 column blocks per head
+    inp = synth.make_inputs(B, 41, H, 64, seed=2500 + B * H, dtype="f32", state_std=0.1)
+    o_ref, s_ref = oracle_run(oracle_mod, inp)
+    o, s = gpu_run(K, to_dev(inp), "forward")
+    check(o, o_ref, TOL["f32"], f"forward f32 B={B} H={H} o")
+    check(s, s_ref, TOL["f32"], f"forward f32 B={B} H={H} state")
+
+
 @pytest.mark.parametrize("kernel", ["step", "forward"])
 def test_zero_state_in_is_null_state(K, oracle_mod, kernel):
     inp = synth.make_inputs(2, 40, 4, 64, seed=31, dtype="bf16", state_std=0.0)
