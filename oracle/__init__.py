@@ -6,7 +6,9 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 the GPU library: the two share no code.
 
 ``forward`` wraps the plain C loop in ``wkv7_oracle.c`` (fp64, sums in
-ascending key order, no fused multiply-adds).  Its header comment names the
+ascending key order, no fused multiply-adds).  ``backward`` is the plain
+reverse-mode adjoint of that loop in numpy fp64, pinned by finite differences
+of ``forward``.  Its header comment names the
 passages of the pages it follows: the "WKV-7 Kernel (Generalized Delta Rule)"
 section of the RWKV-X Architecture page and section 1 of the Core AI RWKV-7
 note.  Every value it returns is fp64.
@@ -184,3 +186,54 @@ def tmix_tail(o, r, k, v, g, r_k, ln_w, ln_b, eps):
                 bonus = (r[bb, t, h] * k[bb, t, h] * r_k[h]).sum()
                 x[bb, t, h] = (y + bonus * v[bb, t, h]) * g[bb, t, h]
     return x
+
+
+def backward(r, w, k, v, a, b, state_in=None, d_o=None, d_state_out=None):
+    """Gradients of the recurrence (fp64): the adjoint of ``forward``'s loop.
+
+    The SwiftRWKV Inference guide (its `.rwkvq` backend section) keeps a
+    trainable WKV kernel whose backward pass rebuilds the state chunk by chunk;
+    the pages give no formulas.  This is the plain reverse-mode adjoint of the
+    recurrence of the RWKV-X Architecture page ("WKV-7 Kernel (Generalized
+    Delta Rule)"),
+        S_t = diag(w_t) S_{t-1} + b_t (a_t^T S_{t-1}) + k_t v_t^T,   o_t = S_t^T r_t,
+    for a loss L with dL/do_t = d_o[t] and dL/dS_T = d_state_out.  With G the
+    gradient of L with respect to S_t (rows = key channels), going backward in t:
+        G    += r_t d_o_t^T
+        dr_t  = S_t d_o_t            dk_t = G v_t            dv_t = G^T k_t
+        dw_t  = rowsum(G * S_{t-1})  db_t = G (S_{t-1}^T a_t)
+        c     = G^T b_t              da_t = S_{t-1} c
+        G     = diag(w_t) G + a_t c^T            (the gradient for S_{t-1})
+    and finally d_state_in = G.  The states S_t come from ``forward``.
+    Inputs as for ``forward`` (fp64 carriers are taken as given); d_o [B,T,H,N]
+    or None (zeros), d_state_out [B,H,N,N] or None (zeros).  Returns a dict of
+    fp64 arrays dr, dw, dk, dv, da, db [B,T,H,N] and d_state_in [B,H,N,N].
+    """
+    f = lambda x: _as_input(x, np.float64)
+    r, w, k, v, a, b = (f(x) for x in (r, w, k, v, a, b))
+    B, T, H, N = r.shape
+    s0 = np.zeros((B, H, N, N)) if state_in is None else f(state_in)
+    _, _, s_pos = forward(r, w, k, v, a, b, s0, per_position=True, f64_inputs=True)
+    g_o = np.zeros((B, T, H, N)) if d_o is None else f(d_o)
+    out = {n: np.zeros((B, T, H, N)) for n in ("dr", "dw", "dk", "dv", "da", "db")}
+    d_s0 = np.zeros((B, H, N, N))
+    for bb in range(B):
+        for h in range(H):
+            G = np.zeros((N, N)) if d_state_out is None else f(d_state_out)[bb, h].copy()
+            for t in range(T - 1, -1, -1):
+                S = s_pos[bb, t, h]
+                Sp = s_pos[bb, t - 1, h] if t > 0 else s0[bb, h]
+                rt, wt, kt, vt, at, bt = (x[bb, t, h] for x in (r, w, k, v, a, b))
+                do = g_o[bb, t, h]
+                G = G + np.outer(rt, do)
+                out["dr"][bb, t, h] = S @ do
+                out["dk"][bb, t, h] = G @ vt
+                out["dv"][bb, t, h] = G.T @ kt
+                out["dw"][bb, t, h] = (G * Sp).sum(axis=1)
+                out["db"][bb, t, h] = G @ (Sp.T @ at)
+                c = G.T @ bt
+                out["da"][bb, t, h] = Sp @ c
+                G = wt[:, None] * G + np.outer(at, c)
+            d_s0[bb, h] = G
+    out["d_state_in"] = d_s0
+    return out

@@ -5,6 +5,8 @@ determine: a hand-worked example, closed forms of special cases (linear
 attention, pure decay, projection / delta-rule recall), exact rational
 arithmetic, a dense matrix brute force, the chunked-parallel form, split-T state
 carry, linearity and value-column separability, and the zero / empty cases.
+The gradients (``backward``) are pinned by central finite differences of the
+forward oracle, the closed form of linear attention, and causality.
 A dropped term, a wrong sign, a transposed state or an off-by-one in time
 fails at least one of them.
 """
@@ -395,3 +397,94 @@ def test_tail_gate_and_head_parameters(oracle_mod):
     x2 = oracle_mod.tmix_tail(o, r, k, v, g, r_k, ln_w, ln_b2, 1e-4)
     np.testing.assert_allclose(x2[:, :, 0], xg[:, :, 0], rtol=0, atol=0)
     np.testing.assert_allclose(x2[:, :, 1], xg[:, :, 1] + g[:, :, 1], rtol=1e-12)
+
+
+# --- the backward pass (gradients of the recurrence) ----------------------------
+
+def _loss_and_grads(oracle_mod, x, s0, go, gs):
+    """L = sum(o * go) + sum(S_T * gs) through the forward oracle, and the adjoint."""
+    def L(xx, s):
+        o, st = oracle_mod.forward(*(xx[n] for n in "rwkvab"), s, f64_inputs=True)
+        return float((o * go).sum() + (st * gs).sum())
+    g = oracle_mod.backward(*(x[n] for n in "rwkvab"), s0, go, gs)
+    return L, g
+
+
+def _rand_inputs(rng, B, T, H, N):
+    x = {n: rng.standard_normal((B, T, H, N)) for n in "rkv"}
+    kk = x["k"] / np.linalg.norm(x["k"], axis=-1, keepdims=True)
+    x["a"] = -kk
+    x["b"] = kk / (1 + np.exp(-rng.standard_normal((B, T, H, N))))
+    x["w"] = np.exp(-0.6065306597 / (1 + np.exp(-rng.standard_normal((B, T, H, N)))))
+    return x
+
+
+@pytest.mark.parametrize("B,T,H", [(1, 9, 1), (2, 5, 3)])
+def test_backward_matches_finite_differences(oracle_mod, B, T, H):
+    # central differences of the (separately pinned) forward oracle along random
+    # directions, one per input; fp64 makes them good to ~1e-8
+    rng = np.random.default_rng(40 + T)
+    N = 64
+    x = _rand_inputs(rng, B, T, H, N)
+    s0 = 0.2 * rng.standard_normal((B, H, N, N))
+    go = rng.standard_normal((B, T, H, N))
+    gs = rng.standard_normal((B, H, N, N))
+    L, g = _loss_and_grads(oracle_mod, x, s0, go, gs)
+    eps = 1e-6
+    for n in "rwkvab":
+        u = rng.standard_normal((B, T, H, N))
+        xp, xm = dict(x), dict(x)
+        xp[n], xm[n] = x[n] + eps * u, x[n] - eps * u
+        fd = (L(xp, s0) - L(xm, s0)) / (2 * eps)
+        an = float((g["d" + n] * u).sum())
+        assert abs(fd - an) <= 1e-6 * max(abs(an), 1.0), (n, fd, an)
+    u = rng.standard_normal((B, H, N, N))
+    fd = (L(x, s0 + eps * u) - L(x, s0 - eps * u)) / (2 * eps)
+    an = float((g["d_state_in"] * u).sum())
+    assert abs(fd - an) <= 1e-6 * max(abs(an), 1.0), ("state_in", fd, an)
+
+
+def test_backward_linear_attention_closed_form(oracle_mod):
+    # a = b = 0, w = 1: S_t = S_0 + sum_{s<=t} k_s v_s^T, and with
+    # G_t = GS + sum_{t'>=t} r_t' do_t'^T the gradients are
+    # dr_t = S_t do_t, dk_t = G_t v_t, dv_t = G_t^T k_t, dw_t = rowsum(G_t * S_{t-1}),
+    # and d_state_in = G_0
+    rng = np.random.default_rng(44)
+    T, N = 11, 64
+    r, k, v, do = (rng.standard_normal((T, N)) for _ in range(4))
+    S0 = rng.standard_normal((N, N))
+    GS = rng.standard_normal((N, N))
+    z = np.zeros((T, N))
+    ex = lambda m: m[None, :, None, :]
+    g = oracle_mod.backward(ex(r), ex(np.ones((T, N))), ex(k), ex(v), ex(z), ex(z), S0[None, None],
+                            ex(do), GS[None, None])
+    S = [S0]
+    for t in range(T):
+        S.append(S[-1] + np.outer(k[t], v[t]))
+    G = [GS + sum(np.outer(r[u], do[u]) for u in range(t, T)) for t in range(T)]
+    get = lambda n: g[n][0, :, 0, :]
+    assert _rel(get("dr"), np.array([S[t + 1] @ do[t] for t in range(T)])) < 1e-12
+    assert _rel(get("dk"), np.array([G[t] @ v[t] for t in range(T)])) < 1e-12
+    assert _rel(get("dv"), np.array([G[t].T @ k[t] for t in range(T)])) < 1e-12
+    assert _rel(get("dw"), np.array([(G[t] * S[t]).sum(axis=1) for t in range(T)])) < 1e-12
+    assert _rel(g["d_state_in"][0, 0], G[0]) < 1e-12
+    # a = b = 0 still has gradients: db_t = G_t S_{t-1}^T a_t = 0 and da_t = S_{t-1} G_t^T b_t = 0
+    assert not np.any(get("da")) and not np.any(get("db"))
+
+
+def test_backward_is_causal(oracle_mod):
+    # with no gradient after token t0 (and none on the final state), every input
+    # gradient after t0 is zero, and those up to t0 do not change
+    rng = np.random.default_rng(45)
+    B, T, H, N, t0 = 1, 8, 2, 64, 4
+    x = _rand_inputs(rng, B, T, H, N)
+    s0 = 0.2 * rng.standard_normal((B, H, N, N))
+    go = rng.standard_normal((B, T, H, N))
+    go[:, t0 + 1:] = 0.0
+    g = oracle_mod.backward(*(x[n] for n in "rwkvab"), s0, go, None)
+    short = {n: x[n][:, :t0 + 1] for n in x}
+    gs = oracle_mod.backward(*(short[n] for n in "rwkvab"), s0, go[:, :t0 + 1], None)
+    for n in ("dr", "dw", "dk", "dv", "da", "db"):
+        assert not np.any(g[n][:, t0 + 1:]), n
+        assert _rel(g[n][:, :t0 + 1], gs[n]) < 1e-13, n
+    assert _rel(g["d_state_in"], gs["d_state_in"]) < 1e-13
