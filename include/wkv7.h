@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define WKV7_ABI_VERSION 3
+#define WKV7_ABI_VERSION 4
 
 /* Element types of r, w, k, v, a, b (in_dtype) and of o (o_dtype). */
 enum wkv7_dtype {
@@ -84,7 +84,7 @@ enum wkv7_status {
 /*
  * Size limits (WKV7_ERR_SHAPE beyond them).  Each head runs as one or a few
  * workgroups of one launch, and a launch holds fewer than 2^32 threads:
- *   B * H <= WKV7_MAX_HEADS_STEP   for wkv7_step, wkv7_step_tail, wkv7_state_commit,
+ *   B * H <= WKV7_MAX_HEADS_STEP   for wkv7_step, wkv7_step_tail, wkv7_state_commit, wkv7_backward,
  *                                  and wkv7_forward[_varlen] with T < 9;
  *   B * H <= WKV7_MAX_HEADS_CHUNK  for wkv7_forward[_varlen] with T >= 9;
  *   B * T * H <= WKV7_MAX_ROWS_TAIL for wkv7_tmix_tail.
@@ -229,6 +229,32 @@ int wkv7_tmix_tail(const void *o, int o_dtype, const void *r, const void *k, con
  */
 int wkv7_state_commit(const float *state_pos, const int *accepted, const float *state_in,
                       float *state_out, int B, int T, int H, int N, void *stream);
+
+/*
+ * wkv7_backward -- gradients of the recurrence (the backward pass of a trainable
+ * WKV layer; the SwiftRWKV Inference guide, its `.rwkvq` backend section, keeps
+ * such a kernel).  For a loss L with dL/do = d_o and dL/dS_T = d_state_out it
+ * returns dL/d(r, w, k, v, a, b) and dL/d(state_in): the reverse-mode adjoint of
+ * the loop of wkv7_forward (RWKV-X Architecture page, section "WKV-7 Kernel
+ * (Generalized Delta Rule)").
+ *
+ *   r, w, k, v, a, b : [B,T,H,N] inputs of the forward pass, of in_dtype.
+ *   state_in    : [B,H,N,N] fp32 state before token 0, or NULL (zeros).
+ *   state_pos   : [B,T,H,N,N] fp32, the state after each token, as wkv7_step
+ *                 writes it (these are read, not rebuilt).
+ *   d_o         : [B,T,H,N] fp32 gradient of o.
+ *   d_state_out : [B,H,N,N] fp32 gradient of the final state, or NULL (zeros).
+ *   dr .. db    : [B,T,H,N] fp32 gradients of the six inputs.
+ *   d_state_in  : [B,H,N,N] fp32 gradient of state_in; may equal d_state_out.
+ * The inputs may be NULL when T = 0 (then d_state_in becomes d_state_out, or
+ * zeros).  No output may overlap another buffer, except d_state_in ==
+ * d_state_out.  B * H <= WKV7_MAX_HEADS_STEP.
+ */
+int wkv7_backward(const void *r, const void *w, const void *k, const void *v,
+                  const void *a, const void *b, int in_dtype, const float *state_in,
+                  const float *state_pos, const float *d_o, const float *d_state_out,
+                  float *dr, float *dw, float *dk, float *dv, float *da, float *db,
+                  float *d_state_in, int B, int T, int H, int N, void *stream);
 
 /* A static, human-readable name for a status code (never NULL). */
 const char *wkv7_status_string(int status);

@@ -22,6 +22,9 @@ Functions (names as in the C ABI):
 * ``wkv7_state_commit(state_pos, accepted, state_in=None)`` -> ``state_out``: the state
   after each row's accepted prefix of a speculative verify step.
 * ``wkv7_state_reset(state, row_mask=None)``: zero the state (all rows or masked ones).
+* ``wkv7_backward(r, w, k, v, a, b, state_in, state_pos, d_o, d_state_out=None)`` -> a dict of
+  the gradients ``dr, dw, dk, dv, da, db`` and ``d_state_in`` (fp32), given the
+  per-position states of the forward pass.
 
 Tensors: r, w, k, v, a, b are [B, T, H, 64] bf16 or fp32 on the GPU; the
 state is [B, H, 64, 64] fp32 with row i a key channel and column j a value
@@ -79,6 +82,8 @@ def lib():
         L.wkv7_tmix_tail.argtypes = [vp, ci, vp, vp, vp, vp, ci, vp, vp, vp, cf, vp, ci, ci, ci, ci, ci, vp]
         L.wkv7_tmix_tail.restype = ci
         L.wkv7_state_reset.argtypes = [vp, ci, ci, ci, vp, vp]
+        L.wkv7_backward.argtypes = [vp] * 6 + [ci] + [vp] * 11 + [ci, ci, ci, ci, vp]
+        L.wkv7_backward.restype = ci
         L.wkv7_state_reset.restype = ci
         L.wkv7_status_string.argtypes = [ci]
         L.wkv7_status_string.restype = ctypes.c_char_p
@@ -275,6 +280,41 @@ def wkv7_state_commit(state_pos, accepted, state_in=None, *, state_out=None):
     _check(lib().wkv7_state_commit(_ptr(state_pos), _ptr(accepted), _ptr(state_in), _ptr(state_out),
                                    B, T, H, N, _stream(dev)))
     return state_out
+
+
+def wkv7_backward(r, w, k, v, a, b, state_in, state_pos, d_o, d_state_out=None, *, grads=None):
+    """Gradients of the recurrence: the backward pass of wkv7_forward.
+
+    state_pos: [B, T, H, N, N] fp32, the state after each token (wkv7_step with
+    per_position=True writes it); d_o: [B, T, H, N] fp32, the gradient of o;
+    d_state_out: [B, H, N, N] fp32 gradient of the final state, or None (zeros).
+    Returns a dict with dr, dw, dk, dv, da, db ([B, T, H, N] fp32) and d_state_in
+    ([B, H, N, N] fp32); ``grads`` may pass that dict preallocated.
+    """
+    B, T, H, N = _check_inputs(r, w, k, v, a, b)
+    dev = r.device
+    state_in = _state_arg(state_in, B, H, N, dev, "state_in")
+    d_state_out = _state_arg(d_state_out, B, H, N, dev, "d_state_out")
+    if (state_pos.dtype != torch.float32 or tuple(state_pos.shape) != (B, T, H, N, N)
+            or not state_pos.is_contiguous() or state_pos.device != dev):
+        raise ValueError(f"state_pos must be a contiguous fp32 [{B}, {T}, {H}, {N}, {N}] tensor on {dev}")
+    if (d_o.dtype != torch.float32 or tuple(d_o.shape) != (B, T, H, N) or not d_o.is_contiguous()
+            or d_o.device != dev):
+        raise ValueError(f"d_o must be a contiguous fp32 [{B}, {T}, {H}, {N}] tensor on {dev}")
+    names = ("dr", "dw", "dk", "dv", "da", "db")
+    if grads is None:
+        grads = {n: torch.empty((B, T, H, N), dtype=torch.float32, device=dev) for n in names}
+        grads["d_state_in"] = torch.empty((B, H, N, N), dtype=torch.float32, device=dev)
+    for n in names:
+        g = grads[n]
+        if g.dtype != torch.float32 or tuple(g.shape) != (B, T, H, N) or not g.is_contiguous() or g.device != dev:
+            raise ValueError(f"{n} must be a contiguous fp32 [{B}, {T}, {H}, {N}] tensor on {dev}")
+    _state_arg(grads["d_state_in"], B, H, N, dev, "d_state_in")
+    _check(lib().wkv7_backward(*[_ptr(x) for x in (r, w, k, v, a, b)], _dt(r), _ptr(state_in),
+                               _ptr(state_pos), _ptr(d_o), _ptr(d_state_out),
+                               *[_ptr(grads[n]) for n in names], _ptr(grads["d_state_in"]),
+                               B, T, H, N, _stream(dev)))
+    return grads
 
 
 def wkv7_state_reset(state, row_mask=None):

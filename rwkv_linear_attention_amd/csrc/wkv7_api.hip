@@ -356,6 +356,74 @@ int wkv7_state_commit(const float *state_pos, const int *accepted, const float *
                : WKV7_ERR_HIP;
 }
 
+int wkv7_backward(const void *r, const void *w, const void *k, const void *v, const void *a, const void *b,
+                  int in_dtype, const float *state_in, const float *state_pos, const float *d_o,
+                  const float *d_state_out, float *dr, float *dw, float *dk, float *dv, float *da, float *db,
+                  float *d_state_in, int B, int T, int H, int N, void *stream)
+{
+    int64_t tok = 0;
+    if (N != kN)
+        return WKV7_ERR_UNSUPPORTED;
+    if (in_dtype != WKV7_F32 && in_dtype != WKV7_BF16)
+        return WKV7_ERR_UNSUPPORTED;
+    if (!shape_ok(B, T, H, &tok, kMaxHeadsStep))
+        return WKV7_ERR_SHAPE;
+    if (!d_state_in)
+        return WKV7_ERR_NULL;
+    const void *ins[] = {r, w, k, v, a, b, state_pos, d_o};
+    float *const grads[] = {dr, dw, dk, dv, da, db};
+    if (T > 0) {
+        for (const void *ptr : ins)
+            if (!ptr)
+                return WKV7_ERR_NULL;
+        for (const float *ptr : grads)
+            if (!ptr)
+                return WKV7_ERR_NULL;
+    }
+    const void *all[] = {r, w, k, v, a, b, state_in, state_pos, d_o, d_state_out,
+                         dr, dw, dk, dv, da, db, d_state_in};
+    for (const void *ptr : all)
+        if (ptr && misaligned(ptr))
+            return WKV7_ERR_ALIGN;
+    // every output overlaps nothing else (d_state_in may be d_state_out itself)
+    const int64_t ein = in_dtype == WKV7_BF16 ? 2 : 4;
+    const int64_t vec = tok * kN, st_bytes = static_cast<int64_t>(B) * H * kN * kN * 4;
+    Range in_r[10];
+    int n_in = 0;
+    if (T > 0) {
+        for (int q = 0; q < 6; ++q)
+            in_r[n_in++] = range_of(ins[q], vec * ein);
+        in_r[n_in++] = range_of(state_pos, vec * kN * 4);
+        in_r[n_in++] = range_of(d_o, vec * 4);
+    }
+    if (state_in)
+        in_r[n_in++] = range_of(state_in, st_bytes);
+    const Range r_dsi = range_of(d_state_in, st_bytes);
+    Range out_r[7];
+    int n_out = 0;
+    if (T > 0)
+        for (const float *ptr : grads)
+            out_r[n_out++] = range_of(ptr, vec * 4);
+    out_r[n_out++] = r_dsi;
+    for (int x = 0; x < n_out; ++x) {
+        for (int y = 0; y < n_in; ++y)
+            if (overlap(out_r[x], in_r[y]))
+                return WKV7_ERR_ALIAS;
+        for (int y = x + 1; y < n_out; ++y)
+            if (overlap(out_r[x], out_r[y]))
+                return WKV7_ERR_ALIAS;
+    }
+    if (d_state_out && d_state_out != d_state_in && overlap(r_dsi, range_of(d_state_out, st_bytes)))
+        return WKV7_ERR_ALIAS;
+    wkv7::BwdArgs p{};
+    p.r = r; p.w = w; p.k = k; p.v = v; p.a = a; p.b = b;
+    p.state_in = state_in; p.state_pos = state_pos; p.d_o = d_o; p.d_state_out = d_state_out;
+    p.dr = dr; p.dw = dw; p.dk = dk; p.dv = dv; p.da = da; p.db = db; p.d_state_in = d_state_in;
+    p.B = B; p.T = T; p.H = H;
+    p.in_bf16 = in_dtype == WKV7_BF16;
+    return wkv7::launch_backward(p, static_cast<hipStream_t>(stream)) == hipSuccess ? WKV7_OK : WKV7_ERR_HIP;
+}
+
 const char *wkv7_status_string(int status)
 {
     switch (status) {

@@ -1,0 +1,228 @@
+// wkv7_bwd.hip -- the backward pass of the WKV-7 recurrence (gradients).
+//
+// The SwiftRWKV Inference guide (its `.rwkvq` backend section) keeps a trainable
+// WKV kernel whose backward pass rebuilds the state chunk by chunk.  The
+// recurrence (RWKV-X Architecture page, section "WKV-7 Kernel (Generalized Delta
+// Rule)") is
+//     S_t = diag(w_t) S_{t-1} + b_t (a_t^T S_{t-1}) + k_t v_t^T,   o_t = S_t^T r_t.
+// Its reverse-mode adjoint, with G the gradient with respect to S_t (G starts
+// as the gradient of the final state), runs backward in t:
+//     G    += r_t do_t^T
+//     dr_t  = S_t do_t            dk_t = G v_t             dv_t = G^T k_t
+//     dw_t  = rowsum(G * S_{t-1}) db_t = G (S_{t-1}^T a_t)
+//     c     = G^T b_t             da_t = S_{t-1} c
+//     G     = diag(w_t) G + a_t c^T
+// and the gradient of the input state is the last G.  The states S_t are an
+// input (the per-position states the step kernel writes), so nothing is
+// rebuilt: with 288 GB of HBM the states of long sequences fit.
+//
+// MAPPING (gfx950).  One workgroup of four waves per (batch, head).  Lane i of
+// every wave is key row i; wave g keeps the 16 value columns 16 g .. 16 g + 15
+// of G, S_t and S_{t-1} in registers.
+//  * Sums over the value columns (dr, dk, dw, db, da) are a 16-term sum in each
+//    lane and a sum of the four waves' partials through LDS (one barrier per
+//    token, double-buffered).
+//  * Sums over the key rows (c, S_{t-1}^T a, dv) stay inside a wave: the lanes
+//    write their 16 terms to LDS, and lane (jj, rb) adds column jj over rows
+//    16 rb .. 16 rb + 15, stored so that the two row blocks read together fall
+//    in different banks, before two lane exchanges finish the sum.
+// All arithmetic is fp32; gradients are written as fp32.
+#include "wkv7_device.h"
+#include "wkv7_launch.h"
+
+namespace wkv7 {
+namespace {
+
+constexpr int NWB = 4;               // waves per head
+constexpr int CW = kN / NWB;         // value columns per wave (16)
+
+struct alignas(16) BwdSmem {
+    float x[NWB][3][kN][CW];          // per-wave column-sum terms, row i at xrow(i)
+    float part[2][5][NWB][kN];        // per-wave row partials: dr, dk, dw, db, da
+    float bc[NWB][2][CW];             // per-wave column sums c and S_{t-1}^T a, broadcast
+};
+
+// Storage row of key row i in x: adjacent rows swap in odd blocks of 16, so the
+// 32 lanes that read rows r and 16 + r together (4-byte reads, 32 banks, rows of
+// 64 bytes) find them in opposite halves of the banks.
+__device__ __forceinline__ int xrow(int i) { return i ^ ((i >> 4) & 1); }
+
+template <typename Tin, bool HAS_STATE_IN, bool HAS_DOUT>
+__global__ __launch_bounds__(NWB * 64) void wkv7_bwd_kernel(BwdArgs p)
+{
+    __shared__ BwdSmem sm;
+    const int i = threadIdx.x & 63;                                   // key row of this lane
+    const int g = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // column block of this wave
+    const int j0 = g * CW;
+    const int bh = blockIdx.x;
+    const int H = p.H, T = p.T;
+    const int bb = bh / H, hh = bh - bb * H;
+    const Tin *__restrict__ r = static_cast<const Tin *>(p.r);
+    const Tin *__restrict__ w = static_cast<const Tin *>(p.w);
+    const Tin *__restrict__ k = static_cast<const Tin *>(p.k);
+    const Tin *__restrict__ v = static_cast<const Tin *>(p.v);
+    const Tin *__restrict__ a = static_cast<const Tin *>(p.a);
+    const Tin *__restrict__ b = static_cast<const Tin *>(p.b);
+    const size_t sbase = static_cast<size_t>(bh) * (kN * kN) + static_cast<size_t>(i) * kN + j0;
+    // element (b, t, h, 0) of the [B, T, H, N] tensors, and (b, t, h, 0, 0) of state_pos
+    auto vec0 = [&](int t) { return (static_cast<size_t>(bb) * T + t) * H + hh; };
+
+    float G[CW], St[CW], Sp[CW];
+#pragma unroll
+    for (int jj = 0; jj < CW; ++jj)
+        G[jj] = HAS_DOUT ? p.d_state_out[sbase + jj] : 0.0f;
+    if (T > 0) {
+        const float *src = p.state_pos + vec0(T - 1) * (kN * kN) + static_cast<size_t>(i) * kN + j0;
+#pragma unroll
+        for (int jj = 0; jj < CW; jj += 4) {
+            const f32x4 x4 = *reinterpret_cast<const f32x4 *>(src + jj);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                St[jj + e] = x4[e];
+        }
+    }
+    // lane roles in the column sums: column jj_l of this wave, rows 16 rb .. 16 rb + 15
+    const int jj_l = i & 15, rb = i >> 4;
+
+    for (int t = T - 1; t >= 0; --t) {
+        const size_t e0 = vec0(t) * kN;
+        const float ri = load_elem(r, e0 + i), wi = load_elem(w, e0 + i), ki = load_elem(k, e0 + i);
+        const float ai = load_elem(a, e0 + i), bi = load_elem(b, e0 + i);
+        float dO[CW], vv[CW];
+#pragma unroll
+        for (int jj = 0; jj < CW; ++jj) {
+            dO[jj] = p.d_o[e0 + j0 + jj];
+            vv[jj] = load_elem(v, e0 + j0 + jj);
+        }
+        // S_{t-1}: the state after token t-1, or the input state
+        if (t > 0) {
+            const float *src = p.state_pos + vec0(t - 1) * (kN * kN) + static_cast<size_t>(i) * kN + j0;
+#pragma unroll
+            for (int jj = 0; jj < CW; jj += 4) {
+                const f32x4 x4 = *reinterpret_cast<const f32x4 *>(src + jj);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    Sp[jj + e] = x4[e];
+            }
+        } else {
+#pragma unroll
+            for (int jj = 0; jj < CW; ++jj)
+                Sp[jj] = HAS_STATE_IN ? p.state_in[sbase + jj] : 0.0f;
+        }
+
+        // G += r_t do_t^T, then the row partials that need only G, S_t, S_{t-1}
+        float p_dr = 0.f, p_dk = 0.f, p_dw = 0.f;
+#pragma unroll
+        for (int jj = 0; jj < CW; ++jj) {
+            G[jj] += ri * dO[jj];
+            p_dr += St[jj] * dO[jj];
+            p_dk += G[jj] * vv[jj];
+            p_dw += G[jj] * Sp[jj];
+        }
+
+        // column sums over the 64 key rows: c = G^T b, sa = S_{t-1}^T a, dv = G^T k
+        float (*xw)[kN][CW] = sm.x[g];
+#pragma unroll
+        for (int jj = 0; jj < CW; jj += 4) {
+            f32x4 xc, xs, xv;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                xc[e] = bi * G[jj + e];
+                xs[e] = ai * Sp[jj + e];
+                xv[e] = ki * G[jj + e];
+            }
+            *reinterpret_cast<f32x4 *>(&xw[0][xrow(i)][jj]) = xc;
+            *reinterpret_cast<f32x4 *>(&xw[1][xrow(i)][jj]) = xs;
+            *reinterpret_cast<f32x4 *>(&xw[2][xrow(i)][jj]) = xv;
+        }
+        float cs[3] = {0.f, 0.f, 0.f};
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+            const int row = xrow(16 * rb + rr);
+#pragma unroll
+            for (int qn = 0; qn < 3; ++qn)
+                cs[qn] += xw[qn][row][jj_l];
+        }
+#pragma unroll
+        for (int qn = 0; qn < 3; ++qn) {
+            cs[qn] += __shfl_xor(cs[qn], 16);
+            cs[qn] += __shfl_xor(cs[qn], 32);
+        }
+        // lanes 0..15 hold column jj = lane: dv out, c and sa broadcast through LDS
+        if (i < 16) {
+            p.dv[e0 + j0 + i] = cs[2];
+            sm.bc[g][0][i] = cs[0];
+            sm.bc[g][1][i] = cs[1];
+        }
+        float c[CW], sa[CW];
+#pragma unroll
+        for (int jj = 0; jj < CW; jj += 4) {
+            const f32x4 c4 = *reinterpret_cast<const f32x4 *>(&sm.bc[g][0][jj]);
+            const f32x4 s4 = *reinterpret_cast<const f32x4 *>(&sm.bc[g][1][jj]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                c[jj + e] = c4[e];
+                sa[jj + e] = s4[e];
+            }
+        }
+
+        // row partials that need c and sa, then G for the previous token
+        float p_db = 0.f, p_da = 0.f;
+#pragma unroll
+        for (int jj = 0; jj < CW; ++jj) {
+            p_db += G[jj] * sa[jj];
+            p_da += Sp[jj] * c[jj];
+            G[jj] = wi * G[jj] + ai * c[jj];
+            St[jj] = Sp[jj];
+        }
+
+        // the four waves' row partials: written, one barrier, then wave q (q < 5,
+        // wave 0 takes two) sums quantity q for all 64 rows
+        const int pb = t & 1;
+        sm.part[pb][0][g][i] = p_dr;
+        sm.part[pb][1][g][i] = p_dk;
+        sm.part[pb][2][g][i] = p_dw;
+        sm.part[pb][3][g][i] = p_db;
+        sm.part[pb][4][g][i] = p_da;
+        __syncthreads();
+        float *const outs[5] = {p.dr, p.dk, p.dw, p.db, p.da};
+#pragma unroll
+        for (int qn = 0; qn < 5; ++qn) {
+            if ((qn < 4 ? qn : 0) != g)
+                continue;
+            float sum = 0.f;
+#pragma unroll
+            for (int gg = 0; gg < NWB; ++gg)
+                sum += sm.part[pb][qn][gg][i];
+            outs[qn][e0 + i] = sum;
+        }
+    }
+#pragma unroll
+    for (int jj = 0; jj < CW; jj += 4)
+        *reinterpret_cast<f32x4 *>(&p.d_state_in[sbase + jj]) = f32x4{G[jj], G[jj + 1], G[jj + 2], G[jj + 3]};
+}
+
+template <typename Tin>
+hipError_t launch_bwd_t(const BwdArgs &p, hipStream_t stream)
+{
+    const dim3 grid(static_cast<unsigned>(p.B) * static_cast<unsigned>(p.H)), block(NWB * 64);
+    const bool sin = p.state_in != nullptr, dout = p.d_state_out != nullptr;
+    if (sin && dout)
+        hipLaunchKernelGGL((wkv7_bwd_kernel<Tin, true, true>), grid, block, 0, stream, p);
+    else if (sin)
+        hipLaunchKernelGGL((wkv7_bwd_kernel<Tin, true, false>), grid, block, 0, stream, p);
+    else if (dout)
+        hipLaunchKernelGGL((wkv7_bwd_kernel<Tin, false, true>), grid, block, 0, stream, p);
+    else
+        hipLaunchKernelGGL((wkv7_bwd_kernel<Tin, false, false>), grid, block, 0, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_backward(const BwdArgs &p, hipStream_t stream)
+{
+    return p.in_bf16 ? launch_bwd_t<uint16_t>(p, stream) : launch_bwd_t<float>(p, stream);
+}
+
+}  // namespace wkv7

@@ -31,12 +31,26 @@ struct TailArgs {
     int in_bf16, o_bf16, x_bf16;
 };
 
+// the backward pass: gradients of the recurrence given its per-position states
+struct BwdArgs {
+    const void *r, *w, *k, *v, *a, *b;  // [B,T,H,64], in_dtype
+    const float *state_in;              // [B,H,64,64] or nullptr (zeros)
+    const float *state_pos;             // [B,T,H,64,64]: the state after each token
+    const float *d_o;                   // [B,T,H,64]: gradient of o
+    const float *d_state_out;           // [B,H,64,64] or nullptr (zeros)
+    float *dr, *dw, *dk, *dv, *da, *db; // [B,T,H,64]
+    float *d_state_in;                  // [B,H,64,64]
+    int B, T, H;
+    int in_bf16;
+};
+
 hipError_t launch_step(const SeqArgs &a, hipStream_t stream);
 hipError_t launch_chunk(const SeqArgs &a, hipStream_t stream);
 hipError_t launch_state_copy(const float *src, float *dst, long long n_floats, hipStream_t stream);
 hipError_t launch_state_reset(float *state, int B, int H, const unsigned char *row_mask,
                               hipStream_t stream);
 hipError_t launch_tail(const TailArgs &a, hipStream_t stream);
+hipError_t launch_backward(const BwdArgs &a, hipStream_t stream);
 hipError_t launch_state_commit(const float *state_pos, const int *accepted, const float *state_in,
                                float *state_out, int B, int T, int H, hipStream_t stream);
 

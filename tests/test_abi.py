@@ -31,8 +31,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     assert names == sorted(["wkv7_forward", "wkv7_forward_varlen", "wkv7_step", "wkv7_step_tail",
-                            "wkv7_tmix_tail", "wkv7_state_commit", "wkv7_state_reset", "wkv7_status_string",
-                            "wkv7_abi_version"])
+                            "wkv7_tmix_tail", "wkv7_state_commit", "wkv7_state_reset", "wkv7_backward",
+                            "wkv7_status_string", "wkv7_abi_version"])
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -246,3 +246,41 @@ def test_launch_size_limits(L):
     assert commit(L, B=max_step + 1, T=5, H=1) == ERR_SHAPE
     assert tmix(L, B=1, T=max_rows + 1, H=1) == ERR_SHAPE
     assert tmix(L, B=1, T=max_rows // 64 + 1, H=64) == ERR_SHAPE
+
+
+def bwd(L, B=2, T=6, H=3, N=64, in_dt=BF16, sin="fake", pos="fake", do="fake", dso="fake", grads=None,
+        dsi="fake"):
+    pick = lambda x, d: d if x == "fake" else x
+    p = [fake(i) for i in range(6)]
+    g = [fake(11 + i) for i in range(6)] if grads is None else grads
+    return L.wkv7_backward(*p, in_dt, pick(sin, fake(7)), pick(pos, fake(9)), pick(do, fake(10)),
+                           pick(dso, fake(17)), *g, pick(dsi, fake(18)), B, T, H, N, None)
+
+
+def test_backward_validation(L):
+    assert bwd(L, N=32) == ERR_UNSUPPORTED
+    assert bwd(L, in_dt=5) == ERR_UNSUPPORTED
+    assert bwd(L, B=0) == ERR_SHAPE
+    assert bwd(L, T=-1) == ERR_SHAPE
+    assert bwd(L, B=8000001, H=1) == ERR_SHAPE
+    assert bwd(L, dsi=None) == ERR_NULL
+    assert bwd(L, pos=None) == ERR_NULL
+    assert bwd(L, do=None) == ERR_NULL
+    for q in range(6):
+        g = [fake(11 + i) for i in range(6)]
+        g[q] = None
+        assert bwd(L, grads=g) == ERR_NULL
+    assert bwd(L, dsi=fake(18, 4)) == ERR_ALIGN
+    assert bwd(L, do=fake(10, 8)) == ERR_ALIGN
+    # an output on an input, on another output, or on part of d_state_out
+    assert bwd(L, dsi=fake(9)) == ERR_ALIAS
+    g = [fake(11 + i) for i in range(6)]
+    g[3] = fake(11)
+    assert bwd(L, grads=g) == ERR_ALIAS
+    g = [fake(11 + i) for i in range(6)]
+    g[0] = fake(2, 64)
+    assert bwd(L, grads=g) == ERR_ALIAS
+    assert bwd(L, dsi=fake(17, 256)) == ERR_ALIAS
+    # T = 0 needs only d_state_in
+    assert L.wkv7_backward(*([None] * 6), BF16, None, None, None, None, *([None] * 6), None, 2, 0, 3, 64,
+                           None) == ERR_NULL
