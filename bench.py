@@ -56,7 +56,7 @@ def recurrent_flops(wl) -> int:
 
 def kernel_source_hash(kind: str) -> str:
     name = {"step": "wkv7_step.hip", "verify": "wkv7_step.hip", "chunk": "wkv7_chunk.hip",
-            "step_tail": "wkv7_step.hip", "tail_pass": "wkv7_tail.hip"}[kind]
+            "step_tail": "wkv7_step.hip", "tail_pass": "wkv7_tail.hip", "bwd": "wkv7_bwd.hip"}[kind]
     h = hashlib.sha256()
     for f in (name, "wkv7_device.h"):
         with open(os.path.join(CSRC, f), "rb") as fh:
@@ -227,6 +227,42 @@ def time_tail_pass(K, synth, idx: int, steps: int, warmup: int):
     x = torch.empty_like(o)
     stream = torch.cuda.Stream()
     run = lambda: K.wkv7_tmix_tail(o, d["r"], d["k"], d["v"], g, *prm, 64e-5, x=x)
+    with torch.cuda.stream(stream):
+        warm(run, warmup)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            run()
+        e1.record(stream)
+        e1.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    return {"sec_per_launch": ms / 1e3}
+
+
+def backward_bytes(wl) -> int:
+    """Algorithmic bytes of one backward call: the per-position states, the six inputs and
+    d_o read once, the six fp32 gradients written once; per head the input state and the
+    final state's gradient read, and the input state's gradient written."""
+    e_in = 2 if wl.dtype == "bf16" else 4
+    tokheads = wl.B * wl.T * wl.H
+    per_head = (3 if wl.state_std > 0 else 2) * N * N * 4
+    return tokheads * (N * N * 4 + 6 * N * e_in + N * 4 + 6 * N * 4) + wl.B * wl.H * per_head
+
+
+def time_backward(K, synth, idx: int, steps: int, warmup: int):
+    """The backward pass over workload idx, given the per-position states of its forward pass
+    (written once by the step kernel, untimed), a random d_o and a random final-state gradient."""
+    import torch
+    wl = synth.WORKLOADS[idx]
+    d = synth.workload_inputs(idx, device="cuda")
+    ins = [d[n] for n in ("r", "w", "k", "v", "a", "b")]
+    _, _, s_pos = K.wkv7_step(*ins, d["state_in"], per_position=True, write_state_out=False)
+    gen = torch.Generator(device="cuda").manual_seed(83)
+    d_o = torch.randn(d["r"].shape, generator=gen, device="cuda")
+    d_so = torch.randn((wl.B, wl.H, N, N), generator=gen, device="cuda")
+    grads = K.wkv7_backward(*ins, d["state_in"], s_pos, d_o, d_so)
+    stream = torch.cuda.Stream()
+    run = lambda: K.wkv7_backward(*ins, d["state_in"], s_pos, d_o, d_so, grads=grads)
     with torch.cuda.stream(stream):
         warm(run, warmup)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -467,6 +503,13 @@ def main():
         rp = roofline(b_pass, tp["sec_per_launch"], "tail_pass", 3)
         others["3-tail-pass"] = {"workload": w3.name + " (time-mix tail pass)",
                                  "ms_per_call": round(tp["sec_per_launch"] * 1e3, 4), "roofline": rp}
+        # the backward pass (gradients) over workload 2, from the per-position states
+        w2 = synth.WORKLOADS[2]
+        tg = time_backward(K, synth, 2, max(5, args.steps // 4), min(args.warmup, 2))
+        rg = roofline(backward_bytes(w2), tg["sec_per_launch"], "bwd", 2)
+        others["2-bwd"] = {"workload": w2.name + " (backward pass)",
+                           "ms_per_call": round(tg["sec_per_launch"] * 1e3, 4), "roofline": rg,
+                           "mtok_s": round(w2.B * w2.T / tg["sec_per_launch"] / 1e6, 2)}
         line["other_workloads"] = others
     print(json.dumps(line), flush=True)
 

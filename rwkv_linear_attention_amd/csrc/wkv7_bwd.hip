@@ -16,25 +16,27 @@
 // input (the per-position states the step kernel writes), so nothing is
 // rebuilt: with 288 GB of HBM the states of long sequences fit.
 //
-// MAPPING (gfx950).  One workgroup of four waves per (batch, head).  Lane i of
-// every wave is key row i; wave g keeps the 16 value columns 16 g .. 16 g + 15
-// of G, S_t and S_{t-1} in registers.
-//  * Sums over the value columns (dr, dk, dw, db, da) are a 16-term sum in each
-//    lane and a sum of the four waves' partials through LDS (one barrier per
+// MAPPING (gfx950).  One workgroup of eight waves per (batch, head).  Lane i of
+// every wave is key row i; wave g keeps the 8 value columns 8 g .. 8 g + 7 of G,
+// S_t and S_{t-1} in registers.
+//  * Sums over the value columns (dr, dk, dw, db, da) are an 8-term sum in each
+//    lane and a sum of the eight waves' partials through LDS (one barrier per
 //    token, double-buffered).
 //  * Sums over the key rows (c, S_{t-1}^T a, dv) stay inside a wave: the lanes
-//    write their 16 terms to LDS, and lane (jj, rb) adds column jj over rows
-//    16 rb .. 16 rb + 15, stored so that the two row blocks read together fall
-//    in different banks, before two lane exchanges finish the sum.
-// All arithmetic is fp32; gradients are written as fp32.
+//    write their 8 terms to LDS, and lane (jj, rb) adds column jj over rows
+//    8 rb .. 8 rb + 7, stored so that the row blocks read together fall in
+//    different banks, before three lane exchanges finish the sum.
+// Each token's inputs and S_{t-1} are loaded three tokens ahead.  All arithmetic
+// is fp32; gradients are written as fp32.
 #include "wkv7_device.h"
 #include "wkv7_launch.h"
 
 namespace wkv7 {
 namespace {
 
-constexpr int NWB = 4;               // waves per head
-constexpr int CW = kN / NWB;         // value columns per wave (16)
+constexpr int NWB = 8;               // waves per head
+constexpr int CW = kN / NWB;         // value columns per wave (8)
+constexpr int RB = 64 / CW;          // row blocks of a column sum (8)
 
 struct alignas(16) BwdSmem {
     float x[NWB][3][kN][CW];          // per-wave column-sum terms, row i at xrow(i)
@@ -42,10 +44,10 @@ struct alignas(16) BwdSmem {
     float bc[NWB][2][CW];             // per-wave column sums c and S_{t-1}^T a, broadcast
 };
 
-// Storage row of key row i in x: adjacent rows swap in odd blocks of 16, so the
-// 32 lanes that read rows r and 16 + r together (4-byte reads, 32 banks, rows of
-// 64 bytes) find them in opposite halves of the banks.
-__device__ __forceinline__ int xrow(int i) { return i ^ ((i >> 4) & 1); }
+// Storage row of key row i in x: rows of 8 floats (8 banks), XOR-ed with the
+// row's block of 8, so that the 32 lanes that read rows r, 8 + r, 16 + r, 24 + r
+// together (4-byte reads, 32 banks) find them in four different bank groups.
+__device__ __forceinline__ int xrow(int i) { return i ^ ((i >> 3) & 3); }
 
 template <typename Tin, bool HAS_STATE_IN, bool HAS_DOUT>
 __global__ __launch_bounds__(NWB * 64) void wkv7_bwd_kernel(BwdArgs p)
@@ -67,7 +69,43 @@ __global__ __launch_bounds__(NWB * 64) void wkv7_bwd_kernel(BwdArgs p)
     // element (b, t, h, 0) of the [B, T, H, N] tensors, and (b, t, h, 0, 0) of state_pos
     auto vec0 = [&](int t) { return (static_cast<size_t>(bb) * T + t) * H + hh; };
 
-    float G[CW], St[CW], Sp[CW];
+    // Everything a token reads (its six inputs, d_o and S_{t-1}) is loaded NSET
+    // tokens ahead into a ring of register sets: each token's work is short next to
+    // the HBM latency.
+    struct StepIn {
+        float ri, wi, ki, ai, bi;
+        float dO[CW], vv[CW], Sp[CW];
+    };
+    auto load_step = [&](int t, StepIn &s) {
+        const size_t e0 = vec0(t) * kN;
+        s.ri = load_elem(r, e0 + i);
+        s.wi = load_elem(w, e0 + i);
+        s.ki = load_elem(k, e0 + i);
+        s.ai = load_elem(a, e0 + i);
+        s.bi = load_elem(b, e0 + i);
+#pragma unroll
+        for (int jj = 0; jj < CW; ++jj) {
+            s.dO[jj] = p.d_o[e0 + j0 + jj];
+            s.vv[jj] = load_elem(v, e0 + j0 + jj);
+        }
+        // S_{t-1}: the state after token t-1, or the input state
+        if (t > 0) {
+            const float *src = p.state_pos + vec0(t - 1) * (kN * kN) + static_cast<size_t>(i) * kN + j0;
+#pragma unroll
+            for (int jj = 0; jj < CW; jj += 4) {
+                const f32x4 x4 = *reinterpret_cast<const f32x4 *>(src + jj);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    s.Sp[jj + e] = x4[e];
+            }
+        } else {
+#pragma unroll
+            for (int jj = 0; jj < CW; ++jj)
+                s.Sp[jj] = HAS_STATE_IN ? p.state_in[sbase + jj] : 0.0f;
+        }
+    };
+
+    float G[CW], St[CW];
 #pragma unroll
     for (int jj = 0; jj < CW; ++jj)
         G[jj] = HAS_DOUT ? p.d_state_out[sbase + jj] : 0.0f;
@@ -81,43 +119,22 @@ __global__ __launch_bounds__(NWB * 64) void wkv7_bwd_kernel(BwdArgs p)
                 St[jj + e] = x4[e];
         }
     }
-    // lane roles in the column sums: column jj_l of this wave, rows 16 rb .. 16 rb + 15
-    const int jj_l = i & 15, rb = i >> 4;
+    // lane roles in the column sums: column jj_l of this wave, rows CW rb .. CW rb + CW - 1
+    const int jj_l = i % CW, rb = i / CW;
 
-    for (int t = T - 1; t >= 0; --t) {
+    // one token of the adjoint, from its loaded inputs
+    auto step = [&](int t, const StepIn &s) {
         const size_t e0 = vec0(t) * kN;
-        const float ri = load_elem(r, e0 + i), wi = load_elem(w, e0 + i), ki = load_elem(k, e0 + i);
-        const float ai = load_elem(a, e0 + i), bi = load_elem(b, e0 + i);
-        float dO[CW], vv[CW];
-#pragma unroll
-        for (int jj = 0; jj < CW; ++jj) {
-            dO[jj] = p.d_o[e0 + j0 + jj];
-            vv[jj] = load_elem(v, e0 + j0 + jj);
-        }
-        // S_{t-1}: the state after token t-1, or the input state
-        if (t > 0) {
-            const float *src = p.state_pos + vec0(t - 1) * (kN * kN) + static_cast<size_t>(i) * kN + j0;
-#pragma unroll
-            for (int jj = 0; jj < CW; jj += 4) {
-                const f32x4 x4 = *reinterpret_cast<const f32x4 *>(src + jj);
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    Sp[jj + e] = x4[e];
-            }
-        } else {
-#pragma unroll
-            for (int jj = 0; jj < CW; ++jj)
-                Sp[jj] = HAS_STATE_IN ? p.state_in[sbase + jj] : 0.0f;
-        }
+        const float ri = s.ri, wi = s.wi, ki = s.ki, ai = s.ai, bi = s.bi;
 
         // G += r_t do_t^T, then the row partials that need only G, S_t, S_{t-1}
         float p_dr = 0.f, p_dk = 0.f, p_dw = 0.f;
 #pragma unroll
         for (int jj = 0; jj < CW; ++jj) {
-            G[jj] += ri * dO[jj];
-            p_dr += St[jj] * dO[jj];
-            p_dk += G[jj] * vv[jj];
-            p_dw += G[jj] * Sp[jj];
+            G[jj] += ri * s.dO[jj];
+            p_dr += St[jj] * s.dO[jj];
+            p_dk += G[jj] * s.vv[jj];
+            p_dw += G[jj] * s.Sp[jj];
         }
 
         // column sums over the 64 key rows: c = G^T b, sa = S_{t-1}^T a, dv = G^T k
@@ -128,7 +145,7 @@ __global__ __launch_bounds__(NWB * 64) void wkv7_bwd_kernel(BwdArgs p)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 xc[e] = bi * G[jj + e];
-                xs[e] = ai * Sp[jj + e];
+                xs[e] = ai * s.Sp[jj + e];
                 xv[e] = ki * G[jj + e];
             }
             *reinterpret_cast<f32x4 *>(&xw[0][xrow(i)][jj]) = xc;
@@ -137,19 +154,19 @@ __global__ __launch_bounds__(NWB * 64) void wkv7_bwd_kernel(BwdArgs p)
         }
         float cs[3] = {0.f, 0.f, 0.f};
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-            const int row = xrow(16 * rb + rr);
+        for (int rr = 0; rr < RB; ++rr) {
+            const int row = xrow(RB * rb + rr);
 #pragma unroll
             for (int qn = 0; qn < 3; ++qn)
                 cs[qn] += xw[qn][row][jj_l];
         }
 #pragma unroll
-        for (int qn = 0; qn < 3; ++qn) {
-            cs[qn] += __shfl_xor(cs[qn], 16);
-            cs[qn] += __shfl_xor(cs[qn], 32);
-        }
-        // lanes 0..15 hold column jj = lane: dv out, c and sa broadcast through LDS
-        if (i < 16) {
+        for (int qn = 0; qn < 3; ++qn)
+#pragma unroll
+            for (int off = CW; off < 64; off <<= 1)
+                cs[qn] += __shfl_xor(cs[qn], off);
+        // lanes 0..CW-1 hold column jj = lane: dv out, c and sa broadcast through LDS
+        if (i < CW) {
             p.dv[e0 + j0 + i] = cs[2];
             sm.bc[g][0][i] = cs[0];
             sm.bc[g][1][i] = cs[1];
@@ -171,13 +188,13 @@ __global__ __launch_bounds__(NWB * 64) void wkv7_bwd_kernel(BwdArgs p)
 #pragma unroll
         for (int jj = 0; jj < CW; ++jj) {
             p_db += G[jj] * sa[jj];
-            p_da += Sp[jj] * c[jj];
+            p_da += s.Sp[jj] * c[jj];
             G[jj] = wi * G[jj] + ai * c[jj];
-            St[jj] = Sp[jj];
+            St[jj] = s.Sp[jj];
         }
 
-        // the four waves' row partials: written, one barrier, then wave q (q < 5,
-        // wave 0 takes two) sums quantity q for all 64 rows
+        // the waves' row partials: written, one barrier, then wave q (q < 5) sums
+        // quantity q for all 64 rows
         const int pb = t & 1;
         sm.part[pb][0][g][i] = p_dr;
         sm.part[pb][1][g][i] = p_dk;
@@ -188,13 +205,33 @@ __global__ __launch_bounds__(NWB * 64) void wkv7_bwd_kernel(BwdArgs p)
         float *const outs[5] = {p.dr, p.dk, p.dw, p.db, p.da};
 #pragma unroll
         for (int qn = 0; qn < 5; ++qn) {
-            if ((qn < 4 ? qn : 0) != g)
+            if (qn != g)
                 continue;
             float sum = 0.f;
 #pragma unroll
             for (int gg = 0; gg < NWB; ++gg)
                 sum += sm.part[pb][qn][gg][i];
             outs[qn][e0 + i] = sum;
+        }
+    };
+
+    // tokens T-1, T-2, ... in rounds of NSET; token t uses set (T-1-t) % NSET and
+    // refills it with token t - NSET
+    constexpr int NSET = 3;
+    StepIn ring[NSET];
+#pragma unroll
+    for (int u = 0; u < NSET; ++u)
+        if (T - 1 - u >= 0)
+            load_step(T - 1 - u, ring[u]);
+    for (int t0 = T - 1; t0 >= 0; t0 -= NSET) {
+#pragma unroll
+        for (int u = 0; u < NSET; ++u) {
+            const int t = t0 - u;
+            if (t < 0)
+                break;
+            step(t, ring[u]);
+            if (t - NSET >= 0)
+                load_step(t - NSET, ring[u]);
         }
     }
 #pragma unroll
