@@ -37,6 +37,7 @@ namespace {
 constexpr int NWB = 8;               // waves per head
 constexpr int CW = kN / NWB;         // value columns per wave (8)
 constexpr int RB = 64 / CW;          // row blocks of a column sum (8)
+constexpr int NSET = 4;              // tokens of inputs in flight (loaded NSET-1 ahead)
 
 struct alignas(16) BwdSmem {
     float x[NWB][3][kN][CW];          // per-wave column-sum terms, row i at xrow(i)
@@ -48,6 +49,10 @@ struct alignas(16) BwdSmem {
 // row's block of 8, so that the 32 lanes that read rows r, 8 + r, 16 + r, 24 + r
 // together (4-byte reads, 32 banks) find them in four different bank groups.
 __device__ __forceinline__ int xrow(int i) { return i ^ ((i >> 3) & 3); }
+
+// an input element as loaded (fp32, or the upper half of an fp32 for bf16)
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(uint16_t x) { return __uint_as_float(static_cast<unsigned>(x) << 16); }
 
 template <typename Tin, bool HAS_STATE_IN, bool HAS_DOUT>
 __global__ __launch_bounds__(NWB * 64) void wkv7_bwd_kernel(BwdArgs p)
@@ -69,47 +74,52 @@ __global__ __launch_bounds__(NWB * 64) void wkv7_bwd_kernel(BwdArgs p)
     // element (b, t, h, 0) of the [B, T, H, N] tensors, and (b, t, h, 0, 0) of state_pos
     auto vec0 = [&](int t) { return (static_cast<size_t>(bb) * T + t) * H + hh; };
 
-    // Everything a token reads (its six inputs, d_o and S_{t-1}) is loaded NSET
-    // tokens ahead into a ring of register sets: each token's work is short next to
-    // the HBM latency.
+    // Everything a token reads (its six inputs, d_o and S_{t-1}) is loaded ahead
+    // into a ring of NSET register sets: each token's work is short next to the
+    // HBM latency.
+    // d_o and v of the wave's columns are the same for every lane: lane i loads
+    // column j0 + i % CW, and the step reads them back with lane reads (into
+    // scalar registers).  A set holds the values as loaded; conversion and the
+    // zero state happen in the step, so that nothing waits for a load at the
+    // time it is issued.
     struct StepIn {
-        float ri, wi, ki, ai, bi;
-        float dO[CW], vv[CW], Sp[CW];
+        Tin ri, wi, ki, ai, bi, v_l;
+        float dO_l;
+        f32x4 Sp4[CW / 4];
+        bool live;
     };
     auto load_step = [&](int t, StepIn &s) {
         const size_t e0 = vec0(t) * kN;
-        s.ri = load_elem(r, e0 + i);
-        s.wi = load_elem(w, e0 + i);
-        s.ki = load_elem(k, e0 + i);
-        s.ai = load_elem(a, e0 + i);
-        s.bi = load_elem(b, e0 + i);
+        s.ri = r[e0 + i];
+        s.wi = w[e0 + i];
+        s.ki = k[e0 + i];
+        s.ai = a[e0 + i];
+        s.bi = b[e0 + i];
+        s.dO_l = p.d_o[e0 + j0 + (i % CW)];
+        s.v_l = v[e0 + j0 + (i % CW)];
+        // S_{t-1}: the state after token t-1, or the input state (zeros without
+        // one: then a valid row is read and not used).  The same loads on every
+        // path keep the compiler's count of loads in flight exact.
+        const float *src = t > 0 ? p.state_pos + vec0(t - 1) * (kN * kN) + static_cast<size_t>(i) * kN + j0
+                                 : HAS_STATE_IN ? p.state_in + sbase
+                                                : p.state_pos + static_cast<size_t>(i) * kN + j0;
+        s.live = t > 0 || HAS_STATE_IN;
 #pragma unroll
-        for (int jj = 0; jj < CW; ++jj) {
-            s.dO[jj] = p.d_o[e0 + j0 + jj];
-            s.vv[jj] = load_elem(v, e0 + j0 + jj);
-        }
-        // S_{t-1}: the state after token t-1, or the input state
-        if (t > 0) {
-            const float *src = p.state_pos + vec0(t - 1) * (kN * kN) + static_cast<size_t>(i) * kN + j0;
-#pragma unroll
-            for (int jj = 0; jj < CW; jj += 4) {
-                const f32x4 x4 = *reinterpret_cast<const f32x4 *>(src + jj);
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    s.Sp[jj + e] = x4[e];
-            }
-        } else {
-#pragma unroll
-            for (int jj = 0; jj < CW; ++jj)
-                s.Sp[jj] = HAS_STATE_IN ? p.state_in[sbase + jj] : 0.0f;
-        }
+        for (int q = 0; q < CW / 4; ++q)
+            s.Sp4[q] = *reinterpret_cast<const f32x4 *>(src + 4 * q);
     };
 
     float G[CW], St[CW];
 #pragma unroll
     for (int jj = 0; jj < CW; ++jj)
         G[jj] = HAS_DOUT ? p.d_state_out[sbase + jj] : 0.0f;
-    if (T > 0) {
+    if (T == 0) {  // no tokens: the gradient passes through
+#pragma unroll
+        for (int jj = 0; jj < CW; jj += 4)
+            *reinterpret_cast<f32x4 *>(&p.d_state_in[sbase + jj]) = f32x4{G[jj], G[jj + 1], G[jj + 2], G[jj + 3]};
+        return;
+    }
+    {
         const float *src = p.state_pos + vec0(T - 1) * (kN * kN) + static_cast<size_t>(i) * kN + j0;
 #pragma unroll
         for (int jj = 0; jj < CW; jj += 4) {
@@ -125,16 +135,24 @@ __global__ __launch_bounds__(NWB * 64) void wkv7_bwd_kernel(BwdArgs p)
     // one token of the adjoint, from its loaded inputs
     auto step = [&](int t, const StepIn &s) {
         const size_t e0 = vec0(t) * kN;
-        const float ri = s.ri, wi = s.wi, ki = s.ki, ai = s.ai, bi = s.bi;
+        const float ri = to_f32(s.ri), wi = to_f32(s.wi), ki = to_f32(s.ki), ai = to_f32(s.ai), bi = to_f32(s.bi);
+        const float v_l = to_f32(s.v_l);
+        float dO[CW], vv[CW], Sp[CW];
+#pragma unroll
+        for (int jj = 0; jj < CW; ++jj) {
+            dO[jj] = lane_bcast(s.dO_l, jj);
+            vv[jj] = lane_bcast(v_l, jj);
+            Sp[jj] = s.live ? s.Sp4[jj / 4][jj % 4] : 0.0f;
+        }
 
         // G += r_t do_t^T, then the row partials that need only G, S_t, S_{t-1}
         float p_dr = 0.f, p_dk = 0.f, p_dw = 0.f;
 #pragma unroll
         for (int jj = 0; jj < CW; ++jj) {
-            G[jj] += ri * s.dO[jj];
-            p_dr += St[jj] * s.dO[jj];
-            p_dk += G[jj] * s.vv[jj];
-            p_dw += G[jj] * s.Sp[jj];
+            G[jj] += ri * dO[jj];
+            p_dr += St[jj] * dO[jj];
+            p_dk += G[jj] * vv[jj];
+            p_dw += G[jj] * Sp[jj];
         }
 
         // column sums over the 64 key rows: c = G^T b, sa = S_{t-1}^T a, dv = G^T k
@@ -145,7 +163,7 @@ __global__ __launch_bounds__(NWB * 64) void wkv7_bwd_kernel(BwdArgs p)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 xc[e] = bi * G[jj + e];
-                xs[e] = ai * s.Sp[jj + e];
+                xs[e] = ai * Sp[jj + e];
                 xv[e] = ki * G[jj + e];
             }
             *reinterpret_cast<f32x4 *>(&xw[0][xrow(i)][jj]) = xc;
@@ -188,9 +206,9 @@ __global__ __launch_bounds__(NWB * 64) void wkv7_bwd_kernel(BwdArgs p)
 #pragma unroll
         for (int jj = 0; jj < CW; ++jj) {
             p_db += G[jj] * sa[jj];
-            p_da += s.Sp[jj] * c[jj];
+            p_da += Sp[jj] * c[jj];
             G[jj] = wi * G[jj] + ai * c[jj];
-            St[jj] = s.Sp[jj];
+            St[jj] = Sp[jj];
         }
 
         // the waves' row partials: written, one barrier, then wave q (q < 5) sums
@@ -201,7 +219,12 @@ __global__ __launch_bounds__(NWB * 64) void wkv7_bwd_kernel(BwdArgs p)
         sm.part[pb][2][g][i] = p_dw;
         sm.part[pb][3][g][i] = p_db;
         sm.part[pb][4][g][i] = p_da;
-        __syncthreads();
+        // a barrier for the LDS partials only: waiting here for this wave's LDS
+        // writes (not for its global loads and stores, which a full fence would
+        // include, and with them the loads issued for the tokens ahead)
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
         float *const outs[5] = {p.dr, p.dk, p.dw, p.db, p.da};
 #pragma unroll
         for (int qn = 0; qn < 5; ++qn) {
@@ -215,23 +238,33 @@ __global__ __launch_bounds__(NWB * 64) void wkv7_bwd_kernel(BwdArgs p)
         }
     };
 
-    // tokens T-1, T-2, ... in rounds of NSET; token t uses set (T-1-t) % NSET and
-    // refills it with token t - NSET
-    constexpr int NSET = 3;
+    // Tokens T-1, T-2, ... ; token t uses set (T-1-t) % NSET.  Its S_{t-1} is the
+    // next token's S_t, so the set stays live one token more: after token t runs,
+    // the set of token t+1 is refilled with token t+1-NSET (NSET-1 tokens ahead).
+    // The loop holds whole rounds whose loads are all real (so the compiler's
+    // wait analysis sees one steady state and waits only for loads a round old);
+    // the last one or two rounds follow it.
     StepIn ring[NSET];
 #pragma unroll
     for (int u = 0; u < NSET; ++u)
-        if (T - 1 - u >= 0)
-            load_step(T - 1 - u, ring[u]);
-    for (int t0 = T - 1; t0 >= 0; t0 -= NSET) {
+        load_step(max(T - 1 - u, 0), ring[u]);  // (a set past token 0 is never used)
+    step(T - 1, ring[0]);
+    int t0 = T - 2;
+    for (; t0 >= 2 * NSET - 2; t0 -= NSET) {
+#pragma unroll
+        for (int u = 0; u < NSET; ++u) {
+            step(t0 - u, ring[(u + 1) % NSET]);
+            load_step(t0 - u + 1 - NSET, ring[u]);
+        }
+    }
+    for (; t0 >= 0; t0 -= NSET) {
 #pragma unroll
         for (int u = 0; u < NSET; ++u) {
             const int t = t0 - u;
-            if (t < 0)
-                break;
-            step(t, ring[u]);
-            if (t - NSET >= 0)
-                load_step(t - NSET, ring[u]);
+            if (t >= 0) {
+                step(t, ring[(u + 1) % NSET]);
+                load_step(max(t + 1 - NSET, 0), ring[u]);
+            }
         }
     }
 #pragma unroll
