@@ -38,10 +38,11 @@ constexpr int NWB = 8;               // waves per head
 constexpr int CW = kN / NWB;         // value columns per wave (8)
 constexpr int RB = 64 / CW;          // row blocks of a column sum (8)
 constexpr int NSET = 4;              // tokens of inputs in flight (loaded NSET-1 ahead)
+constexpr int TB = NSET;             // tokens whose row partials are summed together
 
 struct alignas(16) BwdSmem {
     float x[NWB][3][kN][CW];          // per-wave column-sum terms, row i at xrow(i)
-    float part[2][5][NWB][kN];        // per-wave row partials: dr, dk, dw, db, da
+    float part[2][TB][5][NWB][kN];    // per-wave row partials (dr, dk, dw, db, da) of TB tokens
     float bc[NWB][2][CW];             // per-wave column sums c and S_{t-1}^T a, broadcast
 };
 
@@ -132,8 +133,36 @@ __global__ __launch_bounds__(NWB * 64) void wkv7_bwd_kernel(BwdArgs p)
     // lane roles in the column sums: column jj_l of this wave, rows CW rb .. CW rb + CW - 1
     const int jj_l = i % CW, rb = i / CW;
 
-    // one token of the adjoint, from its loaded inputs
-    auto step = [&](int t, const StepIn &s) {
+    // the row partials of the TB tokens of batch kb (fewer in the last), whose
+    // last token is t_end, at slot slot_end: written by every wave, one barrier,
+    // then the 5 x TB sums spread over the waves
+    auto finish_batch = [&](int t_end, int slot_end, int pb) {
+        // a barrier for the LDS partials only: waiting here for this wave's LDS
+        // writes (not for its global loads and stores, which a full fence would
+        // include, and with them the loads issued for the tokens ahead)
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        // every wave stores the same number of sums (no branch, so that the
+        // compiler's count of stores in flight stays exact): a wave with fewer
+        // pairs, or a pair past the batch's last slot, repeats one it has
+#pragma unroll
+        for (int m = 0; m < (5 * TB + NWB - 1) / NWB; ++m) {
+            const int pi0 = g + NWB * m, pi = pi0 < 5 * TB ? pi0 : pi0 - NWB;
+            const int sl0 = pi / 5, qn = pi - 5 * sl0, sl = min(sl0, slot_end);
+            float sum = 0.f;
+#pragma unroll
+            for (int gg = 0; gg < NWB; ++gg)
+                sum += sm.part[pb][sl][qn][gg][i];
+            // (a select, not an indexed array, keeps the pointer's address space known)
+            float *const dst = qn == 0 ? p.dr : qn == 1 ? p.dk : qn == 2 ? p.dw : qn == 3 ? p.db : p.da;
+            dst[vec0(t_end + slot_end - sl) * kN + i] = sum;
+        }
+    };
+
+    // one token of the adjoint, from its loaded inputs; slot is its place in its
+    // batch of TB tokens, pb the batch's partial buffer
+    auto step = [&](int t, const StepIn &s, int slot, int pb) {
         const size_t e0 = vec0(t) * kN;
         const float ri = to_f32(s.ri), wi = to_f32(s.wi), ki = to_f32(s.ki), ai = to_f32(s.ai), bi = to_f32(s.bi);
         const float v_l = to_f32(s.v_l);
@@ -211,62 +240,52 @@ __global__ __launch_bounds__(NWB * 64) void wkv7_bwd_kernel(BwdArgs p)
             St[jj] = Sp[jj];
         }
 
-        // the waves' row partials: written, one barrier, then wave q (q < 5) sums
-        // quantity q for all 64 rows
-        const int pb = t & 1;
-        sm.part[pb][0][g][i] = p_dr;
-        sm.part[pb][1][g][i] = p_dk;
-        sm.part[pb][2][g][i] = p_dw;
-        sm.part[pb][3][g][i] = p_db;
-        sm.part[pb][4][g][i] = p_da;
-        // a barrier for the LDS partials only: waiting here for this wave's LDS
-        // writes (not for its global loads and stores, which a full fence would
-        // include, and with them the loads issued for the tokens ahead)
-        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-        float *const outs[5] = {p.dr, p.dk, p.dw, p.db, p.da};
-#pragma unroll
-        for (int qn = 0; qn < 5; ++qn) {
-            if (qn != g)
-                continue;
-            float sum = 0.f;
-#pragma unroll
-            for (int gg = 0; gg < NWB; ++gg)
-                sum += sm.part[pb][qn][gg][i];
-            outs[qn][e0 + i] = sum;
-        }
+        // this wave's row partials, summed over the waves once per batch
+        sm.part[pb][slot][0][g][i] = p_dr;
+        sm.part[pb][slot][1][g][i] = p_dk;
+        sm.part[pb][slot][2][g][i] = p_dw;
+        sm.part[pb][slot][3][g][i] = p_db;
+        sm.part[pb][slot][4][g][i] = p_da;
     };
 
-    // Tokens T-1, T-2, ... ; token t uses set (T-1-t) % NSET.  Its S_{t-1} is the
-    // next token's S_t, so the set stays live one token more: after token t runs,
-    // the set of token t+1 is refilled with token t+1-NSET (NSET-1 tokens ahead).
-    // The loop holds whole rounds whose loads are all real (so the compiler's
-    // wait analysis sees one steady state and waits only for loads a round old);
-    // the last one or two rounds follow it.
+    // Tokens T-1, T-2, ... ; the n-th (n = T-1-t) uses set n % NSET and is slot
+    // n % TB of batch n / TB.  Its S_{t-1} is the next token's S_t, so the set stays
+    // live one token more: after token t runs, the set of token t+1 is refilled
+    // with token t+1-NSET (NSET-1 tokens ahead).  The loop holds whole rounds
+    // whose loads are all real (so the compiler's wait analysis sees one steady
+    // state and waits only for loads a round old) and whose batch ends at a fixed
+    // place; the last one or two rounds follow it.
+    static_assert(TB == NSET, "a round of the loop is one batch");
     StepIn ring[NSET];
 #pragma unroll
     for (int u = 0; u < NSET; ++u)
         load_step(max(T - 1 - u, 0), ring[u]);  // (a set past token 0 is never used)
-    step(T - 1, ring[0]);
-    int t0 = T - 2;
-    for (; t0 >= 2 * NSET - 2; t0 -= NSET) {
+    step(T - 1, ring[0], 0, 0);
+    int t0 = T - 2, kb = 0;  // batch of the round's first token (n = 4 kb + 1)
+    for (; t0 >= 2 * NSET - 2; t0 -= NSET, ++kb) {
 #pragma unroll
         for (int u = 0; u < NSET; ++u) {
-            step(t0 - u, ring[(u + 1) % NSET]);
+            step(t0 - u, ring[(u + 1) % NSET], (u + 1) % TB, (kb + (u + 1) / TB) & 1);
             load_step(t0 - u + 1 - NSET, ring[u]);
+            if (u == TB - 2)
+                finish_batch(t0 - u, TB - 1, kb & 1);
         }
     }
-    for (; t0 >= 0; t0 -= NSET) {
+    for (; t0 >= 0; t0 -= NSET, ++kb) {
 #pragma unroll
         for (int u = 0; u < NSET; ++u) {
             const int t = t0 - u;
             if (t >= 0) {
-                step(t, ring[(u + 1) % NSET]);
+                const int pb = (kb + (u + 1) / TB) & 1;
+                step(t, ring[(u + 1) % NSET], (u + 1) % TB, pb);
                 load_step(max(t + 1 - NSET, 0), ring[u]);
+                if (u == TB - 2 || t == 0)
+                    finish_batch(t, (u + 1) % TB, pb);
             }
         }
     }
+    if (T == 1)
+        finish_batch(0, 0, 0);
 #pragma unroll
     for (int jj = 0; jj < CW; jj += 4)
         *reinterpret_cast<f32x4 *>(&p.d_state_in[sbase + jj]) = f32x4{G[jj], G[jj + 1], G[jj + 2], G[jj + 3]};
