@@ -20,12 +20,13 @@
 // every wave is key row i; wave g keeps the 8 value columns 8 g .. 8 g + 7 of G,
 // S_t and S_{t-1} in registers.
 //  * Sums over the value columns (dr, dk, dw, db, da) are an 8-term sum in each
-//    lane and a sum of the eight waves' partials through LDS (one barrier per
-//    token, double-buffered).
+//    lane and a sum of the eight waves' partials through LDS, once per four
+//    tokens (one barrier; the partials double-buffered).
 //  * Sums over the key rows (c, S_{t-1}^T a, dv) stay inside a wave: the lanes
 //    write their 8 terms to LDS, and lane (jj, rb) adds column jj over rows
 //    8 rb .. 8 rb + 7, stored so that the row blocks read together fall in
-//    different banks, before three lane exchanges finish the sum.
+//    different banks, before three cross-lane steps in the vector ALU finish the
+//    sum and lane reads hand c and S_{t-1}^T a to every lane.
 // Each token's inputs and S_{t-1} are loaded three tokens ahead.  All arithmetic
 // is fp32; gradients are written as fp32.
 #include "wkv7_device.h"
@@ -43,13 +44,24 @@ constexpr int TB = NSET;             // tokens whose row partials are summed tog
 struct alignas(16) BwdSmem {
     float x[NWB][3][kN][CW];          // per-wave column-sum terms, row i at xrow(i)
     float part[2][TB][5][NWB][kN];    // per-wave row partials (dr, dk, dw, db, da) of TB tokens
-    float bc[NWB][2][CW];             // per-wave column sums c and S_{t-1}^T a, broadcast
 };
 
 // Storage row of key row i in x: rows of 8 floats (8 banks), XOR-ed with the
 // row's block of 8, so that the 32 lanes that read rows r, 8 + r, 16 + r, 24 + r
 // together (4-byte reads, 32 banks) find them in four different bank groups.
 __device__ __forceinline__ int xrow(int i) { return i ^ ((i >> 3) & 3); }
+
+// Sum of x over lanes i, i^8, i^16, ..., i^56, returned to all eight: a row
+// rotation by 8 (lane i^8 within its row of 16), then the row-pair and half-wave
+// swaps of gfx950, all in the vector ALU.  Every lane adds in the same order.
+__device__ __forceinline__ float sum_lanes_xor8(float x)
+{
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128 /* row_ror:8 */, 0xf, 0xf, false));
+    const auto p16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(p16[0]) + __uint_as_float(p16[1]);
+    const auto p32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(p32[0]) + __uint_as_float(p32[1]);
+}
 
 // an input element as loaded (fp32, or the upper half of an fp32 for bf16)
 __device__ __forceinline__ float to_f32(float x) { return x; }
@@ -207,27 +219,18 @@ __global__ __launch_bounds__(NWB * 64) void wkv7_bwd_kernel(BwdArgs p)
             for (int qn = 0; qn < 3; ++qn)
                 cs[qn] += xw[qn][row][jj_l];
         }
+        static_assert(CW == 8, "the lane sums add lanes i ^ 8, i ^ 16, i ^ 32");
 #pragma unroll
         for (int qn = 0; qn < 3; ++qn)
-#pragma unroll
-            for (int off = CW; off < 64; off <<= 1)
-                cs[qn] += __shfl_xor(cs[qn], off);
-        // lanes 0..CW-1 hold column jj = lane: dv out, c and sa broadcast through LDS
-        if (i < CW) {
+            cs[qn] = sum_lanes_xor8(cs[qn]);
+        // lane jj (jj < CW) holds column jj: dv out, c and sa read back by lane reads
+        if (i < CW)
             p.dv[e0 + j0 + i] = cs[2];
-            sm.bc[g][0][i] = cs[0];
-            sm.bc[g][1][i] = cs[1];
-        }
         float c[CW], sa[CW];
 #pragma unroll
-        for (int jj = 0; jj < CW; jj += 4) {
-            const f32x4 c4 = *reinterpret_cast<const f32x4 *>(&sm.bc[g][0][jj]);
-            const f32x4 s4 = *reinterpret_cast<const f32x4 *>(&sm.bc[g][1][jj]);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                c[jj + e] = c4[e];
-                sa[jj + e] = s4[e];
-            }
+        for (int jj = 0; jj < CW; ++jj) {
+            c[jj] = lane_bcast(cs[0], jj);
+            sa[jj] = lane_bcast(cs[1], jj);
         }
 
         // row partials that need c and sa, then G for the previous token
