@@ -16,17 +16,23 @@
 // input (the per-position states the step kernel writes), so nothing is
 // rebuilt: with 288 GB of HBM the states of long sequences fit.
 //
-// MAPPING (gfx950).  One workgroup of eight waves per (batch, head).  Lane i of
-// every wave is key row i; wave g keeps the 8 value columns 8 g .. 8 g + 7 of G,
-// S_t and S_{t-1} in registers.
-//  * Sums over the value columns (dr, dk, dw, db, da) are an 8-term sum in each
+// The columns of G evolve independently (column j needs only c_j, a sum over
+// the rows of column j); only the outputs dr, dk, dw, db, da sum over columns.
+//
+// MAPPING (gfx950).  SPLIT workgroups of eight waves per (batch, head), each
+// with 64 / SPLIT value columns: SPLIT = 2 when the heads alone would leave most
+// of the 256 compute units idle, else 1.  Lane i of every wave is key row i;
+// wave g keeps CW = 8 / SPLIT value columns of G, S_t and S_{t-1} in registers.
+//  * Sums over the value columns (dr, dk, dw, db, da) are a CW-term sum in each
 //    lane and a sum of the eight waves' partials through LDS, once per four
-//    tokens (one barrier; the partials double-buffered).
+//    tokens (one barrier; the partials double-buffered).  With SPLIT = 2 the two
+//    workgroups' sums meet in an atomic add onto zeroed outputs: two terms, so
+//    the result does not depend on their order.
 //  * Sums over the key rows (c, S_{t-1}^T a, dv) stay inside a wave: the lanes
-//    write their 8 terms to LDS, and lane (jj, rb) adds column jj over rows
-//    8 rb .. 8 rb + 7, stored so that the row blocks read together fall in
-//    different banks, before three cross-lane steps in the vector ALU finish the
-//    sum and lane reads hand c and S_{t-1}^T a to every lane.
+//    write their CW terms to LDS, and lane (jj, rb) adds column jj over rows
+//    CW rb .. CW rb + CW - 1, stored so that the row blocks read together fall in
+//    different banks, before cross-lane steps in the vector ALU finish the sum
+//    and lane reads hand c and S_{t-1}^T a to every lane.
 // Each token's inputs and S_{t-1} are loaded three tokens ahead.  All arithmetic
 // is fp32; gradients are written as fp32.
 #include "wkv7_device.h"
@@ -35,28 +41,34 @@
 namespace wkv7 {
 namespace {
 
-constexpr int NWB = 8;               // waves per head
-constexpr int CW = kN / NWB;         // value columns per wave (8)
-constexpr int RB = 64 / CW;          // row blocks of a column sum (8)
+constexpr int NWB = 8;               // waves per workgroup
 constexpr int NSET = 4;              // tokens of inputs in flight (loaded NSET-1 ahead)
 constexpr int TB = NSET;             // tokens whose row partials are summed together
+constexpr int kCUs = 256;            // compute units of the MI355X
 
+template <int CW>
 struct alignas(16) BwdSmem {
     float x[NWB][3][kN][CW];          // per-wave column-sum terms, row i at xrow(i)
     float part[2][TB][5][NWB][kN];    // per-wave row partials (dr, dk, dw, db, da) of TB tokens
 };
 
-// Storage row of key row i in x: rows of 8 floats (8 banks), XOR-ed with the
-// row's block of 8, so that the 32 lanes that read rows r, 8 + r, 16 + r, 24 + r
-// together (4-byte reads, 32 banks) find them in four different bank groups.
+// Storage row of key row i in x: XOR-ed with (i / 8) % 4.  The 32 lanes of a
+// half wave that read together read rows CW rb + rr (fixed rr) for CW = 8
+// (rows of 8 banks, rb < 4) or CW = 4 (rows of 4 banks, rb < 8): the XOR puts
+// them in 32 / CW different bank groups (4-byte reads, 32 banks).
 __device__ __forceinline__ int xrow(int i) { return i ^ ((i >> 3) & 3); }
 
-// Sum of x over lanes i, i^8, i^16, ..., i^56, returned to all eight: a row
-// rotation by 8 (lane i^8 within its row of 16), then the row-pair and half-wave
-// swaps of gfx950, all in the vector ALU.  Every lane adds in the same order.
-__device__ __forceinline__ float sum_lanes_xor8(float x)
+// Sum of x over the lanes with the same lane % CW (CW = 8 or 4), returned to all
+// of them: row rotations (by 8, then by 4 for CW = 4) within rows of 16 lanes,
+// then the row-pair and half-wave swaps of gfx950, all in the vector ALU.  The
+// lanes of a group end with the same value.
+template <int CW>
+__device__ __forceinline__ float sum_column_lanes(float x)
 {
+    static_assert(CW == 8 || CW == 4, "eight or four columns per wave");
     x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128 /* row_ror:8 */, 0xf, 0xf, false));
+    if (CW == 4)
+        x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124 /* row_ror:4 */, 0xf, 0xf, false));
     const auto p16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     x = __uint_as_float(p16[0]) + __uint_as_float(p16[1]);
     const auto p32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -67,14 +79,30 @@ __device__ __forceinline__ float sum_lanes_xor8(float x)
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(uint16_t x) { return __uint_as_float(static_cast<unsigned>(x) << 16); }
 
-template <typename Tin, bool HAS_STATE_IN, bool HAS_DOUT>
+// Zeroes n floats (n % 4 == 0, 16-byte aligned) in each of five buffers: the
+// outputs that the SPLIT = 2 workgroups add into.
+__global__ __launch_bounds__(256) void zero5_kernel(float *p0, float *p1, float *p2, float *p3, float *p4, size_t n4)
+{
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    for (size_t e = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x; e < n4; e += static_cast<size_t>(gridDim.x) * 256) {
+        reinterpret_cast<f32x4 *>(p0)[e] = z;
+        reinterpret_cast<f32x4 *>(p1)[e] = z;
+        reinterpret_cast<f32x4 *>(p2)[e] = z;
+        reinterpret_cast<f32x4 *>(p3)[e] = z;
+        reinterpret_cast<f32x4 *>(p4)[e] = z;
+    }
+}
+
+template <typename Tin, bool HAS_STATE_IN, bool HAS_DOUT, int SPLIT>
 __global__ __launch_bounds__(NWB * 64) void wkv7_bwd_kernel(BwdArgs p)
 {
-    __shared__ BwdSmem sm;
+    constexpr int CW = kN / (NWB * SPLIT);  // value columns per wave
+    constexpr int RB = CW;                  // key rows per lane in a column sum
+    __shared__ BwdSmem<CW> sm;
     const int i = threadIdx.x & 63;                                   // key row of this lane
     const int g = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // column block of this wave
-    const int j0 = g * CW;
-    const int bh = blockIdx.x;
+    const int bh = blockIdx.x / SPLIT;
+    const int j0 = ((blockIdx.x % SPLIT) * NWB + g) * CW;
     const int H = p.H, T = p.T;
     const int bb = bh / H, hh = bh - bb * H;
     const Tin *__restrict__ r = static_cast<const Tin *>(p.r);
@@ -157,7 +185,8 @@ __global__ __launch_bounds__(NWB * 64) void wkv7_bwd_kernel(BwdArgs p)
         asm volatile("" ::: "memory");
         // every wave stores the same number of sums (no branch, so that the
         // compiler's count of stores in flight stays exact): a wave with fewer
-        // pairs, or a pair past the batch's last slot, repeats one it has
+        // pairs, or a pair past the batch's last slot, repeats one it has (and
+        // adds zero with it when the sums are added into the outputs)
 #pragma unroll
         for (int m = 0; m < (5 * TB + NWB - 1) / NWB; ++m) {
             const int pi0 = g + NWB * m, pi = pi0 < 5 * TB ? pi0 : pi0 - NWB;
@@ -168,7 +197,11 @@ __global__ __launch_bounds__(NWB * 64) void wkv7_bwd_kernel(BwdArgs p)
                 sum += sm.part[pb][sl][qn][gg][i];
             // (a select, not an indexed array, keeps the pointer's address space known)
             float *const dst = qn == 0 ? p.dr : qn == 1 ? p.dk : qn == 2 ? p.dw : qn == 3 ? p.db : p.da;
-            dst[vec0(t_end + slot_end - sl) * kN + i] = sum;
+            float *const at = dst + vec0(t_end + slot_end - sl) * kN + i;
+            if (SPLIT == 1)
+                *at = sum;
+            else
+                unsafeAtomicAdd(at, pi0 < 5 * TB && sl0 <= slot_end ? sum : 0.0f);
         }
     };
 
@@ -219,10 +252,9 @@ __global__ __launch_bounds__(NWB * 64) void wkv7_bwd_kernel(BwdArgs p)
             for (int qn = 0; qn < 3; ++qn)
                 cs[qn] += xw[qn][row][jj_l];
         }
-        static_assert(CW == 8, "the lane sums add lanes i ^ 8, i ^ 16, i ^ 32");
 #pragma unroll
         for (int qn = 0; qn < 3; ++qn)
-            cs[qn] = sum_lanes_xor8(cs[qn]);
+            cs[qn] = sum_column_lanes<CW>(cs[qn]);
         // lane jj (jj < CW) holds column jj: dv out, c and sa read back by lane reads
         if (i < CW)
             p.dv[e0 + j0 + i] = cs[2];
@@ -294,20 +326,35 @@ __global__ __launch_bounds__(NWB * 64) void wkv7_bwd_kernel(BwdArgs p)
         *reinterpret_cast<f32x4 *>(&p.d_state_in[sbase + jj]) = f32x4{G[jj], G[jj + 1], G[jj + 2], G[jj + 3]};
 }
 
+template <typename Tin, int SPLIT>
+hipError_t launch_bwd_split(const BwdArgs &p, hipStream_t stream)
+{
+    const size_t heads = static_cast<size_t>(p.B) * static_cast<size_t>(p.H);
+    if (SPLIT > 1 && p.T > 0) {
+        const size_t n4 = heads * static_cast<size_t>(p.T) * (kN / 4);
+        const unsigned zblocks = static_cast<unsigned>(std::min<size_t>((n4 + 255) / 256, 4 * kCUs));
+        hipLaunchKernelGGL(zero5_kernel, dim3(zblocks), dim3(256), 0, stream, p.dr, p.dk, p.dw, p.db, p.da, n4);
+    }
+    const dim3 grid(static_cast<unsigned>(heads * SPLIT)), block(NWB * 64);
+    const bool sin = p.state_in != nullptr, dout = p.d_state_out != nullptr;
+    if (sin && dout)
+        hipLaunchKernelGGL((wkv7_bwd_kernel<Tin, true, true, SPLIT>), grid, block, 0, stream, p);
+    else if (sin)
+        hipLaunchKernelGGL((wkv7_bwd_kernel<Tin, true, false, SPLIT>), grid, block, 0, stream, p);
+    else if (dout)
+        hipLaunchKernelGGL((wkv7_bwd_kernel<Tin, false, true, SPLIT>), grid, block, 0, stream, p);
+    else
+        hipLaunchKernelGGL((wkv7_bwd_kernel<Tin, false, false, SPLIT>), grid, block, 0, stream, p);
+    return hipGetLastError();
+}
+
+// one workgroup per compute unit (the LDS of a workgroup is more than half of a
+// unit's): two per head while that still fits in one pass over the units
 template <typename Tin>
 hipError_t launch_bwd_t(const BwdArgs &p, hipStream_t stream)
 {
-    const dim3 grid(static_cast<unsigned>(p.B) * static_cast<unsigned>(p.H)), block(NWB * 64);
-    const bool sin = p.state_in != nullptr, dout = p.d_state_out != nullptr;
-    if (sin && dout)
-        hipLaunchKernelGGL((wkv7_bwd_kernel<Tin, true, true>), grid, block, 0, stream, p);
-    else if (sin)
-        hipLaunchKernelGGL((wkv7_bwd_kernel<Tin, true, false>), grid, block, 0, stream, p);
-    else if (dout)
-        hipLaunchKernelGGL((wkv7_bwd_kernel<Tin, false, true>), grid, block, 0, stream, p);
-    else
-        hipLaunchKernelGGL((wkv7_bwd_kernel<Tin, false, false>), grid, block, 0, stream, p);
-    return hipGetLastError();
+    const int64_t heads = static_cast<int64_t>(p.B) * p.H;
+    return heads * 2 <= kCUs ? launch_bwd_split<Tin, 2>(p, stream) : launch_bwd_split<Tin, 1>(p, stream);
 }
 
 }  // namespace

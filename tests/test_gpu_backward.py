@@ -95,6 +95,31 @@ def test_backward_longer_sequence_sampled_heads(K, oracle_mod):
         print(f"  (b={bb}, h={hh}) ok", flush=True)
 
 
+def test_backward_many_heads_one_workgroup_per_head(K, oracle_mod):
+    # 150 heads: more than half the compute units, so each head runs in one
+    # workgroup (up to 128 heads, in two); the oracle on a sample of (b, h)
+    B, T, H = 3, 9, 50
+    inp = synth.make_inputs(B, T, H, 64, seed=3500, dtype="f32", state_std=0.1)
+    gen = torch.Generator().manual_seed(3501)
+    d_o = torch.randn((B, T, H, 64), generator=gen)
+    d_so = torch.randn((B, H, 64, 64), generator=gen)
+    d = {n: inp[n].cuda() for n in "rwkvab"}
+    s_in = inp["state_in"].cuda()
+    _, _, s_pos = K.wkv7_step(*(d[n] for n in "rwkvab"), s_in, per_position=True)
+    g = K.wkv7_backward(*(d[n] for n in "rwkvab"), s_in, s_pos, d_o.cuda(), d_so.cuda())
+    torch.cuda.synchronize()
+    for bb, hh in [(0, 0), (1, 27), (2, 49)]:
+        sub = {n: inp[n][bb:bb + 1, :, hh:hh + 1] for n in "rwkvab"}
+        ref = oracle_mod.backward(*(sub[n] for n in "rwkvab"), inp["state_in"][bb:bb + 1, hh:hh + 1],
+                                  d_o[bb:bb + 1, :, hh:hh + 1], d_so[bb:bb + 1, hh:hh + 1])
+        for n in NAMES:
+            e = rel_l2(g[n][bb:bb + 1, :, hh:hh + 1], ref[n])
+            assert e <= TOL, f"(b={bb}, h={hh}) {n}: {e:.3e}"
+        e = rel_l2(g["d_state_in"][bb:bb + 1, hh:hh + 1], ref["d_state_in"])
+        assert e <= TOL, f"(b={bb}, h={hh}) d_state_in: {e:.3e}"
+        print(f"  (b={bb}, h={hh}) ok", flush=True)
+
+
 def test_backward_empty_sequence_and_in_place(K):
     inp = synth.make_inputs(2, 0, 3, 64, seed=3400, dtype="bf16", state_std=0.1)
     d = {n: inp[n].cuda() for n in "rwkvab"}
