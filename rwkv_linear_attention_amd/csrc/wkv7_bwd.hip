@@ -41,6 +41,9 @@
 namespace wkv7 {
 namespace {
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
 constexpr int NWB = 8;               // waves per workgroup
 constexpr int NSET = 4;              // tokens of inputs in flight (loaded NSET-1 ahead)
 constexpr int TB = NSET;             // tokens whose row partials are summed together
@@ -112,42 +115,78 @@ __global__ __launch_bounds__(NWB * 64) void wkv7_bwd_kernel(BwdArgs p)
     const Tin *__restrict__ a = static_cast<const Tin *>(p.a);
     const Tin *__restrict__ b = static_cast<const Tin *>(p.b);
     const size_t sbase = static_cast<size_t>(bh) * (kN * kN) + static_cast<size_t>(i) * kN + j0;
-    // element (b, t, h, 0) of the [B, T, H, N] tensors, and (b, t, h, 0, 0) of state_pos
-    auto vec0 = [&](int t) { return (static_cast<size_t>(bb) * T + t) * H + hh; };
+    // Offsets by token: element (b, t, h, 0) of the [B, T, H, N] tensors is
+    // e_of(t) = base_e + t tok_e, and state (b, t, h) in state_pos starts at
+    // spos_h + t tok_s.  The loop walks them with running offsets.  Addresses are
+    // a per-wave base plus a 32-bit lane offset (iu, soff), which the loads take
+    // as they are (a scalar base register and a vector offset).
+    const size_t tok_e = static_cast<size_t>(H) * kN, tok_s = tok_e * kN;
+    const size_t base_e = static_cast<size_t>(bb) * T * tok_e + static_cast<size_t>(hh) * kN;
+    const float *const spos_h = p.state_pos + base_e * kN;
+    const unsigned iu = static_cast<unsigned>(i), soff = iu * kN + j0;
 
     // Everything a token reads (its six inputs, d_o and S_{t-1}) is loaded ahead
     // into a ring of NSET register sets: each token's work is short next to the
     // HBM latency.
-    // d_o and v of the wave's columns are the same for every lane: lane i loads
-    // column j0 + i % CW, and the step reads them back with lane reads (into
-    // scalar registers).  A set holds the values as loaded; conversion and the
-    // zero state happen in the step, so that nothing waits for a load at the
-    // time it is issued.
+    // d_o and v of the wave's columns are the same for every lane: every lane
+    // loads all CW of them (one address for the wave).  The address carries a
+    // zero that the compiler takes as varying by lane: else it moves the values
+    // into scalar registers and waits for the load at the time of the next one.
+    // A set holds the values as loaded; conversion and the zero state happen in
+    // the step, so that nothing waits for a load at the time it is issued.
+    const int lane_zero = static_cast<int>(__builtin_amdgcn_mbcnt_lo(0u, 0u));
+    constexpr int VW = CW * static_cast<int>(sizeof(Tin)) / 4;  // 32-bit words of v's CW values
     struct StepIn {
-        Tin ri, wi, ki, ai, bi, v_l;
-        float dO_l;
+        Tin ri, wi, ki, ai, bi;
+        f32x4 dO4[CW / 4];
+        uint32_t vw[VW];
         f32x4 Sp4[CW / 4];
         bool live;
     };
-    auto load_step = [&](int t, StepIn &s) {
-        const size_t e0 = vec0(t) * kN;
-        s.ri = r[e0 + i];
-        s.wi = w[e0 + i];
-        s.ki = k[e0 + i];
-        s.ai = a[e0 + i];
-        s.bi = b[e0 + i];
-        s.dO_l = p.d_o[e0 + j0 + (i % CW)];
-        s.v_l = v[e0 + j0 + (i % CW)];
-        // S_{t-1}: the state after token t-1, or the input state (zeros without
-        // one: then a valid row is read and not used).  The same loads on every
-        // path keep the compiler's count of loads in flight exact.
-        const float *src = t > 0 ? p.state_pos + vec0(t - 1) * (kN * kN) + static_cast<size_t>(i) * kN + j0
-                                 : HAS_STATE_IN ? p.state_in + sbase
-                                                : p.state_pos + static_cast<size_t>(i) * kN + j0;
-        s.live = t > 0 || HAS_STATE_IN;
+    // token t's inputs (e0 = e_of(t)) and S_{t-1} from the state at src; live:
+    // S_{t-1} is not the zero state (else src is a valid state, read and not
+    // used).  The same loads on every path keep the compiler's count of loads in
+    // flight exact.
+    auto load_step = [&](size_t e0, const float *src, bool live, StepIn &s) {
+        // (the lane offsets, in bytes, pass through an empty asm, so that the
+        // compiler keeps them apart from the bases instead of holding a 64-bit
+        // address per load and token in vector registers)
+        unsigned lo = iu * sizeof(Tin), lz = static_cast<unsigned>(lane_zero), so = soff * 4u;
+        asm volatile("" : "+v"(lo), "+v"(lz), "+v"(so));
+        auto at = [](const void *base, unsigned off) { return static_cast<const char *>(base) + off; };
+        s.ri = *reinterpret_cast<const Tin *>(at(r + e0, lo));
+        s.wi = *reinterpret_cast<const Tin *>(at(w + e0, lo));
+        s.ki = *reinterpret_cast<const Tin *>(at(k + e0, lo));
+        s.ai = *reinterpret_cast<const Tin *>(at(a + e0, lo));
+        s.bi = *reinterpret_cast<const Tin *>(at(b + e0, lo));
 #pragma unroll
         for (int q = 0; q < CW / 4; ++q)
-            s.Sp4[q] = *reinterpret_cast<const f32x4 *>(src + 4 * q);
+            s.dO4[q] = *reinterpret_cast<const f32x4 *>(at(p.d_o + e0 + j0 + 4 * q, lz));
+        const uint32_t *vsrc = reinterpret_cast<const uint32_t *>(at(v + e0 + j0, lz));
+        if (VW % 4 == 0) {
+#pragma unroll
+            for (int q = 0; q < VW; q += 4) {
+                const u32x4 x = *reinterpret_cast<const u32x4 *>(vsrc + q);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    s.vw[q + e] = x[e];
+            }
+        } else {
+            static_assert(VW % 4 == 0 || VW == 2, "v words: a multiple of 4, or 2");
+            const u32x2 x = *reinterpret_cast<const u32x2 *>(vsrc);
+            s.vw[0] = x[0];
+            s.vw[VW > 1 ? 1 : 0] = x[1];
+        }
+        s.live = live;
+#pragma unroll
+        for (int q = 0; q < CW / 4; ++q)
+            s.Sp4[q] = *reinterpret_cast<const f32x4 *>(at(src + 4 * q, so));
+    };
+    // the same for any token t >= 0
+    auto load_token = [&](int t, StepIn &s) {
+        const float *src = t > 0 ? spos_h + static_cast<size_t>(t - 1) * tok_s
+                                 : HAS_STATE_IN ? p.state_in + static_cast<size_t>(bh) * (kN * kN) : spos_h;
+        load_step(base_e + static_cast<size_t>(t) * tok_e, src, t > 0 || HAS_STATE_IN, s);
     };
 
     float G[CW], St[CW];
@@ -160,63 +199,74 @@ __global__ __launch_bounds__(NWB * 64) void wkv7_bwd_kernel(BwdArgs p)
             *reinterpret_cast<f32x4 *>(&p.d_state_in[sbase + jj]) = f32x4{G[jj], G[jj + 1], G[jj + 2], G[jj + 3]};
         return;
     }
-    {
-        const float *src = p.state_pos + vec0(T - 1) * (kN * kN) + static_cast<size_t>(i) * kN + j0;
 #pragma unroll
-        for (int jj = 0; jj < CW; jj += 4) {
-            const f32x4 x4 = *reinterpret_cast<const f32x4 *>(src + jj);
+    for (int jj = 0; jj < CW; jj += 4) {
+        const f32x4 x4 = *reinterpret_cast<const f32x4 *>((spos_h + static_cast<size_t>(T - 1) * tok_s) + (soff + jj));
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                St[jj + e] = x4[e];
-        }
+        for (int e = 0; e < 4; ++e)
+            St[jj + e] = x4[e];
     }
-    // lane roles in the column sums: column jj_l of this wave, rows CW rb .. CW rb + CW - 1
+    // lane roles in the column sums: column jj_l of this wave, rows RB rb .. RB rb + RB - 1
     const int jj_l = i % CW, rb = i / CW;
 
-    // the row partials of the TB tokens of batch kb (fewer in the last), whose
-    // last token is t_end, at slot slot_end: written by every wave, one barrier,
-    // then the 5 x TB sums spread over the waves
-    auto finish_batch = [&](int t_end, int slot_end, int pb) {
+    // The row partials of a batch of TB tokens (fewer in the last) are written
+    // by every wave, and after one barrier the 5 x TB sums are spread over the
+    // waves: sum m of wave g is pair g + NWB m = 5 slot + quantity.  Every wave
+    // stores the same number of sums (no branch, so that the compiler's count of
+    // stores in flight stays exact): a wave with fewer pairs, or a pair past the
+    // batch's last slot, repeats one it has (and adds zero with it when the sums
+    // are added into the outputs).
+    constexpr int NM = (5 * TB + NWB - 1) / NWB;
+    float *dst[NM];
+    int sl0[NM];
+    bool extra[NM];
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+        const int pi0 = g + NWB * m, pi = pi0 < 5 * TB ? pi0 : pi0 - NWB;
+        sl0[m] = pi / 5;
+        const int qn = pi - 5 * sl0[m];
+        extra[m] = pi0 >= 5 * TB;
+        // (a select, not an indexed array, keeps the pointer's address space known)
+        dst[m] = qn == 0 ? p.dr : qn == 1 ? p.dk : qn == 2 ? p.dw : qn == 3 ? p.db : p.da;
+    }
+    // e_end: e_of the batch's last token, whose slot is slot_end
+    auto finish_batch = [&](size_t e_end, int slot_end, int pb) {
         // a barrier for the LDS partials only: waiting here for this wave's LDS
         // writes (not for its global loads and stores, which a full fence would
         // include, and with them the loads issued for the tokens ahead)
         __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        // every wave stores the same number of sums (no branch, so that the
-        // compiler's count of stores in flight stays exact): a wave with fewer
-        // pairs, or a pair past the batch's last slot, repeats one it has (and
-        // adds zero with it when the sums are added into the outputs)
 #pragma unroll
-        for (int m = 0; m < (5 * TB + NWB - 1) / NWB; ++m) {
-            const int pi0 = g + NWB * m, pi = pi0 < 5 * TB ? pi0 : pi0 - NWB;
-            const int sl0 = pi / 5, qn = pi - 5 * sl0, sl = min(sl0, slot_end);
+        for (int m = 0; m < NM; ++m) {
+            const int sl = min(sl0[m], slot_end);
+            const int qn = (g + NWB * m - (extra[m] ? NWB : 0)) - 5 * sl0[m];
             float sum = 0.f;
 #pragma unroll
             for (int gg = 0; gg < NWB; ++gg)
                 sum += sm.part[pb][sl][qn][gg][i];
-            // (a select, not an indexed array, keeps the pointer's address space known)
-            float *const dst = qn == 0 ? p.dr : qn == 1 ? p.dk : qn == 2 ? p.dw : qn == 3 ? p.db : p.da;
-            float *const at = dst + vec0(t_end + slot_end - sl) * kN + i;
+            float *const at = (dst[m] + e_end + static_cast<size_t>(slot_end - sl) * tok_e) + iu;
             if (SPLIT == 1)
                 *at = sum;
             else
-                unsafeAtomicAdd(at, pi0 < 5 * TB && sl0 <= slot_end ? sum : 0.0f);
+                unsafeAtomicAdd(at, !extra[m] && sl0[m] <= slot_end ? sum : 0.0f);
         }
     };
 
-    // one token of the adjoint, from its loaded inputs; slot is its place in its
-    // batch of TB tokens, pb the batch's partial buffer
-    auto step = [&](int t, const StepIn &s, int slot, int pb) {
-        const size_t e0 = vec0(t) * kN;
+    // one token of the adjoint (e0 = e_of(t)), from its loaded inputs; slot is its
+    // place in its batch of TB tokens, pb the batch's partial buffer; live_known:
+    // S_{t-1} is known to be a loaded state (t > 0 or an input state)
+    auto step = [&](size_t e0, const StepIn &s, int slot, int pb, bool live_known) {
         const float ri = to_f32(s.ri), wi = to_f32(s.wi), ki = to_f32(s.ki), ai = to_f32(s.ai), bi = to_f32(s.bi);
-        const float v_l = to_f32(s.v_l);
         float dO[CW], vv[CW], Sp[CW];
 #pragma unroll
         for (int jj = 0; jj < CW; ++jj) {
-            dO[jj] = lane_bcast(s.dO_l, jj);
-            vv[jj] = lane_bcast(v_l, jj);
-            Sp[jj] = s.live ? s.Sp4[jj / 4][jj % 4] : 0.0f;
+            dO[jj] = s.dO4[jj / 4][jj % 4];
+            if (sizeof(Tin) == 4)
+                vv[jj] = __uint_as_float(s.vw[jj]);
+            else  // two bf16 per word, the lower one first
+                vv[jj] = __uint_as_float(jj % 2 == 0 ? s.vw[jj / 2] << 16 : s.vw[jj / 2] & 0xffff0000u);
+            Sp[jj] = live_known || s.live ? s.Sp4[jj / 4][jj % 4] : 0.0f;
         }
 
         // G += r_t do_t^T, then the row partials that need only G, S_t, S_{t-1}
@@ -255,9 +305,9 @@ __global__ __launch_bounds__(NWB * 64) void wkv7_bwd_kernel(BwdArgs p)
 #pragma unroll
         for (int qn = 0; qn < 3; ++qn)
             cs[qn] = sum_column_lanes<CW>(cs[qn]);
-        // lane jj (jj < CW) holds column jj: dv out, c and sa read back by lane reads
-        if (i < CW)
-            p.dv[e0 + j0 + i] = cs[2];
+        // every lane holds the sums of its column jj_l: dv out (the lanes of a
+        // column store the same value), c and sa read back by lane reads
+        (p.dv + e0 + j0)[static_cast<unsigned>(jj_l)] = cs[2];
         float c[CW], sa[CW];
 #pragma unroll
         for (int jj = 0; jj < CW; ++jj) {
@@ -287,23 +337,29 @@ __global__ __launch_bounds__(NWB * 64) void wkv7_bwd_kernel(BwdArgs p)
     // n % TB of batch n / TB.  Its S_{t-1} is the next token's S_t, so the set stays
     // live one token more: after token t runs, the set of token t+1 is refilled
     // with token t+1-NSET (NSET-1 tokens ahead).  The loop holds whole rounds
-    // whose loads are all real (so the compiler's wait analysis sees one steady
-    // state and waits only for loads a round old) and whose batch ends at a fixed
-    // place; the last one or two rounds follow it.
+    // whose loads are all real and of tokens t > 0 (so the compiler's wait
+    // analysis sees one steady state and waits only for loads a round old) and
+    // whose batch ends at a fixed place; the last rounds follow it.
     static_assert(TB == NSET, "a round of the loop is one batch");
     StepIn ring[NSET];
 #pragma unroll
     for (int u = 0; u < NSET; ++u)
-        load_step(max(T - 1 - u, 0), ring[u]);  // (a set past token 0 is never used)
-    step(T - 1, ring[0], 0, 0);
+        load_token(max(T - 1 - u, 0), ring[u]);  // (a set past token 0 is never used)
+    step(base_e + static_cast<size_t>(T - 1) * tok_e, ring[0], 0, 0, false);
     int t0 = T - 2, kb = 0;  // batch of the round's first token (n = 4 kb + 1)
-    for (; t0 >= 2 * NSET - 2; t0 -= NSET, ++kb) {
+    if (t0 >= 2 * NSET - 1) {
+        size_t er = base_e + static_cast<size_t>(t0) * tok_e;           // e_of(t0)
+        const float *sr = spos_h + static_cast<size_t>(t0 - NSET) * tok_s;  // state of t0 - NSET
+        for (; t0 >= 2 * NSET - 1; t0 -= NSET, ++kb, er -= NSET * tok_e, sr -= NSET * tok_s) {
 #pragma unroll
-        for (int u = 0; u < NSET; ++u) {
-            step(t0 - u, ring[(u + 1) % NSET], (u + 1) % TB, (kb + (u + 1) / TB) & 1);
-            load_step(t0 - u + 1 - NSET, ring[u]);
-            if (u == TB - 2)
-                finish_batch(t0 - u, TB - 1, kb & 1);
+            for (int u = 0; u < NSET; ++u) {
+                // token t0 - u (t >= NSET, its S_{t-1} loaded), then the load of
+                // token t0 - u + 1 - NSET (>= 1), whose S_{t-1} is state t0 - u - NSET
+                step(er - u * tok_e, ring[(u + 1) % NSET], (u + 1) % TB, (kb + (u + 1) / TB) & 1, true);
+                load_step(er - (u - 1 + NSET) * tok_e, sr - u * tok_s, true, ring[u]);
+                if (u == TB - 2)
+                    finish_batch(er - u * tok_e, TB - 1, kb & 1);
+            }
         }
     }
     for (; t0 >= 0; t0 -= NSET, ++kb) {
@@ -312,15 +368,16 @@ __global__ __launch_bounds__(NWB * 64) void wkv7_bwd_kernel(BwdArgs p)
             const int t = t0 - u;
             if (t >= 0) {
                 const int pb = (kb + (u + 1) / TB) & 1;
-                step(t, ring[(u + 1) % NSET], (u + 1) % TB, pb);
-                load_step(max(t + 1 - NSET, 0), ring[u]);
+                const size_t e0 = base_e + static_cast<size_t>(t) * tok_e;
+                step(e0, ring[(u + 1) % NSET], (u + 1) % TB, pb, false);
+                load_token(max(t + 1 - NSET, 0), ring[u]);
                 if (u == TB - 2 || t == 0)
-                    finish_batch(t, (u + 1) % TB, pb);
+                    finish_batch(e0, (u + 1) % TB, pb);
             }
         }
     }
     if (T == 1)
-        finish_batch(0, 0, 0);
+        finish_batch(base_e, 0, 0);
 #pragma unroll
     for (int jj = 0; jj < CW; jj += 4)
         *reinterpret_cast<f32x4 *>(&p.d_state_in[sbase + jj]) = f32x4{G[jj], G[jj + 1], G[jj + 2], G[jj + 3]};
