@@ -56,7 +56,8 @@ def recurrent_flops(wl) -> int:
 
 def kernel_source_hash(kind: str) -> str:
     name = {"step": "wkv7_step.hip", "verify": "wkv7_step.hip", "chunk": "wkv7_chunk.hip",
-            "step_tail": "wkv7_step.hip", "tail_pass": "wkv7_tail.hip", "bwd": "wkv7_bwd.hip"}[kind]
+            "step_tail": "wkv7_step.hip", "tail_pass": "wkv7_tail.hip", "bwd": "wkv7_bwd.hip",
+            "bwd_zero": "wkv7_bwd.hip"}[kind]
     h = hashlib.sha256()
     for f in (name, "wkv7_device.h"):
         with open(os.path.join(CSRC, f), "rb") as fh:
@@ -64,8 +65,14 @@ def kernel_source_hash(kind: str) -> str:
     return h.hexdigest()[:16]
 
 
+# kernels that one call runs besides the named one: the backward pass with two
+# workgroups per head first zeroes the outputs they add into ("bwd_zero")
+CALL_KERNELS = {"bwd": ("bwd", "bwd_zero")}
+
+
 def read_traffic(kind: str, workload: int):
-    """HBM bytes per launch from profiles/hbm_traffic.txt, or None when absent or stale.
+    """HBM bytes per launch (per call: every kernel of CALL_KERNELS[kind]) from
+    profiles/hbm_traffic.txt, or None when absent or stale.
 
     Lines: <kernel-kind> <workload> <source-hash> <fetch_bytes> <write_bytes>
     (bytes already scaled by the copy-kernel calibration factor).
@@ -74,14 +81,16 @@ def read_traffic(kind: str, workload: int):
     if not os.path.exists(path):
         return None
     cur = kernel_source_hash(kind)
+    want = CALL_KERNELS.get(kind, (kind,))
+    found = {}
     with open(path) as f:
         for line in f:
             parts = line.split("#", 1)[0].split()
-            if len(parts) == 5 and parts[0] == kind and parts[1] == str(workload):
+            if len(parts) == 5 and parts[0] in want and parts[1] == str(workload):
                 if parts[2] != cur:
                     return None
-                return int(float(parts[3]) + float(parts[4]))
-    return None
+                found[parts[0]] = float(parts[3]) + float(parts[4])
+    return int(sum(found.values())) if len(found) == len(want) else None
 
 
 def roofline(bytes_per_launch: int, sec_per_launch: float, kind: str, workload: int):
