@@ -49,33 +49,36 @@ constexpr int NSET = 4;              // tokens of inputs in flight (loaded NSET-
 constexpr int TB = NSET;             // tokens whose row partials are summed together
 constexpr int kCUs = 256;            // compute units of the MI355X
 
+// The column sums over the 64 key rows (c = G^T b, sa = S_{t-1}^T a, dv = G^T k)
+// go through LDS.  There are 3 CW (quantity, column) pairs; pair P is summed by
+// the L lanes L P .. L P + L - 1 (lane L P + h adds rows RPL h .. RPL h + RPL - 1),
+// and one or two quad exchanges finish it.  Lanes past the 3 CW pairs repeat
+// pairs of the third quantity.
 template <int CW>
-struct alignas(16) BwdSmem {
-    float x[NWB][3][kN][CW];          // per-wave column-sum terms, row i at xrow(i)
-    float part[2][TB][5][NWB][kN];    // per-wave row partials (dr, dk, dw, db, da) of TB tokens
+struct ColSum {
+    static constexpr int L = CW == 4 ? 4 : 2;   // lanes per pair (3 CW pairs in 64 / L slots)
+    static constexpr int RPL = kN / L;           // key rows per lane
+    // Storage: quantity q, row block h (RPL rows), row rr, column jj at
+    // q QS + h BS + rr CW + jj.  The padding (CW per block) makes the 32 lanes of
+    // a half wave, which read one row rr at a time, fall in 32 different banks:
+    // jj in the low bits, and (q, h) in distinct groups of CW banks.
+    static constexpr int BS = RPL * CW + CW;
+    static constexpr int QS = L * BS;
+    static_assert(3 * CW <= kN / L && kN / L - 3 * CW <= CW, "pairs and their repeats fit the lanes");
 };
 
-// Storage row of key row i in x: XOR-ed with (i / 8) % 4.  The 32 lanes of a
-// half wave that read together read rows CW rb + rr (fixed rr) for CW = 8
-// (rows of 8 banks, rb < 4) or CW = 4 (rows of 4 banks, rb < 8): the XOR puts
-// them in 32 / CW different bank groups (4-byte reads, 32 banks).
-__device__ __forceinline__ int xrow(int i) { return i ^ ((i >> 3) & 3); }
-
-// Sum of x over the lanes with the same lane % CW (CW = 8 or 4), returned to all
-// of them: row rotations (by 8, then by 4 for CW = 4) within rows of 16 lanes,
-// then the row-pair and half-wave swaps of gfx950, all in the vector ALU.  The
-// lanes of a group end with the same value.
 template <int CW>
-__device__ __forceinline__ float sum_column_lanes(float x)
+struct alignas(16) BwdSmem {
+    float x[NWB][3 * ColSum<CW>::QS];  // per-wave column-sum terms
+    float part[2][TB][5][NWB][kN];     // per-wave row partials (dr, dk, dw, db, da) of TB tokens
+};
+
+// x plus its value in lane l ^ m (m = 1 or 2: within groups of four lanes)
+template <int M>
+__device__ __forceinline__ float add_quad_xor(float x)
 {
-    static_assert(CW == 8 || CW == 4, "eight or four columns per wave");
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128 /* row_ror:8 */, 0xf, 0xf, false));
-    if (CW == 4)
-        x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124 /* row_ror:4 */, 0xf, 0xf, false));
-    const auto p16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    x = __uint_as_float(p16[0]) + __uint_as_float(p16[1]);
-    const auto p32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(p32[0]) + __uint_as_float(p32[1]);
+    constexpr int ctrl = M == 1 ? 0xB1 /* quad_perm [1,0,3,2] */ : 0x4E /* quad_perm [2,3,0,1] */;
+    return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), ctrl, 0xf, 0xf, false));
 }
 
 // an input element as loaded (fp32, or the upper half of an fp32 for bf16)
@@ -100,7 +103,7 @@ template <typename Tin, bool HAS_STATE_IN, bool HAS_DOUT, int SPLIT>
 __global__ __launch_bounds__(NWB * 64) void wkv7_bwd_kernel(BwdArgs p)
 {
     constexpr int CW = kN / (NWB * SPLIT);  // value columns per wave
-    constexpr int RB = CW;                  // key rows per lane in a column sum
+    using CS = ColSum<CW>;
     __shared__ BwdSmem<CW> sm;
     const int i = threadIdx.x & 63;                                   // key row of this lane
     const int g = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // column block of this wave
@@ -206,8 +209,13 @@ __global__ __launch_bounds__(NWB * 64) void wkv7_bwd_kernel(BwdArgs p)
         for (int e = 0; e < 4; ++e)
             St[jj + e] = x4[e];
     }
-    // lane roles in the column sums: column jj_l of this wave, rows RB rb .. RB rb + RB - 1
-    const int jj_l = i % CW, rb = i / CW;
+    // lane roles in the column sums: this lane writes key row i at x_w; it adds
+    // pair P (quantity P / CW, column P % CW), rows RPL h .. RPL h + RPL - 1, from
+    // x_r; after the half-wave swap it holds dv of column dv_col
+    const int x_w = (i / CS::RPL) * CS::BS + (i % CS::RPL) * CW;
+    const int P0 = i / CS::L, P = P0 < 3 * CW ? P0 : P0 - CW, h = i % CS::L;
+    const int x_r = (P / CW) * CS::QS + h * CS::BS + P % CW;
+    const int Pu = (i | 32) / CS::L, dv_col = (Pu < 3 * CW ? Pu : Pu - CW) % CW;
 
     // The row partials of a batch of TB tokens (fewer in the last) are written
     // by every wave, and after one barrier the 5 x TB sums are spread over the
@@ -280,7 +288,7 @@ __global__ __launch_bounds__(NWB * 64) void wkv7_bwd_kernel(BwdArgs p)
         }
 
         // column sums over the 64 key rows: c = G^T b, sa = S_{t-1}^T a, dv = G^T k
-        float (*xw)[kN][CW] = sm.x[g];
+        float *const xw = sm.x[g];
 #pragma unroll
         for (int jj = 0; jj < CW; jj += 4) {
             f32x4 xc, xs, xv;
@@ -290,30 +298,30 @@ __global__ __launch_bounds__(NWB * 64) void wkv7_bwd_kernel(BwdArgs p)
                 xs[e] = ai * Sp[jj + e];
                 xv[e] = ki * G[jj + e];
             }
-            *reinterpret_cast<f32x4 *>(&xw[0][xrow(i)][jj]) = xc;
-            *reinterpret_cast<f32x4 *>(&xw[1][xrow(i)][jj]) = xs;
-            *reinterpret_cast<f32x4 *>(&xw[2][xrow(i)][jj]) = xv;
+            *reinterpret_cast<f32x4 *>(&xw[x_w + jj]) = xc;
+            *reinterpret_cast<f32x4 *>(&xw[CS::QS + x_w + jj]) = xs;
+            *reinterpret_cast<f32x4 *>(&xw[2 * CS::QS + x_w + jj]) = xv;
         }
-        float cs[3] = {0.f, 0.f, 0.f};
+        // (four running sums, added as a tree: a short chain)
+        float c4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int rr = 0; rr < RB; ++rr) {
-            const int row = xrow(RB * rb + rr);
-#pragma unroll
-            for (int qn = 0; qn < 3; ++qn)
-                cs[qn] += xw[qn][row][jj_l];
-        }
-#pragma unroll
-        for (int qn = 0; qn < 3; ++qn)
-            cs[qn] = sum_column_lanes<CW>(cs[qn]);
-        // every lane holds the sums of its column jj_l: dv out (the lanes of a
-        // column store the same value), c and sa read back by lane reads
-        (p.dv + e0 + j0)[static_cast<unsigned>(jj_l)] = cs[2];
+        for (int rr = 0; rr < CS::RPL; ++rr)
+            c4[rr % 4] += xw[x_r + rr * CW];
+        float cs = (c4[0] + c4[1]) + (c4[2] + c4[3]);
+        cs = add_quad_xor<1>(cs);
+        if (CS::L == 4)
+            cs = add_quad_xor<2>(cs);
+        // lane L P holds pair P: c and sa read back by lane reads; dv sits in the
+        // upper half-wave, and the half-wave swap gives it to every lane (the
+        // lanes of a column store the same value)
         float c[CW], sa[CW];
 #pragma unroll
         for (int jj = 0; jj < CW; ++jj) {
-            c[jj] = lane_bcast(cs[0], jj);
-            sa[jj] = lane_bcast(cs[1], jj);
+            c[jj] = lane_bcast(cs, CS::L * jj);
+            sa[jj] = lane_bcast(cs, CS::L * (CW + jj));
         }
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(cs), __float_as_uint(cs), false, false);
+        (p.dv + e0 + j0)[static_cast<unsigned>(dv_col)] = __uint_as_float(sw[1]);
 
         // row partials that need c and sa, then G for the previous token
         float p_db = 0.f, p_da = 0.f;
