@@ -249,6 +249,10 @@ int wkv7_state_commit(const float *state_pos, const int *accepted, const float *
  * The inputs may be NULL when T = 0 (then d_state_in becomes d_state_out, or
  * zeros).  No output may overlap another buffer, except d_state_in ==
  * d_state_out.  B * H <= WKV7_MAX_HEADS_STEP.
+ * With B * H <= 128 a head runs as two workgroups of 32 value columns each, and
+ * the call launches two kernels on the stream: a fill that zeroes dr, dk, dw,
+ * db, da, then the pass, whose two workgroups per head add their row sums into
+ * them (two terms, so the order of the adds does not change the sum).
  */
 int wkv7_backward(const void *r, const void *w, const void *k, const void *v,
                   const void *a, const void *b, int in_dtype, const float *state_in,
