@@ -120,6 +120,33 @@ def test_backward_many_heads_one_workgroup_per_head(K, oracle_mod):
         print(f"  (b={bb}, h={hh}) ok", flush=True)
 
 
+@pytest.mark.parametrize("H", [2, 129])
+def test_backward_every_short_length(K, oracle_mod, H):
+    # T = 1 .. 10 covers every way the token loop splits into its first step, whole
+    # rounds of four and the last partial rounds; H = 2 runs two workgroups per head,
+    # H = 129 one (more than 128 heads); the oracle on heads 0 and H - 1
+    for T in range(1, 11):
+        inp = synth.make_inputs(1, T, H, 64, seed=3600 + T, dtype="bf16", state_std=0.1)
+        gen = torch.Generator().manual_seed(3700 + T)
+        d_o = torch.randn((1, T, H, 64), generator=gen)
+        d_so = torch.randn((1, H, 64, 64), generator=gen)
+        d = {n: inp[n].cuda() for n in "rwkvab"}
+        s_in = inp["state_in"].cuda()
+        _, _, s_pos = K.wkv7_step(*(d[n] for n in "rwkvab"), s_in, per_position=True)
+        g = K.wkv7_backward(*(d[n] for n in "rwkvab"), s_in, s_pos, d_o.cuda(), d_so.cuda())
+        torch.cuda.synchronize()
+        for hh in (0, H - 1):
+            sub = {n: inp[n][:, :, hh:hh + 1] for n in "rwkvab"}
+            ref = oracle_mod.backward(*(sub[n] for n in "rwkvab"), inp["state_in"][:, hh:hh + 1],
+                                      d_o[:, :, hh:hh + 1], d_so[:, hh:hh + 1])
+            for n in NAMES:
+                e = rel_l2(g[n][:, :, hh:hh + 1], ref[n])
+                assert e <= TOL, f"T={T} h={hh} {n}: {e:.3e}"
+            e = rel_l2(g["d_state_in"][:, hh:hh + 1], ref["d_state_in"])
+            assert e <= TOL, f"T={T} h={hh} d_state_in: {e:.3e}"
+        print(f"  H={H} T={T} ok", flush=True)
+
+
 def test_backward_empty_sequence_and_in_place(K):
     inp = synth.make_inputs(2, 0, 3, 64, seed=3400, dtype="bf16", state_std=0.1)
     d = {n: inp[n].cuda() for n in "rwkvab"}
