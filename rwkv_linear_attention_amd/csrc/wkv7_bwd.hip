@@ -29,10 +29,9 @@
 //    workgroups' sums meet in an atomic add onto zeroed outputs: two terms, so
 //    the result does not depend on their order.
 //  * Sums over the key rows (c, S_{t-1}^T a, dv) stay inside a wave: the lanes
-//    write their CW terms to LDS, and lane (jj, rb) adds column jj over rows
-//    CW rb .. CW rb + CW - 1, stored so that the row blocks read together fall in
-//    different banks, before cross-lane steps in the vector ALU finish the sum
-//    and lane reads hand c and S_{t-1}^T a to every lane.
+//    write their CW terms of each to LDS, a group of lanes adds each (quantity,
+//    column) pair over the rows, and quad exchanges in the vector ALU finish
+//    it; lane reads hand c and S_{t-1}^T a to every lane (ColSum below).
 // Each token's inputs and S_{t-1} are loaded three tokens ahead.  All arithmetic
 // is fp32; gradients are written as fp32.
 #include "wkv7_device.h"
