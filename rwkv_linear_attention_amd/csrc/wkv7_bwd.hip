@@ -40,6 +40,7 @@
 namespace wkv7 {
 namespace {
 
+#define GLOBAL_AS __attribute__((address_space(1)))
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -145,51 +146,58 @@ __global__ __launch_bounds__(NWB * 64) void wkv7_bwd_kernel(BwdArgs p)
         f32x4 Sp4[CW / 4];
         bool live;
     };
-    // token t's inputs (e0 = e_of(t)) and S_{t-1} from the state at src; live:
-    // S_{t-1} is not the zero state (else src is a valid state, read and not
-    // used).  The same loads on every path keep the compiler's count of loads in
-    // flight exact.
-    auto load_step = [&](size_t e0, const float *src, bool live, StepIn &s) {
-        // (the lane offsets, in bytes, pass through an empty asm, so that the
-        // compiler keeps them apart from the bases instead of holding a 64-bit
-        // address per load and token in vector registers)
+    // The byte addresses of one token: its (b, t, h) rows of the six inputs and
+    // of d_o (v and d_o at the wave's columns), and the state S_{t-1}.  They are
+    // typed as global memory: in the loop they pass through an empty asm, after
+    // which the compiler could no longer tell.
+    typedef const GLOBAL_AS char *gchar;
+    struct TokPtrs {
+        gchar r, w, k, a, b, v, d_o, s;
+    };
+    // One token's loads into a set; live: S_{t-1} is not the zero state.  The
+    // same loads on every path keep the compiler's count of loads in flight
+    // exact.  (The lane offsets, in bytes, pass through an empty asm, so that the
+    // compiler keeps them apart from the bases instead of holding 64-bit
+    // addresses per load in vector registers.)
+    auto load_ptrs = [&](const TokPtrs &q, bool live, StepIn &s) {
         unsigned lo = iu * sizeof(Tin), lz = static_cast<unsigned>(lane_zero), so = soff * 4u;
         asm volatile("" : "+v"(lo), "+v"(lz), "+v"(so));
-        auto at = [](const void *base, unsigned off) { return static_cast<const char *>(base) + off; };
-        s.ri = *reinterpret_cast<const Tin *>(at(r + e0, lo));
-        s.wi = *reinterpret_cast<const Tin *>(at(w + e0, lo));
-        s.ki = *reinterpret_cast<const Tin *>(at(k + e0, lo));
-        s.ai = *reinterpret_cast<const Tin *>(at(a + e0, lo));
-        s.bi = *reinterpret_cast<const Tin *>(at(b + e0, lo));
+        s.ri = *reinterpret_cast<const GLOBAL_AS Tin *>(q.r + lo);
+        s.wi = *reinterpret_cast<const GLOBAL_AS Tin *>(q.w + lo);
+        s.ki = *reinterpret_cast<const GLOBAL_AS Tin *>(q.k + lo);
+        s.ai = *reinterpret_cast<const GLOBAL_AS Tin *>(q.a + lo);
+        s.bi = *reinterpret_cast<const GLOBAL_AS Tin *>(q.b + lo);
 #pragma unroll
-        for (int q = 0; q < CW / 4; ++q)
-            s.dO4[q] = *reinterpret_cast<const f32x4 *>(at(p.d_o + e0 + j0 + 4 * q, lz));
-        const uint32_t *vsrc = reinterpret_cast<const uint32_t *>(at(v + e0 + j0, lz));
+        for (int qq = 0; qq < CW / 4; ++qq)
+            s.dO4[qq] = *reinterpret_cast<const GLOBAL_AS f32x4 *>(q.d_o + 16 * qq + lz);
         if (VW % 4 == 0) {
 #pragma unroll
-            for (int q = 0; q < VW; q += 4) {
-                const u32x4 x = *reinterpret_cast<const u32x4 *>(vsrc + q);
+            for (int qq = 0; qq < VW; qq += 4) {
+                const u32x4 x = *reinterpret_cast<const GLOBAL_AS u32x4 *>(q.v + 4 * qq + lz);
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    s.vw[q + e] = x[e];
+                    s.vw[qq + e] = x[e];
             }
         } else {
-            static_assert(VW % 4 == 0 || VW == 2, "v words: a multiple of 4, or 2");
-            const u32x2 x = *reinterpret_cast<const u32x2 *>(vsrc);
+            const u32x2 x = *reinterpret_cast<const GLOBAL_AS u32x2 *>(q.v + lz);
             s.vw[0] = x[0];
             s.vw[VW > 1 ? 1 : 0] = x[1];
         }
         s.live = live;
 #pragma unroll
-        for (int q = 0; q < CW / 4; ++q)
-            s.Sp4[q] = *reinterpret_cast<const f32x4 *>(at(src + 4 * q, so));
+        for (int qq = 0; qq < CW / 4; ++qq)
+            s.Sp4[qq] = *reinterpret_cast<const GLOBAL_AS f32x4 *>(q.s + 16 * qq + so);
     };
-    // the same for any token t >= 0
-    auto load_token = [&](int t, StepIn &s) {
+    auto gb = [](const void *x) { return (gchar)(static_cast<const char *>(x)); };
+    // the addresses of token t; its S_{t-1} is the input state for t = 0 (or,
+    // without one, a valid state that is read and not used)
+    auto ptrs_of = [&](int t) {
+        const size_t e = base_e + static_cast<size_t>(t) * tok_e;
         const float *src = t > 0 ? spos_h + static_cast<size_t>(t - 1) * tok_s
                                  : HAS_STATE_IN ? p.state_in + static_cast<size_t>(bh) * (kN * kN) : spos_h;
-        load_step(base_e + static_cast<size_t>(t) * tok_e, src, t > 0 || HAS_STATE_IN, s);
+        return TokPtrs{gb(r + e), gb(w + e), gb(k + e), gb(a + e), gb(b + e), gb(v + e + j0), gb(p.d_o + e + j0), gb(src)};
     };
+    auto load_token = [&](int t, StepIn &s) { load_ptrs(ptrs_of(t), t > 0 || HAS_STATE_IN, s); };
 
     float G[CW], St[CW];
 #pragma unroll
@@ -224,7 +232,6 @@ __global__ __launch_bounds__(NWB * 64) void wkv7_bwd_kernel(BwdArgs p)
     // batch's last slot, repeats one it has (and adds zero with it when the sums
     // are added into the outputs).
     constexpr int NM = (5 * TB + NWB - 1) / NWB;
-    float *dst[NM];
     int sl0[NM];
     bool extra[NM];
 #pragma unroll
@@ -233,8 +240,6 @@ __global__ __launch_bounds__(NWB * 64) void wkv7_bwd_kernel(BwdArgs p)
         sl0[m] = pi / 5;
         const int qn = pi - 5 * sl0[m];
         extra[m] = pi0 >= 5 * TB;
-        // (a select, not an indexed array, keeps the pointer's address space known)
-        dst[m] = qn == 0 ? p.dr : qn == 1 ? p.dk : qn == 2 ? p.dw : qn == 3 ? p.db : p.da;
     }
     // e_end: e_of the batch's last token, whose slot is slot_end
     auto finish_batch = [&](size_t e_end, int slot_end, int pb) {
@@ -252,7 +257,9 @@ __global__ __launch_bounds__(NWB * 64) void wkv7_bwd_kernel(BwdArgs p)
 #pragma unroll
             for (int gg = 0; gg < NWB; ++gg)
                 sum += sm.part[pb][sl][qn][gg][i];
-            float *const at = (dst[m] + e_end + static_cast<size_t>(slot_end - sl) * tok_e) + iu;
+            // (a select, not an indexed array, keeps the pointer's address space known)
+            float *const dst = qn == 0 ? p.dr : qn == 1 ? p.dk : qn == 2 ? p.dw : qn == 3 ? p.db : p.da;
+            float *const at = (dst + e_end + static_cast<size_t>(slot_end - sl) * tok_e) + iu;
             if (SPLIT == 1)
                 *at = sum;
             else
@@ -355,15 +362,24 @@ __global__ __launch_bounds__(NWB * 64) void wkv7_bwd_kernel(BwdArgs p)
     step(base_e + static_cast<size_t>(T - 1) * tok_e, ring[0], 0, 0, false);
     int t0 = T - 2, kb = 0;  // batch of the round's first token (n = 4 kb + 1)
     if (t0 >= 2 * NSET - 1) {
-        size_t er = base_e + static_cast<size_t>(t0) * tok_e;           // e_of(t0)
-        const float *sr = spos_h + static_cast<size_t>(t0 - NSET) * tok_s;  // state of t0 - NSET
-        for (; t0 >= 2 * NSET - 1; t0 -= NSET, ++kb, er -= NSET * tok_e, sr -= NSET * tok_s) {
+        size_t er = base_e + static_cast<size_t>(t0) * tok_e;  // e_of(t0)
+        // the next token to load, t0 + 1 - NSET: running per-tensor addresses, one
+        // token back after each load (through an empty asm, so that the compiler
+        // keeps eight scalar pointers, not an address per tensor and token, which
+        // ran out of scalar registers)
+        TokPtrs lp = ptrs_of(t0 + 1 - NSET);
+        const size_t tb_in = tok_e * sizeof(Tin), tb_f = tok_e * 4, tb_s = tok_s * 4;  // bytes per token
+        for (; t0 >= 2 * NSET - 1; t0 -= NSET, ++kb, er -= NSET * tok_e) {
 #pragma unroll
             for (int u = 0; u < NSET; ++u) {
                 // token t0 - u (t >= NSET, its S_{t-1} loaded), then the load of
                 // token t0 - u + 1 - NSET (>= 1), whose S_{t-1} is state t0 - u - NSET
                 step(er - u * tok_e, ring[(u + 1) % NSET], (u + 1) % TB, (kb + (u + 1) / TB) & 1, true);
-                load_step(er - (u - 1 + NSET) * tok_e, sr - u * tok_s, true, ring[u]);
+                load_ptrs(lp, true, ring[u]);
+                lp.r -= tb_in; lp.w -= tb_in; lp.k -= tb_in; lp.a -= tb_in; lp.b -= tb_in; lp.v -= tb_in;
+                lp.d_o -= tb_f; lp.s -= tb_s;
+                asm volatile("" : "+s"(lp.r), "+s"(lp.w), "+s"(lp.k), "+s"(lp.a), "+s"(lp.b), "+s"(lp.v),
+                             "+s"(lp.d_o), "+s"(lp.s));
                 if (u == TB - 2)
                     finish_batch(er - u * tok_e, TB - 1, kb & 1);
             }
