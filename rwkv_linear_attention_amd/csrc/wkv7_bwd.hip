@@ -107,8 +107,15 @@ __global__ __launch_bounds__(NWB * 64) void wkv7_bwd_kernel(BwdArgs p)
     __shared__ BwdSmem<CW> sm;
     const int i = threadIdx.x & 63;                                   // key row of this lane
     const int g = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // column block of this wave
-    const int bh = blockIdx.x / SPLIT;
-    const int j0 = ((blockIdx.x % SPLIT) * NWB + g) * CW;
+    // workgroups are dealt to the 8 XCDs in turn: with SPLIT = 2, workgroups x
+    // and x + 8 of each group of 16 are the two halves of one head, so that both
+    // run on one XCD and share its L2 (the head's inputs, the adds into dr .. da)
+    const int x = blockIdx.x;
+    const int bh = SPLIT == 1 ? x : (x / 16) * 8 + x % 8;
+    const int half = SPLIT == 1 ? 0 : (x / 8) % 2;
+    if (bh >= p.B * p.H)
+        return;  // (the last group of 16 can be partly empty)
+    const int j0 = (half * NWB + g) * CW;
     const int H = p.H, T = p.T;
     const int bb = bh / H, hh = bh - bb * H;
     const Tin *__restrict__ r = static_cast<const Tin *>(p.r);
@@ -415,7 +422,8 @@ hipError_t launch_bwd_split(const BwdArgs &p, hipStream_t stream)
         const unsigned zblocks = static_cast<unsigned>(std::min<size_t>((n4 + 255) / 256, 4 * kCUs));
         hipLaunchKernelGGL(zero5_kernel, dim3(zblocks), dim3(256), 0, stream, p.dr, p.dk, p.dw, p.db, p.da, n4);
     }
-    const dim3 grid(static_cast<unsigned>(heads * SPLIT)), block(NWB * 64);
+    const size_t nwg = SPLIT == 1 ? heads : (heads + 7) / 8 * 16;
+    const dim3 grid(static_cast<unsigned>(nwg)), block(NWB * 64);
     const bool sin = p.state_in != nullptr, dout = p.d_state_out != nullptr;
     if (sin && dout)
         hipLaunchKernelGGL((wkv7_bwd_kernel<Tin, true, true, SPLIT>), grid, block, 0, stream, p);
