@@ -65,14 +65,20 @@ def kernel_source_hash(kind: str) -> str:
     return h.hexdigest()[:16]
 
 
-# kernels that one call runs besides the named one: the backward pass with two
-# workgroups per head first zeroes the outputs they add into ("bwd_zero")
-CALL_KERNELS = {"bwd": ("bwd", "bwd_zero")}
+def call_kernels(kind: str, workload: int):
+    """The kernels one call of `kind` runs on `workload`: the backward pass with two
+    workgroups per head (at most 128 heads) first zeroes the outputs they add into
+    ("bwd_zero")."""
+    if kind == "bwd":
+        import synth
+        wl = synth.WORKLOADS[workload]
+        return ("bwd", "bwd_zero") if wl.B * wl.H * 2 <= 256 else ("bwd",)
+    return (kind,)
 
 
 def read_traffic(kind: str, workload: int):
-    """HBM bytes per launch (per call: every kernel of CALL_KERNELS[kind]) from
-    profiles/hbm_traffic.txt, or None when absent or stale.
+    """HBM bytes per launch (per call: every kernel of call_kernels(kind, workload))
+    from profiles/hbm_traffic.txt, or None when absent or stale.
 
     Lines: <kernel-kind> <workload> <source-hash> <fetch_bytes> <write_bytes>
     (bytes already scaled by the copy-kernel calibration factor).
@@ -81,7 +87,7 @@ def read_traffic(kind: str, workload: int):
     if not os.path.exists(path):
         return None
     cur = kernel_source_hash(kind)
-    want = CALL_KERNELS.get(kind, (kind,))
+    want = call_kernels(kind, workload)
     found = {}
     with open(path) as f:
         for line in f:
@@ -519,6 +525,12 @@ def main():
         others["2-bwd"] = {"workload": w2.name + " (backward pass)",
                            "ms_per_call": round(tg["sec_per_launch"] * 1e3, 4), "roofline": rg,
                            "mtok_s": round(w2.B * w2.T / tg["sec_per_launch"] / 1e6, 2)}
+        # the same over workload 3: 256 heads, one workgroup per head
+        tg3 = time_backward(K, synth, 3, max(5, args.steps // 4), min(args.warmup, 2))
+        rg3 = roofline(backward_bytes(w3), tg3["sec_per_launch"], "bwd", 3)
+        others["3-bwd"] = {"workload": w3.name + " (backward pass)",
+                           "ms_per_call": round(tg3["sec_per_launch"] * 1e3, 4), "roofline": rg3,
+                           "mtok_s": round(w3.B * w3.T / tg3["sec_per_launch"] / 1e6, 2)}
         line["other_workloads"] = others
     print(json.dumps(line), flush=True)
 
