@@ -245,7 +245,6 @@ __global__ __launch_bounds__(NWB * 64) void wkv7_bwd_kernel(BwdArgs p)
     for (int m = 0; m < NM; ++m) {
         const int pi0 = g + NWB * m, pi = pi0 < 5 * TB ? pi0 : pi0 - NWB;
         sl0[m] = pi / 5;
-        const int qn = pi - 5 * sl0[m];
         extra[m] = pi0 >= 5 * TB;
     }
     // e_end: e_of the batch's last token, whose slot is slot_end
