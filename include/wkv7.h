@@ -252,7 +252,9 @@ int wkv7_state_commit(const float *state_pos, const int *accepted, const float *
  * With B * H <= 128 a head runs as two workgroups of 32 value columns each, and
  * the call launches two kernels on the stream: a fill that zeroes dr, dk, dw,
  * db, da, then the pass, whose two workgroups per head add their row sums into
- * them (two terms, so the order of the adds does not change the sum).
+ * them with hardware float atomics (two terms, so the order of the adds does
+ * not change the sum).  Those five outputs must then be ordinary device memory
+ * (hipMalloc), where such atomics are supported.
  */
 int wkv7_backward(const void *r, const void *w, const void *k, const void *v,
                   const void *a, const void *b, int in_dtype, const float *state_in,
