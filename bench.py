@@ -57,7 +57,7 @@ def recurrent_flops(wl) -> int:
 def kernel_source_hash(kind: str) -> str:
     name = {"step": "wkv7_step.hip", "verify": "wkv7_step.hip", "chunk": "wkv7_chunk.hip",
             "step_tail": "wkv7_step.hip", "tail_pass": "wkv7_tail.hip", "bwd": "wkv7_bwd.hip",
-            "bwd_zero": "wkv7_bwd.hip"}[kind]
+            "bwd_zero": "wkv7_bwd.hip", "commit": "wkv7_step.hip"}[kind]
     h = hashlib.sha256()
     for f in (name, "wkv7_device.h"):
         with open(os.path.join(CSRC, f), "rb") as fh:
@@ -210,24 +210,76 @@ def time_step_workload(K, synth, idx: int, steps: int, warmup: int, tail=False):
             "layers": wl.layers}
 
 
-def time_prefill_workload(K, synth, idx: int, steps: int, warmup: int, o_bf16: bool = False):
+def time_prefill_workload(K, synth, idx: int, steps: int, warmup: int, o_bf16: bool = False, lengths=None):
+    """One prefill call over workload idx; with lengths ([B] int32 on the GPU), row b runs its
+    first lengths[b] tokens (the variable-length form), and mtok_s counts those tokens."""
     import torch
     wl = synth.WORKLOADS[idx]
     d = synth.workload_inputs(idx, device="cuda")
     o = torch.empty((wl.B, wl.T, wl.H, N), dtype=torch.bfloat16 if o_bf16 else torch.float32, device="cuda")
     s_out = torch.empty((wl.B, wl.H, N, N), dtype=torch.float32, device="cuda")
     args = [d[n] for n in ("r", "w", "k", "v", "a", "b")]
+    run = lambda: K.wkv7_forward(*args, d["state_in"], o=o, state_out=s_out, lengths=lengths)
     stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):
-        warm(lambda: K.wkv7_forward(*args, d["state_in"], o=o, state_out=s_out), warmup)
+        warm(run, warmup)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for _ in range(steps):
-            K.wkv7_forward(*args, d["state_in"], o=o, state_out=s_out)
+            run()
         e1.record(stream)
         e1.synchronize()
     ms = e0.elapsed_time(e1) / steps
-    return {"ms_per_step": ms, "sec_per_launch": ms / 1e3, "mtok_s": wl.B * wl.T / (ms / 1e3) / 1e6}
+    tokens = wl.B * wl.T if lengths is None else int(lengths.sum().item())
+    return {"ms_per_step": ms, "sec_per_launch": ms / 1e3, "mtok_s": tokens / (ms / 1e3) / 1e6}
+
+
+def varlen_lengths(wl, seed: int = 91):
+    """A right-padded batch: row lengths drawn uniformly from [T/2, T] (seeded)."""
+    import torch
+    gen = torch.Generator().manual_seed(seed)
+    return torch.randint(wl.T // 2, wl.T + 1, (wl.B,), generator=gen, dtype=torch.int32)
+
+
+def varlen_bytes(wl, lengths) -> int:
+    """Algorithmic bytes of a variable-length prefill: inputs and o of the real tokens only,
+    the state read and written once."""
+    e_in = 2 if wl.dtype == "bf16" else 4
+    b = int(lengths.sum().item()) * wl.H * (6 * N * e_in + 4 * N)
+    return b + (2 if wl.state_std > 0 else 1) * wl.B * wl.H * N * N * 4
+
+
+def time_commit(K, synth, idx: int, steps: int, warmup: int, nsets: int = 8):
+    """wkv7_state_commit after the verify step of workload idx: the state after each row's
+    accepted prefix (accepted counts drawn from [0, T], seeded), over nsets distinct buffer
+    sets in one graph (more bytes than the caches hold), replayed."""
+    import torch
+    wl = synth.WORKLOADS[idx]
+    d = synth.workload_inputs(idx, device="cuda")
+    ins = [d[n] for n in ("r", "w", "k", "v", "a", "b")]
+    gen = torch.Generator().manual_seed(97)
+    acc = torch.randint(0, wl.T + 1, (wl.B,), generator=gen, dtype=torch.int32)
+    sets = []
+    for _ in range(nsets):
+        _, _, s_pos = K.wkv7_step(*ins, d["state_in"], per_position=True, write_state_out=False)
+        sets.append((s_pos, acc.cuda(), torch.empty((wl.B, wl.H, N, N), device="cuda")))
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        for s_pos, a_, s_o in sets:
+            K.wkv7_state_commit(s_pos, a_, d["state_in"], state_out=s_o)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for s_pos, a_, s_o in sets:
+                K.wkv7_state_commit(s_pos, a_, d["state_in"], state_out=s_o)
+        warm(g.replay, warmup)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            g.replay()
+        e1.record(stream)
+        e1.synchronize()
+    sec = e0.elapsed_time(e1) / 1e3 / (steps * nsets)
+    return {"sec_per_launch": sec, "bytes": 2 * wl.B * wl.H * N * N * 4 + wl.B * 4}
 
 
 def time_tail_pass(K, synth, idx: int, steps: int, warmup: int):
@@ -525,6 +577,20 @@ def main():
         others["2-bwd"] = {"workload": w2.name + " (backward pass)",
                            "ms_per_call": round(tg["sec_per_launch"] * 1e3, 4), "roofline": rg,
                            "mtok_s": round(w2.B * w2.T / tg["sec_per_launch"] / 1e6, 2)}
+        # variable-length prefill (a right-padded batch) over workload 3, and the commit of
+        # each row's accepted prefix after the verify step of workload 4
+        lens = varlen_lengths(w3)
+        tvl = time_prefill_workload(K, synth, 3, max(20, args.steps), args.warmup, lengths=lens.cuda())
+        rvl = roofline(varlen_bytes(w3, lens), tvl["sec_per_launch"], "chunk", 3)
+        rvl["traffic"] = None
+        others["3-varlen"] = {"workload": w3.name + " (rows of " + ",".join(str(int(x)) for x in lens) + " tokens)",
+                              "ms_per_call": round(tvl["sec_per_launch"] * 1e3, 4), "roofline": rvl,
+                              "mtok_s": round(tvl["mtok_s"], 2)}
+        tc = time_commit(K, synth, 4, args.steps, args.warmup)
+        rc = roofline(tc["bytes"], tc["sec_per_launch"], "commit", 4)
+        rc["traffic"] = None
+        others["4-commit"] = {"workload": w4.name + " (commit of the accepted prefixes)",
+                              "us_per_call": round(tc["sec_per_launch"] * 1e6, 3), "roofline": rc}
         # the same over workload 3: 256 heads, one workgroup per head
         tg3 = time_backward(K, synth, 3, max(5, args.steps // 4), min(args.warmup, 2))
         rg3 = roofline(backward_bytes(w3), tg3["sec_per_launch"], "bwd", 3)

@@ -306,8 +306,16 @@ __global__ __launch_bounds__(256) void state_commit_kernel(const float4 *state_p
         src = state_in + static_cast<size_t>(bh) * PER;
     if (src == dst)
         return;
-    for (int i = threadIdx.x; i < PER; i += 256)
-        dst[i] = src ? src[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    // all of a lane's loads first, then its stores: four loads in flight per lane
+    // (a load-store loop waits for each load before the next)
+    constexpr int PL = PER / 256;
+    float4 x[PL];
+#pragma unroll
+    for (int q = 0; q < PL; ++q)
+        x[q] = src ? src[threadIdx.x + 256 * q] : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int q = 0; q < PL; ++q)
+        dst[threadIdx.x + 256 * q] = x[q];
 }
 
 unsigned grid_for(long long n4)
