@@ -399,6 +399,32 @@ def test_tail_gate_and_head_parameters(oracle_mod):
     np.testing.assert_allclose(x2[:, :, 1], xg[:, :, 1] + g[:, :, 1], rtol=1e-12)
 
 
+def test_tail_affine_scale_per_head_and_channel(oracle_mod):
+    # With no shift (ln_b = 0), no bonus (r_k = 0) and an open gate, the affine
+    # scale multiplies the normalised row channel by channel: x(ln_w) equals
+    # ln_w[h, j] times x(ones), whose moments the first tail pin fixes.  Every
+    # (head, channel) scale differs and none is 1, so a dropped scale, one taken
+    # from another head or channel, or one applied before the normalisation
+    # (which would cancel it) fails here.
+    rng = np.random.default_rng(74)
+    o, r, k, v, g, r_k, _, _ = _tail_inputs(74, B=2, T=3, H=3)
+    H, N = r_k.shape
+    ln_w = 0.5 + rng.permutation(H * N).reshape(H, N) / (H * N)   # all distinct, in [0.5, 1.5)
+    zb, zk, one = np.zeros((H, N)), np.zeros((H, N)), np.ones_like(g)
+    base = oracle_mod.tmix_tail(o, r, k, v, one, zk, np.ones((H, N)), zb, 0.2)
+    x = oracle_mod.tmix_tail(o, r, k, v, one, zk, ln_w, zb, 0.2)
+    np.testing.assert_allclose(x, base * ln_w[None, None], rtol=1e-13, atol=0)
+    # scaling one (head, channel) entry changes that channel of that head only, by that factor
+    ln_w2 = ln_w.copy()
+    ln_w2[1, 5] *= 3.0
+    x2 = oracle_mod.tmix_tail(o, r, k, v, one, zk, ln_w2, zb, 0.2)
+    changed = x2 != x
+    assert changed[:, :, 1, 5].all()
+    changed[:, :, 1, 5] = False
+    assert not changed.any()
+    np.testing.assert_allclose(x2[:, :, 1, 5], 3.0 * x[:, :, 1, 5], rtol=1e-14)
+
+
 # --- the backward pass (gradients of the recurrence) ----------------------------
 
 def _loss_and_grads(oracle_mod, x, s0, go, gs):
