@@ -87,12 +87,16 @@ enum wkv7_status {
  *   B * H <= WKV7_MAX_HEADS_STEP   for wkv7_step, wkv7_step_tail, wkv7_state_commit, wkv7_backward,
  *                                  and wkv7_forward[_varlen] with T < 9;
  *   B * H <= WKV7_MAX_HEADS_CHUNK  for wkv7_forward[_varlen] with T >= 9;
+ *   H <= WKV7_MAX_H_CHUNK           for wkv7_forward[_varlen] with T >= 9 (a lane of the
+ *                                  chunked kernel addresses its 16 tokens' outputs with 32-bit
+ *                                  byte offsets from the chunk's first output row);
  *   B * T * H <= WKV7_MAX_ROWS_TAIL for wkv7_tmix_tail.
- * Element offsets are 64-bit everywhere: tensors of more than 2^32 elements are
- * supported within these limits.
+ * Tensor offsets are 64-bit: tensors of more than 2^32 elements are supported
+ * within these limits.
  */
 #define WKV7_MAX_HEADS_STEP 8000000
 #define WKV7_MAX_HEADS_CHUNK 4000000
+#define WKV7_MAX_H_CHUNK 1048576
 #define WKV7_MAX_ROWS_TAIL 200000000
 
 /*

@@ -141,6 +141,19 @@ def _state_arg(state, B, H, N, device, name):
     return state
 
 
+def _out_arg(x, shape, device, name, dtypes=(torch.float32, torch.bfloat16)):
+    """A caller-supplied output: a contiguous tensor of `shape` on `device` with one of `dtypes`.
+
+    The C ABI cannot see buffer sizes, so an undersized or strided output would be
+    written past its end; every wrapper checks its outputs here first."""
+    if not torch.is_tensor(x):
+        raise ValueError(f"{name} must be a tensor")
+    if tuple(x.shape) != tuple(shape) or not x.is_contiguous() or x.device != device or x.dtype not in dtypes:
+        kinds = " or ".join(str(d).replace("torch.", "") for d in dtypes)
+        raise ValueError(f"{name} must be a contiguous {kinds} {list(shape)} tensor on {device}")
+    return x
+
+
 def _int_rows(x, B, device, name):
     """A [B] int32 device tensor (converted from any integer tensor or sequence)."""
     x = torch.as_tensor(x, device=device).to(torch.int32).contiguous()
@@ -165,8 +178,7 @@ def wkv7_forward(r, w, k, v, a, b, state_in=None, *, o_dtype=torch.float32, o=No
     _state_arg(state_out, B, H, N, dev, "state_out")
     if o is None:
         o = torch.empty((B, T, H, N), dtype=o_dtype, device=dev)
-    if o.shape != r.shape or not o.is_contiguous() or o.device != dev:
-        raise ValueError("o must be a contiguous [B, T, H, N] tensor on the inputs' device")
+    _out_arg(o, (B, T, H, N), dev, "o")
     if lengths is None:
         _check(lib().wkv7_forward(*[_ptr(x) for x in (r, w, k, v, a, b)], _dt(r), _ptr(state_in), _ptr(o),
                                   _dt(o), _ptr(state_out), B, T, H, N, _stream(dev)))
@@ -197,11 +209,11 @@ def wkv7_step(r, w, k, v, a, b, state_in=None, *, per_position=False, o_dtype=to
         _state_arg(state_out, B, H, N, dev, "state_out")
     if o is None:
         o = torch.empty((B, T, H, N), dtype=o_dtype, device=dev)
+    _out_arg(o, (B, T, H, N), dev, "o")
     if per_position and state_pos is None:
         state_pos = torch.empty((B, T, H, N, N), dtype=torch.float32, device=dev)
-    if state_pos is not None and (tuple(state_pos.shape) != (B, T, H, N, N) or state_pos.dtype != torch.float32
-                                  or not state_pos.is_contiguous()):
-        raise ValueError("state_pos must be a contiguous fp32 [B, T, H, N, N] tensor")
+    if state_pos is not None:
+        _out_arg(state_pos, (B, T, H, N, N), dev, "state_pos", (torch.float32,))
     _check(lib().wkv7_step(*[_ptr(x) for x in (r, w, k, v, a, b)], _dt(r), _ptr(state_in), _ptr(o), _dt(o),
                            _ptr(state_out), _ptr(state_pos), B, T, H, N, _stream(dev)))
     if state_pos is not None:
@@ -235,8 +247,11 @@ def wkv7_step_tail(r, w, k, v, a, b, g, r_k, ln_w, ln_b, eps, state_in=None, *, 
     _state_arg(state_out, B, H, N, dev, "state_out")
     if x is None:
         x = torch.empty((B, T, H, N), dtype=x_dtype, device=dev)
+    _out_arg(x, (B, T, H, N), dev, "x")
     if per_position and state_pos is None:
         state_pos = torch.empty((B, T, H, N, N), dtype=torch.float32, device=dev)
+    if state_pos is not None:
+        _out_arg(state_pos, (B, T, H, N, N), dev, "state_pos", (torch.float32,))
     _check(lib().wkv7_step_tail(*[_ptr(t) for t in (r, w, k, v, a, b)], _dt(r), _ptr(state_in), _ptr(g),
                                 _ptr(r_k), _ptr(ln_w), _ptr(ln_b), float(eps), _ptr(x), _dt(x), _ptr(state_out),
                                 _ptr(state_pos), B, T, H, N, _stream(dev)))
@@ -249,11 +264,11 @@ def wkv7_tmix_tail(o, r, k, v, g, r_k, ln_w, ln_b, eps, *, x_dtype=torch.float32
     """The time-mix tail of o (from wkv7_forward): returns x [B, T, H, N].  x may be o itself."""
     B, T, H, N = _check_inputs(r, r, k, v, g, g)
     dev = r.device
-    if o.shape != r.shape or not o.is_contiguous() or o.device != dev:
-        raise ValueError("o must be a contiguous [B, T, H, N] tensor on the inputs' device")
+    _out_arg(o, (B, T, H, N), dev, "o")
     r_k, ln_w, ln_b = _head_params(H, N, dev, r_k=r_k, ln_w=ln_w, ln_b=ln_b)
     if x is None:
         x = torch.empty((B, T, H, N), dtype=x_dtype, device=dev)
+    _out_arg(x, (B, T, H, N), dev, "x")
     _check(lib().wkv7_tmix_tail(_ptr(o), _dt(o), _ptr(r), _ptr(k), _ptr(v), _ptr(g), _dt(r), _ptr(r_k),
                                 _ptr(ln_w), _ptr(ln_b), float(eps), _ptr(x), _dt(x), B, T, H, N, _stream(dev)))
     return x
@@ -295,21 +310,16 @@ def wkv7_backward(r, w, k, v, a, b, state_in, state_pos, d_o, d_state_out=None, 
     dev = r.device
     state_in = _state_arg(state_in, B, H, N, dev, "state_in")
     d_state_out = _state_arg(d_state_out, B, H, N, dev, "d_state_out")
-    if (state_pos.dtype != torch.float32 or tuple(state_pos.shape) != (B, T, H, N, N)
-            or not state_pos.is_contiguous() or state_pos.device != dev):
-        raise ValueError(f"state_pos must be a contiguous fp32 [{B}, {T}, {H}, {N}, {N}] tensor on {dev}")
-    if (d_o.dtype != torch.float32 or tuple(d_o.shape) != (B, T, H, N) or not d_o.is_contiguous()
-            or d_o.device != dev):
-        raise ValueError(f"d_o must be a contiguous fp32 [{B}, {T}, {H}, {N}] tensor on {dev}")
+    f32 = (torch.float32,)
+    _out_arg(state_pos, (B, T, H, N, N), dev, "state_pos", f32)
+    _out_arg(d_o, (B, T, H, N), dev, "d_o", f32)
     names = ("dr", "dw", "dk", "dv", "da", "db")
     if grads is None:
         grads = {n: torch.empty((B, T, H, N), dtype=torch.float32, device=dev) for n in names}
         grads["d_state_in"] = torch.empty((B, H, N, N), dtype=torch.float32, device=dev)
     for n in names:
-        g = grads[n]
-        if g.dtype != torch.float32 or tuple(g.shape) != (B, T, H, N) or not g.is_contiguous() or g.device != dev:
-            raise ValueError(f"{n} must be a contiguous fp32 [{B}, {T}, {H}, {N}] tensor on {dev}")
-    _state_arg(grads["d_state_in"], B, H, N, dev, "d_state_in")
+        _out_arg(grads[n], (B, T, H, N), dev, n, f32)
+    _out_arg(grads["d_state_in"], (B, H, N, N), dev, "d_state_in", f32)
     _check(lib().wkv7_backward(*[_ptr(x) for x in (r, w, k, v, a, b)], _dt(r), _ptr(state_in),
                                _ptr(state_pos), _ptr(d_o), _ptr(d_state_out),
                                *[_ptr(grads[n]) for n in names], _ptr(grads["d_state_in"]),

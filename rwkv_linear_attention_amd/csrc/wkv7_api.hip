@@ -40,6 +40,10 @@ bool misaligned(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) !
 // 2^32 threads.
 constexpr int64_t kMaxHeadsStep = WKV7_MAX_HEADS_STEP;
 constexpr int64_t kMaxHeadsChunk = WKV7_MAX_HEADS_CHUNK;
+// The chunked kernel stores a chunk's outputs at 32-bit byte offsets from the chunk's
+// first row: (15 H N + 15) * 4 must stay below 2^32.
+constexpr int64_t kMaxHChunk = WKV7_MAX_H_CHUNK;
+static_assert((15 * kMaxHChunk * kN + 15) * 4 < (1ll << 32), "32-bit output offsets of the chunked kernel");
 // Largest B * T * H of the time-mix tail pass (16 threads per row).
 constexpr int64_t kMaxRowsTail = WKV7_MAX_ROWS_TAIL;
 static_assert(kMaxHeadsStep * 512 < (1ll << 32) && kMaxHeadsChunk * 896 < (1ll << 32) &&
@@ -72,8 +76,8 @@ int check_seq(const void *r, const void *w, const void *k, const void *v, const 
     if ((in_dtype != WKV7_F32 && in_dtype != WKV7_BF16) || (o_dtype != WKV7_F32 && o_dtype != WKV7_BF16))
         return WKV7_ERR_UNSUPPORTED;
     // the parallel pass routes T >= kChunkMinT to the chunked kernel
-    const int64_t max_heads = !step_only && T >= kChunkMinT ? kMaxHeadsChunk : kMaxHeadsStep;
-    if (!shape_ok(B, T, H, &tok, max_heads))
+    const bool chunked = !step_only && T >= kChunkMinT;
+    if (!shape_ok(B, T, H, &tok, chunked ? kMaxHeadsChunk : kMaxHeadsStep) || (chunked && H > kMaxHChunk))
         return WKV7_ERR_SHAPE;
     if (!state_out && !(out_optional && state_pos && T > 0))
         return WKV7_ERR_NULL;
@@ -388,7 +392,7 @@ int wkv7_backward(const void *r, const void *w, const void *k, const void *v, co
     // every output overlaps nothing else (d_state_in may be d_state_out itself)
     const int64_t ein = in_dtype == WKV7_BF16 ? 2 : 4;
     const int64_t vec = tok * kN, st_bytes = static_cast<int64_t>(B) * H * kN * kN * 4;
-    Range in_r[10];
+    Range in_r[11];
     int n_in = 0;
     if (T > 0) {
         for (int q = 0; q < 6; ++q)
@@ -398,6 +402,10 @@ int wkv7_backward(const void *r, const void *w, const void *k, const void *v, co
     }
     if (state_in)
         in_r[n_in++] = range_of(state_in, st_bytes);
+    // d_state_out is read by the pass: no gradient of an input may overlap it (d_state_in
+    // may be d_state_out itself, checked below)
+    if (d_state_out && d_state_out != d_state_in)
+        in_r[n_in++] = range_of(d_state_out, st_bytes);
     const Range r_dsi = range_of(d_state_in, st_bytes);
     Range out_r[7];
     int n_out = 0;

@@ -246,6 +246,14 @@ def test_launch_size_limits(L):
     assert commit(L, B=max_step + 1, T=5, H=1) == ERR_SHAPE
     assert tmix(L, B=1, T=max_rows + 1, H=1) == ERR_SHAPE
     assert tmix(L, B=1, T=max_rows // 64 + 1, H=64) == ERR_SHAPE
+    # the chunked kernel's 32-bit output offsets: H up to WKV7_MAX_H_CHUNK = 2^20
+    max_h = 1048576
+    assert fwd(L, B=1, T=16, H=max_h + 1) == ERR_SHAPE
+    assert varlen(L, B=1, T=16, H=max_h + 1) == ERR_SHAPE
+    # at the limit validation goes on (T = 80 makes o span the next fake buffer)
+    assert fwd(L, B=1, T=80, H=max_h) == ERR_ALIAS
+    # the step kernel (T < 9) has no such limit: validation goes on to the (forced) overlap
+    assert fwd(L, B=1, T=8, H=2 * max_h, sout=fake(0)) == ERR_ALIAS
 
 
 def bwd(L, B=2, T=6, H=3, N=64, in_dt=BF16, sin="fake", pos="fake", do="fake", dso="fake", grads=None,
@@ -281,6 +289,11 @@ def test_backward_validation(L):
     g[0] = fake(2, 64)
     assert bwd(L, grads=g) == ERR_ALIAS
     assert bwd(L, dsi=fake(17, 256)) == ERR_ALIAS
+    # a gradient inside d_state_out, which the pass reads
+    for q in range(6):
+        g = [fake(11 + i) for i in range(6)]
+        g[q] = fake(17, 1024)
+        assert bwd(L, grads=g) == ERR_ALIAS, q
     # T = 0 needs only d_state_in
     assert L.wkv7_backward(*([None] * 6), BF16, None, None, None, None, *([None] * 6), None, 2, 0, 3, 64,
                            None) == ERR_NULL
