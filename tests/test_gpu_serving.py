@@ -6,7 +6,8 @@ import pytest
 import torch
 
 import synth
-from test_gpu_parity import K, TOL, check, to_dev  # noqa: F401  (K is a fixture)
+from parity import HEADS_SEQ, HEADS_STATE, check
+from test_gpu_parity import K, TOL, to_dev  # noqa: F401  (K is a fixture)
 
 pytestmark = pytest.mark.gpu
 
@@ -34,10 +35,11 @@ def test_forward_varlen(K, oracle_mod, dtype, B, T, H):
     L = np.clip(np.asarray(lengths), 0, T)
     valid = np.arange(T)[None, :] < L[:, None]                       # [B, T]
     og = o.double().cpu().numpy()
-    if valid.any():
-        check(og[valid], o_ref[valid], TOL[dtype], "o (valid tokens)")
+    # per head over each row's own tokens (the rest set to zero on both sides)
+    m = valid[:, :, None, None]
+    check(np.where(m, og, 0.0), np.where(m, o_ref, 0.0), TOL[dtype], "o (valid tokens)", HEADS_SEQ)
     assert (og[~valid] == sentinel).all(), "o past a row's length must be left untouched"
-    check(s, s_ref, TOL[dtype], "state_out")
+    check(s, s_ref, TOL[dtype], "state_out", HEADS_STATE)
     for bb in np.nonzero(L == 0)[0]:
         assert torch.equal(s[bb], d["state_in"][bb]), "an empty row passes its state through"
 
@@ -73,7 +75,7 @@ def test_state_commit(K, oracle_mod):
     # and against the oracle's commit of its own per-position states
     _, _, sp_ref = oracle_mod.forward(*[inp[n] for n in NAMES], inp["state_in"], per_position=True)
     ref = oracle_mod.state_commit(sp_ref, accepted, inp["state_in"], before.cpu())
-    check(got, ref, TOL["bf16"], "committed state")
+    check(got, ref, TOL["bf16"], "committed state", HEADS_STATE)
     # in place over the state the step started from
     st = d["state_in"].clone()
     K.wkv7_state_commit(sp, accepted, st, state_out=st)
@@ -87,22 +89,17 @@ def test_state_commit(K, oracle_mod):
     assert not torch.any(z)
 
 
-def test_bf16_output_accuracy_workload3(K, oracle_mod):
-    # The cost of a bf16 o (the o_dtype option) on the prefill workload, measured on
-    # sampled heads over the full sequence; it stays inside the bf16-input tolerance.
-    inp = synth.workload_inputs(3)
+def test_bf16_output_accuracy_workload3(K, workload3_oracle):
+    # The cost of a bf16 o (the o_dtype option) on the prefill workload, every head over
+    # the full sequence; it stays inside the bf16-input tolerance (each element within
+    # half a bf16 ulp of its own plus the tolerance times its head's RMS).
+    inp, o_ref, _ = workload3_oracle
     d = to_dev(inp)
     o16, _ = K.wkv7_forward(*[d[n] for n in NAMES], d["state_in"], o_dtype=torch.bfloat16)
-    o32, _ = K.wkv7_forward(*[d[n] for n in NAMES], d["state_in"])
     torch.cuda.synchronize()
-    o16, o32 = o16.float().cpu(), o32.cpu()
+    o16 = o16.float().cpu()
     del d
-    for (bb, hh) in [(0, 5), (3, 60)]:
-        sub = {n: x[bb:bb + 1, :, hh:hh + 1].contiguous() for n, x in inp.items() if n != "state_in"}
-        sub["state_in"] = inp["state_in"][bb:bb + 1, hh:hh + 1].contiguous()
-        o_ref, _ = oracle_mod.forward(*[sub[n] for n in NAMES], sub["state_in"])
-        check(o32[bb:bb + 1, :, hh:hh + 1], o_ref, TOL["bf16"], f"workload 3 (b={bb}, h={hh}) o fp32")
-        check(o16[bb:bb + 1, :, hh:hh + 1], o_ref, TOL["bf16"], f"workload 3 (b={bb}, h={hh}) o bf16")
+    check(o16, o_ref, TOL["bf16"], "workload 3 o bf16", HEADS_SEQ, elem_rel=2.0 ** -8)
 
 
 def _tail_params(H, seed):
@@ -134,8 +131,10 @@ def test_tmix_tail_vs_oracle(K, oracle_mod, dtype, x_dtype):
                          x_dtype=x_dtype)
     torch.cuda.synchronize()
     x_ref = oracle_mod.tmix_tail(o_dev.cpu(), inp["r"], inp["k"], inp["v"], gate, r_k, ln_w, ln_b, eps)
-    tol = 2e-3 if x_dtype == torch.bfloat16 else 1e-5
-    check(x, x_ref, tol, f"tail ({dtype} inputs, {x_dtype} x)")
+    # a bf16 x carries its own rounding (about 1.7e-3 relative L2): held to 4e-3 and half an ulp
+    bf = x_dtype == torch.bfloat16
+    check(x, x_ref, 4e-3 if bf else 1e-5, f"tail ({dtype} inputs, {x_dtype} x)", HEADS_SEQ,
+          elem_rel=2.0 ** -8 if bf else 0.0)
     # in place over o
     o2 = o_dev.clone()
     K.wkv7_tmix_tail(o2, d["r"], d["k"], d["v"], gate.cuda(), r_k.cuda(), ln_w.cuda(), ln_b.cuda(), eps, x=o2)
@@ -159,15 +158,15 @@ def test_step_tail_vs_oracle(K, oracle_mod, dtype, T):
     torch.cuda.synchronize()
     o_ref, s_ref, sp_ref = oracle_mod.forward(*[inp[n] for n in NAMES], inp["state_in"], per_position=True)
     x_ref = oracle_mod.tmix_tail(o_ref, inp["r"], inp["k"], inp["v"], gate, r_k, ln_w, ln_b, eps)
-    check(x, x_ref, TOL[dtype], f"fused tail T={T} x")
-    check(s, s_ref, TOL[dtype], f"fused tail T={T} state")
-    check(sp, sp_ref, TOL[dtype], f"fused tail T={T} state_pos")
+    check(x, x_ref, TOL[dtype], f"fused tail T={T} x", HEADS_SEQ)
+    check(s, s_ref, TOL[dtype], f"fused tail T={T} state", HEADS_STATE)
+    check(sp, sp_ref, TOL[dtype], f"fused tail T={T} state_pos", HEADS_SEQ)
     # the fused epilogue and the separate pass: the same arithmetic on the same o, summed in
     # another order (64 lanes against 16 lanes of four channels)
     o, _ = K.wkv7_step(*[d[n] for n in NAMES], d["state_in"])
     x2 = K.wkv7_tmix_tail(o, d["r"], d["k"], d["v"], gate.cuda(), r_k.cuda(), ln_w.cuda(), ln_b.cuda(), eps)
     torch.cuda.synchronize()
-    check(x, x2.double().cpu().numpy(), 1e-6, "fused against separate tail")
+    check(x, x2.double().cpu().numpy(), 1e-6, "fused against separate tail", HEADS_SEQ)
 
 
 def test_verify_without_separate_state_out(K, oracle_mod):
