@@ -113,9 +113,11 @@ enum wkv7_status {
  * triangular solve for the rank-1 terms inside a chunk, matrix-core products,
  * and the state carried from chunk to chunk in order); short ones run the
  * step kernel.  T = 0 copies state_in to state_out (zeros if state_in is NULL)
- * and leaves o untouched.  Decays below 2^-15 are raised to 2^-15 by the
- * chunked kernel (an absolute change of at most 3.1e-5 in that step's
- * multiplier); RWKV-7's decays never come near that bound.
+ * and leaves o untouched.  Every decay in [0, 1] is taken exactly: a chunk of
+ * 16 tokens that holds a decay below 2^-15 (where the chunk form's decay
+ * factors would leave the fp32 range) is evaluated token by token instead,
+ * which costs that chunk several times its usual time; RWKV-7's decays
+ * (>= 0.545) never come near that bound.
  */
 int wkv7_forward(const void *r, const void *w, const void *k, const void *v,
                  const void *a, const void *b, int in_dtype,

@@ -27,8 +27,12 @@
 //     Z   = T (A' S^ + M_ak V)
 //     O   = R' S^ + [M_rb | M_rk] [Z ; V]
 //     S_C = diag(d_15) (S^ + [B'^T | K'^T] [Z ; V]).
-// Decay multipliers are raised to at least 2^-15 so that every factor stays
-// within 2^(+-120); RWKV-7's decays (>= 0.545) never come near that bound.
+// With every decay multiplier of a chunk at least 2^-15, every factor stays
+// within 2^(+-120).  A chunk with a smaller decay anywhere (RWKV-7's decays,
+// >= 0.545, never come near) is evaluated exactly instead: its decay table is
+// all ones (so S^ enters it unscaled and leaves it scaled for the next chunk)
+// and its consumers run the recurrence itself over its 16 tokens, reading the
+// inputs from global memory.
 //
 // MAPPING (gfx950).  One workgroup per (batch, head, block of NC value
 // columns); value columns evolve independently, so a head splits into
@@ -68,7 +72,8 @@ namespace {
 
 constexpr int CH = 16;             // chunk length
 constexpr int REF = 7;             // decays are measured relative to the state after this position
-constexpr float W_MIN = 0x1p-15f;  // lower bound applied to decay multipliers in this kernel
+// a decay of magnitude below this sends its chunk to the exact recurrent path
+constexpr float W_EXACT = 0x1p-15f;
 // producer waves: ten with bf16 inputs (two inverse and two decay waves), eight with fp32 inputs
 template <typename Tin>
 constexpr int nprod() { return std::is_same<Tin, float>::value ? 8 : 10; }
@@ -171,6 +176,14 @@ __device__ __forceinline__ void split4(const f32x4 v, s16x4 (&out)[NP])
 
 __device__ __forceinline__ s16x8 lds8(const uint16_t *p) { return *reinterpret_cast<const s16x8 *>(p); }
 
+// Four consecutive input elements from global memory, widened to fp32.
+__device__ __forceinline__ f32x4 load4(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
+__device__ __forceinline__ f32x4 load4(const uint16_t *p)
+{
+    const u32x2 u = *reinterpret_cast<const u32x2 *>(p);
+    return f32x4{bf16_lo(u[0]), bf16_hi(u[0]), bf16_lo(u[1]), bf16_hi(u[1])};
+}
+
 // LDS transpose load of a 16x16 bf16 tile stored row-major as X[k][n]: lane
 // 16 q + i passes the address of X[4 q + i/4][4 (i%4)] (four consecutive n),
 // and lane (n = l%16, q = l/16) receives X[4 q + e][n], e = 0..3 -- the
@@ -233,6 +246,7 @@ struct Smem {
     alignas(16) float p7[kN];  // P_7 of the first chunk
     alignas(16) float d15[2][kN];  // d_15 of the last two chunks whose table was written
     alignas(16) float mt[NT][CH][MTP];  // M_ab of one chunk per inverse wave, row-major
+    int exact[8];  // chunk c % 8 takes the exact path (its decay table is all ones)
 };
 
 // Decay factors of one key channel over a chunk: d[tau+1] = P_tau / P_7 and
@@ -340,6 +354,10 @@ __global__ __launch_bounds__((kN / J / 16 + nprod<Tin>()) * 64) void wkv7_chunk_
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 Sx[pt][e] = HAS_STATE_IN ? p.state_in[sbase + (16 * pt + 4 * q + e) * kN + jw + m] : 0.0f;
+        // The state is in registers before the chunk loop starts.  Without this wait the
+        // compiler waits for these loads inside the loop, where the counter also holds the
+        // previous chunk's output stores: every chunk would wait for those to drain.
+        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
         // transpose-load address pieces of this lane: row 4 q + m/4, column group m%4
         const int trow = 4 * q + (m >> 2), tcol = 4 * (m & 3);
         const int mcol_t = mcol(trow, m & 3);  // the same unit in a swizzled matrix tile
@@ -352,6 +370,59 @@ __global__ __launch_bounds__((kN / J / 16 + nprod<Tin>()) * 64) void wkv7_chunk_
         auto store_o = [](Tout *base, uint32_t off, float x) {
             asm volatile("" : "+v"(off));  // keeps the offset 32-bit (not widened ahead of the loop)
             store_elem(reinterpret_cast<Tout *>(reinterpret_cast<char *>(base) + off), 0, x);
+        };
+
+        // The exact path of a chunk with a decay below 2^-15: the recurrence itself,
+        // token by token, on this wave's 64x16 slice of the state (which enters such a
+        // chunk unscaled).  Lane (q, m) holds rows 16 pt + 4 q + e of column jw + m; a
+        // sum over the key rows adds the four lanes of a column (m, m+16, m+32, m+48)
+        // by two exchanges, which give all four the same value.
+        auto exact_chunk = [&](int t0) {
+            const int nt = min(CH, L - t0);
+#pragma unroll 1
+            for (int tau = 0; tau < nt; ++tau) {
+                // uniform row bases; the lanes' keys are small offsets from them, made opaque
+                // here so that no per-lane address is hoisted out of the chunk loop (it would
+                // stay live through the other path and push that one into spills)
+                int kq = 4 * q, jc = jw + m;
+                asm volatile("" : "+v"(kq), "+v"(jc));
+                const uint64_t row = row_of(t0 + tau);
+                const Tin *__restrict__ ra = static_cast<const Tin *>(p.a) + row;
+                const Tin *__restrict__ rw = static_cast<const Tin *>(p.w) + row;
+                const Tin *__restrict__ rb = static_cast<const Tin *>(p.b) + row;
+                const Tin *__restrict__ rk = static_cast<const Tin *>(p.k) + row;
+                const Tin *__restrict__ rr = static_cast<const Tin *>(p.r) + row;
+                const float vj = load_elem(static_cast<const Tin *>(p.v) + row, jc);
+                float sa = 0.0f;
+#pragma unroll
+                for (int pt = 0; pt < 4; ++pt) {
+                    const f32x4 a4 = load4(ra + 16 * pt + kq);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        sa = fmaf(a4[e], Sx[pt][e], sa);
+                }
+                sa += __shfl_xor(sa, 16);
+                sa += __shfl_xor(sa, 32);
+                float op = 0.0f;
+#pragma unroll
+                for (int pt = 0; pt < 4; ++pt) {
+                    // one group of four keys at a time: this path is rare, and its registers
+                    // count against the whole wave's budget
+                    __builtin_amdgcn_sched_barrier(0);
+                    const int key = 16 * pt + kq;
+                    const f32x4 w4 = load4(rw + key), b4 = load4(rb + key);
+                    const f32x4 k4 = load4(rk + key), r4 = load4(rr + key);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        Sx[pt][e] = fmaf(w4[e], Sx[pt][e], fmaf(b4[e], sa, k4[e] * vj));
+                        op = fmaf(r4[e], Sx[pt][e], op);
+                    }
+                }
+                op += __shfl_xor(op, 16);
+                op += __shfl_xor(op, 32);
+                if (q == 0)
+                    store_elem(go + row, jc, op);
+            }
         };
 
         // A' and v of the next chunk are read at the end of each iteration
@@ -371,146 +442,167 @@ __global__ __launch_bounds__((kN / J / 16 + nprod<Tin>()) * 64) void wkv7_chunk_
             for (int pl = 0; pl < NPV; ++pl)
                 pV[pl] = tr4(&sl.Vr[pl][trow][jw + tcol]);
         };
+        // Whether chunk i takes the exact path, as a scalar.  Chunk i+1's flag (final since
+        // its decay table was written) is read early in chunk i and becomes a scalar after
+        // a wait that chunk i's own reads need anyway, so the branch waits for nothing.
+        // The two paths meet on the state before its row factors (acc), so that the common
+        // path keeps its registers (the copies fall on the rare path).
+        int exact_next = 0;
         for (int i = I0; i < nchunks; ++i) {
+            if (i == -1)
+                exact_next = __builtin_amdgcn_readfirstlane(sm.exact[0]);
             if (i >= 0) {
                 const SlotT &sl = sm.slot[i % NS];
                 const int t0 = i * CH;
-                // this chunk's R' rows and the M_ak and T tiles, read first so that
-                // they arrive while S^ is split
-                s16x8 Rf[2][NP];
-                s16x4 Mak[NP], Tf[NP];
+                const int flag_next = sm.exact[(i + 1) & 7];
+                f32x4 acc[4], fv[4];  // the state before its row factors, and those factors
+                if (exact_next) {
+                    // S^ enters unscaled (this chunk's P_7 is 1) and leaves scaled by f = P_7
+                    // of the next chunk (this chunk's d_15 is 1)
+                    exact_chunk(t0);
 #pragma unroll
-                for (int s = 0; s < 2; ++s)
+                    for (int pt = 0; pt < 4; ++pt)
+                        acc[pt] = f32x4{Sx[pt][0], Sx[pt][1], Sx[pt][2], Sx[pt][3]};
 #pragma unroll
-                    for (int pl = 0; pl < NP; ++pl)
-                        Rf[s][pl] = lds8(&sl.X[OP_R][pl][m][32 * s + 8 * q]);
+                    for (int pt = 0; pt < 4; ++pt)
+                        fv[pt] = *reinterpret_cast<const f32x4 *>(&sl.f[16 * pt + 4 * q]);
+                } else {
+                    // this chunk's R' rows and the M_ak and T tiles, read first so that
+                    // they arrive while S^ is split
+                    s16x8 Rf[2][NP];
+                    s16x4 Mak[NP], Tf[NP];
 #pragma unroll
-                for (int pl = 0; pl < NP; ++pl) {
-                    Mak[pl] = tr4(&sl.Mt[MT_AK][pl][trow][mcol_t]);
-                    Tf[pl] = tr4(&sl.Mt[MT_T][pl][trow][mcol_t]);
-                }
-                if (i == 0) {
-                    // S^ = diag(P_7) S_in for the first chunk; afterwards every chunk
-                    // leaves S^ of the next one (its row factor folds both scalings).
+                    for (int s = 0; s < 2; ++s)
+#pragma unroll
+                        for (int pl = 0; pl < NP; ++pl)
+                            Rf[s][pl] = lds8(&sl.X[OP_R][pl][m][32 * s + 8 * q]);
+#pragma unroll
+                    for (int pl = 0; pl < NP; ++pl) {
+                        Mak[pl] = tr4(&sl.Mt[MT_AK][pl][trow][mcol_t]);
+                        Tf[pl] = tr4(&sl.Mt[MT_T][pl][trow][mcol_t]);
+                    }
+                    if (i == 0) {
+                        // S^ = diag(P_7) S_in for the first chunk; afterwards every chunk
+                        // leaves S^ of the next one (its row factor folds both scalings).
+#pragma unroll
+                        for (int pt = 0; pt < 4; ++pt) {
+                            const f32x4 p7v = *reinterpret_cast<const f32x4 *>(&sm.p7[16 * pt + 4 * q]);
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                Sx[pt][e] *= p7v[e];
+                        }
+                    }
+                    // S^ as matrix-core B operands over the key index: key slot (q, e) of
+                    // k-step s is key row 16 (2 s + e/4) + 4 q + e%4, which this lane holds
+                    // in Sx[2 s + e/4][e % 4].
+                    s16x8 Bs[2][NP];
+                    auto split_state = [&](int s) {
+                        float v8[8];
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            v8[e] = Sx[2 * s + e / 4][e & 3];
+                        split8<NP>(v8, Bs[s]);
+                    };
+                    // A'-rows and R'-rows as A operands with the same key slots (stored
+                    // contiguously, see key_slot); one accumulator per k-step.
+                    // Y = A' S^ + M_ak V in accumulator layout (Y[4 q + e][col m]): A' S^ in
+                    // one accumulator over both k-steps and M_ak V in another (a 16x16x16
+                    // product never accumulates onto a 16x16x32 one: the compiler inserts no
+                    // wait states between the two shapes); R' S^ in one accumulator that the
+                    // [M_rb | M_rk] product (the same shape) later continues
+                    // V rows as a B operand over the token index (slot (q, e) = token 4 q + e)
+                    s16x4 Vf[NPV];
+#pragma unroll
+                    for (int pl = 0; pl < NPV; ++pl)
+                        Vf[pl] = pV[pl];
+                    f32x4 ym = {0.f, 0.f, 0.f, 0.f}, ya = {0.f, 0.f, 0.f, 0.f}, oacc = {0.f, 0.f, 0.f, 0.f};
+                    // The first k-step's products run while the second half of S^ is
+                    // split: the scheduling groups interleave one product with a few
+                    // elementwise instructions.
+                    split_state(0);
+                    __builtin_amdgcn_sched_barrier(0);
+                    mma16<NP, NPV>(ym, Mak, Vf);
+                    mma32<NP, NP>(ya, pA[0], Bs[0]);
+                    split_state(1);
+#pragma unroll
+                    for (int g = 0; g < 5; ++g) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one matrix-core product
+                        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // then elementwise work
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                    mma32<NP, NP>(ya, pA[1], Bs[1]);
+#pragma unroll
+                    for (int s = 0; s < 2; ++s)
+                        mma32<NP, NP>(oacc, Rf[s], Bs[s]);
+                    // The LDS reads for the rest of the chunk are issued here, once the
+                    // products above have taken A', R' and S^ out of their registers,
+                    // so that they arrive while Z is formed (the fences keep the
+                    // compiler from sinking them to their first use).
+                    __builtin_amdgcn_sched_barrier(0);
+                    // the state update's [B'^T | K'^T] fragments (key rows 16 pt ..)
+                    s16x8 Uf[4][NP];
 #pragma unroll
                     for (int pt = 0; pt < 4; ++pt) {
-                        const f32x4 p7v = *reinterpret_cast<const f32x4 *>(&sm.p7[16 * pt + 4 * q]);
+                        const int ukey = key_slot(16 * pt + tcol);
 #pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            Sx[pt][e] *= p7v[e];
+                        for (int pl = 0; pl < NP; ++pl)
+                            Uf[pt][pl] = cat(tr4(&sl.X[OP_B][pl][trow][ukey]), tr4(&sl.X[OP_K][pl][trow][ukey]));
                     }
-                }
-                // S^ as matrix-core B operands over the key index: key slot (q, e) of
-                // k-step s is key row 16 (2 s + e/4) + 4 q + e%4, which this lane holds
-                // in Sx[2 s + e/4][e % 4].
-                s16x8 Bs[2][NP];
-                auto split_state = [&](int s) {
-                    float v8[8];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        v8[e] = Sx[2 * s + e / 4][e & 3];
-                    split8<NP>(v8, Bs[s]);
-                };
-                // A'-rows and R'-rows as A operands with the same key slots (stored
-                // contiguously, see key_slot); one accumulator per k-step.
-                // Y = A' S^ + M_ak V in accumulator layout (Y[4 q + e][col m]): A' S^ in
-                // one accumulator over both k-steps and M_ak V in another (a 16x16x16
-                // product never accumulates onto a 16x16x32 one: the compiler inserts no
-                // wait states between the two shapes); R' S^ in one accumulator that the
-                // [M_rb | M_rk] product (the same shape) later continues
-                // V rows as a B operand over the token index (slot (q, e) = token 4 q + e)
-                s16x4 Vf[NPV];
-#pragma unroll
-                for (int pl = 0; pl < NPV; ++pl)
-                    Vf[pl] = pV[pl];
-                f32x4 ym = {0.f, 0.f, 0.f, 0.f}, ya = {0.f, 0.f, 0.f, 0.f}, oacc = {0.f, 0.f, 0.f, 0.f};
-                // The first k-step's products run while the second half of S^ is
-                // split: the scheduling groups interleave one product with a few
-                // elementwise instructions.
-                split_state(0);
-                __builtin_amdgcn_sched_barrier(0);
-                mma16<NP, NPV>(ym, Mak, Vf);
-                mma32<NP, NP>(ya, pA[0], Bs[0]);
-                split_state(1);
-#pragma unroll
-                for (int g = 0; g < 5; ++g) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one matrix-core product
-                    __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // then elementwise work
-                }
-                __builtin_amdgcn_sched_barrier(0);
-                mma32<NP, NP>(ya, pA[1], Bs[1]);
-#pragma unroll
-                for (int s = 0; s < 2; ++s)
-                    mma32<NP, NP>(oacc, Rf[s], Bs[s]);
-                // The LDS reads for the rest of the chunk are issued here, once the
-                // products above have taken A', R' and S^ out of their registers,
-                // so that they arrive while Z is formed (the fences keep the
-                // compiler from sinking them to their first use).
-                __builtin_amdgcn_sched_barrier(0);
-                // the state update's [B'^T | K'^T] fragments (key rows 16 pt ..)
-                s16x8 Uf[4][NP];
-#pragma unroll
-                for (int pt = 0; pt < 4; ++pt) {
-                    const int ukey = key_slot(16 * pt + tcol);
+                    // [M_rb | M_rk] for the output
+                    s16x8 Mf[NP];
 #pragma unroll
                     for (int pl = 0; pl < NP; ++pl)
-                        Uf[pt][pl] = cat(tr4(&sl.X[OP_B][pl][trow][ukey]), tr4(&sl.X[OP_K][pl][trow][ukey]));
-                }
-                // [M_rb | M_rk] for the output
-                s16x8 Mf[NP];
-#pragma unroll
-                for (int pl = 0; pl < NP; ++pl)
-                    Mf[pl] = cat(tr4(&sl.Mt[MT_RB][pl][trow][mcol_t]), tr4(&sl.Mt[MT_RK][pl][trow][mcol_t]));
-                __builtin_amdgcn_sched_barrier(0);
-                // Z = T Y
-                f32x4 z = {0.f, 0.f, 0.f, 0.f};
-                {
-                    f32x4 y4;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        y4[e] = ya[e] + ym[e];
-                    s16x4 Yf[NP];
-                    split4<NP>(y4, Yf);
-                    mma16<NP, NP>(z, Tf, Yf);
-                }
-                // [Z ; V] as one B operand over 32 token slots: (q, e<4) is Z row 4q+e
-                // (this lane's z[e]), (q, e>=4) is V row 4q+e-4.
-                s16x8 ZV[NP];
-                {
-                    s16x4 Zf[NP];
-                    split4<NP>(z, Zf);
-#pragma unroll
-                    for (int pl = 0; pl < NP; ++pl)
-                        ZV[pl] = cat(Zf[pl], pl < NPV ? Vf[pl < NPV ? pl : 0] : s16x4{0, 0, 0, 0});
-                }
-                // o = R' S^ + [M_rb | M_rk] [Z ; V]
-                mma32<NP, NP>(oacc, Mf, ZV);
-                // S^ <- diag(f) (S^ + [B'^T | K'^T] [Z ; V]), one 16-row tile at a time;
-                // the [B'^T | K'^T] fragment of key rows 16 pt .. 16 pt + 15 comes from the
-                // row-major B' and K' planes by transpose loads.  The products go out
-                // before the output stores (a branch the compiler schedules nothing
-                // across), and the row factors are read behind them.
-                f32x4 acc[4], fv[4];
-#pragma unroll
-                for (int pt = 0; pt < 4; ++pt) {
-                    acc[pt] = f32x4{Sx[pt][0], Sx[pt][1], Sx[pt][2], Sx[pt][3]};
-                    mma32<NP, NP>(acc[pt], Uf[pt], ZV);
-                }
-#pragma unroll
-                for (int pt = 0; pt < 4; ++pt)
-                    fv[pt] = *reinterpret_cast<const f32x4 *>(&sl.f[16 * pt + 4 * q]);
-                {
-                    // one uniform base per chunk, per-lane 32-bit offsets
-                    Tout *const ob = go + row_of(t0) + jw;
-                    if (t0 + CH <= L) {
+                        Mf[pl] = cat(tr4(&sl.Mt[MT_RB][pl][trow][mcol_t]), tr4(&sl.Mt[MT_RK][pl][trow][mcol_t]));
+                    __builtin_amdgcn_sched_barrier(0);
+                    // Z = T Y
+                    f32x4 z = {0.f, 0.f, 0.f, 0.f};
+                    {
+                        f32x4 y4;
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
-                            store_o(ob, ooff[e], oacc[e]);
-                    } else {
+                            y4[e] = ya[e] + ym[e];
+                        s16x4 Yf[NP];
+                        split4<NP>(y4, Yf);
+                        mma16<NP, NP>(z, Tf, Yf);
+                    }
+                    // [Z ; V] as one B operand over 32 token slots: (q, e<4) is Z row 4q+e
+                    // (this lane's z[e]), (q, e>=4) is V row 4q+e-4.
+                    s16x8 ZV[NP];
+                    {
+                        s16x4 Zf[NP];
+                        split4<NP>(z, Zf);
 #pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (t0 + 4 * q + e < L)
+                        for (int pl = 0; pl < NP; ++pl)
+                            ZV[pl] = cat(Zf[pl], pl < NPV ? Vf[pl < NPV ? pl : 0] : s16x4{0, 0, 0, 0});
+                    }
+                    // o = R' S^ + [M_rb | M_rk] [Z ; V]
+                    mma32<NP, NP>(oacc, Mf, ZV);
+                    // S^ <- diag(f) (S^ + [B'^T | K'^T] [Z ; V]), one 16-row tile at a time;
+                    // the [B'^T | K'^T] fragment of key rows 16 pt .. 16 pt + 15 comes from the
+                    // row-major B' and K' planes by transpose loads.  The products go out
+                    // before the output stores (a branch the compiler schedules nothing
+                    // across), and the row factors are read behind them.
+#pragma unroll
+                    for (int pt = 0; pt < 4; ++pt) {
+                        acc[pt] = f32x4{Sx[pt][0], Sx[pt][1], Sx[pt][2], Sx[pt][3]};
+                        mma32<NP, NP>(acc[pt], Uf[pt], ZV);
+                    }
+#pragma unroll
+                    for (int pt = 0; pt < 4; ++pt)
+                        fv[pt] = *reinterpret_cast<const f32x4 *>(&sl.f[16 * pt + 4 * q]);
+                    {
+                        // one uniform base per chunk, per-lane 32-bit offsets
+                        Tout *const ob = go + row_of(t0) + jw;
+                        if (t0 + CH <= L) {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
                                 store_o(ob, ooff[e], oacc[e]);
+                        } else {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                if (t0 + 4 * q + e < L)
+                                    store_o(ob, ooff[e], oacc[e]);
+                        }
                     }
                 }
 #pragma unroll
@@ -518,6 +610,7 @@ __global__ __launch_bounds__((kN / J / 16 + nprod<Tin>()) * 64) void wkv7_chunk_
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
                         Sx[pt][e] = acc[pt][e] * fv[pt][e];
+                exact_next = __builtin_amdgcn_readfirstlane(flag_next);
             }
             prefetch(i + 1);
             __builtin_amdgcn_s_barrier();
@@ -638,6 +731,7 @@ __global__ __launch_bounds__((kN / J / 16 + nprod<Tin>()) * 64) void wkv7_chunk_
     // in LDS by the part 2 of chunk c-1, times P_7 of c; d_15 alone once c is
     // past the end).
     float dk[CH + 1], idk[CH + 1];  // factors of the chunk between the two parts
+    int dexact = 0;                 // and whether it takes the exact path (uniform)
     auto decay1_body = [&](const Raw &R, int c) {
         const int i = lane;
         // transpose through LDS: rows in, one key channel per lane out (this
@@ -652,10 +746,9 @@ __global__ __launch_bounds__((kN / J / 16 + nprod<Tin>()) * 64) void wkv7_chunk_
         float w[CH];
 #pragma unroll
         for (int tau = 0; tau < CH; ++tau) {
-            // decays below 2^-15 are raised to it (integer order is float order here)
             const uint32_t bits = F32IN ? __float_as_uint(load_elem(&sm.wbuf[0][0], tau * kN + i))
                                         : static_cast<uint32_t>(reinterpret_cast<const uint16_t *>(&sm.wbuf[0][0])[tau * kN + i]) << 16;
-            w[tau] = __uint_as_float(max(bits, 0x38000000u));
+            w[tau] = __uint_as_float(bits);
         }
         if (c * CH + CH > t_end) {  // partial chunk (uniform): positions past the end decay by 1
 #pragma unroll
@@ -663,7 +756,20 @@ __global__ __launch_bounds__((kN / J / 16 + nprod<Tin>()) * 64) void wkv7_chunk_
                 if (c * CH + tau >= t_end)
                     w[tau] = 1.0f;
         }
+        // the smallest decay magnitude of this key channel; one channel below the bound
+        // (-0.0 included) sends the whole chunk to the exact path, whose decay table is
+        // all ones
+        float wmin = fabsf(w[0]);
+#pragma unroll
+        for (int tau = 1; tau < CH; ++tau)
+            wmin = fminf(wmin, fabsf(w[tau]));
         decay_factors(w, dk, idk);
+        dexact = __builtin_amdgcn_readfirstlane(__ballot(wmin < W_EXACT) != 0ull);
+        if (dexact) {
+#pragma unroll
+            for (int r = 0; r <= CH; ++r)
+                dk[r] = idk[r] = 1.0f;
+        }
     };
     auto decay1 = [&](const Raw &R, int c) {
         if (c >= 0 && c < nchunks)
@@ -683,6 +789,8 @@ __global__ __launch_bounds__((kN / J / 16 + nprod<Tin>()) * 64) void wkv7_chunk_
         else
             sm.slot[(c - 1) % NS].f[i] = sm.d15[(c - 1) & 1][i] * idk[0];
         sm.d15[c & 1][i] = dk[CH];
+        if (i == 0)
+            sm.exact[c & 7] = dexact;
     };
     auto decay2 = [&](int c) {
         if (c == nchunks)

@@ -150,16 +150,63 @@ def test_per_position_states(K, oracle_mod):
 @pytest.mark.parametrize("wval", [0.0, 1e-3])
 @pytest.mark.parametrize("kernel", ["step", "forward"])
 def test_extreme_decays(K, oracle_mod, wval, kernel):
+    # both kernels are exact for every decay in [0, 1]; the chunked kernel evaluates a
+    # chunk that holds a decay below 2^-15 token by token
     inp = synth.make_inputs(2, 50, 3, 64, seed=36, dtype="f32", state_std=0.3)
     w = inp["w"].clone()
     w[:, ::3, :, ::2] = wval  # every third token, half the key channels
     inp["w"] = w
     o_ref, s_ref = oracle_run(oracle_mod, inp)
     o, s = gpu_run(K, to_dev(inp), kernel)
-    # the chunked kernel raises decays below 2^-15 to 2^-15 (documented bound)
-    tol = TOL["f32"] if (kernel == "step" or wval > 0) else 1e-4
-    check(o, o_ref, tol, f"{kernel} w={wval} o", HEADS_SEQ)
-    check(s, s_ref, tol, f"{kernel} w={wval} state", HEADS_STATE)
+    check(o, o_ref, TOL["f32"], f"{kernel} w={wval} o", HEADS_SEQ)
+    check(s, s_ref, TOL["f32"], f"{kernel} w={wval} state", HEADS_STATE)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("B,H", [(1, 2), (2, 64), (4, 64)])
+def test_tiny_decay_chunks_among_ordinary_ones(K, oracle_mod, dtype, B, H):
+    # Chunks 0, 3 and the last, partial one hold a decay below 2^-15 in a few (b, h, key)
+    # entries (0, a denormal, 2^-15 just below); chunk 5 holds exactly 2^-15, which the
+    # factored form still takes; the rest are ordinary.  B*H = 2, 128, 256 run 4, 2 and 1
+    # column blocks per head.
+    T = 16 * 7 + 5
+    inp = synth.make_inputs(B, T, H, 64, seed=3900 + B * H, dtype=dtype, state_std=0.2)
+    w = inp["w"].clone()
+    # the largest value below 2^-15 in the input type
+    below = (torch.nextafter(torch.tensor(2.0 ** -15), torch.tensor(0.0)) if dtype == "f32"
+             else torch.tensor(2.0 ** -15 * (1 - 2.0 ** -8))).to(w.dtype)
+    assert float(below) < 2.0 ** -15
+    w[0, 3, 0, 5] = 0.0
+    w[-1, 50, H - 1, 63] = 1e-40 if dtype == "f32" else 0.0
+    w[:, 16 * 7 + 2, :, 9] = below
+    w[0, 16 * 5 + 7, 0, :] = 2.0 ** -15
+    inp["w"] = w
+    o_ref, s_ref = oracle_run(oracle_mod, inp)
+    o, s = gpu_run(K, to_dev(inp), "forward")
+    check(o, o_ref, TOL[dtype], f"tiny decays {dtype} B={B} H={H} o", HEADS_SEQ)
+    check(s, s_ref, TOL[dtype], f"tiny decays {dtype} B={B} H={H} state", HEADS_STATE)
+
+
+def test_tiny_decays_variable_lengths(K, oracle_mod):
+    # rows of their own lengths, with a zero decay in the last (partial) chunk of one row
+    # and past the end of another (where it must not matter)
+    B, T, H = 3, 60, 4
+    inp = synth.make_inputs(B, T, H, 64, seed=3950, dtype="f32", state_std=0.2)
+    w = inp["w"].clone()
+    w[0, 40, 1, 7] = 0.0   # row 0 runs 45 tokens: inside its last chunk
+    w[1, 50, 2, 3] = 0.0   # row 1 runs 33 tokens: past its end
+    w[2, 1, 0, 0] = 0.0    # row 2 runs all 60
+    inp["w"] = w
+    lengths = [45, 33, 60]
+    o_ref, s_ref = oracle_mod.forward_varlen(*[inp[n] for n in ("r", "w", "k", "v", "a", "b")], inp["state_in"],
+                                             lengths)
+    d = to_dev(inp)
+    o, s = K.wkv7_forward(*[d[n] for n in ("r", "w", "k", "v", "a", "b")], d["state_in"], lengths=lengths)
+    torch.cuda.synchronize()
+    valid = (np.arange(T)[None, :] < np.asarray(lengths)[:, None])[:, :, None, None]
+    og = o.double().cpu().numpy()
+    check(np.where(valid, og, 0.0), np.where(valid, o_ref, 0.0), TOL["f32"], "varlen tiny decays o", HEADS_SEQ)
+    check(s, s_ref, TOL["f32"], "varlen tiny decays state", HEADS_STATE)
 
 
 @pytest.mark.parametrize("kernel", ["step", "forward"])
