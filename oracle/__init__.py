@@ -175,17 +175,12 @@ def tmix_tail(o, r, k, v, g, r_k, ln_w, ln_b, eps):
     o, r, k, v, g = (f(a) for a in (o, r, k, v, g))
     r_k, ln_w, ln_b = (f(a) for a in (r_k, ln_w, ln_b))
     B, T, H, N = o.shape
-    x = np.zeros((B, T, H, N))
-    for bb in range(B):
-        for t in range(T):
-            for h in range(H):
-                row = o[bb, t, h]
-                mu = row.sum() / N
-                var = ((row - mu) ** 2).sum() / N
-                y = (row - mu) / np.sqrt(var + eps) * ln_w[h] + ln_b[h]
-                bonus = (r[bb, t, h] * k[bb, t, h] * r_k[h]).sum()
-                x[bb, t, h] = (y + bonus * v[bb, t, h]) * g[bb, t, h]
-    return x
+    # every (b, t, h) row at once: the sums run over the last axis (the N channels)
+    mu = o.sum(axis=-1, keepdims=True) / N
+    var = ((o - mu) ** 2).sum(axis=-1, keepdims=True) / N
+    y = (o - mu) / np.sqrt(var + eps) * ln_w[None, None] + ln_b[None, None]
+    bonus = (r * k * r_k[None, None]).sum(axis=-1, keepdims=True)
+    return (y + bonus * v) * g
 
 
 def backward(r, w, k, v, a, b, state_in=None, d_o=None, d_state_out=None):
