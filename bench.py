@@ -55,7 +55,7 @@ def recurrent_flops(wl) -> int:
 
 
 def kernel_source_hash(kind: str) -> str:
-    name = {"step": "wkv7_step.hip", "verify": "wkv7_step.hip", "chunk": "wkv7_chunk.hip",
+    name = {"step": "wkv7_step.hip", "verify": "wkv7_step.hip", "chunk": "wkv7_chunk.hip", "chunk_tail": "wkv7_chunk.hip",
             "step_tail": "wkv7_step.hip", "tail_pass": "wkv7_tail.hip", "bwd": "wkv7_bwd.hip",
             "bwd_zero": "wkv7_bwd.hip", "commit": "wkv7_step.hip"}[kind]
     h = hashlib.sha256()
@@ -304,6 +304,40 @@ def time_tail_pass(K, synth, idx: int, steps: int, warmup: int):
         e1.synchronize()
     ms = e0.elapsed_time(e1) / steps
     return {"sec_per_launch": ms / 1e3}
+
+
+def time_forward_tail(K, synth, idx: int, steps: int, warmup: int):
+    """The parallel pass with the time-mix tail fused (wkv7_forward_tail) over prefill workload
+    idx: x (fp32) is written instead of o."""
+    import torch
+    wl = synth.WORKLOADS[idx]
+    d = synth.workload_inputs(idx, device="cuda")
+    gen = torch.Generator(device="cuda").manual_seed(79)
+    g = torch.sigmoid(torch.randn(d["r"].shape, generator=gen, device="cuda")).to(d["r"].dtype)
+    prm = tail_params(wl.H, 80)
+    x = torch.empty((wl.B, wl.T, wl.H, N), dtype=torch.float32, device="cuda")
+    s_out = torch.empty((wl.B, wl.H, N, N), dtype=torch.float32, device="cuda")
+    ins = [d[n] for n in ("r", "w", "k", "v", "a", "b")]
+    stream = torch.cuda.Stream()
+    run = lambda: K.wkv7_forward_tail(*ins, g, *prm, 64e-5, d["state_in"], x=x, state_out=s_out)
+    with torch.cuda.stream(stream):
+        warm(run, warmup)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            run()
+        e1.record(stream)
+        e1.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    return {"sec_per_launch": ms / 1e3, "mtok_s": wl.B * wl.T / (ms / 1e3) / 1e6}
+
+
+def forward_tail_bytes(wl) -> int:
+    """Algorithmic bytes of the fused prefill + tail: the six inputs and the gate read once,
+    x (fp32) written once, the state read and written once, the tail's per-head parameters."""
+    e_in = 2 if wl.dtype == "bf16" else 4
+    b = wl.B * wl.T * wl.H * N * (7 * e_in + 4)
+    return b + (2 if wl.state_std > 0 else 1) * wl.B * wl.H * N * N * 4 + 3 * wl.H * N * 4
 
 
 def backward_bytes(wl) -> int:
@@ -570,6 +604,12 @@ def main():
         rp = roofline(b_pass, tp["sec_per_launch"], "tail_pass", 3)
         others["3-tail-pass"] = {"workload": w3.name + " (time-mix tail pass)",
                                  "ms_per_call": round(tp["sec_per_launch"] * 1e3, 4), "roofline": rp}
+        # the prefill with the tail fused into the chunked kernel (x instead of o)
+        tf = time_forward_tail(K, synth, 3, max(20, args.steps), args.warmup)
+        rf = roofline(forward_tail_bytes(w3), tf["sec_per_launch"], "chunk_tail", 3)
+        others["3-fused-tail"] = {"workload": w3.name + " (prefill with the time-mix tail fused)",
+                                  "ms_per_call": round(tf["sec_per_launch"] * 1e3, 4), "roofline": rf,
+                                  "mtok_s": round(tf["mtok_s"], 2)}
         # the backward pass (gradients) over workload 2, from the per-position states
         w2 = synth.WORKLOADS[2]
         tg = time_backward(K, synth, 2, max(5, args.steps // 4), min(args.warmup, 2))

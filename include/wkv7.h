@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define WKV7_ABI_VERSION 4
+#define WKV7_ABI_VERSION 5
 
 /* Element types of r, w, k, v, a, b (in_dtype) and of o (o_dtype). */
 enum wkv7_dtype {
@@ -200,6 +200,26 @@ int wkv7_step_tail(const void *r, const void *w, const void *k, const void *v,
                    const void *gate, const float *r_k, const float *ln_w, const float *ln_b,
                    float eps, void *x, int x_dtype, float *state_out, float *state_pos,
                    int B, int T, int H, int N, void *stream);
+
+/*
+ * wkv7_forward_tail -- wkv7_forward with the time-mix tail fused: the parallel
+ * (prefill) pass writes x (type x_dtype, layout of o) instead of o, and o never
+ * reaches memory.  The SwiftRWKV Inference guide runs this tail over the B*T rows
+ * of its parallel pass (the fused frozen pass).
+ *   gate : [B,T,H,N] of in_dtype;  r_k, ln_w, ln_b : [H,N] fp32;  eps : as above.
+ * Every other argument as for wkv7_forward (x in the place of o); gate, r_k,
+ * ln_w and ln_b may not overlap x or state_out.  With bf16 inputs and T >= 9 one
+ * chunked kernel computes both (a head per workgroup; o stays in LDS); shorter
+ * sequences take the step kernel with its fused tail.  With fp32 inputs and an fp32
+ * x, the chunked kernel writes o into x and the tail pass then runs in place; with
+ * fp32 inputs and a bf16 x, the step kernel with its fused tail runs the whole
+ * sequence (exact, slower).
+ */
+int wkv7_forward_tail(const void *r, const void *w, const void *k, const void *v,
+                      const void *a, const void *b, int in_dtype, const float *state_in,
+                      const void *gate, const float *r_k, const float *ln_w, const float *ln_b,
+                      float eps, void *x, int x_dtype, float *state_out,
+                      int B, int T, int H, int N, void *stream);
 
 /*
  * wkv7_tmix_tail -- the time-mix tail as a pass of its own, for the output of

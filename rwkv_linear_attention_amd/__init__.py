@@ -17,6 +17,9 @@ Functions (names as in the C ABI):
 * ``wkv7_step_tail(r, w, k, v, a, b, g, r_k, ln_w, ln_b, eps, state_in=None, ...)``
   -> ``(x, state_out[, state_pos])``: the recurrent pass with the time-mix tail
   (group norm, bonus, gate) fused into its epilogue.
+* ``wkv7_forward_tail(r, w, k, v, a, b, g, r_k, ln_w, ln_b, eps, state_in=None, ...)``
+  -> ``(x, state_out)``: the parallel pass with the time-mix tail fused (o is never
+  written).
 * ``wkv7_tmix_tail(o, r, k, v, g, r_k, ln_w, ln_b, eps, x_dtype=torch.float32)`` -> ``x``:
   the same tail as a pass of its own, after the parallel pass.
 * ``wkv7_state_commit(state_pos, accepted, state_in=None)`` -> ``state_out``: the state
@@ -79,6 +82,8 @@ def lib():
         cf = ctypes.c_float
         L.wkv7_step_tail.argtypes = [vp] * 6 + [ci, vp, vp, vp, vp, vp, cf, vp, ci, vp, vp, ci, ci, ci, ci, vp]
         L.wkv7_step_tail.restype = ci
+        L.wkv7_forward_tail.argtypes = [vp] * 6 + [ci, vp, vp, vp, vp, vp, cf, vp, ci, vp, ci, ci, ci, ci, vp]
+        L.wkv7_forward_tail.restype = ci
         L.wkv7_tmix_tail.argtypes = [vp, ci, vp, vp, vp, vp, ci, vp, vp, vp, cf, vp, ci, ci, ci, ci, ci, vp]
         L.wkv7_tmix_tail.restype = ci
         L.wkv7_state_reset.argtypes = [vp, ci, ci, ci, vp, vp]
@@ -257,6 +262,30 @@ def wkv7_step_tail(r, w, k, v, a, b, g, r_k, ln_w, ln_b, eps, state_in=None, *, 
                                 _ptr(state_pos), B, T, H, N, _stream(dev)))
     if state_pos is not None:
         return x, state_out, state_pos
+    return x, state_out
+
+
+def wkv7_forward_tail(r, w, k, v, a, b, g, r_k, ln_w, ln_b, eps, state_in=None, *, x_dtype=torch.float32,
+                      x=None, state_out=None):
+    """wkv7_forward with the time-mix tail fused: returns (x, state_out); o is never written.
+
+    g: gate [B, T, H, N] like r; r_k, ln_w, ln_b: fp32 [H, N]; eps: float.
+    """
+    B, T, H, N = _check_inputs(r, w, k, v, a, b)
+    dev = r.device
+    if g.shape != r.shape or g.dtype != r.dtype or not g.is_contiguous() or g.device != dev:
+        raise ValueError("g must match r in shape, dtype and device, and be contiguous")
+    r_k, ln_w, ln_b = _head_params(H, N, dev, r_k=r_k, ln_w=ln_w, ln_b=ln_b)
+    state_in = _state_arg(state_in, B, H, N, dev, "state_in")
+    if state_out is None:
+        state_out = torch.empty((B, H, N, N), dtype=torch.float32, device=dev)
+    _state_arg(state_out, B, H, N, dev, "state_out")
+    if x is None:
+        x = torch.empty((B, T, H, N), dtype=x_dtype, device=dev)
+    _out_arg(x, (B, T, H, N), dev, "x")
+    _check(lib().wkv7_forward_tail(*[_ptr(t) for t in (r, w, k, v, a, b)], _dt(r), _ptr(state_in), _ptr(g),
+                                   _ptr(r_k), _ptr(ln_w), _ptr(ln_b), float(eps), _ptr(x), _dt(x),
+                                   _ptr(state_out), B, T, H, N, _stream(dev)))
     return x, state_out
 
 

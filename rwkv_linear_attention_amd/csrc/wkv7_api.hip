@@ -36,7 +36,7 @@ bool misaligned(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) !
 // B*T*H*N*N must fit in int64 (and every partial product with it).
 // Largest B * H that one launch of a kernel covers.  A head is one workgroup of
 // the step kernel (up to 512 threads) or up to J workgroups of the chunked kernel
-// (up to 896 threads each, J = 1 beyond 128 heads), and a launch holds fewer than
+// (up to 1024 threads each, J = 1 beyond 128 heads), and a launch holds fewer than
 // 2^32 threads.
 constexpr int64_t kMaxHeadsStep = WKV7_MAX_HEADS_STEP;
 constexpr int64_t kMaxHeadsChunk = WKV7_MAX_HEADS_CHUNK;
@@ -46,7 +46,7 @@ constexpr int64_t kMaxHChunk = WKV7_MAX_H_CHUNK;
 static_assert((15 * kMaxHChunk * kN + 15) * 4 < (1ll << 32), "32-bit output offsets of the chunked kernel");
 // Largest B * T * H of the time-mix tail pass (16 threads per row).
 constexpr int64_t kMaxRowsTail = WKV7_MAX_ROWS_TAIL;
-static_assert(kMaxHeadsStep * 512 < (1ll << 32) && kMaxHeadsChunk * 896 < (1ll << 32) &&
+static_assert(kMaxHeadsStep * 512 < (1ll << 32) && kMaxHeadsChunk * 1024 < (1ll << 32) &&
                   kMaxRowsTail * 16 < (1ll << 32),
               "a launch must hold fewer than 2^32 threads");
 
@@ -281,6 +281,58 @@ int wkv7_step_tail(const void *r, const void *w, const void *k, const void *v, c
     args.ln_b = ln_b;
     args.eps = eps;
     return wkv7::launch_step(args, s) == hipSuccess ? WKV7_OK : WKV7_ERR_HIP;
+}
+
+int wkv7_forward_tail(const void *r, const void *w, const void *k, const void *v, const void *a,
+                      const void *b, int in_dtype, const float *state_in, const void *gate, const float *r_k,
+                      const float *ln_w, const float *ln_b, float eps, void *x, int x_dtype, float *state_out,
+                      int B, int T, int H, int N, void *stream)
+{
+    // fp32 inputs with an fp32 x (T >= kChunkMinT) finish with the tail pass, under its row limit
+    const bool two_pass = in_dtype == WKV7_F32 && x_dtype == WKV7_F32 && T >= kChunkMinT;
+    if (two_pass && B >= 1 && H >= 1 && static_cast<int64_t>(B) * T * H > kMaxRowsTail)
+        return WKV7_ERR_SHAPE;
+    int st = check_seq(r, w, k, v, a, b, in_dtype, state_in, x, x_dtype, state_out, nullptr, B, T, H, N, false,
+                       false);
+    if (st != WKV7_OK)
+        return st;
+    const int64_t tok = static_cast<int64_t>(B) * T * H;
+    const int64_t ex = x_dtype == WKV7_BF16 ? 2 : 4;
+    const Range outs[2] = {T > 0 ? range_of(x, tok * kN * ex) : Range{0, 0},
+                           range_of(state_out, static_cast<int64_t>(B) * H * kN * kN * 4)};
+    st = check_tail_inputs(gate, r_k, ln_w, ln_b, in_dtype, B, T, H, outs, 2);
+    if (st != WKV7_OK)
+        return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (T == 0)
+        return empty_sequence(state_in, state_out, B, H, s);
+    SeqArgs args = make_args(r, w, k, v, a, b, in_dtype, state_in, x, x_dtype, state_out, nullptr, B, T, H);
+    args.gate = gate;
+    args.r_k = r_k;
+    args.ln_w = ln_w;
+    args.ln_b = ln_b;
+    args.eps = eps;
+    hipError_t e;
+    if (T < kChunkMinT || (in_dtype == WKV7_F32 && x_dtype == WKV7_BF16)) {
+        e = wkv7::launch_step(args, s);  // the step kernel with its fused tail
+    } else if (!two_pass) {
+        e = wkv7::launch_chunk(args, s);  // bf16 inputs: one chunked kernel with the tail wave
+    } else {
+        // fp32 inputs: o (fp32) into x, then the tail pass over x in place
+        args.gate = nullptr;
+        e = wkv7::launch_chunk(args, s);
+        if (e == hipSuccess) {
+            wkv7::TailArgs t;
+            t.o = x; t.r = r; t.k = k; t.v = v; t.gate = gate;
+            t.r_k = r_k; t.ln_w = ln_w; t.ln_b = ln_b; t.eps = eps;
+            t.x = x; t.rows = tok; t.H = H;
+            t.in_bf16 = 0;
+            t.o_bf16 = 0;
+            t.x_bf16 = 0;
+            e = wkv7::launch_tail(t, s);
+        }
+    }
+    return e == hipSuccess ? WKV7_OK : WKV7_ERR_HIP;
 }
 
 int wkv7_tmix_tail(const void *o, int o_dtype, const void *r, const void *k, const void *v, const void *gate,

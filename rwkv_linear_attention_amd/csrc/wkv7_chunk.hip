@@ -176,6 +176,15 @@ __device__ __forceinline__ void split4(const f32x4 v, s16x4 (&out)[NP])
 
 __device__ __forceinline__ s16x8 lds8(const uint16_t *p) { return *reinterpret_cast<const s16x8 *>(p); }
 
+// Four consecutive outputs to global memory (fp32, or bf16 rounded to nearest even).
+__device__ __forceinline__ void store4(float *p, const f32x4 x) { *reinterpret_cast<f32x4 *>(p) = x; }
+__device__ __forceinline__ void store4(uint16_t *p, const f32x4 x)
+{
+    const uint32_t lo = f32_to_bf16_bits(x[0]) | (static_cast<uint32_t>(f32_to_bf16_bits(x[1])) << 16);
+    const uint32_t hi = f32_to_bf16_bits(x[2]) | (static_cast<uint32_t>(f32_to_bf16_bits(x[3])) << 16);
+    *reinterpret_cast<u32x2 *>(p) = u32x2{lo, hi};
+}
+
 // Four consecutive input elements from global memory, widened to fp32.
 __device__ __forceinline__ f32x4 load4(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
 __device__ __forceinline__ f32x4 load4(const uint16_t *p)
@@ -238,7 +247,17 @@ struct alignas(16) DSlot {
 };
 
 constexpr int MTP = 20;  // row pitch (floats) of the fp32 transpose tiles of M_ab
-template <typename Tin, int NP, int NPV, int NS, int NT>
+// The tail variant's o of the last two chunks, fp32, [token][column] with a row pitch
+// of OTP floats (the consumers' writes of four token rows then hit different banks).
+constexpr int OTP = kN + 4;
+template <int NOT>
+struct OTiles {
+    alignas(16) float t[NOT][CH][OTP];
+};
+template <>
+struct OTiles<0> {};
+
+template <typename Tin, int NP, int NPV, int NS, int NT, int NOT>
 struct Smem {
     Slot<NP, NPV> slot[NS];
     alignas(16) Tin wbuf[CH][kN];  // w rows of one chunk, transposed through here by the decay wave
@@ -247,6 +266,7 @@ struct Smem {
     alignas(16) float d15[2][kN];  // d_15 of the last two chunks whose table was written
     alignas(16) float mt[NT][CH][MTP];  // M_ab of one chunk per inverse wave, row-major
     int exact[8];  // chunk c % 8 takes the exact path (its decay table is all ones)
+    OTiles<NOT> ot;
 };
 
 // Decay factors of one key channel over a chunk: d[tau+1] = P_tau / P_7 and
@@ -279,9 +299,13 @@ __device__ __forceinline__ void decay_factors(const float (&w)[CH], float (&d)[C
     }
 }
 
-template <typename Tin, typename Tout, int J, bool HAS_STATE_IN>
-__global__ __launch_bounds__((kN / J / 16 + nprod<Tin>()) * 64) void wkv7_chunk_kernel(SeqArgs p, int per_xcd,
-                                                                                   int nblocks)
+// With TAIL (bf16 inputs, J = 1) the time-mix tail is fused: the consumers leave o in
+// LDS, and NTAIL more waves turn each chunk's rows into x (written through p.o, of
+// type Tout) one iteration later.
+constexpr int NTAIL = 2;
+template <typename Tin, typename Tout, int J, bool HAS_STATE_IN, bool TAIL>
+__global__ __launch_bounds__((kN / J / 16 + nprod<Tin>() + (TAIL ? NTAIL : 0)) * 64) void wkv7_chunk_kernel(
+    SeqArgs p, int per_xcd, int nblocks)
 {
     constexpr int NC = kN / J;            // value columns of this workgroup
     constexpr int NSW = NC / 16;          // consumer waves (16 state columns each)
@@ -294,7 +318,8 @@ __global__ __launch_bounds__((kN / J / 16 + nprod<Tin>()) * 64) void wkv7_chunk_
     constexpr bool DEEP = !F32IN;
     constexpr int NS = DEEP ? 4 : 3;
     using SlotT = Slot<NP, NPV>;
-    __shared__ Smem<Tin, NP, NPV, NS, DEEP ? 2 : 1> sm;
+    static_assert(!TAIL || (J == 1 && !F32IN), "the fused tail runs with bf16 inputs and whole heads");
+    __shared__ Smem<Tin, NP, NPV, NS, DEEP ? 2 : 1, TAIL ? 2 : 0> sm;
 
     // Workgroup -> (batch*head, column block).  Workgroups are dealt to the
     // XCDs round-robin; the J column blocks of one head stay on one XCD so the
@@ -377,7 +402,7 @@ __global__ __launch_bounds__((kN / J / 16 + nprod<Tin>()) * 64) void wkv7_chunk_
         // chunk unscaled).  Lane (q, m) holds rows 16 pt + 4 q + e of column jw + m; a
         // sum over the key rows adds the four lanes of a column (m, m+16, m+32, m+48)
         // by two exchanges, which give all four the same value.
-        auto exact_chunk = [&](int t0) {
+        auto exact_chunk = [&](int t0, int c) {
             const int nt = min(CH, L - t0);
 #pragma unroll 1
             for (int tau = 0; tau < nt; ++tau) {
@@ -420,8 +445,12 @@ __global__ __launch_bounds__((kN / J / 16 + nprod<Tin>()) * 64) void wkv7_chunk_
                 }
                 op += __shfl_xor(op, 16);
                 op += __shfl_xor(op, 32);
-                if (q == 0)
-                    store_elem(go + row, jc, op);
+                if (q == 0) {
+                    if constexpr (TAIL)
+                        sm.ot.t[c & 1][tau][jc] = op;
+                    else
+                        store_elem(go + row, jc, op);
+                }
             }
         };
 
@@ -459,7 +488,7 @@ __global__ __launch_bounds__((kN / J / 16 + nprod<Tin>()) * 64) void wkv7_chunk_
                 if (exact_next) {
                     // S^ enters unscaled (this chunk's P_7 is 1) and leaves scaled by f = P_7
                     // of the next chunk (this chunk's d_15 is 1)
-                    exact_chunk(t0);
+                    exact_chunk(t0, i);
 #pragma unroll
                     for (int pt = 0; pt < 4; ++pt)
                         acc[pt] = f32x4{Sx[pt][0], Sx[pt][1], Sx[pt][2], Sx[pt][3]};
@@ -590,7 +619,13 @@ __global__ __launch_bounds__((kN / J / 16 + nprod<Tin>()) * 64) void wkv7_chunk_
 #pragma unroll
                     for (int pt = 0; pt < 4; ++pt)
                         fv[pt] = *reinterpret_cast<const f32x4 *>(&sl.f[16 * pt + 4 * q]);
-                    {
+                    if constexpr (TAIL) {
+                        // the chunk's o stays in LDS for the tail wave (rows past the end too:
+                        // that wave writes x for the row's tokens only)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            sm.ot.t[i & 1][4 * q + e][jw + m] = oacc[e];
+                    } else {
                         // one uniform base per chunk, per-lane 32-bit offsets
                         Tout *const ob = go + row_of(t0) + jw;
                         if (t0 + CH <= L) {
@@ -612,7 +647,15 @@ __global__ __launch_bounds__((kN / J / 16 + nprod<Tin>()) * 64) void wkv7_chunk_
                         Sx[pt][e] = acc[pt][e] * fv[pt][e];
                 exact_next = __builtin_amdgcn_readfirstlane(flag_next);
             }
+            if constexpr (TAIL)
+                asm volatile("" ::: "memory");  // the o-tile writes are issued before the prefetch
             prefetch(i + 1);
+            if constexpr (TAIL) {
+                // this chunk's o-tile writes are complete before the barrier; the last
+                // 2 NP + NPV LDS operations (the prefetch just issued) may stay in flight
+                static_assert(2 * NP + NPV <= 15, "lgkmcnt field");
+                __builtin_amdgcn_s_waitcnt(0xc07f | ((2 * NP + NPV) << 8));
+            }
             __builtin_amdgcn_s_barrier();
             // The barrier alone is not a memory operation to the compiler: this
             // keeps it from moving or merging LDS reads across it (no instruction,
@@ -634,7 +677,8 @@ __global__ __launch_bounds__((kN / J / 16 + nprod<Tin>()) * 64) void wkv7_chunk_
     //   R_T : M_ab and T            R_D : decay table (from w)
     //   R_MA: M_ak                  R_SA, R_SR, R_SB, R_SK: A', R', B', K' (R_SK also v)
     //   R_MR: M_rb, M_rk
-    enum { R_T = 0, R_MA = 1, R_MR = 2, R_D = 3, R_SA = 4, R_SR = 5, R_SB = 6, R_SK = 7, R_T1 = 8, R_D1 = 9 };
+    enum { R_T = 0, R_MA = 1, R_MR = 2, R_D = 3, R_SA = 4, R_SR = 5, R_SB = 6, R_SK = 7, R_T1 = 8, R_D1 = 9,
+           R_TAIL = 10 };
     // Producer k runs on SIMD (NSW + k) % 4, beside the consumer wave of that SIMD
     // if there is one.  The consumers set the pace, so the matrix-core work of the
     // producers (the inverse waves above all) is spread evenly over the consumers'
@@ -643,8 +687,9 @@ __global__ __launch_bounds__((kN / J / 16 + nprod<Tin>()) * 64) void wkv7_chunk_
     //   bf16 inputs, J = 1: (MR, SB, D) (SK, MA, D1) (T, SA) (T1, SR)
     //   bf16 inputs, J = 2 (consumers on SIMDs 0 and 1): (SK, SA) (SB, SR) on the
     //   consumers' SIMDs, (T, D1, MA) (T1, D, MR) on the other two
-    // R_T / R_T1 and R_D / R_D1 take the even and the odd chunks.
-    constexpr unsigned long long ROLES = !DEEP ? 0x25316470ull : J == 1 ? 0x9354168072ull : 0x2154396780ull;
+    // R_T / R_T1 and R_D / R_D1 take the even and the odd chunks.  The tail waves, when
+    // there are any, are the last two (SIMDs 2 and 3, beside the inverse waves).
+    constexpr unsigned long long ROLES = !DEEP ? 0x25316470ull : J == 1 ? 0xAA9354168072ull : 0x2154396780ull;
     const int role = static_cast<int>((ROLES >> (4 * (wv - NSW))) & 15);
     const int t_end = L;
 
@@ -1007,6 +1052,100 @@ __global__ __launch_bounds__((kN / J / 16 + nprod<Tin>()) * 64) void wkv7_chunk_
             inv_b_body(c);
     };
 
+    // ---- tail waves (TAIL): in iteration i, the time-mix tail of chunk i-1, whose o the
+    // consumers left in LDS in iteration i-1; the last chunk after the loop.  Tail wave
+    // u takes tokens 8 u .. 8 u + 7 of each chunk in two passes; lane (r, c) of a pass
+    // takes token 8 u + 4 pass + r, channels 4 c .. 4 c + 3 (tail_row4: one row per 16
+    // lanes).  Its r, k, v and gate were loaded one iteration before.
+    auto tail_role = [&]() {
+        if constexpr (TAIL) {
+            constexpr int NPASS = CH / 4 / NTAIL;
+            const int tw = wv - (NSW + nprod<Tin>());  // which tail wave
+            const int c0 = 4 * (lane & 15), rr = NPASS * 4 * tw + (lane >> 4);
+            const int pj = hh * kN + c0;
+            const f32x4 rk4 = *reinterpret_cast<const f32x4 *>(p.r_k + pj);
+            const f32x4 w4 = *reinterpret_cast<const f32x4 *>(p.ln_w + pj);
+            const f32x4 b4 = *reinterpret_cast<const f32x4 *>(p.ln_b + pj);
+            const Tin *const ins[4] = {static_cast<const Tin *>(p.r), static_cast<const Tin *>(p.k),
+                                       static_cast<const Tin *>(p.v), static_cast<const Tin *>(p.gate)};
+            Tout *__restrict__ gxo = static_cast<Tout *>(p.o);
+            // the rows of one chunk, [pass][r, k, v, gate], four bf16 channels each; three
+            // sets in rotation, loaded three iterations before use (as the scale waves do)
+            typedef u32x2 Rows[NPASS][4];
+            Rows R0, R1, R2;
+            // a chunk's rows as byte offsets (32-bit) from its first row: (15 H N + 60) * 2 < 2^32
+            auto load_rows = [&](Rows &R, int c) {  // unconditional: chunks outside the row re-read one inside
+                c = max(0, min(c, nchunks - 1));
+                const uint64_t base = row_of(c * CH);
+#pragma unroll
+                for (int pz = 0; pz < NPASS; ++pz) {
+                    const int tau = min(4 * pz + rr, t_end - 1 - c * CH);
+                    const uint32_t off = (static_cast<uint32_t>(tau) * rs32 + c0) * 2u;
+#pragma unroll
+                    for (int x = 0; x < 4; ++x)
+                        R[pz][x] = *reinterpret_cast<const u32x2 *>(
+                            reinterpret_cast<const char *>(ins[x] + base) + off);
+                }
+            };
+            auto unpack = [](const u32x2 u) {
+                return f32x4{bf16_lo(u[0]), bf16_hi(u[0]), bf16_lo(u[1]), bf16_hi(u[1])};
+            };
+            auto tail_chunk = [&](int c, const Rows &R) {
+                // the passes' rows straight-line (their chains interleave), then the stores
+                f32x4 o4[NPASS], x4[NPASS];
+#pragma unroll
+                for (int pz = 0; pz < NPASS; ++pz)
+                    o4[pz] = *reinterpret_cast<const f32x4 *>(&sm.ot.t[c & 1][4 * pz + rr][c0]);
+#pragma unroll
+                for (int pz = 0; pz < NPASS; ++pz)
+                    x4[pz] = tail_row4(o4[pz], unpack(R[pz][0]), unpack(R[pz][1]), unpack(R[pz][2]),
+                                       unpack(R[pz][3]), rk4, w4, b4, p.eps);
+                Tout *const xb = gxo + row_of(c * CH);
+#pragma unroll
+                for (int pz = 0; pz < NPASS; ++pz) {
+                    const int tau = 4 * pz + rr;
+                    const uint32_t off = (static_cast<uint32_t>(tau) * rs32 + c0) * static_cast<uint32_t>(sizeof(Tout));
+                    if (c * CH + tau < t_end)
+                        store4(reinterpret_cast<Tout *>(reinterpret_cast<char *>(xb) + off), x4[pz]);
+                }
+            };
+            // iteration i (set (i - I0) % 3) takes chunk i-1 and loads chunk i+2 into the same set
+            auto work = [&](int i, Rows &R) {
+                if (i >= 1)
+                    tail_chunk(i - 1, R);
+                load_rows(R, i + 2);
+            };
+            load_rows(R0, I0 - 1);
+            load_rows(R1, I0);
+            load_rows(R2, I0 + 1);
+            int i = I0;
+            for (; i + 2 < nchunks; i += 3) {
+                work(i, R0);
+                __syncthreads();
+                work(i + 1, R1);
+                __syncthreads();
+                work(i + 2, R2);
+                __syncthreads();
+            }
+            if (i < nchunks) {
+                work(i, R0);
+                __syncthreads();
+                if (i + 1 < nchunks) {
+                    work(i + 1, R1);
+                    __syncthreads();
+                }
+            }
+            // the last chunk, after the last barrier, from the set its iteration would use
+            const int kf = (nchunks - I0) % 3;
+            if (kf == 0)
+                tail_chunk(nchunks - 1, R0);
+            else if (kf == 1)
+                tail_chunk(nchunks - 1, R1);
+            else
+                tail_chunk(nchunks - 1, R2);
+        }
+    };
+
     // Pipeline: each role runs its own copy of the loop, one barrier per
     // iteration.  The waves that load input rows unroll it by three and keep
     // three register sets: the rows a wave works on in iteration i were loaded
@@ -1143,6 +1282,8 @@ __global__ __launch_bounds__((kN / J / 16 + nprod<Tin>()) * 64) void wkv7_chunk_
             }
             load_w(fr, i + OFF_D1 + 3);
         });
+    } else if (TAIL && role == R_TAIL) {
+        tail_role();
     } else if (role == R_SK) {
         scale_role(U{});
     } else {
@@ -1150,23 +1291,32 @@ __global__ __launch_bounds__((kN / J / 16 + nprod<Tin>()) * 64) void wkv7_chunk_
     }
 }
 
-template <typename Tin, typename Tout, int J>
+template <typename Tin, typename Tout, int J, bool TAIL = false>
 hipError_t launch_j(const SeqArgs &p, hipStream_t stream)
 {
     const int nblocks = p.B * p.H * J;
     int per_xcd = (nblocks + 7) / 8;
     per_xcd = (per_xcd + J - 1) / J * J;  // a head's column blocks never straddle two XCDs
-    const dim3 grid(8 * per_xcd), block((kN / J / 16 + nprod<Tin>()) * 64);
+    const dim3 grid(8 * per_xcd), block((kN / J / 16 + nprod<Tin>() + (TAIL ? NTAIL : 0)) * 64);
     if (p.state_in)
-        hipLaunchKernelGGL((wkv7_chunk_kernel<Tin, Tout, J, true>), grid, block, 0, stream, p, per_xcd, nblocks);
+        hipLaunchKernelGGL((wkv7_chunk_kernel<Tin, Tout, J, true, TAIL>), grid, block, 0, stream, p, per_xcd,
+                           nblocks);
     else
-        hipLaunchKernelGGL((wkv7_chunk_kernel<Tin, Tout, J, false>), grid, block, 0, stream, p, per_xcd, nblocks);
+        hipLaunchKernelGGL((wkv7_chunk_kernel<Tin, Tout, J, false, TAIL>), grid, block, 0, stream, p, per_xcd,
+                           nblocks);
     return hipGetLastError();
 }
 
 template <typename Tin, typename Tout>
 hipError_t launch_typed(const SeqArgs &p, hipStream_t stream)
 {
+    // The fused tail needs every column of a token in one workgroup: whole heads.
+    if (p.gate) {
+        if constexpr (std::is_same<Tin, uint16_t>::value)
+            return launch_j<Tin, Tout, 1, true>(p, stream);
+        else
+            return hipErrorInvalidValue;  // the C ABI routes fp32 inputs elsewhere
+    }
     // One workgroup fills a compute unit's LDS; split heads into column blocks
     // only while the grid still fits in one pass over the 256 compute units.
     const long long heads = static_cast<long long>(p.B) * p.H;

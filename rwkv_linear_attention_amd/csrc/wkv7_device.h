@@ -67,4 +67,52 @@ __device__ __forceinline__ float tail_lane(float oj, float rj, float kj, float r
     return tail_norm(oj, wave_sum(rj * kj * rkj), vj, gj, wj, bj, eps);
 }
 
+// x from another lane of the same 16-lane row, by a DPP control (no LDS round trip).
+// Every control used here reads inside the row, so bound_ctrl never applies; setting
+// it lets the compiler fold the move into the add that consumes it.
+template <int CTRL>
+__device__ __forceinline__ float row_dpp(float x)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, true));
+}
+
+// Sum over the 16 lanes of a row group (lanes 16 g .. 16 g + 15), returned to all of
+// them: the other lane of each pair (quad_perm 1,0,3,2), of each quad (2,3,0,1), then
+// the mirrored quad of the half row and the mirrored half of the row.  Each step adds
+// two partial sums that the lanes hold in swapped roles, so every lane gets the same
+// bits.
+__device__ __forceinline__ float group16_sum(float x)
+{
+    x += row_dpp<0xb1>(x);   // quad_perm [1, 0, 3, 2]
+    x += row_dpp<0x4e>(x);   // quad_perm [2, 3, 0, 1]
+    x += row_dpp<0x141>(x);  // row_half_mirror
+    x += row_dpp<0x140>(x);  // row_mirror
+    return x;
+}
+
+// The same tail for one (b, t, h) row held by the 16 lanes of a row group, four
+// channels per lane: o4, r4, k4, v4, g4 are the lane's channels of the row, rk4,
+// w4, b4 its channels of r_k, ln_w, ln_b.  Every lane of the group must take part.
+__device__ __forceinline__ f32x4 tail_row4(const f32x4 o4, const f32x4 r4, const f32x4 k4, const f32x4 v4,
+                                           const f32x4 g4, const f32x4 rk4, const f32x4 w4, const f32x4 b4,
+                                           float eps)
+{
+    const float mu = group16_sum((o4[0] + o4[1]) + (o4[2] + o4[3])) * (1.0f / kN);
+    f32x4 d;
+    float ss = 0.f, bon = 0.f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        d[c] = o4[c] - mu;
+        ss += d[c] * d[c];
+        bon += r4[c] * k4[c] * rk4[c];
+    }
+    const float inv = rsqrtf(group16_sum(ss) * (1.0f / kN) + eps);
+    const float bonus = group16_sum(bon);
+    f32x4 xo;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+        xo[c] = (d[c] * inv * w4[c] + b4[c] + bonus * v4[c]) * g4[c];
+    return xo;
+}
+
 }  // namespace wkv7

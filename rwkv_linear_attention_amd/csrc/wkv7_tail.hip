@@ -27,17 +27,7 @@ __device__ __forceinline__ void store4(uint16_t *p, size_t i, const f32x4 &x)
     *reinterpret_cast<uint2 *>(p + i) = uint2{lo, hi};
 }
 
-// Sum over the 16 lanes of a row group (lanes 16 g .. 16 g + 15).
-__device__ __forceinline__ float group16_sum(float x)
-{
-#pragma unroll
-    for (int off = 8; off >= 1; off >>= 1)
-        x += __shfl_xor(x, off);
-    return x;
-}
-
-// One (b, t, h) row per 16 lanes, four channels per lane (wide loads), the
-// arithmetic of tail_lane with the sums taken over the row's 16 lanes.
+// One (b, t, h) row per 16 lanes, four channels per lane (wide loads): tail_row4.
 template <typename Tin, typename To, typename Tx>
 __global__ __launch_bounds__(256) void tmix_tail_kernel(const To *o, const Tin *r, const Tin *k, const Tin *v,
                                                         const Tin *gate, const float *r_k, const float *ln_w,
@@ -53,22 +43,7 @@ __global__ __launch_bounds__(256) void tmix_tail_kernel(const To *o, const Tin *
     const f32x4 o4 = load4(o, e);
     const f32x4 r4 = load4(r, e), k4 = load4(k, e), v4 = load4(v, e), g4 = load4(gate, e);
     const f32x4 rk4 = load4(r_k, pj), w4 = load4(ln_w, pj), b4 = load4(ln_b, pj);
-    const float mu = group16_sum((o4[0] + o4[1]) + (o4[2] + o4[3])) * (1.0f / kN);
-    f32x4 d;
-    float ss = 0.f, bon = 0.f;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        d[c] = o4[c] - mu;
-        ss += d[c] * d[c];
-        bon += r4[c] * k4[c] * rk4[c];
-    }
-    const float inv = 1.0f / sqrtf(group16_sum(ss) * (1.0f / kN) + eps);
-    const float bonus = group16_sum(bon);
-    f32x4 xo;
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-        xo[c] = (d[c] * inv * w4[c] + b4[c] + bonus * v4[c]) * g4[c];
-    store4(x, e, xo);
+    store4(x, e, tail_row4(o4, r4, k4, v4, g4, rk4, w4, b4, eps));
 }
 
 template <typename Tin, typename To, typename Tx>

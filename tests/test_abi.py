@@ -31,8 +31,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     assert names == sorted(["wkv7_forward", "wkv7_forward_varlen", "wkv7_step", "wkv7_step_tail",
-                            "wkv7_tmix_tail", "wkv7_state_commit", "wkv7_state_reset", "wkv7_backward",
-                            "wkv7_status_string", "wkv7_abi_version"])
+                            "wkv7_forward_tail", "wkv7_tmix_tail", "wkv7_state_commit", "wkv7_state_reset",
+                            "wkv7_backward", "wkv7_status_string", "wkv7_abi_version"])
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -192,6 +192,30 @@ def tmix(L, B=2, T=8, H=3, N=64, o="fake", x="fake", o_dt=F32, x_dt=F32, lnw="fa
     return L.wkv7_tmix_tail(pick(o, fake(6)), o_dt, fake(0), fake(2), fake(3), fake(11), BF16, fake(12),
                             pick(lnw, fake(13)), fake(14), ctypes.c_float(1e-5), pick(x, fake(8)), x_dt,
                             B, T, H, N, None)
+
+
+def fwd_tail(L, B=2, T=40, H=3, N=64, in_dt=BF16, gate="fake", x="fake", x_dt=F32, sout="fake"):
+    p = [fake(i) for i in range(6)]
+    pick = lambda v, d: d if v == "fake" else v
+    return L.wkv7_forward_tail(*p, in_dt, fake(7), pick(gate, fake(11)), fake(12), fake(13), fake(14),
+                               ctypes.c_float(1e-5), pick(x, fake(6)), x_dt, pick(sout, fake(8)), B, T, H, N, None)
+
+
+def test_forward_tail_validation(L):
+    # every refusal comes before any launch (fake pointers)
+    assert fwd_tail(L, N=32) == ERR_UNSUPPORTED
+    assert fwd_tail(L, x_dt=9) == ERR_UNSUPPORTED
+    assert fwd_tail(L, B=0) == ERR_SHAPE
+    assert fwd_tail(L, gate=None) == ERR_NULL
+    assert fwd_tail(L, x=None) == ERR_NULL
+    assert fwd_tail(L, sout=None) == ERR_NULL
+    assert fwd_tail(L, gate=fake(11, 8)) == ERR_ALIGN
+    assert fwd_tail(L, gate=fake(6, 64)) == ERR_ALIAS      # the gate inside x
+    assert fwd_tail(L, x=fake(0)) == ERR_ALIAS             # x on r
+    assert fwd_tail(L, sout=fake(14)) == ERR_ALIAS         # state_out on ln_b
+    assert fwd_tail(L, B=1, T=80, H=1048577) == ERR_SHAPE  # the chunked kernel's head limit
+    # fp32 inputs with an fp32 x take the tail pass too, and its row limit
+    assert fwd_tail(L, B=1, T=2 * 10**8 + 1, H=1, in_dt=F32) == ERR_SHAPE
 
 
 def test_step_tail_validation(L):

@@ -112,6 +112,20 @@ def test_tail_outputs(K, x_dtype):
     assert x2.full()
 
 
+@pytest.mark.parametrize("T", [6, 45])
+def test_forward_tail_outputs(K, T):
+    # the fused prefill tail: x and state_out only (T = 45: the chunked kernel's tail wave)
+    B, H = 2, 3
+    d = to_dev(synth.make_inputs(B, T, H, 64, seed=410 + T, dtype="bf16", state_std=0.1))
+    gen = torch.Generator(device="cuda").manual_seed(411)
+    gate = torch.sigmoid(torch.randn((B, T, H, 64), generator=gen, device="cuda")).to(torch.bfloat16)
+    prm = [0.1 * torch.randn((H, 64), generator=gen, device="cuda") + c for c in (0.0, 1.0, 0.0)]
+    x, s = Guarded((B, T, H, 64)), Guarded((B, H, 64, 64))
+    K.wkv7_forward_tail(*[d[n] for n in NAMES], gate, *prm, 64e-5, d["state_in"], x=x.t, state_out=s.t)
+    _check("forward with the fused tail", x, s)
+    assert x.full() and s.full()
+
+
 @pytest.mark.parametrize("H", [3, 129])
 def test_backward_outputs(K, H):
     # H = 3: two workgroups per head (a fill kernel, then atomic adds); H = 129: one

@@ -184,3 +184,88 @@ def test_verify_without_separate_state_out(K, oracle_mod):
     committed = K.wkv7_state_commit(sp2, [T] * B)
     torch.cuda.synchronize()
     assert torch.equal(committed, s1)
+
+
+# --- the parallel pass with the time-mix tail fused (wkv7_forward_tail) -------------
+
+def _forward_tail_case(K, oracle_mod, B, T, H, dtype, x_dtype, state_std, seed, w_zero=False):
+    inp = synth.make_inputs(B, T, H, 64, seed=seed, dtype=dtype, state_std=state_std)
+    if w_zero:  # a zero decay: its chunk takes the exact path
+        w = inp["w"].clone()
+        w[0, T // 2, 0, 3] = 0.0
+        inp["w"] = w
+    gate = _gate((B, T, H, 64), dtype, seed + 1)
+    r_k, ln_w, ln_b = _tail_params(H, seed + 2)
+    eps = 64e-5
+    d = to_dev(inp)
+    x, s = K.wkv7_forward_tail(*[d[n] for n in NAMES], gate.cuda(), r_k.cuda(), ln_w.cuda(), ln_b.cuda(), eps,
+                               d["state_in"], x_dtype=x_dtype)
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle_mod.forward(*[inp[n] for n in NAMES], inp["state_in"])
+    x_ref = oracle_mod.tmix_tail(o_ref, inp["r"], inp["k"], inp["v"], gate, r_k, ln_w, ln_b, eps)
+    return inp, d, gate, (r_k, ln_w, ln_b, eps), x, s, x_ref, s_ref
+
+
+@pytest.mark.parametrize("x_dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("B,T,H,state_std", [(2, 40, 3, 0.1), (1, 17, 2, 0.0), (2, 100, 64, 0.1), (4, 37, 64, 0.1),
+                                             (3, 8, 5, 0.1), (2, 9, 4, 0.1)])
+def test_forward_tail_vs_oracle(K, oracle_mod, B, T, H, state_std, x_dtype):
+    # bf16 inputs: one chunked kernel with the tail wave (T >= 9, every head count), or
+    # the step kernel's fused tail (T < 9)
+    *_, x, s, x_ref, s_ref = _forward_tail_case(K, oracle_mod, B, T, H, "bf16", x_dtype, state_std,
+                                                seed=4000 + B * T + H)
+    bf = x_dtype == torch.bfloat16
+    check(x, x_ref, 4e-3 if bf else TOL["bf16"], f"forward tail B={B} T={T} H={H} x", HEADS_SEQ,
+          elem_rel=2.0 ** -8 if bf else 0.0)
+    check(s, s_ref, TOL["bf16"], f"forward tail B={B} T={T} H={H} state", HEADS_STATE)
+
+
+@pytest.mark.parametrize("x_dtype", [torch.float32, torch.bfloat16])
+def test_forward_tail_f32_inputs(K, oracle_mod, x_dtype):
+    # fp32 inputs: the chunked kernel into x then the tail pass in place (fp32 x), or
+    # the step kernel's fused tail (bf16 x)
+    *_, x, s, x_ref, s_ref = _forward_tail_case(K, oracle_mod, 2, 41, 5, "f32", x_dtype, 0.1, seed=4100)
+    bf = x_dtype == torch.bfloat16
+    check(x, x_ref, 4e-3 if bf else TOL["f32"], "forward tail f32 x", HEADS_SEQ, elem_rel=2.0 ** -8 if bf else 0.0)
+    check(s, s_ref, TOL["f32"], "forward tail f32 state", HEADS_STATE)
+
+
+def test_forward_tail_exact_path_chunk(K, oracle_mod):
+    *_, x, s, x_ref, s_ref = _forward_tail_case(K, oracle_mod, 2, 70, 8, "bf16", torch.float32, 0.1, seed=4200,
+                                                w_zero=True)
+    check(x, x_ref, TOL["bf16"], "forward tail, zero decay x", HEADS_SEQ)
+    check(s, s_ref, TOL["bf16"], "forward tail, zero decay state", HEADS_STATE)
+
+
+@pytest.mark.parametrize("x_dtype", [torch.float32, torch.bfloat16])
+def test_forward_tail_equals_forward_then_tail_pass(K, x_dtype):
+    # The fused kernel forms each chunk's o exactly as the plain chunked kernel does and
+    # applies the same row arithmetic to it: bit for bit the two-launch result.
+    B, T, H = 2, 75, 64
+    inp = synth.make_inputs(B, T, H, 64, seed=4300, dtype="bf16", state_std=0.1)
+    d = to_dev(inp)
+    gate = _gate((B, T, H, 64), "bf16", 4301).cuda()
+    prm = [t.cuda() for t in _tail_params(H, 4302)]
+    x1, s1 = K.wkv7_forward_tail(*[d[n] for n in NAMES], gate, *prm, 64e-5, d["state_in"], x_dtype=x_dtype)
+    o, s2 = K.wkv7_forward(*[d[n] for n in NAMES], d["state_in"])
+    x2 = K.wkv7_tmix_tail(o, d["r"], d["k"], d["v"], gate, *prm, 64e-5, x_dtype=x_dtype)
+    torch.cuda.synchronize()
+    assert torch.equal(s1, s2)
+    assert torch.equal(x1, x2), f"max |diff| {(x1.float() - x2.float()).abs().max().item():.3e}"
+
+
+def test_forward_tail_workload3_all_heads(K, workload3_oracle, oracle_mod):
+    # the 7.2B-shaped prefill with the tail fused, every head over the full sequence
+    inp, o_ref, s_ref = workload3_oracle
+    B, T, H = inp["r"].shape[:3]
+    gate = _gate((B, T, H, 64), "bf16", 4400)
+    r_k, ln_w, ln_b = _tail_params(H, 4401)
+    d = to_dev(inp)
+    x, s = K.wkv7_forward_tail(*[d[n] for n in NAMES], gate.cuda(), r_k.cuda(), ln_w.cuda(), ln_b.cuda(), 64e-5,
+                               d["state_in"])
+    torch.cuda.synchronize()
+    x, s = x.cpu(), s.cpu()
+    del d
+    x_ref = oracle_mod.tmix_tail(o_ref, inp["r"], inp["k"], inp["v"], gate, r_k, ln_w, ln_b, 64e-5)
+    check(x, x_ref, TOL["bf16"], "workload 3 fused tail x", HEADS_SEQ)
+    check(s, s_ref, TOL["bf16"], "workload 3 fused tail state", HEADS_STATE)
