@@ -126,6 +126,21 @@ int main()
                           ffake(14), 1e-3f, fake(15), WKV7_F32, INT_MAX, INT_MAX, INT_MAX, 64,
                           nullptr) == WKV7_ERR_SHAPE);
 
+    // ---- the prefill with the fused tail: which kernels run
+    auto ftail = [&](int in_dt, int x_dt, int T) {
+        reset_log();
+        return wkv7_forward_tail(fake(0), fake(1), fake(2), fake(3), fake(4), fake(5), in_dt, ffake(7), fake(11),
+                                 ffake(12), ffake(13), ffake(14), 1e-3f, fake(6), x_dt, ffake(8), 4, T, 64, 64,
+                                 nullptr);
+    };
+    EXPECT(ftail(WKV7_BF16, WKV7_F32, 100) == WKV7_OK && g_log.calls == 1 && !std::strcmp(g_log.kind, "chunk") &&
+           g_log.seq.gate == fake(11));
+    EXPECT(ftail(WKV7_BF16, WKV7_BF16, 8) == WKV7_OK && !std::strcmp(g_log.kind, "step") && g_log.seq.gate);
+    EXPECT(ftail(WKV7_F32, WKV7_F32, 100) == WKV7_OK && g_log.calls == 2 && !std::strcmp(g_log.kind, "tail"));
+    EXPECT(ftail(WKV7_F32, WKV7_BF16, 100) == WKV7_OK && g_log.calls == 1 && !std::strcmp(g_log.kind, "step") &&
+           g_log.seq.gate == fake(11));
+    EXPECT(ftail(WKV7_BF16, 3, 100) == WKV7_ERR_UNSUPPORTED && g_log.calls == 0);
+
     // ---- backward
     auto bwd = [&](void *dso, void *dsi, float *g0) {
         reset_log();
