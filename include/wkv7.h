@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define WKV7_ABI_VERSION 5
+#define WKV7_ABI_VERSION 6
 
 /* Element types of r, w, k, v, a, b (in_dtype) and of o (o_dtype). */
 enum wkv7_dtype {
@@ -287,6 +287,46 @@ int wkv7_backward(const void *r, const void *w, const void *k, const void *v,
                   const float *state_pos, const float *d_o, const float *d_state_out,
                   float *dr, float *dw, float *dk, float *dv, float *da, float *db,
                   float *d_state_in, int B, int T, int H, int N, void *stream);
+
+/*
+ * wkv7_forward_ckpt -- the forward pass of training: wkv7_forward (fp32 o) that
+ * also keeps the state entering every chunk of 16 tokens, the checkpoints from
+ * which wkv7_backward_ckpt rebuilds the rest.  The SwiftRWKV Inference guide
+ * (its `.rwkvq` backend section) describes this trainable kernel: it chunks, and
+ * its backward pass rebuilds the state chunk by chunk.
+ *
+ *   ckpt : [B, ceil(T/16), H, N, N] fp32; ckpt[b, c, h] = the state of head h of
+ *          row b before token 16 c (state_in, or zeros, for c = 0).
+ * Everything else as wkv7_forward with o_dtype = WKV7_F32.  ckpt may be NULL
+ * only when T = 0, and overlaps no other buffer.  For 1 <= T <= 8 (one chunk)
+ * the call enqueues a copy of state_in (or a fill of zeros) into ckpt, then the
+ * step kernel; from T = 9 on, the chunked kernel writes the checkpoints itself.
+ * The checkpoints carry the chunked kernel's fp32 state: within about 1e-6
+ * (relative L2) of the states of the definition.
+ */
+int wkv7_forward_ckpt(const void *r, const void *w, const void *k, const void *v,
+                      const void *a, const void *b, int in_dtype, const float *state_in,
+                      float *o, float *state_out, float *ckpt, int B, int T, int H, int N,
+                      void *stream);
+
+/*
+ * wkv7_backward_ckpt -- wkv7_backward from the checkpoints of wkv7_forward_ckpt
+ * instead of per-position states: per chunk, last first, the pass rebuilds the
+ * chunk's 16 states from its checkpoint with the recurrence (in registers) and
+ * runs the adjoint on them.  It reads 1/16 of the state bytes that
+ * wkv7_backward reads, and no state_in (ckpt[:, 0] is the input state).
+ *
+ *   ckpt : [B, ceil(T/16), H, N, N] fp32, as wkv7_forward_ckpt wrote it from the
+ *          same inputs and state_in.
+ * Everything else (d_o, d_state_out, the gradients, NULL rules, aliasing, the
+ * limit B * H <= WKV7_MAX_HEADS_STEP, and the fill plus atomic adds when
+ * B * H <= 128) as wkv7_backward.
+ */
+int wkv7_backward_ckpt(const void *r, const void *w, const void *k, const void *v,
+                       const void *a, const void *b, int in_dtype, const float *ckpt,
+                       const float *d_o, const float *d_state_out, float *dr, float *dw,
+                       float *dk, float *dv, float *da, float *db, float *d_state_in,
+                       int B, int T, int H, int N, void *stream);
 
 /* A static, human-readable name for a status code (never NULL). */
 const char *wkv7_status_string(int status);

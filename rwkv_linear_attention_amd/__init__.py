@@ -89,6 +89,10 @@ def lib():
         L.wkv7_state_reset.argtypes = [vp, ci, ci, ci, vp, vp]
         L.wkv7_backward.argtypes = [vp] * 6 + [ci] + [vp] * 11 + [ci, ci, ci, ci, vp]
         L.wkv7_backward.restype = ci
+        L.wkv7_forward_ckpt.argtypes = [vp] * 6 + [ci, vp, vp, vp, vp, ci, ci, ci, ci, vp]
+        L.wkv7_forward_ckpt.restype = ci
+        L.wkv7_backward_ckpt.argtypes = [vp] * 6 + [ci] + [vp] * 10 + [ci, ci, ci, ci, vp]
+        L.wkv7_backward_ckpt.restype = ci
         L.wkv7_state_reset.restype = ci
         L.wkv7_status_string.argtypes = [ci]
         L.wkv7_status_string.restype = ctypes.c_char_p
@@ -353,6 +357,57 @@ def wkv7_backward(r, w, k, v, a, b, state_in, state_pos, d_o, d_state_out=None, 
                                _ptr(state_pos), _ptr(d_o), _ptr(d_state_out),
                                *[_ptr(grads[n]) for n in names], _ptr(grads["d_state_in"]),
                                B, T, H, N, _stream(dev)))
+    return grads
+
+
+def wkv7_forward_ckpt(r, w, k, v, a, b, state_in=None, *, o=None, state_out=None, ckpt=None):
+    """Forward pass for training: (o, state_out, ckpt), o in fp32.
+
+    ckpt: [B, ceil(T/16), H, N, N] fp32, the state before each chunk of 16 tokens
+    (state_in, or zeros, first): what wkv7_backward_ckpt rebuilds the other states from.
+    """
+    B, T, H, N = _check_inputs(r, w, k, v, a, b)
+    dev = r.device
+    f32 = (torch.float32,)
+    state_in = _state_arg(state_in, B, H, N, dev, "state_in")
+    if state_out is None:
+        state_out = torch.empty((B, H, N, N), dtype=torch.float32, device=dev)
+    _state_arg(state_out, B, H, N, dev, "state_out")
+    if o is None:
+        o = torch.empty((B, T, H, N), dtype=torch.float32, device=dev)
+    _out_arg(o, (B, T, H, N), dev, "o", f32)
+    nck = (T + 15) // 16
+    if ckpt is None:
+        ckpt = torch.empty((B, nck, H, N, N), dtype=torch.float32, device=dev)
+    _out_arg(ckpt, (B, nck, H, N, N), dev, "ckpt", f32)
+    _check(lib().wkv7_forward_ckpt(*[_ptr(x) for x in (r, w, k, v, a, b)], _dt(r), _ptr(state_in), _ptr(o),
+                                   _ptr(state_out), _ptr(ckpt) if nck else None, B, T, H, N, _stream(dev)))
+    return o, state_out, ckpt
+
+
+def wkv7_backward_ckpt(r, w, k, v, a, b, ckpt, d_o, d_state_out=None, *, grads=None):
+    """Gradients of the recurrence from the checkpoints of wkv7_forward_ckpt.
+
+    Returns the same dict as wkv7_backward (dr, dw, dk, dv, da, db, d_state_in).
+    """
+    B, T, H, N = _check_inputs(r, w, k, v, a, b)
+    dev = r.device
+    f32 = (torch.float32,)
+    d_state_out = _state_arg(d_state_out, B, H, N, dev, "d_state_out")
+    nck = (T + 15) // 16
+    _out_arg(ckpt, (B, nck, H, N, N), dev, "ckpt", f32)
+    _out_arg(d_o, (B, T, H, N), dev, "d_o", f32)
+    names = ("dr", "dw", "dk", "dv", "da", "db")
+    if grads is None:
+        grads = {n: torch.empty((B, T, H, N), dtype=torch.float32, device=dev) for n in names}
+        grads["d_state_in"] = torch.empty((B, H, N, N), dtype=torch.float32, device=dev)
+    for n in names:
+        _out_arg(grads[n], (B, T, H, N), dev, n, f32)
+    _out_arg(grads["d_state_in"], (B, H, N, N), dev, "d_state_in", f32)
+    _check(lib().wkv7_backward_ckpt(*[_ptr(x) for x in (r, w, k, v, a, b)], _dt(r),
+                                    _ptr(ckpt) if nck else None, _ptr(d_o), _ptr(d_state_out),
+                                    *[_ptr(grads[n]) for n in names], _ptr(grads["d_state_in"]),
+                                    B, T, H, N, _stream(dev)))
     return grads
 
 

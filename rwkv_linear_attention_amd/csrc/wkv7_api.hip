@@ -131,6 +131,7 @@ SeqArgs make_args(const void *r, const void *w, const void *k, const void *v, co
     SeqArgs s;
     s.r = r; s.w = w; s.k = k; s.v = v; s.a = a; s.b = b;
     s.state_in = state_in; s.o = o; s.state_out = state_out; s.state_pos = state_pos;
+    s.ckpt = nullptr;
     s.lengths = nullptr;
     s.gate = nullptr;
     s.r_k = s.ln_w = s.ln_b = nullptr;
@@ -170,6 +171,89 @@ int empty_sequence(const float *state_in, float *state_out, int B, int H, hipStr
         return WKV7_OK;
     const long long n = static_cast<long long>(B) * H * kN * kN;
     return wkv7::launch_state_copy(state_in, state_out, n, stream) == hipSuccess ? WKV7_OK : WKV7_ERR_HIP;
+}
+
+// Bytes of the chunk checkpoints [B, ceil(T/16), H, N, N] fp32 (within int64 once
+// shape_ok has accepted B, T, H).
+int64_t ckpt_bytes(int B, int T, int H)
+{
+    return static_cast<int64_t>(B) * ((T + 15) / 16) * H * kN * kN * 4;
+}
+
+// The backward passes' arguments: the per-position states (state_pos, with state_in)
+// or the chunk checkpoints (ckpt: states is ckpt).  Fills *p when they are valid.
+int check_backward(const void *r, const void *w, const void *k, const void *v, const void *a, const void *b,
+                   int in_dtype, const float *state_in, const float *states, bool is_ckpt, const float *d_o,
+                   const float *d_state_out, float *dr, float *dw, float *dk, float *dv, float *da, float *db,
+                   float *d_state_in, int B, int T, int H, int N, wkv7::BwdArgs *p)
+{
+    int64_t tok = 0;
+    if (N != kN)
+        return WKV7_ERR_UNSUPPORTED;
+    if (in_dtype != WKV7_F32 && in_dtype != WKV7_BF16)
+        return WKV7_ERR_UNSUPPORTED;
+    if (!shape_ok(B, T, H, &tok, kMaxHeadsStep))
+        return WKV7_ERR_SHAPE;
+    if (!d_state_in)
+        return WKV7_ERR_NULL;
+    const void *ins[] = {r, w, k, v, a, b, states, d_o};
+    float *const grads[] = {dr, dw, dk, dv, da, db};
+    if (T > 0) {
+        for (const void *ptr : ins)
+            if (!ptr)
+                return WKV7_ERR_NULL;
+        for (const float *ptr : grads)
+            if (!ptr)
+                return WKV7_ERR_NULL;
+    }
+    const void *all[] = {r, w, k, v, a, b, state_in, states, d_o, d_state_out,
+                         dr, dw, dk, dv, da, db, d_state_in};
+    for (const void *ptr : all)
+        if (ptr && misaligned(ptr))
+            return WKV7_ERR_ALIGN;
+    // every output overlaps nothing else (d_state_in may be d_state_out itself)
+    const int64_t ein = in_dtype == WKV7_BF16 ? 2 : 4;
+    const int64_t vec = tok * kN, st_bytes = static_cast<int64_t>(B) * H * kN * kN * 4;
+    Range in_r[11];
+    int n_in = 0;
+    if (T > 0) {
+        for (int q = 0; q < 6; ++q)
+            in_r[n_in++] = range_of(ins[q], vec * ein);
+        in_r[n_in++] = range_of(states, is_ckpt ? ckpt_bytes(B, T, H) : vec * kN * 4);
+        in_r[n_in++] = range_of(d_o, vec * 4);
+    }
+    if (state_in)
+        in_r[n_in++] = range_of(state_in, st_bytes);
+    // d_state_out is read by the pass: no gradient of an input may overlap it (d_state_in
+    // may be d_state_out itself, checked below)
+    if (d_state_out && d_state_out != d_state_in)
+        in_r[n_in++] = range_of(d_state_out, st_bytes);
+    const Range r_dsi = range_of(d_state_in, st_bytes);
+    Range out_r[7];
+    int n_out = 0;
+    if (T > 0)
+        for (const float *ptr : grads)
+            out_r[n_out++] = range_of(ptr, vec * 4);
+    out_r[n_out++] = r_dsi;
+    for (int x = 0; x < n_out; ++x) {
+        for (int y = 0; y < n_in; ++y)
+            if (overlap(out_r[x], in_r[y]))
+                return WKV7_ERR_ALIAS;
+        for (int y = x + 1; y < n_out; ++y)
+            if (overlap(out_r[x], out_r[y]))
+                return WKV7_ERR_ALIAS;
+    }
+    if (d_state_out && d_state_out != d_state_in && overlap(r_dsi, range_of(d_state_out, st_bytes)))
+        return WKV7_ERR_ALIAS;
+    p->r = r; p->w = w; p->k = k; p->v = v; p->a = a; p->b = b;
+    p->state_in = state_in;
+    p->state_pos = is_ckpt ? nullptr : states;
+    p->ckpt = is_ckpt ? states : nullptr;
+    p->d_o = d_o; p->d_state_out = d_state_out;
+    p->dr = dr; p->dw = dw; p->dk = dk; p->dv = dv; p->da = da; p->db = db; p->d_state_in = d_state_in;
+    p->B = B; p->T = T; p->H = H;
+    p->in_bf16 = in_dtype == WKV7_BF16;
+    return WKV7_OK;
 }
 
 }  // namespace
@@ -417,71 +501,66 @@ int wkv7_backward(const void *r, const void *w, const void *k, const void *v, co
                   const float *d_state_out, float *dr, float *dw, float *dk, float *dv, float *da, float *db,
                   float *d_state_in, int B, int T, int H, int N, void *stream)
 {
-    int64_t tok = 0;
-    if (N != kN)
-        return WKV7_ERR_UNSUPPORTED;
-    if (in_dtype != WKV7_F32 && in_dtype != WKV7_BF16)
-        return WKV7_ERR_UNSUPPORTED;
-    if (!shape_ok(B, T, H, &tok, kMaxHeadsStep))
-        return WKV7_ERR_SHAPE;
-    if (!d_state_in)
-        return WKV7_ERR_NULL;
-    const void *ins[] = {r, w, k, v, a, b, state_pos, d_o};
-    float *const grads[] = {dr, dw, dk, dv, da, db};
-    if (T > 0) {
-        for (const void *ptr : ins)
-            if (!ptr)
-                return WKV7_ERR_NULL;
-        for (const float *ptr : grads)
-            if (!ptr)
-                return WKV7_ERR_NULL;
-    }
-    const void *all[] = {r, w, k, v, a, b, state_in, state_pos, d_o, d_state_out,
-                         dr, dw, dk, dv, da, db, d_state_in};
-    for (const void *ptr : all)
-        if (ptr && misaligned(ptr))
-            return WKV7_ERR_ALIGN;
-    // every output overlaps nothing else (d_state_in may be d_state_out itself)
-    const int64_t ein = in_dtype == WKV7_BF16 ? 2 : 4;
-    const int64_t vec = tok * kN, st_bytes = static_cast<int64_t>(B) * H * kN * kN * 4;
-    Range in_r[11];
-    int n_in = 0;
-    if (T > 0) {
-        for (int q = 0; q < 6; ++q)
-            in_r[n_in++] = range_of(ins[q], vec * ein);
-        in_r[n_in++] = range_of(state_pos, vec * kN * 4);
-        in_r[n_in++] = range_of(d_o, vec * 4);
-    }
-    if (state_in)
-        in_r[n_in++] = range_of(state_in, st_bytes);
-    // d_state_out is read by the pass: no gradient of an input may overlap it (d_state_in
-    // may be d_state_out itself, checked below)
-    if (d_state_out && d_state_out != d_state_in)
-        in_r[n_in++] = range_of(d_state_out, st_bytes);
-    const Range r_dsi = range_of(d_state_in, st_bytes);
-    Range out_r[7];
-    int n_out = 0;
-    if (T > 0)
-        for (const float *ptr : grads)
-            out_r[n_out++] = range_of(ptr, vec * 4);
-    out_r[n_out++] = r_dsi;
-    for (int x = 0; x < n_out; ++x) {
-        for (int y = 0; y < n_in; ++y)
-            if (overlap(out_r[x], in_r[y]))
-                return WKV7_ERR_ALIAS;
-        for (int y = x + 1; y < n_out; ++y)
-            if (overlap(out_r[x], out_r[y]))
-                return WKV7_ERR_ALIAS;
-    }
-    if (d_state_out && d_state_out != d_state_in && overlap(r_dsi, range_of(d_state_out, st_bytes)))
-        return WKV7_ERR_ALIAS;
     wkv7::BwdArgs p{};
-    p.r = r; p.w = w; p.k = k; p.v = v; p.a = a; p.b = b;
-    p.state_in = state_in; p.state_pos = state_pos; p.d_o = d_o; p.d_state_out = d_state_out;
-    p.dr = dr; p.dw = dw; p.dk = dk; p.dv = dv; p.da = da; p.db = db; p.d_state_in = d_state_in;
-    p.B = B; p.T = T; p.H = H;
-    p.in_bf16 = in_dtype == WKV7_BF16;
+    const int st = check_backward(r, w, k, v, a, b, in_dtype, state_in, state_pos, false, d_o, d_state_out, dr, dw,
+                                  dk, dv, da, db, d_state_in, B, T, H, N, &p);
+    if (st != WKV7_OK)
+        return st;
     return wkv7::launch_backward(p, static_cast<hipStream_t>(stream)) == hipSuccess ? WKV7_OK : WKV7_ERR_HIP;
+}
+
+int wkv7_forward_ckpt(const void *r, const void *w, const void *k, const void *v, const void *a, const void *b,
+                      int in_dtype, const float *state_in, float *o, float *state_out, float *ckpt, int B, int T,
+                      int H, int N, void *stream)
+{
+    int st = check_seq(r, w, k, v, a, b, in_dtype, state_in, o, WKV7_F32, state_out, nullptr, B, T, H, N,
+                       false, false);
+    if (st != WKV7_OK)
+        return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (T == 0)
+        return empty_sequence(state_in, state_out, B, H, s);
+    if (!ckpt)
+        return WKV7_ERR_NULL;
+    if (misaligned(ckpt))
+        return WKV7_ERR_ALIGN;
+    // the checkpoints overlap no input and no other output
+    const int64_t ein = in_dtype == WKV7_BF16 ? 2 : 4;
+    const int64_t vec = static_cast<int64_t>(B) * T * H * kN, st_bytes = static_cast<int64_t>(B) * H * kN * kN * 4;
+    const Range rc = range_of(ckpt, ckpt_bytes(B, T, H));
+    const void *seq[] = {r, w, k, v, a, b};
+    for (const void *ptr : seq)
+        if (overlap(rc, range_of(ptr, vec * ein)))
+            return WKV7_ERR_ALIAS;
+    if (overlap(rc, range_of(o, vec * 4)) || overlap(rc, range_of(state_out, st_bytes)) ||
+        (state_in && overlap(rc, range_of(state_in, st_bytes))))
+        return WKV7_ERR_ALIAS;
+    SeqArgs args = make_args(r, w, k, v, a, b, in_dtype, state_in, o, WKV7_F32, state_out, nullptr, B, T, H);
+    if (T >= kChunkMinT) {
+        args.ckpt = ckpt;
+        return wkv7::launch_chunk(args, s) == hipSuccess ? WKV7_OK : WKV7_ERR_HIP;
+    }
+    // one chunk: its checkpoint is the input state, taken before the pass (which may
+    // update that state in place)
+    const hipError_t e0 = state_in ? wkv7::launch_state_copy(state_in, ckpt, st_bytes / 4, s)
+                                   : wkv7::launch_state_reset(ckpt, B, H, nullptr, s);
+    if (e0 != hipSuccess)
+        return WKV7_ERR_HIP;
+    return wkv7::launch_step(args, s) == hipSuccess ? WKV7_OK : WKV7_ERR_HIP;
+}
+
+int wkv7_backward_ckpt(const void *r, const void *w, const void *k, const void *v, const void *a,
+                       const void *b, int in_dtype, const float *ckpt, const float *d_o, const float *d_state_out,
+                       float *dr, float *dw, float *dk, float *dv, float *da, float *db, float *d_state_in, int B,
+                       int T, int H, int N, void *stream)
+{
+    wkv7::BwdArgs p{};
+    const int st = check_backward(r, w, k, v, a, b, in_dtype, nullptr, ckpt, true, d_o, d_state_out, dr, dw, dk,
+                                  dv, da, db, d_state_in, B, T, H, N, &p);
+    if (st != WKV7_OK)
+        return st;
+    return wkv7::launch_backward_ckpt(p, static_cast<hipStream_t>(stream)) == hipSuccess ? WKV7_OK
+                                                                                          : WKV7_ERR_HIP;
 }
 
 const char *wkv7_status_string(int status)

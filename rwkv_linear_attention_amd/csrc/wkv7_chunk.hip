@@ -256,8 +256,15 @@ struct OTiles {
 };
 template <>
 struct OTiles<0> {};
+// The checkpoint variant's d_15 of each chunk in the operand ring (slot c % NS).
+template <int NG>
+struct GRing {
+    alignas(16) float g[NG][kN];
+};
+template <>
+struct GRing<0> {};
 
-template <typename Tin, int NP, int NPV, int NS, int NT, int NOT>
+template <typename Tin, int NP, int NPV, int NS, int NT, int NOT, int NG>
 struct Smem {
     Slot<NP, NPV> slot[NS];
     alignas(16) Tin wbuf[CH][kN];  // w rows of one chunk, transposed through here by the decay wave
@@ -267,6 +274,7 @@ struct Smem {
     alignas(16) float mt[NT][CH][MTP];  // M_ab of one chunk per inverse wave, row-major
     int exact[8];  // chunk c % 8 takes the exact path (its decay table is all ones)
     OTiles<NOT> ot;
+    GRing<NG> gr;
 };
 
 // Decay factors of one key channel over a chunk: d[tau+1] = P_tau / P_7 and
@@ -299,14 +307,21 @@ __device__ __forceinline__ void decay_factors(const float (&w)[CH], float (&d)[C
     }
 }
 
-// With TAIL (bf16 inputs, J = 1) the time-mix tail is fused: the consumers leave o in
+// MODE_TAIL (bf16 inputs, J = 1): the time-mix tail is fused.  The consumers leave o in
 // LDS, and NTAIL more waves turn each chunk's rows into x (written through p.o, of
 // type Tout) one iteration later.
+// MODE_CKPT: the consumers also write the state entering every chunk to p.state_pos
+// as [B, ceil(T / 16), H, N, N] (chunk 0: the input state), the checkpoints from
+// which a backward pass rebuilds each chunk's states.
+enum { MODE_PLAIN = 0, MODE_TAIL = 1, MODE_CKPT = 2 };
 constexpr int NTAIL = 2;
-template <typename Tin, typename Tout, int J, bool HAS_STATE_IN, bool TAIL>
-__global__ __launch_bounds__((kN / J / 16 + nprod<Tin>() + (TAIL ? NTAIL : 0)) * 64) void wkv7_chunk_kernel(
+template <int MODE>
+constexpr int nextra() { return MODE == MODE_TAIL ? NTAIL : 0; }
+template <typename Tin, typename Tout, int J, bool HAS_STATE_IN, int MODE>
+__global__ __launch_bounds__((kN / J / 16 + nprod<Tin>() + nextra<MODE>()) * 64) void wkv7_chunk_kernel(
     SeqArgs p, int per_xcd, int nblocks)
 {
+    constexpr bool TAIL = MODE == MODE_TAIL, CKPT = MODE == MODE_CKPT;
     constexpr int NC = kN / J;            // value columns of this workgroup
     constexpr int NSW = NC / 16;          // consumer waves (16 state columns each)
     constexpr bool F32IN = std::is_same<Tin, float>::value;
@@ -319,7 +334,7 @@ __global__ __launch_bounds__((kN / J / 16 + nprod<Tin>() + (TAIL ? NTAIL : 0)) *
     constexpr int NS = DEEP ? 4 : 3;
     using SlotT = Slot<NP, NPV>;
     static_assert(!TAIL || (J == 1 && !F32IN), "the fused tail runs with bf16 inputs and whole heads");
-    __shared__ Smem<Tin, NP, NPV, NS, DEEP ? 2 : 1, TAIL ? 2 : 0> sm;
+    __shared__ Smem<Tin, NP, NPV, NS, DEEP ? 2 : 1, TAIL ? 2 : 0, CKPT ? NS : 0> sm;
 
     // Workgroup -> (batch*head, column block).  Workgroups are dealt to the
     // XCDs round-robin; the J column blocks of one head stay on one XCD so the
@@ -383,6 +398,24 @@ __global__ __launch_bounds__((kN / J / 16 + nprod<Tin>() + (TAIL ? NTAIL : 0)) *
         // compiler waits for these loads inside the loop, where the counter also holds the
         // previous chunk's output stores: every chunk would wait for those to drain.
         __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+        // CKPT: [B, NCK, H, N, N] checkpoints; this lane's 16 elements of a head's state sit
+        // at offsets (16 pt + 4 q + e) N + jw + m from the head's base
+        const int nck = (T + CH - 1) / CH;
+        auto ckpt_store = [&](int c, const f32x4 (&x)[4]) {
+            float *const cb = p.ckpt + ((static_cast<size_t>(bb) * nck + c) * H + hh) * (kN * kN) + jw + m;
+#pragma unroll
+            for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    cb[(16 * pt + 4 * q + e) * kN] = x[pt][e];
+        };
+        if constexpr (CKPT) {  // chunk 0 starts from the input state
+            f32x4 x0[4];
+#pragma unroll
+            for (int pt = 0; pt < 4; ++pt)
+                x0[pt] = f32x4{Sx[pt][0], Sx[pt][1], Sx[pt][2], Sx[pt][3]};
+            ckpt_store(0, x0);
+        }
         // transpose-load address pieces of this lane: row 4 q + m/4, column group m%4
         const int trow = 4 * q + (m >> 2), tcol = 4 * (m & 3);
         const int mcol_t = mcol(trow, m & 3);  // the same unit in a swizzled matrix tile
@@ -645,6 +678,16 @@ __global__ __launch_bounds__((kN / J / 16 + nprod<Tin>() + (TAIL ? NTAIL : 0)) *
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
                         Sx[pt][e] = acc[pt][e] * fv[pt][e];
+                if constexpr (CKPT) {
+                    // the state entering chunk i+1, unscaled: acc times this chunk's d_15
+                    if (i + 1 < nchunks) {
+                        f32x4 xs[4];
+#pragma unroll
+                        for (int pt = 0; pt < 4; ++pt)
+                            xs[pt] = acc[pt] * *reinterpret_cast<const f32x4 *>(&sm.gr.g[i % NS][16 * pt + 4 * q]);
+                        ckpt_store(i + 1, xs);
+                    }
+                }
                 exact_next = __builtin_amdgcn_readfirstlane(flag_next);
             }
             if constexpr (TAIL)
@@ -833,15 +876,21 @@ __global__ __launch_bounds__((kN / J / 16 + nprod<Tin>() + (TAIL ? NTAIL : 0)) *
             sm.p7[i] = idk[0];
         else
             sm.slot[(c - 1) % NS].f[i] = sm.d15[(c - 1) & 1][i] * idk[0];
+        if constexpr (CKPT)
+            if (c > 0)
+                sm.gr.g[(c - 1) % NS][i] = sm.d15[(c - 1) & 1][i];
         sm.d15[c & 1][i] = dk[CH];
         if (i == 0)
             sm.exact[c & 7] = dexact;
     };
     auto decay2 = [&](int c) {
-        if (c == nchunks)
+        if (c == nchunks) {
             sm.slot[(c - 1) % NS].f[lane] = sm.d15[(c - 1) & 1][lane];
-        else if (c >= 0 && c < nchunks)
+            if constexpr (CKPT)
+                sm.gr.g[(c - 1) % NS][lane] = sm.d15[(c - 1) & 1][lane];
+        } else if (c >= 0 && c < nchunks) {
             decay2_body(c);
+        }
     };
 
     // ---- scale waves: X' = x * factor, elementwise, lane = (token, slot group):
@@ -1291,18 +1340,18 @@ __global__ __launch_bounds__((kN / J / 16 + nprod<Tin>() + (TAIL ? NTAIL : 0)) *
     }
 }
 
-template <typename Tin, typename Tout, int J, bool TAIL = false>
+template <typename Tin, typename Tout, int J, int MODE = MODE_PLAIN>
 hipError_t launch_j(const SeqArgs &p, hipStream_t stream)
 {
     const int nblocks = p.B * p.H * J;
     int per_xcd = (nblocks + 7) / 8;
     per_xcd = (per_xcd + J - 1) / J * J;  // a head's column blocks never straddle two XCDs
-    const dim3 grid(8 * per_xcd), block((kN / J / 16 + nprod<Tin>() + (TAIL ? NTAIL : 0)) * 64);
+    const dim3 grid(8 * per_xcd), block((kN / J / 16 + nprod<Tin>() + nextra<MODE>()) * 64);
     if (p.state_in)
-        hipLaunchKernelGGL((wkv7_chunk_kernel<Tin, Tout, J, true, TAIL>), grid, block, 0, stream, p, per_xcd,
+        hipLaunchKernelGGL((wkv7_chunk_kernel<Tin, Tout, J, true, MODE>), grid, block, 0, stream, p, per_xcd,
                            nblocks);
     else
-        hipLaunchKernelGGL((wkv7_chunk_kernel<Tin, Tout, J, false, TAIL>), grid, block, 0, stream, p, per_xcd,
+        hipLaunchKernelGGL((wkv7_chunk_kernel<Tin, Tout, J, false, MODE>), grid, block, 0, stream, p, per_xcd,
                            nblocks);
     return hipGetLastError();
 }
@@ -1313,13 +1362,24 @@ hipError_t launch_typed(const SeqArgs &p, hipStream_t stream)
     // The fused tail needs every column of a token in one workgroup: whole heads.
     if (p.gate) {
         if constexpr (std::is_same<Tin, uint16_t>::value)
-            return launch_j<Tin, Tout, 1, true>(p, stream);
+            return launch_j<Tin, Tout, 1, MODE_TAIL>(p, stream);
         else
             return hipErrorInvalidValue;  // the C ABI routes fp32 inputs elsewhere
     }
     // One workgroup fills a compute unit's LDS; split heads into column blocks
     // only while the grid still fits in one pass over the 256 compute units.
     const long long heads = static_cast<long long>(p.B) * p.H;
+    if (p.ckpt) {  // checkpoints (fp32 o only)
+        if constexpr (std::is_same<Tout, float>::value) {
+            if (heads * 4 <= 256)
+                return launch_j<Tin, Tout, 4, MODE_CKPT>(p, stream);
+            if (heads * 2 <= 256)
+                return launch_j<Tin, Tout, 2, MODE_CKPT>(p, stream);
+            return launch_j<Tin, Tout, 1, MODE_CKPT>(p, stream);
+        } else {
+            return hipErrorInvalidValue;  // the C ABI refuses a bf16 o with checkpoints
+        }
+    }
     if (heads * 4 <= 256)
         return launch_j<Tin, Tout, 4>(p, stream);
     if (heads * 2 <= 256)

@@ -12,6 +12,7 @@ struct SeqArgs {
     void *o;                            // [B,T,H,64], o_dtype
     float *state_out;                   // [B,H,64,64]
     float *state_pos;                   // [B,T,H,64,64] or nullptr
+    float *ckpt;                        // [B,ceil(T/16),H,64,64]: state entering each 16-token chunk, or nullptr
     const int *lengths;                 // [B] tokens of each row (clamped to [0, T]), or nullptr: all T
     int B, T, H;
     int in_bf16, o_bf16;                // dtype flags
@@ -35,7 +36,8 @@ struct TailArgs {
 struct BwdArgs {
     const void *r, *w, *k, *v, *a, *b;  // [B,T,H,64], in_dtype
     const float *state_in;              // [B,H,64,64] or nullptr (zeros)
-    const float *state_pos;             // [B,T,H,64,64]: the state after each token
+    const float *state_pos;             // [B,T,H,64,64]: the state after each token (wkv7_backward)
+    const float *ckpt;                  // [B,ceil(T/16),H,64,64]: the state entering each chunk (the rebuild)
     const float *d_o;                   // [B,T,H,64]: gradient of o
     const float *d_state_out;           // [B,H,64,64] or nullptr (zeros)
     float *dr, *dw, *dk, *dv, *da, *db; // [B,T,H,64]
@@ -51,6 +53,7 @@ hipError_t launch_state_reset(float *state, int B, int H, const unsigned char *r
                               hipStream_t stream);
 hipError_t launch_tail(const TailArgs &a, hipStream_t stream);
 hipError_t launch_backward(const BwdArgs &a, hipStream_t stream);
+hipError_t launch_backward_ckpt(const BwdArgs &a, hipStream_t stream);
 hipError_t launch_state_commit(const float *state_pos, const int *accepted, const float *state_in,
                                float *state_out, int B, int T, int H, hipStream_t stream);
 

@@ -153,6 +153,47 @@ int main()
     EXPECT(bwd(fake(17), fake(18), ffake(17, 1024)) == WKV7_ERR_ALIAS);     // a gradient inside d_state_out
     EXPECT(bwd(fake(17), fake(17, 256), ffake(11)) == WKV7_ERR_ALIAS);
     EXPECT(bwd(nullptr, nullptr, ffake(11)) == WKV7_ERR_NULL);
+    EXPECT(bwd(fake(17), fake(18), ffake(11)) == WKV7_OK && g_log.bwd.state_pos == ffake(9) && !g_log.bwd.ckpt);
+
+    // ---- the training pair: chunk checkpoints
+    auto fck = [&](int T, void *sin, void *ck) {
+        reset_log();
+        return wkv7_forward_ckpt(fake(0), fake(1), fake(2), fake(3), fake(4), fake(5), WKV7_BF16,
+                                 static_cast<float *>(sin), ffake(6), ffake(8), static_cast<float *>(ck), 2, T, 3,
+                                 64, nullptr);
+    };
+    EXPECT(fck(40, fake(7), fake(9)) == WKV7_OK && g_log.calls == 1 && !std::strcmp(g_log.kind, "chunk") &&
+           g_log.seq.ckpt == ffake(9) && !g_log.seq.state_pos && !g_log.seq.o_bf16);
+    EXPECT(fck(8, fake(7), fake(9)) == WKV7_OK && g_log.calls == 2 && !std::strcmp(g_log.kind, "step") &&
+           g_log.n == 2LL * 3 * 64 * 64 && !g_log.seq.ckpt);       // a copy of state_in, then the step kernel
+    EXPECT(fck(1, nullptr, fake(9)) == WKV7_OK && g_log.calls == 2 && !std::strcmp(g_log.kind, "step"));
+    EXPECT(fck(0, fake(7), nullptr) == WKV7_OK && !std::strcmp(g_log.kind, "copy"));
+    EXPECT(fck(40, fake(7), nullptr) == WKV7_ERR_NULL && g_log.calls == 0);
+    EXPECT(fck(40, fake(7), fake(9, 8)) == WKV7_ERR_ALIGN);
+    EXPECT(fck(40, fake(7), fake(6, 1024)) == WKV7_ERR_ALIAS);    // inside o
+    EXPECT(fck(40, fake(7), fake(7, 4096)) == WKV7_ERR_ALIAS);    // inside state_in
+    // three chunks of 2 x 3 heads: o just below the checkpoints' end overlaps, at their end it does not
+    const long long ck3 = 2LL * 3 * 3 * 64 * 64 * 4;
+    reset_log();
+    EXPECT(wkv7_forward_ckpt(fake(0), fake(1), fake(2), fake(3), fake(4), fake(5), WKV7_BF16, ffake(7),
+                             ffake(9, ck3 - 16), ffake(8), ffake(9), 2, 40, 3, 64, nullptr) == WKV7_ERR_ALIAS);
+    EXPECT(wkv7_forward_ckpt(fake(0), fake(1), fake(2), fake(3), fake(4), fake(5), WKV7_BF16, ffake(7),
+                             ffake(9, ck3), ffake(8), ffake(9), 2, 40, 3, 64, nullptr) == WKV7_OK);
+    auto bck = [&](void *ck, float *g0, void *dsi) {
+        reset_log();
+        return wkv7_backward_ckpt(fake(0), fake(1), fake(2), fake(3), fake(4), fake(5), WKV7_BF16, static_cast<float *>(ck),
+                                  ffake(10), ffake(17), g0, ffake(12), ffake(13), ffake(14), ffake(15), ffake(16),
+                                  static_cast<float *>(dsi), 2, 30, 3, 64, nullptr);
+    };
+    EXPECT(bck(fake(9), ffake(11), fake(18)) == WKV7_OK && !std::strcmp(g_log.kind, "backward_ckpt") &&
+           g_log.bwd.ckpt == ffake(9) && !g_log.bwd.state_pos && !g_log.bwd.state_in && g_log.T == 30);
+    // T = 30: two chunks; a gradient inside the second one's checkpoints overlaps
+    const long long ck2 = 2LL * 2 * 3 * 64 * 64 * 4;
+    EXPECT(bck(fake(9), ffake(9, ck2 - 16), fake(18)) == WKV7_ERR_ALIAS);
+    EXPECT(bck(fake(9), ffake(9, ck2), fake(18)) == WKV7_OK);
+    EXPECT(bck(nullptr, ffake(11), fake(18)) == WKV7_ERR_NULL && g_log.calls == 0);
+    EXPECT(bck(fake(9, 4), ffake(11), fake(18)) == WKV7_ERR_ALIGN);
+    EXPECT(bck(fake(9), ffake(11), fake(9)) == WKV7_ERR_ALIAS);
 
     for (int st = -8; st <= 2; ++st)
         EXPECT(wkv7_status_string(st) != nullptr && std::strlen(wkv7_status_string(st)) > 0);

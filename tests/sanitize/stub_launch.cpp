@@ -46,7 +46,13 @@ hipError_t launch_tail(const TailArgs &a, hipStream_t)
 }
 hipError_t launch_backward(const BwdArgs &a, hipStream_t)
 {
+    g_log.bwd = a;
     return note("backward", a.B, a.T, a.H);
+}
+hipError_t launch_backward_ckpt(const BwdArgs &a, hipStream_t)
+{
+    g_log.bwd = a;
+    return note("backward_ckpt", a.B, a.T, a.H);
 }
 hipError_t launch_state_commit(const float *, const int *, const float *, float *, int B, int T, int H,
                                hipStream_t)

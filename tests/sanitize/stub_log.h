@@ -9,5 +9,6 @@ struct StubLog {
     int B = 0, T = 0, H = 0;
     long long n = 0;
     wkv7::SeqArgs seq{};
+    wkv7::BwdArgs bwd{};
 };
 extern StubLog g_log;

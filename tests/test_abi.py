@@ -32,7 +32,8 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     assert names == sorted(["wkv7_forward", "wkv7_forward_varlen", "wkv7_step", "wkv7_step_tail",
                             "wkv7_forward_tail", "wkv7_tmix_tail", "wkv7_state_commit", "wkv7_state_reset",
-                            "wkv7_backward", "wkv7_status_string", "wkv7_abi_version"])
+                            "wkv7_backward", "wkv7_forward_ckpt", "wkv7_backward_ckpt", "wkv7_status_string",
+                            "wkv7_abi_version"])
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -321,3 +322,48 @@ def test_backward_validation(L):
     # T = 0 needs only d_state_in
     assert L.wkv7_backward(*([None] * 6), BF16, None, None, None, None, *([None] * 6), None, 2, 0, 3, 64,
                            None) == ERR_NULL
+
+
+def fck(L, B=2, T=40, H=3, N=64, in_dt=BF16, sin="fake", o=None, ck="fake"):
+    pick = lambda x, d: d if x == "fake" else x
+    p = [fake(i) for i in range(6)]
+    return L.wkv7_forward_ckpt(*p, in_dt, pick(sin, fake(7)), fake(6) if o is None else o, fake(8),
+                               pick(ck, fake(9)), B, T, H, N, None)
+
+
+def bck(L, B=2, T=30, H=3, N=64, in_dt=BF16, ck="fake", do="fake", grads=None, dsi="fake"):
+    pick = lambda x, d: d if x == "fake" else x
+    p = [fake(i) for i in range(6)]
+    g = [fake(11 + i) for i in range(6)] if grads is None else grads
+    return L.wkv7_backward_ckpt(*p, in_dt, pick(ck, fake(9)), pick(do, fake(10)), fake(17), *g,
+                                pick(dsi, fake(18)), B, T, H, N, None)
+
+
+def test_forward_ckpt_validation(L):
+    assert fck(L, N=32) == ERR_UNSUPPORTED
+    assert fck(L, in_dt=7) == ERR_UNSUPPORTED
+    assert fck(L, B=0) == ERR_SHAPE
+    assert fck(L, ck=None) == ERR_NULL
+    assert fck(L, ck=fake(9, 8)) == ERR_ALIGN
+    assert fck(L, ck=fake(6, 4096)) == ERR_ALIAS   # inside o
+    assert fck(L, ck=fake(2, 256)) == ERR_ALIAS    # inside k
+    assert fck(L, ck=fake(7, 16)) == ERR_ALIAS     # inside state_in
+    # [2, ceil(40/16) = 3, 3, 64, 64] fp32: o just below the checkpoints' end overlaps them
+    assert fck(L, o=fake(9, 2 * 3 * 3 * 64 * 64 * 4 - 16)) == ERR_ALIAS
+
+
+def test_backward_ckpt_validation(L):
+    assert bck(L, N=16) == ERR_UNSUPPORTED
+    assert bck(L, T=-1) == ERR_SHAPE
+    assert bck(L, ck=None) == ERR_NULL
+    assert bck(L, do=None) == ERR_NULL
+    assert bck(L, dsi=None) == ERR_NULL
+    assert bck(L, ck=fake(9, 4)) == ERR_ALIGN
+    assert bck(L, dsi=fake(9)) == ERR_ALIAS
+    # T = 30: two chunks, [2, 2, 3, 64, 64] fp32; a gradient inside the second overlaps
+    g = [fake(11 + i) for i in range(6)]
+    g[2] = fake(9, 2 * 2 * 3 * 64 * 64 * 4 - 16)
+    assert bck(L, grads=g) == ERR_ALIAS
+    g = [fake(11 + i) for i in range(6)]
+    g[4] = fake(10, 128)   # inside d_o
+    assert bck(L, grads=g) == ERR_ALIAS

@@ -142,3 +142,39 @@ def test_backward_outputs(K, H):
     _check("backward", *gs.values())
     for n, g in gs.items():
         assert g.full(), f"{n} not fully written"
+
+
+@pytest.mark.parametrize("T", [7, 45])
+def test_training_pair_outputs(K, T):
+    # T = 7: a state copy then the step kernel; T = 45: the chunked kernel writing the
+    # checkpoints; then the backward from them (H = 3: two workgroups per head)
+    B, H = 2, 3
+    d = to_dev(synth.make_inputs(B, T, H, 64, seed=420 + T, dtype="bf16", state_std=0.1))
+    nck = (T + 15) // 16
+    o, s, ck = Guarded((B, T, H, 64)), Guarded((B, H, 64, 64)), Guarded((B, nck, H, 64, 64))
+    K.wkv7_forward_ckpt(*[d[n] for n in NAMES], d["state_in"], o=o.t, state_out=s.t, ckpt=ck.t)
+    _check("forward with checkpoints", o, s, ck)
+    assert o.full() and s.full() and ck.full()
+    gen = torch.Generator(device="cuda").manual_seed(421)
+    d_o = torch.randn((B, T, H, 64), generator=gen, device="cuda")
+    d_so = torch.randn((B, H, 64, 64), generator=gen, device="cuda")
+    gs = {n: Guarded((B, T, H, 64)) for n in ("dr", "dw", "dk", "dv", "da", "db")}
+    gs["d_state_in"] = Guarded((B, H, 64, 64))
+    K.wkv7_backward_ckpt(*[d[n] for n in NAMES], ck.t, d_o, d_so, grads={n: g.t for n, g in gs.items()})
+    _check("backward from checkpoints", *gs.values())
+    for n, g in gs.items():
+        assert g.full(), f"{n} not fully written"
+
+
+def test_backward_ckpt_one_workgroup_per_head_outputs(K):
+    B, T, H = 1, 21, 129
+    d = to_dev(synth.make_inputs(B, T, H, 64, seed=422, dtype="f32", state_std=0.1))
+    _, _, ck = K.wkv7_forward_ckpt(*[d[n] for n in NAMES], d["state_in"])
+    gen = torch.Generator(device="cuda").manual_seed(423)
+    d_o = torch.randn((B, T, H, 64), generator=gen, device="cuda")
+    gs = {n: Guarded((B, T, H, 64)) for n in ("dr", "dw", "dk", "dv", "da", "db")}
+    gs["d_state_in"] = Guarded((B, H, 64, 64))
+    K.wkv7_backward_ckpt(*[d[n] for n in NAMES], ck, d_o, None, grads={n: g.t for n, g in gs.items()})
+    _check("backward from checkpoints, whole heads", *gs.values())
+    for n, g in gs.items():
+        assert g.full(), f"{n} not fully written"
