@@ -722,13 +722,20 @@ __global__ __launch_bounds__(NWB * 64) void wkv7_bwd_ckpt_kernel(BwdArgs p)
     const int x_r = (PP / CW) * C2::QS + (i % C2::L) * C2::BS + PP % CW;
     const int dv_col = (i | 32) / C2::L - CW;
     constexpr int NM = (5 * TB + NWB - 1) / NWB;
-    int sl0[NM];
+    int sl0[NM], qn0[NM];
     bool extra[NM];
+    u64 dst0[NM];  // the output of sum m (one of dr, dk, dw, db, da), chosen once
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
         const int pi0 = g + NWB * m, pi = pi0 < 5 * TB ? pi0 : pi0 - NWB;
         sl0[m] = pi / 5;
+        qn0[m] = pi - 5 * sl0[m];
         extra[m] = pi0 >= 5 * TB;
+        const int qn = qn0[m];
+        dst0[m] = pick(qn == 0, reinterpret_cast<u64>(p.dr),
+                       pick(qn == 1, reinterpret_cast<u64>(p.dk),
+                            pick(qn == 2, reinterpret_cast<u64>(p.dw),
+                                 pick(qn == 3, reinterpret_cast<u64>(p.db), reinterpret_cast<u64>(p.da)))));
     }
     // the batch of tokens t_end .. t_end + TB - 1 (slot TB - 1 - s is token t_end + s)
     auto finish_batch = [&](size_t e_end, int t_end, int pb) {
@@ -737,17 +744,12 @@ __global__ __launch_bounds__(NWB * 64) void wkv7_bwd_ckpt_kernel(BwdArgs p)
         asm volatile("" ::: "memory");
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
-            const int sl = sl0[m];
-            const int qn = (g + NWB * m - (extra[m] ? NWB : 0)) - 5 * sl0[m];
+            const int sl = sl0[m], qn = qn0[m];
             float sum = 0.f;
 #pragma unroll
             for (int gg = 0; gg < NWB; ++gg)
                 sum += sm.part[pb][sl][qn][gg][i];
-            const u64 dst = pick(qn == 0, reinterpret_cast<u64>(p.dr),
-                                 pick(qn == 1, reinterpret_cast<u64>(p.dk),
-                                      pick(qn == 2, reinterpret_cast<u64>(p.dw),
-                                           pick(qn == 3, reinterpret_cast<u64>(p.db), reinterpret_cast<u64>(p.da)))));
-            const u64 at = dst + 4u * ((e_end + static_cast<size_t>(TB - 1 - sl) * tok_e) + iu);
+            const u64 at = dst0[m] + 4u * ((e_end + static_cast<size_t>(TB - 1 - sl) * tok_e) + iu);
             if (t_end + (TB - 1 - sl) < T) {  // (the same for the whole wave)
                 if (SPLIT == 1)
                     *reinterpret_cast<GLOBAL_AS float *>(at) = sum;
@@ -757,8 +759,9 @@ __global__ __launch_bounds__(NWB * 64) void wkv7_bwd_ckpt_kernel(BwdArgs p)
             }
         }
     };
-    float St[CW];  // S_u of the token being differentiated
-    auto adjoint = [&](int u, size_t e0, bool live, const float (&Sp)[CW], int slot, int pb) {
+    // one token of the adjoint: Sp = S_{u-1}, St = S_u
+    auto adjoint = [&](int u, size_t e0, bool live, const float (&Sp)[CW], const float (&St)[CW], int slot,
+                       int pb) {
         const float ri = in_row(u, 0), wi = in_row(u, 1), ki = in_row(u, 2), ai = in_row(u, 3), bi = in_row(u, 4);
         float dO[CW], vv[CW];
         in_do(u, dO);
@@ -808,7 +811,6 @@ __global__ __launch_bounds__(NWB * 64) void wkv7_bwd_ckpt_kernel(BwdArgs p)
             p_db += G[jj] * sa[jj];
             p_da += Sp[jj] * c[jj];
             G[jj] = wi * G[jj] + ai * c[jj];
-            St[jj] = Sp[jj];
         }
         sm.part[pb][slot][0][g][i] = p_dr;
         sm.part[pb][slot][1][g][i] = p_dk;
@@ -821,7 +823,7 @@ __global__ __launch_bounds__(NWB * 64) void wkv7_bwd_ckpt_kernel(BwdArgs p)
     static_assert(CK % TB == 0 && (CK / TB) % 2 == 0,
                   "whole batches per chunk; the partial buffers alternate the same way in every chunk");
     u32x4 pre[SG::NPL];
-    float ck[CW], ckn[CW];
+    float ck[CW], ckn[CW], Sl[CW];  // checkpoints of this chunk and the one before; this chunk's last state
     stage_load(nck - 1, pre);
     ck_load(nck - 1, ck);
     stage_store(nck - 1, pre);
@@ -831,9 +833,9 @@ __global__ __launch_bounds__(NWB * 64) void wkv7_bwd_ckpt_kernel(BwdArgs p)
     for (int c = nck - 1; c >= 0; --c) {
         const int t0 = c * CK;
         const size_t ec = base_e + static_cast<size_t>(t0) * tok_e;
-        // the chunk's states: Xs[u] = S_{u-1}, from the checkpoint; S_15 is this chunk's
-        // last, carried in St from the chunk after it, or rebuilt for the last chunk
-        // (past T the steps are the identity, so it is S_{T-1})
+        // the chunk's states: Xs[u] = S_{u-1}, from the checkpoint; S_15, the chunk's
+        // last, is the next chunk's checkpoint (carried in Sl), or for the last chunk
+        // the rebuild's last state (past T the steps are the identity: S_{T-1})
         float X[CW], Xs[CK][CW];
 #pragma unroll
         for (int jj = 0; jj < CW; ++jj)
@@ -850,14 +852,14 @@ __global__ __launch_bounds__(NWB * 64) void wkv7_bwd_ckpt_kernel(BwdArgs p)
         if (c == nck - 1) {
 #pragma unroll
             for (int jj = 0; jj < CW; ++jj)
-                St[jj] = X[jj];
+                Sl[jj] = X[jj];
         }
 #pragma unroll
         for (int u = CK - 1; u >= 0; --u) {
             const int n = CK - 1 - u;  // tokens of the chunk done before this one
             const int slot = n % TB, pb = (n / TB) & 1;
             const size_t e0 = ec + static_cast<size_t>(u) * tok_e;
-            adjoint(u, e0, t0 + u < T, Xs[u], slot, pb);
+            adjoint(u, e0, t0 + u < T, Xs[u], u == CK - 1 ? Sl : Xs[u + 1], slot, pb);
             if (slot == TB - 1)
                 finish_batch(e0, t0 + u, pb);
             if (u == CK / 2 && c > 0) {
@@ -869,8 +871,10 @@ __global__ __launch_bounds__(NWB * 64) void wkv7_bwd_ckpt_kernel(BwdArgs p)
             // every wave is past the barrier of the chunk's last batch, so past its reads
             stage_store(c - 1, pre);
 #pragma unroll
-            for (int jj = 0; jj < CW; ++jj)
+            for (int jj = 0; jj < CW; ++jj) {
+                Sl[jj] = ck[jj];  // this chunk's checkpoint is the previous chunk's last state
                 ck[jj] = ckn[jj];
+            }
             __builtin_amdgcn_s_waitcnt(0xc07f);
             __builtin_amdgcn_s_barrier();
             asm volatile("" ::: "memory");
