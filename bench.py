@@ -2,6 +2,7 @@
 """Benchmark of libwkv7 on one MI355X: decode-step us/layer and prefill Mtok/s.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1|2|3|4] [--no-cpu-baseline]
+    python bench.py --entry NAME [--no-cpu-baseline]     (one measurement alone, e.g. for a profiler)
 
 Prints ONE JSON line.  The headline workload (default) is the 2.9B-shaped
 decode step (B=32, T=1, H=40, N=64, bf16 inputs, fp32 state), one layer per
@@ -11,7 +12,10 @@ call over 32 distinct layer buffer sets, state updated in place: a timed
 the dominant kernel (live HIP-event timing; HBM traffic from committed
 rocprofv3 counter summaries when they were taken on the current kernel
 source), the fp64 CPU oracle timed on a bounded sample of the same workload,
-and (default run) the prefill and verify workloads measured the same way.
+and (default run) every other measurement ("other_workloads": the prefill and
+verify workloads, the fused tail, the variable-length prefill, the commit, and
+the training pair of forward with checkpoints and backward from them), each with
+its own roofline and its own oracle baseline.
 
 Workloads (all synthetic, seeded; see synth/):
   1 decode-2.9B       B=32 T=1    H=40  step kernel, 32 layers, in place
@@ -56,8 +60,8 @@ def recurrent_flops(wl) -> int:
 
 def kernel_source_hash(kind: str) -> str:
     name = {"step": "wkv7_step.hip", "verify": "wkv7_step.hip", "chunk": "wkv7_chunk.hip", "chunk_tail": "wkv7_chunk.hip",
-            "step_tail": "wkv7_step.hip", "tail_pass": "wkv7_tail.hip", "bwd": "wkv7_bwd.hip",
-            "bwd_zero": "wkv7_bwd.hip", "commit": "wkv7_step.hip"}[kind]
+            "chunk_ckpt": "wkv7_chunk.hip", "step_tail": "wkv7_step.hip", "tail_pass": "wkv7_tail.hip",
+            "bwd_ckpt": "wkv7_bwd.hip", "bwd_zero": "wkv7_bwd.hip", "commit": "wkv7_step.hip"}[kind]
     h = hashlib.sha256()
     for f in (name, "wkv7_device.h"):
         with open(os.path.join(CSRC, f), "rb") as fh:
@@ -69,10 +73,10 @@ def call_kernels(kind: str, workload: int):
     """The kernels one call of `kind` runs on `workload`: the backward pass with two
     workgroups per head (at most 128 heads) first zeroes the outputs they add into
     ("bwd_zero")."""
-    if kind == "bwd":
+    if kind == "bwd_ckpt":
         import synth
         wl = synth.WORKLOADS[workload]
-        return ("bwd", "bwd_zero") if wl.B * wl.H * 2 <= 256 else ("bwd",)
+        return ("bwd_ckpt", "bwd_zero") if wl.B * wl.H * 2 <= 256 else ("bwd_ckpt",)
     return (kind,)
 
 
@@ -340,30 +344,30 @@ def forward_tail_bytes(wl) -> int:
     return b + (2 if wl.state_std > 0 else 1) * wl.B * wl.H * N * N * 4 + 3 * wl.H * N * 4
 
 
-def backward_bytes(wl) -> int:
-    """Algorithmic bytes of one backward call: the per-position states, the six inputs and
-    d_o read once, the six fp32 gradients written once; per head the input state and the
-    final state's gradient read, and the input state's gradient written."""
+def checkpoint_bytes(wl) -> int:
+    """The chunk checkpoints of workload wl: one fp32 state per head and 16 tokens."""
+    return wl.B * ((wl.T + 15) // 16) * wl.H * N * N * 4
+
+
+def forward_ckpt_bytes(wl) -> int:
+    """Algorithmic bytes of the forward pass with checkpoints: the prefill's, plus the
+    checkpoints written once."""
+    return algorithmic_bytes(wl, "chunk") + checkpoint_bytes(wl)
+
+
+def backward_ckpt_bytes(wl) -> int:
+    """Algorithmic bytes of one backward call from checkpoints: the six inputs and d_o read
+    once, the six fp32 gradients written once, the checkpoints read once; per head the final
+    state's gradient read and the input state's gradient written."""
     e_in = 2 if wl.dtype == "bf16" else 4
     tokheads = wl.B * wl.T * wl.H
-    per_head = (3 if wl.state_std > 0 else 2) * N * N * 4
-    return tokheads * (N * N * 4 + 6 * N * e_in + N * 4 + 6 * N * 4) + wl.B * wl.H * per_head
+    return tokheads * (6 * N * e_in + N * 4 + 6 * N * 4) + checkpoint_bytes(wl) + wl.B * wl.H * 2 * N * N * 4
 
 
-def time_backward(K, synth, idx: int, steps: int, warmup: int):
-    """The backward pass over workload idx, given the per-position states of its forward pass
-    (written once by the step kernel, untimed), a random d_o and a random final-state gradient."""
+def time_call(run, steps: int, warmup: int) -> float:
+    """Seconds per call of run() on a stream of its own (HIP events around `steps` calls)."""
     import torch
-    wl = synth.WORKLOADS[idx]
-    d = synth.workload_inputs(idx, device="cuda")
-    ins = [d[n] for n in ("r", "w", "k", "v", "a", "b")]
-    _, _, s_pos = K.wkv7_step(*ins, d["state_in"], per_position=True, write_state_out=False)
-    gen = torch.Generator(device="cuda").manual_seed(83)
-    d_o = torch.randn(d["r"].shape, generator=gen, device="cuda")
-    d_so = torch.randn((wl.B, wl.H, N, N), generator=gen, device="cuda")
-    grads = K.wkv7_backward(*ins, d["state_in"], s_pos, d_o, d_so)
     stream = torch.cuda.Stream()
-    run = lambda: K.wkv7_backward(*ins, d["state_in"], s_pos, d_o, d_so, grads=grads)
     with torch.cuda.stream(stream):
         warm(run, warmup)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -372,8 +376,35 @@ def time_backward(K, synth, idx: int, steps: int, warmup: int):
             run()
         e1.record(stream)
         e1.synchronize()
-    ms = e0.elapsed_time(e1) / steps
-    return {"sec_per_launch": ms / 1e3}
+    return e0.elapsed_time(e1) / 1e3 / steps
+
+
+def time_forward_ckpt(K, synth, idx: int, steps: int, warmup: int):
+    """The forward pass of training over prefill workload idx: o, state_out and the chunk
+    checkpoints."""
+    import torch
+    wl = synth.WORKLOADS[idx]
+    d = synth.workload_inputs(idx, device="cuda")
+    ins = [d[n] for n in ("r", "w", "k", "v", "a", "b")]
+    o, s_out, ck = K.wkv7_forward_ckpt(*ins, d["state_in"])
+    sec = time_call(lambda: K.wkv7_forward_ckpt(*ins, d["state_in"], o=o, state_out=s_out, ckpt=ck), steps, warmup)
+    return {"sec_per_launch": sec, "mtok_s": wl.B * wl.T / sec / 1e6}
+
+
+def time_backward_ckpt(K, synth, idx: int, steps: int, warmup: int):
+    """The backward pass over workload idx from the checkpoints of its forward pass (written
+    once, untimed), a random d_o and a random final-state gradient."""
+    import torch
+    wl = synth.WORKLOADS[idx]
+    d = synth.workload_inputs(idx, device="cuda")
+    ins = [d[n] for n in ("r", "w", "k", "v", "a", "b")]
+    _, _, ck = K.wkv7_forward_ckpt(*ins, d["state_in"])
+    gen = torch.Generator(device="cuda").manual_seed(83)
+    d_o = torch.randn(d["r"].shape, generator=gen, device="cuda")
+    d_so = torch.randn((wl.B, wl.H, N, N), generator=gen, device="cuda")
+    grads = K.wkv7_backward_ckpt(*ins, ck, d_o, d_so)
+    sec = time_call(lambda: K.wkv7_backward_ckpt(*ins, ck, d_o, d_so, grads=grads), steps, warmup)
+    return {"sec_per_launch": sec, "mtok_s": wl.B * wl.T / sec / 1e6}
 
 
 def copy_ceiling(idx: int, steps: int, warmup: int):
@@ -441,44 +472,250 @@ def fill_ceiling(idx: int, steps: int, warmup: int):
 
 # ----------------------------------------------------------------------------- CPU baseline
 
-def cpu_baseline(synth, idx: int, budget_s: float = 12.0):
-    """The fp64 oracle, as it stands, on a bounded sample of the headline workload."""
+def _threads() -> int:
+    return min(16, len(os.sched_getaffinity(0)))
+
+
+def _timed(fn, budget_s: float):
+    """fn() once untimed, then repeatedly for at least budget_s: (calls, seconds)."""
+    fn()
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        fn()
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            return reps, el
+
+
+def cpu_baseline(synth, idx: int, budget_s: float = 12.0, tail: bool = False):
+    """The fp64 oracle, as it stands, on full layers of a step workload (1 or 4): µs per layer.
+    With tail, the time-mix tail follows each layer's recurrence."""
+    import numpy as np
     import oracle
     wl = synth.WORKLOADS[idx]
-    threads = min(16, len(os.sched_getaffinity(0)))
+    th = _threads()
     inp = synth.workload_inputs(idx)
     args = [inp[n] for n in ("r", "w", "k", "v", "a", "b")]
-    oracle.forward(*args, inp["state_in"], nthreads=threads)  # load + warm
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        oracle.forward(*args, inp["state_in"], nthreads=threads, per_position=(idx == 4))
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s:
-            break
-    per_layer_us = el / reps * 1e6
-    return {"value": round(per_layer_us, 1), "unit": "us/layer", "cores": threads, "kind": "oracle",
-            "sample": f"{reps} calls of one full layer of workload {idx} ({wl.B}x{wl.T}x{wl.H} token-heads), "
-                      f"{el:.1f} s wall"}
+    if tail:
+        rng = np.random.default_rng(5)
+        g = 1 / (1 + np.exp(-rng.standard_normal(args[0].shape)))
+        prm = [rng.standard_normal((wl.H, N)) * 0.1, 1 + rng.standard_normal((wl.H, N)) * 0.1,
+               rng.standard_normal((wl.H, N)) * 0.1]
+        fn = lambda: oracle.tmix_tail(oracle.forward(*args, inp["state_in"], nthreads=th)[0], args[0], args[2],
+                                      args[3], g, *prm, 64e-5)
+    else:
+        fn = lambda: oracle.forward(*args, inp["state_in"], nthreads=th, per_position=(idx == 4))
+    reps, el = _timed(fn, budget_s)
+    return {"value": round(el / reps * 1e6, 1), "unit": "us/layer", "cores": th, "kind": "oracle",
+            "sample": f"{reps} calls of one full layer of workload {idx} ({wl.B}x{wl.T}x{wl.H} token-heads)"
+                      + (" with the time-mix tail" if tail else "") + f", {el:.1f} s wall"}
 
 
-def cpu_baseline_prefill(synth, idx: int, budget_s: float = 8.0):
+def cpu_baseline_prefill(synth, idx: int, budget_s: float = 8.0, what: str = "forward", Ts: int = 256):
+    """The fp64 oracle on the first Ts tokens of prefill workload idx, in Mtok/s (B Ts tokens
+    per call, every head).  what: "forward", "varlen" (the rows' lengths of the variable-length
+    measurement, scaled to Ts), "per_position" (the states every checkpoint is taken from),
+    "tail" (the time-mix tail alone), "forward_tail" (both), "backward" (the adjoint; one row
+    and 32 tokens per call: its loop runs in Python)."""
+    import numpy as np
     import oracle
     wl = synth.WORKLOADS[idx]
-    threads = min(16, len(os.sched_getaffinity(0)))
-    Ts = 256
+    th = _threads()
+    B = 1 if what == "backward" else wl.B
+    Ts = 32 if what == "backward" else Ts
     inp = synth.make_inputs(wl.B, Ts, wl.H, N, seed=wl.seed, dtype=wl.dtype, sigma_w=wl.sigma_w,
                             state_std=wl.state_std)
-    args = [inp[n] for n in ("r", "w", "k", "v", "a", "b")]
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        oracle.forward(*args, inp["state_in"], nthreads=threads)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s:
-            break
-    return {"value": round(wl.B * Ts * reps / el / 1e6, 4), "unit": "Mtok/s", "cores": threads, "kind": "oracle",
-            "sample": f"{reps} calls over the first {Ts} tokens of workload {idx}, {el:.1f} s wall"}
+    args = [inp[n][:B] for n in ("r", "w", "k", "v", "a", "b")]
+    s_in = None if inp["state_in"] is None else inp["state_in"][:B]
+    rng = np.random.default_rng(6)
+    if what in ("tail", "forward_tail"):
+        g = 1 / (1 + np.exp(-rng.standard_normal(args[0].shape)))
+        prm = [rng.standard_normal((wl.H, N)) * 0.1, 1 + rng.standard_normal((wl.H, N)) * 0.1,
+               rng.standard_normal((wl.H, N)) * 0.1]
+    if what == "forward":
+        fn = lambda: oracle.forward(*args, s_in, nthreads=th)
+    elif what == "per_position":
+        fn = lambda: oracle.forward(*args, s_in, nthreads=th, per_position=True)
+    elif what == "varlen":
+        lens = (varlen_lengths(wl).numpy().astype(np.int64) * Ts) // wl.T
+        fn = lambda: oracle.forward_varlen(*args, s_in, lengths=lens, nthreads=th)
+    elif what == "tail":
+        o = oracle.forward(*args, s_in, nthreads=th)[0]
+        fn = lambda: oracle.tmix_tail(o, args[0], args[2], args[3], g, *prm, 64e-5)
+    elif what == "forward_tail":
+        fn = lambda: oracle.tmix_tail(oracle.forward(*args, s_in, nthreads=th)[0], args[0], args[2], args[3], g,
+                                      *prm, 64e-5)
+    elif what == "backward":
+        d_o = rng.standard_normal((B, Ts, wl.H, N))
+        d_so = rng.standard_normal((B, wl.H, N, N))
+        fn = lambda: oracle.backward(*args, s_in, d_o, d_so)
+    else:
+        raise ValueError(what)
+    reps, el = _timed(fn, budget_s)
+    tokens = int(lens.sum()) if what == "varlen" else B * Ts  # (the rows' real tokens only)
+    return {"value": round(tokens * reps / el / 1e6, 5), "unit": "Mtok/s",
+            "cores": 1 if what in ("tail", "backward") else th, "kind": "oracle",
+            "sample": f"{reps} calls of the oracle's {what.replace('_', ' ')} over {B}x{Ts}x{wl.H} token-heads "
+                      f"of workload {idx}, {el:.1f} s wall"}
+
+
+def cpu_baseline_commit(synth, idx: int, budget_s: float = 3.0):
+    """The oracle's commit of each row's accepted prefix after the verify step: µs per call."""
+    import numpy as np
+    import oracle
+    wl = synth.WORKLOADS[idx]
+    inp = synth.workload_inputs(idx)
+    _, _, s_pos = oracle.forward(*[inp[n] for n in ("r", "w", "k", "v", "a", "b")], inp["state_in"],
+                                 per_position=True, nthreads=_threads())
+    acc = np.random.default_rng(97).integers(0, wl.T + 1, wl.B)
+    reps, el = _timed(lambda: oracle.state_commit(s_pos, acc, inp["state_in"]), budget_s)
+    return {"value": round(el / reps * 1e6, 1), "unit": "us/call", "cores": 1, "kind": "oracle",
+            "sample": f"{reps} commits of workload {idx}'s per-position states ({wl.B} rows), {el:.1f} s wall"}
+
+
+# ----------------------------------------------------------------------------- measurements
+
+def measurements(K, synth, args):
+    """Every measurement of the default run, by name: a function returning its entry
+    (timing, roofline, oracle baseline unless --no-cpu-baseline)."""
+    steps, warmup = args.steps, args.warmup
+    psteps = max(20, steps)
+    bsteps, bwarm = max(5, steps // 4), min(warmup, 2)
+    cpu = not args.no_cpu_baseline
+    budget = 3.0
+    W = synth.WORKLOADS
+
+    def step_wl(j):
+        t = time_step_workload(K, synth, j, steps, warmup)
+        kind = "step" if j == 1 else "verify"
+        e = {"workload": W[j].name, "ms_per_call": round(t["sec_per_launch"] * 1e3, 4),
+             "us_per_layer": round(t["us_per_layer"], 3),
+             "roofline": roofline(algorithmic_bytes(W[j], kind), t["sec_per_launch"], kind, j)}
+        if cpu:
+            e["cpu_baseline"] = cpu_baseline(synth, j, budget)
+        return e
+
+    def prefill_wl(j):
+        t = time_prefill_workload(K, synth, j, psteps, warmup)
+        e = {"workload": W[j].name, "ms_per_call": round(t["sec_per_launch"] * 1e3, 4),
+             "mtok_s": round(t["mtok_s"], 2),
+             "roofline": roofline(algorithmic_bytes(W[j], "chunk"), t["sec_per_launch"], "chunk", j),
+             "alg_flops_frac_bf16": round(recurrent_flops(W[j]) / t["sec_per_launch"] / 1e12 / PEAK_BF16_TFLOPS, 5)}
+        if cpu:
+            e["cpu_baseline"] = cpu_baseline_prefill(synth, j, budget)
+        return e
+
+    def bf16o():
+        # workload 3 with a bf16 o (the ABI's o_dtype option): 896 instead of 1024 algorithmic
+        # bytes per token-head; its HBM counters are not taken (traffic null)
+        w3 = W[3]
+        t = time_prefill_workload(K, synth, 3, psteps, warmup, o_bf16=True)
+        r = roofline(algorithmic_bytes(w3, "chunk", o_bytes=2), t["sec_per_launch"], "chunk", 3)
+        r["traffic"] = None
+        e = {"workload": w3.name + " (bf16 o)", "ms_per_call": round(t["sec_per_launch"] * 1e3, 4), "roofline": r,
+             "mtok_s": round(t["mtok_s"], 2)}
+        if cpu:
+            e["cpu_baseline"] = cpu_baseline_prefill(synth, 3, budget)
+        return e
+
+    def tail1():
+        # the time-mix tail fused into the decode step, and the step followed by the tail pass
+        w1 = W[1]
+        tt = time_step_workload(K, synth, 1, steps, warmup, tail="fused")
+        ts = time_step_workload(K, synth, 1, steps, warmup, tail="separate")
+        b = algorithmic_bytes(w1, "step") + w1.B * w1.T * w1.H * N * 2 + 3 * w1.H * N * 4
+        e = {"workload": w1.name + " (fused time-mix tail)", "us_per_layer": round(tt["us_per_layer"], 3),
+             "roofline": roofline(b, tt["sec_per_launch"], "step_tail", 1),
+             "us_per_layer_step_then_tail_pass": round(ts["us_per_layer"], 3)}
+        if cpu:
+            e["cpu_baseline"] = cpu_baseline(synth, 1, budget, tail=True)
+        return e
+
+    def pos_only():
+        # the verify step writing per-position states only (the final state is the last of them)
+        w4 = W[4]
+        t = time_step_workload(K, synth, 4, steps, warmup, tail="pos_only")
+        r = roofline(algorithmic_bytes(w4, "verify") - w4.B * w4.H * N * N * 4, t["sec_per_launch"], "verify", 4)
+        r["traffic"] = None
+        e = {"workload": w4.name + " (per-position states only)", "us_per_layer": round(t["us_per_layer"], 3),
+             "roofline": r}
+        if cpu:
+            e["cpu_baseline"] = cpu_baseline(synth, 4, budget)
+        return e
+
+    def tail_pass():
+        w3 = W[3]
+        t = time_tail_pass(K, synth, 3, psteps, warmup)
+        b = w3.B * w3.T * w3.H * N * (4 + 4 * 2 + 4) + 3 * w3.H * N * 4
+        e = {"workload": w3.name + " (time-mix tail pass)", "ms_per_call": round(t["sec_per_launch"] * 1e3, 4),
+             "mtok_s": round(w3.B * w3.T / t["sec_per_launch"] / 1e6, 2),
+             "roofline": roofline(b, t["sec_per_launch"], "tail_pass", 3)}
+        if cpu:
+            e["cpu_baseline"] = cpu_baseline_prefill(synth, 3, budget, what="tail")
+        return e
+
+    def fused_tail():
+        # the prefill with the tail fused into the chunked kernel (x instead of o)
+        w3 = W[3]
+        t = time_forward_tail(K, synth, 3, psteps, warmup)
+        e = {"workload": w3.name + " (prefill with the time-mix tail fused)",
+             "ms_per_call": round(t["sec_per_launch"] * 1e3, 4), "mtok_s": round(t["mtok_s"], 2),
+             "roofline": roofline(forward_tail_bytes(w3), t["sec_per_launch"], "chunk_tail", 3)}
+        if cpu:
+            e["cpu_baseline"] = cpu_baseline_prefill(synth, 3, budget, what="forward_tail")
+        return e
+
+    def fwd_ckpt(j):
+        # the forward pass of training: the prefill plus the state before every 16-token chunk
+        t = time_forward_ckpt(K, synth, j, psteps, warmup)
+        e = {"workload": W[j].name + " (forward with chunk checkpoints)",
+             "ms_per_call": round(t["sec_per_launch"] * 1e3, 4), "mtok_s": round(t["mtok_s"], 2),
+             "roofline": roofline(forward_ckpt_bytes(W[j]), t["sec_per_launch"], "chunk_ckpt", j)}
+        if cpu:
+            e["cpu_baseline"] = cpu_baseline_prefill(synth, j, budget, what="per_position")
+        return e
+
+    def bwd_ckpt(j):
+        # the backward pass from those checkpoints (every state rebuilt in the kernel)
+        t = time_backward_ckpt(K, synth, j, bsteps, bwarm)
+        e = {"workload": W[j].name + " (backward pass from chunk checkpoints)",
+             "ms_per_call": round(t["sec_per_launch"] * 1e3, 4), "mtok_s": round(t["mtok_s"], 2),
+             "roofline": roofline(backward_ckpt_bytes(W[j]), t["sec_per_launch"], "bwd_ckpt", j)}
+        if cpu:
+            e["cpu_baseline"] = cpu_baseline_prefill(synth, j, budget, what="backward")
+        return e
+
+    def varlen():
+        # variable-length prefill (a right-padded batch) over workload 3
+        w3 = W[3]
+        lens = varlen_lengths(w3)
+        t = time_prefill_workload(K, synth, 3, psteps, warmup, lengths=lens.cuda())
+        r = roofline(varlen_bytes(w3, lens), t["sec_per_launch"], "chunk", 3)
+        r["traffic"] = None
+        e = {"workload": w3.name + " (rows of " + ",".join(str(int(x)) for x in lens) + " tokens)",
+             "ms_per_call": round(t["sec_per_launch"] * 1e3, 4), "roofline": r, "mtok_s": round(t["mtok_s"], 2)}
+        if cpu:
+            e["cpu_baseline"] = cpu_baseline_prefill(synth, 3, budget, what="varlen")
+        return e
+
+    def commit():
+        # the commit of each row's accepted prefix after the verify step of workload 4
+        w4 = W[4]
+        t = time_commit(K, synth, 4, steps, warmup)
+        r = roofline(t["bytes"], t["sec_per_launch"], "commit", 4)
+        r["traffic"] = None
+        e = {"workload": w4.name + " (commit of the accepted prefixes)",
+             "us_per_call": round(t["sec_per_launch"] * 1e6, 3), "roofline": r}
+        if cpu:
+            e["cpu_baseline"] = cpu_baseline_commit(synth, 4, budget)
+        return e
+
+    return {"1": lambda: step_wl(1), "2": lambda: prefill_wl(2), "3": lambda: prefill_wl(3),
+            "4": lambda: step_wl(4), "3-bf16o": bf16o, "1-tail": tail1, "4-pos-only": pos_only,
+            "3-tail-pass": tail_pass, "3-fused-tail": fused_tail, "2-fwd-ckpt": lambda: fwd_ckpt(2),
+            "2-bwd": lambda: bwd_ckpt(2), "3-fwd-ckpt": lambda: fwd_ckpt(3), "3-bwd": lambda: bwd_ckpt(3),
+            "3-varlen": varlen, "4-commit": commit}
 
 
 # ----------------------------------------------------------------------------- main
@@ -492,6 +729,8 @@ def main():
     ap.add_argument("--workload", type=int, default=1, choices=[1, 2, 3, 4])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", action="store_true", help="measure the chosen workload only")
+    ap.add_argument("--entry", default=None,
+                    help="run one named measurement of the default run alone (e.g. 3-bwd) and print its entry")
     ap.add_argument("--warm-seconds", type=float, default=WARM_SECONDS,
                     help="minimum untimed warm-up per measurement (0: just --warmup steps)")
     ap.add_argument("--fill-ceiling", action="store_true",
@@ -520,24 +759,23 @@ def main():
         return
     import rwkv_linear_attention_amd as K
     K.lib()
-
-    def measure(idx):
-        wl = synth.WORKLOADS[idx]
-        if idx in (1, 4):
-            kind = "step" if idx == 1 else "verify"
-            t = time_step_workload(K, synth, idx, args.steps, args.warmup)
-            rl = roofline(algorithmic_bytes(wl, kind), t["sec_per_launch"], kind, idx)
-            return t, rl
-        t = time_prefill_workload(K, synth, idx, max(20, args.steps), args.warmup)
-        rl = roofline(algorithmic_bytes(wl, "chunk"), t["sec_per_launch"], "chunk", idx)
-        return t, rl
+    table = measurements(K, synth, args)
+    if args.entry is not None:
+        if args.entry not in table:
+            raise SystemExit(f"unknown entry {args.entry!r}; one of {', '.join(table)}")
+        print(json.dumps({"entry": args.entry, **table[args.entry]()}), flush=True)
+        return
 
     idx = args.workload
     wl = synth.WORKLOADS[idx]
-    t, rl = measure(idx)
     if idx in (1, 4):
+        kind = "step" if idx == 1 else "verify"
+        t = time_step_workload(K, synth, idx, args.steps, args.warmup)
+        rl = roofline(algorithmic_bytes(wl, kind), t["sec_per_launch"], kind, idx)
         metric_value, unit, hib = t["us_per_layer"], "us/layer", False
     else:
+        t = time_prefill_workload(K, synth, idx, max(20, args.steps), args.warmup)
+        rl = roofline(algorithmic_bytes(wl, "chunk"), t["sec_per_launch"], "chunk", idx)
         metric_value, unit, hib = t["mtok_s"], "Mtok/s", True
 
     line = {
@@ -561,82 +799,10 @@ def main():
         line["cpu_baseline"] = (cpu_baseline(synth, idx) if idx in (1, 4) else cpu_baseline_prefill(synth, idx))
     if not args.only:
         others = {}
-        for j in (1, 2, 3, 4):
-            if j == idx:
-                continue
-            tj, rj = measure(j)
-            wj = synth.WORKLOADS[j]
-            entry = {"workload": wj.name, "ms_per_call": round(tj["sec_per_launch"] * 1e3, 4), "roofline": rj}
-            if j in (1, 4):
-                entry["us_per_layer"] = round(tj["us_per_layer"], 3)
-            else:
-                entry["mtok_s"] = round(tj["mtok_s"], 2)
-                entry["alg_flops_frac_bf16"] = round(recurrent_flops(wj) / tj["sec_per_launch"] / 1e12
-                                                     / PEAK_BF16_TFLOPS, 5)
-            others[str(j)] = entry
-        # the prefill of workload 3 with a bf16 o (the ABI's o_dtype option): 896 instead of
-        # 1024 algorithmic bytes per token-head; its HBM counters are not taken (traffic null)
-        w3 = synth.WORKLOADS[3]
-        tb = time_prefill_workload(K, synth, 3, max(20, args.steps), args.warmup, o_bf16=True)
-        rb = roofline(algorithmic_bytes(w3, "chunk", o_bytes=2), tb["sec_per_launch"], "chunk", 3)
-        rb["traffic"] = None
-        others["3-bf16o"] = {"workload": w3.name + " (bf16 o)", "ms_per_call": round(tb["sec_per_launch"] * 1e3, 4),
-                             "roofline": rb, "mtok_s": round(tb["mtok_s"], 2)}
-        # the time-mix tail: fused into the decode step (workload 1), and as a pass of its own
-        # over the prefill outputs of workload 3 (fp32 o and x, bf16 r, k, v, g)
-        w1 = synth.WORKLOADS[1]
-        tt = time_step_workload(K, synth, 1, args.steps, args.warmup, tail="fused")
-        ts = time_step_workload(K, synth, 1, args.steps, args.warmup, tail="separate")
-        b_tail = algorithmic_bytes(w1, "step") + w1.B * w1.T * w1.H * N * 2 + 3 * w1.H * N * 4
-        rt = roofline(b_tail, tt["sec_per_launch"], "step_tail", 1)
-        others["1-tail"] = {"workload": w1.name + " (fused time-mix tail)", "us_per_layer": round(tt["us_per_layer"], 3),
-                            "roofline": rt,
-                            "us_per_layer_step_then_tail_pass": round(ts["us_per_layer"], 3)}
-        # the verify step writing per-position states only (the final state is the last of them)
-        w4 = synth.WORKLOADS[4]
-        tv = time_step_workload(K, synth, 4, args.steps, args.warmup, tail="pos_only")
-        rv = roofline(algorithmic_bytes(w4, "verify") - w4.B * w4.H * N * N * 4, tv["sec_per_launch"], "verify", 4)
-        rv["traffic"] = None
-        others["4-pos-only"] = {"workload": w4.name + " (per-position states only)",
-                                "us_per_layer": round(tv["us_per_layer"], 3), "roofline": rv}
-        tp = time_tail_pass(K, synth, 3, max(20, args.steps), args.warmup)
-        b_pass = w3.B * w3.T * w3.H * N * (4 + 4 * 2 + 4) + 3 * w3.H * N * 4
-        rp = roofline(b_pass, tp["sec_per_launch"], "tail_pass", 3)
-        others["3-tail-pass"] = {"workload": w3.name + " (time-mix tail pass)",
-                                 "ms_per_call": round(tp["sec_per_launch"] * 1e3, 4), "roofline": rp}
-        # the prefill with the tail fused into the chunked kernel (x instead of o)
-        tf = time_forward_tail(K, synth, 3, max(20, args.steps), args.warmup)
-        rf = roofline(forward_tail_bytes(w3), tf["sec_per_launch"], "chunk_tail", 3)
-        others["3-fused-tail"] = {"workload": w3.name + " (prefill with the time-mix tail fused)",
-                                  "ms_per_call": round(tf["sec_per_launch"] * 1e3, 4), "roofline": rf,
-                                  "mtok_s": round(tf["mtok_s"], 2)}
-        # the backward pass (gradients) over workload 2, from the per-position states
-        w2 = synth.WORKLOADS[2]
-        tg = time_backward(K, synth, 2, max(5, args.steps // 4), min(args.warmup, 2))
-        rg = roofline(backward_bytes(w2), tg["sec_per_launch"], "bwd", 2)
-        others["2-bwd"] = {"workload": w2.name + " (backward pass)",
-                           "ms_per_call": round(tg["sec_per_launch"] * 1e3, 4), "roofline": rg,
-                           "mtok_s": round(w2.B * w2.T / tg["sec_per_launch"] / 1e6, 2)}
-        # variable-length prefill (a right-padded batch) over workload 3, and the commit of
-        # each row's accepted prefix after the verify step of workload 4
-        lens = varlen_lengths(w3)
-        tvl = time_prefill_workload(K, synth, 3, max(20, args.steps), args.warmup, lengths=lens.cuda())
-        rvl = roofline(varlen_bytes(w3, lens), tvl["sec_per_launch"], "chunk", 3)
-        rvl["traffic"] = None
-        others["3-varlen"] = {"workload": w3.name + " (rows of " + ",".join(str(int(x)) for x in lens) + " tokens)",
-                              "ms_per_call": round(tvl["sec_per_launch"] * 1e3, 4), "roofline": rvl,
-                              "mtok_s": round(tvl["mtok_s"], 2)}
-        tc = time_commit(K, synth, 4, args.steps, args.warmup)
-        rc = roofline(tc["bytes"], tc["sec_per_launch"], "commit", 4)
-        rc["traffic"] = None
-        others["4-commit"] = {"workload": w4.name + " (commit of the accepted prefixes)",
-                              "us_per_call": round(tc["sec_per_launch"] * 1e6, 3), "roofline": rc}
-        # the same over workload 3: 256 heads, one workgroup per head
-        tg3 = time_backward(K, synth, 3, max(5, args.steps // 4), min(args.warmup, 2))
-        rg3 = roofline(backward_bytes(w3), tg3["sec_per_launch"], "bwd", 3)
-        others["3-bwd"] = {"workload": w3.name + " (backward pass)",
-                           "ms_per_call": round(tg3["sec_per_launch"] * 1e3, 4), "roofline": rg3,
-                           "mtok_s": round(w3.B * w3.T / tg3["sec_per_launch"] / 1e6, 2)}
+        for name, fn in table.items():
+            if name != str(idx):
+                others[name] = fn()
+                print(f"bench: {name} measured", file=sys.stderr, flush=True)  # (progress, on stderr)
         line["other_workloads"] = others
     print(json.dumps(line), flush=True)
 
