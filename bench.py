@@ -61,7 +61,8 @@ def recurrent_flops(wl) -> int:
 def kernel_source_hash(kind: str) -> str:
     name = {"step": "wkv7_step.hip", "verify": "wkv7_step.hip", "chunk": "wkv7_chunk.hip", "chunk_tail": "wkv7_chunk.hip",
             "chunk_ckpt": "wkv7_chunk.hip", "step_tail": "wkv7_step.hip", "tail_pass": "wkv7_tail.hip",
-            "bwd_ckpt": "wkv7_bwd.hip", "bwd_zero": "wkv7_bwd.hip", "commit": "wkv7_step.hip"}[kind]
+            "bwd_ckpt": "wkv7_bwd.hip", "bwd": "wkv7_bwd.hip", "bwd_zero": "wkv7_bwd.hip",
+            "commit": "wkv7_step.hip"}[kind]
     h = hashlib.sha256()
     for f in (name, "wkv7_device.h"):
         with open(os.path.join(CSRC, f), "rb") as fh:
@@ -73,10 +74,10 @@ def call_kernels(kind: str, workload: int):
     """The kernels one call of `kind` runs on `workload`: the backward pass with two
     workgroups per head (at most 128 heads) first zeroes the outputs they add into
     ("bwd_zero")."""
-    if kind == "bwd_ckpt":
+    if kind in ("bwd_ckpt", "bwd"):
         import synth
         wl = synth.WORKLOADS[workload]
-        return ("bwd_ckpt", "bwd_zero") if wl.B * wl.H * 2 <= 256 else ("bwd_ckpt",)
+        return (kind, "bwd_zero") if wl.B * wl.H * 2 <= 256 else (kind,)
     return (kind,)
 
 
@@ -364,6 +365,16 @@ def backward_ckpt_bytes(wl) -> int:
     return tokheads * (6 * N * e_in + N * 4 + 6 * N * 4) + checkpoint_bytes(wl) + wl.B * wl.H * 2 * N * N * 4
 
 
+def perpos_backward_bytes(wl) -> int:
+    """Algorithmic bytes of one call of the backward from per-position states (wkv7_backward):
+    the states, the six inputs and d_o read once, the six gradients written once; per head the
+    input state and the final state's gradient read, the input state's gradient written."""
+    e_in = 2 if wl.dtype == "bf16" else 4
+    tokheads = wl.B * wl.T * wl.H
+    per_head = (3 if wl.state_std > 0 else 2) * N * N * 4
+    return tokheads * (N * N * 4 + 6 * N * e_in + N * 4 + 6 * N * 4) + wl.B * wl.H * per_head
+
+
 def time_call(run, steps: int, warmup: int) -> float:
     """Seconds per call of run() on a stream of its own (HIP events around `steps` calls)."""
     import torch
@@ -468,6 +479,23 @@ def fill_ceiling(idx: int, steps: int, warmup: int):
         e1.synchronize()
     sec = e0.elapsed_time(e1) / 1e3 / (steps * layers)
     return {"bytes_per_fill": 4 * n, "us_per_fill": round(sec * 1e6, 3), "GB/s": round(4 * n / sec / 1e9, 1)}
+
+
+def time_backward_perpos(K, synth, idx: int, steps: int, warmup: int):
+    """The training pair without checkpoints, for comparison: the recurrent pass writing every
+    per-position state (wkv7_step), then the backward reading them (wkv7_backward)."""
+    import torch
+    wl = synth.WORKLOADS[idx]
+    d = synth.workload_inputs(idx, device="cuda")
+    ins = [d[n] for n in ("r", "w", "k", "v", "a", "b")]
+    o, s_out, s_pos = K.wkv7_step(*ins, d["state_in"], per_position=True)
+    gen = torch.Generator(device="cuda").manual_seed(83)
+    d_o = torch.randn(d["r"].shape, generator=gen, device="cuda")
+    d_so = torch.randn((wl.B, wl.H, N, N), generator=gen, device="cuda")
+    grads = K.wkv7_backward(*ins, d["state_in"], s_pos, d_o, d_so)
+    fwd = time_call(lambda: K.wkv7_step(*ins, d["state_in"], o=o, state_out=s_out, state_pos=s_pos), steps, warmup)
+    bwd = time_call(lambda: K.wkv7_backward(*ins, d["state_in"], s_pos, d_o, d_so, grads=grads), steps, warmup)
+    return {"sec_per_launch": bwd, "sec_forward": fwd, "state_bytes": s_pos.numel() * 4}
 
 
 # ----------------------------------------------------------------------------- CPU baseline
@@ -686,6 +714,19 @@ def measurements(K, synth, args):
             e["cpu_baseline"] = cpu_baseline_prefill(synth, j, budget, what="backward")
         return e
 
+    def bwd_perpos(j):
+        # for comparison: the backward from per-position states, which the recurrent pass
+        # must write first (16 KB per token-head)
+        t = time_backward_perpos(K, synth, j, bsteps, bwarm)
+        e = {"workload": W[j].name + " (backward pass from per-position states)",
+             "ms_per_call": round(t["sec_per_launch"] * 1e3, 4),
+             "ms_forward_writing_the_states": round(t["sec_forward"] * 1e3, 4),
+             "state_bytes": t["state_bytes"],
+             "roofline": roofline(perpos_backward_bytes(W[j]), t["sec_per_launch"], "bwd", j)}
+        if cpu:
+            e["cpu_baseline"] = cpu_baseline_prefill(synth, j, budget, what="backward")
+        return e
+
     def varlen():
         # variable-length prefill (a right-padded batch) over workload 3
         w3 = W[3]
@@ -715,6 +756,7 @@ def measurements(K, synth, args):
             "4": lambda: step_wl(4), "3-bf16o": bf16o, "1-tail": tail1, "4-pos-only": pos_only,
             "3-tail-pass": tail_pass, "3-fused-tail": fused_tail, "2-fwd-ckpt": lambda: fwd_ckpt(2),
             "2-bwd": lambda: bwd_ckpt(2), "3-fwd-ckpt": lambda: fwd_ckpt(3), "3-bwd": lambda: bwd_ckpt(3),
+            "3-bwd-perpos": lambda: bwd_perpos(3),
             "3-varlen": varlen, "4-commit": commit}
 
 
