@@ -755,8 +755,8 @@ def measurements(K, synth, args):
     return {"1": lambda: step_wl(1), "2": lambda: prefill_wl(2), "3": lambda: prefill_wl(3),
             "4": lambda: step_wl(4), "3-bf16o": bf16o, "1-tail": tail1, "4-pos-only": pos_only,
             "3-tail-pass": tail_pass, "3-fused-tail": fused_tail, "2-fwd-ckpt": lambda: fwd_ckpt(2),
-            "2-bwd": lambda: bwd_ckpt(2), "3-fwd-ckpt": lambda: fwd_ckpt(3), "3-bwd": lambda: bwd_ckpt(3),
-            "3-bwd-perpos": lambda: bwd_perpos(3),
+            "2-bwd": lambda: bwd_ckpt(2), "2-bwd-perpos": lambda: bwd_perpos(2), "3-fwd-ckpt": lambda: fwd_ckpt(3),
+            "3-bwd": lambda: bwd_ckpt(3), "3-bwd-perpos": lambda: bwd_perpos(3),
             "3-varlen": varlen, "4-commit": commit}
 
 
