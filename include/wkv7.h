@@ -30,6 +30,7 @@
  *   r, w, k, v, a, b, o : [B, T, H, N]      element (b,t,h,n) at ((b*T+t)*H+h)*N+n
  *   state_in, state_out : [B, H, N, N] fp32 element (b,h,i,j) at ((b*H+h)*N+i)*N+j
  *   state_pos           : [B, T, H, N, N] fp32, [b,t,h] = S after token t
+ *   ckpt                : [B, ceil(T/16), H, N, N] fp32, [b,c,h] = S before token 16c
  *
  * MEMORY.  Every pointer is a DEVICE pointer on the current HIP device,
  * 16-byte aligned.  The caller owns every buffer; the library never
@@ -61,6 +62,10 @@
 extern "C" {
 #endif
 
+/* 2: commit and variable-length rows; 3: the two tail entry points; 4: the
+ * backward pass; 5: wkv7_forward_tail (and the chunked kernel exact for every
+ * decay); 6: wkv7_forward_ckpt and wkv7_backward_ckpt.  No entry point's
+ * meaning changed in any of these. */
 #define WKV7_ABI_VERSION 6
 
 /* Element types of r, w, k, v, a, b (in_dtype) and of o (o_dtype). */
