@@ -471,19 +471,25 @@ hipError_t launch_bwd_t(const BwdArgs &p, hipStream_t stream)
 // Lane i is key row i, wave g holds CW value columns, as in the kernel above.
 constexpr int CK = 16;  // tokens per checkpoint
 
-// Column sums of NQ quantities over the 64 key rows, through LDS: quantity q's CW
-// columns are NQ CW pairs, pair P summed by the L = 64 / (NQ CW) lanes L P .. L P + L - 1
-// (RPL = 64 / L rows each), then by DPP adds across those lanes.  Storage: quantity q,
-// row block h (RPL rows), row rr, column jj at q QS + h BS + rr CW + jj; the padding
-// puts the 32 lanes of a half wave, which read one row rr at a time, in 32 banks
-// (pairs of a half wave in the low bits, row blocks 32 / L banks apart).
+// Column sums of NQ quantities over the 64 key rows, through LDS: the NQ CW (quantity,
+// column) pairs are summed by L = 64 / (NQ CW) lanes each, pair P by lanes L P .. L P + L - 1
+// (RPL = 64 / L rows each), then by DPP adds across those lanes.  Storage, in groups of
+// four columns: quantity q, group cg, row block h (RPL rows), row rr, column c4 at
+// q QS + (cg L + h) BS + 4 rr + c4.  A lane writes a group's four values as one 16-byte
+// write, next to the neighbouring row's; the padding of a row block (BS = min(4, 32/L)
+// modulo 32) puts the 32 lanes of a half wave, which read one row rr of their pairs at
+// a time, in 32 different banks.
 template <int CW, int NQ>
 struct ColSumN {
     static constexpr int L = kN / (NQ * CW);
     static constexpr int RPL = kN / L;
-    static constexpr int BS = RPL * CW + ((32 / L - RPL * CW) % 32 + 32) % 32;
-    static constexpr int QS = L * BS;
-    static_assert(NQ * CW * L == kN && L >= 4 && L <= 16, "pairs fill the wave; 4 to 16 lanes per pair");
+    static constexpr int BS = RPL * 4 + (((L >= 8 ? 32 / L : 4) - RPL * 4) % 32 + 32) % 32;
+    static constexpr int QS = (CW / 4) * L * BS;
+    static_assert(NQ * CW * L == kN && L >= 4 && L <= 16 && CW % 4 == 0, "pairs fill the wave; 4 to 16 lanes per pair");
+    // where lane i writes group cg of quantity 0, and where the lane of pair P, row block h
+    // reads its first row
+    static __device__ int wr(int i, int cg) { return (cg * L + i / RPL) * BS + 4 * (i % RPL); }
+    static __device__ int rd(int P, int h) { return (P / CW) * QS + ((P % CW) / 4 * L + h) * BS + (P % CW) % 4; }
 };
 
 // Sum over the L lanes of a pair (aligned groups of L lanes), to every one of them.
@@ -499,20 +505,24 @@ __device__ __forceinline__ float pair_sum(float x)
     return x;
 }
 
-// The staging of one chunk's inputs in 16-byte pieces, tensor after tensor: r, w, k, a,
-// b (64 elements per token, in_dtype), v (the workgroup's NC columns, in_dtype), d_o
-// (NC columns, fp32); within a tensor, token after token.  Every tensor has a
-// multiple of 64 pieces, so the 64 pieces a wave loads at a time lie in one tensor.
+// The staging of one chunk's inputs, loaded in 16-byte pieces, tensor after tensor: r,
+// w, k, a, b (64 elements per token, in_dtype), v (the workgroup's NC columns, in_dtype),
+// d_o (NC columns, fp32); within a tensor, token after token.  Every tensor has a
+// multiple of 64 pieces, so the 64 pieces a wave loads at a time lie in one tensor.  In
+// LDS every tensor is fp32 (bf16 pieces are widened once, when stored), token after
+// token, so that a token's reads need no conversion.
 template <typename Tin, int SPLIT>
 struct Stage {
     static constexpr int ES = static_cast<int>(sizeof(Tin));
     static constexpr int NC = kN / SPLIT;
     static constexpr int QP = kN * ES / 16, VP = NC * ES / 16, DP = NC * 4 / 16;  // pieces per token
     static constexpr int R = CK * QP, RV = CK * VP, RD = CK * DP;                 // pieces per tensor
-    static constexpr int OV = 5 * R * 16, OD = (5 * R + RV) * 16;                 // byte offsets of v, d_o
     static constexpr int TOT = 5 * R + RV + RD;
     static constexpr int NPL = (TOT + NWB * 64 - 1) / (NWB * 64);  // pieces per lane
-    static constexpr int BYTES = NPL * NWB * 64 * 16;              // with the last lanes' padding
+    static constexpr int LQ = CK * kN * 4, LV = CK * NC * 4;      // LDS bytes of a row tensor, of v or d_o
+    static constexpr int OV = 5 * LQ, OD = 5 * LQ + LV;            // LDS byte offsets of v, d_o
+    static constexpr int PAD = OD + LV;                            // 32 bytes that the lanes past TOT write
+    static constexpr int BYTES = PAD + 32;
     static_assert(R % 64 == 0 && RV % 64 == 0 && RD % 64 == 0, "a wave's 64 pieces lie in one tensor");
 };
 
@@ -530,6 +540,7 @@ template <typename Tin, int CW, int SPLIT>
 struct alignas(16) CkSmem {
     static constexpr int XS = 2 * ColSumN<CW, 2>::QS > ColSumN<CW, 1>::QS ? 2 * ColSumN<CW, 2>::QS
                                                                         : ColSumN<CW, 1>::QS;
+    static_assert(XS % 4 == 0, "16-byte rows");
     char in[Stage<Tin, SPLIT>::BYTES];     // the chunk's inputs
     float x[NWB][XS];                      // per-wave column-sum terms
     float sa[NWB][CK][CW];                 // per-wave S_{u-1}^T a_u of the chunk's tokens
@@ -589,6 +600,8 @@ __global__ __launch_bounds__(NWB * 64) void wkv7_bwd_ckpt_kernel(BwdArgs p)
         u64 tb;     // its bytes per token
         int u, o;   // token within the chunk, 16-byte piece within the token's row
         bool w1;    // a piece of w (1 in an identity step; every other tensor 0)
+        bool wide;  // in_dtype bf16, not d_o: widened to two 16-byte fp32 pieces in LDS
+        int dst;    // its LDS byte offset (the 32 bytes at PAD for the lanes past the last piece)
     };
     auto piece = [&](int n) {
         // (recomputed at each use: the empty asm keeps the compiler from holding every
@@ -616,6 +629,11 @@ __global__ __launch_bounds__(NWB * 64) void wkv7_bwd_ckpt_kernel(BwdArgs p)
         pc.u = l >> sh;
         pc.o = l & (pt - 1);
         pc.w1 = !is_v && !is_do && q == 1;
+        pc.wide = SG::ES == 2 && !is_do;
+        // LDS: fp32 elements from the tensor's region; a piece of d_o is four of them, a
+        // piece of another tensor 16 / ES (eight when widened from bf16)
+        const int lds0 = is_do ? SG::OD : is_v ? SG::OV : q * SG::LQ;
+        pc.dst = n * NWB * 64 + gw * 64 + i < SG::TOT ? lds0 + l * (pc.wide ? 32 : 16) : SG::PAD;
         return pc;
     };
     auto stage_load = [&](int c, u32x4 (&pre)[SG::NPL]) {
@@ -628,13 +646,25 @@ __global__ __launch_bounds__(NWB * 64) void wkv7_bwd_ckpt_kernel(BwdArgs p)
         }
     };
     auto stage_store = [&](int c, const u32x4 (&pre)[SG::NPL]) {
-        constexpr uint32_t one = SG::ES == 2 ? 0x3f803f80u : 0x3f800000u;  // 1.0 in every element
 #pragma unroll
         for (int n = 0; n < SG::NPL; ++n) {
             const Piece pc = piece(n);
-            const uint32_t id = pc.w1 ? one : 0u;
-            const u32x4 x = c * CK + pc.u < T ? pre[n] : u32x4{id, id, id, id};
-            *reinterpret_cast<u32x4 *>(sm.in + 16 * (n * NWB * 64 + g * 64 + i)) = x;
+            const bool live = c * CK + pc.u < T;
+            const uint32_t id = pc.w1 ? 0x3f800000u : 0u;  // the identity step: w = 1, the rest 0
+            char *const d = sm.in + pc.dst;
+            if (pc.wide) {  // (uniform per wave) eight bf16, widened: the upper halves of fp32
+                const u32x4 x = pre[n];
+                f32x4 lo, hi;
+                lo[0] = __uint_as_float(x[0] << 16); lo[1] = __uint_as_float(x[0] & 0xffff0000u);
+                lo[2] = __uint_as_float(x[1] << 16); lo[3] = __uint_as_float(x[1] & 0xffff0000u);
+                hi[0] = __uint_as_float(x[2] << 16); hi[1] = __uint_as_float(x[2] & 0xffff0000u);
+                hi[2] = __uint_as_float(x[3] << 16); hi[3] = __uint_as_float(x[3] & 0xffff0000u);
+                const f32x4 idv = {__uint_as_float(id), __uint_as_float(id), __uint_as_float(id), __uint_as_float(id)};
+                *reinterpret_cast<f32x4 *>(d) = live ? lo : idv;
+                *reinterpret_cast<f32x4 *>(d + 16) = live ? hi : idv;
+            } else {
+                *reinterpret_cast<u32x4 *>(d) = live ? pre[n] : u32x4{id, id, id, id};
+            }
         }
     };
     // this lane's part of checkpoint c: row i, the wave's CW columns
@@ -650,37 +680,20 @@ __global__ __launch_bounds__(NWB * 64) void wkv7_bwd_ckpt_kernel(BwdArgs p)
     };
     // ---- a token's staged inputs
     auto in_row = [&](int u, int qq) {  // quantity qq (r, w, k, a, b) at key row i
-        return to_f32(reinterpret_cast<const Tin *>(sm.in + (qq * SG::R + u * SG::QP) * 16)[i]);
+        return reinterpret_cast<const float *>(sm.in + qq * SG::LQ + u * kN * 4)[i];
     };
     auto in_v = [&](int u, float (&vv)[CW]) {  // v at the wave's columns (the same in every lane)
-        const char *pv = sm.in + SG::OV + u * SG::VP * 16 + jl * SG::ES;
-        if constexpr (sizeof(Tin) == 2) {
-            uint32_t wd[CW / 2];
-            if constexpr (CW == 8) {
-                const u32x4 x4 = *reinterpret_cast<const u32x4 *>(pv);
+        const char *pv = sm.in + SG::OV + u * SG::NC * 4 + 4 * jl;
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    wd[e] = x4[e];
-            } else {
-                const u32x2 x2 = *reinterpret_cast<const u32x2 *>(pv);
-                wd[0] = x2[0];
-                wd[1] = x2[1];
-            }
+        for (int jj = 0; jj < CW; jj += 4) {
+            const f32x4 x4 = *reinterpret_cast<const f32x4 *>(pv + 4 * jj);
 #pragma unroll
-            for (int jj = 0; jj < CW; ++jj)  // two bf16 per word, the lower one first
-                vv[jj] = __uint_as_float(jj % 2 == 0 ? wd[jj / 2] << 16 : wd[jj / 2] & 0xffff0000u);
-        } else {
-#pragma unroll
-            for (int jj = 0; jj < CW; jj += 4) {
-                const f32x4 x4 = *reinterpret_cast<const f32x4 *>(pv + 4 * jj);
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    vv[jj + e] = x4[e];
-            }
+            for (int e = 0; e < 4; ++e)
+                vv[jj + e] = x4[e];
         }
     };
     auto in_do = [&](int u, float (&dO)[CW]) {  // d_o at the wave's columns
-        const char *pd = sm.in + SG::OD + u * SG::DP * 16 + 4 * jl;
+        const char *pd = sm.in + SG::OD + u * SG::NC * 4 + 4 * jl;
 #pragma unroll
         for (int jj = 0; jj < CW; jj += 4) {
             const f32x4 x4 = *reinterpret_cast<const f32x4 *>(pd + 4 * jj);
@@ -692,20 +705,19 @@ __global__ __launch_bounds__(NWB * 64) void wkv7_bwd_ckpt_kernel(BwdArgs p)
 
     float *const xw = sm.x[g];
     // ---- one rebuild step: X <- diag(w) X + b (a^T X) + k v^T for token u; a^T X is kept
-    const int x1_w = (i / C1::RPL) * C1::BS + (i % C1::RPL) * CW;
-    const int x1_r = (i % C1::L) * C1::BS + i / C1::L;
+    const int x1_r = C1::rd(i / C1::L, i % C1::L);
     auto rebuild = [&](int u, float (&X)[CW]) {
         const float wi = in_row(u, 1), ki = in_row(u, 2), ai = in_row(u, 3), bi = in_row(u, 4);
         float vv[CW];
         in_v(u, vv);
 #pragma unroll
         for (int jj = 0; jj < CW; jj += 4)
-            *reinterpret_cast<f32x4 *>(&xw[x1_w + jj]) =
+            *reinterpret_cast<f32x4 *>(&xw[C1::wr(i, jj / 4)]) =
                 f32x4{ai * X[jj], ai * X[jj + 1], ai * X[jj + 2], ai * X[jj + 3]};
         float s2[2] = {0.f, 0.f};
 #pragma unroll
         for (int rr = 0; rr < C1::RPL; ++rr)
-            s2[rr % 2] += xw[x1_r + rr * CW];
+            s2[rr % 2] += xw[x1_r + 4 * rr];
         const float cs = pair_sum<C1::L>(s2[0] + s2[1]);
         sm.sa[g][u][i / C1::L] = cs;  // (the L lanes of a column store the same value)
 #pragma unroll
@@ -717,9 +729,7 @@ __global__ __launch_bounds__(NWB * 64) void wkv7_bwd_ckpt_kernel(BwdArgs p)
 
     // ---- the adjoint (the same arithmetic as the kernel above; S_{u-1}^T a_u from the
     // rebuild), column-sum lane roles: c in lanes 0 .. 31, dv in lanes 32 .. 63
-    const int x_w = (i / C2::RPL) * C2::BS + (i % C2::RPL) * CW;
-    const int PP = i / C2::L;
-    const int x_r = (PP / CW) * C2::QS + (i % C2::L) * C2::BS + PP % CW;
+    const int x_r = C2::rd(i / C2::L, i % C2::L);
     const int dv_col = (i | 32) / C2::L - CW;
     constexpr int NM = (5 * TB + NWB - 1) / NWB;
     int sl0[NM], qn0[NM];
@@ -732,10 +742,16 @@ __global__ __launch_bounds__(NWB * 64) void wkv7_bwd_ckpt_kernel(BwdArgs p)
         qn0[m] = pi - 5 * sl0[m];
         extra[m] = pi0 >= 5 * TB;
         const int qn = qn0[m];
-        dst0[m] = pick(qn == 0, reinterpret_cast<u64>(p.dr),
-                       pick(qn == 1, reinterpret_cast<u64>(p.dk),
-                            pick(qn == 2, reinterpret_cast<u64>(p.dw),
-                                 pick(qn == 3, reinterpret_cast<u64>(p.db), reinterpret_cast<u64>(p.da)))));
+        const u64 d = pick(qn == 0, reinterpret_cast<u64>(p.dr),
+                           pick(qn == 1, reinterpret_cast<u64>(p.dk),
+                                pick(qn == 2, reinterpret_cast<u64>(p.dw),
+                                     pick(qn == 3, reinterpret_cast<u64>(p.db), reinterpret_cast<u64>(p.da)))));
+        // (the same in every lane: held in scalar registers through the loop; the lane read
+        // returns an int, taken as unsigned before widening so that the low word is not
+        // sign-extended into the high one)
+        const unsigned lo = static_cast<unsigned>(__builtin_amdgcn_readfirstlane(static_cast<unsigned>(d)));
+        const unsigned hi = static_cast<unsigned>(__builtin_amdgcn_readfirstlane(static_cast<unsigned>(d >> 32)));
+        dst0[m] = static_cast<u64>(lo) | static_cast<u64>(hi) << 32;
     }
     // the batch of tokens t_end .. t_end + TB - 1 (slot TB - 1 - s is token t_end + s)
     auto finish_batch = [&](size_t e_end, int t_end, int pb) {
@@ -782,8 +798,8 @@ __global__ __launch_bounds__(NWB * 64) void wkv7_bwd_ckpt_kernel(BwdArgs p)
                 xc[e] = bi * G[jj + e];
                 xv[e] = ki * G[jj + e];
             }
-            *reinterpret_cast<f32x4 *>(&xw[x_w + jj]) = xc;
-            *reinterpret_cast<f32x4 *>(&xw[C2::QS + x_w + jj]) = xv;
+            *reinterpret_cast<f32x4 *>(&xw[C2::wr(i, jj / 4)]) = xc;
+            *reinterpret_cast<f32x4 *>(&xw[C2::QS + C2::wr(i, jj / 4)]) = xv;
         }
         float sa[CW];
 #pragma unroll
@@ -796,7 +812,7 @@ __global__ __launch_bounds__(NWB * 64) void wkv7_bwd_ckpt_kernel(BwdArgs p)
         float c4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int rr = 0; rr < C2::RPL; ++rr)
-            c4[rr % 4] += xw[x_r + rr * CW];
+            c4[rr % 4] += xw[x_r + 4 * rr];
         const float cs = pair_sum<C2::L>((c4[0] + c4[1]) + (c4[2] + c4[3]));
         float c[CW];
 #pragma unroll

@@ -192,3 +192,43 @@ def test_workload_training_pair_sampled_heads(K, oracle_mod, idx, heads):
         for n in NAMES:
             check(g[n][bb:bb + 1, :, hh:hh + 1], ref[n], TOL, f"{what} {n}", HEADS_SEQ)
         check(g["d_state_in"][bb:bb + 1, hh:hh + 1], ref["d_state_in"], TOL, f"{what} d_state_in", HEADS_STATE)
+
+
+def _high_window(nbytes_each, count):
+    """count fp32 views of nbytes_each bytes, all at device addresses whose low 32-bit word
+    has bit 31 set (a lane read of such a word, taken as a signed int and widened, would
+    turn the address into a wild one).  Returns (owner, views)."""
+    need = count * (nbytes_each + 256)
+    big = torch.empty(((1 << 32) + need) // 4 + 64, dtype=torch.float32, device="cuda")
+    base = big.data_ptr()
+    off = (0x80000000 - (base & 0xFFFFFFFF)) % (1 << 32)
+    off = (off + 255) // 256 * 256
+    views = []
+    for j in range(count):
+        o = off + j * (nbytes_each + 256)
+        v = big[o // 4:o // 4 + nbytes_each // 4]
+        assert (v.data_ptr() & 0xFFFFFFFF) >= 0x80000000
+        views.append(v)
+    return big, views
+
+
+@pytest.mark.parametrize("H", [3, 129])
+def test_backward_ckpt_outputs_at_high_addresses(K, H):
+    # H = 3: two workgroups per head (atomic adds); H = 129: one (plain stores)
+    B, T = 1, 37
+    inp = synth.make_inputs(B, T, H, 64, seed=5000 + H, dtype="bf16", state_std=0.1)
+    d = {n: inp[n].cuda() for n in RWKVAB}
+    _, _, ck = K.wkv7_forward_ckpt(*(d[n] for n in RWKVAB), inp["state_in"].cuda())
+    gen = torch.Generator(device="cuda").manual_seed(5001)
+    d_o = torch.randn((B, T, H, 64), generator=gen, device="cuda")
+    d_so = torch.randn((B, H, 64, 64), generator=gen, device="cuda")
+    ref = K.wkv7_backward_ckpt(*(d[n] for n in RWKVAB), ck, d_o, d_so)
+    n_seq = B * T * H * 64 * 4
+    owner, views = _high_window(max(n_seq, B * H * 64 * 64 * 4), 7)
+    grads = {n: views[j][:n_seq // 4].view(B, T, H, 64) for j, n in enumerate(NAMES)}
+    grads["d_state_in"] = views[6][:B * H * 64 * 64].view(B, H, 64, 64)
+    K.wkv7_backward_ckpt(*(d[n] for n in RWKVAB), ck, d_o, d_so, grads=grads)
+    torch.cuda.synchronize()
+    for n in NAMES + ("d_state_in",):
+        assert torch.equal(grads[n], ref[n]), n
+    del owner
