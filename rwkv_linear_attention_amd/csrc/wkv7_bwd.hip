@@ -782,13 +782,19 @@ __global__ __launch_bounds__(NWB * 64) void wkv7_bwd_ckpt_kernel(BwdArgs p)
         float dO[CW], vv[CW];
         in_do(u, dO);
         in_v(u, vv);
-        float p_dr = 0.f, p_dk = 0.f, p_dw = 0.f;
+        // With four columns per wave the column-sum reads go out before the row partials,
+        // which do not need c and run while the reads are in flight.  With eight the
+        // partials come first: the reads held across them cost spills.
+        constexpr bool EARLY = CW <= 4;
+        float p_dr = 0.f, p_dk = 0.f, p_dw = 0.f, p_db = 0.f;
 #pragma unroll
         for (int jj = 0; jj < CW; ++jj) {
             G[jj] += ri * dO[jj];
-            p_dr += St[jj] * dO[jj];
-            p_dk += G[jj] * vv[jj];
-            p_dw += G[jj] * Sp[jj];
+            if constexpr (!EARLY) {
+                p_dr += St[jj] * dO[jj];
+                p_dk += G[jj] * vv[jj];
+                p_dw += G[jj] * Sp[jj];
+            }
         }
 #pragma unroll
         for (int jj = 0; jj < CW; jj += 4) {
@@ -810,9 +816,26 @@ __global__ __launch_bounds__(NWB * 64) void wkv7_bwd_ckpt_kernel(BwdArgs p)
                 sa[jj + e] = x4[e];
         }
         float c4[4] = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (EARLY) {
+            float xr[C2::RPL];
 #pragma unroll
-        for (int rr = 0; rr < C2::RPL; ++rr)
-            c4[rr % 4] += xw[x_r + 4 * rr];
+            for (int rr = 0; rr < C2::RPL; ++rr)
+                xr[rr] = xw[x_r + 4 * rr];
+#pragma unroll
+            for (int jj = 0; jj < CW; ++jj) {
+                p_dr += St[jj] * dO[jj];
+                p_dk += G[jj] * vv[jj];
+                p_dw += G[jj] * Sp[jj];
+                p_db += G[jj] * sa[jj];
+            }
+#pragma unroll
+            for (int rr = 0; rr < C2::RPL; ++rr)
+                c4[rr % 4] += xr[rr];
+        } else {
+#pragma unroll
+            for (int rr = 0; rr < C2::RPL; ++rr)
+                c4[rr % 4] += xw[x_r + 4 * rr];
+        }
         const float cs = pair_sum<C2::L>((c4[0] + c4[1]) + (c4[2] + c4[3]));
         float c[CW];
 #pragma unroll
@@ -821,10 +844,11 @@ __global__ __launch_bounds__(NWB * 64) void wkv7_bwd_ckpt_kernel(BwdArgs p)
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(cs), __float_as_uint(cs), false, false);
         if (live)
             (p.dv + e0 + j0)[static_cast<unsigned>(dv_col)] = __uint_as_float(sw[1]);
-        float p_db = 0.f, p_da = 0.f;
+        float p_da = 0.f;
 #pragma unroll
         for (int jj = 0; jj < CW; ++jj) {
-            p_db += G[jj] * sa[jj];
+            if constexpr (!EARLY)
+                p_db += G[jj] * sa[jj];
             p_da += Sp[jj] * c[jj];
             G[jj] = wi * G[jj] + ai * c[jj];
         }
