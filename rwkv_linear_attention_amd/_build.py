@@ -9,7 +9,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB_PATH = os.path.join(PKG, "libwkv7.so")
-SOURCES = ["wkv7_api.hip", "wkv7_step.hip", "wkv7_chunk.hip", "wkv7_tail.hip", "wkv7_bwd.hip"]
+SOURCES = ["wkv7_api.hip", "wkv7_step.hip", "wkv7_chunk.hip", "wkv7_tail.hip", "wkv7_bwd.hip", "wkv7_bwdc.hip"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops: no packed fp32 math is emitted for any kernel of this library.

@@ -559,8 +559,8 @@ int wkv7_backward_ckpt(const void *r, const void *w, const void *k, const void *
                                   dv, da, db, d_state_in, B, T, H, N, &p);
     if (st != WKV7_OK)
         return st;
-    return wkv7::launch_backward_ckpt(p, static_cast<hipStream_t>(stream)) == hipSuccess ? WKV7_OK
-                                                                                          : WKV7_ERR_HIP;
+    return wkv7::launch_backward_chunked(p, static_cast<hipStream_t>(stream)) == hipSuccess ? WKV7_OK
+                                                                                             : WKV7_ERR_HIP;
 }
 
 const char *wkv7_status_string(int status)

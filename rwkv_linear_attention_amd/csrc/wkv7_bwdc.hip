@@ -1,0 +1,789 @@
+// wkv7_bwdc.hip -- the backward pass from chunk checkpoints, in chunk form.
+//
+// The pages name a trainable WKV kernel whose backward pass rebuilds the state
+// chunk by chunk (the SwiftRWKV Inference guide, its `.rwkvq` backend section)
+// and give no formulas.  The gradients are the reverse-mode adjoint of the
+// recurrence of the RWKV-X Architecture page, section "WKV-7 Kernel
+// (Generalized Delta Rule)":
+//     S_t = diag(w_t) S_{t-1} + b_t (a_t^T S_{t-1}) + k_t v_t^T,    o_t = S_t^T r_t.
+// With G = dL/dS_t, going back over the tokens,
+//     G += r_t dO_t^T;   c_t = G^T b_t;   G <- diag(w_t) G + a_t c_t^T,
+// which needs no states at all.  Everything else is local to a chunk of 16
+// tokens once the state entering it (its checkpoint, S0) and the gradient for
+// the state leaving it (G_end) are known.  So the pass runs as three launches:
+//
+//   1. the chunk kernel on every head's last chunk (its G_end is d_state_out);
+//   2. the gradient chain, one workgroup per head, serial over the tokens: it
+//      writes G_end of every other chunk, and the gradient of the input state;
+//   3. the chunk kernel on every other chunk, all at once.
+//
+// G_end of chunk c is written into c's own rows of dr, dk, da and db (16 tokens
+// x 64 channels each, four of them hold the 64 x 64 matrix), which the chunk
+// kernel reads before it overwrites them with the gradients: no workspace.
+//
+// The chunk kernel.  With P_tau the running product of w over the chunk and the
+// factors measured against position 7, d_tau = P_tau / P_7 (no absolute product
+// is formed), A' = a d_{tau-1}, R' = r d_tau, B' = b / d_tau, K' = k / d_tau,
+// S^ = diag(P_7) S0, G^ = diag(d_15) G_end, M_xy = tril(X'Y'^T) (strict for the
+// a-rows) and T = (I - M_ab)^{-1}, the chunk's forward is
+//     X = A' S^ + M_ak V,  Z = T X,  O = R' S^ + M_rb Z + M_rk V,
+//     S_end = diag(d_15) (S^ + B'^T Z + K'^T V),
+// and its reverse mode
+//     dZ = B' G^ + M_rb^T dO,  dX = T^T dZ,  dV = K' G^ + M_rk^T dO + M_ak^T dX,
+//     dM_ab = tril(dX Z^T, -1), dM_ak = tril(dX V^T, -1), dM_rb = tril(dO Z^T), dM_rk = tril(dO V^T),
+//     dA' = dX S^T + dM_ab B' + dM_ak K',   dR' = dO S^T + dM_rb B' + dM_rk K',
+//     dB' = Z G^T + dM_ab^T A' + dM_rb^T R', dK' = V G^T + dM_ak^T A' + dM_rk^T R',
+//     da = dA' d_{tau-1},  dr = dR' d_tau,  db = dB' / d_tau,  dk = dK' / d_tau,  dv = dV.
+// The decay gradient is taken in its direct form dw_t = rowsum(G_t * S_{t-1}),
+// with both states written in the chunk's terms:
+//     w_t dw_t = rowsum(G^ * S^) + sum_{u<t} (B'_u (G^ z_u) + K'_u (G^ v_u))
+//              + sum_{s>=t} R'_s (S^ dO_s + sum_{u<t} (B'_u dO_s.z_u + K'_u dO_s.v_u))
+//              + sum_{s>t}  A'_s (S^ dX_s + sum_{u<t} (B'_u dX_s.z_u + K'_u dX_s.v_u)),
+// elementwise in the key index.  Every term carries w_t among its decay
+// factors, so the division by w_t loses nothing.  (The log-decay form, a suffix
+// sum of d log P divided by w, loses about eps / w to cancellation.)  The
+// products run on the matrix cores in fp32 (16x16x4), so the chunk form is as
+// exact as the recurrence; a chunk with a decay below 2^-15 (factors outside the
+// fp32 range, w = 0 included) runs the recurrence itself instead.
+#include "wkv7_device.h"
+#include "wkv7_launch.h"
+
+#include <algorithm>
+
+namespace wkv7 {
+namespace {
+
+constexpr int CC = 16;                          // chunk length: the checkpoint spacing
+constexpr int REF = 7;                          // reference position of the decay factors
+constexpr float kExactBelow = 1.0f / 32768.0f;  // 2^-15
+
+// Four consecutive elements at p (16-byte aligned for fp32, 8-byte for bf16), widened.
+__device__ __forceinline__ f32x4 load4w(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
+__device__ __forceinline__ f32x4 load4w(const uint16_t *p)
+{
+    const uint2 u = *reinterpret_cast<const uint2 *>(p);
+    return f32x4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
+                 __uint_as_float(u.y & 0xffff0000u)};
+}
+
+// ---------------------------------------------------------------------------------
+// The gradient chain.  The value columns of G evolve independently, so each head runs
+// as two workgroups of 32 columns.  A workgroup has NW waves; lane l holds column
+// 32 h + (l & 31) of its half h and, with l >= 32 taking the second four, key rows
+// 8 g + 4 (l >> 5) .. + 3 of wave g.  Per token, c = G^T b is a sum over the key rows:
+// in-lane over four rows, across the two lane halves (a half-wave swap), then over the
+// waves through LDS (double-buffered, one barrier per token).  A chunk's r, w, a, b (per
+// key) and dO (the half's columns) are staged in LDS, loaded into registers one chunk
+// ahead; a token's rows are read right after the barrier of the token before.
+constexpr int GNW = 8, GRW = 4, GCOL = kN / 2;
+
+template <typename Tin>
+struct ChainStage {
+    // 16-byte pieces: 4 key-side tensors x 16 tokens x 64 channels, then dO 16 x 32 (fp32)
+    static constexpr int EPP = 16 / sizeof(Tin);
+    static constexpr int KP = 4 * CC * kN / EPP;
+    static constexpr int DP = CC * GCOL / 4;
+    static constexpr int PPT = (KP + DP + GNW * 64 - 1) / (GNW * 64);
+};
+
+struct ChainSmem {
+    float in[2][4][CC][kN];   // r, w, a, b of a chunk (two chunks in turn)
+    float dout[2][CC][GCOL];  // dO at the half's columns
+    float part[2][GNW][GCOL]; // per-wave partial sums of c
+};
+
+template <typename Tin, bool HAS_DOUT>
+__global__ __launch_bounds__(GNW * 64) void wkv7_bwdc_chain_kernel(BwdArgs p)
+{
+    using SG = ChainStage<Tin>;
+    __shared__ alignas(16) ChainSmem sm;
+    const int lane = threadIdx.x & 63, jl = lane & 31, rh = lane >> 5;
+    const int g = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int bh = blockIdx.x >> 1, half = blockIdx.x & 1;
+    const int H = p.H, T = p.T;
+    const int bb = bh / H, hh = bh - bb * H;
+    const int nck = (T + CC - 1) / CC;
+    const int j = half * GCOL + jl;  // this lane's column
+    const int r0 = g * 8 + rh * GRW; // this lane's first key row
+    const size_t tok_e = static_cast<size_t>(H) * kN;
+    const size_t head_e = static_cast<size_t>(bb) * T * tok_e + static_cast<size_t>(hh) * kN;
+    const size_t sbase = static_cast<size_t>(bh) * (kN * kN) + static_cast<size_t>(r0) * kN + j;
+    const Tin *const kin[4] = {static_cast<const Tin *>(p.r), static_cast<const Tin *>(p.w),
+                               static_cast<const Tin *>(p.a), static_cast<const Tin *>(p.b)};
+    float *const gout[4] = {p.dr, p.dk, p.da, p.db};
+
+    float G[GRW];
+#pragma unroll
+    for (int u = 0; u < GRW; ++u)
+        G[u] = HAS_DOUT ? p.d_state_out[sbase + u * kN] : 0.0f;
+    if (T == 0) {  // no tokens: the gradient passes through
+#pragma unroll
+        for (int u = 0; u < GRW; ++u)
+            p.d_state_in[sbase + u * kN] = G[u];
+        return;
+    }
+
+    // staging of chunk c: piece q of the thread is n = tid + q * 512; tokens are clamped
+    // into the sequence (past T they are never read)
+    f32x4 stg[SG::PPT][SG::EPP / 4];
+    auto stage_load = [&](int c) {
+#pragma unroll
+        for (int q = 0; q < SG::PPT; ++q) {
+            const int n = static_cast<int>(threadIdx.x) + q * GNW * 64;
+            if (n < SG::KP) {
+                const int ten = n / (CC * kN / SG::EPP), rem = n % (CC * kN / SG::EPP);
+                const int tau = rem / (kN / SG::EPP), col = (rem % (kN / SG::EPP)) * SG::EPP;
+                const int t = min(c * CC + tau, T - 1);
+                const Tin *src = kin[ten] + head_e + static_cast<size_t>(t) * tok_e + col;
+#pragma unroll
+                for (int h4 = 0; h4 < SG::EPP / 4; ++h4)
+                    stg[q][h4] = load4w(src + 4 * h4);
+            } else if (n < SG::KP + SG::DP) {
+                const int m = n - SG::KP, tau = m / (GCOL / 4), col = (m % (GCOL / 4)) * 4;
+                const int t = min(c * CC + tau, T - 1);
+                stg[q][0] = load4w(p.d_o + head_e + static_cast<size_t>(t) * tok_e + half * GCOL + col);
+            }
+        }
+    };
+    auto stage_store = [&](int c) {
+        const int bsel = c & 1;
+#pragma unroll
+        for (int q = 0; q < SG::PPT; ++q) {
+            const int n = static_cast<int>(threadIdx.x) + q * GNW * 64;
+            if (n < SG::KP) {
+                const int ten = n / (CC * kN / SG::EPP), rem = n % (CC * kN / SG::EPP);
+                const int tau = rem / (kN / SG::EPP), col = (rem % (kN / SG::EPP)) * SG::EPP;
+#pragma unroll
+                for (int h4 = 0; h4 < SG::EPP / 4; ++h4)
+                    *reinterpret_cast<f32x4 *>(&sm.in[bsel][ten][tau][col + 4 * h4]) = stg[q][h4];
+            } else if (n < SG::KP + SG::DP) {
+                const int m = n - SG::KP, tau = m / (GCOL / 4), col = (m % (GCOL / 4)) * 4;
+                *reinterpret_cast<f32x4 *>(&sm.dout[bsel][tau][col]) = stg[q][0];
+            }
+        }
+    };
+    // a token's rows of r, w, a, b (this lane's four keys) and its dO
+    struct Tok {
+        f32x4 r, w, a, b;
+        float d;
+    };
+    auto read_tok = [&](int bsel, int tau) {
+        Tok x;
+        x.r = *reinterpret_cast<const f32x4 *>(&sm.in[bsel][0][tau][r0]);
+        x.w = *reinterpret_cast<const f32x4 *>(&sm.in[bsel][1][tau][r0]);
+        x.a = *reinterpret_cast<const f32x4 *>(&sm.in[bsel][2][tau][r0]);
+        x.b = *reinterpret_cast<const f32x4 *>(&sm.in[bsel][3][tau][r0]);
+        x.d = sm.dout[bsel][tau][jl];
+        return x;
+    };
+
+    stage_load(nck - 1);
+    stage_store(nck - 1);
+    __syncthreads();
+    int par = 0;
+    for (int c = nck - 1; c >= 0; --c) {
+        const int bsel = c & 1;
+        if (c > 0)
+            stage_load(c - 1);  // in flight during this chunk
+        if (c < nck - 1) {
+            // G_end of chunk c: key row 16 s + tau goes to token 16 c + tau of tensor s
+#pragma unroll
+            for (int u = 0; u < GRW; ++u) {
+                const int row = r0 + u;
+                gout[row / CC][head_e + static_cast<size_t>(c * CC + row % CC) * tok_e + j] = G[u];
+            }
+        }
+        const int t_hi = min(T, (c + 1) * CC) - 1, t_lo = c * CC;
+        Tok cur = read_tok(bsel, t_hi - t_lo);
+        for (int t = t_hi; t >= t_lo; --t) {
+            float pc0 = 0.f, pc1 = 0.f;
+#pragma unroll
+            for (int u = 0; u < GRW; u += 2) {
+                G[u] = fmaf(cur.r[u], cur.d, G[u]);
+                G[u + 1] = fmaf(cur.r[u + 1], cur.d, G[u + 1]);
+                pc0 = fmaf(cur.b[u], G[u], pc0);
+                pc1 = fmaf(cur.b[u + 1], G[u + 1], pc1);
+            }
+            float pc = pc0 + pc1;
+            // the other half of the wave holds the other four rows of this column
+            pc += __shfl_xor(pc, 32);
+            if (rh == 0)
+                sm.part[par][g][jl] = pc;
+            __syncthreads();
+            const Tok nxt = read_tok(bsel, max(t - 1 - t_lo, 0));
+            float cj = sm.part[par][0][jl];
+#pragma unroll
+            for (int gg = 1; gg < GNW; ++gg)
+                cj += sm.part[par][gg][jl];
+            par ^= 1;
+#pragma unroll
+            for (int u = 0; u < GRW; ++u)
+                G[u] = fmaf(cur.w[u], G[u], cur.a[u] * cj);
+            cur = nxt;
+        }
+        if (c > 0) {
+            stage_store(c - 1);  // the other buffer: chunk c + 1 used it, long finished
+            __syncthreads();
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < GRW; ++u)
+        p.d_state_in[sbase + u * kN] = G[u];
+}
+
+// ---------------------------------------------------------------------------------
+// The chunk kernel: one workgroup of four waves per (chunk, batch, head).
+constexpr int RS = kN + 1;  // row stride of the LDS matrices (column reads hit distinct banks)
+constexpr int SS = CC + 1;  // row stride of the 16 x 16 matrices
+
+// The 16 x 64 matrices.  dR0 = dO S^T, dA0 = dX S^T, dBz = Z G^T and dKv = V G^T (the
+// first terms of dR', dA', dB', dK', kept for the decay gradient) take the places of dO,
+// dX, Z and V once those are no longer read.
+enum Row { X_R, X_W, X_K, X_V, X_A, X_B, X_DO, X_Z, X_DX, X_D, NROW };
+constexpr int X_DR0 = X_DO, X_DA0 = X_DX, X_DBZ = X_Z, X_DKV = X_V;
+// The 16 x 16 matrices: T is formed over M_ab; dO Z^T, dX Z^T and dX V^T (the masked dM's
+// and the token-pair products of the decay gradient) over M_ak, M_rb and M_rk.
+enum Small { M_AB, M_AK, M_RB, M_RK, W_OV, NSMALL };
+constexpr int M_T = M_AB, W_OZ = M_AK, W_XZ = M_RB, W_XV = M_RK;
+
+// 80.6 KB: two workgroups share a compute unit.
+struct ChunkSmem {
+    float rows[NROW][CC][RS];  // 16 x 64 matrices (tokens x channels)
+    float sq[2][kN][RS];       // S^ and G^ (key rows x value columns)
+    float sm[NSMALL][CC][SS];  // 16 x 16 matrices
+    float base[kN];            // P_7 per key, then rowsum(G^ * S^)
+    int flag;                  // the chunk takes the exact path
+};
+
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+
+// The exact path of a chunk with a decay below 2^-15 (w = 0 included): the recurrence
+// itself.  Thread (key row i, column quarter) holds 16 elements of a row of S and of G.
+// A forward sweep forms z_tau = S_{tau-1}^T a_tau (kept in LDS); then, going back over
+// the tokens, S_{t-1} and S_t are replayed from the checkpoint with those z (no more
+// column sums), and each token's gradients are those of the recurrent adjoint:
+//     dr = S_t dO_t, dk = G v_t, dw = rowsum(G * S_{t-1}), db = G z_t,
+//     c = G^T b_t, dv = G^T k_t, da = S_{t-1} c, then G <- diag(w_t) G + a_t c^T.
+// The raw inputs, the checkpoint and G_end are in LDS (no factors were applied).
+__device__ void exact_chunk(const BwdArgs &p, ChunkSmem &sm, int t0, int L, size_t head_e, size_t tok_e)
+{
+    const int tid = threadIdx.x, i = tid >> 2, j0 = (tid & 3) * 16;
+    float *const tmp = &sm.sq[0][0][0];  // 64 rows of RS, once the checkpoint is in registers
+    float *const cvec = &sm.sm[W_OZ][0][0], *const dvvec = &sm.sm[W_OV][0][0];
+    auto zrow = [&](int tau) { return &sm.rows[X_D][tau][0]; };
+    auto colsum = [&](const float (&x)[16], float *dst) {
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj)
+            tmp[i * RS + j0 + jj] = x[jj];
+        __syncthreads();
+        if (tid < kN) {
+            float acc = 0.f;
+            for (int ii = 0; ii < kN; ++ii)
+                acc += tmp[ii * RS + tid];
+            dst[tid] = acc;
+        }
+        __syncthreads();
+    };
+    auto rsum = [](float x) {
+        x += __shfl_xor(x, 1);
+        x += __shfl_xor(x, 2);
+        return x;
+    };
+    float S0r[16], G[16];
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj) {
+        S0r[jj] = sm.sq[0][i][j0 + jj];
+        G[jj] = sm.sq[1][i][j0 + jj];
+    }
+    __syncthreads();
+    auto step = [&](int u, float (&S)[16]) {
+        const float wu = sm.rows[X_W][u][i], bu = sm.rows[X_B][u][i], ku = sm.rows[X_K][u][i];
+        const float *z = zrow(u);
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj)
+            S[jj] = fmaf(wu, S[jj], fmaf(bu, z[j0 + jj], ku * sm.rows[X_V][u][j0 + jj]));
+    };
+    {
+        float S[16];
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj)
+            S[jj] = S0r[jj];
+        for (int tau = 0; tau < L; ++tau) {
+            const float at = sm.rows[X_A][tau][i];
+            float x[16];
+#pragma unroll
+            for (int jj = 0; jj < 16; ++jj)
+                x[jj] = at * S[jj];
+            colsum(x, zrow(tau));
+            step(tau, S);
+        }
+    }
+    for (int t = L - 1; t >= 0; --t) {
+        const float rt = sm.rows[X_R][t][i], wt = sm.rows[X_W][t][i], at = sm.rows[X_A][t][i];
+        const float bt = sm.rows[X_B][t][i], kt = sm.rows[X_K][t][i];
+        const float *z = zrow(t);
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj)
+            G[jj] = fmaf(rt, sm.rows[X_DO][t][j0 + jj], G[jj]);
+        float Sp[16], St[16];
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj)
+            Sp[jj] = S0r[jj];
+        for (int u = 0; u < t; ++u)
+            step(u, Sp);
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj)
+            St[jj] = Sp[jj];
+        step(t, St);
+        float s_dr = 0.f, s_dk = 0.f, s_dw = 0.f, s_db = 0.f;
+        float xc[16], xv[16];
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) {
+            const int j = j0 + jj;
+            s_dr = fmaf(St[jj], sm.rows[X_DO][t][j], s_dr);
+            s_dk = fmaf(G[jj], sm.rows[X_V][t][j], s_dk);
+            s_dw = fmaf(G[jj], Sp[jj], s_dw);
+            s_db = fmaf(G[jj], z[j], s_db);
+            xc[jj] = bt * G[jj];
+            xv[jj] = kt * G[jj];
+        }
+        s_dr = rsum(s_dr);
+        s_dk = rsum(s_dk);
+        s_dw = rsum(s_dw);
+        s_db = rsum(s_db);
+        colsum(xc, cvec);
+        colsum(xv, dvvec);
+        float s_da = 0.f;
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj)
+            s_da = fmaf(Sp[jj], cvec[j0 + jj], s_da);
+        s_da = rsum(s_da);
+        const size_t row = head_e + static_cast<size_t>(t0 + t) * tok_e;
+        if ((tid & 3) == 0) {
+            p.dr[row + i] = s_dr;
+            p.dk[row + i] = s_dk;
+            p.dw[row + i] = s_dw;
+            p.db[row + i] = s_db;
+            p.da[row + i] = s_da;
+        }
+        if (tid < kN)
+            p.dv[row + tid] = dvvec[tid];
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj)
+            G[jj] = fmaf(wt, G[jj], at * cvec[j0 + jj]);
+    }
+}
+
+template <typename Tin>
+__global__ __launch_bounds__(256) void wkv7_bwdc_chunk_kernel(BwdArgs p, int c_lo, int nbh)
+{
+    __shared__ ChunkSmem sm;
+    const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, m = lane & 15;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int c = c_lo + static_cast<int>(blockIdx.x) / nbh;
+    const int bh = static_cast<int>(blockIdx.x) % nbh;
+    const int H = p.H, T = p.T;
+    const int bb = bh / H, hh = bh - bb * H;
+    const int nck = (T + CC - 1) / CC;
+    const int t0 = c * CC, L = min(CC, T - t0);
+    const size_t tok_e = static_cast<size_t>(H) * kN;
+    const size_t head_e = static_cast<size_t>(bb) * T * tok_e + static_cast<size_t>(hh) * kN;
+    auto rowp = [&](int tau) { return head_e + static_cast<size_t>(t0 + min(tau, L - 1)) * tok_e; };
+
+    // ---- load: inputs (tokens past the end as identity steps: w = 1, the rest 0),
+    // dO, the checkpoint and G_end
+    {
+        const int tau = tid >> 4, col = (tid & 15) * 4;
+        const bool live = tau < L;
+        const Tin *const srcs[6] = {static_cast<const Tin *>(p.r), static_cast<const Tin *>(p.w),
+                                    static_cast<const Tin *>(p.k), static_cast<const Tin *>(p.v),
+                                    static_cast<const Tin *>(p.a), static_cast<const Tin *>(p.b)};
+#pragma unroll
+        for (int x = 0; x < 6; ++x) {
+            f32x4 v4 = load4w(srcs[x] + rowp(tau) + col);
+            if (!live)
+                v4 = x == X_W ? f32x4{1.f, 1.f, 1.f, 1.f} : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                sm.rows[x][tau][col + e] = v4[e];
+        }
+        f32x4 o4 = load4w(p.d_o + rowp(tau) + col);
+        if (!live)
+            o4 = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            sm.rows[X_DO][tau][col + e] = o4[e];
+    }
+    {
+        const int i = tid >> 2, j0 = (tid & 3) * 16;
+        const float *s0 = p.ckpt + ((static_cast<size_t>(bb) * nck + c) * H + hh) * (kN * kN) + i * kN + j0;
+        const float *ge = nullptr;
+        if (c < nck - 1) {
+            const float *const gsrc[4] = {p.dr, p.dk, p.da, p.db};
+            ge = gsrc[i / CC] + head_e + static_cast<size_t>(t0 + i % CC) * tok_e + j0;
+        } else if (p.d_state_out) {
+            ge = p.d_state_out + static_cast<size_t>(bh) * (kN * kN) + i * kN + j0;
+        }
+#pragma unroll
+        for (int h4 = 0; h4 < 4; ++h4) {
+            const f32x4 s4 = *reinterpret_cast<const f32x4 *>(s0 + 4 * h4);
+            const f32x4 g4 = ge ? *reinterpret_cast<const f32x4 *>(ge + 4 * h4) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                sm.sq[0][i][j0 + 4 * h4 + e] = s4[e];
+                sm.sq[1][i][j0 + 4 * h4 + e] = g4[e];
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- decay factors, one key per lane of wave 0
+    if (wv == 0) {
+        const int i = lane;
+        float wcol[CC];
+        float wmin = 1.0f;
+#pragma unroll
+        for (int tau = 0; tau < CC; ++tau) {
+            wcol[tau] = sm.rows[X_W][tau][i];
+            wmin = fminf(wmin, fabsf(wcol[tau]));
+        }
+        const bool exact = __ballot(!(wmin >= kExactBelow)) != 0ull;  // NaN included
+        if (lane == 0)
+            sm.flag = exact ? 1 : 0;
+        if (!exact) {
+            float d[CC];
+            d[REF] = 1.0f;
+#pragma unroll
+            for (int tau = REF + 1; tau < CC; ++tau)
+                d[tau] = d[tau - 1] * wcol[tau];
+#pragma unroll
+            for (int tau = REF - 1; tau >= 0; --tau)
+                d[tau] = d[tau + 1] / wcol[tau + 1];
+            float pr = wcol[0];
+#pragma unroll
+            for (int tau = 1; tau <= REF; ++tau)
+                pr *= wcol[tau];
+            sm.base[i] = pr;
+#pragma unroll
+            for (int tau = 0; tau < CC; ++tau) {
+                const float dp = tau == 0 ? d[0] / wcol[0] : d[tau - 1];
+                const float inv = 1.0f / d[tau];
+                sm.rows[X_D][tau][i] = d[tau];
+                sm.rows[X_R][tau][i] *= d[tau];
+                sm.rows[X_A][tau][i] *= dp;
+                sm.rows[X_B][tau][i] *= inv;
+                sm.rows[X_K][tau][i] *= inv;
+            }
+        }
+    }
+    __syncthreads();
+    if (sm.flag) {
+        exact_chunk(p, sm, t0, L, head_e, tok_e);
+        return;
+    }
+
+    // ---- S^ = diag(P_7) S0, G^ = diag(d_15) G_end, and rowsum(G^ * S^)
+    {
+        const int i = tid >> 2, j0 = (tid & 3) * 16;
+        const float pr = sm.base[i], d15 = sm.rows[X_D][CC - 1][i];
+        float acc = 0.f;
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) {
+            const float sv = sm.sq[0][i][j0 + jj] * pr, gv = sm.sq[1][i][j0 + jj] * d15;
+            sm.sq[0][i][j0 + jj] = sv;
+            sm.sq[1][i][j0 + jj] = gv;
+            acc = fmaf(gv, sv, acc);
+        }
+        acc += __shfl_xor(acc, 1);
+        acc += __shfl_xor(acc, 2);
+        if ((tid & 3) == 0)
+            sm.base[i] = acc;
+    }
+    __syncthreads();
+
+    // ---- matrix-core fragments (16x16x4 fp32: lane (q, m) supplies A[m][k] and B[k][m]
+    // for k = 16 q + i over a 64-long sum, k = 4 q + i over a 16-long one; the result
+    // holds rows 4 q + e of column m).  Wave wv owns column tile wv of every 16 x 64 result.
+    const int tc = 16 * wv + m;  // this lane's column in the tile
+    auto frag_rows = [&](int x, float (&f)[16]) {  // X[m][16 q + i] (also X^T as a B operand)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            f[i] = sm.rows[x][m][16 * q + i];
+    };
+    auto frag_sq_rows = [&](int sq, float (&f)[16]) {  // S[16 wv + m][16 q + i]: B of Y S^T
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            f[i] = sm.sq[sq][tc][16 * q + i];
+    };
+    auto frag_sq_cols = [&](int sq, float (&f)[16]) {  // S[16 q + i][16 wv + m]: B of Y S
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            f[i] = sm.sq[sq][16 * q + i][tc];
+    };
+    auto frag_tile = [&](int x, float (&f)[4]) {  // X[4 q + i][16 wv + m]: B over tokens
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            f[i] = sm.rows[x][4 * q + i][tc];
+    };
+    // a 16 x 16 matrix as the A operand over tokens, optionally transposed and masked to
+    // its lower triangle (strict or with the diagonal)
+    auto frag_small = [&](int sx, bool trans, int mask, float (&f)[4]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int kk = 4 * q + i, row = trans ? kk : m, col = trans ? m : kk;
+            const bool keep = mask == 0 || (mask == 1 ? col < row : col <= row);
+            f[i] = keep ? sm.sm[sx][row][col] : 0.f;
+        }
+    };
+    auto mm64 = [](f32x4 &acc, const float (&a)[16], const float (&b)[16]) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            acc = mfma4(a[i], b[i], acc);
+    };
+    auto mm16 = [](f32x4 &acc, const float (&a)[4], const float (&b)[4]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            acc = mfma4(a[i], b[i], acc);
+    };
+    auto to_rows = [&](int x, const f32x4 &acc) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            sm.rows[x][4 * q + e][tc] = acc[e];
+    };
+    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+    float fa[16], fb[16], a4[4], b4[4];
+
+    // ---- M_ab, M_ak (strict), M_rb, M_rk: one per wave
+    {
+        const int xa = wv < 2 ? X_A : X_R, xb = (wv & 1) ? X_K : X_B;
+        frag_rows(xa, fa);
+        frag_rows(xb, fb);
+        f32x4 acc = zero4;
+        mm64(acc, fa, fb);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int tau = 4 * q + e;
+            const bool keep = wv < 2 ? m < tau : m <= tau;  // entries above are dropped (they
+            sm.sm[wv][tau][m] = keep ? acc[e] : 0.f;        // may have overflowed)
+        }
+    }
+    // ---- this wave's tiles of X = A' S^, dZ = B' G^, dV = K' G^, dR0 = dO S^T, dKv = V G^T
+    f32x4 xacc = zero4, dzacc = zero4, dvacc = zero4, dracc = zero4, dkacc = zero4;
+    frag_sq_cols(0, fb);
+    frag_rows(X_A, fa);
+    mm64(xacc, fa, fb);
+    frag_sq_cols(1, fb);
+    frag_rows(X_B, fa);
+    mm64(dzacc, fa, fb);
+    frag_rows(X_K, fa);
+    mm64(dvacc, fa, fb);
+    frag_sq_rows(0, fb);
+    frag_rows(X_DO, fa);
+    mm64(dracc, fa, fb);
+    frag_sq_rows(1, fb);
+    frag_rows(X_V, fa);
+    mm64(dkacc, fa, fb);
+    __syncthreads();
+
+    // ---- the 16-long products that need the M's; T = (I - M_ab)^{-1} (wave 0, one
+    // column per lane: T = I + M_ab T row by row); dO V^T (wave 1)
+    frag_tile(X_V, b4);
+    frag_small(M_AK, false, 0, a4);
+    mm16(xacc, a4, b4);      // X += M_ak V
+    frag_tile(X_DO, b4);
+    frag_small(M_RB, true, 0, a4);
+    mm16(dzacc, a4, b4);     // dZ += M_rb^T dO
+    frag_small(M_RK, true, 0, a4);
+    mm16(dvacc, a4, b4);     // dV += M_rk^T dO
+    if (wv == 0) {
+        const int sc = lane & 15;
+        float tcol[CC];
+#pragma unroll
+        for (int t = 0; t < CC; ++t) {
+            float acc = t == sc ? 1.f : 0.f;
+#pragma unroll
+            for (int u = 0; u < t; ++u)
+                acc = fmaf(sm.sm[M_AB][t][u], tcol[u], acc);
+            tcol[t] = acc;
+        }
+        if (lane < 16)  // over M_ab: this wave's reads of it are done (program order)
+#pragma unroll
+            for (int t = 0; t < CC; ++t)
+                sm.sm[M_T][t][sc] = tcol[t];
+    } else if (wv == 1) {
+        frag_rows(X_DO, fa);
+        frag_rows(X_V, fb);
+        f32x4 acc = zero4;
+        mm64(acc, fa, fb);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            sm.sm[W_OV][4 * q + e][m] = acc[e];
+    }
+    __syncthreads();
+
+    // ---- Z = T X, dX = T^T dZ (the B operands are this lane's own rows), dV += M_ak^T dX
+    f32x4 zacc = zero4, dxacc = zero4;
+    {
+        float xb4[4] = {xacc[0], xacc[1], xacc[2], xacc[3]};
+        float zb4[4] = {dzacc[0], dzacc[1], dzacc[2], dzacc[3]};
+        frag_small(M_T, false, 0, a4);
+        mm16(zacc, a4, xb4);
+        frag_small(M_T, true, 0, a4);
+        mm16(dxacc, a4, zb4);
+        float db4[4] = {dxacc[0], dxacc[1], dxacc[2], dxacc[3]};
+        frag_small(M_AK, true, 0, a4);
+        mm16(dvacc, a4, db4);
+    }
+    to_rows(X_Z, zacc);
+    to_rows(X_DX, dxacc);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        if (4 * q + e < L)
+            p.dv[rowp(4 * q + e) + tc] = dvacc[e];
+    __syncthreads();
+
+    // ---- dO Z^T (wave 0), dX Z^T (wave 2), dX V^T (wave 3); dA0 = dX S^T, dBz = Z G^T
+    if (wv != 1) {
+        frag_rows(wv == 0 ? X_DO : X_DX, fa);
+        frag_rows(wv == 3 ? X_V : X_Z, fb);
+        f32x4 acc = zero4;
+        mm64(acc, fa, fb);
+        const int dst = wv == 0 ? W_OZ : (wv == 2 ? W_XZ : W_XV);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            sm.sm[dst][4 * q + e][m] = acc[e];
+    }
+    f32x4 daacc = zero4, dbacc = zero4;
+    frag_sq_rows(0, fb);
+    frag_rows(X_DX, fa);
+    mm64(daacc, fa, fb);
+    frag_sq_rows(1, fb);
+    frag_rows(X_Z, fa);
+    mm64(dbacc, fa, fb);
+    __syncthreads();
+    // dO, dX, Z and V are read no more: their places take dR0, dA0, dBz, dKv
+    to_rows(X_DR0, dracc);
+    to_rows(X_DA0, daacc);
+    to_rows(X_DBZ, dbacc);
+    to_rows(X_DKV, dkacc);
+
+    // ---- dR' = dR0 + dM_rb B' + dM_rk K',  dA' = dA0 + dM_ab B' + dM_ak K',
+    //      dB' = dBz + dM_ab^T A' + dM_rb^T R',  dK' = dKv + dM_ak^T A' + dM_rk^T R'
+    // (dM_rb, dM_rk: dO Z^T, dO V^T with the diagonal; dM_ab, dM_ak: dX Z^T, dX V^T strict)
+    frag_tile(X_B, b4);
+    frag_small(W_OZ, false, 2, a4);
+    mm16(dracc, a4, b4);
+    frag_small(W_XZ, false, 1, a4);
+    mm16(daacc, a4, b4);
+    frag_tile(X_K, b4);
+    frag_small(W_OV, false, 2, a4);
+    mm16(dracc, a4, b4);
+    frag_small(W_XV, false, 1, a4);
+    mm16(daacc, a4, b4);
+    frag_tile(X_A, b4);
+    frag_small(W_XZ, true, 1, a4);
+    mm16(dbacc, a4, b4);
+    frag_small(W_XV, true, 1, a4);
+    mm16(dkacc, a4, b4);
+    frag_tile(X_R, b4);
+    frag_small(W_OZ, true, 2, a4);
+    mm16(dbacc, a4, b4);
+    frag_small(W_OV, true, 2, a4);
+    mm16(dkacc, a4, b4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int tau = 4 * q + e;
+        if (tau < L) {
+            const float d = sm.rows[X_D][tau][tc];
+            const float dp = tau == 0 ? d / sm.rows[X_W][0][tc] : sm.rows[X_D][tau - 1][tc];
+            const size_t at = rowp(tau) + tc;
+            p.dr[at] = dracc[e] * d;
+            p.da[at] = daacc[e] * dp;
+            p.db[at] = dbacc[e] / d;
+            p.dk[at] = dkacc[e] / d;
+        }
+    }
+
+    // ---- dw, in its direct form.  Thread (key i, wave g) sums the terms of the s = g
+    // (mod 4) rows for every token t; the four partials meet in LDS (over S^, no longer read).
+    __syncthreads();
+    {
+        const int i = lane, g = wv;
+        float bu[CC], ku[CC], acc[CC];
+#pragma unroll
+        for (int u = 0; u < CC; ++u) {
+            bu[u] = sm.rows[X_B][u][i];
+            ku[u] = sm.rows[X_K][u][i];
+            acc[u] = 0.f;
+        }
+#pragma unroll
+        for (int s = 0; s < CC; ++s) {
+            if ((s & 3) != g)
+                continue;
+            const float rs = sm.rows[X_R][s][i], as = sm.rows[X_A][s][i];
+            const float r0 = sm.rows[X_DR0][s][i], a0 = sm.rows[X_DA0][s][i];
+            float qr = 0.f, qa = 0.f;
+#pragma unroll
+            for (int t = 0; t <= s; ++t) {
+                acc[t] = fmaf(rs, r0 + qr, acc[t]);
+                if (t < s)
+                    acc[t] = fmaf(as, a0 + qa, acc[t]);
+                qr = fmaf(bu[t], sm.sm[W_OZ][s][t], fmaf(ku[t], sm.sm[W_OV][s][t], qr));
+                qa = fmaf(bu[t], sm.sm[W_XZ][s][t], fmaf(ku[t], sm.sm[W_XV][s][t], qa));
+            }
+        }
+        __syncthreads();  // every wave is past its reads of S^
+        float *part = &sm.sq[0][0][0];  // [4][16][64]
+#pragma unroll
+        for (int t = 0; t < CC; ++t)
+            part[(g * CC + t) * kN + i] = acc[t];
+        __syncthreads();
+        float pre = sm.base[i];
+#pragma unroll
+        for (int t = 0; t < CC; ++t) {
+            if ((t & 3) == g && t < L) {
+                float tot = pre;
+#pragma unroll
+                for (int gg = 0; gg < 4; ++gg)
+                    tot += part[(gg * CC + t) * kN + i];
+                p.dw[rowp(t) + i] = tot / sm.rows[X_W][t][i];
+            }
+            pre = fmaf(bu[t], sm.rows[X_DBZ][t][i], fmaf(ku[t], sm.rows[X_DKV][t][i], pre));
+        }
+    }
+}
+template <typename Tin>
+hipError_t launch_bwdc_t(const BwdArgs &p, hipStream_t stream)
+{
+    const int nbh = p.B * p.H;
+    const int nck = (p.T + CC - 1) / CC;
+    if (nck > 0)  // every head's last chunk: G_end is d_state_out
+        hipLaunchKernelGGL(wkv7_bwdc_chunk_kernel<Tin>, dim3(static_cast<unsigned>(nbh)), dim3(256), 0, stream, p,
+                           nck - 1, nbh);
+    const dim3 cgrid(2 * static_cast<unsigned>(nbh));  // two workgroups (column halves) per head
+    if (p.d_state_out)
+        hipLaunchKernelGGL((wkv7_bwdc_chain_kernel<Tin, true>), cgrid, dim3(GNW * 64), 0, stream, p);
+    else
+        hipLaunchKernelGGL((wkv7_bwdc_chain_kernel<Tin, false>), cgrid, dim3(GNW * 64), 0, stream, p);
+    // the other chunks, at most 2^30 workgroups per launch
+    const int per = static_cast<int>(std::max<long long>(1, (1ll << 30) / nbh));
+    for (int c0 = 0; c0 < nck - 1; c0 += per) {
+        const int n = std::min(per, nck - 1 - c0);
+        hipLaunchKernelGGL(wkv7_bwdc_chunk_kernel<Tin>, dim3(static_cast<unsigned>(n) * static_cast<unsigned>(nbh)),
+                           dim3(256), 0, stream, p, c0, nbh);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_backward_chunked(const BwdArgs &p, hipStream_t stream)
+{
+    return p.in_bf16 ? launch_bwdc_t<uint16_t>(p, stream) : launch_bwdc_t<float>(p, stream);
+}
+
+}  // namespace wkv7

@@ -54,6 +54,7 @@ hipError_t launch_state_reset(float *state, int B, int H, const unsigned char *r
 hipError_t launch_tail(const TailArgs &a, hipStream_t stream);
 hipError_t launch_backward(const BwdArgs &a, hipStream_t stream);
 hipError_t launch_backward_ckpt(const BwdArgs &a, hipStream_t stream);
+hipError_t launch_backward_chunked(const BwdArgs &a, hipStream_t stream);
 hipError_t launch_state_commit(const float *state_pos, const int *accepted, const float *state_in,
                                float *state_out, int B, int T, int H, hipStream_t stream);
 

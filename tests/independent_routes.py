@@ -110,3 +110,104 @@ def pure_decay(r, w, k, v, S0):
             S_t = S_t + (np.exp(logg[t] - logg[s]) * k[s])[:, None] * v[s][None, :]
         o[t] = S_t.T @ r[t]
     return o, S_t
+
+
+def g_chain(r, w, a, b, d_o, G_T, C):
+    """The gradient recurrence alone (it needs no states): with G = dL/dS_t, going back
+    over the tokens, G += r_t d_o_t^T, then G <- diag(w_t) G + a_t (G^T b_t)^T.
+    Returns [G at the end of chunk c for every c] (c's last token not yet applied) and
+    the gradient of the input state.  One head, fp arrays [T, N], G_T [N, N]."""
+    T, N = r.shape
+    nck = -(-T // C)
+    G = np.array(G_T, copy=True)
+    ends = [None] * nck
+    for t in range(T - 1, -1, -1):
+        if t == min(T, (t // C + 1) * C) - 1:
+            ends[t // C] = G.copy()
+        G = G + np.outer(r[t], d_o[t])
+        c = G.T @ b[t]
+        G = w[t][:, None] * G + np.outer(a[t], c)
+    return ends, G
+
+
+def chunk_adjoint(r, w, k, v, a, b, S0, d_o, G_end, ref=7):
+    """Gradients of one chunk in chunk form, from the state entering it (S0) and the
+    gradient for the state leaving it (G_end).  Tokens tau = 0..L-1 of one head.
+
+    Forward, with P_tau the running product of w over the chunk, d_tau = P_tau/P_ref
+    (a reference position keeps the factors inside the exponent range),
+    A' = a d_{tau-1}, R' = r d_tau, B' = b / d_tau, K' = k / d_tau, S^ = diag(P_ref) S0,
+    M_xy = tril(X'Y'^T) (strict for the a-rows), T = (I - M_ab)^{-1}:
+        X = A' S^ + M_ak V,   Z = T X,   O = R' S^ + M_rb Z + M_rk V,
+        S_end = diag(d_last) (S^ + B'^T Z + K'^T V).
+    Reverse mode through those products, with G^ = diag(d_last) G_end:
+        dZ = B' G^ + M_rb^T dO,  dX = T^T dZ,  dV = K' G^ + M_rk^T dO + M_ak^T dX,
+        dM_ab = tril(dX Z^T, -1), dM_ak = tril(dX V^T, -1), dM_rb = tril(dO Z^T), dM_rk = tril(dO V^T),
+        dA' = dX S^T + dM_ab B' + dM_ak K',   dR' = dO S^T + dM_rb B' + dM_rk K',
+        dB' = Z G^T + dM_ab^T A' + dM_rb^T R', dK' = V G^T + dM_ak^T A' + dM_rk^T R',
+    then da = dA' d_{tau-1}, dr = dR' d_tau, db = dB' / d_tau, dk = dK' / d_tau.  The decay
+    gradient is taken in its direct form dw_t = rowsum(G_t * S_{t-1}), with both states in
+    the chunk's terms, S_{t-1} = diag(d_{t-1}) (S^ + sum_{s<t} B'_s^T z_s + K'_s^T v_s) and
+    G_t = diag(1/d_t) (G^ + sum_{s>=t} R'_s^T dO_s + sum_{s>t} A'_s^T dX_s), so that
+        w_t dw_t = rowsum(G^ * S^) + sum_{s<t} (B'_s (G^ z_s) + K'_s (G^ v_s))
+                 + sum_{s>=t} R'_s (S^ dO_s) + sum_{s>t} A'_s (S^ dX_s)
+                 + sum_{s>=t} sum_{u<t} R'_s (B'_u (dO_s . z_u) + K'_u (dO_s . v_u))
+                 + sum_{s>t} sum_{u<t} A'_s (B'_u (dX_s . z_u) + K'_u (dX_s . v_u))
+    (elementwise in the key index).  Every term carries w_t among its decay factors, so
+    the division by w_t cancels without loss.  (The log-decay form, a suffix sum of
+    d(log P_tau) divided by w_s, loses about eps / w_s to cancellation.)
+    Returns dict of [L, N] arrays."""
+    L, N = r.shape
+    dt = r.dtype
+    rho = min(ref, L - 1)
+    Pr = np.prod(w[:rho + 1], axis=0)                       # P_ref
+    d = np.ones((L, N), dt)                                  # d_tau = P_tau / P_ref, formed
+    for t in range(rho + 1, L):                              # from the nearer end so that
+        d[t] = d[t - 1] * w[t]                               # no absolute P is needed
+    for t in range(rho - 1, -1, -1):
+        d[t] = d[t + 1] / w[t + 1]
+    d_prev = np.vstack([d[:1] / w[:1], d[:-1]])             # d_{tau-1}; d_{-1} = 1 / P_ref
+    Ap, Rp, Bp, Kp = a * d_prev, r * d, b / d, k / d
+    Sh = Pr[:, None] * S0
+    with np.errstate(over="ignore", invalid="ignore"):  # entries above the diagonal may
+        M_ab = np.tril(Ap @ Bp.T, -1)                      # overflow; they are dropped
+        M_ak = np.tril(Ap @ Kp.T, -1)
+        M_rb = np.tril(Rp @ Bp.T, 0)
+        M_rk = np.tril(Rp @ Kp.T, 0)
+    Tm = np.linalg.inv(np.eye(L, dtype=dt) - M_ab)
+    X = Ap @ Sh + M_ak @ v
+    Z = Tm @ X
+    Gh = d[-1][:, None] * G_end
+    dZ = Bp @ Gh + M_rb.T @ d_o
+    dX = Tm.T @ dZ
+    dV = Kp @ Gh + M_rk.T @ d_o + M_ak.T @ dX
+    dM_ab = np.tril(dX @ Z.T, -1)
+    dM_ak = np.tril(dX @ v.T, -1)
+    dM_rb = np.tril(d_o @ Z.T, 0)
+    dM_rk = np.tril(d_o @ v.T, 0)
+    dA = dX @ Sh.T + dM_ab @ Bp + dM_ak @ Kp
+    dR = d_o @ Sh.T + dM_rb @ Bp + dM_rk @ Kp
+    dBz, dKv = Z @ Gh.T, v @ Gh.T
+    dB = dBz + dM_ab.T @ Ap + dM_rb.T @ Rp
+    dK = dKv + dM_ak.T @ Ap + dM_rk.T @ Rp
+    # the direct decay gradient: the quantities G^ z_s, G^ v_s, S^ dO_s, S^ dX_s per key
+    # (the first terms of dB', dK', dR', dA') and the token-pair dot products
+    dR0, dA0 = d_o @ Sh.T, dX @ Sh.T
+    W1, W2, W3, W4 = d_o @ Z.T, d_o @ v.T, dX @ Z.T, dX @ v.T
+    wdw = np.zeros((L, N), dt)
+    base = (Gh * Sh).sum(axis=1)
+    for t in range(L):
+        acc = base.copy()
+        for u in range(t):
+            acc += Bp[u] * dBz[u] + Kp[u] * dKv[u]
+        for s_ in range(t, L):
+            acc += Rp[s_] * dR0[s_]
+            for u in range(t):
+                acc += Rp[s_] * (Bp[u] * W1[s_, u] + Kp[u] * W2[s_, u])
+        for s_ in range(t + 1, L):
+            acc += Ap[s_] * dA0[s_]
+            for u in range(t):
+                acc += Ap[s_] * (Bp[u] * W3[s_, u] + Kp[u] * W4[s_, u])
+        wdw[t] = acc
+    dw = wdw / w
+    return {"dr": dR * d, "dk": dK / d, "da": dA * d_prev, "db": dB / d, "dv": dV, "dw": dw}
