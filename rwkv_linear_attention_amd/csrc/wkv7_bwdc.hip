@@ -67,29 +67,45 @@ __device__ __forceinline__ f32x4 load4w(const uint16_t *p)
 }
 
 // ---------------------------------------------------------------------------------
-// The gradient chain.  The value columns of G evolve independently, so each head runs
-// as two workgroups of 32 columns.  A workgroup has NW waves; lane l holds column
-// 32 h + (l & 31) of its half h and, with l >= 32 taking the second four, key rows
-// 8 g + 4 (l >> 5) .. + 3 of wave g.  Per token, c = G^T b is a sum over the key rows:
-// in-lane over four rows, across the two lane halves (a half-wave swap), then over the
-// waves through LDS (double-buffered, one barrier per token).  A chunk's r, w, a, b (per
-// key) and dO (the half's columns) are staged in LDS, loaded into registers one chunk
-// ahead; a token's rows are read right after the barrier of the token before.
-constexpr int GNW = 8, GRW = 4, GCOL = kN / 2;
+// The gradient chain.  The value columns of G evolve independently: each head runs as
+// two workgroups of 32 columns, four waves of 8 columns each.  Lane (rg, cg) of a wave,
+// rg = lane % 16 and cg = lane / 16, holds key rows 4 rg .. 4 rg + 3 of the wave's
+// columns 2 cg and 2 cg + 1.  Per token, c = G^T b is a sum over the key rows: in-lane
+// over four rows, then over the 16 lanes of the lane's DPP row (the other rows of the
+// same columns) -- inside the wave, so the token loop has no barrier and the waves run
+// independently.  A chunk's r, w, a, b (per key) and dO (the workgroup's columns) are
+// staged in LDS, loaded into registers one chunk ahead; each lane reads its four keys'
+// values and its two columns' dO, one token ahead of their use.
+constexpr int GNW = 4, GCOL = 32;
 
 template <typename Tin>
 struct ChainStage {
-    // 16-byte pieces: 4 key-side tensors x 16 tokens x 64 channels, then dO 16 x 32 (fp32)
+    // 16-byte pieces: 4 key-side tensors x 16 tokens x 64 channels (KPT per thread, tensor
+    // after tensor, so a wave's pieces lie in one tensor), then dO 16 x 32 fp32 (one per
+    // thread: 128 pieces, the second 128 threads load and store them again)
     static constexpr int EPP = 16 / sizeof(Tin);
-    static constexpr int KP = 4 * CC * kN / EPP;
-    static constexpr int DP = CC * GCOL / 4;
-    static constexpr int PPT = (KP + DP + GNW * 64 - 1) / (GNW * 64);
+    static constexpr int PPTEN = CC * kN / EPP;   // pieces per tensor
+    static constexpr int KPT = 4 * PPTEN / (GNW * 64);
+    static_assert(KPT * GNW * 64 == 4 * PPTEN && PPTEN % 64 == 0, "whole waves per tensor");
+    static_assert(CC * GCOL / 4 == 128, "one dO piece per thread, twice");
 };
+
+#define GLOBAL_AS __attribute__((address_space(1)))
+typedef unsigned long long u64;
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// x or y by a per-lane condition the compiler cannot see through (so it selects the
+// values and does not build a table of them)
+__device__ __forceinline__ u64 pick(bool f, u64 x, u64 y)
+{
+    unsigned m = f;
+    asm volatile("" : "+v"(m));
+    return m ? x : y;
+}
 
 struct ChainSmem {
     float in[2][4][CC][kN];   // r, w, a, b of a chunk (two chunks in turn)
-    float dout[2][CC][GCOL];  // dO at the half's columns
-    float part[2][GNW][GCOL]; // per-wave partial sums of c
+    float dout[2][CC][GCOL];  // dO at the workgroup's columns
 };
 
 template <typename Tin, bool HAS_DOUT>
@@ -97,75 +113,97 @@ __global__ __launch_bounds__(GNW * 64) void wkv7_bwdc_chain_kernel(BwdArgs p)
 {
     using SG = ChainStage<Tin>;
     __shared__ alignas(16) ChainSmem sm;
-    const int lane = threadIdx.x & 63, jl = lane & 31, rh = lane >> 5;
-    const int g = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63, rg = lane & 15, cg = lane >> 4;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int bh = blockIdx.x >> 1, half = blockIdx.x & 1;
     const int H = p.H, T = p.T;
     const int bb = bh / H, hh = bh - bb * H;
     const int nck = (T + CC - 1) / CC;
-    const int j = half * GCOL + jl;  // this lane's column
-    const int r0 = g * 8 + rh * GRW; // this lane's first key row
+    const int jw = wv * 8 + cg * 2;        // this lane's first column within the workgroup's
+    const int j = half * GCOL + jw;        // ... and within the head's
+    const int r0 = 4 * rg;                 // this lane's first key row
     const size_t tok_e = static_cast<size_t>(H) * kN;
     const size_t head_e = static_cast<size_t>(bb) * T * tok_e + static_cast<size_t>(hh) * kN;
     const size_t sbase = static_cast<size_t>(bh) * (kN * kN) + static_cast<size_t>(r0) * kN + j;
-    const Tin *const kin[4] = {static_cast<const Tin *>(p.r), static_cast<const Tin *>(p.w),
-                               static_cast<const Tin *>(p.a), static_cast<const Tin *>(p.b)};
-    float *const gout[4] = {p.dr, p.dk, p.da, p.db};
-
-    float G[GRW];
+    float G[4][2];  // rows r0 + u, columns j, j + 1
 #pragma unroll
-    for (int u = 0; u < GRW; ++u)
-        G[u] = HAS_DOUT ? p.d_state_out[sbase + u * kN] : 0.0f;
+    for (int u = 0; u < 4; ++u) {
+        const float2 x = HAS_DOUT ? *reinterpret_cast<const float2 *>(&p.d_state_out[sbase + u * kN])
+                                  : make_float2(0.f, 0.f);
+        G[u][0] = x.x;
+        G[u][1] = x.y;
+    }
+    auto put = [&](float *dst) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            *reinterpret_cast<float2 *>(dst + u * kN) = make_float2(G[u][0], G[u][1]);
+    };
     if (T == 0) {  // no tokens: the gradient passes through
-#pragma unroll
-        for (int u = 0; u < GRW; ++u)
-            p.d_state_in[sbase + u * kN] = G[u];
+        put(p.d_state_in + sbase);
         return;
     }
 
-    // staging of chunk c: piece q of the thread is n = tid + q * 512; tokens are clamped
-    // into the sequence (past T they are never read)
-    f32x4 stg[SG::PPT][SG::EPP / 4];
+    // staging of chunk c, without a branch: key-side piece n = tid + 256 q lies in tensor
+    // n / PPTEN (uniform over the wave); tokens are clamped into the sequence (past T
+    // they are never read)
+    auto tensor = [&](int x) -> u64 {  // x is a constant after unrolling
+        return reinterpret_cast<u64>(x == 0 ? p.r : x == 1 ? p.w : x == 2 ? p.a : p.b);
+    };
+    constexpr int WPT = SG::PPTEN / 64;  // waves per tensor in one slot
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    u32x4 stg[SG::KPT], sdo;  // raw bits: widened when stored to LDS, so no load is waited for early
     auto stage_load = [&](int c) {
 #pragma unroll
-        for (int q = 0; q < SG::PPT; ++q) {
-            const int n = static_cast<int>(threadIdx.x) + q * GNW * 64;
-            if (n < SG::KP) {
-                const int ten = n / (CC * kN / SG::EPP), rem = n % (CC * kN / SG::EPP);
-                const int tau = rem / (kN / SG::EPP), col = (rem % (kN / SG::EPP)) * SG::EPP;
-                const int t = min(c * CC + tau, T - 1);
-                const Tin *src = kin[ten] + head_e + static_cast<size_t>(t) * tok_e + col;
-#pragma unroll
-                for (int h4 = 0; h4 < SG::EPP / 4; ++h4)
-                    stg[q][h4] = load4w(src + 4 * h4);
-            } else if (n < SG::KP + SG::DP) {
-                const int m = n - SG::KP, tau = m / (GCOL / 4), col = (m % (GCOL / 4)) * 4;
-                const int t = min(c * CC + tau, T - 1);
-                stg[q][0] = load4w(p.d_o + head_e + static_cast<size_t>(t) * tok_e + half * GCOL + col);
-            }
+        for (int q = 0; q < SG::KPT; ++q) {
+            const int n = static_cast<int>(threadIdx.x) + q * GNW * 64, rem = n % SG::PPTEN;
+            const int tau = rem / (kN / SG::EPP), col = (rem % (kN / SG::EPP)) * SG::EPP;
+            const int t = min(c * CC + tau, T - 1);
+            // slot q's first tensor is a constant; the wave's is that one or the next
+            constexpr int per_slot = GNW / WPT;
+            const int ten0 = q * per_slot;
+            const u64 base = (per_slot > 1 && wv >= WPT) ? tensor(ten0 + 1) : tensor(ten0);
+            const GLOBAL_AS Tin *src = reinterpret_cast<const GLOBAL_AS Tin *>(base) + head_e +
+                                       static_cast<size_t>(t) * tok_e + col;
+            stg[q] = *reinterpret_cast<const GLOBAL_AS u32x4 *>(src);
         }
+        const int m = threadIdx.x & 127, tau = m / (GCOL / 4), col = (m % (GCOL / 4)) * 4;
+        const int t = min(c * CC + tau, T - 1);
+        sdo = *reinterpret_cast<const GLOBAL_AS u32x4 *>(reinterpret_cast<const GLOBAL_AS float *>(
+                                                              reinterpret_cast<u64>(p.d_o)) +
+                                                          head_e + static_cast<size_t>(t) * tok_e + half * GCOL + col);
     };
     auto stage_store = [&](int c) {
         const int bsel = c & 1;
 #pragma unroll
-        for (int q = 0; q < SG::PPT; ++q) {
+        for (int q = 0; q < SG::KPT; ++q) {
             const int n = static_cast<int>(threadIdx.x) + q * GNW * 64;
-            if (n < SG::KP) {
-                const int ten = n / (CC * kN / SG::EPP), rem = n % (CC * kN / SG::EPP);
-                const int tau = rem / (kN / SG::EPP), col = (rem % (kN / SG::EPP)) * SG::EPP;
+            const int ten = n / SG::PPTEN, rem = n % SG::PPTEN;
+            const int tau = rem / (kN / SG::EPP), col = (rem % (kN / SG::EPP)) * SG::EPP;
+            float *const dst = &sm.in[bsel][ten][tau][col];
+            if constexpr (sizeof(Tin) == 2) {
 #pragma unroll
-                for (int h4 = 0; h4 < SG::EPP / 4; ++h4)
-                    *reinterpret_cast<f32x4 *>(&sm.in[bsel][ten][tau][col + 4 * h4]) = stg[q][h4];
-            } else if (n < SG::KP + SG::DP) {
-                const int m = n - SG::KP, tau = m / (GCOL / 4), col = (m % (GCOL / 4)) * 4;
-                *reinterpret_cast<f32x4 *>(&sm.dout[bsel][tau][col]) = stg[q][0];
+                for (int h = 0; h < 2; ++h)
+                    *reinterpret_cast<f32x4 *>(dst + 4 * h) =
+                        f32x4{__uint_as_float(stg[q][2 * h] << 16), __uint_as_float(stg[q][2 * h] & 0xffff0000u),
+                              __uint_as_float(stg[q][2 * h + 1] << 16),
+                              __uint_as_float(stg[q][2 * h + 1] & 0xffff0000u)};
+            } else {
+                *reinterpret_cast<u32x4 *>(dst) = stg[q];
             }
         }
+        const int m = threadIdx.x & 127, tau = m / (GCOL / 4), col = (m % (GCOL / 4)) * 4;
+        *reinterpret_cast<u32x4 *>(&sm.dout[bsel][tau][col]) = sdo;
     };
-    // a token's rows of r, w, a, b (this lane's four keys) and its dO
+    // G_end goes to tensor r0 / 16 of dr, dk, da, db: a per-lane choice, made once
+    const int sidx = r0 / CC;
+    const u64 gbase = pick(sidx == 0, reinterpret_cast<u64>(p.dr),
+                           pick(sidx == 1, reinterpret_cast<u64>(p.dk),
+                                pick(sidx == 2, reinterpret_cast<u64>(p.da), reinterpret_cast<u64>(p.db))));
+    GLOBAL_AS float *const gdst = reinterpret_cast<GLOBAL_AS float *>(gbase) + head_e + (r0 % CC) * tok_e + j;
+    // a token's r, w, a, b at this lane's four keys and dO at its two columns
     struct Tok {
         f32x4 r, w, a, b;
-        float d;
+        float2 d;
     };
     auto read_tok = [&](int bsel, int tau) {
         Tok x;
@@ -173,52 +211,42 @@ __global__ __launch_bounds__(GNW * 64) void wkv7_bwdc_chain_kernel(BwdArgs p)
         x.w = *reinterpret_cast<const f32x4 *>(&sm.in[bsel][1][tau][r0]);
         x.a = *reinterpret_cast<const f32x4 *>(&sm.in[bsel][2][tau][r0]);
         x.b = *reinterpret_cast<const f32x4 *>(&sm.in[bsel][3][tau][r0]);
-        x.d = sm.dout[bsel][tau][jl];
+        x.d = *reinterpret_cast<const float2 *>(&sm.dout[bsel][tau][jw]);
         return x;
     };
 
     stage_load(nck - 1);
     stage_store(nck - 1);
     __syncthreads();
-    int par = 0;
     for (int c = nck - 1; c >= 0; --c) {
         const int bsel = c & 1;
         if (c > 0)
             stage_load(c - 1);  // in flight during this chunk
         if (c < nck - 1) {
             // G_end of chunk c: key row 16 s + tau goes to token 16 c + tau of tensor s
+            GLOBAL_AS float *const dst = gdst + static_cast<size_t>(c * CC) * tok_e;
 #pragma unroll
-            for (int u = 0; u < GRW; ++u) {
-                const int row = r0 + u;
-                gout[row / CC][head_e + static_cast<size_t>(c * CC + row % CC) * tok_e + j] = G[u];
-            }
+            for (int u = 0; u < 4; ++u)
+                *reinterpret_cast<GLOBAL_AS f32x2 *>(dst + u * tok_e) = f32x2{G[u][0], G[u][1]};
         }
         const int t_hi = min(T, (c + 1) * CC) - 1, t_lo = c * CC;
         Tok cur = read_tok(bsel, t_hi - t_lo);
         for (int t = t_hi; t >= t_lo; --t) {
+            const Tok nxt = read_tok(bsel, max(t - 1 - t_lo, 0));
             float pc0 = 0.f, pc1 = 0.f;
 #pragma unroll
-            for (int u = 0; u < GRW; u += 2) {
-                G[u] = fmaf(cur.r[u], cur.d, G[u]);
-                G[u + 1] = fmaf(cur.r[u + 1], cur.d, G[u + 1]);
-                pc0 = fmaf(cur.b[u], G[u], pc0);
-                pc1 = fmaf(cur.b[u + 1], G[u + 1], pc1);
+            for (int u = 0; u < 4; ++u) {
+                G[u][0] = fmaf(cur.r[u], cur.d.x, G[u][0]);
+                G[u][1] = fmaf(cur.r[u], cur.d.y, G[u][1]);
+                pc0 = fmaf(cur.b[u], G[u][0], pc0);
+                pc1 = fmaf(cur.b[u], G[u][1], pc1);
             }
-            float pc = pc0 + pc1;
-            // the other half of the wave holds the other four rows of this column
-            pc += __shfl_xor(pc, 32);
-            if (rh == 0)
-                sm.part[par][g][jl] = pc;
-            __syncthreads();
-            const Tok nxt = read_tok(bsel, max(t - 1 - t_lo, 0));
-            float cj = sm.part[par][0][jl];
+            const float c0 = group16_sum(pc0), c1 = group16_sum(pc1);
 #pragma unroll
-            for (int gg = 1; gg < GNW; ++gg)
-                cj += sm.part[par][gg][jl];
-            par ^= 1;
-#pragma unroll
-            for (int u = 0; u < GRW; ++u)
-                G[u] = fmaf(cur.w[u], G[u], cur.a[u] * cj);
+            for (int u = 0; u < 4; ++u) {
+                G[u][0] = fmaf(cur.w[u], G[u][0], cur.a[u] * c0);
+                G[u][1] = fmaf(cur.w[u], G[u][1], cur.a[u] * c1);
+            }
             cur = nxt;
         }
         if (c > 0) {
@@ -226,9 +254,7 @@ __global__ __launch_bounds__(GNW * 64) void wkv7_bwdc_chain_kernel(BwdArgs p)
             __syncthreads();
         }
     }
-#pragma unroll
-    for (int u = 0; u < GRW; ++u)
-        p.d_state_in[sbase + u * kN] = G[u];
+    put(p.d_state_in + sbase);
 }
 
 // ---------------------------------------------------------------------------------
@@ -394,50 +420,56 @@ __global__ __launch_bounds__(256) void wkv7_bwdc_chunk_kernel(BwdArgs p, int c_l
     const size_t head_e = static_cast<size_t>(bb) * T * tok_e + static_cast<size_t>(hh) * kN;
     auto rowp = [&](int tau) { return head_e + static_cast<size_t>(t0 + min(tau, L - 1)) * tok_e; };
 
-    // ---- load: inputs (tokens past the end as identity steps: w = 1, the rest 0),
-    // dO, the checkpoint and G_end
+    // ---- load: inputs (tokens past the end as identity steps: w = 1, the rest 0), dO,
+    // the checkpoint and G_end -- every global load is issued before the first is used
     {
         const int tau = tid >> 4, col = (tid & 15) * 4;
         const bool live = tau < L;
         const Tin *const srcs[6] = {static_cast<const Tin *>(p.r), static_cast<const Tin *>(p.w),
                                     static_cast<const Tin *>(p.k), static_cast<const Tin *>(p.v),
                                     static_cast<const Tin *>(p.a), static_cast<const Tin *>(p.b)};
+        f32x4 in4[6], o4;
+#pragma unroll
+        for (int x = 0; x < 6; ++x)
+            in4[x] = load4w(srcs[x] + rowp(tau) + col);
+        o4 = load4w(p.d_o + rowp(tau) + col);
+        // the checkpoint and G_end, row i, columns j0 .. j0 + 15 (a missing d_state_out
+        // reads the checkpoint and is zeroed), through global pointers
+        const int i = tid >> 2, j0 = (tid & 3) * 16;
+        const u64 s0 = reinterpret_cast<u64>(p.ckpt) +
+                       4ull * (((static_cast<size_t>(bb) * nck + c) * H + hh) * (kN * kN) + i * kN + j0);
+        const bool inner = c < nck - 1, has_g = inner || p.d_state_out != nullptr;
+        const int sidx = i / CC;  // G_end rows of an inner chunk sit in dr, dk, da, db
+        const u64 gin = pick(sidx == 0, reinterpret_cast<u64>(p.dr),
+                             pick(sidx == 1, reinterpret_cast<u64>(p.dk),
+                                  pick(sidx == 2, reinterpret_cast<u64>(p.da), reinterpret_cast<u64>(p.db)))) +
+                        4ull * (head_e + static_cast<size_t>(t0 + i % CC) * tok_e + j0);
+        const u64 gend = reinterpret_cast<u64>(p.d_state_out) +
+                         4ull * (static_cast<size_t>(bh) * (kN * kN) + i * kN + j0);
+        const u64 ge = inner ? gin : (p.d_state_out ? gend : s0);
+        f32x4 s4[4], g4[4];
+#pragma unroll
+        for (int h4 = 0; h4 < 4; ++h4) {
+            s4[h4] = *reinterpret_cast<const GLOBAL_AS f32x4 *>(s0 + 16u * h4);
+            g4[h4] = *reinterpret_cast<const GLOBAL_AS f32x4 *>(ge + 16u * h4);
+        }
 #pragma unroll
         for (int x = 0; x < 6; ++x) {
-            f32x4 v4 = load4w(srcs[x] + rowp(tau) + col);
-            if (!live)
-                v4 = x == X_W ? f32x4{1.f, 1.f, 1.f, 1.f} : f32x4{0.f, 0.f, 0.f, 0.f};
+            const f32x4 v4 = live ? in4[x] : (x == X_W ? f32x4{1.f, 1.f, 1.f, 1.f} : f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 sm.rows[x][tau][col + e] = v4[e];
         }
-        f32x4 o4 = load4w(p.d_o + rowp(tau) + col);
-        if (!live)
-            o4 = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-            sm.rows[X_DO][tau][col + e] = o4[e];
-    }
-    {
-        const int i = tid >> 2, j0 = (tid & 3) * 16;
-        const float *s0 = p.ckpt + ((static_cast<size_t>(bb) * nck + c) * H + hh) * (kN * kN) + i * kN + j0;
-        const float *ge = nullptr;
-        if (c < nck - 1) {
-            const float *const gsrc[4] = {p.dr, p.dk, p.da, p.db};
-            ge = gsrc[i / CC] + head_e + static_cast<size_t>(t0 + i % CC) * tok_e + j0;
-        } else if (p.d_state_out) {
-            ge = p.d_state_out + static_cast<size_t>(bh) * (kN * kN) + i * kN + j0;
-        }
+            sm.rows[X_DO][tau][col + e] = live ? o4[e] : 0.f;
 #pragma unroll
-        for (int h4 = 0; h4 < 4; ++h4) {
-            const f32x4 s4 = *reinterpret_cast<const f32x4 *>(s0 + 4 * h4);
-            const f32x4 g4 = ge ? *reinterpret_cast<const f32x4 *>(ge + 4 * h4) : f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int h4 = 0; h4 < 4; ++h4)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                sm.sq[0][i][j0 + 4 * h4 + e] = s4[e];
-                sm.sq[1][i][j0 + 4 * h4 + e] = g4[e];
+                sm.sq[0][i][j0 + 4 * h4 + e] = s4[h4][e];
+                sm.sq[1][i][j0 + 4 * h4 + e] = has_g ? g4[h4][e] : 0.f;
             }
-        }
     }
     __syncthreads();
 
