@@ -49,11 +49,13 @@
 #include "wkv7_launch.h"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace wkv7 {
 namespace {
 
 constexpr int CC = 16;                          // chunk length: the checkpoint spacing
+constexpr int kCUs = 256;                       // compute units of the chip
 constexpr int REF = 7;                          // reference position of the decay factors
 constexpr float kExactBelow = 1.0f / 32768.0f;  // 2^-15
 
@@ -636,11 +638,11 @@ __global__ __launch_bounds__(256) void wkv7_bwdc_chunk_kernel(BwdArgs p, int c_l
         float tcol[CC];
 #pragma unroll
         for (int t = 0; t < CC; ++t) {
-            float acc = t == sc ? 1.f : 0.f;
+            float acc[4] = {t == sc ? 1.f : 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int u = 0; u < t; ++u)
-                acc = fmaf(sm.sm[M_AB][t][u], tcol[u], acc);
-            tcol[t] = acc;
+                acc[u & 3] = fmaf(sm.sm[M_AB][t][u], tcol[u], acc[u & 3]);
+            tcol[t] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
         }
         if (lane < 16)  // over M_ab: this wave's reads of it are done (program order)
 #pragma unroll
@@ -730,18 +732,23 @@ __global__ __launch_bounds__(256) void wkv7_bwdc_chunk_kernel(BwdArgs p, int c_l
     for (int e = 0; e < 4; ++e) {
         const int tau = 4 * q + e;
         if (tau < L) {
-            const float d = sm.rows[X_D][tau][tc];
-            const float dp = tau == 0 ? d / sm.rows[X_W][0][tc] : sm.rows[X_D][tau - 1][tc];
+            const float d = sm.rows[X_D][tau][tc], inv = __builtin_amdgcn_rcpf(d);
+            const float dp = tau == 0 ? d * __builtin_amdgcn_rcpf(sm.rows[X_W][0][tc]) : sm.rows[X_D][tau - 1][tc];
             const size_t at = rowp(tau) + tc;
             p.dr[at] = dracc[e] * d;
             p.da[at] = daacc[e] * dp;
-            p.db[at] = dbacc[e] / d;
-            p.dk[at] = dkacc[e] / d;
+            p.db[at] = dbacc[e] * inv;
+            p.dk[at] = dkacc[e] * inv;
         }
     }
 
-    // ---- dw, in its direct form.  Thread (key i, wave g) sums the terms of the s = g
-    // (mod 4) rows for every token t; the four partials meet in LDS (over S^, no longer read).
+    // ---- dw, in its direct form.  With Q_s(t) = sum_{u<t} (B'_u dO_s.z_u + K'_u dO_s.v_u)
+    // and P_s(t) the same with dX_s, per key:
+    //   w_t dw_t = base + sum_{u<t} (B'_u dBz_u + K'_u dKv_u)
+    //            + sum_{s>=t} R'_s (dR0_s + Q_s(t)) + sum_{s>t} A'_s (dA0_s + P_s(t)).
+    // Thread (key i, wave g) forms the Q/P terms of rows s = g (mod 4) for every token;
+    // the four partials meet in LDS (over S^, no longer read).  The dR0, dA0 terms and the
+    // prefix over u are running sums in the final pass.
     __syncthreads();
     {
         const int i = lane, g = wv;
@@ -753,41 +760,320 @@ __global__ __launch_bounds__(256) void wkv7_bwdc_chunk_kernel(BwdArgs p, int c_l
             acc[u] = 0.f;
         }
 #pragma unroll
-        for (int s = 0; s < CC; ++s) {
+        for (int s = 1; s < CC; ++s) {
             if ((s & 3) != g)
                 continue;
             const float rs = sm.rows[X_R][s][i], as = sm.rows[X_A][s][i];
-            const float r0 = sm.rows[X_DR0][s][i], a0 = sm.rows[X_DA0][s][i];
             float qr = 0.f, qa = 0.f;
 #pragma unroll
-            for (int t = 0; t <= s; ++t) {
-                acc[t] = fmaf(rs, r0 + qr, acc[t]);
-                if (t < s)
-                    acc[t] = fmaf(as, a0 + qa, acc[t]);
-                qr = fmaf(bu[t], sm.sm[W_OZ][s][t], fmaf(ku[t], sm.sm[W_OV][s][t], qr));
-                qa = fmaf(bu[t], sm.sm[W_XZ][s][t], fmaf(ku[t], sm.sm[W_XV][s][t], qa));
+            for (int t = 1; t <= s; ++t) {
+                qr = fmaf(bu[t - 1], sm.sm[W_OZ][s][t - 1], fmaf(ku[t - 1], sm.sm[W_OV][s][t - 1], qr));
+                acc[t] = fmaf(rs, qr, acc[t]);
+                if (t < s) {
+                    qa = fmaf(bu[t - 1], sm.sm[W_XZ][s][t - 1], fmaf(ku[t - 1], sm.sm[W_XV][s][t - 1], qa));
+                    acc[t] = fmaf(as, qa, acc[t]);
+                }
             }
         }
         __syncthreads();  // every wave is past its reads of S^
         float *part = &sm.sq[0][0][0];  // [4][16][64]
 #pragma unroll
-        for (int t = 0; t < CC; ++t)
+        for (int t = 1; t < CC; ++t)
             part[(g * CC + t) * kN + i] = acc[t];
         __syncthreads();
+        // suffix sums of R'_s dR0_s (s >= t) and A'_s dA0_s (s > t), prefix of the base terms
+        float suf[CC];
+        {
+            float sr = 0.f, sa = 0.f;
+#pragma unroll
+            for (int t = CC - 1; t >= 0; --t) {
+                sr = fmaf(sm.rows[X_R][t][i], sm.rows[X_DR0][t][i], sr);
+                suf[t] = sr + sa;
+                sa = fmaf(sm.rows[X_A][t][i], sm.rows[X_DA0][t][i], sa);
+            }
+        }
         float pre = sm.base[i];
 #pragma unroll
         for (int t = 0; t < CC; ++t) {
             if ((t & 3) == g && t < L) {
-                float tot = pre;
+                float tot = pre + suf[t];
+                if (t > 0)
 #pragma unroll
-                for (int gg = 0; gg < 4; ++gg)
-                    tot += part[(gg * CC + t) * kN + i];
-                p.dw[rowp(t) + i] = tot / sm.rows[X_W][t][i];
+                    for (int gg = 0; gg < 4; ++gg)
+                        tot += part[(gg * CC + t) * kN + i];
+                p.dw[rowp(t) + i] = tot * __builtin_amdgcn_rcpf(sm.rows[X_W][t][i]);
             }
             pre = fmaf(bu[t], sm.rows[X_DBZ][t][i], fmaf(ku[t], sm.rows[X_DKV][t][i], pre));
         }
     }
 }
+// ---------------------------------------------------------------------------------
+// The gradient chain in chunk form, on the matrix cores.  One workgroup of four waves
+// per (batch, head); wave wv holds value columns 16 wv .. 16 wv + 15 of G in the
+// accumulator layout: lane (q, n) holds G[16 pt + 4 q + e][16 wv + n] in g[pt][e].
+// Per chunk, last first, with the chunk's factors and matrices formed at its start:
+//     G^ = diag(d_15) G_end,   dZ = B' G^ + M_rb^T dO,   dX = T^T dZ,
+//     G_end of the chunk before = diag(P_7) (G^ + R'^T dO + A'^T dX).
+// In dZ = B' G^ a lane's own rows of G^ are its operand: the sum over the keys runs in
+// the order (pt, q, e) of the accumulator layout, and B' is read in that order.  A chunk
+// with a decay below 2^-15 runs the recurrence token by token instead.
+struct GchainSmem {
+    float raw[4][CC][RS];  // r, w, a, b (identity steps past the end)
+    float der[3][CC][RS];  // A', R', B'
+    float dout[CC][RS];    // dO (zero past the end)
+    float sm[3][CC][SS];   // M_ab, M_rb, T
+    alignas(16) float d15[kN];
+    alignas(16) float p7[kN];
+    int flag;
+};
+enum { G_R, G_W, G_A, G_B };
+enum { D_A, D_R, D_B };
+enum { S_AB, S_RB, S_T };
+
+template <typename Tin, bool HAS_DOUT>
+__global__ __launch_bounds__(256) void wkv7_bwdc_gchain_kernel(BwdArgs p)
+{
+    __shared__ GchainSmem sm;
+    typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+    typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
+    using Raw = typename std::conditional<sizeof(Tin) == 2, u32x2, u32x4v>::type;
+    const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, n = lane & 15;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int bh = blockIdx.x;
+    const int H = p.H, T = p.T;
+    const int bb = bh / H, hh = bh - bb * H;
+    const int nck = (T + CC - 1) / CC;
+    const int col = 16 * wv + n;
+    const size_t tok_e = static_cast<size_t>(H) * kN;
+    const size_t head_e = static_cast<size_t>(bb) * T * tok_e + static_cast<size_t>(hh) * kN;
+    const size_t sbase = static_cast<size_t>(bh) * (kN * kN) + col;
+
+    float g[4][4];
+#pragma unroll
+    for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            g[pt][e] = HAS_DOUT ? p.d_state_out[sbase + (16 * pt + 4 * q + e) * kN] : 0.0f;
+    auto put_state = [&](float *dst) {
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                dst[sbase + (16 * pt + 4 * q + e) * kN] = g[pt][e];
+    };
+    if (T == 0) {  // no tokens: the gradient passes through
+        put_state(p.d_state_in);
+        return;
+    }
+
+    // staging of a chunk: thread (token tid / 16, channels 4 (tid % 16) ..) loads four
+    // elements of r, w, a, b and of dO, kept as raw bits until they are stored to LDS
+    const int s_tau = tid >> 4, s_c4 = (tid & 15) * 4;
+    Raw rin[4];
+    u32x4v rdo;
+    auto stage_load = [&](int c) {
+        const int t0 = c * CC, L = min(CC, T - t0);
+        const size_t off = head_e + static_cast<size_t>(t0 + min(s_tau, L - 1)) * tok_e + s_c4;
+        const Tin *const src[4] = {static_cast<const Tin *>(p.r), static_cast<const Tin *>(p.w),
+                                   static_cast<const Tin *>(p.a), static_cast<const Tin *>(p.b)};
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+            rin[x] = *reinterpret_cast<const GLOBAL_AS Raw *>(
+                reinterpret_cast<const GLOBAL_AS Tin *>(reinterpret_cast<u64>(src[x])) + off);
+        rdo = *reinterpret_cast<const GLOBAL_AS u32x4v *>(
+            reinterpret_cast<const GLOBAL_AS float *>(reinterpret_cast<u64>(p.d_o)) + off);
+    };
+    auto stage_store = [&](int c) {
+        const bool live = s_tau < min(CC, T - c * CC);
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            f32x4 v4;
+            if constexpr (sizeof(Tin) == 2)
+                v4 = f32x4{__uint_as_float(rin[x][0] << 16), __uint_as_float(rin[x][0] & 0xffff0000u),
+                           __uint_as_float(rin[x][1] << 16), __uint_as_float(rin[x][1] & 0xffff0000u)};
+            else
+                v4 = f32x4{__uint_as_float(rin[x][0]), __uint_as_float(rin[x][1]), __uint_as_float(rin[x][2]),
+                           __uint_as_float(rin[x][3])};
+            if (!live)
+                v4 = x == G_W ? f32x4{1.f, 1.f, 1.f, 1.f} : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                sm.raw[x][s_tau][s_c4 + e] = v4[e];
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            sm.dout[s_tau][s_c4 + e] = live ? __uint_as_float(rdo[e]) : 0.f;
+    };
+
+    stage_load(nck - 1);
+    for (int c = nck - 1; c >= 0; --c) {
+        stage_store(c);
+        __syncthreads();
+        if (c > 0)
+            stage_load(c - 1);  // in flight during this chunk
+        // ---- the chunk's factors and A', R', B' (wave 0, one key per lane)
+        if (wv == 0) {
+            const int i = lane;
+            float wc[CC];
+            float wmin = 1.0f;
+#pragma unroll
+            for (int tau = 0; tau < CC; ++tau) {
+                wc[tau] = sm.raw[G_W][tau][i];
+                wmin = fminf(wmin, fabsf(wc[tau]));
+            }
+            const bool exact = __ballot(!(wmin >= kExactBelow)) != 0ull;  // NaN included
+            if (lane == 0)
+                sm.flag = exact ? 1 : 0;
+            if (!exact) {
+                float d[CC];
+                d[REF] = 1.0f;
+#pragma unroll
+                for (int tau = REF + 1; tau < CC; ++tau)
+                    d[tau] = d[tau - 1] * wc[tau];
+#pragma unroll
+                for (int tau = REF - 1; tau >= 0; --tau)
+                    d[tau] = d[tau + 1] * __builtin_amdgcn_rcpf(wc[tau + 1]);
+                float pr = wc[0];
+#pragma unroll
+                for (int tau = 1; tau <= REF; ++tau)
+                    pr *= wc[tau];
+                sm.p7[i] = pr;
+                sm.d15[i] = d[CC - 1];
+#pragma unroll
+                for (int tau = 0; tau < CC; ++tau) {
+                    const float dp = tau == 0 ? d[0] * __builtin_amdgcn_rcpf(wc[0]) : d[tau - 1];
+                    sm.der[D_A][tau][i] = sm.raw[G_A][tau][i] * dp;
+                    sm.der[D_R][tau][i] = sm.raw[G_R][tau][i] * d[tau];
+                    sm.der[D_B][tau][i] = sm.raw[G_B][tau][i] * __builtin_amdgcn_rcpf(d[tau]);
+                }
+            }
+        }
+        __syncthreads();
+        if (sm.flag) {
+            // the recurrence over the chunk's tokens, wave-local: c = G^T b sums the lane's
+            // sixteen keys, then the four lanes of the column (lanes n + 16 q)
+            const int L = min(CC, T - c * CC);
+            for (int t = L - 1; t >= 0; --t) {
+                const float dj = sm.dout[t][col];
+                float cs = 0.f;
+#pragma unroll
+                for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int key = 16 * pt + 4 * q + e;
+                        g[pt][e] = fmaf(sm.raw[G_R][t][key], dj, g[pt][e]);
+                        cs = fmaf(sm.raw[G_B][t][key], g[pt][e], cs);
+                    }
+                cs += __shfl_xor(cs, 16);
+                cs += __shfl_xor(cs, 32);
+#pragma unroll
+                for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int key = 16 * pt + 4 * q + e;
+                        g[pt][e] = fmaf(sm.raw[G_W][t][key], g[pt][e], sm.raw[G_A][t][key] * cs);
+                    }
+            }
+        } else {
+            const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+            // G^ = diag(d_15) G
+            float gh[4][4];
+#pragma unroll
+            for (int pt = 0; pt < 4; ++pt) {
+                const f32x4 d4 = *reinterpret_cast<const f32x4 *>(&sm.d15[16 * pt + 4 * q]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    gh[pt][e] = g[pt][e] * d4[e];
+            }
+            // M_ab = tril(A' B'^T, -1) (wave 0), M_rb = tril(R' B'^T) (wave 1)
+            if (wv < 2) {
+                const int xa = wv == 0 ? D_A : D_R;
+                f32x4 acc = zero4;
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    acc = mfma4(sm.der[xa][n][16 * q + i], sm.der[D_B][n][16 * q + i], acc);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int tau = 4 * q + e;
+                    const bool keep = wv == 0 ? n < tau : n <= tau;
+                    sm.sm[wv == 0 ? S_AB : S_RB][tau][n] = keep ? acc[e] : 0.f;
+                }
+            }
+            // dZ = B' G^ (keys in the accumulator order)
+            f32x4 dz0 = zero4, dz1 = zero4;
+#pragma unroll
+            for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float a = sm.der[D_B][n][16 * pt + 4 * q + e];
+                    if (pt & 1)
+                        dz1 = mfma4(a, gh[pt][e], dz1);
+                    else
+                        dz0 = mfma4(a, gh[pt][e], dz0);
+                }
+            f32x4 dz = dz0 + dz1;
+            __syncthreads();
+            // dZ += M_rb^T dO; T = (I - M_ab)^{-1} (wave 0, a column per lane: T = I + M_ab T)
+            float dob[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                dob[i] = sm.dout[4 * q + i][col];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                dz = mfma4(sm.sm[S_RB][4 * q + i][n], dob[i], dz);
+            if (wv == 0) {
+                const int sc = lane & 15;
+                float tcol[CC];
+#pragma unroll
+                for (int t = 0; t < CC; ++t) {
+                    float acc[4] = {t == sc ? 1.f : 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int u = 0; u < t; ++u)
+                        acc[u & 3] = fmaf(sm.sm[S_AB][t][u], tcol[u], acc[u & 3]);
+                    tcol[t] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+                }
+                if (lane < 16)
+#pragma unroll
+                    for (int t = 0; t < CC; ++t)
+                        sm.sm[S_T][t][sc] = tcol[t];
+            }
+            __syncthreads();
+            // dX = T^T dZ (the B operand is this lane's own rows of dZ)
+            f32x4 dx = zero4;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                dx = mfma4(sm.sm[S_T][4 * q + i][n], dz[i], dx);
+            // G_end of the chunk before = diag(P_7) (G^ + R'^T dO + A'^T dX), tile by tile
+#pragma unroll
+            for (int pt = 0; pt < 4; ++pt) {
+                f32x4 acc = {gh[pt][0], gh[pt][1], gh[pt][2], gh[pt][3]};
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    acc = mfma4(sm.der[D_R][4 * q + i][16 * pt + n], dob[i], acc);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    acc = mfma4(sm.der[D_A][4 * q + i][16 * pt + n], dx[i], acc);
+                const f32x4 p4 = *reinterpret_cast<const f32x4 *>(&sm.p7[16 * pt + 4 * q]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    g[pt][e] = acc[e] * p4[e];
+            }
+        }
+        if (c > 0) {
+            // G_end of chunk c - 1: key row 16 pt + 4 q + e goes to token 16 (c - 1) + 4 q + e
+            // of tensor pt (dr, dk, da, db)
+            float *const outs[4] = {p.dr, p.dk, p.da, p.db};
+#pragma unroll
+            for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    outs[pt][head_e + static_cast<size_t>((c - 1) * CC + 4 * q + e) * tok_e + col] = g[pt][e];
+        }
+        __syncthreads();  // the chunk's LDS is read no more
+    }
+    put_state(p.d_state_in);
+}
+
 template <typename Tin>
 hipError_t launch_bwdc_t(const BwdArgs &p, hipStream_t stream)
 {
@@ -796,11 +1082,21 @@ hipError_t launch_bwdc_t(const BwdArgs &p, hipStream_t stream)
     if (nck > 0)  // every head's last chunk: G_end is d_state_out
         hipLaunchKernelGGL(wkv7_bwdc_chunk_kernel<Tin>, dim3(static_cast<unsigned>(nbh)), dim3(256), 0, stream, p,
                            nck - 1, nbh);
-    const dim3 cgrid(2 * static_cast<unsigned>(nbh));  // two workgroups (column halves) per head
-    if (p.d_state_out)
-        hipLaunchKernelGGL((wkv7_bwdc_chain_kernel<Tin, true>), cgrid, dim3(GNW * 64), 0, stream, p);
-    else
-        hipLaunchKernelGGL((wkv7_bwdc_chain_kernel<Tin, false>), cgrid, dim3(GNW * 64), 0, stream, p);
+    // the chain: with few heads, the token recurrence in two workgroups per head (more
+    // waves in flight); otherwise the chunk form on the matrix cores, a workgroup per head
+    if (2 * nbh <= kCUs) {
+        const dim3 cgrid(2 * static_cast<unsigned>(nbh));
+        if (p.d_state_out)
+            hipLaunchKernelGGL((wkv7_bwdc_chain_kernel<Tin, true>), cgrid, dim3(GNW * 64), 0, stream, p);
+        else
+            hipLaunchKernelGGL((wkv7_bwdc_chain_kernel<Tin, false>), cgrid, dim3(GNW * 64), 0, stream, p);
+    } else if (p.d_state_out) {
+        hipLaunchKernelGGL((wkv7_bwdc_gchain_kernel<Tin, true>), dim3(static_cast<unsigned>(nbh)), dim3(256), 0,
+                           stream, p);
+    } else {
+        hipLaunchKernelGGL((wkv7_bwdc_gchain_kernel<Tin, false>), dim3(static_cast<unsigned>(nbh)), dim3(256), 0,
+                           stream, p);
+    }
     // the other chunks, at most 2^30 workgroups per launch
     const int per = static_cast<int>(std::max<long long>(1, (1ll << 30) / nbh));
     for (int c0 = 0; c0 < nck - 1; c0 += per) {

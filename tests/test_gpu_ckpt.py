@@ -121,14 +121,16 @@ def test_backward_ckpt_longer_sequence_every_head(K, oracle_mod):
     grads_vs_oracle(K, oracle_mod, inp, d_o, d_so, f"B={B} T={T} H={H}")
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_backward_ckpt_tiny_decays(K, oracle_mod, dtype):
-    # chunks with w = 0 and w = 1e-3 (the forward's exact path) among ordinary ones
-    B, T, H = 2, 70, 3
-    inp = synth.make_inputs(B, T, H, 64, seed=4700, dtype=dtype, state_std=0.1)
+@pytest.mark.parametrize("dtype,B,H", [("f32", 2, 3), ("bf16", 2, 3), ("f32", 1, 129), ("bf16", 1, 129)])
+def test_backward_ckpt_tiny_decays(K, oracle_mod, dtype, B, H):
+    # chunks with w = 0 and w = 1e-3 (the exact paths) among ordinary ones; with few
+    # heads the gradient chain runs token by token, with 129 it runs in chunk form
+    T = 70
+    inp = synth.make_inputs(B, T, H, 64, seed=4700 + H, dtype=dtype, state_std=0.1)
     w = inp["w"].clone()
     w[:, 16:32] = 0.0
-    w[1, 40:44, 2] = 1e-3
+    w[B - 1, 40:44, 2] = 1e-3
+    w[0, 50:52, H - 1] = 2.0 ** -14  # just above the exact-path threshold
     inp["w"] = w.contiguous()
     gen = torch.Generator().manual_seed(4701)
     d_o = torch.randn((B, T, H, 64), generator=gen)
@@ -136,24 +138,25 @@ def test_backward_ckpt_tiny_decays(K, oracle_mod, dtype):
     grads_vs_oracle(K, oracle_mod, inp, d_o, d_so, f"{dtype} tiny decays")
 
 
-def test_backward_ckpt_empty_sequence_and_in_place(K):
-    inp = synth.make_inputs(2, 0, 3, 64, seed=4800, dtype="bf16", state_std=0.1)
+@pytest.mark.parametrize("H", [3, 129])
+def test_backward_ckpt_empty_sequence_and_in_place(K, H):
+    inp = synth.make_inputs(2, 0, H, 64, seed=4800, dtype="bf16", state_std=0.1)
     d = {n: inp[n].cuda() for n in RWKVAB}
     s_in = inp["state_in"].cuda()
     o, s, ck = K.wkv7_forward_ckpt(*(d[n] for n in RWKVAB), s_in)
     torch.cuda.synchronize()
-    assert ck.shape == (2, 0, 3, 64, 64) and torch.equal(s, s_in)
-    d_o = torch.empty((2, 0, 3, 64), device="cuda")
-    d_so = torch.randn((2, 3, 64, 64), device="cuda")
+    assert ck.shape == (2, 0, H, 64, 64) and torch.equal(s, s_in)
+    d_o = torch.empty((2, 0, H, 64), device="cuda")
+    d_so = torch.randn((2, H, 64, 64), device="cuda")
     g = K.wkv7_backward_ckpt(*(d[n] for n in RWKVAB), ck, d_o, d_so)
     torch.cuda.synchronize()
     assert torch.equal(g["d_state_in"], d_so)
     # d_state_in may be d_state_out itself
-    inp = synth.make_inputs(1, 40, 2, 64, seed=4801, dtype="bf16", state_std=0.1)
+    inp = synth.make_inputs(1, 40, H, 64, seed=4801, dtype="bf16", state_std=0.1)
     d = {n: inp[n].cuda() for n in RWKVAB}
     _, _, ck = K.wkv7_forward_ckpt(*(d[n] for n in RWKVAB), inp["state_in"].cuda())
-    d_o = torch.randn((1, 40, 2, 64), device="cuda")
-    d_so = torch.randn((1, 2, 64, 64), device="cuda")
+    d_o = torch.randn((1, 40, H, 64), device="cuda")
+    d_so = torch.randn((1, H, 64, 64), device="cuda")
     ref = K.wkv7_backward_ckpt(*(d[n] for n in RWKVAB), ck, d_o, d_so.clone())
     grads = {n: torch.empty_like(ref[n]) for n in NAMES}
     grads["d_state_in"] = d_so
