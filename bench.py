@@ -61,7 +61,7 @@ def recurrent_flops(wl) -> int:
 def kernel_source_hash(kind: str) -> str:
     name = {"step": "wkv7_step.hip", "verify": "wkv7_step.hip", "chunk": "wkv7_chunk.hip", "chunk_tail": "wkv7_chunk.hip",
             "chunk_ckpt": "wkv7_chunk.hip", "step_tail": "wkv7_step.hip", "tail_pass": "wkv7_tail.hip",
-            "bwd_ckpt": "wkv7_bwd.hip", "bwd": "wkv7_bwd.hip", "bwd_zero": "wkv7_bwd.hip",
+            "bwd_ckpt": "wkv7_bwdc.hip", "bwd": "wkv7_bwd.hip", "bwd_zero": "wkv7_bwd.hip",
             "commit": "wkv7_step.hip"}[kind]
     h = hashlib.sha256()
     for f in (name, "wkv7_device.h"):
@@ -71,10 +71,11 @@ def kernel_source_hash(kind: str) -> str:
 
 
 def call_kernels(kind: str, workload: int):
-    """The kernels one call of `kind` runs on `workload`: the backward pass with two
-    workgroups per head (at most 128 heads) first zeroes the outputs they add into
-    ("bwd_zero")."""
-    if kind in ("bwd_ckpt", "bwd"):
+    """The kernels one call of `kind` runs on `workload`: the backward pass from
+    per-position states with two workgroups per head (at most 128 heads) first zeroes
+    the outputs they add into ("bwd_zero").  The backward from checkpoints ("bwd_ckpt")
+    counts its three launches (chunk kernel, chain, chunk kernel) together."""
+    if kind == "bwd":
         import synth
         wl = synth.WORKLOADS[workload]
         return (kind, "bwd_zero") if wl.B * wl.H * 2 <= 256 else (kind,)

@@ -14,7 +14,8 @@
 //     G     = diag(w_t) G + a_t c^T
 // and the gradient of the input state is the last G.  The states S_t are an
 // input (the per-position states the step kernel writes), so nothing is
-// rebuilt: with 288 GB of HBM the states of long sequences fit.
+// rebuilt: with 288 GB of HBM the states of long sequences fit.  (The backward
+// from chunk checkpoints, which rebuilds them, is wkv7_bwdc.hip.)
 //
 // The columns of G evolve independently (column j needs only c_j, a sum over
 // the rows of column j); only the outputs dr, dk, dw, db, da sum over columns.
@@ -444,522 +445,11 @@ hipError_t launch_bwd_t(const BwdArgs &p, hipStream_t stream)
     return heads * 2 <= kCUs ? launch_bwd_split<Tin, 2>(p, stream) : launch_bwd_split<Tin, 1>(p, stream);
 }
 
-
-// ------------------------------------------------------------------------------
-// The backward pass from chunk checkpoints (the trainable chunk kernel of the
-// SwiftRWKV guide's `.rwkvq` backend section: its backward pass rebuilds the state
-// chunk by chunk).  The chunked forward keeps only the state entering each chunk of
-// CK = 16 tokens, ckpt[b, c, h] = S_{16 c - 1} (the input state for c = 0): 1/16 of
-// the per-position states.  Chunks run in descending order; for each one the
-// workgroup rebuilds its states from the checkpoint with the recurrence itself,
-//     S_u = diag(w_u) S_{u-1} + b_u (a_u^T S_{u-1}) + k_u v_u^T,
-// and runs the adjoint above on them.
-//  * The chunk's inputs (r, w, k, a, b, and v and d_o at the workgroup's columns)
-//    are staged in LDS once, in the layout loaded (16-byte pieces, token after
-//    token); the next (earlier) chunk's inputs and checkpoint are loaded into
-//    registers in the second half of this one's adjoint (when half of its rebuilt
-//    states are no longer needed), and go to LDS at its end.  Tokens past T are
-//    staged as identity steps (w = 1, every other input 0: the state and its
-//    gradient pass through unchanged), so that every chunk runs the same 16 steps
-//    without a branch; only the stores of those tokens' gradients are skipped.
-//  * A chunk's 16 rebuilt states live in registers (16 CW of them per lane; with
-//    CW = 8 the kernel fits the 256 VGPRs that two waves per SIMD allow, without
-//    spilling), so each state is rebuilt once: 16 recurrence steps per chunk.
-//  * A rebuild step's column sum sa = S_{u-1}^T a_u goes through LDS (ColSumN with one
-//    quantity) and is kept for the adjoint, whose own column sums are then two,
-//    c = G^T b and dv = G^T k (ColSumN with two quantities).
-// Lane i is key row i, wave g holds CW value columns, as in the kernel above.
-constexpr int CK = 16;  // tokens per checkpoint
-
-// Column sums of NQ quantities over the 64 key rows, through LDS: the NQ CW (quantity,
-// column) pairs are summed by L = 64 / (NQ CW) lanes each, pair P by lanes L P .. L P + L - 1
-// (RPL = 64 / L rows each), then by DPP adds across those lanes.  Storage, in groups of
-// four columns: quantity q, group cg, row block h (RPL rows), row rr, column c4 at
-// q QS + (cg L + h) BS + 4 rr + c4.  A lane writes a group's four values as one 16-byte
-// write, next to the neighbouring row's; the padding of a row block (BS = min(4, 32/L)
-// modulo 32) puts the 32 lanes of a half wave, which read one row rr of their pairs at
-// a time, in 32 different banks.
-template <int CW, int NQ>
-struct ColSumN {
-    static constexpr int L = kN / (NQ * CW);
-    static constexpr int RPL = kN / L;
-    static constexpr int BS = RPL * 4 + (((L >= 8 ? 32 / L : 4) - RPL * 4) % 32 + 32) % 32;
-    static constexpr int QS = (CW / 4) * L * BS;
-    static_assert(NQ * CW * L == kN && L >= 4 && L <= 16 && CW % 4 == 0, "pairs fill the wave; 4 to 16 lanes per pair");
-    // where lane i writes group cg of quantity 0, and where the lane of pair P, row block h
-    // reads its first row
-    static __device__ int wr(int i, int cg) { return (cg * L + i / RPL) * BS + 4 * (i % RPL); }
-    static __device__ int rd(int P, int h) { return (P / CW) * QS + ((P % CW) / 4 * L + h) * BS + (P % CW) % 4; }
-};
-
-// Sum over the L lanes of a pair (aligned groups of L lanes), to every one of them.
-template <int L>
-__device__ __forceinline__ float pair_sum(float x)
-{
-    x += row_dpp<0xb1>(x);       // quad_perm [1, 0, 3, 2]
-    x += row_dpp<0x4e>(x);       // quad_perm [2, 3, 0, 1]
-    if constexpr (L >= 8)
-        x += row_dpp<0x141>(x);  // row_half_mirror
-    if constexpr (L >= 16)
-        x += row_dpp<0x140>(x);  // row_mirror
-    return x;
-}
-
-// The staging of one chunk's inputs, loaded in 16-byte pieces, tensor after tensor: r,
-// w, k, a, b (64 elements per token, in_dtype), v (the workgroup's NC columns, in_dtype),
-// d_o (NC columns, fp32); within a tensor, token after token.  Every tensor has a
-// multiple of 64 pieces, so the 64 pieces a wave loads at a time lie in one tensor.  In
-// LDS every tensor is fp32 (bf16 pieces are widened once, when stored), token after
-// token, so that a token's reads need no conversion.
-template <typename Tin, int SPLIT>
-struct Stage {
-    static constexpr int ES = static_cast<int>(sizeof(Tin));
-    static constexpr int NC = kN / SPLIT;
-    static constexpr int QP = kN * ES / 16, VP = NC * ES / 16, DP = NC * 4 / 16;  // pieces per token
-    static constexpr int R = CK * QP, RV = CK * VP, RD = CK * DP;                 // pieces per tensor
-    static constexpr int TOT = 5 * R + RV + RD;
-    static constexpr int NPL = (TOT + NWB * 64 - 1) / (NWB * 64);  // pieces per lane
-    static constexpr int LQ = CK * kN * 4, LV = CK * NC * 4;      // LDS bytes of a row tensor, of v or d_o
-    static constexpr int OV = 5 * LQ, OD = 5 * LQ + LV;            // LDS byte offsets of v, d_o
-    static constexpr int PAD = OD + LV;                            // 32 bytes that the lanes past TOT write
-    static constexpr int BYTES = PAD + 32;
-    static_assert(R % 64 == 0 && RV % 64 == 0 && RD % 64 == 0, "a wave's 64 pieces lie in one tensor");
-};
-
-// f ? x : y with f passed through an empty asm: a chain of these stays a chain of
-// selects (the compiler could otherwise turn a select chain over a few pointers into
-// a table in private memory).
-__device__ __forceinline__ unsigned long long pick(bool f, unsigned long long x, unsigned long long y)
-{
-    unsigned m = f;
-    asm volatile("" : "+v"(m));
-    return m ? x : y;
-}
-
-template <typename Tin, int CW, int SPLIT>
-struct alignas(16) CkSmem {
-    static constexpr int XS = 2 * ColSumN<CW, 2>::QS > ColSumN<CW, 1>::QS ? 2 * ColSumN<CW, 2>::QS
-                                                                        : ColSumN<CW, 1>::QS;
-    static_assert(XS % 4 == 0, "16-byte rows");
-    char in[Stage<Tin, SPLIT>::BYTES];     // the chunk's inputs
-    float x[NWB][XS];                      // per-wave column-sum terms
-    float sa[NWB][CK][CW];                 // per-wave S_{u-1}^T a_u of the chunk's tokens
-    float part[2][TB][5][NWB][kN];         // per-wave row partials, as in the kernel above
-};
-
-template <typename Tin, bool HAS_DOUT, int SPLIT>
-__global__ __launch_bounds__(NWB * 64) void wkv7_bwd_ckpt_kernel(BwdArgs p)
-{
-    constexpr int CW = kN / (NWB * SPLIT);  // value columns per wave
-    using C1 = ColSumN<CW, 1>;
-    using C2 = ColSumN<CW, 2>;
-    using SG = Stage<Tin, SPLIT>;
-    __shared__ CkSmem<Tin, CW, SPLIT> sm;
-    const int i = threadIdx.x & 63;
-    const int g = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    // workgroups of one head on one XCD, as in the kernel above
-    const int x = blockIdx.x;
-    const int bh = SPLIT == 1 ? x : (x / 16) * 8 + x % 8;
-    const int half = SPLIT == 1 ? 0 : (x / 8) % 2;
-    if (bh >= p.B * p.H)
-        return;
-    const int jl = g * CW;                // the wave's first column among the workgroup's
-    const int j0 = half * SG::NC + jl;    // ... among the head's
-    const int H = p.H, T = p.T;
-    const int bb = bh / H, hh = bh - bb * H;
-    const int nck = (T + CK - 1) / CK;
-    const Tin *__restrict__ r = static_cast<const Tin *>(p.r);
-    const Tin *__restrict__ w = static_cast<const Tin *>(p.w);
-    const Tin *__restrict__ k = static_cast<const Tin *>(p.k);
-    const Tin *__restrict__ v = static_cast<const Tin *>(p.v);
-    const Tin *__restrict__ a = static_cast<const Tin *>(p.a);
-    const Tin *__restrict__ b = static_cast<const Tin *>(p.b);
-    const size_t sbase = static_cast<size_t>(bh) * (kN * kN) + static_cast<size_t>(i) * kN + j0;
-    const size_t tok_e = static_cast<size_t>(H) * kN;
-    const size_t base_e = static_cast<size_t>(bb) * T * tok_e + static_cast<size_t>(hh) * kN;
-    const unsigned iu = static_cast<unsigned>(i);
-
-    float G[CW];
-#pragma unroll
-    for (int jj = 0; jj < CW; ++jj)
-        G[jj] = HAS_DOUT ? p.d_state_out[sbase + jj] : 0.0f;
-    if (T == 0) {  // no tokens: the gradient passes through
-#pragma unroll
-        for (int jj = 0; jj < CW; jj += 4)
-            *reinterpret_cast<f32x4 *>(&p.d_state_in[sbase + jj]) = f32x4{G[jj], G[jj + 1], G[jj + 2], G[jj + 3]};
-        return;
-    }
-
-    // ---- staging: lane i of wave g loads pieces g 64 + i + n 512 (n < NPL) of a chunk; the
-    // wave's tensor is uniform.  The token is clamped into the sequence (tokens past T
-    // become identity steps when stored); lanes past the last piece load the last 64
-    // again and store them into the buffer's padding.
-    typedef unsigned long long u64;
-    struct Piece {
-        u64 base;   // the tensor's address at token 0 of this row, head and columns
-        u64 tb;     // its bytes per token
-        int u, o;   // token within the chunk, 16-byte piece within the token's row
-        bool w1;    // a piece of w (1 in an identity step; every other tensor 0)
-        bool wide;  // in_dtype bf16, not d_o: widened to two 16-byte fp32 pieces in LDS
-        int dst;    // its LDS byte offset (the 32 bytes at PAD for the lanes past the last piece)
-    };
-    auto piece = [&](int n) {
-        // (recomputed at each use: the empty asm keeps the compiler from holding every
-        // piece's description in registers across the chunk loop)
-        int gw = g;
-        asm volatile("" : "+s"(gw));
-        const int pw = min(n * NWB * 64 + gw * 64, SG::TOT - 64);  // the wave's first piece
-        const bool is_v = pw >= 5 * SG::R && pw < 5 * SG::R + SG::RV, is_do = pw >= 5 * SG::R + SG::RV;
-        const int q = min(pw / SG::R, 4);
-        u64 row = pick(q == 3, reinterpret_cast<u64>(a), reinterpret_cast<u64>(b));
-        row = pick(q == 2, reinterpret_cast<u64>(k), row);
-        row = pick(q == 1, reinterpret_cast<u64>(w), row);
-        row = pick(q == 0, reinterpret_cast<u64>(r), row);
-        const u64 esz = is_do ? 4u : static_cast<u64>(SG::ES);
-        const u64 col = is_v || is_do ? static_cast<u64>(half * SG::NC) : 0u;
-        Piece pc;
-        pc.base = pick(is_do, reinterpret_cast<u64>(p.d_o), pick(is_v, reinterpret_cast<u64>(v), row)) +
-                  (base_e + col) * esz;
-        pc.tb = tok_e * esz;
-        const int l = pw + i - (is_do ? 5 * SG::R + SG::RV : is_v ? 5 * SG::R : q * SG::R);
-        const int pt = is_do ? SG::DP : is_v ? SG::VP : SG::QP;  // (powers of two)
-        const int sh = pt == 4 ? 2 : pt == 8 ? 3 : 4;
-        static_assert((SG::QP == 8 || SG::QP == 16) && (SG::VP == 4 || SG::VP == 8 || SG::VP == 16) &&
-                          (SG::DP == 8 || SG::DP == 16), "pieces per token: 4, 8 or 16");
-        pc.u = l >> sh;
-        pc.o = l & (pt - 1);
-        pc.w1 = !is_v && !is_do && q == 1;
-        pc.wide = SG::ES == 2 && !is_do;
-        // LDS: fp32 elements from the tensor's region; a piece of d_o is four of them, a
-        // piece of another tensor 16 / ES (eight when widened from bf16)
-        const int lds0 = is_do ? SG::OD : is_v ? SG::OV : q * SG::LQ;
-        pc.dst = n * NWB * 64 + gw * 64 + i < SG::TOT ? lds0 + l * (pc.wide ? 32 : 16) : SG::PAD;
-        return pc;
-    };
-    auto stage_load = [&](int c, u32x4 (&pre)[SG::NPL]) {
-#pragma unroll
-        for (int n = 0; n < SG::NPL; ++n) {
-            const Piece pc = piece(n);
-            const u64 t = static_cast<u64>(min(c * CK + pc.u, T - 1));
-            // (a global load: a flat one would also count as an LDS access in the waits)
-            pre[n] = *reinterpret_cast<const GLOBAL_AS u32x4 *>(pc.base + t * pc.tb + 16u * static_cast<unsigned>(pc.o));
-        }
-    };
-    auto stage_store = [&](int c, const u32x4 (&pre)[SG::NPL]) {
-#pragma unroll
-        for (int n = 0; n < SG::NPL; ++n) {
-            const Piece pc = piece(n);
-            const bool live = c * CK + pc.u < T;
-            const uint32_t id = pc.w1 ? 0x3f800000u : 0u;  // the identity step: w = 1, the rest 0
-            char *const d = sm.in + pc.dst;
-            if (pc.wide) {  // (uniform per wave) eight bf16, widened: the upper halves of fp32
-                const u32x4 x = pre[n];
-                f32x4 lo, hi;
-                lo[0] = __uint_as_float(x[0] << 16); lo[1] = __uint_as_float(x[0] & 0xffff0000u);
-                lo[2] = __uint_as_float(x[1] << 16); lo[3] = __uint_as_float(x[1] & 0xffff0000u);
-                hi[0] = __uint_as_float(x[2] << 16); hi[1] = __uint_as_float(x[2] & 0xffff0000u);
-                hi[2] = __uint_as_float(x[3] << 16); hi[3] = __uint_as_float(x[3] & 0xffff0000u);
-                const f32x4 idv = {__uint_as_float(id), __uint_as_float(id), __uint_as_float(id), __uint_as_float(id)};
-                *reinterpret_cast<f32x4 *>(d) = live ? lo : idv;
-                *reinterpret_cast<f32x4 *>(d + 16) = live ? hi : idv;
-            } else {
-                *reinterpret_cast<u32x4 *>(d) = live ? pre[n] : u32x4{id, id, id, id};
-            }
-        }
-    };
-    // this lane's part of checkpoint c: row i, the wave's CW columns
-    auto ck_load = [&](int c, float (&X)[CW]) {
-        const float *src = p.ckpt + ((static_cast<size_t>(bb) * nck + c) * H + hh) * (kN * kN) + iu * kN + j0;
-#pragma unroll
-        for (int jj = 0; jj < CW; jj += 4) {
-            const f32x4 x4 = *reinterpret_cast<const f32x4 *>(src + jj);
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                X[jj + e] = x4[e];
-        }
-    };
-    // ---- a token's staged inputs
-    auto in_row = [&](int u, int qq) {  // quantity qq (r, w, k, a, b) at key row i
-        return reinterpret_cast<const float *>(sm.in + qq * SG::LQ + u * kN * 4)[i];
-    };
-    auto in_v = [&](int u, float (&vv)[CW]) {  // v at the wave's columns (the same in every lane)
-        const char *pv = sm.in + SG::OV + u * SG::NC * 4 + 4 * jl;
-#pragma unroll
-        for (int jj = 0; jj < CW; jj += 4) {
-            const f32x4 x4 = *reinterpret_cast<const f32x4 *>(pv + 4 * jj);
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                vv[jj + e] = x4[e];
-        }
-    };
-    auto in_do = [&](int u, float (&dO)[CW]) {  // d_o at the wave's columns
-        const char *pd = sm.in + SG::OD + u * SG::NC * 4 + 4 * jl;
-#pragma unroll
-        for (int jj = 0; jj < CW; jj += 4) {
-            const f32x4 x4 = *reinterpret_cast<const f32x4 *>(pd + 4 * jj);
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                dO[jj + e] = x4[e];
-        }
-    };
-
-    float *const xw = sm.x[g];
-    // ---- one rebuild step: X <- diag(w) X + b (a^T X) + k v^T for token u; a^T X is kept
-    const int x1_r = C1::rd(i / C1::L, i % C1::L);
-    auto rebuild = [&](int u, float (&X)[CW]) {
-        const float wi = in_row(u, 1), ki = in_row(u, 2), ai = in_row(u, 3), bi = in_row(u, 4);
-        float vv[CW];
-        in_v(u, vv);
-#pragma unroll
-        for (int jj = 0; jj < CW; jj += 4)
-            *reinterpret_cast<f32x4 *>(&xw[C1::wr(i, jj / 4)]) =
-                f32x4{ai * X[jj], ai * X[jj + 1], ai * X[jj + 2], ai * X[jj + 3]};
-        float s2[2] = {0.f, 0.f};
-#pragma unroll
-        for (int rr = 0; rr < C1::RPL; ++rr)
-            s2[rr % 2] += xw[x1_r + 4 * rr];
-        const float cs = pair_sum<C1::L>(s2[0] + s2[1]);
-        sm.sa[g][u][i / C1::L] = cs;  // (the L lanes of a column store the same value)
-#pragma unroll
-        for (int jj = 0; jj < CW; ++jj) {
-            const float sa = lane_bcast(cs, C1::L * jj);
-            X[jj] = fmaf(wi, X[jj], fmaf(bi, sa, ki * vv[jj]));
-        }
-    };
-
-    // ---- the adjoint (the same arithmetic as the kernel above; S_{u-1}^T a_u from the
-    // rebuild), column-sum lane roles: c in lanes 0 .. 31, dv in lanes 32 .. 63
-    const int x_r = C2::rd(i / C2::L, i % C2::L);
-    const int dv_col = (i | 32) / C2::L - CW;
-    constexpr int NM = (5 * TB + NWB - 1) / NWB;
-    int sl0[NM], qn0[NM];
-    bool extra[NM];
-    u64 dst0[NM];  // the output of sum m (one of dr, dk, dw, db, da), chosen once
-#pragma unroll
-    for (int m = 0; m < NM; ++m) {
-        const int pi0 = g + NWB * m, pi = pi0 < 5 * TB ? pi0 : pi0 - NWB;
-        sl0[m] = pi / 5;
-        qn0[m] = pi - 5 * sl0[m];
-        extra[m] = pi0 >= 5 * TB;
-        const int qn = qn0[m];
-        const u64 d = pick(qn == 0, reinterpret_cast<u64>(p.dr),
-                           pick(qn == 1, reinterpret_cast<u64>(p.dk),
-                                pick(qn == 2, reinterpret_cast<u64>(p.dw),
-                                     pick(qn == 3, reinterpret_cast<u64>(p.db), reinterpret_cast<u64>(p.da)))));
-        // (the same in every lane: held in scalar registers through the loop; the lane read
-        // returns an int, taken as unsigned before widening so that the low word is not
-        // sign-extended into the high one)
-        const unsigned lo = static_cast<unsigned>(__builtin_amdgcn_readfirstlane(static_cast<unsigned>(d)));
-        const unsigned hi = static_cast<unsigned>(__builtin_amdgcn_readfirstlane(static_cast<unsigned>(d >> 32)));
-        dst0[m] = static_cast<u64>(lo) | static_cast<u64>(hi) << 32;
-    }
-    // the batch of tokens t_end .. t_end + TB - 1 (slot TB - 1 - s is token t_end + s)
-    auto finish_batch = [&](size_t e_end, int t_end, int pb) {
-        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's partials are in LDS
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-#pragma unroll
-        for (int m = 0; m < NM; ++m) {
-            const int sl = sl0[m], qn = qn0[m];
-            float sum = 0.f;
-#pragma unroll
-            for (int gg = 0; gg < NWB; ++gg)
-                sum += sm.part[pb][sl][qn][gg][i];
-            const u64 at = dst0[m] + 4u * ((e_end + static_cast<size_t>(TB - 1 - sl) * tok_e) + iu);
-            if (t_end + (TB - 1 - sl) < T) {  // (the same for the whole wave)
-                if (SPLIT == 1)
-                    *reinterpret_cast<GLOBAL_AS float *>(at) = sum;
-                else  // (a global atomic: a flat one would also count as an LDS access)
-                    __builtin_amdgcn_global_atomic_fadd_f32(reinterpret_cast<GLOBAL_AS float *>(at),
-                                                            extra[m] ? 0.0f : sum);
-            }
-        }
-    };
-    // one token of the adjoint: Sp = S_{u-1}, St = S_u
-    auto adjoint = [&](int u, size_t e0, bool live, const float (&Sp)[CW], const float (&St)[CW], int slot,
-                       int pb) {
-        const float ri = in_row(u, 0), wi = in_row(u, 1), ki = in_row(u, 2), ai = in_row(u, 3), bi = in_row(u, 4);
-        float dO[CW], vv[CW];
-        in_do(u, dO);
-        in_v(u, vv);
-        // With four columns per wave the column-sum reads go out before the row partials,
-        // which do not need c and run while the reads are in flight.  With eight the
-        // partials come first: the reads held across them cost spills.
-        constexpr bool EARLY = CW <= 4;
-        float p_dr = 0.f, p_dk = 0.f, p_dw = 0.f, p_db = 0.f;
-#pragma unroll
-        for (int jj = 0; jj < CW; ++jj) {
-            G[jj] += ri * dO[jj];
-            if constexpr (!EARLY) {
-                p_dr += St[jj] * dO[jj];
-                p_dk += G[jj] * vv[jj];
-                p_dw += G[jj] * Sp[jj];
-            }
-        }
-#pragma unroll
-        for (int jj = 0; jj < CW; jj += 4) {
-            f32x4 xc, xv;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                xc[e] = bi * G[jj + e];
-                xv[e] = ki * G[jj + e];
-            }
-            *reinterpret_cast<f32x4 *>(&xw[C2::wr(i, jj / 4)]) = xc;
-            *reinterpret_cast<f32x4 *>(&xw[C2::QS + C2::wr(i, jj / 4)]) = xv;
-        }
-        float sa[CW];
-#pragma unroll
-        for (int jj = 0; jj < CW; jj += 4) {
-            const f32x4 x4 = *reinterpret_cast<const f32x4 *>(&sm.sa[g][u][jj]);
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                sa[jj + e] = x4[e];
-        }
-        float c4[4] = {0.f, 0.f, 0.f, 0.f};
-        if constexpr (EARLY) {
-            float xr[C2::RPL];
-#pragma unroll
-            for (int rr = 0; rr < C2::RPL; ++rr)
-                xr[rr] = xw[x_r + 4 * rr];
-#pragma unroll
-            for (int jj = 0; jj < CW; ++jj) {
-                p_dr += St[jj] * dO[jj];
-                p_dk += G[jj] * vv[jj];
-                p_dw += G[jj] * Sp[jj];
-                p_db += G[jj] * sa[jj];
-            }
-#pragma unroll
-            for (int rr = 0; rr < C2::RPL; ++rr)
-                c4[rr % 4] += xr[rr];
-        } else {
-#pragma unroll
-            for (int rr = 0; rr < C2::RPL; ++rr)
-                c4[rr % 4] += xw[x_r + 4 * rr];
-        }
-        const float cs = pair_sum<C2::L>((c4[0] + c4[1]) + (c4[2] + c4[3]));
-        float c[CW];
-#pragma unroll
-        for (int jj = 0; jj < CW; ++jj)
-            c[jj] = lane_bcast(cs, C2::L * jj);
-        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(cs), __float_as_uint(cs), false, false);
-        if (live)
-            (p.dv + e0 + j0)[static_cast<unsigned>(dv_col)] = __uint_as_float(sw[1]);
-        float p_da = 0.f;
-#pragma unroll
-        for (int jj = 0; jj < CW; ++jj) {
-            if constexpr (!EARLY)
-                p_db += G[jj] * sa[jj];
-            p_da += Sp[jj] * c[jj];
-            G[jj] = wi * G[jj] + ai * c[jj];
-        }
-        sm.part[pb][slot][0][g][i] = p_dr;
-        sm.part[pb][slot][1][g][i] = p_dk;
-        sm.part[pb][slot][2][g][i] = p_dw;
-        sm.part[pb][slot][3][g][i] = p_db;
-        sm.part[pb][slot][4][g][i] = p_da;
-    };
-
-    // ---- the chunks, last first
-    static_assert(CK % TB == 0 && (CK / TB) % 2 == 0,
-                  "whole batches per chunk; the partial buffers alternate the same way in every chunk");
-    u32x4 pre[SG::NPL];
-    float ck[CW], ckn[CW], Sl[CW];  // checkpoints of this chunk and the one before; this chunk's last state
-    stage_load(nck - 1, pre);
-    ck_load(nck - 1, ck);
-    stage_store(nck - 1, pre);
-    __builtin_amdgcn_s_waitcnt(0xc07f);
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    for (int c = nck - 1; c >= 0; --c) {
-        const int t0 = c * CK;
-        const size_t ec = base_e + static_cast<size_t>(t0) * tok_e;
-        // the chunk's states: Xs[u] = S_{u-1}, from the checkpoint; S_15, the chunk's
-        // last, is the next chunk's checkpoint (carried in Sl), or for the last chunk
-        // the rebuild's last state (past T the steps are the identity: S_{T-1})
-        float X[CW], Xs[CK][CW];
-#pragma unroll
-        for (int jj = 0; jj < CW; ++jj)
-            Xs[0][jj] = X[jj] = ck[jj];
-#pragma unroll
-        for (int u = 0; u < CK; ++u) {
-            rebuild(u, X);
-            if (u + 1 < CK) {
-#pragma unroll
-                for (int jj = 0; jj < CW; ++jj)
-                    Xs[u + 1][jj] = X[jj];
-            }
-        }
-        if (c == nck - 1) {
-#pragma unroll
-            for (int jj = 0; jj < CW; ++jj)
-                Sl[jj] = X[jj];
-        }
-#pragma unroll
-        for (int u = CK - 1; u >= 0; --u) {
-            const int n = CK - 1 - u;  // tokens of the chunk done before this one
-            const int slot = n % TB, pb = (n / TB) & 1;
-            const size_t e0 = ec + static_cast<size_t>(u) * tok_e;
-            adjoint(u, e0, t0 + u < T, Xs[u], u == CK - 1 ? Sl : Xs[u + 1], slot, pb);
-            if (slot == TB - 1)
-                finish_batch(e0, t0 + u, pb);
-            if (u == CK / 2 && c > 0) {
-                stage_load(c - 1, pre);
-                ck_load(c - 1, ckn);
-            }
-        }
-        if (c > 0) {
-            // every wave is past the barrier of the chunk's last batch, so past its reads
-            stage_store(c - 1, pre);
-#pragma unroll
-            for (int jj = 0; jj < CW; ++jj) {
-                Sl[jj] = ck[jj];  // this chunk's checkpoint is the previous chunk's last state
-                ck[jj] = ckn[jj];
-            }
-            __builtin_amdgcn_s_waitcnt(0xc07f);
-            __builtin_amdgcn_s_barrier();
-            asm volatile("" ::: "memory");
-        }
-    }
-#pragma unroll
-    for (int jj = 0; jj < CW; jj += 4)
-        *reinterpret_cast<f32x4 *>(&p.d_state_in[sbase + jj]) = f32x4{G[jj], G[jj + 1], G[jj + 2], G[jj + 3]};
-}
-
-template <typename Tin, int SPLIT>
-hipError_t launch_bwd_ckpt_split(const BwdArgs &p, hipStream_t stream)
-{
-    const size_t heads = static_cast<size_t>(p.B) * static_cast<size_t>(p.H);
-    if (SPLIT > 1 && p.T > 0) {
-        const size_t n4 = heads * static_cast<size_t>(p.T) * (kN / 4);
-        const unsigned zblocks = static_cast<unsigned>(std::min<size_t>((n4 + 255) / 256, 4 * kCUs));
-        hipLaunchKernelGGL(zero5_kernel, dim3(zblocks), dim3(256), 0, stream, p.dr, p.dk, p.dw, p.db, p.da, n4);
-    }
-    const size_t nwg = SPLIT == 1 ? heads : (heads + 7) / 8 * 16;
-    const dim3 grid(static_cast<unsigned>(nwg)), block(NWB * 64);
-    if (p.d_state_out)
-        hipLaunchKernelGGL((wkv7_bwd_ckpt_kernel<Tin, true, SPLIT>), grid, block, 0, stream, p);
-    else
-        hipLaunchKernelGGL((wkv7_bwd_ckpt_kernel<Tin, false, SPLIT>), grid, block, 0, stream, p);
-    return hipGetLastError();
-}
-
-template <typename Tin>
-hipError_t launch_bwd_ckpt_t(const BwdArgs &p, hipStream_t stream)
-{
-    const int64_t heads = static_cast<int64_t>(p.B) * p.H;
-    return heads * 2 <= kCUs ? launch_bwd_ckpt_split<Tin, 2>(p, stream) : launch_bwd_ckpt_split<Tin, 1>(p, stream);
-}
-
 }  // namespace
 
 hipError_t launch_backward(const BwdArgs &p, hipStream_t stream)
 {
     return p.in_bf16 ? launch_bwd_t<uint16_t>(p, stream) : launch_bwd_t<float>(p, stream);
-}
-
-hipError_t launch_backward_ckpt(const BwdArgs &p, hipStream_t stream)
-{
-    return p.in_bf16 ? launch_bwd_ckpt_t<uint16_t>(p, stream) : launch_bwd_ckpt_t<float>(p, stream);
 }
 
 }  // namespace wkv7

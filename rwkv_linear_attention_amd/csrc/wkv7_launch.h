@@ -37,7 +37,7 @@ struct BwdArgs {
     const void *r, *w, *k, *v, *a, *b;  // [B,T,H,64], in_dtype
     const float *state_in;              // [B,H,64,64] or nullptr (zeros)
     const float *state_pos;             // [B,T,H,64,64]: the state after each token (wkv7_backward)
-    const float *ckpt;                  // [B,ceil(T/16),H,64,64]: the state entering each chunk (the rebuild)
+    const float *ckpt;                  // [B,ceil(T/16),H,64,64]: the state entering each chunk
     const float *d_o;                   // [B,T,H,64]: gradient of o
     const float *d_state_out;           // [B,H,64,64] or nullptr (zeros)
     float *dr, *dw, *dk, *dv, *da, *db; // [B,T,H,64]
@@ -53,7 +53,6 @@ hipError_t launch_state_reset(float *state, int B, int H, const unsigned char *r
                               hipStream_t stream);
 hipError_t launch_tail(const TailArgs &a, hipStream_t stream);
 hipError_t launch_backward(const BwdArgs &a, hipStream_t stream);
-hipError_t launch_backward_ckpt(const BwdArgs &a, hipStream_t stream);
 hipError_t launch_backward_chunked(const BwdArgs &a, hipStream_t stream);
 hipError_t launch_state_commit(const float *state_pos, const int *accepted, const float *state_in,
                                float *state_out, int B, int T, int H, hipStream_t stream);

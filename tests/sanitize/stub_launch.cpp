@@ -49,11 +49,6 @@ hipError_t launch_backward(const BwdArgs &a, hipStream_t)
     g_log.bwd = a;
     return note("backward", a.B, a.T, a.H);
 }
-hipError_t launch_backward_ckpt(const BwdArgs &a, hipStream_t)
-{
-    g_log.bwd = a;
-    return note("backward_ckpt", a.B, a.T, a.H);
-}
 hipError_t launch_backward_chunked(const BwdArgs &a, hipStream_t)
 {
     g_log.bwd = a;
