@@ -90,7 +90,7 @@ enum wkv7_status {
  * Size limits (WKV7_ERR_SHAPE beyond them).  Each head runs as one or a few
  * workgroups of one launch, and a launch holds fewer than 2^32 threads:
  *   B * H <= WKV7_MAX_HEADS_STEP   for wkv7_step, wkv7_step_tail, wkv7_state_commit, wkv7_backward,
- *                                  and wkv7_forward[_varlen] with T < 9;
+ *                                  wkv7_backward_ckpt, and wkv7_forward[_varlen] with T < 9;
  *   B * H <= WKV7_MAX_HEADS_CHUNK  for wkv7_forward[_varlen] with T >= 9;
  *   H <= WKV7_MAX_H_CHUNK           for wkv7_forward[_varlen] with T >= 9 (a lane of the
  *                                  chunked kernel addresses its 16 tokens' outputs with 32-bit
@@ -316,16 +316,21 @@ int wkv7_forward_ckpt(const void *r, const void *w, const void *k, const void *v
 
 /*
  * wkv7_backward_ckpt -- wkv7_backward from the checkpoints of wkv7_forward_ckpt
- * instead of per-position states: per chunk, last first, the pass rebuilds the
- * chunk's 16 states from its checkpoint with the recurrence (in registers) and
- * runs the adjoint on them.  It reads 1/16 of the state bytes that
- * wkv7_backward reads, and no state_in (ckpt[:, 0] is the input state).
+ * instead of per-position states.  The gradient for the state is carried back
+ * over the tokens on its own (it needs no states); the gradients of each chunk of
+ * 16 tokens then follow from the chunk's checkpoint and that gradient at the
+ * chunk's end, in the chunk form of the recurrence (matrix products), for all
+ * chunks at once.  A chunk with a decay below 2^-15 in magnitude (w = 0
+ * included) runs the recurrence token by token instead.  It reads 1/16 of the
+ * state bytes that wkv7_backward reads, and no state_in (ckpt[:, 0] is the input
+ * state).
  *
  *   ckpt : [B, ceil(T/16), H, N, N] fp32, as wkv7_forward_ckpt wrote it from the
  *          same inputs and state_in.
  * Everything else (d_o, d_state_out, the gradients, NULL rules, aliasing, the
- * limit B * H <= WKV7_MAX_HEADS_STEP, and the fill plus atomic adds when
- * B * H <= 128) as wkv7_backward.
+ * limit B * H <= WKV7_MAX_HEADS_STEP) as wkv7_backward.  While the call runs,
+ * dr, dk, da and db also hold the gradient for the state at each chunk's end
+ * (16 rows of each per chunk) before the gradients replace it.
  */
 int wkv7_backward_ckpt(const void *r, const void *w, const void *k, const void *v,
                        const void *a, const void *b, int in_dtype, const float *ckpt,

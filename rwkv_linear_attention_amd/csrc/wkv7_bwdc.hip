@@ -1097,8 +1097,8 @@ hipError_t launch_bwdc_t(const BwdArgs &p, hipStream_t stream)
         hipLaunchKernelGGL((wkv7_bwdc_gchain_kernel<Tin, false>), dim3(static_cast<unsigned>(nbh)), dim3(256), 0,
                            stream, p);
     }
-    // the other chunks, at most 2^30 workgroups per launch
-    const int per = static_cast<int>(std::max<long long>(1, (1ll << 30) / nbh));
+    // the other chunks, fewer than 2^32 threads (2^24 workgroups) per launch
+    const int per = static_cast<int>(std::max<long long>(1, ((1ll << 24) - 1) / nbh));
     for (int c0 = 0; c0 < nck - 1; c0 += per) {
         const int n = std::min(per, nck - 1 - c0);
         hipLaunchKernelGGL(wkv7_bwdc_chunk_kernel<Tin>, dim3(static_cast<unsigned>(n) * static_cast<unsigned>(nbh)),
