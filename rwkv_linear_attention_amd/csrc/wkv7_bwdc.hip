@@ -260,27 +260,30 @@ __global__ __launch_bounds__(GNW * 64) void wkv7_bwdc_chain_kernel(BwdArgs p)
 }
 
 // ---------------------------------------------------------------------------------
-// The chunk kernel: one workgroup of four waves per (chunk, batch, head).
+// The chunk kernel: one workgroup of four waves per (chunk, batch, head).  S^ and G^
+// never enter LDS: each lane loads the parts of S0 and G_end that its own matrix-core
+// products take (a row segment and a column segment of each), so three workgroups
+// share a compute unit.
 constexpr int RS = kN + 1;  // row stride of the LDS matrices (column reads hit distinct banks)
 constexpr int SS = CC + 1;  // row stride of the 16 x 16 matrices
 
 // The 16 x 64 matrices.  dR0 = dO S^T, dA0 = dX S^T, dBz = Z G^T and dKv = V G^T (the
 // first terms of dR', dA', dB', dK', kept for the decay gradient) take the places of dO,
 // dX, Z and V once those are no longer read.
-enum Row { X_R, X_W, X_K, X_V, X_A, X_B, X_DO, X_Z, X_DX, X_D, NROW };
+enum Row { X_R, X_W, X_K, X_V, X_A, X_B, X_DO, X_Z, X_DX, NROW };
 constexpr int X_DR0 = X_DO, X_DA0 = X_DX, X_DBZ = X_Z, X_DKV = X_V;
 // The 16 x 16 matrices: T is formed over M_ab; dO Z^T, dX Z^T and dX V^T (the masked dM's
 // and the token-pair products of the decay gradient) over M_ak, M_rb and M_rk.
 enum Small { M_AB, M_AK, M_RB, M_RK, W_OV, NSMALL };
 constexpr int M_T = M_AB, W_OZ = M_AK, W_XZ = M_RB, W_XV = M_RK;
 
-// 80.6 KB: two workgroups share a compute unit.
+// 43.4 KB: three workgroups share a compute unit.
 struct ChunkSmem {
     float rows[NROW][CC][RS];  // 16 x 64 matrices (tokens x channels)
-    float sq[2][kN][RS];       // S^ and G^ (key rows x value columns)
     float sm[NSMALL][CC][SS];  // 16 x 16 matrices
-    float base[kN];            // P_7 per key, then rowsum(G^ * S^)
-    int flag;                  // the chunk takes the exact path
+    alignas(16) float p7[kN];  // P_7 per key
+    alignas(16) float d15[kN]; // d_15 per key
+    alignas(16) int flag[4];   // per wave: a decay below 2^-15 in its quarter of the chunk
 };
 
 __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c)
@@ -288,46 +291,56 @@ __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c)
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// x[4 q + e] for a per-lane q in 0 .. 3 (three selects; no table)
+__device__ __forceinline__ float sel4(int q, float x0, float x1, float x2, float x3)
+{
+    return (q & 2) ? ((q & 1) ? x3 : x2) : ((q & 1) ? x1 : x0);
+}
 
 // The exact path of a chunk with a decay below 2^-15 (w = 0 included): the recurrence
-// itself.  Thread (key row i, column quarter) holds 16 elements of a row of S and of G.
-// A forward sweep forms z_tau = S_{tau-1}^T a_tau (kept in LDS); then, going back over
-// the tokens, S_{t-1} and S_t are replayed from the checkpoint with those z (no more
-// column sums), and each token's gradients are those of the recurrent adjoint:
+// itself.  Lane (q, m) of wave wv holds columns 16 q .. 16 q + 15 of key row 16 wv + m
+// of S and of G (the raw S0 and G_end are passed in).  A forward sweep forms
+// z_tau = S_{tau-1}^T a_tau (kept in LDS); then, going back over the tokens, S_{t-1} and
+// S_t are replayed from the checkpoint with those z (no more column sums), and each
+// token's gradients are those of the recurrent adjoint:
 //     dr = S_t dO_t, dk = G v_t, dw = rowsum(G * S_{t-1}), db = G z_t,
 //     c = G^T b_t, dv = G^T k_t, da = S_{t-1} c, then G <- diag(w_t) G + a_t c^T.
-// The raw inputs, the checkpoint and G_end are in LDS (no factors were applied).
-__device__ void exact_chunk(const BwdArgs &p, ChunkSmem &sm, int t0, int L, size_t head_e, size_t tok_e)
+// The raw inputs are in LDS (no factors were applied).
+__device__ void exact_chunk(const BwdArgs &p, ChunkSmem &sm, int t0, int L, size_t head_e, size_t tok_e,
+                            const float (&S0r)[16], const float (&Gin)[16])
 {
-    const int tid = threadIdx.x, i = tid >> 2, j0 = (tid & 3) * 16;
-    float *const tmp = &sm.sq[0][0][0];  // 64 rows of RS, once the checkpoint is in registers
+    const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, m = lane & 15;
+    const int wv = tid >> 6, i = 16 * wv + m, j0 = 16 * q;
+    float *const part = &sm.sm[M_AB][0][0];  // [4 waves][64 columns] partial column sums
     float *const cvec = &sm.sm[W_OZ][0][0], *const dvvec = &sm.sm[W_OV][0][0];
-    auto zrow = [&](int tau) { return &sm.rows[X_D][tau][0]; };
-    auto colsum = [&](const float (&x)[16], float *dst) {
+    auto zrow = [&](int tau) { return &sm.rows[X_Z][tau][0]; };
+    // the sum over the 64 key rows of f x (this lane's 16 columns): over the 16 rows of
+    // the wave by shuffles, then over the four waves in LDS
+    auto colsum = [&](float f, const float (&x)[16], float *dst) {
 #pragma unroll
-        for (int jj = 0; jj < 16; ++jj)
-            tmp[i * RS + j0 + jj] = x[jj];
-        __syncthreads();
-        if (tid < kN) {
-            float acc = 0.f;
-            for (int ii = 0; ii < kN; ++ii)
-                acc += tmp[ii * RS + tid];
-            dst[tid] = acc;
+        for (int jj = 0; jj < 16; ++jj) {
+            float v = f * x[jj];
+            v += __shfl_xor(v, 1);
+            v += __shfl_xor(v, 2);
+            v += __shfl_xor(v, 4);
+            v += __shfl_xor(v, 8);
+            if (m == 0)
+                part[wv * kN + j0 + jj] = v;
         }
         __syncthreads();
+        if (tid < kN)
+            dst[tid] = (part[tid] + part[kN + tid]) + (part[2 * kN + tid] + part[3 * kN + tid]);
+        __syncthreads();
     };
-    auto rsum = [](float x) {
-        x += __shfl_xor(x, 1);
-        x += __shfl_xor(x, 2);
+    auto rsum = [](float x) {  // over the four column quarters of the row
+        x += __shfl_xor(x, 16);
+        x += __shfl_xor(x, 32);
         return x;
     };
-    float S0r[16], G[16];
+    float G[16];
 #pragma unroll
-    for (int jj = 0; jj < 16; ++jj) {
-        S0r[jj] = sm.sq[0][i][j0 + jj];
-        G[jj] = sm.sq[1][i][j0 + jj];
-    }
-    __syncthreads();
+    for (int jj = 0; jj < 16; ++jj)
+        G[jj] = Gin[jj];
     auto step = [&](int u, float (&S)[16]) {
         const float wu = sm.rows[X_W][u][i], bu = sm.rows[X_B][u][i], ku = sm.rows[X_K][u][i];
         const float *z = zrow(u);
@@ -341,12 +354,7 @@ __device__ void exact_chunk(const BwdArgs &p, ChunkSmem &sm, int t0, int L, size
         for (int jj = 0; jj < 16; ++jj)
             S[jj] = S0r[jj];
         for (int tau = 0; tau < L; ++tau) {
-            const float at = sm.rows[X_A][tau][i];
-            float x[16];
-#pragma unroll
-            for (int jj = 0; jj < 16; ++jj)
-                x[jj] = at * S[jj];
-            colsum(x, zrow(tau));
+            colsum(sm.rows[X_A][tau][i], S, zrow(tau));
             step(tau, S);
         }
     }
@@ -368,7 +376,6 @@ __device__ void exact_chunk(const BwdArgs &p, ChunkSmem &sm, int t0, int L, size
             St[jj] = Sp[jj];
         step(t, St);
         float s_dr = 0.f, s_dk = 0.f, s_dw = 0.f, s_db = 0.f;
-        float xc[16], xv[16];
 #pragma unroll
         for (int jj = 0; jj < 16; ++jj) {
             const int j = j0 + jj;
@@ -376,22 +383,20 @@ __device__ void exact_chunk(const BwdArgs &p, ChunkSmem &sm, int t0, int L, size
             s_dk = fmaf(G[jj], sm.rows[X_V][t][j], s_dk);
             s_dw = fmaf(G[jj], Sp[jj], s_dw);
             s_db = fmaf(G[jj], z[j], s_db);
-            xc[jj] = bt * G[jj];
-            xv[jj] = kt * G[jj];
         }
         s_dr = rsum(s_dr);
         s_dk = rsum(s_dk);
         s_dw = rsum(s_dw);
         s_db = rsum(s_db);
-        colsum(xc, cvec);
-        colsum(xv, dvvec);
+        colsum(bt, G, cvec);
+        colsum(kt, G, dvvec);
         float s_da = 0.f;
 #pragma unroll
         for (int jj = 0; jj < 16; ++jj)
             s_da = fmaf(Sp[jj], cvec[j0 + jj], s_da);
         s_da = rsum(s_da);
         const size_t row = head_e + static_cast<size_t>(t0 + t) * tok_e;
-        if ((tid & 3) == 0) {
+        if (q == 0) {
             p.dr[row + i] = s_dr;
             p.dk[row + i] = s_dk;
             p.dw[row + i] = s_dw;
@@ -407,11 +412,12 @@ __device__ void exact_chunk(const BwdArgs &p, ChunkSmem &sm, int t0, int L, size
 }
 
 template <typename Tin>
-__global__ __launch_bounds__(256) void wkv7_bwdc_chunk_kernel(BwdArgs p, int c_lo, int nbh)
+__global__ __launch_bounds__(256, 3) void wkv7_bwdc_chunk_kernel(BwdArgs p, int c_lo, int nbh)
 {
     __shared__ ChunkSmem sm;
     const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, m = lane & 15;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int tc = 16 * wv + m;  // this lane's key: its column of every 16 x 64 tile
     const int c = c_lo + static_cast<int>(blockIdx.x) / nbh;
     const int bh = static_cast<int>(blockIdx.x) % nbh;
     const int H = p.H, T = p.T;
@@ -422,9 +428,51 @@ __global__ __launch_bounds__(256) void wkv7_bwdc_chunk_kernel(BwdArgs p, int c_l
     const size_t head_e = static_cast<size_t>(bb) * T * tok_e + static_cast<size_t>(hh) * kN;
     auto rowp = [&](int tau) { return head_e + static_cast<size_t>(t0 + min(tau, L - 1)) * tok_e; };
 
-    // ---- load: inputs (tokens past the end as identity steps: w = 1, the rest 0), dO,
-    // the checkpoint and G_end -- every global load is issued before the first is used
+    // ---- load.  Of the checkpoint S0 and G_end this lane takes row tc, columns
+    // 16 q .. 16 q + 15 (the B operand of the products against S^T and G^T), loaded first,
+    // and column tc, rows 16 q .. 16 q + 15 (the B operand of the products against S^ and
+    // G^), loaded once the chunk is known to take the factor path.  Row u of G_end's
+    // block sb (rows 16 sb .. 16 sb + 15) is, for an inner chunk, token t0 + u of dr, dk,
+    // da, db (sb = 0 .. 3); for the last chunk, row 16 sb + u of d_state_out (a missing
+    // d_state_out reads the checkpoint and is zeroed).  The inputs go to LDS (tokens past
+    // the end as identity steps: w = 1, the rest 0), with dO.
+    float srow[16], scol[16], grow[16], gcol[16];
+    const bool inner = c < nck - 1, has_g = inner || p.d_state_out != nullptr;
+    u64 scol_a, gcol_a, gstride;
     {
+        const u64 s0 = reinterpret_cast<u64>(p.ckpt) + 4ull * (((static_cast<size_t>(bb) * nck + c) * H + hh) * (kN * kN));
+        gstride = inner ? 4ull * tok_e : 4ull * kN;
+        const u64 ginner = 4ull * (head_e + static_cast<size_t>(t0) * tok_e);
+        const u64 glast = p.d_state_out ? reinterpret_cast<u64>(p.d_state_out) + 4ull * static_cast<size_t>(bh) * (kN * kN)
+                                        : s0;
+        // block wv (uniform over the wave) for the row segment, block q for the column one
+        u64 grb;
+        if (inner) {
+            const void *const t = wv == 0 ? p.dr : (wv == 1 ? p.dk : (wv == 2 ? p.da : p.db));
+            grb = reinterpret_cast<u64>(t) + ginner;
+        } else {
+            grb = glast + 4ull * CC * kN * wv;
+        }
+        const u64 gcb = inner ? pick(q == 0, reinterpret_cast<u64>(p.dr),
+                                     pick(q == 1, reinterpret_cast<u64>(p.dk),
+                                          pick(q == 2, reinterpret_cast<u64>(p.da), reinterpret_cast<u64>(p.db)))) +
+                                    ginner
+                              : glast + 4ull * CC * kN * q;
+        const u64 srow_a = s0 + 4ull * (tc * kN + 16 * q);
+        const u64 grow_a = grb + m * gstride + 4ull * 16 * q;
+        scol_a = s0 + 4ull * (16 * q * kN + tc);
+        gcol_a = gcb + 4ull * tc;
+#pragma unroll
+        for (int h4 = 0; h4 < 4; ++h4) {
+            const f32x4 sv = *reinterpret_cast<const GLOBAL_AS f32x4 *>(srow_a + 16u * h4);
+            const f32x4 gv = *reinterpret_cast<const GLOBAL_AS f32x4 *>(grow_a + 16u * h4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                srow[4 * h4 + e] = sv[e];
+                grow[4 * h4 + e] = gv[e];
+            }
+        }
+
         const int tau = tid >> 4, col = (tid & 15) * 4;
         const bool live = tau < L;
         const Tin *const srcs[6] = {static_cast<const Tin *>(p.r), static_cast<const Tin *>(p.w),
@@ -435,128 +483,127 @@ __global__ __launch_bounds__(256) void wkv7_bwdc_chunk_kernel(BwdArgs p, int c_l
         for (int x = 0; x < 6; ++x)
             in4[x] = load4w(srcs[x] + rowp(tau) + col);
         o4 = load4w(p.d_o + rowp(tau) + col);
-        // the checkpoint and G_end, row i, columns j0 .. j0 + 15 (a missing d_state_out
-        // reads the checkpoint and is zeroed), through global pointers
-        const int i = tid >> 2, j0 = (tid & 3) * 16;
-        const u64 s0 = reinterpret_cast<u64>(p.ckpt) +
-                       4ull * (((static_cast<size_t>(bb) * nck + c) * H + hh) * (kN * kN) + i * kN + j0);
-        const bool inner = c < nck - 1, has_g = inner || p.d_state_out != nullptr;
-        const int sidx = i / CC;  // G_end rows of an inner chunk sit in dr, dk, da, db
-        const u64 gin = pick(sidx == 0, reinterpret_cast<u64>(p.dr),
-                             pick(sidx == 1, reinterpret_cast<u64>(p.dk),
-                                  pick(sidx == 2, reinterpret_cast<u64>(p.da), reinterpret_cast<u64>(p.db)))) +
-                        4ull * (head_e + static_cast<size_t>(t0 + i % CC) * tok_e + j0);
-        const u64 gend = reinterpret_cast<u64>(p.d_state_out) +
-                         4ull * (static_cast<size_t>(bh) * (kN * kN) + i * kN + j0);
-        const u64 ge = inner ? gin : (p.d_state_out ? gend : s0);
-        f32x4 s4[4], g4[4];
-#pragma unroll
-        for (int h4 = 0; h4 < 4; ++h4) {
-            s4[h4] = *reinterpret_cast<const GLOBAL_AS f32x4 *>(s0 + 16u * h4);
-            g4[h4] = *reinterpret_cast<const GLOBAL_AS f32x4 *>(ge + 16u * h4);
-        }
+
+        // the rows past the end by masks the compiler cannot turn into branches (a load
+        // moved under one is waited for at once)
+        unsigned keep = live ? ~0u : 0u;
+        asm volatile("" : "+v"(keep));
+        auto mask = [&](float v, float dflt) {
+            return __uint_as_float((__float_as_uint(v) & keep) | (__float_as_uint(dflt) & ~keep));
+        };
+        bool tiny = false;
 #pragma unroll
         for (int x = 0; x < 6; ++x) {
-            const f32x4 v4 = live ? in4[x] : (x == X_W ? f32x4{1.f, 1.f, 1.f, 1.f} : f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                sm.rows[x][tau][col + e] = v4[e];
+            for (int e = 0; e < 4; ++e) {
+                const float v = mask(in4[x][e], x == X_W ? 1.f : 0.f);
+                sm.rows[x][tau][col + e] = v;
+                if (x == X_W)
+                    tiny = tiny || !(fabsf(v) >= kExactBelow);  // NaN included
+            }
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-            sm.rows[X_DO][tau][col + e] = live ? o4[e] : 0.f;
-#pragma unroll
-        for (int h4 = 0; h4 < 4; ++h4)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                sm.sq[0][i][j0 + 4 * h4 + e] = s4[h4][e];
-                sm.sq[1][i][j0 + 4 * h4 + e] = has_g ? g4[h4][e] : 0.f;
-            }
-    }
-    __syncthreads();
-
-    // ---- decay factors, one key per lane of wave 0
-    if (wv == 0) {
-        const int i = lane;
-        float wcol[CC];
-        float wmin = 1.0f;
-#pragma unroll
-        for (int tau = 0; tau < CC; ++tau) {
-            wcol[tau] = sm.rows[X_W][tau][i];
-            wmin = fminf(wmin, fabsf(wcol[tau]));
-        }
-        const bool exact = __ballot(!(wmin >= kExactBelow)) != 0ull;  // NaN included
+            sm.rows[X_DO][tau][col + e] = mask(o4[e], 0.f);
+        const bool any_tiny = __ballot(tiny) != 0ull;
         if (lane == 0)
-            sm.flag = exact ? 1 : 0;
-        if (!exact) {
-            float d[CC];
-            d[REF] = 1.0f;
-#pragma unroll
-            for (int tau = REF + 1; tau < CC; ++tau)
-                d[tau] = d[tau - 1] * wcol[tau];
-#pragma unroll
-            for (int tau = REF - 1; tau >= 0; --tau)
-                d[tau] = d[tau + 1] / wcol[tau + 1];
-            float pr = wcol[0];
-#pragma unroll
-            for (int tau = 1; tau <= REF; ++tau)
-                pr *= wcol[tau];
-            sm.base[i] = pr;
-#pragma unroll
-            for (int tau = 0; tau < CC; ++tau) {
-                const float dp = tau == 0 ? d[0] / wcol[0] : d[tau - 1];
-                const float inv = 1.0f / d[tau];
-                sm.rows[X_D][tau][i] = d[tau];
-                sm.rows[X_R][tau][i] *= d[tau];
-                sm.rows[X_A][tau][i] *= dp;
-                sm.rows[X_B][tau][i] *= inv;
-                sm.rows[X_K][tau][i] *= inv;
-            }
-        }
+            sm.flag[wv] = any_tiny ? 1 : 0;
     }
     __syncthreads();
-    if (sm.flag) {
-        exact_chunk(p, sm, t0, L, head_e, tok_e);
+    if ((sm.flag[0] | sm.flag[1] | sm.flag[2] | sm.flag[3]) != 0) {
+        if (!has_g)
+#pragma unroll
+            for (int jj = 0; jj < 16; ++jj)
+                grow[jj] = 0.f;
+        exact_chunk(p, sm, t0, L, head_e, tok_e, srow, grow);
         return;
     }
+#pragma unroll
+    for (int ii = 0; ii < 16; ++ii) {
+        scol[ii] = *reinterpret_cast<const GLOBAL_AS float *>(scol_a + 4ull * kN * ii);
+        gcol[ii] = *reinterpret_cast<const GLOBAL_AS float *>(gcol_a + gstride * ii);
+    }
 
-    // ---- S^ = diag(P_7) S0, G^ = diag(d_15) G_end, and rowsum(G^ * S^)
+    // ---- decay factors of key tc (each lane of the key forms all 16), applied to this
+    // lane's tokens 4 q .. 4 q + 3 of r, a, b, k
+    float dq[4], dpq[4], iq[4];  // d, d_{tau-1} and 1/d at this lane's tokens
+    float p7, d15;
     {
-        const int i = tid >> 2, j0 = (tid & 3) * 16;
-        const float pr = sm.base[i], d15 = sm.rows[X_D][CC - 1][i];
+        float wcol[CC];
+#pragma unroll
+        for (int tau = 0; tau < CC; ++tau)
+            wcol[tau] = sm.rows[X_W][tau][tc];
+        float d[CC];
+        d[REF] = 1.0f;
+#pragma unroll
+        for (int tau = REF + 1; tau < CC; ++tau)
+            d[tau] = d[tau - 1] * wcol[tau];
+#pragma unroll
+        for (int tau = REF - 1; tau >= 0; --tau)
+            d[tau] = d[tau + 1] / wcol[tau + 1];
+        float pr = wcol[0];
+#pragma unroll
+        for (int tau = 1; tau <= REF; ++tau)
+            pr *= wcol[tau];
+        p7 = pr;
+        d15 = d[CC - 1];
+        if (q == 0) {
+            sm.p7[tc] = pr;
+            sm.d15[tc] = d15;
+        }
+        const float dm1 = d[0] / wcol[0];  // d_{-1}: the factor of a at the chunk's first token
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            dq[e] = sel4(q, d[e], d[4 + e], d[8 + e], d[12 + e]);
+            dpq[e] = sel4(q, e == 0 ? dm1 : d[e - 1], d[3 + e], d[7 + e], d[11 + e]);
+            iq[e] = 1.0f / dq[e];
+            const int tau = 4 * q + e;
+            sm.rows[X_R][tau][tc] *= dq[e];
+            sm.rows[X_A][tau][tc] *= dpq[e];
+            sm.rows[X_B][tau][tc] *= iq[e];
+            sm.rows[X_K][tau][tc] *= iq[e];
+        }
+    }
+    __syncthreads();
+
+    // ---- S^ = diag(P_7) S0, G^ = diag(d_15) G_end on this lane's segments, and
+    // rowsum(G^ * S^) of key tc (over the four lanes of the row)
+    float gs_sum;
+    {
+        if (!has_g)
+#pragma unroll
+            for (int jj = 0; jj < 16; ++jj) {
+                grow[jj] = 0.f;
+                gcol[jj] = 0.f;
+            }
         float acc = 0.f;
 #pragma unroll
         for (int jj = 0; jj < 16; ++jj) {
-            const float sv = sm.sq[0][i][j0 + jj] * pr, gv = sm.sq[1][i][j0 + jj] * d15;
-            sm.sq[0][i][j0 + jj] = sv;
-            sm.sq[1][i][j0 + jj] = gv;
-            acc = fmaf(gv, sv, acc);
+            srow[jj] *= p7;
+            grow[jj] *= d15;
+            acc = fmaf(grow[jj], srow[jj], acc);
         }
-        acc += __shfl_xor(acc, 1);
-        acc += __shfl_xor(acc, 2);
-        if ((tid & 3) == 0)
-            sm.base[i] = acc;
+        acc += __shfl_xor(acc, 16);
+        gs_sum = acc + __shfl_xor(acc, 32);
+#pragma unroll
+        for (int h4 = 0; h4 < 4; ++h4) {
+            const f32x4 pv = *reinterpret_cast<const f32x4 *>(&sm.p7[16 * q + 4 * h4]);
+            const f32x4 dv = *reinterpret_cast<const f32x4 *>(&sm.d15[16 * q + 4 * h4]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                scol[4 * h4 + e] *= pv[e];
+                gcol[4 * h4 + e] *= dv[e];
+            }
+        }
     }
-    __syncthreads();
 
     // ---- matrix-core fragments (16x16x4 fp32: lane (q, m) supplies A[m][k] and B[k][m]
     // for k = 16 q + i over a 64-long sum, k = 4 q + i over a 16-long one; the result
     // holds rows 4 q + e of column m).  Wave wv owns column tile wv of every 16 x 64 result.
-    const int tc = 16 * wv + m;  // this lane's column in the tile
     auto frag_rows = [&](int x, float (&f)[16]) {  // X[m][16 q + i] (also X^T as a B operand)
 #pragma unroll
         for (int i = 0; i < 16; ++i)
             f[i] = sm.rows[x][m][16 * q + i];
-    };
-    auto frag_sq_rows = [&](int sq, float (&f)[16]) {  // S[16 wv + m][16 q + i]: B of Y S^T
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-            f[i] = sm.sq[sq][tc][16 * q + i];
-    };
-    auto frag_sq_cols = [&](int sq, float (&f)[16]) {  // S[16 q + i][16 wv + m]: B of Y S
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-            f[i] = sm.sq[sq][16 * q + i][tc];
     };
     auto frag_tile = [&](int x, float (&f)[4]) {  // X[4 q + i][16 wv + m]: B over tokens
 #pragma unroll
@@ -607,20 +654,16 @@ __global__ __launch_bounds__(256) void wkv7_bwdc_chunk_kernel(BwdArgs p, int c_l
     }
     // ---- this wave's tiles of X = A' S^, dZ = B' G^, dV = K' G^, dR0 = dO S^T, dKv = V G^T
     f32x4 xacc = zero4, dzacc = zero4, dvacc = zero4, dracc = zero4, dkacc = zero4;
-    frag_sq_cols(0, fb);
     frag_rows(X_A, fa);
-    mm64(xacc, fa, fb);
-    frag_sq_cols(1, fb);
+    mm64(xacc, fa, scol);
     frag_rows(X_B, fa);
-    mm64(dzacc, fa, fb);
+    mm64(dzacc, fa, gcol);
     frag_rows(X_K, fa);
-    mm64(dvacc, fa, fb);
-    frag_sq_rows(0, fb);
+    mm64(dvacc, fa, gcol);
     frag_rows(X_DO, fa);
-    mm64(dracc, fa, fb);
-    frag_sq_rows(1, fb);
+    mm64(dracc, fa, srow);
     frag_rows(X_V, fa);
-    mm64(dkacc, fa, fb);
+    mm64(dkacc, fa, grow);
     __syncthreads();
 
     // ---- the 16-long products that need the M's; T = (I - M_ab)^{-1} (wave 0, one
@@ -692,12 +735,10 @@ __global__ __launch_bounds__(256) void wkv7_bwdc_chunk_kernel(BwdArgs p, int c_l
             sm.sm[dst][4 * q + e][m] = acc[e];
     }
     f32x4 daacc = zero4, dbacc = zero4;
-    frag_sq_rows(0, fb);
     frag_rows(X_DX, fa);
-    mm64(daacc, fa, fb);
-    frag_sq_rows(1, fb);
+    mm64(daacc, fa, srow);
     frag_rows(X_Z, fa);
-    mm64(dbacc, fa, fb);
+    mm64(dbacc, fa, grow);
     __syncthreads();
     // dO, dX, Z and V are read no more: their places take dR0, dA0, dBz, dKv
     to_rows(X_DR0, dracc);
@@ -730,28 +771,25 @@ __global__ __launch_bounds__(256) void wkv7_bwdc_chunk_kernel(BwdArgs p, int c_l
     mm16(dkacc, a4, b4);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-        const int tau = 4 * q + e;
-        if (tau < L) {
-            const float d = sm.rows[X_D][tau][tc], inv = __builtin_amdgcn_rcpf(d);
-            const float dp = tau == 0 ? d * __builtin_amdgcn_rcpf(sm.rows[X_W][0][tc]) : sm.rows[X_D][tau - 1][tc];
-            const size_t at = rowp(tau) + tc;
-            p.dr[at] = dracc[e] * d;
-            p.da[at] = daacc[e] * dp;
-            p.db[at] = dbacc[e] * inv;
-            p.dk[at] = dkacc[e] * inv;
+        if (4 * q + e < L) {
+            const size_t at = rowp(4 * q + e) + tc;
+            p.dr[at] = dracc[e] * dq[e];
+            p.da[at] = daacc[e] * dpq[e];
+            p.db[at] = dbacc[e] * iq[e];
+            p.dk[at] = dkacc[e] * iq[e];
         }
     }
 
     // ---- dw, in its direct form.  With Q_s(t) = sum_{u<t} (B'_u dO_s.z_u + K'_u dO_s.v_u)
     // and P_s(t) the same with dX_s, per key:
-    //   w_t dw_t = base + sum_{u<t} (B'_u dBz_u + K'_u dKv_u)
+    //   w_t dw_t = rowsum(G^ * S^) + sum_{u<t} (B'_u dBz_u + K'_u dKv_u)
     //            + sum_{s>=t} R'_s (dR0_s + Q_s(t)) + sum_{s>t} A'_s (dA0_s + P_s(t)).
-    // Thread (key i, wave g) forms the Q/P terms of rows s = g (mod 4) for every token;
-    // the four partials meet in LDS (over S^, no longer read).  The dR0, dA0 terms and the
-    // prefix over u are running sums in the final pass.
-    __syncthreads();
+    // Lane (q, m) forms the Q/P terms of key tc for the rows s = 4 j + q; the four
+    // partials meet by shuffles.  Everything it reads is column tc, which this wave wrote
+    // (or the 16 x 16 matrices, complete since the last barrier): no barrier here.  The
+    // dR0, dA0 terms and the prefix over u are running sums in the final pass.
     {
-        const int i = lane, g = wv;
+        const int i = tc;
         float bu[CC], ku[CC], acc[CC];
 #pragma unroll
         for (int u = 0; u < CC; ++u) {
@@ -760,50 +798,49 @@ __global__ __launch_bounds__(256) void wkv7_bwdc_chunk_kernel(BwdArgs p, int c_l
             acc[u] = 0.f;
         }
 #pragma unroll
-        for (int s = 1; s < CC; ++s) {
-            if ((s & 3) != g)
-                continue;
+        for (int j = 0; j < 4; ++j) {
+            const int s = 4 * j + q;
             const float rs = sm.rows[X_R][s][i], as = sm.rows[X_A][s][i];
             float qr = 0.f, qa = 0.f;
+            // t runs to the largest s of the four lanes; past this lane's s the terms are
+            // formed and dropped (selects, so a non-finite dropped term does no harm)
 #pragma unroll
-            for (int t = 1; t <= s; ++t) {
+            for (int t = 1; t <= 4 * j + 3; ++t) {
                 qr = fmaf(bu[t - 1], sm.sm[W_OZ][s][t - 1], fmaf(ku[t - 1], sm.sm[W_OV][s][t - 1], qr));
-                acc[t] = fmaf(rs, qr, acc[t]);
-                if (t < s) {
-                    qa = fmaf(bu[t - 1], sm.sm[W_XZ][s][t - 1], fmaf(ku[t - 1], sm.sm[W_XV][s][t - 1], qa));
-                    acc[t] = fmaf(as, qa, acc[t]);
-                }
+                qa = fmaf(bu[t - 1], sm.sm[W_XZ][s][t - 1], fmaf(ku[t - 1], sm.sm[W_XV][s][t - 1], qa));
+                const float cr = fmaf(rs, qr, acc[t]);
+                const float ca = fmaf(as, qa, cr);
+                acc[t] = t < s ? ca : (t == s ? cr : acc[t]);
             }
         }
-        __syncthreads();  // every wave is past its reads of S^
-        float *part = &sm.sq[0][0][0];  // [4][16][64]
 #pragma unroll
-        for (int t = 1; t < CC; ++t)
-            part[(g * CC + t) * kN + i] = acc[t];
-        __syncthreads();
+        for (int t = 1; t < CC; ++t) {
+            acc[t] += __shfl_xor(acc[t], 16);
+            acc[t] += __shfl_xor(acc[t], 32);
+        }
         // suffix sums of R'_s dR0_s (s >= t) and A'_s dA0_s (s > t), prefix of the base terms
-        float suf[CC];
+        float tot[CC];
         {
             float sr = 0.f, sa = 0.f;
 #pragma unroll
             for (int t = CC - 1; t >= 0; --t) {
                 sr = fmaf(sm.rows[X_R][t][i], sm.rows[X_DR0][t][i], sr);
-                suf[t] = sr + sa;
+                tot[t] = sr + sa;
                 sa = fmaf(sm.rows[X_A][t][i], sm.rows[X_DA0][t][i], sa);
             }
         }
-        float pre = sm.base[i];
+        float pre = gs_sum;
 #pragma unroll
         for (int t = 0; t < CC; ++t) {
-            if ((t & 3) == g && t < L) {
-                float tot = pre + suf[t];
-                if (t > 0)
-#pragma unroll
-                    for (int gg = 0; gg < 4; ++gg)
-                        tot += part[(gg * CC + t) * kN + i];
-                p.dw[rowp(t) + i] = tot * __builtin_amdgcn_rcpf(sm.rows[X_W][t][i]);
-            }
+            tot[t] = t > 0 ? (pre + tot[t]) + acc[t] : pre + tot[t];
             pre = fmaf(bu[t], sm.rows[X_DBZ][t][i], fmaf(ku[t], sm.rows[X_DKV][t][i], pre));
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int t = 4 * q + e;
+            if (t < L)
+                p.dw[rowp(t) + i] =
+                    sel4(q, tot[e], tot[4 + e], tot[8 + e], tot[12 + e]) * __builtin_amdgcn_rcpf(sm.rows[X_W][t][i]);
         }
     }
 }
