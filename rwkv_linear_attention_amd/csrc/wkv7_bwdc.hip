@@ -529,10 +529,18 @@ __global__ __launch_bounds__(256, 3) void wkv7_bwdc_chunk_kernel(BwdArgs p, int 
     float dq[4], dpq[4], iq[4];  // d, d_{tau-1} and 1/d at this lane's tokens
     float p7, d15;
     {
-        float wcol[CC];
+        float wcol[CC], xr[4], xa[4], xb[4], xk[4];
+        // every read before the first write (see the chain's factors)
 #pragma unroll
         for (int tau = 0; tau < CC; ++tau)
             wcol[tau] = sm.rows[X_W][tau][tc];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            xr[e] = sm.rows[X_R][4 * q + e][tc];
+            xa[e] = sm.rows[X_A][4 * q + e][tc];
+            xb[e] = sm.rows[X_B][4 * q + e][tc];
+            xk[e] = sm.rows[X_K][4 * q + e][tc];
+        }
         float d[CC];
         d[REF] = 1.0f;
 #pragma unroll
@@ -558,10 +566,10 @@ __global__ __launch_bounds__(256, 3) void wkv7_bwdc_chunk_kernel(BwdArgs p, int 
             dpq[e] = sel4(q, e == 0 ? dm1 : d[e - 1], d[3 + e], d[7 + e], d[11 + e]);
             iq[e] = 1.0f / dq[e];
             const int tau = 4 * q + e;
-            sm.rows[X_R][tau][tc] *= dq[e];
-            sm.rows[X_A][tau][tc] *= dpq[e];
-            sm.rows[X_B][tau][tc] *= iq[e];
-            sm.rows[X_K][tau][tc] *= iq[e];
+            sm.rows[X_R][tau][tc] = xr[e] * dq[e];
+            sm.rows[X_A][tau][tc] = xa[e] * dpq[e];
+            sm.rows[X_B][tau][tc] = xb[e] * iq[e];
+            sm.rows[X_K][tau][tc] = xk[e] * iq[e];
         }
     }
     __syncthreads();
@@ -845,30 +853,46 @@ __global__ __launch_bounds__(256, 3) void wkv7_bwdc_chunk_kernel(BwdArgs p, int 
     }
 }
 // ---------------------------------------------------------------------------------
-// The gradient chain in chunk form, on the matrix cores.  One workgroup of four waves
-// per (batch, head); wave wv holds value columns 16 wv .. 16 wv + 15 of G in the
-// accumulator layout: lane (q, n) holds G[16 pt + 4 q + e][16 wv + n] in g[pt][e].
-// Per chunk, last first, with the chunk's factors and matrices formed at its start:
+// The gradient chain in chunk form, on the matrix cores.  One workgroup of eight waves
+// per (batch, head).  Chain wave cw (waves 0 .. 3) holds value columns 16 cw .. 16 cw + 15
+// of G in the accumulator layout: lane (q, n) holds G[16 pt + 4 q + e][16 cw + n] in
+// g[pt][e].  Per chunk, last first:
 //     G^ = diag(d_15) G_end,   dZ = B' G^ + M_rb^T dO,   dX = T^T dZ,
 //     G_end of the chunk before = diag(P_7) (G^ + R'^T dO + A'^T dX).
+// Only B' G^, T^T dZ and A'^T dX depend on G.  The four prep waves (waves 4 .. 7, one
+// beside each chain wave on its SIMD) form everything else one chunk ahead, into the
+// other of two LDS buffers: the factors, A', R', B', M_ab, M_rb, T, and for each chain
+// wave's columns R'^T dO and M_rb^T dO.  A chunk step is two phases, two barriers:
+//   phase 1: chain: G^, B' G^ of chunk c.  prep: the factors of chunk c - 1 (staged raw
+//            rows); M_rb^T dO of chunk c; T of chunk c (wave 7);
+//   phase 2: chain: dX and G of chunk c, stored as G_end of chunk c - 1.  prep: M_ab
+//            (wave 4), M_rb (wave 5) and R'^T dO of chunk c - 1; the raw rows of chunk
+//            c - 2 staged (their loads were issued a chunk before).
 // In dZ = B' G^ a lane's own rows of G^ are its operand: the sum over the keys runs in
 // the order (pt, q, e) of the accumulator layout, and B' is read in that order.  A chunk
-// with a decay below 2^-15 runs the recurrence token by token instead.
-struct GchainSmem {
-    float raw[4][CC][RS];  // r, w, a, b (identity steps past the end)
-    float der[3][CC][RS];  // A', R', B'
-    float dout[CC][RS];    // dO (zero past the end)
-    float sm[3][CC][SS];   // M_ab, M_rb, T
+// with a decay below 2^-15 runs the recurrence token by token instead (chain waves, in
+// phase 1, on the raw rows, which the prep waves copied into its buffer).
+struct GchainBuf {
+    float der[4][CC][RS];   // A', R', B' (raw a, r, b on the exact path) and raw w
+    float dout[CC][RS];     // dO (zero past the end)
+    float sm[3][CC][SS];    // M_ab, M_rb, T
     alignas(16) float d15[kN];
     alignas(16) float p7[kN];
-    int flag;
+    int flag[4];            // per prep wave: a decay below 2^-15 among its keys
+    float qd[4][16][64];    // R'^T dO of chain wave cw, value 4 pt + e of lane l
+    float yd[4][4][64];     // M_rb^T dO of chain wave cw, value e of lane l
+};
+// 104.3 KB
+struct GchainSmem {
+    float raw[4][CC][RS];  // r, w, a, b of the chunk being prepared (identity steps past the end)
+    GchainBuf buf[2];
 };
 enum { G_R, G_W, G_A, G_B };
-enum { D_A, D_R, D_B };
+enum { D_A, D_R, D_B, D_W };
 enum { S_AB, S_RB, S_T };
 
 template <typename Tin, bool HAS_DOUT>
-__global__ __launch_bounds__(256) void wkv7_bwdc_gchain_kernel(BwdArgs p)
+__global__ __launch_bounds__(512) void wkv7_bwdc_gchain_kernel(BwdArgs p)
 {
     __shared__ GchainSmem sm;
     typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
@@ -876,21 +900,20 @@ __global__ __launch_bounds__(256) void wkv7_bwdc_gchain_kernel(BwdArgs p)
     using Raw = typename std::conditional<sizeof(Tin) == 2, u32x2, u32x4v>::type;
     const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, n = lane & 15;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool chain = wv < 4;
+    const int w4 = wv & 3;    // chain wave cw, or the prep wave's partner
+    const int ptid = tid & 255;
     const int bh = blockIdx.x;
     const int H = p.H, T = p.T;
     const int bb = bh / H, hh = bh - bb * H;
     const int nck = (T + CC - 1) / CC;
-    const int col = 16 * wv + n;
+    const int col = 16 * w4 + n;  // a chain wave's column; a prep wave's key (factors)
     const size_t tok_e = static_cast<size_t>(H) * kN;
     const size_t head_e = static_cast<size_t>(bb) * T * tok_e + static_cast<size_t>(hh) * kN;
     const size_t sbase = static_cast<size_t>(bh) * (kN * kN) + col;
+    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
     float g[4][4];
-#pragma unroll
-    for (int pt = 0; pt < 4; ++pt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            g[pt][e] = HAS_DOUT ? p.d_state_out[sbase + (16 * pt + 4 * q + e) * kN] : 0.0f;
     auto put_state = [&](float *dst) {
 #pragma unroll
         for (int pt = 0; pt < 4; ++pt)
@@ -898,14 +921,31 @@ __global__ __launch_bounds__(256) void wkv7_bwdc_gchain_kernel(BwdArgs p)
             for (int e = 0; e < 4; ++e)
                 dst[sbase + (16 * pt + 4 * q + e) * kN] = g[pt][e];
     };
-    if (T == 0) {  // no tokens: the gradient passes through
-        put_state(p.d_state_in);
+    if (chain) {
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                g[pt][e] = HAS_DOUT ? p.d_state_out[sbase + (16 * pt + 4 * q + e) * kN] : 0.0f;
+        // the loads complete here: registers still awaiting a load at the loop's head
+        // would make every chunk wait on the memory counter, which the G_end stores of
+        // the chunk before also hold
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                asm volatile("" : "+v"(g[pt][e]));
+        if (T == 0) {  // no tokens: the gradient passes through
+            put_state(p.d_state_in);
+            return;
+        }
+    } else if (T == 0) {
         return;
     }
 
-    // staging of a chunk: thread (token tid / 16, channels 4 (tid % 16) ..) loads four
+    // staging (prep waves): thread (token ptid / 16, channels 4 (ptid % 16) ..) loads four
     // elements of r, w, a, b and of dO, kept as raw bits until they are stored to LDS
-    const int s_tau = tid >> 4, s_c4 = (tid & 15) * 4;
+    const int s_tau = ptid >> 4, s_c4 = (ptid & 15) * 4;
     Raw rin[4];
     u32x4v rdo;
     auto stage_load = [&](int c) {
@@ -920,7 +960,7 @@ __global__ __launch_bounds__(256) void wkv7_bwdc_gchain_kernel(BwdArgs p)
         rdo = *reinterpret_cast<const GLOBAL_AS u32x4v *>(
             reinterpret_cast<const GLOBAL_AS float *>(reinterpret_cast<u64>(p.d_o)) + off);
     };
-    auto stage_store = [&](int c) {
+    auto stage_store = [&](int c, GchainBuf &b) {
         const bool live = s_tau < min(CC, T - c * CC);
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
@@ -939,176 +979,293 @@ __global__ __launch_bounds__(256) void wkv7_bwdc_gchain_kernel(BwdArgs p)
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-            sm.dout[s_tau][s_c4 + e] = live ? __uint_as_float(rdo[e]) : 0.f;
+            b.dout[s_tau][s_c4 + e] = live ? __uint_as_float(rdo[e]) : 0.f;
+    };
+    auto exact_of = [](const GchainBuf &b) { return (b.flag[0] | b.flag[1] | b.flag[2] | b.flag[3]) != 0; };
+
+    // (prep) the factors of the staged chunk, and its A', R', B': lane (q, n) of prep
+    // wave w4 forms those of key 16 w4 + n and writes its tokens 4 q .. 4 q + 3
+    auto factors = [&](GchainBuf &b) {
+        const int i = col;
+        float wc[CC], ra[4], rr[4], rb[4];
+        // every read before the first write (LDS writes the compiler cannot tell apart
+        // from the reads would make each read wait for the write before it)
+#pragma unroll
+        for (int tau = 0; tau < CC; ++tau)
+            wc[tau] = sm.raw[G_W][tau][i];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            ra[e] = sm.raw[G_A][4 * q + e][i];
+            rr[e] = sm.raw[G_R][4 * q + e][i];
+            rb[e] = sm.raw[G_B][4 * q + e][i];
+        }
+        bool tiny = false;
+#pragma unroll
+        for (int tau = 0; tau < CC; ++tau)
+            tiny = tiny || !(fabsf(wc[tau]) >= kExactBelow);  // NaN included
+        const bool any_tiny = __ballot(tiny) != 0ull;
+        if (lane == 0)
+            b.flag[w4] = any_tiny ? 1 : 0;
+        float d[CC];
+        d[REF] = 1.0f;
+#pragma unroll
+        for (int tau = REF + 1; tau < CC; ++tau)
+            d[tau] = d[tau - 1] * wc[tau];
+#pragma unroll
+        for (int tau = REF - 1; tau >= 0; --tau)
+            d[tau] = d[tau + 1] * __builtin_amdgcn_rcpf(wc[tau + 1]);
+        float pr = wc[0];
+#pragma unroll
+        for (int tau = 1; tau <= REF; ++tau)
+            pr *= wc[tau];
+        if (q == 0) {
+            b.p7[i] = pr;
+            b.d15[i] = d[CC - 1];
+        }
+        const float dm1 = d[0] * __builtin_amdgcn_rcpf(wc[0]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int tau = 4 * q + e;
+            const float dq = sel4(q, d[e], d[4 + e], d[8 + e], d[12 + e]);
+            const float dp = sel4(q, e == 0 ? dm1 : d[e - 1], d[3 + e], d[7 + e], d[11 + e]);
+            b.der[D_A][tau][i] = ra[e] * dp;
+            b.der[D_R][tau][i] = rr[e] * dq;
+            b.der[D_B][tau][i] = rb[e] * __builtin_amdgcn_rcpf(dq);
+        }
+    };
+    // (prep) the exact path keeps the raw rows: this thread copies the elements it
+    // staged (and is the one to overwrite them next)
+    auto copy_raw = [&](GchainBuf &b) {
+        float v[4][4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            v[0][e] = sm.raw[G_A][s_tau][s_c4 + e];
+            v[1][e] = sm.raw[G_R][s_tau][s_c4 + e];
+            v[2][e] = sm.raw[G_B][s_tau][s_c4 + e];
+            v[3][e] = sm.raw[G_W][s_tau][s_c4 + e];
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            b.der[D_A][s_tau][s_c4 + e] = v[0][e];
+            b.der[D_R][s_tau][s_c4 + e] = v[1][e];
+            b.der[D_B][s_tau][s_c4 + e] = v[2][e];
+            b.der[D_W][s_tau][s_c4 + e] = v[3][e];
+        }
+    };
+    // (prep) M_ab = tril(A' B'^T, -1) (wave 4), M_rb = tril(R' B'^T) (wave 5)
+    auto mprod = [&](GchainBuf &b) {
+        if (w4 < 2) {
+            const int xa = w4 == 0 ? D_A : D_R;
+            f32x4 acc = zero4;
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                acc = mfma4(b.der[xa][n][16 * q + i], b.der[D_B][n][16 * q + i], acc);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int tau = 4 * q + e;
+                const bool keep = w4 == 0 ? n < tau : n <= tau;  // entries above are dropped
+                b.sm[w4 == 0 ? S_AB : S_RB][tau][n] = keep ? acc[e] : 0.f;
+            }
+        }
+    };
+    // (prep, wave 7) T = (I - M_ab)^{-1}, a column per lane (T = I + M_ab T row by row)
+    auto tsolve = [&](GchainBuf &b) {
+        const int sc = lane & 15;
+        float tcol[CC];
+#pragma unroll
+        for (int t = 0; t < CC; ++t) {
+            float acc[4] = {t == sc ? 1.f : 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int u = 0; u < t; ++u)
+                acc[u & 3] = fmaf(b.sm[S_AB][t][u], tcol[u], acc[u & 3]);
+            tcol[t] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+        }
+        if (lane < 16)
+#pragma unroll
+            for (int t = 0; t < CC; ++t)
+                b.sm[S_T][t][sc] = tcol[t];
+    };
+    // (prep) R'^T dO at the partner chain wave's columns, tile by tile (keys 16 pt ..), in
+    // its accumulator layout
+    auto qprod = [&](GchainBuf &b) {
+        float dob[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            dob[i] = b.dout[4 * q + i][col];
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt) {
+            f32x4 acc = zero4;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                acc = mfma4(b.der[D_R][4 * q + i][16 * pt + n], dob[i], acc);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                b.qd[w4][4 * pt + e][lane] = acc[e];
+        }
+    };
+    // (prep) M_rb^T dO at the partner's columns
+    auto yprod = [&](GchainBuf &b) {
+        f32x4 acc = zero4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            acc = mfma4(b.sm[S_RB][4 * q + i][n], b.dout[4 * q + i][col], acc);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            b.yd[w4][e][lane] = acc[e];
     };
 
-    stage_load(nck - 1);
-    for (int c = nck - 1; c >= 0; --c) {
-        stage_store(c);
-        __syncthreads();
+    // ---- prologue: the last chunk prepared in buffer 0, the one before it staged
+    int c = nck - 1;
+    if (!chain) {
+        stage_load(c);
+        stage_store(c, sm.buf[0]);
         if (c > 0)
-            stage_load(c - 1);  // in flight during this chunk
-        // ---- the chunk's factors and A', R', B' (wave 0, one key per lane)
-        if (wv == 0) {
-            const int i = lane;
-            float wc[CC];
-            float wmin = 1.0f;
-#pragma unroll
-            for (int tau = 0; tau < CC; ++tau) {
-                wc[tau] = sm.raw[G_W][tau][i];
-                wmin = fminf(wmin, fabsf(wc[tau]));
-            }
-            const bool exact = __ballot(!(wmin >= kExactBelow)) != 0ull;  // NaN included
-            if (lane == 0)
-                sm.flag = exact ? 1 : 0;
-            if (!exact) {
-                float d[CC];
-                d[REF] = 1.0f;
-#pragma unroll
-                for (int tau = REF + 1; tau < CC; ++tau)
-                    d[tau] = d[tau - 1] * wc[tau];
-#pragma unroll
-                for (int tau = REF - 1; tau >= 0; --tau)
-                    d[tau] = d[tau + 1] * __builtin_amdgcn_rcpf(wc[tau + 1]);
-                float pr = wc[0];
-#pragma unroll
-                for (int tau = 1; tau <= REF; ++tau)
-                    pr *= wc[tau];
-                sm.p7[i] = pr;
-                sm.d15[i] = d[CC - 1];
-#pragma unroll
-                for (int tau = 0; tau < CC; ++tau) {
-                    const float dp = tau == 0 ? d[0] * __builtin_amdgcn_rcpf(wc[0]) : d[tau - 1];
-                    sm.der[D_A][tau][i] = sm.raw[G_A][tau][i] * dp;
-                    sm.der[D_R][tau][i] = sm.raw[G_R][tau][i] * d[tau];
-                    sm.der[D_B][tau][i] = sm.raw[G_B][tau][i] * __builtin_amdgcn_rcpf(d[tau]);
-                }
-            }
-        }
-        __syncthreads();
-        if (sm.flag) {
-            // the recurrence over the chunk's tokens, wave-local: c = G^T b sums the lane's
-            // sixteen keys, then the four lanes of the column (lanes n + 16 q)
-            const int L = min(CC, T - c * CC);
-            for (int t = L - 1; t >= 0; --t) {
-                const float dj = sm.dout[t][col];
-                float cs = 0.f;
-#pragma unroll
-                for (int pt = 0; pt < 4; ++pt)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int key = 16 * pt + 4 * q + e;
-                        g[pt][e] = fmaf(sm.raw[G_R][t][key], dj, g[pt][e]);
-                        cs = fmaf(sm.raw[G_B][t][key], g[pt][e], cs);
-                    }
-                cs += __shfl_xor(cs, 16);
-                cs += __shfl_xor(cs, 32);
-#pragma unroll
-                for (int pt = 0; pt < 4; ++pt)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int key = 16 * pt + 4 * q + e;
-                        g[pt][e] = fmaf(sm.raw[G_W][t][key], g[pt][e], sm.raw[G_A][t][key] * cs);
-                    }
-            }
+            stage_load(c - 1);
+    }
+    __syncthreads();
+    if (!chain)
+        factors(sm.buf[0]);
+    __syncthreads();
+    if (!chain) {
+        if (exact_of(sm.buf[0])) {
+            copy_raw(sm.buf[0]);
         } else {
-            const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
-            // G^ = diag(d_15) G
-            float gh[4][4];
-#pragma unroll
-            for (int pt = 0; pt < 4; ++pt) {
-                const f32x4 d4 = *reinterpret_cast<const f32x4 *>(&sm.d15[16 * pt + 4 * q]);
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    gh[pt][e] = g[pt][e] * d4[e];
-            }
-            // M_ab = tril(A' B'^T, -1) (wave 0), M_rb = tril(R' B'^T) (wave 1)
-            if (wv < 2) {
-                const int xa = wv == 0 ? D_A : D_R;
-                f32x4 acc = zero4;
-#pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    acc = mfma4(sm.der[xa][n][16 * q + i], sm.der[D_B][n][16 * q + i], acc);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int tau = 4 * q + e;
-                    const bool keep = wv == 0 ? n < tau : n <= tau;
-                    sm.sm[wv == 0 ? S_AB : S_RB][tau][n] = keep ? acc[e] : 0.f;
-                }
-            }
-            // dZ = B' G^ (keys in the accumulator order)
-            f32x4 dz0 = zero4, dz1 = zero4;
-#pragma unroll
-            for (int pt = 0; pt < 4; ++pt)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float a = sm.der[D_B][n][16 * pt + 4 * q + e];
-                    if (pt & 1)
-                        dz1 = mfma4(a, gh[pt][e], dz1);
-                    else
-                        dz0 = mfma4(a, gh[pt][e], dz0);
-                }
-            f32x4 dz = dz0 + dz1;
-            __syncthreads();
-            // dZ += M_rb^T dO; T = (I - M_ab)^{-1} (wave 0, a column per lane: T = I + M_ab T)
-            float dob[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                dob[i] = sm.dout[4 * q + i][col];
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                dz = mfma4(sm.sm[S_RB][4 * q + i][n], dob[i], dz);
-            if (wv == 0) {
-                const int sc = lane & 15;
-                float tcol[CC];
-#pragma unroll
-                for (int t = 0; t < CC; ++t) {
-                    float acc[4] = {t == sc ? 1.f : 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int u = 0; u < t; ++u)
-                        acc[u & 3] = fmaf(sm.sm[S_AB][t][u], tcol[u], acc[u & 3]);
-                    tcol[t] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-                }
-                if (lane < 16)
-#pragma unroll
-                    for (int t = 0; t < CC; ++t)
-                        sm.sm[S_T][t][sc] = tcol[t];
-            }
-            __syncthreads();
-            // dX = T^T dZ (the B operand is this lane's own rows of dZ)
-            f32x4 dx = zero4;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                dx = mfma4(sm.sm[S_T][4 * q + i][n], dz[i], dx);
-            // G_end of the chunk before = diag(P_7) (G^ + R'^T dO + A'^T dX), tile by tile
-#pragma unroll
-            for (int pt = 0; pt < 4; ++pt) {
-                f32x4 acc = {gh[pt][0], gh[pt][1], gh[pt][2], gh[pt][3]};
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    acc = mfma4(sm.der[D_R][4 * q + i][16 * pt + n], dob[i], acc);
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    acc = mfma4(sm.der[D_A][4 * q + i][16 * pt + n], dx[i], acc);
-                const f32x4 p4 = *reinterpret_cast<const f32x4 *>(&sm.p7[16 * pt + 4 * q]);
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    g[pt][e] = acc[e] * p4[e];
-            }
+            mprod(sm.buf[0]);
+            qprod(sm.buf[0]);
         }
         if (c > 0) {
-            // G_end of chunk c - 1: key row 16 pt + 4 q + e goes to token 16 (c - 1) + 4 q + e
-            // of tensor pt (dr, dk, da, db)
-            float *const outs[4] = {p.dr, p.dk, p.da, p.db};
+            stage_store(c - 1, sm.buf[1]);
+            if (c > 1)
+                stage_load(c - 2);
+        }
+    }
+    __syncthreads();
+
+    // The chain waves and the prep waves run loops of their own with the same barriers
+    // (two per chunk), so that neither waits on the other's memory operations.
+    if (chain) {
+        for (int k = 0; c >= 0; ++k, --c) {
+            const GchainBuf &cur = sm.buf[k & 1];
+            // ---- phase 1: G^ = diag(d_15) G;  dZ = B' G^ (keys in the accumulator order)
+            const bool ex = exact_of(cur);
+            float gh[4][4];
+            f32x4 dz = zero4;
+            if (ex) {
+                // the recurrence over the chunk's tokens, wave-local: c = G^T b sums the
+                // lane's sixteen keys, then the four lanes of the column (lanes n + 16 q)
+                const int L = min(CC, T - c * CC);
+                for (int t = L - 1; t >= 0; --t) {
+                    const float dj = cur.dout[t][col];
+                    float cs = 0.f;
 #pragma unroll
-            for (int pt = 0; pt < 4; ++pt)
+                    for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int key = 16 * pt + 4 * q + e;
+                            g[pt][e] = fmaf(cur.der[D_R][t][key], dj, g[pt][e]);
+                            cs = fmaf(cur.der[D_B][t][key], g[pt][e], cs);
+                        }
+                    cs += __shfl_xor(cs, 16);
+                    cs += __shfl_xor(cs, 32);
+#pragma unroll
+                    for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int key = 16 * pt + 4 * q + e;
+                            g[pt][e] = fmaf(cur.der[D_W][t][key], g[pt][e], cur.der[D_A][t][key] * cs);
+                        }
+                }
+            } else {
+#pragma unroll
+                for (int pt = 0; pt < 4; ++pt) {
+                    const f32x4 d4 = *reinterpret_cast<const f32x4 *>(&cur.d15[16 * pt + 4 * q]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        gh[pt][e] = g[pt][e] * d4[e];
+                }
+                f32x4 dz0 = zero4, dz1 = zero4;
+#pragma unroll
+                for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float a = cur.der[D_B][n][16 * pt + 4 * q + e];
+                        if (pt & 1)
+                            dz1 = mfma4(a, gh[pt][e], dz1);
+                        else
+                            dz0 = mfma4(a, gh[pt][e], dz0);
+                    }
+                dz = dz0 + dz1;
+            }
+            __syncthreads();
+            // ---- phase 2
+            if (!ex) {
+                // dZ += M_rb^T dO;  dX = T^T dZ (the B operand is this lane's own rows of dZ)
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    outs[pt][head_e + static_cast<size_t>((c - 1) * CC + 4 * q + e) * tok_e + col] = g[pt][e];
+                    dz[e] += cur.yd[w4][e][lane];
+                f32x4 dx = zero4;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    dx = mfma4(cur.sm[S_T][4 * q + i][n], dz[i], dx);
+                // G_end of the chunk before = diag(P_7) (G^ + R'^T dO + A'^T dX), tile by tile
+#pragma unroll
+                for (int pt = 0; pt < 4; ++pt) {
+                    f32x4 acc;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        acc[e] = gh[pt][e] + cur.qd[w4][4 * pt + e][lane];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        acc = mfma4(cur.der[D_A][4 * q + i][16 * pt + n], dx[i], acc);
+                    const f32x4 p4 = *reinterpret_cast<const f32x4 *>(&cur.p7[16 * pt + 4 * q]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        g[pt][e] = acc[e] * p4[e];
+                }
+            }
+            if (c > 0) {
+                // G_end of chunk c - 1: key row 16 pt + 4 q + e goes to token
+                // 16 (c - 1) + 4 q + e of tensor pt (dr, dk, da, db)
+                float *const outs[4] = {p.dr, p.dk, p.da, p.db};
+#pragma unroll
+                for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        outs[pt][head_e + static_cast<size_t>((c - 1) * CC + 4 * q + e) * tok_e + col] = g[pt][e];
+            }
+            __syncthreads();
         }
-        __syncthreads();  // the chunk's LDS is read no more
+        put_state(p.d_state_in);
+    } else {
+        for (int k = 0; c >= 0; ++k, --c) {
+            GchainBuf &cur = sm.buf[k & 1], &nxt = sm.buf[(k & 1) ^ 1];
+            // ---- phase 1: M_rb^T dO and T of chunk c; the factors of chunk c - 1
+            if (!exact_of(cur)) {
+                yprod(cur);
+                if (w4 == 3)
+                    tsolve(cur);
+            }
+            if (c > 0)
+                factors(nxt);
+            __syncthreads();
+            // ---- phase 2: chunk c - 1's matrices (its raw rows are still staged), then
+            // chunk c - 2 staged (over chunk c's dO, read no more)
+            if (c > 0) {
+                if (exact_of(nxt)) {
+                    copy_raw(nxt);
+                } else {
+                    mprod(nxt);
+                    qprod(nxt);
+                }
+                if (c > 1) {
+                    stage_store(c - 2, cur);
+                    if (c > 2)
+                        stage_load(c - 3);
+                }
+            }
+            __syncthreads();
+        }
     }
-    put_state(p.d_state_in);
 }
 
 template <typename Tin>
@@ -1128,10 +1285,10 @@ hipError_t launch_bwdc_t(const BwdArgs &p, hipStream_t stream)
         else
             hipLaunchKernelGGL((wkv7_bwdc_chain_kernel<Tin, false>), cgrid, dim3(GNW * 64), 0, stream, p);
     } else if (p.d_state_out) {
-        hipLaunchKernelGGL((wkv7_bwdc_gchain_kernel<Tin, true>), dim3(static_cast<unsigned>(nbh)), dim3(256), 0,
+        hipLaunchKernelGGL((wkv7_bwdc_gchain_kernel<Tin, true>), dim3(static_cast<unsigned>(nbh)), dim3(512), 0,
                            stream, p);
     } else {
-        hipLaunchKernelGGL((wkv7_bwdc_gchain_kernel<Tin, false>), dim3(static_cast<unsigned>(nbh)), dim3(256), 0,
+        hipLaunchKernelGGL((wkv7_bwdc_gchain_kernel<Tin, false>), dim3(static_cast<unsigned>(nbh)), dim3(512), 0,
                            stream, p);
     }
     // the other chunks, fewer than 2^32 threads (2^24 workgroups) per launch
