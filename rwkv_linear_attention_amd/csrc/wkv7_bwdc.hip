@@ -859,14 +859,15 @@ __global__ __launch_bounds__(256, 3) void wkv7_bwdc_chunk_kernel(BwdArgs p, int 
 // g[pt][e].  Per chunk, last first:
 //     G^ = diag(d_15) G_end,   dZ = B' G^ + M_rb^T dO,   dX = T^T dZ,
 //     G_end of the chunk before = diag(P_7) (G^ + R'^T dO + A'^T dX).
-// Only B' G^, T^T dZ and A'^T dX depend on G.  The four prep waves (waves 4 .. 7, one
-// beside each chain wave on its SIMD) form everything else one chunk ahead, into the
-// other of two LDS buffers: the factors, A', R', B', M_ab, M_rb, T, and for each chain
-// wave's columns R'^T dO and M_rb^T dO.  A chunk step is two phases, two barriers:
-//   phase 1: chain: G^, B' G^ of chunk c.  prep: the factors of chunk c - 1 (staged raw
-//            rows); M_rb^T dO of chunk c; T of chunk c (wave 7);
-//   phase 2: chain: dX and G of chunk c, stored as G_end of chunk c - 1.  prep: M_ab
-//            (wave 4), M_rb (wave 5) and R'^T dO of chunk c - 1; the raw rows of chunk
+// Only B' G^, T^T dZ and A'^T dX depend on G.  The rest is formed a phase or a chunk
+// ahead, in two LDS buffers (chunk c in one, chunk c - 1 in the other).  A chunk step is
+// two phases and two barriers:
+//   phase 1: chain waves: dZ of chunk c, then the factors, A', R', B' of chunk c - 1
+//            (from its staged raw rows).  Prep waves (4 .. 7, one beside each chain
+//            wave on its SIMD): T of chunk c (wave 7); R'^T dO of chunk c at the chain
+//            waves' columns (waves 4 .. 6);
+//   phase 2: chain waves: dX and G of chunk c, stored as G_end of chunk c - 1.  Prep
+//            waves: M_ab (wave 4) and M_rb (wave 5) of chunk c - 1; the raw rows of chunk
 //            c - 2 staged (their loads were issued a chunk before).
 // In dZ = B' G^ a lane's own rows of G^ are its operand: the sum over the keys runs in
 // the order (pt, q, e) of the accumulator layout, and B' is read in that order.  A chunk
@@ -878,11 +879,10 @@ struct GchainBuf {
     float sm[3][CC][SS];    // M_ab, M_rb, T
     alignas(16) float d15[kN];
     alignas(16) float p7[kN];
-    int flag[4];            // per prep wave: a decay below 2^-15 among its keys
+    int flag[4];            // per chain wave: a decay below 2^-15 among its keys
     float qd[4][16][64];    // R'^T dO of chain wave cw, value 4 pt + e of lane l
-    float yd[4][4][64];     // M_rb^T dO of chain wave cw, value e of lane l
 };
-// 104.3 KB
+// 100.2 KB
 struct GchainSmem {
     float raw[4][CC][RS];  // r, w, a, b of the chunk being prepared (identity steps past the end)
     GchainBuf buf[2];
@@ -983,8 +983,8 @@ __global__ __launch_bounds__(512) void wkv7_bwdc_gchain_kernel(BwdArgs p)
     };
     auto exact_of = [](const GchainBuf &b) { return (b.flag[0] | b.flag[1] | b.flag[2] | b.flag[3]) != 0; };
 
-    // (prep) the factors of the staged chunk, and its A', R', B': lane (q, n) of prep
-    // wave w4 forms those of key 16 w4 + n and writes its tokens 4 q .. 4 q + 3
+    // (chain) the factors of the staged chunk, and its A', R', B': lane (q, n) of chain
+    // wave cw forms those of key 16 cw + n and writes its tokens 4 q .. 4 q + 3
     auto factors = [&](GchainBuf &b) {
         const int i = col;
         float wc[CC], ra[4], rr[4], rb[4];
@@ -1085,13 +1085,14 @@ __global__ __launch_bounds__(512) void wkv7_bwdc_gchain_kernel(BwdArgs p)
             for (int t = 0; t < CC; ++t)
                 b.sm[S_T][t][sc] = tcol[t];
     };
-    // (prep) R'^T dO at the partner chain wave's columns, tile by tile (keys 16 pt ..), in
-    // its accumulator layout
-    auto qprod = [&](GchainBuf &b) {
+    // (prep) R'^T dO at chain wave cw's columns, tile by tile (keys 16 pt ..), in its
+    // accumulator layout
+    auto qprod = [&](GchainBuf &b, int cw) {
+        const int qc = 16 * cw + n;
         float dob[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            dob[i] = b.dout[4 * q + i][col];
+            dob[i] = b.dout[4 * q + i][qc];
 #pragma unroll
         for (int pt = 0; pt < 4; ++pt) {
             f32x4 acc = zero4;
@@ -1100,18 +1101,8 @@ __global__ __launch_bounds__(512) void wkv7_bwdc_gchain_kernel(BwdArgs p)
                 acc = mfma4(b.der[D_R][4 * q + i][16 * pt + n], dob[i], acc);
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                b.qd[w4][4 * pt + e][lane] = acc[e];
+                b.qd[cw][4 * pt + e][lane] = acc[e];
         }
-    };
-    // (prep) M_rb^T dO at the partner's columns
-    auto yprod = [&](GchainBuf &b) {
-        f32x4 acc = zero4;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            acc = mfma4(b.sm[S_RB][4 * q + i][n], b.dout[4 * q + i][col], acc);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            b.yd[w4][e][lane] = acc[e];
     };
 
     // ---- prologue: the last chunk prepared in buffer 0, the one before it staged
@@ -1123,16 +1114,14 @@ __global__ __launch_bounds__(512) void wkv7_bwdc_gchain_kernel(BwdArgs p)
             stage_load(c - 1);
     }
     __syncthreads();
-    if (!chain)
+    if (chain)
         factors(sm.buf[0]);
     __syncthreads();
     if (!chain) {
-        if (exact_of(sm.buf[0])) {
+        if (exact_of(sm.buf[0]))
             copy_raw(sm.buf[0]);
-        } else {
+        else
             mprod(sm.buf[0]);
-            qprod(sm.buf[0]);
-        }
         if (c > 0) {
             stage_store(c - 1, sm.buf[1]);
             if (c > 1)
@@ -1144,11 +1133,16 @@ __global__ __launch_bounds__(512) void wkv7_bwdc_gchain_kernel(BwdArgs p)
     // The chain waves and the prep waves run loops of their own with the same barriers
     // (two per chunk), so that neither waits on the other's memory operations.
     if (chain) {
+        // G_end of chunk c - 1, key row 16 pt + 4 q + e, goes to token 16 (c - 1) + 4 q + e
+        // of tensor pt (dr, dk, da, db): byte offsets from this lane's row of token 0
+        const u64 e_step = 4ull * tok_e;
+        const u64 row0 = 4ull * (head_e + static_cast<size_t>(4 * q) * tok_e + col);
         for (int k = 0; c >= 0; ++k, --c) {
-            const GchainBuf &cur = sm.buf[k & 1];
+            GchainBuf &cur = sm.buf[k & 1], &nxt = sm.buf[(k & 1) ^ 1];
             // ---- phase 1: G^ = diag(d_15) G;  dZ = B' G^ (keys in the accumulator order)
+            // + M_rb^T dO;  then chunk c - 1's factors
             const bool ex = exact_of(cur);
-            float gh[4][4];
+            float gh[4][4], ap[4][4], p7v[4][4];
             f32x4 dz = zero4;
             if (ex) {
                 // the recurrence over the chunk's tokens, wave-local: c = G^T b sums the
@@ -1183,7 +1177,10 @@ __global__ __launch_bounds__(512) void wkv7_bwdc_gchain_kernel(BwdArgs p)
                     for (int e = 0; e < 4; ++e)
                         gh[pt][e] = g[pt][e] * d4[e];
                 }
-                f32x4 dz0 = zero4, dz1 = zero4;
+                f32x4 dz0 = zero4, dz1 = zero4, dzy = zero4;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    dzy = mfma4(cur.sm[S_RB][4 * q + i][n], cur.dout[4 * q + i][col], dzy);
 #pragma unroll
                 for (int pt = 0; pt < 4; ++pt)
 #pragma unroll
@@ -1194,20 +1191,28 @@ __global__ __launch_bounds__(512) void wkv7_bwdc_gchain_kernel(BwdArgs p)
                         else
                             dz0 = mfma4(a, gh[pt][e], dz0);
                     }
-                dz = dz0 + dz1;
-            }
-            __syncthreads();
-            // ---- phase 2
-            if (!ex) {
-                // dZ += M_rb^T dO;  dX = T^T dZ (the B operand is this lane's own rows of dZ)
+                dz = (dz0 + dz1) + dzy;
+                // the operands of phase 2 that are ready now
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    dz[e] += cur.yd[w4][e][lane];
+                for (int pt = 0; pt < 4; ++pt) {
+                    const f32x4 p4 = *reinterpret_cast<const f32x4 *>(&cur.p7[16 * pt + 4 * q]);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        ap[pt][i] = cur.der[D_A][4 * q + i][16 * pt + n];
+                        p7v[pt][i] = p4[i];
+                    }
+                }
+            }
+            if (c > 0)
+                factors(nxt);
+            __syncthreads();
+            // ---- phase 2: dX = T^T dZ (the B operand is this lane's own rows of dZ);
+            // G_end of the chunk before = diag(P_7) (G^ + R'^T dO + A'^T dX), tile by tile
+            if (!ex) {
                 f32x4 dx = zero4;
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     dx = mfma4(cur.sm[S_T][4 * q + i][n], dz[i], dx);
-                // G_end of the chunk before = diag(P_7) (G^ + R'^T dO + A'^T dX), tile by tile
 #pragma unroll
                 for (int pt = 0; pt < 4; ++pt) {
                     f32x4 acc;
@@ -1216,22 +1221,22 @@ __global__ __launch_bounds__(512) void wkv7_bwdc_gchain_kernel(BwdArgs p)
                         acc[e] = gh[pt][e] + cur.qd[w4][4 * pt + e][lane];
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        acc = mfma4(cur.der[D_A][4 * q + i][16 * pt + n], dx[i], acc);
-                    const f32x4 p4 = *reinterpret_cast<const f32x4 *>(&cur.p7[16 * pt + 4 * q]);
+                        acc = mfma4(ap[pt][i], dx[i], acc);
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        g[pt][e] = acc[e] * p4[e];
+                        g[pt][e] = acc[e] * p7v[pt][e];
                 }
             }
             if (c > 0) {
-                // G_end of chunk c - 1: key row 16 pt + 4 q + e goes to token
-                // 16 (c - 1) + 4 q + e of tensor pt (dr, dk, da, db)
+                const u64 rowc = row0 + static_cast<u64>((c - 1) * CC) * e_step;
                 float *const outs[4] = {p.dr, p.dk, p.da, p.db};
 #pragma unroll
-                for (int pt = 0; pt < 4; ++pt)
+                for (int pt = 0; pt < 4; ++pt) {
+                    const u64 at = reinterpret_cast<u64>(outs[pt]) + rowc;
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        outs[pt][head_e + static_cast<size_t>((c - 1) * CC + 4 * q + e) * tok_e + col] = g[pt][e];
+                        *reinterpret_cast<GLOBAL_AS float *>(at + e * e_step) = g[pt][e];
+                }
             }
             __syncthreads();
         }
@@ -1239,24 +1244,25 @@ __global__ __launch_bounds__(512) void wkv7_bwdc_gchain_kernel(BwdArgs p)
     } else {
         for (int k = 0; c >= 0; ++k, --c) {
             GchainBuf &cur = sm.buf[k & 1], &nxt = sm.buf[(k & 1) ^ 1];
-            // ---- phase 1: M_rb^T dO and T of chunk c; the factors of chunk c - 1
+            // ---- phase 1: T of chunk c (wave 7); R'^T dO of chunk c at the chain waves'
+            // columns (wave 4 for chain waves 0 and 3, waves 5 and 6 for 1 and 2)
             if (!exact_of(cur)) {
-                yprod(cur);
-                if (w4 == 3)
+                if (w4 == 3) {
                     tsolve(cur);
+                } else {
+                    qprod(cur, w4);
+                    if (w4 == 0)
+                        qprod(cur, 3);
+                }
             }
-            if (c > 0)
-                factors(nxt);
             __syncthreads();
             // ---- phase 2: chunk c - 1's matrices (its raw rows are still staged), then
             // chunk c - 2 staged (over chunk c's dO, read no more)
             if (c > 0) {
-                if (exact_of(nxt)) {
+                if (exact_of(nxt))
                     copy_raw(nxt);
-                } else {
+                else
                     mprod(nxt);
-                    qprod(nxt);
-                }
                 if (c > 1) {
                     stage_store(c - 2, cur);
                     if (c > 2)
