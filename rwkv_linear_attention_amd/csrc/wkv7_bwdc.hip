@@ -265,7 +265,9 @@ __global__ __launch_bounds__(GNW * 64) void wkv7_bwdc_chain_kernel(BwdArgs p)
 // products take (a row segment and a column segment of each), so three workgroups
 // share a compute unit.
 constexpr int RS = kN + 1;  // row stride of the LDS matrices (column reads hit distinct banks)
-constexpr int SS = CC + 1;  // row stride of the 16 x 16 matrices
+// row stride of the 16 x 16 matrices: rows 16-byte aligned, and a column read by 16
+// lanes (or a column per lane group) hits distinct banks
+constexpr int SS = CC + 4;
 
 // The 16 x 64 matrices.  dR0 = dO S^T, dA0 = dX S^T, dBz = Z G^T and dKv = V G^T (the
 // first terms of dR', dA', dB', dK', kept for the decay gradient) take the places of dO,
@@ -277,10 +279,10 @@ constexpr int X_DR0 = X_DO, X_DA0 = X_DX, X_DBZ = X_Z, X_DKV = X_V;
 enum Small { M_AB, M_AK, M_RB, M_RK, W_OV, NSMALL };
 constexpr int M_T = M_AB, W_OZ = M_AK, W_XZ = M_RB, W_XV = M_RK;
 
-// 43.4 KB: three workgroups share a compute unit.
+// 44.4 KB: three workgroups share a compute unit.
 struct ChunkSmem {
     float rows[NROW][CC][RS];  // 16 x 64 matrices (tokens x channels)
-    float sm[NSMALL][CC][SS];  // 16 x 16 matrices
+    alignas(16) float sm[NSMALL][CC][SS];  // 16 x 16 matrices
     alignas(16) float p7[kN];  // P_7 per key
     alignas(16) float d15[kN]; // d_15 per key
     alignas(16) int flag[4];   // per wave: a decay below 2^-15 in its quarter of the chunk
@@ -548,7 +550,7 @@ __global__ __launch_bounds__(256, 3) void wkv7_bwdc_chunk_kernel(BwdArgs p, int 
             d[tau] = d[tau - 1] * wcol[tau];
 #pragma unroll
         for (int tau = REF - 1; tau >= 0; --tau)
-            d[tau] = d[tau + 1] / wcol[tau + 1];
+            d[tau] = d[tau + 1] * __builtin_amdgcn_rcpf(wcol[tau + 1]);
         float pr = wcol[0];
 #pragma unroll
         for (int tau = 1; tau <= REF; ++tau)
@@ -559,12 +561,12 @@ __global__ __launch_bounds__(256, 3) void wkv7_bwdc_chunk_kernel(BwdArgs p, int 
             sm.p7[tc] = pr;
             sm.d15[tc] = d15;
         }
-        const float dm1 = d[0] / wcol[0];  // d_{-1}: the factor of a at the chunk's first token
+        const float dm1 = d[0] * __builtin_amdgcn_rcpf(wcol[0]);  // d_{-1}: the factor of a at the first token
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             dq[e] = sel4(q, d[e], d[4 + e], d[8 + e], d[12 + e]);
             dpq[e] = sel4(q, e == 0 ? dm1 : d[e - 1], d[3 + e], d[7 + e], d[11 + e]);
-            iq[e] = 1.0f / dq[e];
+            iq[e] = __builtin_amdgcn_rcpf(dq[e]);
             const int tau = 4 * q + e;
             sm.rows[X_R][tau][tc] = xr[e] * dq[e];
             sm.rows[X_A][tau][tc] = xa[e] * dpq[e];
@@ -809,13 +811,23 @@ __global__ __launch_bounds__(256, 3) void wkv7_bwdc_chunk_kernel(BwdArgs p, int 
         for (int j = 0; j < 4; ++j) {
             const int s = 4 * j + q;
             const float rs = sm.rows[X_R][s][i], as = sm.rows[X_A][s][i];
+            // row s of the four token-pair matrices, entries 0 .. 4 j + 3, four at a time
+            f32x4 oz[4], ov[4], xz[4], xv[4];
+#pragma unroll
+            for (int h = 0; h <= j; ++h) {
+                oz[h] = *reinterpret_cast<const f32x4 *>(&sm.sm[W_OZ][s][4 * h]);
+                ov[h] = *reinterpret_cast<const f32x4 *>(&sm.sm[W_OV][s][4 * h]);
+                xz[h] = *reinterpret_cast<const f32x4 *>(&sm.sm[W_XZ][s][4 * h]);
+                xv[h] = *reinterpret_cast<const f32x4 *>(&sm.sm[W_XV][s][4 * h]);
+            }
             float qr = 0.f, qa = 0.f;
             // t runs to the largest s of the four lanes; past this lane's s the terms are
             // formed and dropped (selects, so a non-finite dropped term does no harm)
 #pragma unroll
             for (int t = 1; t <= 4 * j + 3; ++t) {
-                qr = fmaf(bu[t - 1], sm.sm[W_OZ][s][t - 1], fmaf(ku[t - 1], sm.sm[W_OV][s][t - 1], qr));
-                qa = fmaf(bu[t - 1], sm.sm[W_XZ][s][t - 1], fmaf(ku[t - 1], sm.sm[W_XV][s][t - 1], qa));
+                const int u = t - 1;
+                qr = fmaf(bu[u], oz[u >> 2][u & 3], fmaf(ku[u], ov[u >> 2][u & 3], qr));
+                qa = fmaf(bu[u], xz[u >> 2][u & 3], fmaf(ku[u], xv[u >> 2][u & 3], qa));
                 const float cr = fmaf(rs, qr, acc[t]);
                 const float ca = fmaf(as, qa, cr);
                 acc[t] = t < s ? ca : (t == s ? cr : acc[t]);
@@ -876,13 +888,13 @@ __global__ __launch_bounds__(256, 3) void wkv7_bwdc_chunk_kernel(BwdArgs p, int 
 struct GchainBuf {
     float der[4][CC][RS];   // A', R', B' (raw a, r, b on the exact path) and raw w
     float dout[CC][RS];     // dO (zero past the end)
-    float sm[3][CC][SS];    // M_ab, M_rb, T
+    alignas(16) float sm[3][CC][SS];  // M_ab, M_rb, T
     alignas(16) float d15[kN];
     alignas(16) float p7[kN];
     int flag[4];            // per chain wave: a decay below 2^-15 among its keys
     float qd[4][16][64];    // R'^T dO of chain wave cw, value 4 pt + e of lane l
 };
-// 100.2 KB
+// 100.7 KB
 struct GchainSmem {
     float raw[4][CC][RS];  // r, w, a, b of the chunk being prepared (identity steps past the end)
     GchainBuf buf[2];
