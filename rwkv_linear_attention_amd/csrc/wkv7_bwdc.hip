@@ -1080,22 +1080,59 @@ __global__ __launch_bounds__(512) void wkv7_bwdc_gchain_kernel(BwdArgs p)
             }
         }
     };
-    // (prep, wave 7) T = (I - M_ab)^{-1}, a column per lane (T = I + M_ab T row by row)
+    // (prep, wave 7) T = (I - M_ab)^{-1}.  M = M_ab is strictly lower triangular, so
+    // M^16 = 0 and T = I + M + ... + M^15 = (I + M8)(I + M4)(I + M2)(I + M) (the factors
+    // commute): six 16 x 16 products on the matrix cores.  A product X Y takes X as the A
+    // operand (lane (q, n): X[n][4 q + i]) and Y in the accumulator layout (lane (q, n):
+    // Y[4 q + e][n]); a power needed as an A operand passes through LDS (over M_ab, read
+    // no more once both layouts of M are in registers).
     auto tsolve = [&](GchainBuf &b) {
-        const int sc = lane & 15;
-        float tcol[CC];
+        float(*const x)[SS] = b.sm[S_AB];
+        float am[4], cm[4];
 #pragma unroll
-        for (int t = 0; t < CC; ++t) {
-            float acc[4] = {t == sc ? 1.f : 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int u = 0; u < t; ++u)
-                acc[u & 3] = fmaf(b.sm[S_AB][t][u], tcol[u], acc[u & 3]);
-            tcol[t] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+        for (int i = 0; i < 4; ++i) {
+            am[i] = x[n][4 * q + i];
+            cm[i] = x[4 * q + i][n];
         }
-        if (lane < 16)
+        auto prod = [&](const float (&a)[4], const f32x4 &c0, const float (&bm)[4]) {
+            f32x4 acc = c0;
 #pragma unroll
-            for (int t = 0; t < CC; ++t)
-                b.sm[S_T][t][sc] = tcol[t];
+            for (int i = 0; i < 4; ++i)
+                acc = mfma4(a[i], bm[i], acc);
+            return acc;
+        };
+        auto as_a = [&](const f32x4 &c, float (&a)[4]) {  // accumulator layout -> A operand
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                x[4 * q + e][n] = c[e];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                a[i] = x[n][4 * q + i];
+        };
+        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+        f32x4 c2 = prod(am, zero, cm);  // M^2
+        float a2[4], a4[4], a8[4];
+        as_a(c2, a2);
+        float c2v[4] = {c2[0], c2[1], c2[2], c2[3]};
+        const f32x4 c4 = prod(a2, zero, c2v);  // M^4
+        as_a(c4, a4);
+        float c4v[4] = {c4[0], c4[1], c4[2], c4[3]};
+        const f32x4 c8 = prod(a4, zero, c4v);  // M^8
+        as_a(c8, a8);
+        // R = I + M, then R += M2 R, R += M4 R, R += M8 R
+        float r[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            r[e] = cm[e] + (4 * q + e == n ? 1.f : 0.f);
+        f32x4 rc = {r[0], r[1], r[2], r[3]};
+        rc = prod(a2, rc, r);
+        float r2[4] = {rc[0], rc[1], rc[2], rc[3]};
+        rc = prod(a4, rc, r2);
+        float r4[4] = {rc[0], rc[1], rc[2], rc[3]};
+        rc = prod(a8, rc, r4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            b.sm[S_T][4 * q + e][n] = rc[e];
     };
     // (prep) R'^T dO at chain wave cw's columns, tile by tile (keys 16 pt ..), in its
     // accumulator layout
