@@ -299,6 +299,62 @@ __device__ __forceinline__ float sel4(int q, float x0, float x1, float x2, float
     return (q & 2) ? ((q & 1) ? x3 : x2) : ((q & 1) ? x1 : x0);
 }
 
+// T = (I - M)^{-1} for a strictly lower triangular 16 x 16 M (in LDS, rows of SS), by one
+// wave.  M^16 = 0, so T = I + M + ... + M^15 = (I + M8)(I + M4)(I + M2)(I + M) (the
+// factors commute): six products on the matrix cores instead of a row-by-row solve.  A
+// product X Y takes X as the A operand (lane (q, n): X[n][4 q + i]) and Y in the
+// accumulator layout (lane (q, n): Y[4 q + e][n]); a power needed as an A operand passes
+// through m, which is overwritten.  T is written to t (m itself allowed).
+__device__ __forceinline__ void unit_lower_inverse(float (*m)[SS], float (*t)[SS], int lane)
+{
+    const int q = lane >> 4, n = lane & 15;
+    float am[4], cm[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        am[i] = m[n][4 * q + i];
+        cm[i] = m[4 * q + i][n];
+    }
+    auto prod = [&](const float (&a)[4], const f32x4 &c0, const float (&bm)[4]) {
+        f32x4 acc = c0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            acc = mfma4(a[i], bm[i], acc);
+        return acc;
+    };
+    auto as_a = [&](const f32x4 &c, float (&a)[4]) {  // accumulator layout -> A operand
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            m[4 * q + e][n] = c[e];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            a[i] = m[n][4 * q + i];
+    };
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    float a2[4], a4[4], a8[4];
+    const f32x4 c2 = prod(am, zero, cm);  // M^2
+    as_a(c2, a2);
+    const float c2v[4] = {c2[0], c2[1], c2[2], c2[3]};
+    const f32x4 c4 = prod(a2, zero, c2v);  // M^4
+    as_a(c4, a4);
+    const float c4v[4] = {c4[0], c4[1], c4[2], c4[3]};
+    const f32x4 c8 = prod(a4, zero, c4v);  // M^8
+    as_a(c8, a8);
+    // R = I + M, then R += M2 R, R += M4 R, R += M8 R
+    float r[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        r[e] = cm[e] + (4 * q + e == n ? 1.f : 0.f);
+    f32x4 rc = {r[0], r[1], r[2], r[3]};
+    rc = prod(a2, rc, r);
+    const float r2[4] = {rc[0], rc[1], rc[2], rc[3]};
+    rc = prod(a4, rc, r2);
+    const float r4[4] = {rc[0], rc[1], rc[2], rc[3]};
+    rc = prod(a8, rc, r4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        t[4 * q + e][n] = rc[e];
+}
+
 // The exact path of a chunk with a decay below 2^-15 (w = 0 included): the recurrence
 // itself.  Lane (q, m) of wave wv holds columns 16 q .. 16 q + 15 of key row 16 wv + m
 // of S and of G (the raw S0 and G_end are passed in).  A forward sweep forms
@@ -676,8 +732,8 @@ __global__ __launch_bounds__(256, 3) void wkv7_bwdc_chunk_kernel(BwdArgs p, int 
     mm64(dkacc, fa, grow);
     __syncthreads();
 
-    // ---- the 16-long products that need the M's; T = (I - M_ab)^{-1} (wave 0, one
-    // column per lane: T = I + M_ab T row by row); dO V^T (wave 1)
+    // ---- the 16-long products that need the M's; T = (I - M_ab)^{-1} (wave 0); dO V^T
+    // (wave 1)
     frag_tile(X_V, b4);
     frag_small(M_AK, false, 0, a4);
     mm16(xacc, a4, b4);      // X += M_ak V
@@ -687,20 +743,7 @@ __global__ __launch_bounds__(256, 3) void wkv7_bwdc_chunk_kernel(BwdArgs p, int 
     frag_small(M_RK, true, 0, a4);
     mm16(dvacc, a4, b4);     // dV += M_rk^T dO
     if (wv == 0) {
-        const int sc = lane & 15;
-        float tcol[CC];
-#pragma unroll
-        for (int t = 0; t < CC; ++t) {
-            float acc[4] = {t == sc ? 1.f : 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int u = 0; u < t; ++u)
-                acc[u & 3] = fmaf(sm.sm[M_AB][t][u], tcol[u], acc[u & 3]);
-            tcol[t] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-        }
-        if (lane < 16)  // over M_ab: this wave's reads of it are done (program order)
-#pragma unroll
-            for (int t = 0; t < CC; ++t)
-                sm.sm[M_T][t][sc] = tcol[t];
+        unit_lower_inverse(sm.sm[M_AB], sm.sm[M_T], lane);  // T over M_ab
     } else if (wv == 1) {
         frag_rows(X_DO, fa);
         frag_rows(X_V, fb);
@@ -1080,60 +1123,8 @@ __global__ __launch_bounds__(512) void wkv7_bwdc_gchain_kernel(BwdArgs p)
             }
         }
     };
-    // (prep, wave 7) T = (I - M_ab)^{-1}.  M = M_ab is strictly lower triangular, so
-    // M^16 = 0 and T = I + M + ... + M^15 = (I + M8)(I + M4)(I + M2)(I + M) (the factors
-    // commute): six 16 x 16 products on the matrix cores.  A product X Y takes X as the A
-    // operand (lane (q, n): X[n][4 q + i]) and Y in the accumulator layout (lane (q, n):
-    // Y[4 q + e][n]); a power needed as an A operand passes through LDS (over M_ab, read
-    // no more once both layouts of M are in registers).
-    auto tsolve = [&](GchainBuf &b) {
-        float(*const x)[SS] = b.sm[S_AB];
-        float am[4], cm[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            am[i] = x[n][4 * q + i];
-            cm[i] = x[4 * q + i][n];
-        }
-        auto prod = [&](const float (&a)[4], const f32x4 &c0, const float (&bm)[4]) {
-            f32x4 acc = c0;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                acc = mfma4(a[i], bm[i], acc);
-            return acc;
-        };
-        auto as_a = [&](const f32x4 &c, float (&a)[4]) {  // accumulator layout -> A operand
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                x[4 * q + e][n] = c[e];
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                a[i] = x[n][4 * q + i];
-        };
-        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-        f32x4 c2 = prod(am, zero, cm);  // M^2
-        float a2[4], a4[4], a8[4];
-        as_a(c2, a2);
-        float c2v[4] = {c2[0], c2[1], c2[2], c2[3]};
-        const f32x4 c4 = prod(a2, zero, c2v);  // M^4
-        as_a(c4, a4);
-        float c4v[4] = {c4[0], c4[1], c4[2], c4[3]};
-        const f32x4 c8 = prod(a4, zero, c4v);  // M^8
-        as_a(c8, a8);
-        // R = I + M, then R += M2 R, R += M4 R, R += M8 R
-        float r[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            r[e] = cm[e] + (4 * q + e == n ? 1.f : 0.f);
-        f32x4 rc = {r[0], r[1], r[2], r[3]};
-        rc = prod(a2, rc, r);
-        float r2[4] = {rc[0], rc[1], rc[2], rc[3]};
-        rc = prod(a4, rc, r2);
-        float r4[4] = {rc[0], rc[1], rc[2], rc[3]};
-        rc = prod(a8, rc, r4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            b.sm[S_T][4 * q + e][n] = rc[e];
-    };
+    // (prep, wave 7) T = (I - M_ab)^{-1} (over M_ab, read no more)
+    auto tsolve = [&](GchainBuf &b) { unit_lower_inverse(b.sm[S_AB], b.sm[S_T], lane); };
     // (prep) R'^T dO at chain wave cw's columns, tile by tile (keys 16 pt ..), in its
     // accumulator layout
     auto qprod = [&](GchainBuf &b, int cw) {
