@@ -514,3 +514,52 @@ def test_backward_is_causal(oracle_mod):
         assert not np.any(g[n][:, t0 + 1:]), n
         assert _rel(g[n][:, :t0 + 1], gs[n]) < 1e-13, n
     assert _rel(g["d_state_in"], gs["d_state_in"]) < 1e-13
+
+
+def _chunk_route(oracle_mod, r, w, k, v, a, b, S0, do, GS, dtype, C=16):
+    """The gradients by another route: the state-free gradient chain gives each chunk's
+    end gradient, and the chunk-form adjoint (tests/independent_routes.py) each chunk's
+    gradients from the state entering it (the oracle's per-position states) and that end
+    gradient.  Inputs one head, [T, N] fp64; the chunk algebra runs in ``dtype``."""
+    T, N = r.shape
+    _, _, sp = _one_head(oracle_mod, r, w, k, v, a, b, S0, per_position=True)
+    ends, d_state_in = routes.g_chain(r, w, a, b, do, GS, C)
+    out = {n: np.zeros((T, N)) for n in ("dr", "dw", "dk", "dv", "da", "db")}
+    for c in range(-(-T // C)):
+        t0, t1 = c * C, min(T, (c + 1) * C)
+        s_enter = S0 if c == 0 else sp[t0 - 1]
+        cast = lambda x: np.asarray(x, dtype)
+        g = routes.chunk_adjoint(*(cast(x[t0:t1]) for x in (r, w, k, v, a, b)), cast(s_enter),
+                                 cast(do[t0:t1]), cast(ends[c]))
+        for n in out:
+            out[n][t0:t1] = g[n]
+    return out, d_state_in
+
+
+@pytest.mark.parametrize("T,tiny", [(37, False), (40, True)])
+def test_backward_matches_chunk_form_route(oracle_mod, T, tiny):
+    # every gradient of the oracle's adjoint loop against the chunk-form route in fp64;
+    # with tiny decays (2^-14 .. 2^-10 on some tokens, above the exact-path threshold)
+    # the direct decay gradient keeps its accuracy where a log-decay form would not
+    rng = np.random.default_rng(46 + T)
+    N = 64
+    x = _rand_inputs(rng, 1, T, 1, N)
+    if tiny:
+        x["w"][0, 18:22, 0, :7] = 2.0 ** rng.uniform(-14, -10, (4, 7))
+    h = {n: x[n][0, :, 0, :] for n in "rwkvab"}
+    S0 = 0.2 * rng.standard_normal((N, N))
+    do = rng.standard_normal((T, N))
+    GS = rng.standard_normal((N, N))
+    ex = lambda m: m[None, :, None, :]
+    g = oracle_mod.backward(*(ex(h[n]) for n in "rwkvab"), S0[None, None], ex(do), GS[None, None])
+    route, dsi = _chunk_route(oracle_mod, *(h[n] for n in "rwkvab"), S0, do, GS, np.float64)
+    for n in route:
+        assert _rel(route[n], g[n][0, :, 0, :]) < 1e-11, n
+        # per token and key, against the row's scale: no element hides under the norm
+        scale = np.abs(g[n][0, :, 0, :]).max(axis=1, keepdims=True) + 1e-300
+        assert np.max(np.abs(route[n] - g[n][0, :, 0, :]) / scale) < 1e-9, n
+    assert _rel(dsi, g["d_state_in"][0, 0]) < 1e-12
+    # the same algebra in fp32 stays within the kernels' fp32 bar (1e-5)
+    r32, _ = _chunk_route(oracle_mod, *(h[n] for n in "rwkvab"), S0, do, GS, np.float32)
+    for n in r32:
+        assert _rel(r32[n], g[n][0, :, 0, :]) < 1e-5, n
