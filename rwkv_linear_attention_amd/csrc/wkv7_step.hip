@@ -202,6 +202,10 @@ __global__ __launch_bounds__(NW * 64) void wkv7_step_kernel(
                 for (int u = 0; u < RW; ++u)
                     __builtin_nontemporal_store(S[u], dst + u * kN);
             }
+            if (STAGED && state_out && t == L - 1)  // the final state leaves before the o reduction
+#pragma unroll
+                for (int u = 0; u < RW; ++u)
+                    __builtin_nontemporal_store(S[u], state_out + sbase + u * kN);
             part_r[g][j] = op;
             __syncthreads();
             if (g == 0) {
@@ -215,7 +219,7 @@ __global__ __launch_bounds__(NW * 64) void wkv7_step_kernel(
             }
         }
     }
-    if (state_out)  // absent when the per-position states carry the final state
+    if (state_out && (!STAGED || L == 0))  // (staged runs store it with their last token)
 #pragma unroll
         for (int u = 0; u < RW; ++u)
             __builtin_nontemporal_store(S[u], state_out + sbase + u * kN);
