@@ -839,8 +839,7 @@ __global__ __launch_bounds__(256, 3) void wkv7_bwdc_chunk_kernel(BwdArgs p, int 
     //            + sum_{s>=t} R'_s (dR0_s + Q_s(t)) + sum_{s>t} A'_s (dA0_s + P_s(t)).
     // Lane (q, m) forms the Q/P terms of key tc for the rows s = 4 j + q; the four
     // partials meet by shuffles.  Everything it reads is column tc, which this wave wrote
-    // (or the 16 x 16 matrices, complete since the last barrier): no barrier here.  The
-    // dR0, dA0 terms and the prefix over u are running sums in the final pass.
+    // (or the 16 x 16 matrices, complete since the last barrier): no barrier here.
     {
         const int i = tc;
         float bu[CC], ku[CC], acc[CC];
@@ -876,34 +875,56 @@ __global__ __launch_bounds__(256, 3) void wkv7_bwdc_chunk_kernel(BwdArgs p, int 
                 acc[t] = t < s ? ca : (t == s ? cr : acc[t]);
             }
         }
+        // The four lanes of key tc (lanes m + 16 q) hold partials of acc[t] over their rows
+        // s.  A reduce-scatter leaves lane q the sums of its own tokens 4 q .. 4 q + 3: the
+        // lane pairs q, q ^ 2 exchange token halves, then q, q ^ 1 token quarters.
+        const bool hi2 = (q & 2) != 0, hi1 = (q & 1) != 0;
+        float h8[8], mine[4];
 #pragma unroll
-        for (int t = 1; t < CC; ++t) {
-            acc[t] += __shfl_xor(acc[t], 16);
-            acc[t] += __shfl_xor(acc[t], 32);
+        for (int e = 0; e < 8; ++e) {
+            const float keep = hi2 ? acc[8 + e] : acc[e], send = hi2 ? acc[e] : acc[8 + e];
+            h8[e] = keep + __shfl_xor(send, 32);
         }
-        // suffix sums of R'_s dR0_s (s >= t) and A'_s dA0_s (s > t), prefix of the base terms
-        float tot[CC];
-        {
-            float sr = 0.f, sa = 0.f;
 #pragma unroll
-            for (int t = CC - 1; t >= 0; --t) {
-                sr = fmaf(sm.rows[X_R][t][i], sm.rows[X_DR0][t][i], sr);
-                tot[t] = sr + sa;
-                sa = fmaf(sm.rows[X_A][t][i], sm.rows[X_DA0][t][i], sa);
-            }
+        for (int e = 0; e < 4; ++e) {
+            const float keep = hi1 ? h8[4 + e] : h8[e], send = hi1 ? h8[e] : h8[4 + e];
+            mine[e] = keep + __shfl_xor(send, 16);
         }
-        float pre = gs_sum;
+        // This lane's tokens' R'_t dR0_t, A'_t dA0_t and B'_t dBz_t + K'_t dKv_t; the
+        // suffix over s >= t (s > t for the A' terms) and the prefix over u < t run across
+        // the four lanes' blocks by shuffles, then inside the block.
+        float rd[4], ad[4], bk[4];
+        float ra = 0.f, bks = 0.f;
 #pragma unroll
-        for (int t = 0; t < CC; ++t) {
-            tot[t] = t > 0 ? (pre + tot[t]) + acc[t] : pre + tot[t];
-            pre = fmaf(bu[t], sm.rows[X_DBZ][t][i], fmaf(ku[t], sm.rows[X_DKV][t][i], pre));
+        for (int e = 0; e < 4; ++e) {
+            const int t = 4 * q + e;
+            rd[e] = sm.rows[X_R][t][i] * sm.rows[X_DR0][t][i];
+            ad[e] = sm.rows[X_A][t][i] * sm.rows[X_DA0][t][i];
+            bk[e] = fmaf(sm.rows[X_B][t][i], sm.rows[X_DBZ][t][i], sm.rows[X_K][t][i] * sm.rows[X_DKV][t][i]);
+            ra += rd[e] + ad[e];
+            bks += bk[e];
+        }
+        float sr = 0.f, pr = gs_sum;
+#pragma unroll
+        for (int d = 1; d < 4; ++d) {
+            const float up = __shfl(ra, (lane + 16 * d) & 63), down = __shfl(bks, (lane - 16 * d) & 63);
+            sr += q + d < 4 ? up : 0.f;
+            pr += q - d >= 0 ? down : 0.f;
+        }
+        float suf[4];
+#pragma unroll
+        for (int e = 3; e >= 0; --e) {
+            sr += rd[e];
+            suf[e] = sr;
+            sr += ad[e];
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int t = 4 * q + e;
+            const float tot = (pr + suf[e]) + mine[e];
+            pr += bk[e];
             if (t < L)
-                p.dw[rowp(t) + i] =
-                    sel4(q, tot[e], tot[4 + e], tot[8 + e], tot[12 + e]) * __builtin_amdgcn_rcpf(sm.rows[X_W][t][i]);
+                p.dw[rowp(t) + i] = tot * __builtin_amdgcn_rcpf(sm.rows[X_W][t][i]);
         }
     }
 }
