@@ -676,14 +676,13 @@ __global__ __launch_bounds__(256, 3) void wkv7_bwdc_chunk_kernel(BwdArgs p, int 
         for (int i = 0; i < 4; ++i)
             f[i] = sm.rows[x][4 * q + i][tc];
     };
-    // a 16 x 16 matrix as the A operand over tokens, optionally transposed and masked to
-    // its lower triangle (strict or with the diagonal)
-    auto frag_small = [&](int sx, bool trans, int mask, float (&f)[4]) {
+    // a 16 x 16 matrix as the A operand over tokens, optionally transposed (every one is
+    // stored with its mask applied)
+    auto frag_small = [&](int sx, bool trans, float (&f)[4]) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int kk = 4 * q + i, row = trans ? kk : m, col = trans ? m : kk;
-            const bool keep = mask == 0 || (mask == 1 ? col < row : col <= row);
-            f[i] = keep ? sm.sm[sx][row][col] : 0.f;
+            f[i] = sm.sm[sx][row][col];
         }
     };
     auto mm64 = [](f32x4 &acc, const float (&a)[16], const float (&b)[16]) {
@@ -735,12 +734,12 @@ __global__ __launch_bounds__(256, 3) void wkv7_bwdc_chunk_kernel(BwdArgs p, int 
     // ---- the 16-long products that need the M's; T = (I - M_ab)^{-1} (wave 0); dO V^T
     // (wave 1)
     frag_tile(X_V, b4);
-    frag_small(M_AK, false, 0, a4);
+    frag_small(M_AK, false, a4);
     mm16(xacc, a4, b4);      // X += M_ak V
     frag_tile(X_DO, b4);
-    frag_small(M_RB, true, 0, a4);
+    frag_small(M_RB, true, a4);
     mm16(dzacc, a4, b4);     // dZ += M_rb^T dO
-    frag_small(M_RK, true, 0, a4);
+    frag_small(M_RK, true, a4);
     mm16(dvacc, a4, b4);     // dV += M_rk^T dO
     if (wv == 0) {
         unit_lower_inverse(sm.sm[M_AB], sm.sm[M_T], lane);  // T over M_ab
@@ -750,8 +749,8 @@ __global__ __launch_bounds__(256, 3) void wkv7_bwdc_chunk_kernel(BwdArgs p, int 
         f32x4 acc = zero4;
         mm64(acc, fa, fb);
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            sm.sm[W_OV][4 * q + e][m] = acc[e];
+        for (int e = 0; e < 4; ++e)  // stored as dM_rk: lower triangle with the diagonal
+            sm.sm[W_OV][4 * q + e][m] = m <= 4 * q + e ? acc[e] : 0.f;
     }
     __syncthreads();
 
@@ -760,12 +759,12 @@ __global__ __launch_bounds__(256, 3) void wkv7_bwdc_chunk_kernel(BwdArgs p, int 
     {
         float xb4[4] = {xacc[0], xacc[1], xacc[2], xacc[3]};
         float zb4[4] = {dzacc[0], dzacc[1], dzacc[2], dzacc[3]};
-        frag_small(M_T, false, 0, a4);
+        frag_small(M_T, false, a4);
         mm16(zacc, a4, xb4);
-        frag_small(M_T, true, 0, a4);
+        frag_small(M_T, true, a4);
         mm16(dxacc, a4, zb4);
         float db4[4] = {dxacc[0], dxacc[1], dxacc[2], dxacc[3]};
-        frag_small(M_AK, true, 0, a4);
+        frag_small(M_AK, true, a4);
         mm16(dvacc, a4, db4);
     }
     to_rows(X_Z, zacc);
@@ -783,9 +782,12 @@ __global__ __launch_bounds__(256, 3) void wkv7_bwdc_chunk_kernel(BwdArgs p, int 
         f32x4 acc = zero4;
         mm64(acc, fa, fb);
         const int dst = wv == 0 ? W_OZ : (wv == 2 ? W_XZ : W_XV);
+        // stored as dM_rb (lower triangle with the diagonal), dM_ab and dM_ak (strict)
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            sm.sm[dst][4 * q + e][m] = acc[e];
+        for (int e = 0; e < 4; ++e) {
+            const int tau = 4 * q + e;
+            sm.sm[dst][tau][m] = (wv == 0 ? m <= tau : m < tau) ? acc[e] : 0.f;
+        }
     }
     f32x4 daacc = zero4, dbacc = zero4;
     frag_rows(X_DX, fa);
@@ -801,26 +803,27 @@ __global__ __launch_bounds__(256, 3) void wkv7_bwdc_chunk_kernel(BwdArgs p, int 
 
     // ---- dR' = dR0 + dM_rb B' + dM_rk K',  dA' = dA0 + dM_ab B' + dM_ak K',
     //      dB' = dBz + dM_ab^T A' + dM_rb^T R',  dK' = dKv + dM_ak^T A' + dM_rk^T R'
-    // (dM_rb, dM_rk: dO Z^T, dO V^T with the diagonal; dM_ab, dM_ak: dX Z^T, dX V^T strict)
+    // (dM_rb, dM_rk: dO Z^T, dO V^T with the diagonal; dM_ab, dM_ak: dX Z^T, dX V^T strict;
+    // stored masked)
     frag_tile(X_B, b4);
-    frag_small(W_OZ, false, 2, a4);
+    frag_small(W_OZ, false, a4);
     mm16(dracc, a4, b4);
-    frag_small(W_XZ, false, 1, a4);
+    frag_small(W_XZ, false, a4);
     mm16(daacc, a4, b4);
     frag_tile(X_K, b4);
-    frag_small(W_OV, false, 2, a4);
+    frag_small(W_OV, false, a4);
     mm16(dracc, a4, b4);
-    frag_small(W_XV, false, 1, a4);
+    frag_small(W_XV, false, a4);
     mm16(daacc, a4, b4);
     frag_tile(X_A, b4);
-    frag_small(W_XZ, true, 1, a4);
+    frag_small(W_XZ, true, a4);
     mm16(dbacc, a4, b4);
-    frag_small(W_XV, true, 1, a4);
+    frag_small(W_XV, true, a4);
     mm16(dkacc, a4, b4);
     frag_tile(X_R, b4);
-    frag_small(W_OZ, true, 2, a4);
+    frag_small(W_OZ, true, a4);
     mm16(dbacc, a4, b4);
-    frag_small(W_OV, true, 2, a4);
+    frag_small(W_OV, true, a4);
     mm16(dkacc, a4, b4);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
