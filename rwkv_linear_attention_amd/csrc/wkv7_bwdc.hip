@@ -1233,6 +1233,7 @@ __global__ __launch_bounds__(512) void wkv7_bwdc_gchain_kernel(BwdArgs p)
                             g[pt][e] = fmaf(cur.der[D_W][t][key], g[pt][e], cur.der[D_A][t][key] * cs);
                         }
                 }
+                factors(nxt);
             } else {
 #pragma unroll
                 for (int pt = 0; pt < 4; ++pt) {
@@ -1255,6 +1256,9 @@ __global__ __launch_bounds__(512) void wkv7_bwdc_gchain_kernel(BwdArgs p)
                         else
                             dz0 = mfma4(a, gh[pt][e], dz0);
                     }
+                // the next chunk's factors while the products run (with no chunk left,
+                // harmlessly over the idle buffer: nothing reads it again)
+                factors(nxt);
                 dz = (dz0 + dz1) + dzy;
                 // the operands of phase 2 that are ready now
 #pragma unroll
@@ -1267,8 +1271,6 @@ __global__ __launch_bounds__(512) void wkv7_bwdc_gchain_kernel(BwdArgs p)
                     }
                 }
             }
-            if (c > 0)
-                factors(nxt);
             __syncthreads();
             // ---- phase 2: dX = T^T dZ (the B operand is this lane's own rows of dZ);
             // G_end of the chunk before = diag(P_7) (G^ + R'^T dO + A'^T dX), tile by tile
