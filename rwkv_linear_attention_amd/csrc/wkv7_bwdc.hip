@@ -274,8 +274,9 @@ constexpr int SS = CC + 4;
 // dX, Z and V once those are no longer read.
 enum Row { X_R, X_W, X_K, X_V, X_A, X_B, X_DO, X_Z, X_DX, NROW };
 constexpr int X_DR0 = X_DO, X_DA0 = X_DX, X_DBZ = X_Z, X_DKV = X_V;
-// The 16 x 16 matrices: T is formed over M_ab; dO Z^T, dX Z^T and dX V^T (the masked dM's
-// and the token-pair products of the decay gradient) over M_ak, M_rb and M_rk.
+// The 16 x 16 matrices: T is formed over M_ab; dM_rb = tril(dO Z^T), dM_ab = tril(dX Z^T, -1)
+// and dM_ak = tril(dX V^T, -1) (also the token-pair products of the decay gradient) over
+// M_ak, M_rb and M_rk; dM_rk = tril(dO V^T) has a slot of its own.
 enum Small { M_AB, M_AK, M_RB, M_RK, W_OV, NSMALL };
 constexpr int M_T = M_AB, W_OZ = M_AK, W_XZ = M_RB, W_XV = M_RK;
 
@@ -941,10 +942,10 @@ __global__ __launch_bounds__(256, 3) void wkv7_bwdc_chunk_kernel(BwdArgs p, int 
 // Only B' G^, T^T dZ and A'^T dX depend on G.  The rest is formed a phase or a chunk
 // ahead, in two LDS buffers (chunk c in one, chunk c - 1 in the other).  A chunk step is
 // two phases and two barriers:
-//   phase 1: chain waves: dZ of chunk c, then the factors, A', R', B' of chunk c - 1
-//            (from its staged raw rows).  Prep waves (4 .. 7, one beside each chain
-//            wave on its SIMD): T of chunk c (wave 7); R'^T dO of chunk c at the chain
-//            waves' columns (waves 4 .. 6);
+//   phase 1: chain waves: dZ of chunk c, with the factors, A', R', B' of chunk c - 1
+//            (from its staged raw rows) formed while the products run.  Prep waves
+//            (4 .. 7, one beside each chain wave on its SIMD): T of chunk c (wave 7);
+//            R'^T dO of chunk c at the chain waves' columns (waves 4 .. 6);
 //   phase 2: chain waves: dX and G of chunk c, stored as G_end of chunk c - 1.  Prep
 //            waves: M_ab (wave 4) and M_rb (wave 5) of chunk c - 1; the raw rows of chunk
 //            c - 2 staged (their loads were issued a chunk before).
@@ -980,13 +981,13 @@ __global__ __launch_bounds__(512) void wkv7_bwdc_gchain_kernel(BwdArgs p)
     const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, n = lane & 15;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const bool chain = wv < 4;
-    const int w4 = wv & 3;    // chain wave cw, or the prep wave's partner
+    const int w4 = wv & 3;    // chain wave cw, or the prep wave's place beside it
     const int ptid = tid & 255;
     const int bh = blockIdx.x;
     const int H = p.H, T = p.T;
     const int bb = bh / H, hh = bh - bb * H;
     const int nck = (T + CC - 1) / CC;
-    const int col = 16 * w4 + n;  // a chain wave's column; a prep wave's key (factors)
+    const int col = 16 * w4 + n;  // a chain wave's column (and key, in the factors)
     const size_t tok_e = static_cast<size_t>(H) * kN;
     const size_t head_e = static_cast<size_t>(bb) * T * tok_e + static_cast<size_t>(hh) * kN;
     const size_t sbase = static_cast<size_t>(bh) * (kN * kN) + col;
