@@ -104,11 +104,14 @@ def test_backward_ckpt_one_workgroup_per_head(K, oracle_mod, dtype, T):
     grads_vs_oracle(K, oracle_mod, inp, d_o, d_so, f"{dtype} H=129 T={T}")
 
 
-def test_backward_ckpt_no_state_in_no_final_gradient(K, oracle_mod):
-    inp = synth.make_inputs(2, 40, 5, 64, seed=4500, dtype="bf16", state_std=0.0)
+@pytest.mark.parametrize("B,H", [(2, 5), (1, 129)])
+def test_backward_ckpt_no_state_in_no_final_gradient(K, oracle_mod, B, H):
+    # with 129 heads the chunk-form chain starts from a zero gradient, and the chunk
+    # kernel's last chunk has no G_end to read
+    inp = synth.make_inputs(B, 40, H, 64, seed=4500 + H, dtype="bf16", state_std=0.0)
     assert inp["state_in"] is None
-    d_o = torch.randn((2, 40, 5, 64), generator=torch.Generator().manual_seed(4501))
-    grads_vs_oracle(K, oracle_mod, inp, d_o, None, "no state_in")
+    d_o = torch.randn((B, 40, H, 64), generator=torch.Generator().manual_seed(4501))
+    grads_vs_oracle(K, oracle_mod, inp, d_o, None, f"no state_in, H={H}")
 
 
 def test_backward_ckpt_longer_sequence_every_head(K, oracle_mod):
