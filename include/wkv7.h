@@ -30,7 +30,9 @@
  *   r, w, k, v, a, b, o : [B, T, H, N]      element (b,t,h,n) at ((b*T+t)*H+h)*N+n
  *   state_in, state_out : [B, H, N, N] fp32 element (b,h,i,j) at ((b*H+h)*N+i)*N+j
  *   state_pos           : [B, T, H, N, N] fp32, [b,t,h] = S after token t
- *   ckpt                : [B, ceil(T/16), H, N, N] fp32, [b,c,h] = S before token 16c
+ *   ckpt                : [B, ceil(T/16), H, N*N] fp32, [b,c,h] = S before token 16c,
+ *                         its element (i,j) at (j/16)*1024 + (i/16)*256 + (i/4%4)*64
+ *                         + (j%16)*4 + i%4 (tile order, see wkv7_forward_ckpt)
  *
  * MEMORY.  Every pointer is a DEVICE pointer on the current HIP device,
  * 16-byte aligned.  The caller owns every buffer; the library never
@@ -64,9 +66,10 @@ extern "C" {
 
 /* 2: commit and variable-length rows; 3: the two tail entry points; 4: the
  * backward pass; 5: wkv7_forward_tail (and the chunked kernel exact for every
- * decay); 6: wkv7_forward_ckpt and wkv7_backward_ckpt.  No entry point's
- * meaning changed in any of these. */
-#define WKV7_ABI_VERSION 6
+ * decay); 6: wkv7_forward_ckpt and wkv7_backward_ckpt; 7: the checkpoints in
+ * tile order (version 6 kept each checkpoint state row-major).  No other entry
+ * point's meaning changed in any of these. */
+#define WKV7_ABI_VERSION 7
 
 /* Element types of r, w, k, v, a, b (in_dtype) and of o (o_dtype). */
 enum wkv7_dtype {
@@ -300,8 +303,14 @@ int wkv7_backward(const void *r, const void *w, const void *k, const void *v,
  * (its `.rwkvq` backend section) describes this trainable kernel: it chunks, and
  * its backward pass rebuilds the state chunk by chunk.
  *
- *   ckpt : [B, ceil(T/16), H, N, N] fp32; ckpt[b, c, h] = the state of head h of
- *          row b before token 16 c (state_in, or zeros, for c = 0).
+ *   ckpt : [B, ceil(T/16), H, N*N] fp32; ckpt[b, c, h] = the state of head h of
+ *          row b before token 16 c (state_in, or zeros, for c = 0), in tile
+ *          order: element (i, j) (key row i, value column j) at
+ *          (j/16)*1024 + (i/16)*256 + (i/4 % 4)*64 + (j % 16)*4 + i % 4.  The
+ *          16 x 16 tiles of one block of 16 value columns lie together, and in
+ *          a tile each column's values of a group of four rows form one
+ *          16-byte unit: the chunked kernel keeps its state in that order, so
+ *          each of its stores writes whole contiguous kilobytes.
  * Everything else as wkv7_forward with o_dtype = WKV7_F32.  ckpt may be NULL
  * only when T = 0, and overlaps no other buffer.  For 1 <= T <= 8 (one chunk)
  * the call enqueues a copy of state_in (or a fill of zeros) into ckpt, then the
@@ -325,8 +334,8 @@ int wkv7_forward_ckpt(const void *r, const void *w, const void *k, const void *v
  * state bytes that wkv7_backward reads, and no state_in (ckpt[:, 0] is the input
  * state).
  *
- *   ckpt : [B, ceil(T/16), H, N, N] fp32, as wkv7_forward_ckpt wrote it from the
- *          same inputs and state_in.
+ *   ckpt : [B, ceil(T/16), H, N*N] fp32 in tile order, as wkv7_forward_ckpt
+ *          wrote it from the same inputs and state_in.
  * Everything else (d_o, d_state_out, the gradients, NULL rules, aliasing, the
  * limit B * H <= WKV7_MAX_HEADS_STEP) as wkv7_backward.  While the call runs,
  * dr, dk, da and db also hold the gradient for the state at each chunk's end

@@ -363,8 +363,10 @@ def wkv7_backward(r, w, k, v, a, b, state_in, state_pos, d_o, d_state_out=None, 
 def wkv7_forward_ckpt(r, w, k, v, a, b, state_in=None, *, o=None, state_out=None, ckpt=None):
     """Forward pass for training: (o, state_out, ckpt), o in fp32.
 
-    ckpt: [B, ceil(T/16), H, N, N] fp32, the state before each chunk of 16 tokens
+    ckpt: [B, ceil(T/16), H, N*N] fp32, the state before each chunk of 16 tokens
     (state_in, or zeros, first): what wkv7_backward_ckpt rebuilds the other states from.
+    Each state is in the C ABI's tile order: element (i, j) at (j//16)*1024 + (i//16)*256
+    + (i//4 % 4)*64 + (j % 16)*4 + i % 4.
     """
     B, T, H, N = _check_inputs(r, w, k, v, a, b)
     dev = r.device
@@ -378,8 +380,8 @@ def wkv7_forward_ckpt(r, w, k, v, a, b, state_in=None, *, o=None, state_out=None
     _out_arg(o, (B, T, H, N), dev, "o", f32)
     nck = (T + 15) // 16
     if ckpt is None:
-        ckpt = torch.empty((B, nck, H, N, N), dtype=torch.float32, device=dev)
-    _out_arg(ckpt, (B, nck, H, N, N), dev, "ckpt", f32)
+        ckpt = torch.empty((B, nck, H, N * N), dtype=torch.float32, device=dev)
+    _out_arg(ckpt, (B, nck, H, N * N), dev, "ckpt", f32)
     _check(lib().wkv7_forward_ckpt(*[_ptr(x) for x in (r, w, k, v, a, b)], _dt(r), _ptr(state_in), _ptr(o),
                                    _ptr(state_out), _ptr(ckpt) if nck else None, B, T, H, N, _stream(dev)))
     return o, state_out, ckpt
@@ -395,7 +397,7 @@ def wkv7_backward_ckpt(r, w, k, v, a, b, ckpt, d_o, d_state_out=None, *, grads=N
     f32 = (torch.float32,)
     d_state_out = _state_arg(d_state_out, B, H, N, dev, "d_state_out")
     nck = (T + 15) // 16
-    _out_arg(ckpt, (B, nck, H, N, N), dev, "ckpt", f32)
+    _out_arg(ckpt, (B, nck, H, N * N), dev, "ckpt", f32)
     _out_arg(d_o, (B, T, H, N), dev, "d_o", f32)
     names = ("dr", "dw", "dk", "dv", "da", "db")
     if grads is None:

@@ -542,9 +542,7 @@ int wkv7_forward_ckpt(const void *r, const void *w, const void *k, const void *v
     }
     // one chunk: its checkpoint is the input state, taken before the pass (which may
     // update that state in place)
-    const hipError_t e0 = state_in ? wkv7::launch_state_copy(state_in, ckpt, st_bytes / 4, s)
-                                   : wkv7::launch_state_reset(ckpt, B, H, nullptr, s);
-    if (e0 != hipSuccess)
+    if (wkv7::launch_ckpt_from_state(state_in, ckpt, B, H, s) != hipSuccess)
         return WKV7_ERR_HIP;
     return wkv7::launch_step(args, s) == hipSuccess ? WKV7_OK : WKV7_ERR_HIP;
 }

@@ -517,17 +517,18 @@ __global__ __launch_bounds__(256, 3) void wkv7_bwdc_chunk_kernel(BwdArgs p, int 
                                           pick(q == 2, reinterpret_cast<u64>(p.da), reinterpret_cast<u64>(p.db)))) +
                                     ginner
                               : glast + 4ull * CC * kN * q;
-        const u64 srow_a = s0 + 4ull * (tc * kN + 16 * q);
+        // the checkpoint in tile order: the row segment is 16 values 16 bytes apart, the
+        // column segment four 16-byte units 256 bytes apart
+        const u64 srow_a = s0 + 4ull * ckpt_offset(tc, 16 * q);
         const u64 grow_a = grb + m * gstride + 4ull * 16 * q;
-        scol_a = s0 + 4ull * (16 * q * kN + tc);
+        scol_a = s0 + 4ull * ckpt_offset(16 * q, tc);
         gcol_a = gcb + 4ull * tc;
 #pragma unroll
         for (int h4 = 0; h4 < 4; ++h4) {
-            const f32x4 sv = *reinterpret_cast<const GLOBAL_AS f32x4 *>(srow_a + 16u * h4);
             const f32x4 gv = *reinterpret_cast<const GLOBAL_AS f32x4 *>(grow_a + 16u * h4);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                srow[4 * h4 + e] = sv[e];
+                srow[4 * h4 + e] = *reinterpret_cast<const GLOBAL_AS float *>(srow_a + 16u * (4 * h4 + e));
                 grow[4 * h4 + e] = gv[e];
             }
         }
@@ -578,10 +579,15 @@ __global__ __launch_bounds__(256, 3) void wkv7_bwdc_chunk_kernel(BwdArgs p, int 
         return;
     }
 #pragma unroll
-    for (int ii = 0; ii < 16; ++ii) {
-        scol[ii] = *reinterpret_cast<const GLOBAL_AS float *>(scol_a + 4ull * kN * ii);
-        gcol[ii] = *reinterpret_cast<const GLOBAL_AS float *>(gcol_a + gstride * ii);
+    for (int h4 = 0; h4 < 4; ++h4) {
+        const f32x4 sv = *reinterpret_cast<const GLOBAL_AS f32x4 *>(scol_a + 256u * h4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            scol[4 * h4 + e] = sv[e];
     }
+#pragma unroll
+    for (int ii = 0; ii < 16; ++ii)
+        gcol[ii] = *reinterpret_cast<const GLOBAL_AS float *>(gcol_a + gstride * ii);
 
     // ---- decay factors of key tc (each lane of the key forms all 16), applied to this
     // lane's tokens 4 q .. 4 q + 3 of r, a, b, k

@@ -398,16 +398,17 @@ __global__ __launch_bounds__((kN / J / 16 + nprod<Tin>() + nextra<MODE>()) * 64)
         // compiler waits for these loads inside the loop, where the counter also holds the
         // previous chunk's output stores: every chunk would wait for those to drain.
         __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
-        // CKPT: [B, NCK, H, N, N] checkpoints; this lane's 16 elements of a head's state sit
-        // at offsets (16 pt + 4 q + e) N + jw + m from the head's base
+        // CKPT: [B, NCK, H, N*N] checkpoints in tile order (element (i, j) of a head's
+        // state at ckpt_offset(i, j) from its base): this lane's four values of row tile pt
+        // (rows 16 pt + 4 q + e, column jw + m) are one 16-byte unit, and the wave's store
+        // of a row tile is one contiguous kilobyte
         const int nck = (T + CH - 1) / CH;
         auto ckpt_store = [&](int c, const f32x4 (&x)[4]) {
-            float *const cb = p.ckpt + ((static_cast<size_t>(bb) * nck + c) * H + hh) * (kN * kN) + jw + m;
+            float *const cb = p.ckpt + ((static_cast<size_t>(bb) * nck + c) * H + hh) * (kN * kN) +
+                              ckpt_offset(4 * q, jw + m);
 #pragma unroll
             for (int pt = 0; pt < 4; ++pt)
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    cb[(16 * pt + 4 * q + e) * kN] = x[pt][e];
+                *reinterpret_cast<f32x4 *>(cb + ckpt_offset(16 * pt, 0)) = x[pt];
         };
         if constexpr (CKPT) {  // chunk 0 starts from the input state
             f32x4 x0[4];
@@ -1387,7 +1388,33 @@ hipError_t launch_typed(const SeqArgs &p, hipStream_t stream)
     return launch_j<Tin, Tout, 1>(p, stream);
 }
 
+// The checkpoint of a one-chunk pass: each head's input state (zeros when src is null)
+// in tile order, one 16-byte unit (four rows of one column) per thread.
+__global__ __launch_bounds__(256) void ckpt_from_state_kernel(const float *src, f32x4 *dst, long long n4)
+{
+    for (long long i = blockIdx.x * 256ll + threadIdx.x; i < n4; i += static_cast<long long>(gridDim.x) * 256) {
+        const long long head = i >> 10;
+        const int u = static_cast<int>(i & 1023);
+        // unit u holds rows 16 (u/64 % 4) + 4 (u/16 % 4) + e, column 16 (u/256) + u % 16
+        const int row0 = 16 * ((u >> 6) & 3) + 4 * ((u >> 4) & 3), col = 16 * (u >> 8) + (u & 15);
+        f32x4 x = {0.f, 0.f, 0.f, 0.f};
+        if (src)
+            for (int e = 0; e < 4; ++e)
+                x[e] = src[head * (kN * kN) + (row0 + e) * kN + col];
+        dst[i] = x;
+    }
+}
+
 }  // namespace
+
+hipError_t launch_ckpt_from_state(const float *state, float *ckpt, int B, int H, hipStream_t stream)
+{
+    const long long n4 = static_cast<long long>(B) * H * (kN * kN / 4);
+    const long long blocks = (n4 + 255) / 256;
+    hipLaunchKernelGGL(ckpt_from_state_kernel, dim3(static_cast<unsigned>(blocks < 65536 ? blocks : 65536)), dim3(256),
+                       0, stream, state, reinterpret_cast<f32x4 *>(ckpt), n4);
+    return hipGetLastError();
+}
 
 hipError_t launch_chunk(const SeqArgs &p, hipStream_t stream)
 {

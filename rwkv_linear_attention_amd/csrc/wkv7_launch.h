@@ -6,13 +6,23 @@
 
 namespace wkv7 {
 
+// Offset of element (i, j) (key row i, value column j) of one head's 64 x 64 state
+// within a checkpoint: the state is kept as 16 x 16 tiles, the tiles of one block of
+// 16 value columns together (row tiles inside), and within a tile as four groups of
+// four rows, each column's four values of a group in one 16-byte unit.
+__host__ __device__ constexpr int ckpt_offset(int i, int j)
+{
+    return (j >> 4) * 1024 + (i >> 4) * 256 + ((i >> 2) & 3) * 64 + (j & 15) * 4 + (i & 3);
+}
+
 struct SeqArgs {
     const void *r, *w, *k, *v, *a, *b;  // [B,T,H,64], in_dtype
     const float *state_in;              // [B,H,64,64] or nullptr (zeros)
     void *o;                            // [B,T,H,64], o_dtype
     float *state_out;                   // [B,H,64,64]
     float *state_pos;                   // [B,T,H,64,64] or nullptr
-    float *ckpt;                        // [B,ceil(T/16),H,64,64]: state entering each 16-token chunk, or nullptr
+    float *ckpt;                        // [B,ceil(T/16),H,64*64]: state entering each 16-token chunk
+                                        // (element order ckpt_offset), or nullptr
     const int *lengths;                 // [B] tokens of each row (clamped to [0, T]), or nullptr: all T
     int B, T, H;
     int in_bf16, o_bf16;                // dtype flags
@@ -37,7 +47,7 @@ struct BwdArgs {
     const void *r, *w, *k, *v, *a, *b;  // [B,T,H,64], in_dtype
     const float *state_in;              // [B,H,64,64] or nullptr (zeros)
     const float *state_pos;             // [B,T,H,64,64]: the state after each token (wkv7_backward)
-    const float *ckpt;                  // [B,ceil(T/16),H,64,64]: the state entering each chunk
+    const float *ckpt;                  // [B,ceil(T/16),H,64*64]: the state entering each chunk (ckpt_offset)
     const float *d_o;                   // [B,T,H,64]: gradient of o
     const float *d_state_out;           // [B,H,64,64] or nullptr (zeros)
     float *dr, *dw, *dk, *dv, *da, *db; // [B,T,H,64]
@@ -48,6 +58,7 @@ struct BwdArgs {
 
 hipError_t launch_step(const SeqArgs &a, hipStream_t stream);
 hipError_t launch_chunk(const SeqArgs &a, hipStream_t stream);
+hipError_t launch_ckpt_from_state(const float *state, float *ckpt, int B, int H, hipStream_t stream);
 hipError_t launch_state_copy(const float *src, float *dst, long long n_floats, hipStream_t stream);
 hipError_t launch_state_reset(float *state, int B, int H, const unsigned char *row_mask,
                               hipStream_t stream);

@@ -165,7 +165,7 @@ int main()
     EXPECT(fck(40, fake(7), fake(9)) == WKV7_OK && g_log.calls == 1 && !std::strcmp(g_log.kind, "chunk") &&
            g_log.seq.ckpt == ffake(9) && !g_log.seq.state_pos && !g_log.seq.o_bf16);
     EXPECT(fck(8, fake(7), fake(9)) == WKV7_OK && g_log.calls == 2 && !std::strcmp(g_log.kind, "step") &&
-           g_log.n == 2LL * 3 * 64 * 64 && !g_log.seq.ckpt);       // a copy of state_in, then the step kernel
+           g_log.n == 2LL * 3 * 64 * 64 && !g_log.seq.ckpt);       // state_in in tile order, then the step kernel
     EXPECT(fck(1, nullptr, fake(9)) == WKV7_OK && g_log.calls == 2 && !std::strcmp(g_log.kind, "step"));
     EXPECT(fck(0, fake(7), nullptr) == WKV7_OK && !std::strcmp(g_log.kind, "copy"));
     EXPECT(fck(40, fake(7), nullptr) == WKV7_ERR_NULL && g_log.calls == 0);

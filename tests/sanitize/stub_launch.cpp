@@ -39,6 +39,11 @@ hipError_t launch_state_reset(float *, int B, int H, const unsigned char *, hipS
 {
     return note("reset", B, 0, H);
 }
+hipError_t launch_ckpt_from_state(const float *, float *, int B, int H, hipStream_t)
+{
+    g_log.n = static_cast<long long>(B) * H * 64 * 64;
+    return note("ckpt_from_state", B, 0, H);
+}
 hipError_t launch_tail(const TailArgs &a, hipStream_t)
 {
     g_log.n = a.rows;

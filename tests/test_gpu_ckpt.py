@@ -3,7 +3,7 @@ the C ABI) against the fp64 oracle.
 
 The forward's checkpoints are compared with the oracle's states at the chunk
 boundaries (ckpt[:, c] = the state after token 16 c - 1, the input state for
-c = 0), o and state_out as for wkv7_forward.  The backward rebuilds every state
+c = 0), put in the checkpoints' tile order; o and state_out as for wkv7_forward.  The backward rebuilds every state
 from those fp32 checkpoints; its gradients are compared with the oracle's fp64
 adjoint (which forms its own fp64 states) at 1e-5 for bf16 and fp32 inputs alike,
 globally, per (batch, head) and elementwise (tests/parity.py).
@@ -32,15 +32,25 @@ def K():
     return m
 
 
+def tile_order(s):
+    """States [..., N, N] (key row i, value column j) in the checkpoints' element order:
+    element (i, j) of a state at offset 1024 (j // 16) + 256 (i // 16) + 64 (i // 4 % 4)
+    + 4 (j % 16) + i % 4 of its [N*N] block."""
+    lead = s.shape[:-2]
+    x = s.reshape(*lead, 4, 4, 4, 4, 16)  # i = 16 ib + 4 iq + ie, j = 16 jb + jm
+    k = len(lead)
+    return x.transpose(*range(k), k + 3, k, k + 1, k + 4, k + 2).reshape(*lead, 64 * 64)
+
+
 def expected_ckpt(s_pos, state_in, B, T, H):
-    """[B, ceil(T/16), H, N, N]: the state before each chunk of 16 tokens."""
+    """[B, ceil(T/16), H, N*N]: the state before each chunk of 16 tokens, in tile order."""
     nck = (T + 15) // 16
     out = np.zeros((B, nck, H, 64, 64))
     if state_in is not None:
         out[:, 0] = state_in.double().numpy()
     for c in range(1, nck):
         out[:, c] = s_pos[:, 16 * c - 1]
-    return out
+    return tile_order(out)
 
 
 def grads_vs_oracle(K, oracle_mod, inp, d_o, d_so, what):
@@ -148,7 +158,7 @@ def test_backward_ckpt_empty_sequence_and_in_place(K, H):
     s_in = inp["state_in"].cuda()
     o, s, ck = K.wkv7_forward_ckpt(*(d[n] for n in RWKVAB), s_in)
     torch.cuda.synchronize()
-    assert ck.shape == (2, 0, H, 64, 64) and torch.equal(s, s_in)
+    assert ck.shape == (2, 0, H, 64 * 64) and torch.equal(s, s_in)
     d_o = torch.empty((2, 0, H, 64), device="cuda")
     d_so = torch.randn((2, H, 64, 64), device="cuda")
     g = K.wkv7_backward_ckpt(*(d[n] for n in RWKVAB), ck, d_o, d_so)

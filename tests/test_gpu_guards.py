@@ -151,7 +151,7 @@ def test_training_pair_outputs(K, T):
     B, H = 2, 3
     d = to_dev(synth.make_inputs(B, T, H, 64, seed=420 + T, dtype="bf16", state_std=0.1))
     nck = (T + 15) // 16
-    o, s, ck = Guarded((B, T, H, 64)), Guarded((B, H, 64, 64)), Guarded((B, nck, H, 64, 64))
+    o, s, ck = Guarded((B, T, H, 64)), Guarded((B, H, 64, 64)), Guarded((B, nck, H, 64 * 64))
     K.wkv7_forward_ckpt(*[d[n] for n in NAMES], d["state_in"], o=o.t, state_out=s.t, ckpt=ck.t)
     _check("forward with checkpoints", o, s, ck)
     assert o.full() and s.full() and ck.full()
