@@ -313,8 +313,9 @@ int wkv7_backward(const void *r, const void *w, const void *k, const void *v,
  *          each of its stores writes whole contiguous kilobytes.
  * Everything else as wkv7_forward with o_dtype = WKV7_F32.  ckpt may be NULL
  * only when T = 0, and overlaps no other buffer.  For 1 <= T <= 8 (one chunk)
- * the call enqueues a copy of state_in (or a fill of zeros) into ckpt, then the
- * step kernel; from T = 9 on, the chunked kernel writes the checkpoints itself.
+ * the call enqueues a copy of state_in in tile order (or a fill of zeros) into
+ * ckpt, then the step kernel; from T = 9 on, the chunked kernel writes the
+ * checkpoints itself.
  * The checkpoints carry the chunked kernel's fp32 state: within about 1e-6
  * (relative L2) of the states of the definition.
  */
