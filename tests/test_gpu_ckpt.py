@@ -70,7 +70,7 @@ def grads_vs_oracle(K, oracle_mod, inp, d_o, d_so, what):
     (2, 45, 3, True),     # few heads: four column blocks per head
     (2, 41, 40, True),    # two column blocks
     (3, 37, 50, True),    # whole heads
-    (2, 5, 3, True),      # one chunk, the step kernel: the checkpoint is a copy of state_in
+    (2, 5, 3, True),      # one chunk, the step kernel: the checkpoint is state_in in tile order
     (1, 8, 2, False),     # ... or zeros
     (1, 16, 2, True),     # exactly one chunk (chunked kernel)
     (1, 17, 2, False),    # a last chunk of one token
