@@ -195,6 +195,32 @@ int main()
     EXPECT(bck(fake(9, 4), ffake(11), fake(18)) == WKV7_ERR_ALIGN);
     EXPECT(bck(fake(9), ffake(11), fake(9)) == WKV7_ERR_ALIAS);
 
+    // The checkpoints' tile order: a permutation of one state's N*N offsets, equal to the
+    // formula the header documents, and the order the chunked kernel's stores and the
+    // backward's loads assume (a wave's row tile is one contiguous kilobyte, a lane's four
+    // rows of a column one 16-byte unit).
+    {
+        static bool seen[64 * 64];
+        bool perm = true, documented = true, kernel = true;
+        for (int i = 0; i < 64; ++i)
+            for (int j = 0; j < 64; ++j) {
+                const int off = wkv7::ckpt_offset(i, j);
+                perm = perm && off >= 0 && off < 64 * 64 && !seen[off];
+                if (off >= 0 && off < 64 * 64)
+                    seen[off] = true;
+                documented = documented && off == (j / 16) * 1024 + (i / 16) * 256 + (i / 4 % 4) * 64 + (j % 16) * 4 + i % 4;
+            }
+        for (int jb = 0; jb < 4; ++jb)
+            for (int pt = 0; pt < 4; ++pt)
+                for (int lane = 0; lane < 64; ++lane)
+                    for (int e = 0; e < 4; ++e)
+                        kernel = kernel && wkv7::ckpt_offset(16 * pt + 4 * (lane / 16) + e, 16 * jb + lane % 16) ==
+                                               jb * 1024 + pt * 256 + lane * 4 + e;
+        EXPECT(perm);
+        EXPECT(documented);
+        EXPECT(kernel);
+    }
+
     for (int st = -8; st <= 2; ++st)
         EXPECT(wkv7_status_string(st) != nullptr && std::strlen(wkv7_status_string(st)) > 0);
     EXPECT(wkv7_abi_version() == WKV7_ABI_VERSION);
