@@ -180,6 +180,21 @@ def test_backward_ckpt_empty_sequence_and_in_place(K, H):
         assert torch.equal(grads[n], ref[n])
 
 
+@pytest.mark.parametrize("T", [5, 40])
+def test_forward_ckpt_in_place(K, T):
+    # state_out may be state_in itself: the one-chunk path takes its checkpoint before the
+    # step kernel updates the state, the chunked kernel keeps the input state in registers
+    inp = synth.make_inputs(2, T, 3, 64, seed=4810 + T, dtype="bf16", state_std=0.1)
+    d = {n: inp[n].cuda() for n in RWKVAB}
+    s_in = inp["state_in"].cuda()
+    o_ref, s_ref, ck_ref = K.wkv7_forward_ckpt(*(d[n] for n in RWKVAB), s_in)
+    state = s_in.clone()
+    o, s, ck = K.wkv7_forward_ckpt(*(d[n] for n in RWKVAB), state, state_out=state)
+    torch.cuda.synchronize()
+    assert s.data_ptr() == state.data_ptr()
+    assert torch.equal(o, o_ref) and torch.equal(state, s_ref) and torch.equal(ck, ck_ref)
+
+
 @pytest.mark.parametrize("idx,heads", [(2, [(0, 0), (7, 11)]), (3, [(0, 0), (2, 37), (3, 63)])])
 def test_workload_training_pair_sampled_heads(K, oracle_mod, idx, heads):
     # the prefill workloads at full size, in the launch configuration the benchmark
